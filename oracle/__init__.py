@@ -1,0 +1,216 @@
+"""CPU oracle for the top-k MoE FFN layer forward pass (fp64, plain C).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline are the only callers.  The GPU library never imports, links or runs
+anything from here, and this package imports nothing from it.
+
+Each wrapper below states the definition it evaluates; the C source
+(``moe_oracle.c``) cites the page and section of each step.
+
+Parity status: every function here is pinned by the ``-m "not gpu"`` tests
+in ``tests/test_oracle_pins.py`` (closed forms, special cases that reduce to a
+dense softmax ensemble or a library routine, brute force over subsets, and
+the pages' printed counts).  None is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# ORACLE_LIB_OVERRIDE loads another build of moe_oracle.c; the mutation tests
+# use it to check that the pins fail on a copy with a planted mistake.
+_LIB_PATH = os.environ.get("ORACLE_LIB_OVERRIDE") or os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+SOFTMAX, SIGMOID = 0, 1
+F32, BF16 = 0, 1
+
+
+def build(verbose: bool = False) -> str:
+    src = os.path.join(_HERE, "moe_oracle.c")
+    out = os.path.join(_HERE, "liboracle.so")
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-shared", "-fPIC", src,
+           "-o", out, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.check_call(cmd)
+    return out
+
+
+def _nthreads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        i32, i64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+        L.oracle_logits.argtypes = [i64, i64, i32, i32, vp, vp, i32, vp, i32]
+        L.oracle_logits.restype = None
+        L.oracle_route.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        L.oracle_route.restype = i32
+        L.oracle_dispatch.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp]
+        L.oracle_dispatch.restype = i32
+        L.oracle_expert_rows.argtypes = [i32, i32, i32, vp, i32, vp, i64, vp, vp, vp, vp, vp, i32]
+        L.oracle_expert_rows.restype = None
+        L.oracle_forward_tokens.argtypes = ([i32] * 9 + [vp] * 8 + [vp, vp, i64, vp, vp, vp, vp, i32])
+        L.oracle_forward_tokens.restype = i32
+        L.oracle_forward_expert_loop.argtypes = ([i64] + [i32] * 7 + [vp] * 7 + [vp, vp, vp, i32])
+        L.oracle_forward_expert_loop.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _dtype_of(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"oracle inputs are fp32 or bf16 bit patterns (uint16), got {a.dtype}")
+
+
+def _c(a):
+    return None if a is None else np.ascontiguousarray(a)
+
+
+def logits(x: np.ndarray, w_router: np.ndarray, rows: slice | None = None,
+           nthreads: int | None = None) -> np.ndarray:
+    """h[t,e] = sum_i x[t,i] W_r[e,i] in fp64, for the tokens in ``rows``."""
+    x, w_router = _c(x), _c(w_router)
+    T, d = x.shape
+    E = w_router.shape[0]
+    t0, t1 = (0, T) if rows is None else (rows.start or 0, rows.stop if rows.stop is not None else T)
+    out = np.empty((t1 - t0, E), dtype=np.float64)
+    lib().oracle_logits(t1 - t0, t0, d, E, x.ctypes.data, w_router.ctypes.data, _dtype_of(x),
+                        out.ctypes.data, nthreads or _nthreads())
+    return out
+
+
+def route(lg: np.ndarray, k: int, score_fn: int = SOFTMAX, renormalize: int = 1,
+          bias: np.ndarray | None = None, forced_ids: np.ndarray | None = None,
+          nthreads: int | None = None) -> dict:
+    """Scores, top-k ids (descending logit, ties to the lower index), gates and
+    the k-th/(k+1)-th gaps in score and logit space."""
+    lg = np.ascontiguousarray(lg, dtype=np.float64)
+    n, E = lg.shape
+    ids = np.empty((n, k), dtype=np.int32)
+    gates = np.empty((n, k), dtype=np.float64)
+    scores = np.empty((n, E), dtype=np.float64)
+    gs = np.empty(n, dtype=np.float64)
+    gl = np.empty(n, dtype=np.float64)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64)
+    fi = None if forced_ids is None else np.ascontiguousarray(forced_ids, dtype=np.int32)
+    rc = lib().oracle_route(n, E, k, score_fn, renormalize, lg.ctypes.data, _ptr(b), _ptr(fi),
+                            ids.ctypes.data, gates.ctypes.data, scores.ctypes.data,
+                            gs.ctypes.data, gl.ctypes.data, nthreads or _nthreads())
+    if rc:
+        raise ValueError(f"oracle_route failed ({rc})")
+    return dict(ids=ids, gates=gates, scores=scores, gap_score=gs, gap_logit=gl)
+
+
+def dispatch(ids: np.ndarray, E: int) -> dict:
+    """Pairs p = t*k + j grouped by expert (index order), ascending p inside."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, k = ids.shape
+    counts = np.empty(E, dtype=np.int32)
+    offsets = np.empty(E + 1, dtype=np.int32)
+    sp = np.empty(T * k, dtype=np.int32)
+    pp = np.empty(T * k, dtype=np.int32)
+    rc = lib().oracle_dispatch(T, k, E, ids.ctypes.data, counts.ctypes.data, offsets.ctypes.data,
+                               sp.ctypes.data, pp.ctypes.data)
+    if rc:
+        raise ValueError(f"oracle_dispatch failed ({rc})")
+    return dict(counts=counts, offsets=offsets, sorted_pairs=sp, pair_pos=pp)
+
+
+def expert_rows(e: int, x: np.ndarray, rows: np.ndarray, w_gate, w_up, w_down,
+                want_h: bool = False, nthreads: int | None = None):
+    """Expert e's SwiGLU on token rows ``rows``: (h [n,d_ff] or None, o [n,d])."""
+    x, w_gate, w_up, w_down = _c(x), _c(w_gate), _c(w_up), _c(w_down)
+    d = x.shape[1]
+    f = w_gate.shape[-2]
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    n = rows.size
+    h = np.empty((n, f), dtype=np.float64) if want_h else None
+    o = np.empty((n, d), dtype=np.float64)
+    lib().oracle_expert_rows(d, f, e, x.ctypes.data, _dtype_of(x), rows.ctypes.data, n,
+                             w_gate.ctypes.data, w_up.ctypes.data, w_down.ctypes.data, _ptr(h),
+                             o.ctypes.data, nthreads or _nthreads())
+    return h, o
+
+
+def forward_tokens(inp: dict, k: int, tokens, score_fn: int = SOFTMAX, renormalize: int = 1,
+                   forced_ids: np.ndarray | None = None, bias: np.ndarray | None = None,
+                   nthreads: int | None = None) -> dict:
+    """y for the listed tokens, token by token: y = sum_j g_j f_{id_j}(x) (+ f_s(x))."""
+    x = _c(inp["x"])
+    wr, wg, wu, wd = (_c(inp[n]) for n in ("w_router", "w_gate", "w_up", "w_down"))
+    sg, su, sd = (_c(inp.get(n)) for n in ("ws_gate", "ws_up", "ws_down"))
+    T, d = x.shape
+    E = wr.shape[0]
+    f = wg.shape[-2]
+    S = 0 if sg is None else 1
+    f_s = 0 if sg is None else sg.shape[0]
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    n = tokens.size
+    if n and (tokens.min() < 0 or tokens.max() >= T):
+        raise ValueError("token index out of range")
+    y = np.empty((n, d), dtype=np.float64)
+    ids = np.empty((n, k), dtype=np.int32)
+    gates = np.empty((n, k), dtype=np.float64)
+    fi = None if forced_ids is None else np.ascontiguousarray(forced_ids, dtype=np.int32)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64)
+    rc = lib().oracle_forward_tokens(d, E, k, f, S, f_s, score_fn, renormalize, _dtype_of(x),
+                                     x.ctypes.data, wr.ctypes.data, wg.ctypes.data,
+                                     wu.ctypes.data, wd.ctypes.data, _ptr(sg), _ptr(su), _ptr(sd),
+                                     _ptr(b), tokens.ctypes.data, n, _ptr(fi), y.ctypes.data,
+                                     ids.ctypes.data, gates.ctypes.data, nthreads or _nthreads())
+    if rc:
+        raise ValueError(f"oracle_forward_tokens failed ({rc})")
+    return dict(y=y, ids=ids, gates=gates)
+
+
+def forward_expert_loop(inp: dict, ids: np.ndarray, gates: np.ndarray,
+                        nthreads: int | None = None) -> np.ndarray:
+    """y [T,d] by looping over experts and the tokens that chose each."""
+    x = _c(inp["x"])
+    wg, wu, wd = (_c(inp[n]) for n in ("w_gate", "w_up", "w_down"))
+    sg, su, sd = (_c(inp.get(n)) for n in ("ws_gate", "ws_up", "ws_down"))
+    T, d = x.shape
+    E, f = wg.shape[0], wg.shape[1]
+    k = ids.shape[1]
+    S = 0 if sg is None else 1
+    f_s = 0 if sg is None else sg.shape[0]
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    gates = np.ascontiguousarray(gates, dtype=np.float64)
+    y = np.empty((T, d), dtype=np.float64)
+    lib().oracle_forward_expert_loop(T, d, E, k, f, S, f_s, _dtype_of(x), x.ctypes.data,
+                                     wg.ctypes.data, wu.ctypes.data, wd.ctypes.data, _ptr(sg),
+                                     _ptr(su), _ptr(sd), ids.ctypes.data, gates.ctypes.data,
+                                     y.ctypes.data, nthreads or _nthreads())
+    return y
+
+
+def forward(inp: dict, k: int, score_fn: int = SOFTMAX, renormalize: int = 1,
+            bias: np.ndarray | None = None, nthreads: int | None = None) -> dict:
+    """Whole layer for all tokens: routing, dispatch and y (expert-loop form)."""
+    lg = logits(inp["x"], inp["w_router"], nthreads=nthreads)
+    r = route(lg, k, score_fn, renormalize, bias=bias, nthreads=nthreads)
+    E = inp["w_router"].shape[0]
+    disp = dispatch(r["ids"], E)
+    y = forward_expert_loop(inp, r["ids"], r["gates"], nthreads=nthreads)
+    return dict(logits=lg, y=y, **r, **disp)

@@ -1,0 +1,333 @@
+/*
+ * CPU oracle for the forward pass of one top-k Mixture-of-Experts FFN layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline do.  It shares no code with the GPU library.
+ *
+ * Plain, slow, fp64.  Every stored input (fp32 or bf16) is widened exactly
+ * to double, and every sum is taken in double in a fixed order.  No blocking,
+ * fusion or reordering beyond what the definitions below state.
+ *
+ * What it computes, and where the pages define it:
+ *   - router logits  h(x) = W_r x, W_r in R^{E x d}, no bias
+ *       ("Mixture-of-Experts Internals", sec. 2.1 Router Architecture;
+ *        "Mixture of Experts: What Actually Happens...", Step 1)
+ *   - scores: softmax over all E (sec. 2.1 above), or a per-expert sigmoid
+ *       ("Mixture-of-Experts, from the router to the all-to-all", The router)
+ *   - top-k set I: the k largest, taken on the logits (softmax and sigmoid are
+ *       strictly increasing, so the set is the same); equal logits go to the
+ *       lower expert index; ids are listed by descending logit
+ *   - gates: g_i = s_i / sum_{j in I} s_j for i in I when renormalising
+ *       (sec. 2.1 above), else g_i = s_i (Switch's top-1 form, "from the
+ *       router to the all-to-all", The router)
+ *   - experts: f_e(x) = W_down (silu(W_gate x) * (W_up x)), silu(z) = z/(1+e^-z)
+ *       ("What Actually Happens...", DenseFFN and Step 4; "8.6 Mixture of
+ *        Experts", sec. 2)
+ *   - output: y = sum_{i in I} g_i f_i(x) (+ f_shared(x) with weight 1)
+ *       ("8.6 Mixture of Experts", sec. 2 boxed equation and sec. 4.1)
+ *   - dispatch: tokens grouped by expert, experts in index order, tokens in
+ *       ascending order inside each group ("What Actually Happens...", Step 3)
+ *
+ * Layouts (row-major): x [T,d]; w_router [E,d]; w_gate, w_up [E,d_ff,d];
+ * w_down [E,d,d_ff]; ws_gate, ws_up [d_ff_s,d]; ws_down [d,d_ff_s].
+ * dtype 0 = fp32, 1 = bf16 (uint16 bit patterns).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+#define OR_SOFTMAX 0
+#define OR_SIGMOID 1
+
+static double widen(const void* base, int dtype, int64_t i) {
+    if (dtype == OR_F32) return (double)((const float*)base)[i];
+    uint32_t u = (uint32_t)((const uint16_t*)base)[i] << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* logits[t,e] = sum_i x[t,i] * w_r[e,i], for t in [t0, t0+n). */
+void oracle_logits(int64_t n, int64_t t0, int d, int E, const void* x, const void* w_r, int dtype,
+                   double* logits, int nthreads) {
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+    for (int64_t tt = 0; tt < n; ++tt) {
+        int64_t t = t0 + tt;
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int i = 0; i < d; ++i)
+                acc += widen(x, dtype, t * (int64_t)d + i) * widen(w_r, dtype, (int64_t)e * d + i);
+            logits[tt * E + e] = acc;
+        }
+    }
+}
+
+/* Scores of one token from its logits. */
+static void scores_of(const double* l, int E, int score_fn, double* s) {
+    if (score_fn == OR_SOFTMAX) {
+        double m = l[0];
+        for (int e = 1; e < E; ++e) if (l[e] > m) m = l[e];
+        double z = 0.0;
+        for (int e = 0; e < E; ++e) { s[e] = exp(l[e] - m); z += s[e]; }
+        for (int e = 0; e < E; ++e) s[e] /= z;
+    } else {
+        for (int e = 0; e < E; ++e) s[e] = 1.0 / (1.0 + exp(-l[e]));
+    }
+}
+
+/* Does expert a come before expert b in the selection order?
+ * Larger logit first; equal logits: lower index first. */
+static int before(const double* l, int a, int b) {
+    if (l[a] != l[b]) return l[a] > l[b];
+    return a < b;
+}
+
+/*
+ * Routing of n tokens from their logits [n,E].
+ *   ids   [n,k]  chosen experts, in selection order
+ *   gates [n,k]  gate of each chosen expert
+ *   scores [n,E] (nullable) all scores
+ *   gap_score, gap_logit [n] (nullable): s_(k)-s_(k+1) and l_(k)-l_(k+1) in
+ *       selection order; +inf when k == E.
+ *   bias [E] (nullable): added to the logits for choosing only; the gates use
+ *       the unbiased scores ("Mixture-of-Experts Internals", sec. 3.3).
+ *   forced_ids [n,k] (nullable): skip selection and use these ids.
+ */
+static int route_one(int E, int k, int score_fn, int renorm, const double* l, const double* bias,
+                     const int32_t* forced, int32_t* id, double* gates, double* scores,
+                     double* gap_score, double* gap_logit, double* s, double* key, int* order) {
+    scores_of(l, E, score_fn, s);
+    if (scores) memcpy(scores, s, sizeof(double) * E);
+    for (int e = 0; e < E; ++e) key[e] = l[e] + (bias ? bias[e] : 0.0);
+    /* full selection order by insertion: plain and obviously correct */
+    for (int e = 0; e < E; ++e) {
+        int p = e;
+        while (p > 0 && before(key, e, order[p - 1])) { order[p] = order[p - 1]; --p; }
+        order[p] = e;
+    }
+    if (forced) {
+        for (int j = 0; j < k; ++j) {
+            if (forced[j] < 0 || forced[j] >= E) return -2;
+            id[j] = forced[j];
+        }
+    } else {
+        for (int j = 0; j < k; ++j) id[j] = order[j];
+    }
+    if (gap_score) *gap_score = (k < E) ? s[order[k - 1]] - s[order[k]] : INFINITY;
+    if (gap_logit) *gap_logit = (k < E) ? key[order[k - 1]] - key[order[k]] : INFINITY;
+    double denom = 0.0;
+    for (int j = 0; j < k; ++j) denom += s[id[j]];
+    for (int j = 0; j < k; ++j) gates[j] = renorm ? s[id[j]] / denom : s[id[j]];
+    return 0;
+}
+
+int oracle_route(int64_t n, int E, int k, int score_fn, int renorm, const double* logits,
+                 const double* bias, const int32_t* forced_ids, int32_t* ids, double* gates,
+                 double* scores, double* gap_score, double* gap_logit, int nthreads) {
+    if (k < 1 || k > E) return -2;
+    int err = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* s = (double*)malloc(sizeof(double) * E);
+        double* key = (double*)malloc(sizeof(double) * E);
+        int* order = (int*)malloc(sizeof(int) * E);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < n; ++t) {
+            int rc = route_one(E, k, score_fn, renorm, logits + t * E, bias,
+                               forced_ids ? forced_ids + t * k : NULL, ids + t * k, gates + t * k,
+                               scores ? scores + t * E : NULL, gap_score ? gap_score + t : NULL,
+                               gap_logit ? gap_logit + t : NULL, s, key, order);
+            if (rc) {
+#pragma omp atomic write
+                err = rc;
+            }
+        }
+        free(s); free(key); free(order);
+    }
+    return err;
+}
+
+/*
+ * Group the T*k (token, slot) pairs by expert: expert 0's pairs first, then
+ * expert 1's, ...; inside a group, pairs in ascending pair index p = t*k + j.
+ *   counts [E], offsets [E+1], sorted_pairs [T*k] (pair index at each
+ *   grouped position), pair_pos [T*k] (grouped position of each pair).
+ */
+int oracle_dispatch(int64_t T, int k, int E, const int32_t* ids, int32_t* counts,
+                    int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos) {
+    int64_t P = T * k;
+    int64_t pos = 0;
+    for (int e = 0; e < E; ++e) {
+        offsets[e] = (int32_t)pos;
+        int32_t c = 0;
+        for (int64_t p = 0; p < P; ++p) {
+            if (ids[p] < 0 || ids[p] >= E) return -2;
+            if (ids[p] == e) {
+                sorted_pairs[pos] = (int32_t)p;
+                pair_pos[p] = (int32_t)pos;
+                ++pos; ++c;
+            }
+        }
+        counts[e] = c;
+    }
+    offsets[E] = (int32_t)pos;
+    return pos == P ? 0 : -2;
+}
+
+/*
+ * One SwiGLU expert on one token vector (fp64):
+ *   a = W_gate x, b = W_up x, h = silu(a) * b, o = W_down h.
+ * wg, wu: [f, d]; wd: [d, f], all at element offset `woff_in` / `woff_dn` of
+ * their arrays.  h_out (nullable) gets h [f].
+ */
+static void swiglu_one(int d, int f, const void* x, int64_t xoff, int dtype, const void* wg,
+                       const void* wu, int64_t woff_in, const void* wd, int64_t woff_dn,
+                       double* h, double* o) {
+    for (int r = 0; r < f; ++r) {
+        double a = 0.0, b = 0.0;
+        for (int i = 0; i < d; ++i) {
+            double xi = widen(x, dtype, xoff + i);
+            a += widen(wg, dtype, woff_in + (int64_t)r * d + i) * xi;
+            b += widen(wu, dtype, woff_in + (int64_t)r * d + i) * xi;
+        }
+        h[r] = silu(a) * b;
+    }
+    for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int r = 0; r < f; ++r) acc += widen(wd, dtype, woff_dn + (int64_t)c * f + r) * h[r];
+        o[c] = acc;
+    }
+}
+
+/*
+ * Expert e applied to rows `rows[0..n)` of x: h_out [n,f] (nullable),
+ * o_out [n,d].
+ */
+void oracle_expert_rows(int d, int f, int e, const void* x, int dtype, const int32_t* rows,
+                        int64_t n, const void* wg, const void* wu, const void* wd,
+                        double* h_out, double* o_out, int nthreads) {
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* h = (double*)malloc(sizeof(double) * f);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n; ++i) {
+            swiglu_one(d, f, x, (int64_t)rows[i] * d, dtype, wg, wu, (int64_t)e * f * d, wd,
+                       (int64_t)e * d * f, h, o_out + i * d);
+            if (h_out) memcpy(h_out + i * f, h, sizeof(double) * f);
+        }
+        free(h);
+    }
+}
+
+/*
+ * Layer output for the tokens listed in `tokens[0..n)`, token by token, in
+ * the per-token form y = sum_j g_j f_{ids_j}(x) + f_shared(x).
+ *   forced_ids [n,k] (nullable): use these ids instead of selecting.
+ *   bias [E] (nullable): selection-only bias.
+ *   y [n,d]; ids_out [n,k], gates_out [n,k] (both nullable).
+ */
+int oracle_forward_tokens(int d, int E, int k, int f, int num_shared, int f_s, int score_fn,
+                          int renorm, int dtype, const void* x, const void* w_r, const void* wg,
+                          const void* wu, const void* wd, const void* sg, const void* su,
+                          const void* sd, const double* bias, const int32_t* tokens, int64_t n,
+                          const int32_t* forced_ids, double* y, int32_t* ids_out,
+                          double* gates_out, int nthreads) {
+    if (k < 1 || k > E || num_shared < 0 || num_shared > 1) return -2;
+    int err = 0;
+#pragma omp parallel num_threads(nthreads)
+    {
+        double* l = (double*)malloc(sizeof(double) * E);
+        double* s = (double*)malloc(sizeof(double) * E);
+        double* key = (double*)malloc(sizeof(double) * E);
+        int* order = (int*)malloc(sizeof(int) * E);
+        int32_t* id = (int32_t*)malloc(sizeof(int32_t) * k);
+        double* g = (double*)malloc(sizeof(double) * k);
+        int fmax = f > f_s ? f : f_s;
+        double* h = (double*)malloc(sizeof(double) * fmax);
+        double* o = (double*)malloc(sizeof(double) * d);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n; ++i) {
+            int64_t t = tokens[i];
+            for (int e = 0; e < E; ++e) {
+                double acc = 0.0;
+                for (int c = 0; c < d; ++c)
+                    acc += widen(x, dtype, t * d + c) * widen(w_r, dtype, (int64_t)e * d + c);
+                l[e] = acc;
+            }
+            int rc = route_one(E, k, score_fn, renorm, l, bias,
+                               forced_ids ? forced_ids + i * k : NULL, id, g, NULL, NULL, NULL,
+                               s, key, order);
+            if (rc) {
+#pragma omp atomic write
+                err = rc;
+                continue;
+            }
+            double* yt = y + i * d;
+            for (int c = 0; c < d; ++c) yt[c] = 0.0;
+            for (int j = 0; j < k; ++j) {
+                swiglu_one(d, f, x, t * d, dtype, wg, wu, (int64_t)id[j] * f * d, wd,
+                           (int64_t)id[j] * d * f, h, o);
+                for (int c = 0; c < d; ++c) yt[c] += g[j] * o[c];
+            }
+            if (num_shared) {
+                swiglu_one(d, f_s, x, t * d, dtype, sg, su, 0, sd, 0, h, o);
+                for (int c = 0; c < d; ++c) yt[c] += o[c];
+            }
+            if (ids_out) memcpy(ids_out + i * k, id, sizeof(int32_t) * k);
+            if (gates_out) memcpy(gates_out + i * k, g, sizeof(double) * k);
+        }
+        free(l); free(s); free(key); free(order); free(id); free(g); free(h); free(o);
+    }
+    return err;
+}
+
+/*
+ * Whole layer in the expert-loop form ("What Actually Happens...", Step 3):
+ * for each expert in index order, the tokens that chose it (ascending), each
+ * token's output accumulating g * f_e(x) in expert order; then the shared
+ * expert.  Routing (ids, gates) is an input here, from oracle_route.
+ *   y [T,d].
+ */
+int oracle_forward_expert_loop(int64_t T, int d, int E, int k, int f, int num_shared, int f_s,
+                               int dtype, const void* x, const void* wg, const void* wu,
+                               const void* wd, const void* sg, const void* su, const void* sd,
+                               const int32_t* ids, const double* gates, double* y, int nthreads) {
+    for (int64_t i = 0; i < T * d; ++i) y[i] = 0.0;
+    for (int e = 0; e < E; ++e) {
+#pragma omp parallel num_threads(nthreads)
+        {
+            double* h = (double*)malloc(sizeof(double) * f);
+            double* o = (double*)malloc(sizeof(double) * d);
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t t = 0; t < T; ++t) {
+                for (int j = 0; j < k; ++j) {
+                    if (ids[t * k + j] != e) continue;
+                    swiglu_one(d, f, x, t * d, dtype, wg, wu, (int64_t)e * f * d, wd,
+                               (int64_t)e * d * f, h, o);
+                    for (int c = 0; c < d; ++c) y[t * d + c] += gates[t * k + j] * o[c];
+                }
+            }
+            free(h); free(o);
+        }
+    }
+    if (num_shared) {
+#pragma omp parallel num_threads(nthreads)
+        {
+            double* h = (double*)malloc(sizeof(double) * f_s);
+            double* o = (double*)malloc(sizeof(double) * d);
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t t = 0; t < T; ++t) {
+                swiglu_one(d, f_s, x, t * d, dtype, sg, su, 0, sd, 0, h, o);
+                for (int c = 0; c < d; ++c) y[t * d + c] += o[c];
+            }
+            free(h); free(o);
+        }
+    }
+    return 0;
+}

@@ -1,0 +1,44 @@
+"""The pins catch planted mistakes.
+
+Each case plants one plausible slip into a copy of the oracle's C source
+(on the CPU, in a temporary directory), builds it, and runs the pin tests
+against that build in a subprocess.  At least one pin must fail for every
+slip.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
+
+MUTATIONS = {
+    "silu_on_up": ("h[r] = silu(a) * b;", "h[r] = a * silu(b);"),
+    "down_transposed": ("acc += widen(wd, dtype, woff_dn + (int64_t)c * f + r) * h[r];",
+                        "acc += widen(wd, dtype, woff_dn + (int64_t)r * d + c) * h[r];"),
+    "drop_shared": ("for (int c = 0; c < d; ++c) yt[c] += o[c];", ";"),
+    "tie_to_higher_index": ("return a < b;", "return a > b;"),
+    "no_renorm": ("gates[j] = renorm ? s[id[j]] / denom : s[id[j]];", "gates[j] = s[id[j]];"),
+    "sigmoid_sign": ("s[e] = 1.0 / (1.0 + exp(-l[e]));", "s[e] = 1.0 / (1.0 + exp(l[e]));"),
+    "dispatch_unstable": ("for (int64_t p = 0; p < P; ++p) {", "for (int64_t p = P - 1; p >= 0; --p) {"),
+    "softmax_denominator": ("s[e] = exp(l[e] - m); z += s[e];", "s[e] = exp(l[e] - m); z += s[e] * 1.0000001;"),
+    "logit_index": ("widen(w_r, dtype, (int64_t)e * d + c)", "widen(w_r, dtype, (int64_t)c * E + e)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    a, b = MUTATIONS[name]
+    src = open(SRC).read()
+    assert a in src, f"mutation site for {name} not found"
+    (tmp_path / "moe_oracle.c").write_text(src.replace(a, b))
+    lib = tmp_path / "liboracle.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", str(tmp_path / "moe_oracle.c"),
+                           "-o", str(lib), "-lm"])
+    env = dict(os.environ, ORACLE_LIB_OVERRIDE=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       env=env, capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert r.returncode != 0, f"no pin failed for planted mistake {name}:\n{r.stdout[-2000:]}"
