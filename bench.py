@@ -1,0 +1,222 @@
+"""Benchmark of the top-k MoE FFN layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one whole forward of the layer (route, dispatch, routed SwiGLU
+grouped GEMMs, shared expert, combine) over one batch of seeded synthetic
+inputs already resident in HBM.  The default workload is the Mixtral-8x7B-
+shaped prefill layer (T=4096, d=4096, E=8, k=2, d_ff=14336, bf16).
+
+Prints one JSON line with the throughput (tokens/s), the roofline of the
+dominant kernel measured live with HIP events on the launch stream, and the
+CPU oracle timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="mixtral_prefill")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target wall time of the CPU oracle sample")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_sparse_moe_amd", "csrc")
+    for n in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, n), "rb") as f:
+            h.update(n.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def upload(a: np.ndarray, torch, dev):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev)
+
+
+def algorithmic(sh, counts: np.ndarray) -> dict:
+    """Algorithmic work of the layer and of its two expert GEMM kernels.
+
+    FLOPs: router 2TdE, routed experts 6 d d_ff per pair (4 in gate/up, 2 in
+    down), shared expert 6 d d_ff_s per token.  Bytes: weights of the experts
+    actually touched (union read), the router weights, x read once, y written
+    once, 8 bytes of routing per pair; per kernel, its weights plus its
+    activation input and output."""
+    w = sh.elem_bytes
+    T, d, E, k, f = sh.T, sh.d, sh.E, sh.k, sh.d_ff
+    touched = int((counts > 0).sum())
+    P = T * k
+    layer_flops = sh.flops()
+    layer_bytes = (E * d * w + touched * 3 * d * f * w + sh.num_shared * 3 * d * sh.d_ff_shared * w
+                   + 2 * T * d * w + P * 8)
+    gate_up = dict(flops=4.0 * P * d * f, bytes=touched * 2 * d * f * w + T * d * w + P * f * w)
+    down = dict(flops=2.0 * P * d * f, bytes=touched * d * f * w + P * f * w + P * d * w)
+    return dict(layer_flops=layer_flops, layer_bytes=layer_bytes, gate_up=gate_up, down=down,
+                touched=touched)
+
+
+def cpu_baseline(sh, inp, target_s: float) -> dict:
+    """The oracle as it stands, on a bounded sample of tokens of the same layer."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    n = max(cores, 1)
+    tokens_done, t_used, sample_desc = 0, 0.0, ""
+    rng = np.random.default_rng(123)
+    while True:
+        toks = np.sort(rng.choice(sh.T, size=min(n, sh.T), replace=False))
+        t0 = time.perf_counter()
+        oracle.forward_tokens(inp, sh.k, toks, sh.score_fn, sh.renormalize, nthreads=cores)
+        dt = time.perf_counter() - t0
+        tokens_done, t_used = toks.size, dt
+        sample_desc = (f"{toks.size} of {sh.T} tokens (seeded random), full routing and "
+                       f"{sh.k} experts" + (" + shared expert" if sh.num_shared else "") +
+                       " per token, fp64")
+        if dt >= target_s / 4 or toks.size >= sh.T:
+            break
+        n = int(min(sh.T, max(n * 2, n * (target_s / max(dt, 1e-3)) * 0.8)))
+    return {"value": tokens_done / t_used, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": sample_desc, "seconds": round(t_used, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the layer is measured at N=1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mixture_experts_sparse_moe_amd as moe
+    import synth
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    moe.lib()
+    sh = synth.SHAPES[args.workload]
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    inp = synth.make_inputs(sh, args.seed)
+    d = {n: (None if a is None else upload(a, torch, dev)) for n, a in inp.items()}
+    print(f"[bench] {sh.name}: inputs generated and resident in HBM in "
+          f"{time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    cfg = moe.MoeConfig.of(sh.T, sh.d, sh.E, sh.k, sh.d_ff, sh.num_shared, sh.d_ff_shared,
+                           sh.score_fn, sh.renormalize, sh.dtype)
+    ws = moe.alloc_workspace(cfg, dev)
+    y = torch.empty(sh.T, sh.d, dtype=torch.bfloat16 if sh.dtype else torch.float32, device=dev)
+    counts = torch.empty(sh.E, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(start, evs):
+        moe.moe_forward_staged(cfg, d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"],
+                               d["ws_gate"], d["ws_up"], d["ws_down"], y, expert_counts=counts,
+                               ws=ws, start_event=start, stage_events=evs, stream=stream)
+
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        step(None, None)
+    torch.cuda.synchronize()
+    starts = [mk() for _ in range(args.steps)]
+    stages = [[mk() for _ in range(moe.MOE_NUM_STAGES)] for _ in range(args.steps)]
+    for i in range(args.steps):       # create the events before the timed region
+        starts[i].record(stream)
+        for e in stages[i]:
+            e.record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(starts[i], stages[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+
+    stage_ms = np.zeros((args.steps, moe.MOE_NUM_STAGES))
+    for i in range(args.steps):
+        prev = starts[i]
+        for j, e in enumerate(stages[i]):
+            stage_ms[i, j] = prev.elapsed_time(e)
+            prev = e
+    stage_avg = stage_ms.mean(0)
+    cnt = counts.cpu().numpy()
+    alg = algorithmic(sh, cnt)
+
+    gu_ms = float(stage_avg[2])
+    decode = sh.T * sh.k <= 8 * sh.E * 16      # few rows per expert: weight-read bound
+    if decode:
+        achieved = alg["gate_up"]["bytes"] / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        peak = PEAK_BF16_TFLOPS if sh.dtype == synth.BF16 else PEAK_F32_TFLOPS
+        achieved = alg["gate_up"]["flops"] / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = "gate_up_gemm (grouped gate/up GEMM + SiLU*up)"
+    roof["per_launch"] = {"flops": alg["gate_up"]["flops"], "bytes": alg["gate_up"]["bytes"],
+                          "avg_ms": gu_ms}
+    roof["traffic"] = None
+    src_hash = kernel_source_hash()
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE)).get(sh.name, {})
+        if rec.get("source_hash") == src_hash:
+            roof["traffic"] = rec.get("bytes_per_launch")
+    layer_s = ms_per_step * 1e-3
+    out = {
+        "metric": "MoE-layer tokens/s",
+        "value": sh.T / layer_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if sh.dtype == synth.BF16 else "f32",
+        "data": "synthetic (seeded Philox normals; weights N(0,1/fan_in))",
+        "config": {"workload": sh.name, "T": sh.T, "d": sh.d, "E": sh.E, "k": sh.k,
+                   "d_ff": sh.d_ff, "num_shared": sh.num_shared, "d_ff_shared": sh.d_ff_shared,
+                   "score": "sigmoid" if sh.score_fn else "softmax",
+                   "renormalize": sh.renormalize, "parallelism": "single GPU"},
+        "layer_tflops": alg["layer_flops"] / layer_s / 1e12,
+        "layer_pct_bf16_peak": alg["layer_flops"] / layer_s / 1e12 / PEAK_BF16_TFLOPS,
+        "layer_gbs": alg["layer_bytes"] / layer_s / 1e9,
+        "layer_pct_hbm": alg["layer_bytes"] / layer_s / 1e9 / PEAK_HBM_GBS,
+        "stages_ms": {n: round(float(v), 4) for n, v in zip(moe.STAGE_NAMES, stage_avg)},
+        "expert_load": {"max_over_mean": float(cnt.max() / max(cnt.mean(), 1e-9)),
+                        "touched": alg["touched"], "min": int(cnt.min()), "max": int(cnt.max())},
+        "roofline": roof,
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(sh, inp, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) top-k Mixture-of-Experts FFN layer,
+ * forward pass.
+ *
+ * The layer (pages: "Mixture-of-Experts Internals: A Systems Engineer's Field
+ * Manual" sec. 2.1; "8.6 -- Mixture of Experts (MoE)" sec. 2 and 4.1;
+ * "Mixture-of-Experts, from the router to the all-to-all", The router;
+ * "Mixture of Experts: What Actually Happens When a Token Hits the Router",
+ * Steps 1-4):
+ *
+ *   h = W_r x                              router logits, fp32
+ *   s = softmax(h) | sigmoid(h)            scores
+ *   I = top-k of h (ties: lower index)     selection
+ *   g_i = s_i / sum_{j in I} s_j           gates (or g_i = s_i unrenormalised)
+ *   y = sum_{i in I} g_i f_i(x) + f_s(x)   f(x) = W_down(silu(W_gate x) * W_up x)
+ *
+ * Conventions shared by every entry point:
+ *   - Ownership: the caller owns every buffer.  The library never allocates,
+ *     frees or keeps state between calls; calls are thread-safe.
+ *   - Pointers: every tensor pointer is a DEVICE pointer (HBM of the current
+ *     HIP device).  `cfg` is a HOST pointer read during the call only.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *     stream).  Every call only enqueues work on it: no host synchronisation,
+ *     no device-to-host copy.  Results are valid once the stream reaches them.
+ *   - Layouts, row-major, C order:
+ *       x, y [T, d]; w_router [E, d]
+ *       w_gate, w_up [E, d_ff, d]; w_down [E, d, d_ff]
+ *       ws_gate, ws_up [d_ff_s, d]; ws_down [d, d_ff_s]
+ *       topk_ids, topk_weights [T, k]
+ *       expert_out [T*k, d] in expert-grouped order; shared_out [T, d]
+ *   - Types: x, y, weights, expert_out, shared_out use cfg->dtype (fp32 or
+ *     bf16).  Gates, gaps and logits are fp32; indices and counts int32.
+ *   - Pairs: the T*k (token, slot) assignments are numbered p = t*k + j.
+ *   - Limits: 1 <= E <= 256, 1 <= k <= min(E, 16), d, d_ff, d_ff_s multiples
+ *     of 64, T*k < 2^31, T >= 0 (T = 0 is a valid no-op).  Pointers 16-byte
+ *     aligned.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued; on error nothing is enqueued and a negative moe_status is
+ *     returned.  A failed launch returns MOE_ERR_HIP.  Device faults surface
+ *     at the caller's next synchronisation.  Inputs must be finite: the
+ *     result for NaN or Inf inputs is undefined.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+    MOE_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+    MOE_ERR_UNSUPPORTED = -3, /* outside the limits above (E > 256, k > 16, d % 64, dtype) */
+    MOE_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+    MOE_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required */
+    MOE_ERR_HIP = -6          /* a HIP launch failed */
+} moe_status;
+
+typedef enum moe_score_fn {
+    MOE_SCORE_SOFTMAX = 0,    /* softmax over all E experts */
+    MOE_SCORE_SIGMOID = 1     /* independent sigmoid per expert */
+} moe_score_fn;
+
+typedef enum moe_dtype {
+    MOE_F32 = 0,
+    MOE_BF16 = 1
+} moe_dtype;
+
+typedef struct moe_config {
+    int32_t num_tokens;   /* T */
+    int32_t d_model;      /* d */
+    int32_t num_experts;  /* E, routed experts */
+    int32_t top_k;        /* k */
+    int32_t d_ff;         /* width of each routed expert */
+    int32_t num_shared;   /* 0 or 1 always-on shared expert(s), weight 1 */
+    int32_t d_ff_shared;  /* width of the shared expert (ignored if num_shared == 0) */
+    int32_t score_fn;     /* moe_score_fn */
+    int32_t renormalize;  /* 1: gates renormalised over the k chosen; 0: raw scores */
+    int32_t dtype;        /* moe_dtype of activations and weights */
+} moe_config;
+
+/* Bytes of device workspace moe_forward needs for `cfg` (also enough for
+ * every other entry point).  0 for an invalid cfg.  Host only. */
+size_t moe_workspace_bytes(const moe_config* cfg);
+
+/* Human-readable name of a status code.  Host only; static storage. */
+const char* moe_status_str(int status);
+
+/*
+ * Router + top-k + gates ("Mixture-of-Experts Internals" sec. 2.1; "from the
+ * router to the all-to-all", The router).
+ *   x [T,d], w_router [E,d]                 in
+ *   topk_ids [T,k] int32                    out: chosen experts, by descending
+ *                                                logit, ties to the lower index
+ *   topk_weights [T,k] fp32                 out: gates
+ *   topk_gap [T] fp32 (nullable)            out: h_(k) - h_(k+1), the logit
+ *                                                margin of the k-th choice
+ *                                                (+inf when k == E)
+ * Logits are accumulated in fp32 (products of bf16 inputs are exact in fp32).
+ */
+int moe_route(const moe_config* cfg, const void* x, const void* w_router, int32_t* topk_ids,
+              float* topk_weights, float* topk_gap, void* stream);
+
+/*
+ * Group the T*k pairs by expert ("What Actually Happens...", Step 3: sort
+ * tokens by assigned expert into contiguous blocks).  Stable: inside expert
+ * e's block, pairs keep ascending p.
+ *   topk_ids [T,k]                          in
+ *   expert_counts [E] int32                 out: pairs per expert
+ *   expert_offsets [E+1] int32              out: exclusive prefix sum; the
+ *                                                block of expert e is rows
+ *                                                [off[e], off[e+1])
+ *   sorted_pairs [T*k] int32                out: pair p at each grouped row
+ *   pair_pos [T*k] int32                    out: grouped row of each pair
+ *   ws, ws_bytes                            scratch, >= moe_workspace_bytes
+ * ids outside [0, E) are a precondition violation (undefined result).
+ */
+int moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t* expert_counts,
+                 int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/*
+ * Expert SwiGLU FFNs as one grouped GEMM pair ("8.6 Mixture of Experts" sec.
+ * 2; "What Actually Happens...", Step 4): for every grouped row r of expert
+ * e with pair p = sorted_pairs[r] and token t = p / k,
+ *   expert_out[r] = W_down,e (silu(W_gate,e x_t) * (W_up,e x_t)),
+ * and, when cfg->num_shared == 1, for every token t
+ *   shared_out[t] = W_sdown (silu(W_sgate x_t) * (W_sup x_t)).
+ * The intermediate silu(.)*(.) is rounded to cfg->dtype.
+ *   x [T,d], sorted_pairs [T*k], expert_offsets [E+1]   in
+ *   w_gate, w_up, w_down                                in (routed experts)
+ *   ws_gate, ws_up, ws_down                             in (nullable iff num_shared == 0)
+ *   expert_out [T*k, d]                                 out
+ *   shared_out [T, d]                                   out (nullable iff num_shared == 0)
+ *   ws, ws_bytes                                        scratch
+ */
+int moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* sorted_pairs,
+                   const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                   const void* w_down, const void* ws_gate, const void* ws_up,
+                   const void* ws_down, void* expert_out, void* shared_out, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/*
+ * Gate-weighted combine back into token order ("8.6 Mixture of Experts" sec.
+ * 2 boxed equation and sec. 4.1):
+ *   y[t] = sum_{j=0..k-1} topk_weights[t,j] * expert_out[pair_pos[t*k+j]]
+ *          (+ shared_out[t])
+ * summed in fp32 in slot order j = 0..k-1, then rounded to cfg->dtype.  No
+ * atomics: every y row is written once.
+ *   shared_out nullable iff num_shared == 0.
+ */
+int moe_combine(const moe_config* cfg, const void* expert_out, const float* topk_weights,
+                const int32_t* pair_pos, const void* shared_out, void* y, void* stream);
+
+/*
+ * The whole layer: route, dispatch, expert FFNs (and the shared expert) and
+ * combine, enqueued back to back on `stream`.
+ *   topk_ids_out [T,k], topk_weights_out [T,k], expert_counts_out [E]:
+ *   optional copies of the routing (nullable; the workspace is used when
+ *   NULL).
+ */
+int moe_forward(const moe_config* cfg, const void* x, const void* w_router, const void* w_gate,
+                const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,
+                const void* ws_down, void* y, int32_t* topk_ids_out, float* topk_weights_out,
+                int32_t* expert_counts_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_forward with per-stage timing ("T2.6 -- What Mixture of Experts
+ * Changes", In practice: watch per-expert counts and expert compute time;
+ * profile each stage).  Same arguments and results as moe_forward, plus
+ *   stage_events: MOE_NUM_STAGES hipEvent_t handles (passed as void*),
+ *                 created by the caller; event i is recorded on `stream`
+ *                 right after stage i is enqueued:
+ *                 0 route, 1 dispatch, 2 routed gate/up GEMM (+SiLU*up),
+ *                 3 routed down GEMM, 4 shared gate/up, 5 shared down,
+ *                 6 combine.  Stages 4-5 are empty when num_shared == 0.
+ *   start_event:  recorded before stage 0 (nullable).
+ * The elapsed time between consecutive events is the stage's device time.
+ */
+#define MOE_NUM_STAGES 7
+int moe_forward_staged(const moe_config* cfg, const void* x, const void* w_router,
+                       const void* w_gate, const void* w_up, const void* w_down,
+                       const void* ws_gate, const void* ws_up, const void* ws_down, void* y,
+                       int32_t* topk_ids_out, float* topk_weights_out,
+                       int32_t* expert_counts_out, void* ws, size_t ws_bytes, void* start_event,
+                       void* const* stage_events, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,364 @@
+// Grouped GEMMs of the expert SwiGLU FFNs ("8.6 Mixture of Experts" sec. 2;
+// "What Actually Happens When a Token Hits the Router", Step 4).
+//
+// For each group (expert) e with grouped rows [off[e], off[e+1]):
+//   dual:   C[r, n] = silu(sum_k A[src(r), k] B0[e, n, k]) * (sum_k A[src(r), k] B1[e, n, k])
+//   single: C[r, n] = sum_k A[src(r), k] B0[e, n, k]
+// src(r) = gather[r] / gather_div (token of the pair) when gathering, else r.
+// Both operands are K-contiguous ("NT"), the natural MFMA operand layout.
+//
+// bf16 kernel (gfx950):
+//   - v_mfma_f32_32x32x16_bf16, fp32 accumulation.
+//   - Workgroup 256 threads = 2x2 waves on a BM x BN output tile (x2 weight
+//     matrices in dual mode: the gate and up tiles of the same columns sit
+//     in the same lanes, so silu(g)*u is a register-only epilogue).
+//   - BK = 64.  Global -> registers -> LDS, double-buffered: the next K tile
+//     is in flight while the MFMAs consume the current one; one barrier per
+//     K tile.  A rows are gathered on load (no permuted copy of x).
+//   - LDS rows are 64 bf16 = 8 chunks of 16 B; chunk c of row r is stored at
+//     c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1), so the 16-byte fragment reads
+//     of 32 consecutive rows hit distinct banks.
+//   - M tiles are data dependent: tile mt of the flattened list maps to
+//     (expert, row range) by a prefix sum of ceil(count_e / BM) done in the
+//     workgroup, so no host sync is needed; the grid is sized by the upper
+//     bound ceil(rows / BM) + G and surplus tiles exit at once.
+//   - Workgroup ids are remapped so that the 8 XCDs (ids dealt round-robin)
+//     each run a contiguous range of logical tiles; logical tiles run WMW
+//     M-tiles at a time per N column, so tiles sharing a weight panel are
+//     resident in the same XCD's L2 together.
+// fp32 kernel: LDS-tiled FMA (the tiny fp32 layer only).
+#include "device_util.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBK = 64;
+constexpr int kThreads = 256;
+constexpr int kWMW = 4;   // M tiles per window (share one weight panel)
+
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Block-wide: map flattened M tile `mt` to (group, first row, rows).  Returns
+// false if mt is past the last real tile.
+template <int BM>
+__device__ bool locate_tile(const GemmGroup& g, int mt, int* grp, int* row0, int* nrows) {
+    if (g.offsets == nullptr) {
+        const int r0 = mt * BM;
+        if (r0 >= g.M) return false;
+        *grp = 0;
+        *row0 = r0;
+        *nrows = min(BM, g.M - r0);
+        return true;
+    }
+    __shared__ int s_wsum[kThreads / 64];
+    __shared__ int s_res[3];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (threadIdx.x == 0) s_res[0] = -1;
+    int nt = 0, cnt = 0, off = 0;
+    const int e = threadIdx.x;
+    if (e < g.G) {
+        off = g.offsets[e];
+        cnt = g.offsets[e + 1] - off;
+        nt = (cnt + BM - 1) / BM;
+    }
+    int v = nt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) s_wsum[w] = v;
+    __syncthreads();
+    int before = 0;
+    for (int q = 0; q < w; ++q) before += s_wsum[q];
+    const int incl = v + before, excl = incl - nt;
+    if (e < g.G && mt >= excl && mt < incl) {
+        s_res[0] = e;
+        s_res[1] = off + (mt - excl) * BM;
+        s_res[2] = min(BM, cnt - (mt - excl) * BM);
+    }
+    __syncthreads();
+    if (s_res[0] < 0) return false;
+    *grp = s_res[0];
+    *row0 = s_res[1];
+    *nrows = s_res[2];
+    return true;
+}
+
+// Logical tile of this workgroup: XCD-contiguous, then windows of kWMW M tiles
+// per N column.
+__device__ __forceinline__ void logical_tile(int tiles_n, int mt_upper, int* mt, int* nt) {
+    const int grid = gridDim.x;              // multiple of 8
+    const int wid = blockIdx.x;
+    const int L = (wid & 7) * (grid >> 3) + (wid >> 3);
+    const int per_win = tiles_n * kWMW;
+    const int win = L / per_win;
+    const int rem = L - win * per_win;
+    const int wm = min(kWMW, mt_upper - win * kWMW);
+    if (wm <= 0) { *mt = mt_upper; *nt = 0; return; }
+    *nt = rem / wm;
+    *mt = win * kWMW + rem % wm;
+}
+
+template <int BM, int BN, bool DUAL>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmGroup g, int tiles_n, int mt_upper) {
+    constexpr int NMAT = DUAL ? 2 : 1;
+    constexpr int WM = BM / 2, WN = BN / 2;       // per-wave tile
+    constexpr int FM = WM / 32, FN = WN / 32;     // 32x32 MFMA blocks per wave
+    constexpr int A_CHUNKS = BM * 8 / kThreads;   // 16-byte chunks per thread per K tile
+    constexpr int B_CHUNKS = BN * 8 / kThreads;
+    static_assert(A_CHUNKS >= 1 && B_CHUNKS >= 1, "tile too small");
+
+    extern __shared__ __align__(16) uint16_t lds[];
+    uint16_t* As = lds;                                 // [2][BM][64]
+    uint16_t* Bs = lds + 2 * BM * kBK;                  // [2][NMAT][BN][64]
+
+    int mt, ntile;
+    logical_tile(tiles_n, mt_upper, &mt, &ntile);
+    if (mt >= mt_upper || ntile >= tiles_n) return;
+    int grp, row0, nrows;
+    if (!locate_tile<BM>(g, mt, &grp, &row0, &nrows)) return;
+    const int n0 = ntile * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int K = g.K;
+    const int KT = K / kBK;
+
+    // global source pointers of this thread's chunks
+    const uint16_t* A = static_cast<const uint16_t*>(g.A);
+    const int kc = tid & 7;
+    const uint16_t* a_src[A_CHUNKS];
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) {
+        int r = (tid >> 3) + i * (kThreads / 8);
+        int rr = min(r, nrows - 1);
+        int src = g.gather ? g.gather[row0 + rr] / g.gather_div : row0 + rr;
+        a_src[i] = A + (int64_t)src * K + kc * 8;
+    }
+    const uint16_t* b_src[NMAT][B_CHUNKS];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+        const uint16_t* B = static_cast<const uint16_t*>(m == 0 ? g.B0 : g.B1);
+        B += (int64_t)grp * g.N * K;
+#pragma unroll
+        for (int i = 0; i < B_CHUNKS; ++i) {
+            int n = (tid >> 3) + i * (kThreads / 8);
+            b_src[m][i] = B + (int64_t)(n0 + n) * K + kc * 8;
+        }
+    }
+
+    uint4 ra[A_CHUNKS], rb[NMAT][B_CHUNKS];
+#define MOE_LOAD_REGS(kt_)                                                                   \
+    do {                                                                                     \
+        _Pragma("unroll") for (int i = 0; i < A_CHUNKS; ++i) ra[i] =                         \
+            *reinterpret_cast<const uint4*>(a_src[i] + (kt_) * kBK);                         \
+        _Pragma("unroll") for (int m = 0; m < NMAT; ++m)                                     \
+            _Pragma("unroll") for (int i = 0; i < B_CHUNKS; ++i) rb[m][i] =                  \
+                *reinterpret_cast<const uint4*>(b_src[m][i] + (kt_) * kBK);                  \
+    } while (0)
+#define MOE_STORE_LDS(buf_)                                                                  \
+    do {                                                                                     \
+        _Pragma("unroll") for (int i = 0; i < A_CHUNKS; ++i) {                               \
+            const int r = (tid >> 3) + i * (kThreads / 8);                                   \
+            *reinterpret_cast<uint4*>(As + (buf_) * BM * kBK + r * kBK + ((kc ^ swz(r)) * 8)) = \
+                ra[i];                                                                       \
+        }                                                                                    \
+        _Pragma("unroll") for (int m = 0; m < NMAT; ++m)                                     \
+            _Pragma("unroll") for (int i = 0; i < B_CHUNKS; ++i) {                           \
+                const int n = (tid >> 3) + i * (kThreads / 8);                               \
+                *reinterpret_cast<uint4*>(Bs + ((buf_) * NMAT + m) * BN * kBK + n * kBK +    \
+                                          ((kc ^ swz(n)) * 8)) = rb[m][i];                   \
+            }                                                                                \
+    } while (0)
+
+    f32x16_t acc[NMAT][FM][FN];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[m][i][j][q] = 0.0f;
+
+    const int half = lane >> 5, r32 = lane & 31;
+    MOE_LOAD_REGS(0);
+    MOE_STORE_LDS(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        // prefetch the next K tile (the last iteration reloads its own tile;
+        // keeping the load unconditional keeps the staging in registers)
+        const int kn = kt + 1 < KT ? kt + 1 : kt;
+        MOE_LOAD_REGS(kn);
+        const uint16_t* Ab = As + cur * BM * kBK;
+        const uint16_t* Bb = Bs + cur * NMAT * BN * kBK;
+#pragma unroll
+        for (int s = 0; s < kBK / 16; ++s) {
+            const int c = 2 * s + half;
+            bf16x8_t af[FM], bfr[NMAT][FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int r = wm * WM + i * 32 + r32;
+                af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(Ab + r * kBK + ((c ^ swz(r)) * 8)));
+            }
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int n = wn * WN + j * 32 + r32;
+                    bfr[m][j] = as_bf16x8(*reinterpret_cast<const uint4*>(
+                        Bb + m * BN * kBK + n * kBK + ((c ^ swz(n)) * 8)));
+                }
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[m][j],
+                                                                               acc[m][i][j], 0, 0, 0);
+        }
+        MOE_STORE_LDS(cur ^ 1);   // unused after the last iteration
+        __syncthreads();
+    }
+
+#undef MOE_LOAD_REGS
+#undef MOE_STORE_LDS
+    // epilogue: D element q of block (i, j): row 8*(q/4) + 4*half + q%4, col r32
+    uint16_t* C = static_cast<uint16_t*>(g.C);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int col = n0 + wn * WN + j * 32 + r32;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int r = wm * WM + i * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
+                if (r < nrows) {
+                    float v = acc[0][i][j][q];
+                    if (DUAL) v = silu_f32(v) * acc[NMAT - 1][i][j][q];
+                    C[(int64_t)(row0 + r) * g.N + col] = f32_to_bf16(v);
+                }
+            }
+        }
+}
+
+// fp32 grouped GEMM: 64x64 tiles, BK 16, 4x4 outputs per thread.
+template <bool DUAL>
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmGroup g, int tiles_n, int mt_upper) {
+    constexpr int BM = 64, BN = 64, BK = 16;
+    constexpr int NMAT = DUAL ? 2 : 1;
+    __shared__ float As[BK][BM + 4];
+    __shared__ float Bs[NMAT][BK][BN + 4];
+    const int mt = blockIdx.x / tiles_n, ntile = blockIdx.x % tiles_n;
+    if (mt >= mt_upper) return;
+    int grp, row0, nrows;
+    if (!locate_tile<BM>(g, mt, &grp, &row0, &nrows)) return;
+    const int n0 = ntile * BN;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const float* A = static_cast<const float*>(g.A);
+    const int K = g.K;
+    // loader: 64 rows x 16 k = 1024 elements, 4 per thread: row = tid/4 , k4 = (tid%4)*4
+    const int lr = tid >> 2, lk = (tid & 3) * 4;
+    const int rr = min(lr, nrows - 1);
+    const int src = g.gather ? g.gather[row0 + rr] / g.gather_div : row0 + rr;
+    const float* a_src = A + (int64_t)src * K + lk;
+    const float* b_src[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+        b_src[m] = static_cast<const float*>(m == 0 ? g.B0 : g.B1) + (int64_t)grp * g.N * K +
+                   (int64_t)(n0 + lr) * K + lk;
+    float acc[NMAT][4][4] = {};
+    for (int k0 = 0; k0 < K; k0 += BK) {
+        float4 av = *reinterpret_cast<const float4*>(a_src + k0);
+        As[lk + 0][lr] = av.x; As[lk + 1][lr] = av.y; As[lk + 2][lr] = av.z; As[lk + 3][lr] = av.w;
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+            float4 bv = *reinterpret_cast<const float4*>(b_src[m] + k0);
+            Bs[m][lk + 0][lr] = bv.x; Bs[m][lk + 1][lr] = bv.y;
+            Bs[m][lk + 2][lr] = bv.z; Bs[m][lk + 3][lr] = bv.w;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < BK; ++kk) {
+            float a[4], b[NMAT][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) b[m][j] = Bs[m][kk][tx * 4 + j];
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[m][i][j] = fmaf(a[i], b[m][j], acc[m][i][j]);
+        }
+        __syncthreads();
+    }
+    float* C = static_cast<float*>(g.C);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = ty * 4 + i;
+        if (r >= nrows) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float v = acc[0][i][j];
+            if (DUAL) v = silu_f32(v) * acc[NMAT - 1][i][j];
+            C[(int64_t)(row0 + r) * g.N + n0 + tx * 4 + j] = v;
+        }
+    }
+}
+
+template <int BM, int BN, bool DUAL>
+hipError_t launch_bf16(const GemmGroup& g, hipStream_t s) {
+    const int tiles_n = g.N / BN;
+    const int64_t mtu = g.offsets ? grouped_m_tiles_upper(g.M, g.G, BM) : (g.M + BM - 1) / BM;
+    if (mtu == 0) return hipSuccess;
+    int64_t nwg = mtu * tiles_n;
+    nwg = (nwg + 7) / 8 * 8;
+    constexpr int NMAT = DUAL ? 2 : 1;
+    const size_t lds = (size_t)2 * (BM + NMAT * BN) * kBK * sizeof(uint16_t);
+    auto kern = gemm_bf16_kernel<BM, BN, DUAL>;
+    static bool attr_set = false;   // same value on every device; set once per process
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(kThreads), lds, s, g, tiles_n, (int)mtu);
+    return hipGetLastError();
+}
+
+template <bool DUAL>
+hipError_t launch_f32(const GemmGroup& g, hipStream_t s) {
+    const int tiles_n = g.N / 64;
+    const int64_t mtu = g.offsets ? grouped_m_tiles_upper(g.M, g.G, 64) : (g.M + 63) / 64;
+    if (mtu == 0) return hipSuccess;
+    hipLaunchKernelGGL(gemm_f32_kernel<DUAL>, dim3((unsigned)(mtu * tiles_n)), dim3(kThreads), 0, s,
+                       g, tiles_n, (int)mtu);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t grouped_m_tiles_upper(int64_t rows, int G, int bm) {
+    // sum_e ceil(n_e / bm) <= floor((sum_e n_e + G*(bm-1)) / bm)
+    return (rows + (int64_t)G * (bm - 1)) / bm;
+}
+
+hipError_t launch_grouped_gemm(const GemmGroup& g, bool dual, bool bf16, hipStream_t s) {
+    if (g.M == 0) return hipSuccess;
+    if (!bf16) return dual ? launch_f32<true>(g, s) : launch_f32<false>(g, s);
+    if (g.N % 128 == 0) return dual ? launch_bf16<128, 128, true>(g, s) : launch_bf16<128, 128, false>(g, s);
+    return dual ? launch_bf16<128, 64, true>(g, s) : launch_bf16<128, 64, false>(g, s);
+}
+
+}  // namespace moe

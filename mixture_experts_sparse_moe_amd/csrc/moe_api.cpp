@@ -1,0 +1,315 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace layout and the launch sequence.  Everything is validated before
+// the first launch; nothing here synchronises or copies to the host.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int validate_cfg(const moe_config* c) {
+    if (!c) return MOE_ERR_NULL;
+    if (c->num_tokens < 0 || c->d_model <= 0 || c->num_experts <= 0 || c->top_k <= 0 ||
+        c->d_ff <= 0)
+        return MOE_ERR_SHAPE;
+    if (c->num_shared < 0 || c->num_shared > 1) return MOE_ERR_SHAPE;
+    if (c->num_shared == 1 && c->d_ff_shared <= 0) return MOE_ERR_SHAPE;
+    if (c->top_k > c->num_experts) return MOE_ERR_SHAPE;
+    if (c->num_experts > 256 || c->top_k > 16) return MOE_ERR_UNSUPPORTED;
+    if (c->d_model % 64 || c->d_ff % 64 || (c->num_shared && c->d_ff_shared % 64))
+        return MOE_ERR_UNSUPPORTED;
+    if (c->score_fn != MOE_SCORE_SOFTMAX && c->score_fn != MOE_SCORE_SIGMOID)
+        return MOE_ERR_UNSUPPORTED;
+    if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_UNSUPPORTED;
+    if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)c->num_tokens * c->top_k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+size_t elem(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
+
+// Device workspace layout.  Every region starts on a 256-byte boundary.
+struct Layout {
+    size_t ids, wts, counts, offsets, chunk, sorted, pos, H, O, Hs, S, total;
+    size_t dispatch_need, ffn_need;   // bytes used by moe_dispatch / moe_expert_ffn (from 0)
+};
+
+Layout layout(const moe_config* c) {
+    const size_t T = (size_t)c->num_tokens, P = T * c->top_k, E = c->num_experts;
+    const size_t nchunks = (size_t)dispatch_num_chunks((int)P);
+    Layout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+    // moe_expert_ffn's scratch first, so it can start at offset 0
+    L.H = take(P * c->d_ff * elem(c));
+    L.Hs = take(c->num_shared ? T * c->d_ff_shared * elem(c) : 0);
+    L.ffn_need = o;
+    L.chunk = take(nchunks * E * sizeof(int32_t));
+    L.ids = take(P * sizeof(int32_t));
+    L.wts = take(P * sizeof(float));
+    L.counts = take(E * sizeof(int32_t));
+    L.offsets = take((E + 1) * sizeof(int32_t));
+    L.sorted = take(P * sizeof(int32_t));
+    L.pos = take(P * sizeof(int32_t));
+    L.O = take(P * c->d_model * elem(c));
+    L.S = take(c->num_shared ? T * c->d_model * elem(c) : 0);
+    L.total = o;
+    L.dispatch_need = align_up(nchunks * E * sizeof(int32_t));
+    return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+// A tensor pointer must be non-null unless its size is zero, and 16-byte aligned.
+int check_ptr(const void* p, bool empty_ok) {
+    if (!p) return empty_ok ? MOE_OK : MOE_ERR_NULL;
+    return misaligned(p) ? MOE_ERR_ALIGN : MOE_OK;
+}
+
+#define MOE_TRY(expr)                  \
+    do {                               \
+        int rc_ = (expr);              \
+        if (rc_ != MOE_OK) return rc_; \
+    } while (0)
+
+#define MOE_HIP(expr)                                  \
+    do {                                               \
+        if ((expr) != hipSuccess) return MOE_ERR_HIP;  \
+    } while (0)
+
+int run_route(const moe_config* c, const void* x, const void* w_router, int32_t* ids, float* wts,
+              float* gap, hipStream_t s) {
+    RouteArgs a{x, w_router, ids, wts, gap, c->num_tokens, c->d_model, c->num_experts,
+                c->top_k, c->score_fn, c->renormalize};
+    MOE_HIP(launch_route(a, c->dtype == MOE_BF16, s));
+    return MOE_OK;
+}
+
+int run_dispatch(const moe_config* c, const int32_t* ids, int32_t* counts, int32_t* offsets,
+                 int32_t* sorted, int32_t* pos, int32_t* chunk, hipStream_t s) {
+    DispatchArgs a{ids, counts, offsets, sorted, pos, chunk, c->num_tokens * c->top_k,
+                   c->num_experts};
+    MOE_HIP(launch_dispatch(a, s));
+    return MOE_OK;
+}
+
+// Record stage event i if events were given.
+int mark(void* const* ev, int i, hipStream_t s) {
+    if (ev && ev[i]) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(ev[i]), s));
+    return MOE_OK;
+}
+
+int run_ffn(const moe_config* c, const void* x, const int32_t* sorted, const int32_t* offsets,
+            const void* wg, const void* wu, const void* wd, const void* sg, const void* su,
+            const void* sd, void* out, void* shared_out, void* H, void* Hs, hipStream_t s,
+            void* const* ev = nullptr) {
+    const bool bf16 = c->dtype == MOE_BF16;
+    const int P = c->num_tokens * c->top_k;
+    if (P > 0) {
+        GemmGroup up{x, sorted, c->top_k, offsets, c->num_experts, P, wg, wu, H, c->d_ff,
+                     c->d_model};
+        MOE_HIP(launch_grouped_gemm(up, true, bf16, s));
+        MOE_TRY(mark(ev, 2, s));
+        GemmGroup down{H, nullptr, 1, offsets, c->num_experts, P, wd, nullptr, out, c->d_model,
+                       c->d_ff};
+        MOE_HIP(launch_grouped_gemm(down, false, bf16, s));
+        MOE_TRY(mark(ev, 3, s));
+    }
+    if (c->num_shared && c->num_tokens > 0) {
+        GemmGroup up{x, nullptr, 1, nullptr, 1, c->num_tokens, sg, su, Hs, c->d_ff_shared,
+                     c->d_model};
+        MOE_HIP(launch_grouped_gemm(up, true, bf16, s));
+        MOE_TRY(mark(ev, 4, s));
+        GemmGroup down{Hs, nullptr, 1, nullptr, 1, c->num_tokens, sd, nullptr, shared_out,
+                       c->d_model, c->d_ff_shared};
+        MOE_HIP(launch_grouped_gemm(down, false, bf16, s));
+        MOE_TRY(mark(ev, 5, s));
+    } else {
+        MOE_TRY(mark(ev, 4, s));
+        MOE_TRY(mark(ev, 5, s));
+    }
+    return MOE_OK;
+}
+
+int run_combine(const moe_config* c, const void* out, const float* wts, const int32_t* pos,
+                const void* shared_out, void* y, hipStream_t s) {
+    CombineArgs a{out, wts, pos, shared_out, y, c->num_tokens, c->d_model, c->top_k};
+    MOE_HIP(launch_combine(a, c->dtype == MOE_BF16, s));
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_config* cfg) {
+    if (validate_cfg(cfg) != MOE_OK) return 0;
+    return layout(cfg).total;
+}
+
+const char* moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: a size is out of range or inconsistent";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: outside the supported limits";
+        case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a pointer is not 16-byte aligned";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+        default: return "unknown moe_status";
+    }
+}
+
+int moe_route(const moe_config* cfg, const void* x, const void* w_router, int32_t* topk_ids,
+              float* topk_weights, float* topk_gap, void* stream) {
+    MOE_TRY(validate_cfg(cfg));
+    const bool empty = cfg->num_tokens == 0;
+    MOE_TRY(check_ptr(x, empty));
+    MOE_TRY(check_ptr(w_router, false));
+    MOE_TRY(check_ptr(topk_ids, empty));
+    MOE_TRY(check_ptr(topk_weights, empty));
+    if (topk_gap) MOE_TRY(check_ptr(topk_gap, true));
+    if (empty) return MOE_OK;
+    return run_route(cfg, x, w_router, topk_ids, topk_weights, topk_gap,
+                     static_cast<hipStream_t>(stream));
+}
+
+int moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t* expert_counts,
+                 int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos, void* ws,
+                 size_t ws_bytes, void* stream) {
+    MOE_TRY(validate_cfg(cfg));
+    const bool empty = cfg->num_tokens == 0;
+    MOE_TRY(check_ptr(topk_ids, empty));
+    MOE_TRY(check_ptr(expert_counts, false));
+    MOE_TRY(check_ptr(expert_offsets, false));
+    MOE_TRY(check_ptr(sorted_pairs, empty));
+    MOE_TRY(check_ptr(pair_pos, empty));
+    const Layout L = layout(cfg);
+    if (L.dispatch_need > 0) {
+        if (!ws || ws_bytes < L.dispatch_need) return MOE_ERR_WORKSPACE;
+        MOE_TRY(check_ptr(ws, false));
+    }
+    return run_dispatch(cfg, topk_ids, expert_counts, expert_offsets, sorted_pairs, pair_pos,
+                        static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream));
+}
+
+int moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* sorted_pairs,
+                   const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                   const void* w_down, const void* ws_gate, const void* ws_up,
+                   const void* ws_down, void* expert_out, void* shared_out, void* ws,
+                   size_t ws_bytes, void* stream) {
+    MOE_TRY(validate_cfg(cfg));
+    const bool empty = cfg->num_tokens == 0;
+    MOE_TRY(check_ptr(x, empty));
+    MOE_TRY(check_ptr(sorted_pairs, empty));
+    MOE_TRY(check_ptr(expert_offsets, false));
+    MOE_TRY(check_ptr(w_gate, false));
+    MOE_TRY(check_ptr(w_up, false));
+    MOE_TRY(check_ptr(w_down, false));
+    MOE_TRY(check_ptr(expert_out, empty));
+    if (cfg->num_shared) {
+        MOE_TRY(check_ptr(ws_gate, false));
+        MOE_TRY(check_ptr(ws_up, false));
+        MOE_TRY(check_ptr(ws_down, false));
+        MOE_TRY(check_ptr(shared_out, empty));
+    }
+    const Layout L = layout(cfg);
+    if (L.ffn_need > 0) {
+        if (!ws || ws_bytes < L.ffn_need) return MOE_ERR_WORKSPACE;
+        MOE_TRY(check_ptr(ws, false));
+    }
+    if (empty) return MOE_OK;
+    return run_ffn(cfg, x, sorted_pairs, expert_offsets, w_gate, w_up, w_down, ws_gate, ws_up,
+                   ws_down, expert_out, shared_out, at<void>(ws, L.H), at<void>(ws, L.Hs),
+                   static_cast<hipStream_t>(stream));
+}
+
+int moe_combine(const moe_config* cfg, const void* expert_out, const float* topk_weights,
+                const int32_t* pair_pos, const void* shared_out, void* y, void* stream) {
+    MOE_TRY(validate_cfg(cfg));
+    const bool empty = cfg->num_tokens == 0;
+    MOE_TRY(check_ptr(expert_out, empty));
+    MOE_TRY(check_ptr(topk_weights, empty));
+    MOE_TRY(check_ptr(pair_pos, empty));
+    MOE_TRY(check_ptr(y, empty));
+    if (cfg->num_shared) MOE_TRY(check_ptr(shared_out, empty));
+    if (empty) return MOE_OK;
+    return run_combine(cfg, expert_out, topk_weights, pair_pos,
+                       cfg->num_shared ? shared_out : nullptr, y, static_cast<hipStream_t>(stream));
+}
+
+int moe_forward_staged(const moe_config* cfg, const void* x, const void* w_router,
+                       const void* w_gate, const void* w_up, const void* w_down,
+                       const void* ws_gate, const void* ws_up, const void* ws_down, void* y,
+                       int32_t* topk_ids_out, float* topk_weights_out,
+                       int32_t* expert_counts_out, void* ws, size_t ws_bytes, void* start_event,
+                       void* const* ev, void* stream) {
+    MOE_TRY(validate_cfg(cfg));
+    const bool empty = cfg->num_tokens == 0;
+    MOE_TRY(check_ptr(x, empty));
+    MOE_TRY(check_ptr(w_router, false));
+    MOE_TRY(check_ptr(w_gate, false));
+    MOE_TRY(check_ptr(w_up, false));
+    MOE_TRY(check_ptr(w_down, false));
+    if (cfg->num_shared) {
+        MOE_TRY(check_ptr(ws_gate, false));
+        MOE_TRY(check_ptr(ws_up, false));
+        MOE_TRY(check_ptr(ws_down, false));
+    }
+    MOE_TRY(check_ptr(y, empty));
+    if (topk_ids_out) MOE_TRY(check_ptr(topk_ids_out, true));
+    if (topk_weights_out) MOE_TRY(check_ptr(topk_weights_out, true));
+    if (expert_counts_out) MOE_TRY(check_ptr(expert_counts_out, true));
+    const Layout L = layout(cfg);
+    if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    MOE_TRY(check_ptr(ws, false));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+    float* wts = topk_weights_out ? topk_weights_out : at<float>(ws, L.wts);
+    int32_t* counts = expert_counts_out ? expert_counts_out : at<int32_t>(ws, L.counts);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    int32_t* sorted = at<int32_t>(ws, L.sorted);
+    int32_t* pos = at<int32_t>(ws, L.pos);
+    if (start_event) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(start_event), s));
+    if (empty) {
+        // routing outputs are empty; expert counts are all zero
+        MOE_TRY(mark(ev, 0, s));
+        MOE_TRY(run_dispatch(cfg, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s));
+        for (int i = 1; i < MOE_NUM_STAGES; ++i) MOE_TRY(mark(ev, i, s));
+        return MOE_OK;
+    }
+    MOE_TRY(run_route(cfg, x, w_router, ids, wts, nullptr, s));
+    MOE_TRY(mark(ev, 0, s));
+    MOE_TRY(run_dispatch(cfg, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s));
+    MOE_TRY(mark(ev, 1, s));
+    void* O = at<void>(ws, L.O);
+    void* S = cfg->num_shared ? at<void>(ws, L.S) : nullptr;
+    MOE_TRY(run_ffn(cfg, x, sorted, offsets, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, O, S,
+                    at<void>(ws, L.H), at<void>(ws, L.Hs), s, ev));
+    MOE_TRY(run_combine(cfg, O, wts, pos, S, y, s));
+    return mark(ev, 6, s);
+}
+
+int moe_forward(const moe_config* cfg, const void* x, const void* w_router, const void* w_gate,
+                const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,
+                const void* ws_down, void* y, int32_t* topk_ids_out, float* topk_weights_out,
+                int32_t* expert_counts_out, void* ws, size_t ws_bytes, void* stream) {
+    return moe_forward_staged(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
+                              topk_ids_out, topk_weights_out, expert_counts_out, ws, ws_bytes,
+                              nullptr, nullptr, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Internal declarations shared by the HIP kernels and the C-ABI host code.
+// gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+using bf16_t = uint16_t;  // bf16 storage: upper half of an IEEE fp32
+
+// ---- router + top-k ---------------------------------------------------------
+struct RouteArgs {
+    const void* x;          // [T, d]
+    const void* w;          // [E, d]
+    int32_t* ids;           // [T, k]
+    float* weights;         // [T, k]
+    float* gap;             // [T] or nullptr
+    int T, d, E, k;
+    int score_fn;           // 0 softmax, 1 sigmoid
+    int renorm;
+};
+hipError_t launch_route(const RouteArgs& a, bool bf16, hipStream_t s);
+
+// ---- dispatch: histogram, scan, stable scatter ------------------------------
+constexpr int kDispatchChunk = 2048;   // pairs per chunk (one workgroup each)
+struct DispatchArgs {
+    const int32_t* ids;     // [P]
+    int32_t* counts;        // [E]
+    int32_t* offsets;       // [E+1]
+    int32_t* sorted_pairs;  // [P]
+    int32_t* pair_pos;      // [P]
+    int32_t* chunk_counts;  // [nchunks, E] scratch
+    int P, E;
+};
+int dispatch_num_chunks(int P);
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+
+// ---- grouped GEMMs ----------------------------------------------------------
+// One "problem group" of the grouped GEMM: rows of A (optionally gathered)
+// times per-group weight matrices.  Row r of group g spans
+// [offsets[g], offsets[g+1]) (or [0, M) when offsets == nullptr).
+struct GemmGroup {
+    const void* A;          // activation source [*, K]
+    const int32_t* gather;  // grouped row -> pair id (nullptr: identity rows)
+    int gather_div;         // source row = pair id / gather_div
+    const int32_t* offsets; // [G+1] or nullptr
+    int G;                  // number of groups (experts)
+    int M;                  // rows when offsets == nullptr; upper bound otherwise
+    const void* B0;         // [G, N, K]   (gate weights, or down weights)
+    const void* B1;         // [G, N, K]   (up weights; dual mode only)
+    void* C;                // [rows, N]
+    int N, K;
+};
+// Dual mode: C = silu(A B0^T) * (A B1^T).  Single: C = A B0^T.
+hipError_t launch_grouped_gemm(const GemmGroup& g, bool dual, bool bf16, hipStream_t s);
+// Upper bound of M-tiles over all groups for tile height bm.
+int64_t grouped_m_tiles_upper(int64_t rows, int G, int bm);
+
+// ---- combine ------------------------------------------------------------------
+struct CombineArgs {
+    const void* expert_out; // [P, d]
+    const float* weights;   // [T, k]
+    const int32_t* pair_pos;// [P]
+    const void* shared;     // [T, d] or nullptr
+    void* y;                // [T, d]
+    int T, d, k;
+};
+hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t s);
+
+}  // namespace moe

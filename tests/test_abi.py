@@ -1,0 +1,138 @@
+"""The C-ABI library on the host: it loads, exports every declared entry point,
+and its validator rejects bad arguments with the documented status codes
+before anything is enqueued (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_sparse_moe_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.LIB_PATH), reason="libmoe.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTS), names
+    L = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+
+
+def test_library_links_no_oracle_or_torch():
+    """The product library depends on the HIP runtime only."""
+    import subprocess
+    out = subprocess.run(["ldd", moe.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oracle" not in out and "torch" not in out and "libsynth" not in out
+    assert "amdhip64" in out
+
+
+def cfg(**kw):
+    base = dict(T=64, d=128, E=8, k=2, d_ff=256)
+    base.update(kw)
+    return moe.MoeConfig.of(base["T"], base["d"], base["E"], base["k"], base["d_ff"],
+                            num_shared=kw.get("num_shared", 0), d_ff_shared=kw.get("d_ff_shared", 0),
+                            score_fn=kw.get("score_fn", 0), renormalize=kw.get("renormalize", 1),
+                            dtype=kw.get("dtype", moe.MOE_BF16))
+
+
+FAKE = 0x10000   # an aligned, never-dereferenced address: validation fails first
+
+
+def route(c, x=FAKE, w=FAKE, ids=FAKE, wts=FAKE, gap=None):
+    return moe.lib().moe_route(ctypes.byref(c) if c is not None else None, x, w, ids, wts, gap, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), moe.MOE_ERR_SHAPE),
+    (dict(d=0), moe.MOE_ERR_SHAPE),
+    (dict(E=0), moe.MOE_ERR_SHAPE),
+    (dict(k=0), moe.MOE_ERR_SHAPE),
+    (dict(k=9), moe.MOE_ERR_SHAPE),                 # k > E
+    (dict(d_ff=0), moe.MOE_ERR_SHAPE),
+    (dict(num_shared=2, d_ff_shared=64), moe.MOE_ERR_SHAPE),
+    (dict(num_shared=1, d_ff_shared=0), moe.MOE_ERR_SHAPE),
+    (dict(E=257, k=2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(E=32, k=17), moe.MOE_ERR_UNSUPPORTED),
+    (dict(d=96), moe.MOE_ERR_UNSUPPORTED),
+    (dict(d_ff=100), moe.MOE_ERR_UNSUPPORTED),
+    (dict(num_shared=1, d_ff_shared=96), moe.MOE_ERR_UNSUPPORTED),
+    (dict(score_fn=2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(renormalize=3), moe.MOE_ERR_UNSUPPORTED),
+    (dict(dtype=5), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=2**28, k=8), moe.MOE_ERR_UNSUPPORTED),  # T*k >= 2^31
+])
+def test_config_validation(kw, status):
+    c = cfg(**kw)
+    assert route(c) == status
+    assert moe.moe_workspace_bytes(c) == 0
+    L = moe.lib()
+    assert L.moe_forward(ctypes.byref(c), *([FAKE] * 13), FAKE, 1 << 40, None) == status
+    assert L.moe_dispatch(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == status
+    assert L.moe_combine(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
+
+
+def test_null_and_alignment():
+    c = cfg()
+    L = moe.lib()
+    assert L.moe_route(None, FAKE, FAKE, FAKE, FAKE, None, None) == moe.MOE_ERR_NULL
+    assert route(c, x=None) == moe.MOE_ERR_NULL
+    assert route(c, w=None) == moe.MOE_ERR_NULL
+    assert route(c, ids=None) == moe.MOE_ERR_NULL
+    assert route(c, x=FAKE + 2) == moe.MOE_ERR_ALIGN
+    assert route(c, wts=FAKE + 8) == moe.MOE_ERR_ALIGN
+    assert route(c, gap=FAKE + 4) == moe.MOE_ERR_ALIGN
+    # shared expert weights are required only when num_shared == 1
+    cs = cfg(num_shared=1, d_ff_shared=128)
+    ffn = lambda c_, sg: L.moe_expert_ffn(ctypes.byref(c_), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, sg,
+                                          FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert ffn(cs, None) == moe.MOE_ERR_NULL
+
+
+def test_workspace_checks():
+    c = cfg()
+    L = moe.lib()
+    need = moe.moe_workspace_bytes(c)
+    assert need > 0 and need % 256 == 0
+    args = [FAKE] * 13
+    assert L.moe_forward(ctypes.byref(c), *args, None, need, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_forward(ctypes.byref(c), *args, FAKE, need - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_dispatch(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_expert_ffn(ctypes.byref(c), *([FAKE] * 11), None, 0, None) == moe.MOE_ERR_WORKSPACE
+
+
+def test_workspace_size_covers_intermediates():
+    """The workspace holds at least the [T*k, d_ff] intermediate, the [T*k, d]
+    expert outputs and the routing tables; the shared expert adds its own."""
+    for dtype, eb in ((moe.MOE_BF16, 2), (moe.MOE_F32, 4)):
+        c = cfg(T=1000, d=256, E=64, k=8, d_ff=512, dtype=dtype)
+        P = 1000 * 8
+        need = moe.moe_workspace_bytes(c)
+        assert need >= P * 512 * eb + P * 256 * eb + 4 * P * 4
+        cs = cfg(T=1000, d=256, E=64, k=8, d_ff=512, dtype=dtype, num_shared=1, d_ff_shared=384)
+        assert moe.moe_workspace_bytes(cs) >= need + 1000 * 384 * eb + 1000 * 256 * eb
+
+
+def test_empty_token_batch_is_a_noop():
+    c = cfg(T=0)
+    L = moe.lib()
+    assert L.moe_route(ctypes.byref(c), None, FAKE, None, None, None, None) == moe.MOE_OK
+    assert L.moe_combine(ctypes.byref(c), None, None, None, None, None, None) == moe.MOE_OK
+    assert L.moe_expert_ffn(ctypes.byref(c), None, None, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                            None, None, None, 0, None) == moe.MOE_OK
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert moe.moe_status_str(s).startswith("MOE_")
+    assert "unknown" in moe.moe_status_str(42)
