@@ -76,9 +76,9 @@ def lib():
         L.moe_expert_ffn.restype = i32
         L.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
         L.moe_combine.restype = i32
-        L.moe_forward.argtypes = [cfgp] + [vp] * 13 + [vp, sz, vp]
+        L.moe_forward.argtypes = [cfgp] + [vp] * 12 + [vp, sz, vp]
         L.moe_forward.restype = i32
-        L.moe_forward_staged.argtypes = [cfgp] + [vp] * 13 + [vp, sz, vp, vp, vp]
+        L.moe_forward_staged.argtypes = [cfgp] + [vp] * 12 + [vp, sz, vp, vp, vp]
         L.moe_forward_staged.restype = i32
         _lib = L
     return _lib

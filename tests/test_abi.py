@@ -29,6 +29,23 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(L, n), f"{n} not exported"
 
 
+def declared_param_counts():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(moe_[a-z_]+)\s*\(([^;{]*?)\)\s*;", src):
+        params = [p for p in m.group(2).split(",") if p.strip() and p.strip() != "void"]
+        out[m.group(1)] = len(params)
+    return out
+
+
+def test_binding_argument_counts_match_header():
+    counts = declared_param_counts()
+    L = moe.lib()
+    for n in moe.EXPORTS:
+        assert len(getattr(L, n).argtypes) == counts[n], n
+
+
 def test_library_links_no_oracle_or_torch():
     """The product library depends on the HIP runtime only."""
     import subprocess
@@ -77,7 +94,7 @@ def test_config_validation(kw, status):
     assert route(c) == status
     assert moe.moe_workspace_bytes(c) == 0
     L = moe.lib()
-    assert L.moe_forward(ctypes.byref(c), *([FAKE] * 13), FAKE, 1 << 40, None) == status
+    assert L.moe_forward(ctypes.byref(c), *([FAKE] * 12), FAKE, 1 << 40, None) == status
     assert L.moe_dispatch(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == status
     assert L.moe_combine(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
 
@@ -104,9 +121,10 @@ def test_workspace_checks():
     L = moe.lib()
     need = moe.moe_workspace_bytes(c)
     assert need > 0 and need % 256 == 0
-    args = [FAKE] * 13
+    args = [FAKE] * 12
     assert L.moe_forward(ctypes.byref(c), *args, None, need, None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_forward(ctypes.byref(c), *args, FAKE, need - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_forward_staged(ctypes.byref(c), *args, FAKE, need - 1, None, None, None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_dispatch(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_expert_ffn(ctypes.byref(c), *([FAKE] * 11), None, 0, None) == moe.MOE_ERR_WORKSPACE
 
