@@ -248,6 +248,143 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmGroup g, int ti
         }
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Main bf16 kernel: 256 x 256 tile of MFMA work per workgroup.
+//   single: C tile 256 rows x 256 cols of one weight matrix;
+//   dual:   C tile 256 rows x 128 cols, computed for the gate and the up
+//           matrix (B rows 0..127 = gate, 128..255 = up, same columns).
+// 4 waves in 2 x 2; each wave owns 128 rows x 4 blocks of 32 B-rows, i.e.
+// 4 x 4 MFMA 32x32 blocks = 256 fp32 accumulators (AGPRs).
+// Global -> LDS by direct 16-byte DMA (global_load_lds_dwordx4): lane i of
+// an instruction fills bytes [16 i, 16 i + 16) of a 1 KB block = 8 LDS rows,
+// so each lane fetches the global chunk that the XOR swizzle places there.
+// Two LDS buffers (separate arrays, so the compiler sees the DMA into one
+// does not alias the fragment reads of the other); the next K tile's DMA is
+// in flight during the current tile's 64 MFMAs per wave.
+template <bool DUAL>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(GemmGroup g, int tiles_n,
+                                                                    int mt_upper) {
+    constexpr int BM = 256;
+    constexpr int BN = DUAL ? 128 : 256;
+    __shared__ __align__(16) uint16_t sA0[BM * kBK];
+    __shared__ __align__(16) uint16_t sA1[BM * kBK];
+    __shared__ __align__(16) uint16_t sB0[256 * kBK];
+    __shared__ __align__(16) uint16_t sB1[256 * kBK];
+
+    int mt, ntile;
+    logical_tile(tiles_n, mt_upper, &mt, &ntile);
+    if (mt >= mt_upper || ntile >= tiles_n) return;
+    int grp, row0, nrows;
+    if (!locate_tile<BM>(g, mt, &grp, &row0, &nrows)) return;
+    const int n0 = ntile * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int K = g.K;
+    const int KT = K / kBK;
+
+    // DMA sources: instruction j of wave w fills LDS rows 64 w + 8 j + lane / 8
+    // at physical chunk lane % 8, which holds logical chunk (lane % 8) ^ swz(row).
+    // Addresses are a wave-uniform base plus a 32-bit per-lane byte offset.
+    const char* a_base = static_cast<const char*>(g.A);
+    // B rows 64 w .. 64 w + 63: dual -> gate (w < 2) or up (w >= 2) matrix, column
+    // n0 + row % 128; single -> column n0 + row.
+    const char* b_base = static_cast<const char*>(DUAL ? (w < 2 ? g.B0 : g.B1) : g.B0) +
+                         ((int64_t)grp * g.N + n0) * K * 2;
+    uint32_t a_off[8], b_off[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int r = w * 64 + j * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
+        const int rr = min(r, nrows - 1);
+        const int src = g.gather ? g.gather[row0 + rr] / g.gather_div : row0 + rr;
+        a_off[j] = (uint32_t)src * (uint32_t)(K * 2) + c * 16;
+        b_off[j] = (uint32_t)(DUAL ? (r & 127) : r) * (uint32_t)(K * 2) + c * 16;
+    }
+
+#define MOE_DMA(sA_, sB_, kt_)                                                                  \
+    do {                                                                                        \
+        const char* ab_ = a_base + (kt_) * (kBK * 2);                                           \
+        const char* bb_ = b_base + (kt_) * (kBK * 2);                                           \
+        _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                         \
+            __builtin_amdgcn_global_load_lds(ab_ + a_off[j],                                    \
+                                             (lds_ptr_t)((sA_) + (w * 64 + j * 8) * kBK), 16, 0, 0); \
+            __builtin_amdgcn_global_load_lds(bb_ + b_off[j],                                    \
+                                             (lds_ptr_t)((sB_) + (w * 64 + j * 8) * kBK), 16, 0, 0); \
+        }                                                                                       \
+    } while (0)
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    const int half = lane >> 5, r32 = lane & 31;
+    // LDS element offsets of this lane's fragment rows (chunk added per step)
+    int a_row[4], b_row[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a_row[i] = wm * 128 + i * 32 + r32;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        b_row[b] = DUAL ? (b >> 1) * 128 + wn * 64 + (b & 1) * 32 + r32 : wn * 128 + b * 32 + r32;
+
+#define MOE_COMPUTE(sA_, sB_)                                                                   \
+    do {                                                                                        \
+        _Pragma("unroll") for (int s = 0; s < kBK / 16; ++s) {                                  \
+            const int c = 2 * s + half;                                                         \
+            bf16x8_t af[4], bfr[4];                                                             \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) af[i] = as_bf16x8(                    \
+                *reinterpret_cast<const uint4*>((sA_) + a_row[i] * kBK + ((c ^ swz(a_row[i])) * 8))); \
+            _Pragma("unroll") for (int b = 0; b < 4; ++b) bfr[b] = as_bf16x8(                   \
+                *reinterpret_cast<const uint4*>((sB_) + b_row[b] * kBK + ((c ^ swz(b_row[b])) * 8))); \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                       \
+                _Pragma("unroll") for (int b = 0; b < 4; ++b) acc[i][b] =                       \
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[b], acc[i][b], 0, 0, 0); \
+        }                                                                                       \
+    } while (0)
+
+    // K tiles in pairs (KT is even): buffer 0 holds even tiles, buffer 1 odd.
+    MOE_DMA(sA0, sB0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int kt = 0; kt < KT; kt += 2) {
+        MOE_DMA(sA1, sB1, kt + 1);
+        MOE_COMPUTE(sA0, sB0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (kt + 2 < KT) MOE_DMA(sA0, sB0, kt + 2);
+        MOE_COMPUTE(sA1, sB1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+#undef MOE_DMA
+#undef MOE_COMPUTE
+
+    // epilogue: D element q of block (i, b): row 8 (q / 4) + 4 half + q % 4, col r32
+    uint16_t* C = static_cast<uint16_t*>(g.C);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int bo = 0; bo < (DUAL ? 2 : 4); ++bo) {
+            const int col = DUAL ? n0 + wn * 64 + bo * 32 + r32 : n0 + wn * 128 + bo * 32 + r32;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int r = wm * 128 + i * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
+                if (r < nrows) {
+                    float v = acc[i][bo][q];
+                    if (DUAL) v = silu_f32(v) * acc[i][bo + 2][q];
+                    C[(int64_t)(row0 + r) * g.N + col] = f32_to_bf16(v);
+                }
+            }
+        }
+    }
+}
+
 // fp32 grouped GEMM: 64x64 tiles, BK 16, 4x4 outputs per thread.
 template <bool DUAL>
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmGroup g, int tiles_n, int mt_upper) {
@@ -338,6 +475,19 @@ hipError_t launch_bf16(const GemmGroup& g, hipStream_t s) {
 }
 
 template <bool DUAL>
+hipError_t launch_bf16_256(const GemmGroup& g, hipStream_t s) {
+    constexpr int BM = 256, BN = DUAL ? 128 : 256;
+    const int tiles_n = g.N / BN;
+    const int64_t mtu = g.offsets ? grouped_m_tiles_upper(g.M, g.G, BM) : (g.M + BM - 1) / BM;
+    if (mtu == 0) return hipSuccess;
+    int64_t nwg = mtu * tiles_n;
+    nwg = (nwg + 7) / 8 * 8;
+    hipLaunchKernelGGL(gemm_bf16_256_kernel<DUAL>, dim3((unsigned)nwg), dim3(kThreads), 0, s, g,
+                       tiles_n, (int)mtu);
+    return hipGetLastError();
+}
+
+template <bool DUAL>
 hipError_t launch_f32(const GemmGroup& g, hipStream_t s) {
     const int tiles_n = g.N / 64;
     const int64_t mtu = g.offsets ? grouped_m_tiles_upper(g.M, g.G, 64) : (g.M + 63) / 64;
@@ -357,6 +507,9 @@ int64_t grouped_m_tiles_upper(int64_t rows, int G, int bm) {
 hipError_t launch_grouped_gemm(const GemmGroup& g, bool dual, bool bf16, hipStream_t s) {
     if (g.M == 0) return hipSuccess;
     if (!bf16) return dual ? launch_f32<true>(g, s) : launch_f32<false>(g, s);
+    // the 256-tile kernel takes K tiles in pairs: K % 128 == 0
+    if (g.K % 128 == 0 && dual && g.N % 128 == 0) return launch_bf16_256<true>(g, s);
+    if (g.K % 128 == 0 && !dual && g.N % 256 == 0) return launch_bf16_256<false>(g, s);
     if (g.N % 128 == 0) return dual ? launch_bf16<128, 128, true>(g, s) : launch_bf16<128, 128, false>(g, s);
     return dual ? launch_bf16<128, 64, true>(g, s) : launch_bf16<128, 64, false>(g, s);
 }
