@@ -25,7 +25,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z), with the hardware reciprocal (about 1 ulp)
+__device__ __forceinline__ float silu_f32(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // Reinterpret 16 bytes as 8 bf16 MFMA operands.
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {

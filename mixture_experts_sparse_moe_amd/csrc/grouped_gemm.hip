@@ -52,7 +52,7 @@ __device__ bool locate_tile(const GemmGroup& g, int mt, int* grp, int* row0, int
         *nrows = min(BM, g.M - r0);
         return true;
     }
-    __shared__ int s_wsum[kThreads / 64];
+    __shared__ int s_wsum[8];      // one slot per wave, up to 512 threads
     __shared__ int s_res[3];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (threadIdx.x == 0) s_res[0] = -1;
@@ -250,82 +250,87 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmGroup g, int ti
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Main bf16 kernel: 256 x 256 tile of MFMA work per workgroup.
+constexpr int kBKs = 32;   // K elements per pipeline stage of the 256 kernel
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]).  The builtin, unlike inline asm, is seen by the
+// compiler's own wait insertion, so it adds no waits of its own after these.
+constexpr int kWaitVm16Lgkm0 = (1 << 14) | (7 << 4) | (0 << 8);   // vmcnt(16) lgkmcnt(0)
+constexpr int kWaitVm0 = (7 << 4) | (15 << 8);                     // vmcnt(0)
+
+// Swizzle of 64-byte LDS rows (4 chunks of 16 B): chunk c of row r sits at
+// c ^ f(r).  32 lanes reading rows r..r+31 at one logical chunk then hit
+// distinct bank groups whether the LDS serves 8 or 16 lanes per cycle.
+__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// Main bf16 kernel, persistent: one workgroup per CU walks a list of
+// 256 x 256 tiles of MFMA work.
 //   single: C tile 256 rows x 256 cols of one weight matrix;
 //   dual:   C tile 256 rows x 128 cols, computed for the gate and the up
 //           matrix (B rows 0..127 = gate, 128..255 = up, same columns).
+// Tile schedule: the real M tiles (ceil(count_e / 256) per expert, prefix sums
+// in LDS) times the N tiles form a list of logical tiles, cut into 8 equal
+// ranges, one per XCD (workgroup ids are dealt to the XCDs round-robin).
+// Inside a range the XCD's workgroups take consecutive tiles in rounds; a
+// round is a window of 4 M tiles x (workgroups / 4) N tiles, so its A and B
+// panels are shared in the XCD's L2 while all its tiles advance through K in
+// step (same work per tile, all resident at once).
 // 4 waves in 2 x 2; each wave owns 128 rows x 4 blocks of 32 B-rows, i.e.
 // 4 x 4 MFMA 32x32 blocks = 256 fp32 accumulators (AGPRs).
 // Global -> LDS by direct 16-byte DMA (global_load_lds_dwordx4): lane i of
-// an instruction fills bytes [16 i, 16 i + 16) of a 1 KB block = 8 LDS rows,
-// so each lane fetches the global chunk that the XOR swizzle places there.
-// Two LDS buffers (separate arrays, so the compiler sees the DMA into one
-// does not alias the fragment reads of the other); the next K tile's DMA is
-// in flight during the current tile's 64 MFMAs per wave.
+// an instruction fills bytes [16 i, 16 i + 16) of a 1 KB block = 16 LDS rows
+// of 32 bf16, so each lane fetches the chunk the swizzle places there.
+// Four LDS stages of 32 K-elements (separate arrays, so the compiler can see
+// that a DMA into one stage does not alias fragment reads of another), DMA
+// issued three stages ahead.  One barrier per stage, in the middle of the
+// stage: after it, the next stage's first fragments are read while the
+// current stage's last MFMAs run.
 template <bool DUAL>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(GemmGroup g, int tiles_n,
-                                                                    int mt_upper) {
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(GemmGroup g, int tiles_n) {
     constexpr int BM = 256;
     constexpr int BN = DUAL ? 128 : 256;
-    __shared__ __align__(16) uint16_t sA0[BM * kBK];
-    __shared__ __align__(16) uint16_t sA1[BM * kBK];
-    __shared__ __align__(16) uint16_t sB0[256 * kBK];
-    __shared__ __align__(16) uint16_t sB1[256 * kBK];
-
-    int mt, ntile;
-    logical_tile(tiles_n, mt_upper, &mt, &ntile);
-    if (mt >= mt_upper || ntile >= tiles_n) return;
-    int grp, row0, nrows;
-    if (!locate_tile<BM>(g, mt, &grp, &row0, &nrows)) return;
-    const int n0 = ntile * BN;
+    constexpr int STG = 256 * kBKs;   // elements of one A or B stage
+    __shared__ __align__(16) uint16_t sA0[STG], sA1[STG], sA2[STG], sA3[STG];
+    __shared__ __align__(16) uint16_t sB0[STG], sB1[STG], sB2[STG], sB3[STG];
+    __shared__ int s_tb[257];          // M tiles before group e; s_tb[G] = all M tiles
+    __shared__ int s_wsum[kThreads / 64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
     const int K = g.K;
-    const int KT = K / kBK;
+    const int KT = K / kBKs;          // multiple of 4
 
-    // DMA sources: instruction j of wave w fills LDS rows 64 w + 8 j + lane / 8
-    // at physical chunk lane % 8, which holds logical chunk (lane % 8) ^ swz(row).
-    // Addresses are a wave-uniform base plus a 32-bit per-lane byte offset.
-    const char* a_base = static_cast<const char*>(g.A);
-    // B rows 64 w .. 64 w + 63: dual -> gate (w < 2) or up (w >= 2) matrix, column
-    // n0 + row % 128; single -> column n0 + row.
-    const char* b_base = static_cast<const char*>(DUAL ? (w < 2 ? g.B0 : g.B1) : g.B0) +
-                         ((int64_t)grp * g.N + n0) * K * 2;
-    uint32_t a_off[8], b_off[8];
+    // ---- M tiles per group: exclusive prefix of ceil(count / BM), in LDS
+    if (g.offsets) {
+        int nt = 0;
+        if (tid < g.G) nt = (g.offsets[tid + 1] - g.offsets[tid] + BM - 1) / BM;
+        int v = nt;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = w * 64 + j * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swz(r);
-        const int rr = min(r, nrows - 1);
-        const int src = g.gather ? g.gather[row0 + rr] / g.gather_div : row0 + rr;
-        a_off[j] = (uint32_t)src * (uint32_t)(K * 2) + c * 16;
-        b_off[j] = (uint32_t)(DUAL ? (r & 127) : r) * (uint32_t)(K * 2) + c * 16;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(v, o, 64);
+            if (lane >= o) v += u;
+        }
+        if (lane == 63) s_wsum[w] = v;
+        __syncthreads();
+        int before = 0;
+        for (int q = 0; q < w; ++q) before += s_wsum[q];
+        if (tid < g.G) s_tb[tid] = v + before - nt;
+        if (tid == g.G - 1) s_tb[g.G] = v + before;     // all M tiles (G <= 256 threads)
+    } else if (tid == 0) {
+        s_tb[0] = 0;
+        s_tb[1] = (g.M + BM - 1) / BM;
     }
-
-#define MOE_DMA(sA_, sB_, kt_)                                                                  \
-    do {                                                                                        \
-        const char* ab_ = a_base + (kt_) * (kBK * 2);                                           \
-        const char* bb_ = b_base + (kt_) * (kBK * 2);                                           \
-        _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                         \
-            __builtin_amdgcn_global_load_lds(ab_ + a_off[j],                                    \
-                                             (lds_ptr_t)((sA_) + (w * 64 + j * 8) * kBK), 16, 0, 0); \
-            __builtin_amdgcn_global_load_lds(bb_ + b_off[j],                                    \
-                                             (lds_ptr_t)((sB_) + (w * 64 + j * 8) * kBK), 16, 0, 0); \
-        }                                                                                       \
-    } while (0)
-
-    f32x16_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    __syncthreads();
+    const int G = g.offsets ? g.G : 1;
+    const int mt_total = s_tb[G];
+    const int TL = mt_total * tiles_n;
+    const int nslot = gridDim.x >> 3;             // workgroups per XCD
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per = (TL + 7) >> 3;
+    const int Lend = min(TL, (xcd + 1) * per);
+    const int wn_win = max(nslot / kWMW, 1);      // N tiles per round window
 
     const int half = lane >> 5, r32 = lane & 31;
-    // LDS element offsets of this lane's fragment rows (chunk added per step)
     int a_row[4], b_row[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) a_row[i] = wm * 128 + i * 32 + r32;
@@ -333,52 +338,158 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(GemmGroup g,
     for (int b = 0; b < 4; ++b)
         b_row[b] = DUAL ? (b >> 1) * 128 + wn * 64 + (b & 1) * 32 + r32 : wn * 128 + b * 32 + r32;
 
-#define MOE_COMPUTE(sA_, sB_)                                                                   \
+    for (int L = xcd * per + slot; L < Lend; L += nslot) {
+        // ---- logical tile -> (M tile, N tile): windows of kWMW M tiles x wn_win
+        // N tiles, N-window-major inside a band of kWMW M tiles
+        const int band = L / (kWMW * tiles_n);
+        const int mb0 = band * kWMW;
+        const int mh = min(kWMW, mt_total - mb0);        // M tiles in this band
+        const int rem = L - band * kWMW * tiles_n;       // < mh * tiles_n
+        const int nwin = rem / (mh * wn_win);
+        const int nw0 = nwin * wn_win;
+        const int nwh = min(wn_win, tiles_n - nw0);      // N tiles in this window
+        const int r2 = rem - nwin * mh * wn_win;
+        const int mt = mb0 + r2 % mh;
+        const int ntile = nw0 + r2 / mh;
+        (void)nwh;
+        // ---- M tile -> group and rows (groups with no tiles are skipped)
+        int lo = 0, hi = G;                               // s_tb[lo] <= mt < s_tb[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_tb[mid] <= mt) lo = mid; else hi = mid;
+        }
+        const int grp = lo;
+        const int base_row = g.offsets ? g.offsets[grp] : 0;
+        const int grp_rows = g.offsets ? g.offsets[grp + 1] - base_row : g.M;
+        const int row0 = base_row + (mt - s_tb[grp]) * BM;
+        const int nrows = min(BM, base_row + grp_rows - row0);
+        const int n0 = ntile * BN;
+
+        // DMA sources: instruction j of wave w fills LDS rows 64 w + 16 j + lane / 4
+        // at physical chunk lane % 4, which holds logical chunk (lane % 4) ^ swz4(row).
+        // Addresses are a wave-uniform base plus a 32-bit per-lane byte offset.
+        const char* a_base = static_cast<const char*>(g.A);
+        // B rows 64 w .. 64 w + 63: dual -> gate (w < 2) or up (w >= 2) matrix,
+        // column n0 + row % 128; single -> column n0 + row.
+        const char* b_base = static_cast<const char*>(DUAL ? (w < 2 ? g.B0 : g.B1) : g.B0) +
+                             ((int64_t)grp * g.N + n0) * K * 2;
+        uint32_t a_off[4], b_off[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = w * 64 + j * 16 + (lane >> 2);
+            const int c = (lane & 3) ^ swz4(r);
+            const int rr = min(r, nrows - 1);
+            const int src = g.gather ? g.gather[row0 + rr] / g.gather_div : row0 + rr;
+            a_off[j] = (uint32_t)src * (uint32_t)(K * 2) + c * 16;
+            b_off[j] = (uint32_t)(DUAL ? (r & 127) : r) * (uint32_t)(K * 2) + c * 16;
+        }
+
+        f32x16_t acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+        bf16x8_t fa0[4], fb0[4], fa1[4], fb1[4];
+
+#define MOE_DMA(sA_, sB_, kt_)                                                                  \
     do {                                                                                        \
-        _Pragma("unroll") for (int s = 0; s < kBK / 16; ++s) {                                  \
-            const int c = 2 * s + half;                                                         \
-            bf16x8_t af[4], bfr[4];                                                             \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i) af[i] = as_bf16x8(                    \
-                *reinterpret_cast<const uint4*>((sA_) + a_row[i] * kBK + ((c ^ swz(a_row[i])) * 8))); \
-            _Pragma("unroll") for (int b = 0; b < 4; ++b) bfr[b] = as_bf16x8(                   \
-                *reinterpret_cast<const uint4*>((sB_) + b_row[b] * kBK + ((c ^ swz(b_row[b])) * 8))); \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                       \
-                _Pragma("unroll") for (int b = 0; b < 4; ++b) acc[i][b] =                       \
-                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[b], acc[i][b], 0, 0, 0); \
+        const char* ab_ = a_base + (kt_) * (kBKs * 2);                                          \
+        const char* bb_ = b_base + (kt_) * (kBKs * 2);                                          \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                         \
+            __builtin_amdgcn_global_load_lds(ab_ + a_off[j],                                    \
+                                             (lds_ptr_t)((sA_) + (w * 64 + j * 16) * kBKs), 16, 0, 0); \
+            __builtin_amdgcn_global_load_lds(bb_ + b_off[j],                                    \
+                                             (lds_ptr_t)((sB_) + (w * 64 + j * 16) * kBKs), 16, 0, 0); \
         }                                                                                       \
     } while (0)
+#define MOE_LOAD_FRAGS(sA_, sB_, s_, af_, bf_)                                                  \
+    do {                                                                                        \
+        const int c_ = 2 * (s_) + half;                                                        \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) af_[i] = as_bf16x8(                       \
+            *reinterpret_cast<const uint4*>((sA_) + a_row[i] * kBKs + ((c_ ^ swz4(a_row[i])) * 8))); \
+        _Pragma("unroll") for (int b = 0; b < 4; ++b) bf_[b] = as_bf16x8(                       \
+            *reinterpret_cast<const uint4*>((sB_) + b_row[b] * kBKs + ((c_ ^ swz4(b_row[b])) * 8))); \
+    } while (0)
+#define MOE_MFMAS(af_, bf_)                                                                     \
+    do {                                                                                        \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
+            _Pragma("unroll") for (int b = 0; b < 4; ++b) acc[i][b] =                           \
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_[i], bf_[b], acc[i][b], 0, 0, 0);    \
+    } while (0)
+// 16 MFMAs with the 8 fragment reads of the following step between the first 8
+#define MOE_INTERLEAVE()                                                                        \
+    do {                                                                                        \
+        _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                      \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                  \
+        }                                                                                       \
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                      \
+    } while (0)
+// Stage kt in buffers (sAc, sBc); next stage in (sAn, sBn); DMA target of
+// stage kt + 3 in (sAp, sBp).  On entry fa0/fb0 hold step 0 of stage kt.
+// Branch-free, so each half is one scheduling region: past the last K tile
+// the DMA re-fetches the last tile into the free buffer (never read), so
+// exactly 8 DMAs are always issued per stage and vmcnt(16) always means
+// "stage kt + 1 has landed"; the fragment prefetch past the end is unused.
+#define MOE_STAGE(sAc, sBc, sAn, sBn, sAp, sBp, kt_)                                            \
+    do {                                                                                        \
+        const int st_ = (kt_);                                                                  \
+        MOE_DMA(sAp, sBp, min(st_ + 3, KT - 1));                                                \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        MOE_LOAD_FRAGS(sAc, sBc, 1, fa1, fb1);                                                  \
+        MOE_MFMAS(fa0, fb0);                                                                    \
+        MOE_INTERLEAVE();                                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        /* stage kt + 1 landed (own DMAs) and this wave's reads of stage kt are done */        \
+        __builtin_amdgcn_s_waitcnt(kWaitVm16Lgkm0);                                             \
+        __builtin_amdgcn_s_barrier();                                                           \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        MOE_LOAD_FRAGS(sAn, sBn, 0, fa0, fb0);                                                  \
+        MOE_MFMAS(fa1, fb1);                                                                    \
+        MOE_INTERLEAVE();                                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+    } while (0)
 
-    // K tiles in pairs (KT is even): buffer 0 holds even tiles, buffer 1 odd.
-    MOE_DMA(sA0, sB0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int kt = 0; kt < KT; kt += 2) {
-        MOE_DMA(sA1, sB1, kt + 1);
-        MOE_COMPUTE(sA0, sB0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // every wave is past its reads of the previous tile's buffers
         __syncthreads();
-        if (kt + 2 < KT) MOE_DMA(sA0, sB0, kt + 2);
-        MOE_COMPUTE(sA1, sB1);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    }
+        MOE_DMA(sA0, sB0, 0);
+        MOE_DMA(sA1, sB1, 1);
+        MOE_DMA(sA2, sB2, 2);
+        __builtin_amdgcn_s_waitcnt(kWaitVm16Lgkm0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        MOE_LOAD_FRAGS(sA0, sB0, 0, fa0, fb0);
+        for (int kt = 0; kt < KT; kt += 4) {
+            MOE_STAGE(sA0, sB0, sA1, sB1, sA3, sB3, kt);
+            MOE_STAGE(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
+            MOE_STAGE(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
+            MOE_STAGE(sA3, sB3, sA0, sB0, sA2, sB2, kt + 3);
+        }
 #undef MOE_DMA
-#undef MOE_COMPUTE
+#undef MOE_LOAD_FRAGS
+#undef MOE_MFMAS
+#undef MOE_INTERLEAVE
+#undef MOE_STAGE
+        // the trailing (re-fetch) DMAs land before the buffers are reused
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
 
-    // epilogue: D element q of block (i, b): row 8 (q / 4) + 4 half + q % 4, col r32
-    uint16_t* C = static_cast<uint16_t*>(g.C);
+        // epilogue: D element q of block (i, b): row 8 (q / 4) + 4 half + q % 4, col r32
+        uint16_t* C = static_cast<uint16_t*>(g.C);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int bo = 0; bo < (DUAL ? 2 : 4); ++bo) {
-            const int col = DUAL ? n0 + wn * 64 + bo * 32 + r32 : n0 + wn * 128 + bo * 32 + r32;
+            for (int bo = 0; bo < (DUAL ? 2 : 4); ++bo) {
+                const int col = DUAL ? n0 + wn * 64 + bo * 32 + r32 : n0 + wn * 128 + bo * 32 + r32;
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int r = wm * 128 + i * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
-                if (r < nrows) {
-                    float v = acc[i][bo][q];
-                    if (DUAL) v = silu_f32(v) * acc[i][bo + 2][q];
-                    C[(int64_t)(row0 + r) * g.N + col] = f32_to_bf16(v);
+                for (int q = 0; q < 16; ++q) {
+                    const int r = wm * 128 + i * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
+                    if (r < nrows) {
+                        float v = acc[i][bo][q];
+                        if (DUAL) v = silu_f32(v) * acc[i][bo + 2][q];
+                        C[(int64_t)(row0 + r) * g.N + col] = f32_to_bf16(v);
+                    }
                 }
             }
         }
@@ -474,16 +585,24 @@ hipError_t launch_bf16(const GemmGroup& g, hipStream_t s) {
     return hipGetLastError();
 }
 
+int persistent_grid() {
+    static int cus = 0;   // CUs of the current device, read once
+    if (cus == 0) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+            cus = prop.multiProcessorCount;
+        if (cus < 8) cus = 256;
+    }
+    return cus / 8 * 8;
+}
+
 template <bool DUAL>
 hipError_t launch_bf16_256(const GemmGroup& g, hipStream_t s) {
-    constexpr int BM = 256, BN = DUAL ? 128 : 256;
+    constexpr int BN = DUAL ? 128 : 256;
     const int tiles_n = g.N / BN;
-    const int64_t mtu = g.offsets ? grouped_m_tiles_upper(g.M, g.G, BM) : (g.M + BM - 1) / BM;
-    if (mtu == 0) return hipSuccess;
-    int64_t nwg = mtu * tiles_n;
-    nwg = (nwg + 7) / 8 * 8;
-    hipLaunchKernelGGL(gemm_bf16_256_kernel<DUAL>, dim3((unsigned)nwg), dim3(kThreads), 0, s, g,
-                       tiles_n, (int)mtu);
+    hipLaunchKernelGGL((gemm_bf16_256_kernel<DUAL>), dim3(persistent_grid()), dim3(kThreads), 0, s,
+                       g, tiles_n);
     return hipGetLastError();
 }
 
