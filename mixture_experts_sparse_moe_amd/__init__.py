@@ -16,7 +16,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe.so")
+# MOE_LIB_PATH loads another build of the same library (e.g. one compiled with
+# different tile options) in place of the in-tree libmoe.so.
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(_PKG, "libmoe.so")
 
 MOE_OK = 0
 MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED = -1, -2, -3

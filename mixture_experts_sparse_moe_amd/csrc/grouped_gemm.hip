@@ -256,6 +256,67 @@ constexpr int kBKs = 32;   // K elements per pipeline stage of the 256 kernel
 // compiler's own wait insertion, so it adds no waits of its own after these.
 constexpr int kWaitVm16Lgkm0 = (1 << 14) | (7 << 4) | (0 << 8);   // vmcnt(16) lgkmcnt(0)
 constexpr int kWaitVm0 = (7 << 4) | (15 << 8);                     // vmcnt(0)
+constexpr int kWaitVm0Lgkm0 = (7 << 4);                            // vmcnt(0) lgkmcnt(0)
+
+// ---- persistent tile schedule shared by the 256-tile kernels -------------
+// s_tb[e] = M tiles (of BM rows) before group e, s_tb[G] = all of them.
+template <int BM>
+__device__ __forceinline__ int tile_prefix(const GemmGroup& g, int* s_tb, int* s_wsum) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (g.offsets) {
+        int nt = 0;
+        if (tid < g.G) nt = (g.offsets[tid + 1] - g.offsets[tid] + BM - 1) / BM;
+        int v = nt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(v, o, 64);
+            if (lane >= o) v += u;
+        }
+        if (lane == 63) s_wsum[w] = v;
+        __syncthreads();
+        int before = 0;
+        for (int q = 0; q < w; ++q) before += s_wsum[q];
+        if (tid < g.G) s_tb[tid] = v + before - nt;
+        if (tid == g.G - 1) s_tb[g.G] = v + before;     // all M tiles (G <= 256 threads)
+    } else if (tid == 0) {
+        s_tb[0] = 0;
+        s_tb[1] = (g.M + BM - 1) / BM;
+    }
+    __syncthreads();
+    return g.offsets ? g.G : 1;
+}
+
+struct TileRef {
+    int grp, row0, nrows, n0;
+};
+
+// Logical tile L -> (group, rows, first column).  Bands of kWMW M tiles; in a
+// band, windows of wn_win N tiles; inside a window, M-tile-fastest order.
+template <int BM, int BN>
+__device__ __forceinline__ TileRef tile_at(const GemmGroup& g, const int* s_tb, int G, int mt_total,
+                                           int tiles_n, int wn_win, int L) {
+    const int band = L / (kWMW * tiles_n);
+    const int mb0 = band * kWMW;
+    const int mh = min(kWMW, mt_total - mb0);
+    const int rem = L - band * kWMW * tiles_n;
+    const int nwin = rem / (mh * wn_win);
+    const int r2 = rem - nwin * mh * wn_win;
+    const int mt = mb0 + r2 % mh;
+    const int ntile = nwin * wn_win + r2 / mh;
+    int lo = 0, hi = G;                              // s_tb[lo] <= mt < s_tb[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_tb[mid] <= mt) lo = mid; else hi = mid;
+    }
+    TileRef t;
+    t.grp = lo;
+    const int base_row = g.offsets ? g.offsets[lo] : 0;
+    const int end_row = g.offsets ? g.offsets[lo + 1] : g.M;
+    t.row0 = base_row + (mt - s_tb[lo]) * BM;
+    t.nrows = min(BM, end_row - t.row0);
+    t.n0 = ntile * BN;
+    return t;
+}
 
 // Swizzle of 64-byte LDS rows (4 chunks of 16 B): chunk c of row r sits at
 // c ^ f(r).  32 lanes reading rows r..r+31 at one logical chunk then hit
@@ -300,28 +361,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(GemmGroup g,
     const int K = g.K;
     const int KT = K / kBKs;          // multiple of 4
 
-    // ---- M tiles per group: exclusive prefix of ceil(count / BM), in LDS
-    if (g.offsets) {
-        int nt = 0;
-        if (tid < g.G) nt = (g.offsets[tid + 1] - g.offsets[tid] + BM - 1) / BM;
-        int v = nt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int u = __shfl_up(v, o, 64);
-            if (lane >= o) v += u;
-        }
-        if (lane == 63) s_wsum[w] = v;
-        __syncthreads();
-        int before = 0;
-        for (int q = 0; q < w; ++q) before += s_wsum[q];
-        if (tid < g.G) s_tb[tid] = v + before - nt;
-        if (tid == g.G - 1) s_tb[g.G] = v + before;     // all M tiles (G <= 256 threads)
-    } else if (tid == 0) {
-        s_tb[0] = 0;
-        s_tb[1] = (g.M + BM - 1) / BM;
-    }
-    __syncthreads();
-    const int G = g.offsets ? g.G : 1;
+    const int G = tile_prefix<BM>(g, s_tb, s_wsum);
     const int mt_total = s_tb[G];
     const int TL = mt_total * tiles_n;
     const int nslot = gridDim.x >> 3;             // workgroups per XCD
@@ -339,31 +379,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(GemmGroup g,
         b_row[b] = DUAL ? (b >> 1) * 128 + wn * 64 + (b & 1) * 32 + r32 : wn * 128 + b * 32 + r32;
 
     for (int L = xcd * per + slot; L < Lend; L += nslot) {
-        // ---- logical tile -> (M tile, N tile): windows of kWMW M tiles x wn_win
-        // N tiles, N-window-major inside a band of kWMW M tiles
-        const int band = L / (kWMW * tiles_n);
-        const int mb0 = band * kWMW;
-        const int mh = min(kWMW, mt_total - mb0);        // M tiles in this band
-        const int rem = L - band * kWMW * tiles_n;       // < mh * tiles_n
-        const int nwin = rem / (mh * wn_win);
-        const int nw0 = nwin * wn_win;
-        const int nwh = min(wn_win, tiles_n - nw0);      // N tiles in this window
-        const int r2 = rem - nwin * mh * wn_win;
-        const int mt = mb0 + r2 % mh;
-        const int ntile = nw0 + r2 / mh;
-        (void)nwh;
-        // ---- M tile -> group and rows (groups with no tiles are skipped)
-        int lo = 0, hi = G;                               // s_tb[lo] <= mt < s_tb[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_tb[mid] <= mt) lo = mid; else hi = mid;
-        }
-        const int grp = lo;
-        const int base_row = g.offsets ? g.offsets[grp] : 0;
-        const int grp_rows = g.offsets ? g.offsets[grp + 1] - base_row : g.M;
-        const int row0 = base_row + (mt - s_tb[grp]) * BM;
-        const int nrows = min(BM, base_row + grp_rows - row0);
-        const int n0 = ntile * BN;
+        const TileRef tr = tile_at<BM, BN>(g, s_tb, G, mt_total, tiles_n, wn_win, L);
+        const int grp = tr.grp, row0 = tr.row0, nrows = tr.nrows, n0 = tr.n0;
 
         // DMA sources: instruction j of wave w fills LDS rows 64 w + 16 j + lane / 4
         // at physical chunk lane % 4, which holds logical chunk (lane % 4) ^ swz4(row).
@@ -496,6 +513,332 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(GemmGroup g,
     }
 }
 
+// Variant of the persistent 256-tile kernel with 64-element K stages: every
+// LDS row is a full 128-byte line (8 chunks, swizzle swz), so each row's DMA
+// is one 128-byte request; two LDS stages, the DMA one stage ahead.
+template <bool DUAL>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256w_kernel(GemmGroup g, int tiles_n) {
+    constexpr int BM = 256;
+    constexpr int BN = DUAL ? 128 : 256;
+    constexpr int STG = 256 * kBK;    // elements of one A or B stage (32 KB)
+    __shared__ __align__(16) uint16_t sA0[STG], sA1[STG];
+    __shared__ __align__(16) uint16_t sB0[STG], sB1[STG];
+    __shared__ int s_tb[257];
+    __shared__ int s_wsum[kThreads / 64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int K = g.K;
+    const int KT = K / kBK;            // even
+
+    const int G = tile_prefix<BM>(g, s_tb, s_wsum);
+    const int mt_total = s_tb[G];
+    const int TL = mt_total * tiles_n;
+    const int nslot = gridDim.x >> 3;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per = (TL + 7) >> 3;
+    const int Lend = min(TL, (xcd + 1) * per);
+    const int wn_win = max(nslot / kWMW, 1);
+
+    const int half = lane >> 5, r32 = lane & 31;
+    int a_row[4], b_row[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a_row[i] = wm * 128 + i * 32 + r32;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+        b_row[b] = DUAL ? (b >> 1) * 128 + wn * 64 + (b & 1) * 32 + r32 : wn * 128 + b * 32 + r32;
+
+    for (int L = xcd * per + slot; L < Lend; L += nslot) {
+        const TileRef tr = tile_at<BM, BN>(g, s_tb, G, mt_total, tiles_n, wn_win, L);
+        const int grp = tr.grp, row0 = tr.row0, nrows = tr.nrows, n0 = tr.n0;
+
+        // instruction j of wave w fills LDS rows 64 w + 8 j + lane / 8 at physical
+        // chunk lane % 8, which holds logical chunk (lane % 8) ^ swz(row)
+        const char* a_base = static_cast<const char*>(g.A);
+        const char* b_base = static_cast<const char*>(DUAL ? (w < 2 ? g.B0 : g.B1) : g.B0) +
+                             ((int64_t)grp * g.N + n0) * K * 2;
+        uint32_t a_off[8], b_off[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = w * 64 + j * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ swz(r);
+            const int rr = min(r, nrows - 1);
+            const int src = g.gather ? g.gather[row0 + rr] / g.gather_div : row0 + rr;
+            a_off[j] = (uint32_t)src * (uint32_t)(K * 2) + c * 16;
+            b_off[j] = (uint32_t)(DUAL ? (r & 127) : r) * (uint32_t)(K * 2) + c * 16;
+        }
+
+        f32x16_t acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+        bf16x8_t fa0[4], fb0[4], fa1[4], fb1[4];
+
+#define MOE_DMA(sA_, sB_, kt_)                                                                  \
+    do {                                                                                        \
+        const char* ab_ = a_base + (kt_) * (kBK * 2);                                           \
+        const char* bb_ = b_base + (kt_) * (kBK * 2);                                           \
+        _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                         \
+            __builtin_amdgcn_global_load_lds(ab_ + a_off[j],                                    \
+                                             (lds_ptr_t)((sA_) + (w * 64 + j * 8) * kBK), 16, 0, 0); \
+            __builtin_amdgcn_global_load_lds(bb_ + b_off[j],                                    \
+                                             (lds_ptr_t)((sB_) + (w * 64 + j * 8) * kBK), 16, 0, 0); \
+        }                                                                                       \
+    } while (0)
+#define MOE_LOAD_FRAGS(sA_, sB_, s_, af_, bf_)                                                  \
+    do {                                                                                        \
+        const int c_ = 2 * (s_) + half;                                                         \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) af_[i] = as_bf16x8(                       \
+            *reinterpret_cast<const uint4*>((sA_) + a_row[i] * kBK + ((c_ ^ swz(a_row[i])) * 8))); \
+        _Pragma("unroll") for (int b = 0; b < 4; ++b) bf_[b] = as_bf16x8(                       \
+            *reinterpret_cast<const uint4*>((sB_) + b_row[b] * kBK + ((c_ ^ swz(b_row[b])) * 8))); \
+    } while (0)
+#define MOE_MFMAS(af_, bf_)                                                                     \
+    do {                                                                                        \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
+            _Pragma("unroll") for (int b = 0; b < 4; ++b) acc[i][b] =                           \
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_[i], bf_[b], acc[i][b], 0, 0, 0);    \
+    } while (0)
+#define MOE_INTERLEAVE()                                                                        \
+    do {                                                                                        \
+        _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                      \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                  \
+        }                                                                                       \
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                      \
+    } while (0)
+// Stage kt in (sAc, sBc), stage kt + 1 DMA'd into (sAn, sBn); fa0/fb0 hold
+// step 0 on entry.  Past the end the DMA re-fetches the last tile (unread).
+#define MOE_STAGE(sAc, sBc, sAn, sBn, kt_)                                                      \
+    do {                                                                                        \
+        MOE_DMA(sAn, sBn, min((kt_) + 1, KT - 1));                                              \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        MOE_LOAD_FRAGS(sAc, sBc, 1, fa1, fb1);                                                  \
+        MOE_MFMAS(fa0, fb0);                                                                    \
+        MOE_INTERLEAVE();                                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        MOE_LOAD_FRAGS(sAc, sBc, 2, fa0, fb0);                                                  \
+        MOE_MFMAS(fa1, fb1);                                                                    \
+        MOE_INTERLEAVE();                                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        MOE_LOAD_FRAGS(sAc, sBc, 3, fa1, fb1);                                                  \
+        MOE_MFMAS(fa0, fb0);                                                                    \
+        MOE_INTERLEAVE();                                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);                                              \
+        __builtin_amdgcn_s_barrier();                                                           \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        MOE_LOAD_FRAGS(sAn, sBn, 0, fa0, fb0);                                                  \
+        MOE_MFMAS(fa1, fb1);                                                                    \
+        MOE_INTERLEAVE();                                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+    } while (0)
+
+        __syncthreads();
+        MOE_DMA(sA0, sB0, 0);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        MOE_LOAD_FRAGS(sA0, sB0, 0, fa0, fb0);
+        for (int kt = 0; kt < KT; kt += 2) {
+            MOE_STAGE(sA0, sB0, sA1, sB1, kt);
+            MOE_STAGE(sA1, sB1, sA0, sB0, kt + 1);
+        }
+#undef MOE_DMA
+#undef MOE_LOAD_FRAGS
+#undef MOE_MFMAS
+#undef MOE_INTERLEAVE
+#undef MOE_STAGE
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+        uint16_t* C = static_cast<uint16_t*>(g.C);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int bo = 0; bo < (DUAL ? 2 : 4); ++bo) {
+                const int col = DUAL ? n0 + wn * 64 + bo * 32 + r32 : n0 + wn * 128 + bo * 32 + r32;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int r = wm * 128 + i * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
+                    if (r < nrows) {
+                        float v = acc[i][bo][q];
+                        if (DUAL) v = silu_f32(v) * acc[i][bo + 2][q];
+                        C[(int64_t)(row0 + r) * g.N + col] = f32_to_bf16(v);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// 8-wave variant (512 threads, two waves per SIMD) of the persistent
+// 256-tile kernel with 64-element K stages.  Eight waves keep twice as many
+// DMA requests in flight per CU as four, which the load path needs to feed
+// the MFMAs.  Waves form a 2 x 4 grid: wave (wm, wn) owns 128 rows and two
+// 32-row blocks of B (dual: gate columns 32 wn .. 32 wn + 31 and the same up
+// columns, so silu(g)*u stays in registers; single: B rows 64 wn .. 64 wn +
+// 63), i.e. 4 x 2 MFMA blocks = 128 accumulators.
+template <bool DUAL>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_256x8_kernel(GemmGroup g, int tiles_n) {
+    constexpr int BM = 256;
+    constexpr int BN = DUAL ? 128 : 256;
+    constexpr int STG = 256 * kBK;    // elements of one A or B stage (32 KB)
+    __shared__ __align__(16) uint16_t sA0[STG], sA1[STG];
+    __shared__ __align__(16) uint16_t sB0[STG], sB1[STG];
+    __shared__ int s_tb[257];
+    __shared__ int s_wsum[8];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 2, wn = w & 3;
+    const int K = g.K;
+    const int KT = K / kBK;            // even
+
+    const int G = tile_prefix<BM>(g, s_tb, s_wsum);
+    const int mt_total = s_tb[G];
+    const int TL = mt_total * tiles_n;
+    const int nslot = gridDim.x >> 3;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per = (TL + 7) >> 3;
+    const int Lend = min(TL, (xcd + 1) * per);
+    const int wn_win = max(nslot / kWMW, 1);
+
+    const int half = lane >> 5, r32 = lane & 31;
+    int a_row[4], b_row[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a_row[i] = wm * 128 + i * 32 + r32;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) b_row[b] = DUAL ? b * 128 + wn * 32 + r32 : wn * 64 + b * 32 + r32;
+
+    for (int L = xcd * per + slot; L < Lend; L += nslot) {
+        const TileRef tr = tile_at<BM, BN>(g, s_tb, G, mt_total, tiles_n, wn_win, L);
+        const int grp = tr.grp, row0 = tr.row0, nrows = tr.nrows, n0 = tr.n0;
+
+        // instruction j (0..3) of wave w fills LDS rows 32 w + 8 j + lane / 8 at
+        // physical chunk lane % 8, which holds logical chunk (lane % 8) ^ swz(row)
+        const char* a_base = static_cast<const char*>(g.A);
+        const char* b_base = static_cast<const char*>(DUAL ? (w < 4 ? g.B0 : g.B1) : g.B0) +
+                             ((int64_t)grp * g.N + n0) * K * 2;
+        uint32_t a_off[4], b_off[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = w * 32 + j * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ swz(r);
+            const int rr = min(r, nrows - 1);
+            const int src = g.gather ? g.gather[row0 + rr] / g.gather_div : row0 + rr;
+            a_off[j] = (uint32_t)src * (uint32_t)(K * 2) + c * 16;
+            b_off[j] = (uint32_t)(DUAL ? (r & 127) : r) * (uint32_t)(K * 2) + c * 16;
+        }
+
+        f32x16_t acc[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+        bf16x8_t fa0[4], fb0[2], fa1[4], fb1[2];
+
+#define MOE_DMA(sA_, sB_, kt_)                                                                  \
+    do {                                                                                        \
+        const char* ab_ = a_base + (kt_) * (kBK * 2);                                           \
+        const char* bb_ = b_base + (kt_) * (kBK * 2);                                           \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                         \
+            __builtin_amdgcn_global_load_lds(ab_ + a_off[j],                                    \
+                                             (lds_ptr_t)((sA_) + (w * 32 + j * 8) * kBK), 16, 0, 0); \
+            __builtin_amdgcn_global_load_lds(bb_ + b_off[j],                                    \
+                                             (lds_ptr_t)((sB_) + (w * 32 + j * 8) * kBK), 16, 0, 0); \
+        }                                                                                       \
+    } while (0)
+#define MOE_LOAD_FRAGS(sA_, sB_, s_, af_, bf_)                                                  \
+    do {                                                                                        \
+        const int c_ = 2 * (s_) + half;                                                         \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) af_[i] = as_bf16x8(                       \
+            *reinterpret_cast<const uint4*>((sA_) + a_row[i] * kBK + ((c_ ^ swz(a_row[i])) * 8))); \
+        _Pragma("unroll") for (int b = 0; b < 2; ++b) bf_[b] = as_bf16x8(                       \
+            *reinterpret_cast<const uint4*>((sB_) + b_row[b] * kBK + ((c_ ^ swz(b_row[b])) * 8))); \
+    } while (0)
+#define MOE_MFMAS(af_, bf_)                                                                     \
+    do {                                                                                        \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
+            _Pragma("unroll") for (int b = 0; b < 2; ++b) acc[i][b] =                           \
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_[i], bf_[b], acc[i][b], 0, 0, 0);    \
+    } while (0)
+// 8 MFMAs with the 6 fragment reads of the following step between them
+#define MOE_INTERLEAVE()                                                                        \
+    do {                                                                                        \
+        _Pragma("unroll") for (int i_ = 0; i_ < 6; ++i_) {                                      \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                  \
+        }                                                                                       \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                      \
+    } while (0)
+#define MOE_STAGE(sAc, sBc, sAn, sBn, kt_)                                                      \
+    do {                                                                                        \
+        MOE_DMA(sAn, sBn, min((kt_) + 1, KT - 1));                                              \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        MOE_LOAD_FRAGS(sAc, sBc, 1, fa1, fb1);                                                  \
+        MOE_MFMAS(fa0, fb0);                                                                    \
+        MOE_INTERLEAVE();                                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        MOE_LOAD_FRAGS(sAc, sBc, 2, fa0, fb0);                                                  \
+        MOE_MFMAS(fa1, fb1);                                                                    \
+        MOE_INTERLEAVE();                                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        MOE_LOAD_FRAGS(sAc, sBc, 3, fa1, fb1);                                                  \
+        MOE_MFMAS(fa0, fb0);                                                                    \
+        MOE_INTERLEAVE();                                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);                                              \
+        __builtin_amdgcn_s_barrier();                                                           \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        MOE_LOAD_FRAGS(sAn, sBn, 0, fa0, fb0);                                                  \
+        MOE_MFMAS(fa1, fb1);                                                                    \
+        MOE_INTERLEAVE();                                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+    } while (0)
+
+        __syncthreads();
+        MOE_DMA(sA0, sB0, 0);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        MOE_LOAD_FRAGS(sA0, sB0, 0, fa0, fb0);
+        for (int kt = 0; kt < KT; kt += 2) {
+            MOE_STAGE(sA0, sB0, sA1, sB1, kt);
+            MOE_STAGE(sA1, sB1, sA0, sB0, kt + 1);
+        }
+#undef MOE_DMA
+#undef MOE_LOAD_FRAGS
+#undef MOE_MFMAS
+#undef MOE_INTERLEAVE
+#undef MOE_STAGE
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+        uint16_t* C = static_cast<uint16_t*>(g.C);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int bo = 0; bo < (DUAL ? 1 : 2); ++bo) {
+                const int col = DUAL ? n0 + wn * 32 + r32 : n0 + wn * 64 + bo * 32 + r32;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int r = wm * 128 + i * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
+                    if (r < nrows) {
+                        float v = acc[i][bo][q];
+                        if (DUAL) v = silu_f32(v) * acc[i][1][q];
+                        C[(int64_t)(row0 + r) * g.N + col] = f32_to_bf16(v);
+                    }
+                }
+            }
+        }
+    }
+}
+
 // fp32 grouped GEMM: 64x64 tiles, BK 16, 4x4 outputs per thread.
 template <bool DUAL>
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmGroup g, int tiles_n, int mt_upper) {
@@ -597,12 +940,26 @@ int persistent_grid() {
     return cus / 8 * 8;
 }
 
+#ifndef MOE_GEMM_WIDE_STAGES
+#define MOE_GEMM_WIDE_STAGES 1
+#endif
+#ifndef MOE_GEMM_EIGHT_WAVES
+#define MOE_GEMM_EIGHT_WAVES 1
+#endif
+
 template <bool DUAL>
 hipError_t launch_bf16_256(const GemmGroup& g, hipStream_t s) {
     constexpr int BN = DUAL ? 128 : 256;
     const int tiles_n = g.N / BN;
-    hipLaunchKernelGGL((gemm_bf16_256_kernel<DUAL>), dim3(persistent_grid()), dim3(kThreads), 0, s,
-                       g, tiles_n);
+    if (MOE_GEMM_EIGHT_WAVES)
+        hipLaunchKernelGGL((gemm_bf16_256x8_kernel<DUAL>), dim3(persistent_grid()), dim3(512), 0, s,
+                           g, tiles_n);
+    else if (MOE_GEMM_WIDE_STAGES)
+        hipLaunchKernelGGL((gemm_bf16_256w_kernel<DUAL>), dim3(persistent_grid()), dim3(kThreads), 0,
+                           s, g, tiles_n);
+    else
+        hipLaunchKernelGGL((gemm_bf16_256_kernel<DUAL>), dim3(persistent_grid()), dim3(kThreads), 0, s,
+                           g, tiles_n);
     return hipGetLastError();
 }
 
