@@ -41,6 +41,12 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the CPU oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain device copy of 1 GiB (the reference for HBM counters)")
+    p.add_argument("--traffic-from", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_DIR"),
+                   help="rocprofv3 --pmc output dirs (FETCH_SIZE run of the bench, WRITE_SIZE run "
+                        "of the bench, FETCH_SIZE+WRITE_SIZE runs of --copy-calibration); writes "
+                        "profiles/traffic.json for --workload")
     return p.parse_args()
 
 
@@ -103,8 +109,73 @@ def cpu_baseline(sh, inp, target_s: float) -> dict:
             "sample": sample_desc, "seconds": round(t_used, 3)}
 
 
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration():
+    """A plain 1 GiB device-to-device copy: its FETCH_SIZE / WRITE_SIZE readings
+    give the scale between those counters and bytes moved."""
+    import torch
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES}), flush=True)
+
+
+def _pmc_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def _per_dispatch(rows, counter, name_has):
+    vals = [float(r["Counter_Value"]) for r in rows
+            if r["Counter_Name"] == counter and name_has in r["Kernel_Name"]]
+    return sum(vals) / len(vals) if vals else None
+
+
+def traffic_from(args):
+    """HBM bytes per launch of the gate/up GEMM from rocprofv3 FETCH_SIZE and
+    WRITE_SIZE runs, each scaled by the same counter's reading for the 1 GiB copy."""
+    fetch_dir, write_dir, copy_dir = args.traffic_from
+    copy_rows = _pmc_rows(copy_dir)
+    # the copy kernel is the largest dispatch of the calibration run
+    cf = max((float(r["Counter_Value"]) for r in copy_rows if r["Counter_Name"] == "FETCH_SIZE"),
+             default=None)
+    cw = max((float(r["Counter_Value"]) for r in copy_rows if r["Counter_Name"] == "WRITE_SIZE"),
+             default=None)
+    f_kib = _per_dispatch(_pmc_rows(fetch_dir), "FETCH_SIZE", "gemm_bf16_256x8_kernel<true>")
+    w_kib = _per_dispatch(_pmc_rows(write_dir), "WRITE_SIZE", "gemm_bf16_256x8_kernel<true>")
+    if None in (cf, cw, f_kib, w_kib):
+        sys.exit(f"missing counters: copy {cf} {cw}, kernel {f_kib} {w_kib}")
+    f_scale, w_scale = COPY_BYTES / cf, COPY_BYTES / cw
+    rec = {"kernel": "gemm_bf16_256x8_kernel<true> (gate/up)",
+           "fetch_kib": f_kib, "write_kib": w_kib,
+           "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_scale_bytes_per_kib": f_scale, "write_scale_bytes_per_kib": w_scale,
+           "bytes_per_launch": f_kib * f_scale + w_kib * w_scale,
+           "source_hash": kernel_source_hash()}
+    data = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+    data[args.workload] = rec
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(data, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(rec))
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(args)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the layer is measured at N=1", file=sys.stderr)
@@ -165,7 +236,7 @@ def main():
     alg = algorithmic(sh, cnt)
 
     gu_ms = float(stage_avg[2])
-    decode = sh.T * sh.k <= 8 * sh.E * 16      # few rows per expert: weight-read bound
+    decode = sh.T * sh.k < 64 * sh.E          # under 64 rows per expert: weight-read bound
     if decode:
         achieved = alg["gate_up"]["bytes"] / (gu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}

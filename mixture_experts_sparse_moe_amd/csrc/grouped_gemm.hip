@@ -366,7 +366,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(GemmGroup g,
     const int TL = mt_total * tiles_n;
     const int nslot = gridDim.x >> 3;             // workgroups per XCD
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int per = (TL + 7) >> 3;
+    // per-XCD range: a whole number of rounds, so every round is one window
+    const int per = ((TL + 7) / 8 + nslot - 1) / nslot * nslot;
     const int Lend = min(TL, (xcd + 1) * per);
     const int wn_win = max(nslot / kWMW, 1);      // N tiles per round window
 
@@ -537,7 +538,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256w_kernel(GemmGroup g
     const int TL = mt_total * tiles_n;
     const int nslot = gridDim.x >> 3;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int per = (TL + 7) >> 3;
+    // per-XCD range: a whole number of rounds, so every round is one window
+    const int per = ((TL + 7) / 8 + nslot - 1) / nslot * nslot;
     const int Lend = min(TL, (xcd + 1) * per);
     const int wn_win = max(nslot / kWMW, 1);
 
@@ -703,7 +705,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_256x8_kernel(GemmGroup g, in
     const int TL = mt_total * tiles_n;
     const int nslot = gridDim.x >> 3;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int per = (TL + 7) >> 3;
+    // per-XCD range: a whole number of rounds, so every round is one window
+    const int per = ((TL + 7) / 8 + nslot - 1) / nslot * nslot;
     const int Lend = min(TL, (xcd + 1) * per);
     const int wn_win = max(nslot / kWMW, 1);
 
