@@ -7,25 +7,20 @@
 // src(r) = gather[r] / gather_div (token of the pair) when gathering, else r.
 // Both operands are K-contiguous ("NT"), the natural MFMA operand layout.
 //
-// bf16 kernel (gfx950):
-//   - v_mfma_f32_32x32x16_bf16, fp32 accumulation.
-//   - Workgroup 256 threads = 2x2 waves on a BM x BN output tile (x2 weight
-//     matrices in dual mode: the gate and up tiles of the same columns sit
-//     in the same lanes, so silu(g)*u is a register-only epilogue).
-//   - BK = 64.  Global -> registers -> LDS, double-buffered: the next K tile
-//     is in flight while the MFMAs consume the current one; one barrier per
-//     K tile.  A rows are gathered on load (no permuted copy of x).
+// bf16 kernels (gfx950), fp32 accumulation on v_mfma_f32_32x32x16_bf16:
+//   - gemm_bf16_persistent_kernel: the main path.  One workgroup of 8 waves
+//     per CU walks 256 x 256 tiles of MFMA work with a direct-to-LDS DMA
+//     pipeline that runs on across tiles; described at the kernel.
+//   - gemm_bf16_kernel: the general fallback for N or K that the persistent
+//     kernel does not take (N % 128, K % 128 != 0): 4 waves, BM x BN tiles,
+//     global -> registers -> LDS, double-buffered, one workgroup per tile.
 //   - LDS rows are 64 bf16 = 8 chunks of 16 B; chunk c of row r is stored at
 //     c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1), so the 16-byte fragment reads
 //     of 32 consecutive rows hit distinct banks.
-//   - M tiles are data dependent: tile mt of the flattened list maps to
+//   - M tiles are data dependent: the flattened M-tile list maps to
 //     (expert, row range) by a prefix sum of ceil(count_e / BM) done in the
-//     workgroup, so no host sync is needed; the grid is sized by the upper
-//     bound ceil(rows / BM) + G and surplus tiles exit at once.
-//   - Workgroup ids are remapped so that the 8 XCDs (ids dealt round-robin)
-//     each run a contiguous range of logical tiles; logical tiles run WMW
-//     M-tiles at a time per N column, so tiles sharing a weight panel are
-//     resident in the same XCD's L2 together.
+//     workgroup from the device-side offsets, so no host sync is needed.
+//   - A rows are gathered on load (no permuted copy of x).
 // fp32 kernel: LDS-tiled FMA (the tiny fp32 layer only).
 #include "device_util.h"
 #include "moe_internal.h"
@@ -250,22 +245,24 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmGroup g, int ti
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kBKs = 32;   // K elements per pipeline stage of the 256 kernel
+// ---- persistent 256 x 256 kernel ---------------------------------------------
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
 // [6:4], lgkmcnt [11:8]).  The builtin, unlike inline asm, is seen by the
 // compiler's own wait insertion, so it adds no waits of its own after these.
-constexpr int kWaitVm16Lgkm0 = (1 << 14) | (7 << 4) | (0 << 8);   // vmcnt(16) lgkmcnt(0)
-constexpr int kWaitVm0 = (7 << 4) | (15 << 8);                     // vmcnt(0)
-constexpr int kWaitVm0Lgkm0 = (7 << 4);                            // vmcnt(0) lgkmcnt(0)
+constexpr int kWaitVm8 = 8 | (7 << 4) | (15 << 8);      // vmcnt(8)
+constexpr int kWaitVm0Lgkm0 = (7 << 4);                 // vmcnt(0) lgkmcnt(0)
 
-// ---- persistent tile schedule shared by the 256-tile kernels -------------
-// s_tb[e] = M tiles (of BM rows) before group e, s_tb[G] = all of them.
+// Per-workgroup tile table in LDS: s_tb[e] = M tiles (of BM rows) before
+// group e, s_tb[G] = all of them; s_off[e] = first grouped row of group e.
 template <int BM>
-__device__ __forceinline__ int tile_prefix(const GemmGroup& g, int* s_tb, int* s_wsum) {
+__device__ __forceinline__ int tile_prefix(const GemmGroup& g, int* s_tb, int* s_off, int* s_wsum) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     if (g.offsets) {
-        int nt = 0;
-        if (tid < g.G) nt = (g.offsets[tid + 1] - g.offsets[tid] + BM - 1) / BM;
+        int nt = 0, off = 0;
+        if (tid < g.G) {
+            off = g.offsets[tid];
+            nt = (g.offsets[tid + 1] - off + BM - 1) / BM;
+        }
         int v = nt;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -276,11 +273,19 @@ __device__ __forceinline__ int tile_prefix(const GemmGroup& g, int* s_tb, int* s
         __syncthreads();
         int before = 0;
         for (int q = 0; q < w; ++q) before += s_wsum[q];
-        if (tid < g.G) s_tb[tid] = v + before - nt;
-        if (tid == g.G - 1) s_tb[g.G] = v + before;     // all M tiles (G <= 256 threads)
+        if (tid < g.G) {
+            s_tb[tid] = v + before - nt;
+            s_off[tid] = off;
+        }
+        if (tid == g.G - 1) {           // G <= 256 < threads
+            s_tb[g.G] = v + before;
+            s_off[g.G] = g.offsets[g.G];
+        }
     } else if (tid == 0) {
         s_tb[0] = 0;
         s_tb[1] = (g.M + BM - 1) / BM;
+        s_off[0] = 0;
+        s_off[1] = g.M;
     }
     __syncthreads();
     return g.offsets ? g.G : 1;
@@ -293,7 +298,7 @@ struct TileRef {
 // Logical tile L -> (group, rows, first column).  Bands of kWMW M tiles; in a
 // band, windows of wn_win N tiles; inside a window, M-tile-fastest order.
 template <int BM, int BN>
-__device__ __forceinline__ TileRef tile_at(const GemmGroup& g, const int* s_tb, int G, int mt_total,
+__device__ __forceinline__ TileRef tile_at(const int* s_tb, const int* s_off, int G, int mt_total,
                                            int tiles_n, int wn_win, int L) {
     const int band = L / (kWMW * tiles_n);
     const int mb0 = band * kWMW;
@@ -310,397 +315,112 @@ __device__ __forceinline__ TileRef tile_at(const GemmGroup& g, const int* s_tb, 
     }
     TileRef t;
     t.grp = lo;
-    const int base_row = g.offsets ? g.offsets[lo] : 0;
-    const int end_row = g.offsets ? g.offsets[lo + 1] : g.M;
-    t.row0 = base_row + (mt - s_tb[lo]) * BM;
-    t.nrows = min(BM, end_row - t.row0);
+    t.row0 = s_off[lo] + (mt - s_tb[lo]) * BM;
+    t.nrows = min(BM, s_off[lo + 1] - t.row0);
     t.n0 = ntile * BN;
     return t;
 }
 
-// Swizzle of 64-byte LDS rows (4 chunks of 16 B): chunk c of row r sits at
-// c ^ f(r).  32 lanes reading rows r..r+31 at one logical chunk then hit
-// distinct bank groups whether the LDS serves 8 or 16 lanes per cycle.
-__device__ __forceinline__ int swz4(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// DMA sources of one tile for one wave: wave-uniform bases and 32-bit per-lane
+// byte offsets.  Instruction j (0..3) of wave w fills LDS rows 32 w + 8 j +
+// lane / 8 at physical 16-byte chunk lane % 8, which holds logical chunk
+// (lane % 8) ^ swz(row).  Gathered A rows are addressed from the start of A
+// (the host keeps A under 4 GiB for that case); other A rows from the tile.
+struct DmaSrc {
+    const char* a;
+    const char* b;
+    uint32_t ao[4], bo[4];
+};
 
-// Main bf16 kernel, persistent: one workgroup per CU walks a list of
-// 256 x 256 tiles of MFMA work.
+template <bool DUAL>
+__device__ __forceinline__ DmaSrc dma_src(const GemmGroup& g, const TileRef& t, int w, int lane) {
+    const uint32_t K2 = (uint32_t)g.K * 2;
+    DmaSrc s;
+    s.a = static_cast<const char*>(g.A) + (g.gather ? 0 : (int64_t)t.row0 * K2);
+    // dual: waves 0-3 stage gate rows n0 .. n0 + 127, waves 4-7 the same up rows
+    s.b = static_cast<const char*>(DUAL ? (w < 4 ? g.B0 : g.B1) : g.B0) +
+          ((int64_t)t.grp * g.N + t.n0) * K2;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = w * 32 + j * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
+        const int rr = min(r, t.nrows - 1);
+        const int src = g.gather ? g.gather[t.row0 + rr] / g.gather_div : rr;
+        s.ao[j] = (uint32_t)src * K2 + c * 16;
+        s.bo[j] = (uint32_t)(DUAL ? (r & 127) : r) * K2 + c * 16;
+    }
+    return s;
+}
+
+// Stores one 32 x 32 block of MFMA results as bf16.  Lane (half, r32) holds
+// column r32 of block rows 8 a + 4 half + b in v[4 a + b].  Inside each quad
+// of lanes a 4 x 4 transpose (two DPP exchanges and byte permutes) gives lane
+// j = r32 % 4 row 8 a + 4 half + j, columns r32 - j .. r32 - j + 3, written as
+// one 8-byte store per a.  Rows at or past rows_left are not written.
+__device__ __forceinline__ void store_block_bf16(uint16_t* Cb, int64_t ldc, int rows_left,
+                                                 const float* v, int lane) {
+    const int half = lane >> 5, r32 = lane & 31, j = r32 & 3;
+    const uint32_t sel = (j & 1) ? 0x03020706u : 0x05040100u;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const uint32_t d0 = pack_bf16x2(v[4 * a + 0], v[4 * a + 1]);   // rows b = 0, 1
+        const uint32_t d1 = pack_bf16x2(v[4 * a + 2], v[4 * a + 3]);   // rows b = 2, 3
+        // exchange with lane j ^ 1: even lanes keep rows 0 and 2, odd lanes rows 1 and 3
+        const uint32_t n0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d0, 0xB1, 0xF, 0xF, true);
+        const uint32_t n1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d1, 0xB1, 0xF, 0xF, true);
+        const uint32_t e0 = __builtin_amdgcn_perm(n0, d0, sel);
+        const uint32_t e1 = __builtin_amdgcn_perm(n1, d1, sel);
+        // exchange with lane j ^ 2: lane j ends with row j, all four columns
+        const uint32_t s = (j & 2) ? e0 : e1;
+        const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)s, 0x4E, 0xF, 0xF, true);
+        uint2 out;
+        out.x = (j & 2) ? r : e0;
+        out.y = (j & 2) ? e1 : r;
+        const int row = 8 * a + 4 * half + j;
+        if (row < rows_left) *reinterpret_cast<uint2*>(Cb + row * ldc + (r32 - j)) = out;
+    }
+}
+
+// Main bf16 kernel, persistent: one workgroup of 8 waves per CU walks a list
+// of 256 x 256 tiles of MFMA work.
 //   single: C tile 256 rows x 256 cols of one weight matrix;
 //   dual:   C tile 256 rows x 128 cols, computed for the gate and the up
 //           matrix (B rows 0..127 = gate, 128..255 = up, same columns).
 // Tile schedule: the real M tiles (ceil(count_e / 256) per expert, prefix sums
-// in LDS) times the N tiles form a list of logical tiles, cut into 8 equal
-// ranges, one per XCD (workgroup ids are dealt to the XCDs round-robin).
+// in LDS) times the N tiles form a list of logical tiles, cut into 8 ranges of
+// whole rounds, one per XCD (workgroup ids are dealt to the XCDs round-robin).
 // Inside a range the XCD's workgroups take consecutive tiles in rounds; a
 // round is a window of 4 M tiles x (workgroups / 4) N tiles, so its A and B
-// panels are shared in the XCD's L2 while all its tiles advance through K in
-// step (same work per tile, all resident at once).
-// 4 waves in 2 x 2; each wave owns 128 rows x 4 blocks of 32 B-rows, i.e.
-// 4 x 4 MFMA 32x32 blocks = 256 fp32 accumulators (AGPRs).
-// Global -> LDS by direct 16-byte DMA (global_load_lds_dwordx4): lane i of
-// an instruction fills bytes [16 i, 16 i + 16) of a 1 KB block = 16 LDS rows
-// of 32 bf16, so each lane fetches the chunk the swizzle places there.
-// Four LDS stages of 32 K-elements (separate arrays, so the compiler can see
-// that a DMA into one stage does not alias fragment reads of another), DMA
-// issued three stages ahead.  One barrier per stage, in the middle of the
-// stage: after it, the next stage's first fragments are read while the
-// current stage's last MFMAs run.
+// panels are shared in the XCD's L2 while its tiles advance through K together.
+// Waves form a 2 x 4 grid: wave (wm, wn) owns 128 rows and two 32-row blocks
+// of B (dual: gate columns 32 wn .. 32 wn + 31 and the same up columns, so
+// silu(g)*u stays in registers; single: B rows 64 wn .. 64 wn + 63), i.e.
+// 4 x 2 MFMA blocks = 128 fp32 accumulators per lane.
+// Global -> LDS by direct 16-byte DMA (global_load_lds_dwordx4), two LDS
+// buffers of 64 K-elements (separate arrays, so the compiler can see that a
+// DMA into one does not alias fragment reads of the other).  Each K stage is
+// four MFMA steps; one barrier per stage, before the last step.  Right after
+// the barrier the buffer just consumed is refilled with the stage after next,
+// so every DMA has a whole stage of MFMA work to land behind.  The stream of
+// stages runs on across tiles: the last two stages of a tile fetch the first
+// two of the workgroup's next tile, whose loads are in flight during the
+// epilogue.
 template <bool DUAL>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256_kernel(GemmGroup g, int tiles_n) {
-    constexpr int BM = 256;
-    constexpr int BN = DUAL ? 128 : 256;
-    constexpr int STG = 256 * kBKs;   // elements of one A or B stage
-    __shared__ __align__(16) uint16_t sA0[STG], sA1[STG], sA2[STG], sA3[STG];
-    __shared__ __align__(16) uint16_t sB0[STG], sB1[STG], sB2[STG], sB3[STG];
-    __shared__ int s_tb[257];          // M tiles before group e; s_tb[G] = all M tiles
-    __shared__ int s_wsum[kThreads / 64];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1;
-    const int K = g.K;
-    const int KT = K / kBKs;          // multiple of 4
-
-    const int G = tile_prefix<BM>(g, s_tb, s_wsum);
-    const int mt_total = s_tb[G];
-    const int TL = mt_total * tiles_n;
-    const int nslot = gridDim.x >> 3;             // workgroups per XCD
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    // per-XCD range: a whole number of rounds, so every round is one window
-    const int per = ((TL + 7) / 8 + nslot - 1) / nslot * nslot;
-    const int Lend = min(TL, (xcd + 1) * per);
-    const int wn_win = max(nslot / kWMW, 1);      // N tiles per round window
-
-    const int half = lane >> 5, r32 = lane & 31;
-    int a_row[4], b_row[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a_row[i] = wm * 128 + i * 32 + r32;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-        b_row[b] = DUAL ? (b >> 1) * 128 + wn * 64 + (b & 1) * 32 + r32 : wn * 128 + b * 32 + r32;
-
-    for (int L = xcd * per + slot; L < Lend; L += nslot) {
-        const TileRef tr = tile_at<BM, BN>(g, s_tb, G, mt_total, tiles_n, wn_win, L);
-        const int grp = tr.grp, row0 = tr.row0, nrows = tr.nrows, n0 = tr.n0;
-
-        // DMA sources: instruction j of wave w fills LDS rows 64 w + 16 j + lane / 4
-        // at physical chunk lane % 4, which holds logical chunk (lane % 4) ^ swz4(row).
-        // Addresses are a wave-uniform base plus a 32-bit per-lane byte offset.
-        const char* a_base = static_cast<const char*>(g.A);
-        // B rows 64 w .. 64 w + 63: dual -> gate (w < 2) or up (w >= 2) matrix,
-        // column n0 + row % 128; single -> column n0 + row.
-        const char* b_base = static_cast<const char*>(DUAL ? (w < 2 ? g.B0 : g.B1) : g.B0) +
-                             ((int64_t)grp * g.N + n0) * K * 2;
-        uint32_t a_off[4], b_off[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = w * 64 + j * 16 + (lane >> 2);
-            const int c = (lane & 3) ^ swz4(r);
-            const int rr = min(r, nrows - 1);
-            const int src = g.gather ? g.gather[row0 + rr] / g.gather_div : row0 + rr;
-            a_off[j] = (uint32_t)src * (uint32_t)(K * 2) + c * 16;
-            b_off[j] = (uint32_t)(DUAL ? (r & 127) : r) * (uint32_t)(K * 2) + c * 16;
-        }
-
-        f32x16_t acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-        bf16x8_t fa0[4], fb0[4], fa1[4], fb1[4];
-
-#define MOE_DMA(sA_, sB_, kt_)                                                                  \
-    do {                                                                                        \
-        const char* ab_ = a_base + (kt_) * (kBKs * 2);                                          \
-        const char* bb_ = b_base + (kt_) * (kBKs * 2);                                          \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                         \
-            __builtin_amdgcn_global_load_lds(ab_ + a_off[j],                                    \
-                                             (lds_ptr_t)((sA_) + (w * 64 + j * 16) * kBKs), 16, 0, 0); \
-            __builtin_amdgcn_global_load_lds(bb_ + b_off[j],                                    \
-                                             (lds_ptr_t)((sB_) + (w * 64 + j * 16) * kBKs), 16, 0, 0); \
-        }                                                                                       \
-    } while (0)
-#define MOE_LOAD_FRAGS(sA_, sB_, s_, af_, bf_)                                                  \
-    do {                                                                                        \
-        const int c_ = 2 * (s_) + half;                                                        \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) af_[i] = as_bf16x8(                       \
-            *reinterpret_cast<const uint4*>((sA_) + a_row[i] * kBKs + ((c_ ^ swz4(a_row[i])) * 8))); \
-        _Pragma("unroll") for (int b = 0; b < 4; ++b) bf_[b] = as_bf16x8(                       \
-            *reinterpret_cast<const uint4*>((sB_) + b_row[b] * kBKs + ((c_ ^ swz4(b_row[b])) * 8))); \
-    } while (0)
-#define MOE_MFMAS(af_, bf_)                                                                     \
-    do {                                                                                        \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
-            _Pragma("unroll") for (int b = 0; b < 4; ++b) acc[i][b] =                           \
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_[i], bf_[b], acc[i][b], 0, 0, 0);    \
-    } while (0)
-// 16 MFMAs with the 8 fragment reads of the following step between the first 8
-#define MOE_INTERLEAVE()                                                                        \
-    do {                                                                                        \
-        _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                      \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                  \
-        }                                                                                       \
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                      \
-    } while (0)
-// Stage kt in buffers (sAc, sBc); next stage in (sAn, sBn); DMA target of
-// stage kt + 3 in (sAp, sBp).  On entry fa0/fb0 hold step 0 of stage kt.
-// Branch-free, so each half is one scheduling region: past the last K tile
-// the DMA re-fetches the last tile into the free buffer (never read), so
-// exactly 8 DMAs are always issued per stage and vmcnt(16) always means
-// "stage kt + 1 has landed"; the fragment prefetch past the end is unused.
-#define MOE_STAGE(sAc, sBc, sAn, sBn, sAp, sBp, kt_)                                            \
-    do {                                                                                        \
-        const int st_ = (kt_);                                                                  \
-        MOE_DMA(sAp, sBp, min(st_ + 3, KT - 1));                                                \
-        __builtin_amdgcn_sched_barrier(0);                                                      \
-        MOE_LOAD_FRAGS(sAc, sBc, 1, fa1, fb1);                                                  \
-        MOE_MFMAS(fa0, fb0);                                                                    \
-        MOE_INTERLEAVE();                                                                       \
-        __builtin_amdgcn_sched_barrier(0);                                                      \
-        /* stage kt + 1 landed (own DMAs) and this wave's reads of stage kt are done */        \
-        __builtin_amdgcn_s_waitcnt(kWaitVm16Lgkm0);                                             \
-        __builtin_amdgcn_s_barrier();                                                           \
-        __builtin_amdgcn_sched_barrier(0);                                                      \
-        MOE_LOAD_FRAGS(sAn, sBn, 0, fa0, fb0);                                                  \
-        MOE_MFMAS(fa1, fb1);                                                                    \
-        MOE_INTERLEAVE();                                                                       \
-        __builtin_amdgcn_sched_barrier(0);                                                      \
-    } while (0)
-
-        // every wave is past its reads of the previous tile's buffers
-        __syncthreads();
-        MOE_DMA(sA0, sB0, 0);
-        MOE_DMA(sA1, sB1, 1);
-        MOE_DMA(sA2, sB2, 2);
-        __builtin_amdgcn_s_waitcnt(kWaitVm16Lgkm0);
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        MOE_LOAD_FRAGS(sA0, sB0, 0, fa0, fb0);
-        for (int kt = 0; kt < KT; kt += 4) {
-            MOE_STAGE(sA0, sB0, sA1, sB1, sA3, sB3, kt);
-            MOE_STAGE(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
-            MOE_STAGE(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
-            MOE_STAGE(sA3, sB3, sA0, sB0, sA2, sB2, kt + 3);
-        }
-#undef MOE_DMA
-#undef MOE_LOAD_FRAGS
-#undef MOE_MFMAS
-#undef MOE_INTERLEAVE
-#undef MOE_STAGE
-        // the trailing (re-fetch) DMAs land before the buffers are reused
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-
-        // epilogue: D element q of block (i, b): row 8 (q / 4) + 4 half + q % 4, col r32
-        uint16_t* C = static_cast<uint16_t*>(g.C);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int bo = 0; bo < (DUAL ? 2 : 4); ++bo) {
-                const int col = DUAL ? n0 + wn * 64 + bo * 32 + r32 : n0 + wn * 128 + bo * 32 + r32;
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int r = wm * 128 + i * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
-                    if (r < nrows) {
-                        float v = acc[i][bo][q];
-                        if (DUAL) v = silu_f32(v) * acc[i][bo + 2][q];
-                        C[(int64_t)(row0 + r) * g.N + col] = f32_to_bf16(v);
-                    }
-                }
-            }
-        }
-    }
-}
-
-// Variant of the persistent 256-tile kernel with 64-element K stages: every
-// LDS row is a full 128-byte line (8 chunks, swizzle swz), so each row's DMA
-// is one 128-byte request; two LDS stages, the DMA one stage ahead.
-template <bool DUAL>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_256w_kernel(GemmGroup g, int tiles_n) {
+__global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup g, int tiles_n) {
     constexpr int BM = 256;
     constexpr int BN = DUAL ? 128 : 256;
     constexpr int STG = 256 * kBK;    // elements of one A or B stage (32 KB)
     __shared__ __align__(16) uint16_t sA0[STG], sA1[STG];
     __shared__ __align__(16) uint16_t sB0[STG], sB1[STG];
-    __shared__ int s_tb[257];
-    __shared__ int s_wsum[kThreads / 64];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1;
-    const int K = g.K;
-    const int KT = K / kBK;            // even
-
-    const int G = tile_prefix<BM>(g, s_tb, s_wsum);
-    const int mt_total = s_tb[G];
-    const int TL = mt_total * tiles_n;
-    const int nslot = gridDim.x >> 3;
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    // per-XCD range: a whole number of rounds, so every round is one window
-    const int per = ((TL + 7) / 8 + nslot - 1) / nslot * nslot;
-    const int Lend = min(TL, (xcd + 1) * per);
-    const int wn_win = max(nslot / kWMW, 1);
-
-    const int half = lane >> 5, r32 = lane & 31;
-    int a_row[4], b_row[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a_row[i] = wm * 128 + i * 32 + r32;
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-        b_row[b] = DUAL ? (b >> 1) * 128 + wn * 64 + (b & 1) * 32 + r32 : wn * 128 + b * 32 + r32;
-
-    for (int L = xcd * per + slot; L < Lend; L += nslot) {
-        const TileRef tr = tile_at<BM, BN>(g, s_tb, G, mt_total, tiles_n, wn_win, L);
-        const int grp = tr.grp, row0 = tr.row0, nrows = tr.nrows, n0 = tr.n0;
-
-        // instruction j of wave w fills LDS rows 64 w + 8 j + lane / 8 at physical
-        // chunk lane % 8, which holds logical chunk (lane % 8) ^ swz(row)
-        const char* a_base = static_cast<const char*>(g.A);
-        const char* b_base = static_cast<const char*>(DUAL ? (w < 2 ? g.B0 : g.B1) : g.B0) +
-                             ((int64_t)grp * g.N + n0) * K * 2;
-        uint32_t a_off[8], b_off[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int r = w * 64 + j * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ swz(r);
-            const int rr = min(r, nrows - 1);
-            const int src = g.gather ? g.gather[row0 + rr] / g.gather_div : row0 + rr;
-            a_off[j] = (uint32_t)src * (uint32_t)(K * 2) + c * 16;
-            b_off[j] = (uint32_t)(DUAL ? (r & 127) : r) * (uint32_t)(K * 2) + c * 16;
-        }
-
-        f32x16_t acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-        bf16x8_t fa0[4], fb0[4], fa1[4], fb1[4];
-
-#define MOE_DMA(sA_, sB_, kt_)                                                                  \
-    do {                                                                                        \
-        const char* ab_ = a_base + (kt_) * (kBK * 2);                                           \
-        const char* bb_ = b_base + (kt_) * (kBK * 2);                                           \
-        _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                         \
-            __builtin_amdgcn_global_load_lds(ab_ + a_off[j],                                    \
-                                             (lds_ptr_t)((sA_) + (w * 64 + j * 8) * kBK), 16, 0, 0); \
-            __builtin_amdgcn_global_load_lds(bb_ + b_off[j],                                    \
-                                             (lds_ptr_t)((sB_) + (w * 64 + j * 8) * kBK), 16, 0, 0); \
-        }                                                                                       \
-    } while (0)
-#define MOE_LOAD_FRAGS(sA_, sB_, s_, af_, bf_)                                                  \
-    do {                                                                                        \
-        const int c_ = 2 * (s_) + half;                                                         \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) af_[i] = as_bf16x8(                       \
-            *reinterpret_cast<const uint4*>((sA_) + a_row[i] * kBK + ((c_ ^ swz(a_row[i])) * 8))); \
-        _Pragma("unroll") for (int b = 0; b < 4; ++b) bf_[b] = as_bf16x8(                       \
-            *reinterpret_cast<const uint4*>((sB_) + b_row[b] * kBK + ((c_ ^ swz(b_row[b])) * 8))); \
-    } while (0)
-#define MOE_MFMAS(af_, bf_)                                                                     \
-    do {                                                                                        \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
-            _Pragma("unroll") for (int b = 0; b < 4; ++b) acc[i][b] =                           \
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_[i], bf_[b], acc[i][b], 0, 0, 0);    \
-    } while (0)
-#define MOE_INTERLEAVE()                                                                        \
-    do {                                                                                        \
-        _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) {                                      \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                  \
-        }                                                                                       \
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                                      \
-    } while (0)
-// Stage kt in (sAc, sBc), stage kt + 1 DMA'd into (sAn, sBn); fa0/fb0 hold
-// step 0 on entry.  Past the end the DMA re-fetches the last tile (unread).
-#define MOE_STAGE(sAc, sBc, sAn, sBn, kt_)                                                      \
-    do {                                                                                        \
-        MOE_DMA(sAn, sBn, min((kt_) + 1, KT - 1));                                              \
-        __builtin_amdgcn_sched_barrier(0);                                                      \
-        MOE_LOAD_FRAGS(sAc, sBc, 1, fa1, fb1);                                                  \
-        MOE_MFMAS(fa0, fb0);                                                                    \
-        MOE_INTERLEAVE();                                                                       \
-        __builtin_amdgcn_sched_barrier(0);                                                      \
-        MOE_LOAD_FRAGS(sAc, sBc, 2, fa0, fb0);                                                  \
-        MOE_MFMAS(fa1, fb1);                                                                    \
-        MOE_INTERLEAVE();                                                                       \
-        __builtin_amdgcn_sched_barrier(0);                                                      \
-        MOE_LOAD_FRAGS(sAc, sBc, 3, fa1, fb1);                                                  \
-        MOE_MFMAS(fa0, fb0);                                                                    \
-        MOE_INTERLEAVE();                                                                       \
-        __builtin_amdgcn_sched_barrier(0);                                                      \
-        __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);                                              \
-        __builtin_amdgcn_s_barrier();                                                           \
-        __builtin_amdgcn_sched_barrier(0);                                                      \
-        MOE_LOAD_FRAGS(sAn, sBn, 0, fa0, fb0);                                                  \
-        MOE_MFMAS(fa1, fb1);                                                                    \
-        MOE_INTERLEAVE();                                                                       \
-        __builtin_amdgcn_sched_barrier(0);                                                      \
-    } while (0)
-
-        __syncthreads();
-        MOE_DMA(sA0, sB0, 0);
-        __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        MOE_LOAD_FRAGS(sA0, sB0, 0, fa0, fb0);
-        for (int kt = 0; kt < KT; kt += 2) {
-            MOE_STAGE(sA0, sB0, sA1, sB1, kt);
-            MOE_STAGE(sA1, sB1, sA0, sB0, kt + 1);
-        }
-#undef MOE_DMA
-#undef MOE_LOAD_FRAGS
-#undef MOE_MFMAS
-#undef MOE_INTERLEAVE
-#undef MOE_STAGE
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-
-        uint16_t* C = static_cast<uint16_t*>(g.C);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int bo = 0; bo < (DUAL ? 2 : 4); ++bo) {
-                const int col = DUAL ? n0 + wn * 64 + bo * 32 + r32 : n0 + wn * 128 + bo * 32 + r32;
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int r = wm * 128 + i * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
-                    if (r < nrows) {
-                        float v = acc[i][bo][q];
-                        if (DUAL) v = silu_f32(v) * acc[i][bo + 2][q];
-                        C[(int64_t)(row0 + r) * g.N + col] = f32_to_bf16(v);
-                    }
-                }
-            }
-        }
-    }
-}
-
-// 8-wave variant (512 threads, two waves per SIMD) of the persistent
-// 256-tile kernel with 64-element K stages.  Eight waves keep twice as many
-// DMA requests in flight per CU as four, which the load path needs to feed
-// the MFMAs.  Waves form a 2 x 4 grid: wave (wm, wn) owns 128 rows and two
-// 32-row blocks of B (dual: gate columns 32 wn .. 32 wn + 31 and the same up
-// columns, so silu(g)*u stays in registers; single: B rows 64 wn .. 64 wn +
-// 63), i.e. 4 x 2 MFMA blocks = 128 accumulators.
-template <bool DUAL>
-__global__ __launch_bounds__(512, 1) void gemm_bf16_256x8_kernel(GemmGroup g, int tiles_n) {
-    constexpr int BM = 256;
-    constexpr int BN = DUAL ? 128 : 256;
-    constexpr int STG = 256 * kBK;    // elements of one A or B stage (32 KB)
-    __shared__ __align__(16) uint16_t sA0[STG], sA1[STG];
-    __shared__ __align__(16) uint16_t sB0[STG], sB1[STG];
-    __shared__ int s_tb[257];
+    __shared__ int s_tb[257], s_off[257];
     __shared__ int s_wsum[8];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3;
-    const int K = g.K;
-    const int KT = K / kBK;            // even
+    const int KT = g.K / kBK;          // even, >= 2
 
-    const int G = tile_prefix<BM>(g, s_tb, s_wsum);
+    const int G = tile_prefix<BM>(g, s_tb, s_off, s_wsum);
     const int mt_total = s_tb[G];
     const int TL = mt_total * tiles_n;
     const int nslot = gridDim.x >> 3;
@@ -709,6 +429,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_256x8_kernel(GemmGroup g, in
     const int per = ((TL + 7) / 8 + nslot - 1) / nslot * nslot;
     const int Lend = min(TL, (xcd + 1) * per);
     const int wn_win = max(nslot / kWMW, 1);
+    int L = xcd * per + slot;
+    if (L >= Lend) return;
 
     const int half = lane >> 5, r32 = lane & 31;
     int a_row[4], b_row[2];
@@ -717,43 +439,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_256x8_kernel(GemmGroup g, in
 #pragma unroll
     for (int b = 0; b < 2; ++b) b_row[b] = DUAL ? b * 128 + wn * 32 + r32 : wn * 64 + b * 32 + r32;
 
-    for (int L = xcd * per + slot; L < Lend; L += nslot) {
-        const TileRef tr = tile_at<BM, BN>(g, s_tb, G, mt_total, tiles_n, wn_win, L);
-        const int grp = tr.grp, row0 = tr.row0, nrows = tr.nrows, n0 = tr.n0;
-
-        // instruction j (0..3) of wave w fills LDS rows 32 w + 8 j + lane / 8 at
-        // physical chunk lane % 8, which holds logical chunk (lane % 8) ^ swz(row)
-        const char* a_base = static_cast<const char*>(g.A);
-        const char* b_base = static_cast<const char*>(DUAL ? (w < 4 ? g.B0 : g.B1) : g.B0) +
-                             ((int64_t)grp * g.N + n0) * K * 2;
-        uint32_t a_off[4], b_off[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = w * 32 + j * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ swz(r);
-            const int rr = min(r, nrows - 1);
-            const int src = g.gather ? g.gather[row0 + rr] / g.gather_div : row0 + rr;
-            a_off[j] = (uint32_t)src * (uint32_t)(K * 2) + c * 16;
-            b_off[j] = (uint32_t)(DUAL ? (r & 127) : r) * (uint32_t)(K * 2) + c * 16;
-        }
-
-        f32x16_t acc[4][2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-        bf16x8_t fa0[4], fb0[2], fa1[4], fb1[2];
-
-#define MOE_DMA(sA_, sB_, kt_)                                                                  \
+#define MOE_DMA(sA_, sB_, src_, kt_)                                                            \
     do {                                                                                        \
-        const char* ab_ = a_base + (kt_) * (kBK * 2);                                           \
-        const char* bb_ = b_base + (kt_) * (kBK * 2);                                           \
+        const char* ab_ = (src_).a + (kt_) * (kBK * 2);                                         \
+        const char* bb_ = (src_).b + (kt_) * (kBK * 2);                                         \
         _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                         \
-            __builtin_amdgcn_global_load_lds(ab_ + a_off[j],                                    \
+            __builtin_amdgcn_global_load_lds(ab_ + (src_).ao[j],                                \
                                              (lds_ptr_t)((sA_) + (w * 32 + j * 8) * kBK), 16, 0, 0); \
-            __builtin_amdgcn_global_load_lds(bb_ + b_off[j],                                    \
+            __builtin_amdgcn_global_load_lds(bb_ + (src_).bo[j],                                \
                                              (lds_ptr_t)((sB_) + (w * 32 + j * 8) * kBK), 16, 0, 0); \
         }                                                                                       \
     } while (0)
@@ -780,10 +473,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_256x8_kernel(GemmGroup g, in
         }                                                                                       \
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                      \
     } while (0)
-#define MOE_STAGE(sAc, sBc, sAn, sBn, kt_)                                                      \
+// One K stage from buffer (sAc, sBc); afterwards that buffer is refilled with
+// stage kd_ of src_ (if fetch_) and the first fragments of (sAn, sBn) are read.
+#define MOE_STAGE(sAc, sBc, sAn, sBn, src_, kd_, fetch_)                                        \
     do {                                                                                        \
-        MOE_DMA(sAn, sBn, min((kt_) + 1, KT - 1));                                              \
-        __builtin_amdgcn_sched_barrier(0);                                                      \
         MOE_LOAD_FRAGS(sAc, sBc, 1, fa1, fb1);                                                  \
         MOE_MFMAS(fa0, fb0);                                                                    \
         MOE_INTERLEAVE();                                                                       \
@@ -799,47 +492,72 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_256x8_kernel(GemmGroup g, in
         __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);                                              \
         __builtin_amdgcn_s_barrier();                                                           \
         __builtin_amdgcn_sched_barrier(0);                                                      \
+        if (fetch_) MOE_DMA(sAc, sBc, src_, kd_);                                               \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
         MOE_LOAD_FRAGS(sAn, sBn, 0, fa0, fb0);                                                  \
         MOE_MFMAS(fa1, fb1);                                                                    \
         MOE_INTERLEAVE();                                                                       \
         __builtin_amdgcn_sched_barrier(0);                                                      \
     } while (0)
 
-        __syncthreads();
-        MOE_DMA(sA0, sB0, 0);
-        __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        MOE_LOAD_FRAGS(sA0, sB0, 0, fa0, fb0);
-        for (int kt = 0; kt < KT; kt += 2) {
-            MOE_STAGE(sA0, sB0, sA1, sB1, kt);
-            MOE_STAGE(sA1, sB1, sA0, sB0, kt + 1);
+    TileRef tr = tile_at<BM, BN>(s_tb, s_off, G, mt_total, tiles_n, wn_win, L);
+    DmaSrc cur = dma_src<DUAL>(g, tr, w, lane);
+    bf16x8_t fa0[4], fb0[2], fa1[4], fb1[2];
+    // prologue: the first tile's stages 0 and 1; wait for this wave's stage 0
+    MOE_DMA(sA0, sB0, cur, 0);
+    MOE_DMA(sA1, sB1, cur, 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    MOE_LOAD_FRAGS(sA0, sB0, 0, fa0, fb0);
+
+    uint16_t* C = static_cast<uint16_t*>(g.C);
+    for (;;) {
+        const int Ln = L + nslot;
+        const bool more = Ln < Lend;
+        const TileRef tn = tile_at<BM, BN>(s_tb, s_off, G, mt_total, tiles_n, wn_win, more ? Ln : L);
+        const DmaSrc nxt = dma_src<DUAL>(g, tn, w, lane);
+
+        f32x16_t acc[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+        for (int kt = 0; kt < KT - 2; kt += 2) {
+            MOE_STAGE(sA0, sB0, sA1, sB1, cur, kt + 2, true);
+            MOE_STAGE(sA1, sB1, sA0, sB0, cur, kt + 3, true);
         }
+        MOE_STAGE(sA0, sB0, sA1, sB1, nxt, 0, more);
+        MOE_STAGE(sA1, sB1, sA0, sB0, nxt, 1, more);
+
+        // epilogue: the next tile's first two stages are in flight meanwhile
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int bo = 0; bo < (DUAL ? 1 : 2); ++bo) {
+                float v[16];
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    v[q] = DUAL ? silu_f32(acc[i][0][q]) * acc[i][1][q] : acc[i][bo][q];
+                const int rb = wm * 128 + i * 32;
+                const int cb = DUAL ? wn * 32 : wn * 64 + bo * 32;
+                store_block_bf16(C + (int64_t)(tr.row0 + rb) * g.N + tr.n0 + cb, g.N, tr.nrows - rb, v,
+                                 lane);
+            }
+        }
+        if (!more) break;
+        L = Ln;
+        tr = tn;
+        cur = nxt;
+    }
 #undef MOE_DMA
 #undef MOE_LOAD_FRAGS
 #undef MOE_MFMAS
 #undef MOE_INTERLEAVE
 #undef MOE_STAGE
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-
-        uint16_t* C = static_cast<uint16_t*>(g.C);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int bo = 0; bo < (DUAL ? 1 : 2); ++bo) {
-                const int col = DUAL ? n0 + wn * 32 + r32 : n0 + wn * 64 + bo * 32 + r32;
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int r = wm * 128 + i * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
-                    if (r < nrows) {
-                        float v = acc[i][bo][q];
-                        if (DUAL) v = silu_f32(v) * acc[i][1][q];
-                        C[(int64_t)(row0 + r) * g.N + col] = f32_to_bf16(v);
-                    }
-                }
-            }
-        }
-    }
 }
 
 // fp32 grouped GEMM: 64x64 tiles, BK 16, 4x4 outputs per thread.
@@ -943,26 +661,11 @@ int persistent_grid() {
     return cus / 8 * 8;
 }
 
-#ifndef MOE_GEMM_WIDE_STAGES
-#define MOE_GEMM_WIDE_STAGES 1
-#endif
-#ifndef MOE_GEMM_EIGHT_WAVES
-#define MOE_GEMM_EIGHT_WAVES 1
-#endif
-
 template <bool DUAL>
-hipError_t launch_bf16_256(const GemmGroup& g, hipStream_t s) {
+hipError_t launch_bf16_persistent(const GemmGroup& g, hipStream_t s) {
     constexpr int BN = DUAL ? 128 : 256;
-    const int tiles_n = g.N / BN;
-    if (MOE_GEMM_EIGHT_WAVES)
-        hipLaunchKernelGGL((gemm_bf16_256x8_kernel<DUAL>), dim3(persistent_grid()), dim3(512), 0, s,
-                           g, tiles_n);
-    else if (MOE_GEMM_WIDE_STAGES)
-        hipLaunchKernelGGL((gemm_bf16_256w_kernel<DUAL>), dim3(persistent_grid()), dim3(kThreads), 0,
-                           s, g, tiles_n);
-    else
-        hipLaunchKernelGGL((gemm_bf16_256_kernel<DUAL>), dim3(persistent_grid()), dim3(kThreads), 0, s,
-                           g, tiles_n);
+    hipLaunchKernelGGL((gemm_bf16_persistent_kernel<DUAL>), dim3(persistent_grid()), dim3(512), 0, s,
+                       g, g.N / BN);
     return hipGetLastError();
 }
 
@@ -986,9 +689,12 @@ int64_t grouped_m_tiles_upper(int64_t rows, int G, int bm) {
 hipError_t launch_grouped_gemm(const GemmGroup& g, bool dual, bool bf16, hipStream_t s) {
     if (g.M == 0) return hipSuccess;
     if (!bf16) return dual ? launch_f32<true>(g, s) : launch_f32<false>(g, s);
-    // the 256-tile kernel takes K tiles in pairs: K % 128 == 0
-    if (g.K % 128 == 0 && dual && g.N % 128 == 0) return launch_bf16_256<true>(g, s);
-    if (g.K % 128 == 0 && !dual && g.N % 256 == 0) return launch_bf16_256<false>(g, s);
+    // The persistent kernel takes K stages in pairs (K % 128 == 0) and
+    // addresses gathered A rows with 32-bit byte offsets from the start of A.
+    const int64_t a_rows = g.gather ? ((int64_t)g.M + g.gather_div - 1) / g.gather_div : 0;
+    const bool fits = g.K % 128 == 0 && a_rows * g.K * 2 < (int64_t(1) << 32);
+    if (fits && dual && g.N % 128 == 0) return launch_bf16_persistent<true>(g, s);
+    if (fits && !dual && g.N % 256 == 0) return launch_bf16_persistent<false>(g, s);
     if (g.N % 128 == 0) return dual ? launch_bf16<128, 128, true>(g, s) : launch_bf16<128, 128, false>(g, s);
     return dual ? launch_bf16<128, 64, true>(g, s) : launch_bf16<128, 64, false>(g, s);
 }
