@@ -5,6 +5,9 @@
 // One workgroup per token row, fp32 sums in slot order j = 0..k-1, then the
 // shared row, then rounding.  Each y row is written exactly once: no atomics,
 // deterministic.  bf16 rows move as 16-byte vectors (8 elements per lane).
+// When the down projection was computed in K ranges, expert_out (and shared)
+// hold one bf16 slice per range; a row is the fp32 sum of its slices in slice
+// order, taken before the gate weight.
 #include "device_util.h"
 #include "moe_internal.h"
 
@@ -13,6 +16,26 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+
+// 8 bf16 elements at p, summed in fp32 over `slices` slices `stride` apart.
+__device__ __forceinline__ void load_row_sum(const uint16_t* p, int slices, int64_t stride, float* r) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = bf16_to_f32((uint16_t)(u[i] & 0xFFFF));
+        r[2 * i + 1] = bf16_to_f32((uint16_t)(u[i] >> 16));
+    }
+    for (int sl = 1; sl < slices; ++sl) {
+        const uint4 e = *reinterpret_cast<const uint4*>(p + sl * stride);
+        const uint32_t w[4] = {e.x, e.y, e.z, e.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            r[2 * i] += bf16_to_f32((uint16_t)(w[i] & 0xFFFF));
+            r[2 * i + 1] += bf16_to_f32((uint16_t)(w[i] >> 16));
+        }
+    }
+}
 
 __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(CombineArgs a) {
     const int t = blockIdx.x;
@@ -30,23 +53,17 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(CombineArgs a) {
     for (int v = threadIdx.x; v < nvec; v += kThreads) {
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         for (int j = 0; j < a.k; ++j) {
-            const uint4 q = *reinterpret_cast<const uint4*>(O + (int64_t)s_pos[j] * a.d + v * 8);
+            float row[8];
+            load_row_sum(O + (int64_t)s_pos[j] * a.d + v * 8, a.splitk, a.part_stride, row);
             const float wj = s_w[j];
-            const uint32_t u[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[2 * i] = fmaf(wj, bf16_to_f32((uint16_t)(u[i] & 0xFFFF)), acc[2 * i]);
-                acc[2 * i + 1] = fmaf(wj, bf16_to_f32((uint16_t)(u[i] >> 16)), acc[2 * i + 1]);
-            }
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, row[i], acc[i]);
         }
         if (S) {
-            const uint4 q = *reinterpret_cast<const uint4*>(S + (int64_t)t * a.d + v * 8);
-            const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+            float row[8];
+            load_row_sum(S + (int64_t)t * a.d + v * 8, a.shared_splitk, a.shared_stride, row);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[2 * i] += bf16_to_f32((uint16_t)(u[i] & 0xFFFF));
-                acc[2 * i + 1] += bf16_to_f32((uint16_t)(u[i] >> 16));
-            }
+            for (int i = 0; i < 8; ++i) acc[i] += row[i];
         }
         uint4 o;
         o.x = pack_bf16x2(acc[0], acc[1]);

@@ -292,7 +292,7 @@ __device__ __forceinline__ int tile_prefix(const GemmGroup& g, int* s_tb, int* s
 }
 
 struct TileRef {
-    int grp, row0, nrows, n0;
+    int grp, row0, nrows, n0, ks;
 };
 
 // Logical tile L -> (group, rows, first column).  Bands of kWMW M tiles; in a
@@ -318,6 +318,19 @@ __device__ __forceinline__ TileRef tile_at(const int* s_tb, const int* s_off, in
     t.row0 = s_off[lo] + (mt - s_tb[lo]) * BM;
     t.nrows = min(BM, s_off[lo + 1] - t.row0);
     t.n0 = ntile * BN;
+    t.ks = 0;
+    return t;
+}
+
+// Logical tile L of a K-split GEMM: the split index is the slowest, so each
+// split walks the same windows of M x N tiles.
+template <int BM, int BN>
+__device__ __forceinline__ TileRef split_tile_at(const int* s_tb, const int* s_off, int G, int mt_total,
+                                                 int tiles_n, int wn_win, int L) {
+    const int per_split = mt_total * tiles_n;
+    const int ks = L / per_split;
+    TileRef t = tile_at<BM, BN>(s_tb, s_off, G, mt_total, tiles_n, wn_win, L - ks * per_split);
+    t.ks = ks;
     return t;
 }
 
@@ -326,23 +339,30 @@ __device__ __forceinline__ TileRef tile_at(const int* s_tb, const int* s_off, in
 // lane / 8 at physical 16-byte chunk lane % 8, which holds logical chunk
 // (lane % 8) ^ swz(row).  Gathered A rows are addressed from the start of A
 // (the host keeps A under 4 GiB for that case); other A rows from the tile.
+template <int J>
 struct DmaSrc {
     const char* a;
     const char* b;
-    uint32_t ao[4], bo[4];
+    uint32_t ao[J], bo[J];
 };
 
-template <bool DUAL>
-__device__ __forceinline__ DmaSrc dma_src(const GemmGroup& g, const TileRef& t, int w, int lane) {
+// NW waves; wave w stages rows (256 / NW) w .. (256 / NW)(w + 1) - 1 of the A
+// and the B tile, J = 32 / NW instructions of 8 rows each per operand.
+template <bool DUAL, int NW>
+__device__ __forceinline__ DmaSrc<32 / NW> dma_src(const GemmGroup& g, const TileRef& t, int w, int lane,
+                                                  int k_split) {
+    constexpr int J = 32 / NW;
     const uint32_t K2 = (uint32_t)g.K * 2;
-    DmaSrc s;
-    s.a = static_cast<const char*>(g.A) + (g.gather ? 0 : (int64_t)t.row0 * K2);
-    // dual: waves 0-3 stage gate rows n0 .. n0 + 127, waves 4-7 the same up rows
-    s.b = static_cast<const char*>(DUAL ? (w < 4 ? g.B0 : g.B1) : g.B0) +
-          ((int64_t)t.grp * g.N + t.n0) * K2;
+    const int64_t k0 = (int64_t)t.ks * k_split * 2;    // first byte of the tile's K range
+    DmaSrc<J> s;
+    s.a = static_cast<const char*>(g.A) + (g.gather ? 0 : (int64_t)t.row0 * K2) + k0;
+    // dual: the first half of the waves stage gate rows n0 .. n0 + 127, the
+    // second half the same up rows
+    s.b = static_cast<const char*>(DUAL ? (w < NW / 2 ? g.B0 : g.B1) : g.B0) +
+          ((int64_t)t.grp * g.N + t.n0) * K2 + k0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = w * 32 + j * 8 + (lane >> 3);
+    for (int j = 0; j < J; ++j) {
+        const int r = w * (256 / NW) + j * 8 + (lane >> 3);
         const int c = (lane & 7) ^ swz(r);
         const int rr = min(r, t.nrows - 1);
         const int src = g.gather ? g.gather[t.row0 + rr] / g.gather_div : rr;
@@ -418,11 +438,12 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3;
-    const int KT = g.K / kBK;          // even, >= 2
+    const int S = DUAL ? 1 : g.splitk;  // K ranges (single GEMM only)
+    const int KT = g.K / kBK / S;       // stages per tile: even, >= 2
 
     const int G = tile_prefix<BM>(g, s_tb, s_off, s_wsum);
     const int mt_total = s_tb[G];
-    const int TL = mt_total * tiles_n;
+    const int TL = mt_total * tiles_n * S;
     const int nslot = gridDim.x >> 3;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     // per-XCD range: a whole number of rounds, so every round is one window
@@ -500,8 +521,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
         __builtin_amdgcn_sched_barrier(0);                                                      \
     } while (0)
 
-    TileRef tr = tile_at<BM, BN>(s_tb, s_off, G, mt_total, tiles_n, wn_win, L);
-    DmaSrc cur = dma_src<DUAL>(g, tr, w, lane);
+    TileRef tr = split_tile_at<BM, BN>(s_tb, s_off, G, mt_total, tiles_n, wn_win, L);
+    DmaSrc<4> cur = dma_src<DUAL, 8>(g, tr, w, lane, KT * kBK);
     bf16x8_t fa0[4], fb0[2], fa1[4], fb1[2];
     // prologue: the first tile's stages 0 and 1; wait for this wave's stage 0
     MOE_DMA(sA0, sB0, cur, 0);
@@ -515,8 +536,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     for (;;) {
         const int Ln = L + nslot;
         const bool more = Ln < Lend;
-        const TileRef tn = tile_at<BM, BN>(s_tb, s_off, G, mt_total, tiles_n, wn_win, more ? Ln : L);
-        const DmaSrc nxt = dma_src<DUAL>(g, tn, w, lane);
+        const TileRef tn = split_tile_at<BM, BN>(s_tb, s_off, G, mt_total, tiles_n, wn_win, more ? Ln : L);
+        const DmaSrc<4> nxt = dma_src<DUAL, 8>(g, tn, w, lane, KT * kBK);
 
         f32x16_t acc[4][2];
 #pragma unroll
@@ -544,8 +565,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
                     v[q] = DUAL ? silu_f32(acc[i][0][q]) * acc[i][1][q] : acc[i][bo][q];
                 const int rb = wm * 128 + i * 32;
                 const int cb = DUAL ? wn * 32 : wn * 64 + bo * 32;
-                store_block_bf16(C + (int64_t)(tr.row0 + rb) * g.N + tr.n0 + cb, g.N, tr.nrows - rb, v,
-                                 lane);
+                store_block_bf16(C + tr.ks * g.part_stride + (int64_t)(tr.row0 + rb) * g.N + tr.n0 + cb, g.N,
+                                 tr.nrows - rb, v, lane);
             }
         }
         if (!more) break;
@@ -686,8 +707,26 @@ int64_t grouped_m_tiles_upper(int64_t rows, int G, int bm) {
     return (rows + (int64_t)G * (bm - 1)) / bm;
 }
 
+int choose_splitk(int64_t mt_expected, int N, int K) {
+    constexpr int kCUs = 256;                  // MI355X; only the choice depends on it
+    if (N % 256 || K % 128 || mt_expected <= 0) return 1;
+    const int64_t tiles = mt_expected * (N / 256);
+    int best = 1;
+    double best_cost = (double)((tiles + kCUs - 1) / kCUs);
+    for (int sk = 2; sk <= 8; sk *= 2) {
+        // at least 24 K stages of 64 per split, or the tile set-up dominates
+        if (K % (128 * sk) || K / (64 * sk) < 24) break;
+        // rounds of tiles, each 1/sk of a whole tile; a split must save 5 %
+        const double cost = (double)((tiles * sk + kCUs - 1) / kCUs) / sk;
+        if (cost < best_cost * 0.95) { best = sk; best_cost = cost; }
+    }
+    return best;
+}
+
 hipError_t launch_grouped_gemm(const GemmGroup& g, bool dual, bool bf16, hipStream_t s) {
     if (g.M == 0) return hipSuccess;
+    if (g.splitk != 1 && (dual || !bf16 || g.splitk < 1 || g.K % (128 * g.splitk) || g.N % 256))
+        return hipErrorInvalidValue;
     if (!bf16) return dual ? launch_f32<true>(g, s) : launch_f32<false>(g, s);
     // The persistent kernel takes K stages in pairs (K % 128 == 0) and
     // addresses gathered A rows with 32-bit byte offsets from the start of A.
@@ -695,6 +734,7 @@ hipError_t launch_grouped_gemm(const GemmGroup& g, bool dual, bool bf16, hipStre
     const bool fits = g.K % 128 == 0 && a_rows * g.K * 2 < (int64_t(1) << 32);
     if (fits && dual && g.N % 128 == 0) return launch_bf16_persistent<true>(g, s);
     if (fits && !dual && g.N % 256 == 0) return launch_bf16_persistent<false>(g, s);
+    if (g.splitk != 1) return hipErrorInvalidValue;
     if (g.N % 128 == 0) return dual ? launch_bf16<128, 128, true>(g, s) : launch_bf16<128, 128, false>(g, s);
     return dual ? launch_bf16<128, 64, true>(g, s) : launch_bf16<128, 64, false>(g, s);
 }

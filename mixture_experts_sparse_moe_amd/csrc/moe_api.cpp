@@ -3,6 +3,7 @@
 // the first launch; nothing here synchronises or copies to the host.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstddef>
 #include <cstdint>
 
@@ -40,6 +41,25 @@ int validate_cfg(const moe_config* c) {
 
 size_t elem(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 
+// K splits of the down projections inside moe_forward (moe_expert_ffn never
+// splits: its expert_out is the finished product).  The routed GEMM has about
+// P / 256 + min(E, P) / 2 M tiles (each expert's last tile is partial); the
+// shared one T / 256.  Only bf16 layers split.
+struct Splits {
+    int routed, shared;
+};
+
+Splits splits(const moe_config* c) {
+    Splits sp{1, 1};
+    if (c->dtype != MOE_BF16 || c->num_tokens == 0) return sp;
+    const int64_t P = (int64_t)c->num_tokens * c->top_k, E = c->num_experts;
+    const int64_t mt_upper = grouped_m_tiles_upper(P, (int)E, 256);
+    const int64_t mt_exp = std::min<int64_t>(mt_upper, (P + 255) / 256 + std::min<int64_t>(E, P) / 2);
+    sp.routed = choose_splitk(mt_exp, c->d_model, c->d_ff);
+    if (c->num_shared) sp.shared = choose_splitk(((int64_t)c->num_tokens + 255) / 256, c->d_model, c->d_ff_shared);
+    return sp;
+}
+
 // Device workspace layout.  Every region starts on a 256-byte boundary.
 struct Layout {
     size_t ids, wts, counts, offsets, chunk, sorted, pos, H, O, Hs, S, total;
@@ -63,8 +83,9 @@ Layout layout(const moe_config* c) {
     L.offsets = take((E + 1) * sizeof(int32_t));
     L.sorted = take(P * sizeof(int32_t));
     L.pos = take(P * sizeof(int32_t));
-    L.O = take(P * c->d_model * elem(c));
-    L.S = take(c->num_shared ? T * c->d_model * elem(c) : 0);
+    const Splits sp = splits(c);
+    L.O = take(sp.routed * P * c->d_model * elem(c));
+    L.S = take(c->num_shared ? sp.shared * T * c->d_model * elem(c) : 0);
     L.total = o;
     L.dispatch_need = align_up(nchunks * E * sizeof(int32_t));
     return L;
@@ -112,10 +133,11 @@ int mark(void* const* ev, int i, hipStream_t s) {
     return MOE_OK;
 }
 
+// out / shared_out receive sp.routed / sp.shared slices of [P, d] / [T, d].
 int run_ffn(const moe_config* c, const void* x, const int32_t* sorted, const int32_t* offsets,
             const void* wg, const void* wu, const void* wd, const void* sg, const void* su,
             const void* sd, void* out, void* shared_out, void* H, void* Hs, hipStream_t s,
-            void* const* ev = nullptr) {
+            void* const* ev = nullptr, Splits sp = Splits{1, 1}) {
     const bool bf16 = c->dtype == MOE_BF16;
     const int P = c->num_tokens * c->top_k;
     if (P > 0) {
@@ -124,7 +146,7 @@ int run_ffn(const moe_config* c, const void* x, const int32_t* sorted, const int
         MOE_HIP(launch_grouped_gemm(up, true, bf16, s));
         MOE_TRY(mark(ev, 2, s));
         GemmGroup down{H, nullptr, 1, offsets, c->num_experts, P, wd, nullptr, out, c->d_model,
-                       c->d_ff};
+                       c->d_ff, sp.routed, (int64_t)P * c->d_model};
         MOE_HIP(launch_grouped_gemm(down, false, bf16, s));
         MOE_TRY(mark(ev, 3, s));
     }
@@ -134,7 +156,7 @@ int run_ffn(const moe_config* c, const void* x, const int32_t* sorted, const int
         MOE_HIP(launch_grouped_gemm(up, true, bf16, s));
         MOE_TRY(mark(ev, 4, s));
         GemmGroup down{Hs, nullptr, 1, nullptr, 1, c->num_tokens, sd, nullptr, shared_out,
-                       c->d_model, c->d_ff_shared};
+                       c->d_model, c->d_ff_shared, sp.shared, (int64_t)c->num_tokens * c->d_model};
         MOE_HIP(launch_grouped_gemm(down, false, bf16, s));
         MOE_TRY(mark(ev, 5, s));
     } else {
@@ -145,8 +167,10 @@ int run_ffn(const moe_config* c, const void* x, const int32_t* sorted, const int
 }
 
 int run_combine(const moe_config* c, const void* out, const float* wts, const int32_t* pos,
-                const void* shared_out, void* y, hipStream_t s) {
-    CombineArgs a{out, wts, pos, shared_out, y, c->num_tokens, c->d_model, c->top_k};
+                const void* shared_out, void* y, hipStream_t s, Splits sp = Splits{1, 1}) {
+    const int64_t P = (int64_t)c->num_tokens * c->top_k;
+    CombineArgs a{out, wts, pos, shared_out, y, c->num_tokens, c->d_model, c->top_k,
+                  sp.routed, P * c->d_model, sp.shared, (int64_t)c->num_tokens * c->d_model};
     MOE_HIP(launch_combine(a, c->dtype == MOE_BF16, s));
     return MOE_OK;
 }
@@ -297,9 +321,10 @@ int moe_forward_staged(const moe_config* cfg, const void* x, const void* w_route
     MOE_TRY(mark(ev, 1, s));
     void* O = at<void>(ws, L.O);
     void* S = cfg->num_shared ? at<void>(ws, L.S) : nullptr;
+    const Splits sp = splits(cfg);
     MOE_TRY(run_ffn(cfg, x, sorted, offsets, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, O, S,
-                    at<void>(ws, L.H), at<void>(ws, L.Hs), s, ev));
-    MOE_TRY(run_combine(cfg, O, wts, pos, S, y, s));
+                    at<void>(ws, L.H), at<void>(ws, L.Hs), s, ev, sp));
+    MOE_TRY(run_combine(cfg, O, wts, pos, S, y, s, sp));
     return mark(ev, 6, s);
 }
 

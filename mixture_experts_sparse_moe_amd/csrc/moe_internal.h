@@ -49,11 +49,19 @@ struct GemmGroup {
     int M;                  // rows when offsets == nullptr; upper bound otherwise
     const void* B0;         // [G, N, K]   (gate weights, or down weights)
     const void* B1;         // [G, N, K]   (up weights; dual mode only)
-    void* C;                // [rows, N]
+    void* C;                // [rows, N]; split K: [splitk][part_stride]
     int N, K;
+    int splitk = 1;         // single bf16 only: K cut into splitk ranges, one C slice each
+    int64_t part_stride = 0;// elements between C slices when splitk > 1
 };
-// Dual mode: C = silu(A B0^T) * (A B1^T).  Single: C = A B0^T.
+// Dual mode: C = silu(A B0^T) * (A B1^T).  Single: C = A B0^T, or with
+// splitk > 1 the partial products of the K ranges, C slice s = A[:, Ks] B0[:, Ks]^T.
 hipError_t launch_grouped_gemm(const GemmGroup& g, bool dual, bool bf16, hipStream_t s);
+// K split for a single bf16 GEMM with about mt_expected M tiles of 256 rows
+// and N / 256 N tiles: the split in {1, 2, 4, 8} (K % (128 split) == 0, at
+// least 24 stages of 64 per split) whose rounds of tiles over 256 CUs waste
+// the least.  Depends only on its arguments.
+int choose_splitk(int64_t mt_expected, int N, int K);
 // Upper bound of M-tiles over all groups for tile height bm.
 int64_t grouped_m_tiles_upper(int64_t rows, int G, int bm);
 
@@ -65,6 +73,10 @@ struct CombineArgs {
     const void* shared;     // [T, d] or nullptr
     void* y;                // [T, d]
     int T, d, k;
+    int splitk = 1;         // bf16: expert_out holds splitk slices, summed in slice order
+    int64_t part_stride = 0;// elements between expert_out slices
+    int shared_splitk = 1;  // the same for the shared rows
+    int64_t shared_stride = 0;
 };
 hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t s);
 

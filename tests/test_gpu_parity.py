@@ -65,9 +65,10 @@ def check_layer(sh, inp, sample=None, check_expert_out=True):
     ref = oracle_routing(inp, sh)
     gids = to_host(st["ids"])
     exempt = check_routing(gids, ref, sh.k)
-    # the whole-layer call equals the step-by-step calls bit for bit
+    # the whole-layer call routes exactly like the step-by-step calls; its y
+    # is checked against the oracle below (moe_forward may run the down
+    # projection in K ranges, which rounds differently from moe_expert_ffn)
     np.testing.assert_array_equal(to_host(fw["ids"]), gids)
-    np.testing.assert_array_equal(to_host(fw["y"]), to_host(st["y"]))
     np.testing.assert_array_equal(to_host(fw["weights"]), to_host(st["weights"]))
     # gates for the GPU's ids
     rf = oracle.route(ref["logits"], sh.k, sh.score_fn, sh.renormalize, forced_ids=gids)
@@ -104,7 +105,8 @@ def check_layer(sh, inp, sample=None, check_expert_out=True):
     toks = np.arange(sh.T) if sample is None else np.asarray(sample)
     r = oracle.forward_tokens(inp, sh.k, toks, sh.score_fn, sh.renormalize, forced_ids=gids[toks])
     y = widen(to_host(st["y"]))[toks]
-    rel = assert_close(y, r["y"], tau, "y")
+    rel = assert_close(y, r["y"], tau, "y of the step-by-step calls")
+    rel = max(rel, assert_close(widen(to_host(fw["y"]))[toks], r["y"], tau, "y of moe_forward"))
     say(f"[ok] max|err|/max|y| = {rel:.3e}, near-tie tokens {exempt.tolist()}, "
         f"counts max/mean {d['counts'].max() / max(d['counts'].mean(), 1e-9):.2f}")
     return dict(rel=rel, exempt=exempt, counts=d["counts"])
