@@ -330,7 +330,12 @@ __device__ __forceinline__ TileRef split_tile_at(const int* s_tb, const int* s_o
     const int per_split = mt_total * tiles_n;
     const int ks = L / per_split;
     TileRef t = tile_at<BM, BN>(s_tb, s_off, G, mt_total, tiles_n, wn_win, L - ks * per_split);
-    t.ks = ks;
+    // the same in every lane (read from LDS at uniform addresses): scalar registers
+    t.grp = __builtin_amdgcn_readfirstlane(t.grp);
+    t.row0 = __builtin_amdgcn_readfirstlane(t.row0);
+    t.nrows = __builtin_amdgcn_readfirstlane(t.nrows);
+    t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+    t.ks = __builtin_amdgcn_readfirstlane(ks);
     return t;
 }
 
@@ -348,9 +353,29 @@ struct DmaSrc {
 
 // NW waves; wave w stages rows (256 / NW) w .. (256 / NW)(w + 1) - 1 of the A
 // and the B tile, J = 32 / NW instructions of 8 rows each per operand.
+// gather_rows() issues the loads of the gathered pair ids of those rows (rows
+// past the tile's end repeat its last row); dma_src() turns them into the
+// tile's DMA sources.  Kept apart so the loads can be in flight long before
+// their values are needed.
+template <int NW>
+__device__ __forceinline__ void gather_rows(const GemmGroup& g, const TileRef& t, int w, int lane,
+                                            int* src) {
+    constexpr int J = 32 / NW;
+    if (g.gather) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int r = w * (256 / NW) + j * 8 + (lane >> 3);
+            src[j] = g.gather[t.row0 + min(r, t.nrows - 1)];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j) src[j] = min(w * (256 / NW) + j * 8 + (lane >> 3), t.nrows - 1);
+    }
+}
+
 template <bool DUAL, int NW>
-__device__ __forceinline__ DmaSrc<32 / NW> dma_src(const GemmGroup& g, const TileRef& t, int w, int lane,
-                                                  int k_split) {
+__device__ __forceinline__ DmaSrc<32 / NW> dma_src(const GemmGroup& g, const TileRef& t, const int* src,
+                                                  int w, int lane, int k_split) {
     constexpr int J = 32 / NW;
     const uint32_t K2 = (uint32_t)g.K * 2;
     const int64_t k0 = (int64_t)t.ks * k_split * 2;    // first byte of the tile's K range
@@ -364,9 +389,8 @@ __device__ __forceinline__ DmaSrc<32 / NW> dma_src(const GemmGroup& g, const Til
     for (int j = 0; j < J; ++j) {
         const int r = w * (256 / NW) + j * 8 + (lane >> 3);
         const int c = (lane & 7) ^ swz(r);
-        const int rr = min(r, t.nrows - 1);
-        const int src = g.gather ? g.gather[t.row0 + rr] / g.gather_div : rr;
-        s.ao[j] = (uint32_t)src * K2 + c * 16;
+        const int a_row = g.gather ? src[j] / g.gather_div : src[j];   // token row, or tile row
+        s.ao[j] = (uint32_t)a_row * K2 + c * 16;
         s.bo[j] = (uint32_t)(DUAL ? (r & 127) : r) * K2 + c * 16;
     }
     return s;
@@ -436,7 +460,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     __shared__ int s_wsum[8];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w >> 2, wn = w & 3;
     const int S = DUAL ? 1 : g.splitk;  // K ranges (single GEMM only)
     const int KT = g.K / kBK / S;       // stages per tile: even, >= 2
@@ -460,6 +484,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 #pragma unroll
     for (int b = 0; b < 2; ++b) b_row[b] = DUAL ? b * 128 + wn * 32 + r32 : wn * 64 + b * 32 + r32;
 
+// Refill of a stage buffer: every A and B instruction, unconditionally (rows
+// past the tile's end repeat its last row).  Skipping A instructions of empty
+// rows would need control flow among the DMA instructions, after which the
+// compiler waits for them before the next fragment reads.
 #define MOE_DMA(sA_, sB_, src_, kt_)                                                            \
     do {                                                                                        \
         const char* ab_ = (src_).a + (kt_) * (kBK * 2);                                         \
@@ -471,73 +499,100 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
                                              (lds_ptr_t)((sB_) + (w * 32 + j * 8) * kBK), 16, 0, 0); \
         }                                                                                       \
     } while (0)
-#define MOE_LOAD_FRAGS(sA_, sB_, s_, af_, bf_)                                                  \
+// Fragments of step s_ for the first NA_ row blocks (and B, if NA_ > 0).
+#define MOE_LOAD_FRAGS(sA_, sB_, s_, af_, bf_, NA_)                                             \
     do {                                                                                        \
         const int c_ = 2 * (s_) + half;                                                         \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) af_[i] = as_bf16x8(                       \
+        _Pragma("unroll") for (int i = 0; i < (NA_); ++i) af_[i] = as_bf16x8(                   \
             *reinterpret_cast<const uint4*>((sA_) + a_row[i] * kBK + ((c_ ^ swz(a_row[i])) * 8))); \
-        _Pragma("unroll") for (int b = 0; b < 2; ++b) bf_[b] = as_bf16x8(                       \
+        _Pragma("unroll") for (int b = 0; b < ((NA_) ? 2 : 0); ++b) bf_[b] = as_bf16x8(         \
             *reinterpret_cast<const uint4*>((sB_) + b_row[b] * kBK + ((c_ ^ swz(b_row[b])) * 8))); \
     } while (0)
-#define MOE_MFMAS(af_, bf_)                                                                     \
+#define MOE_MFMAS(af_, bf_, NA_)                                                                \
     do {                                                                                        \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                           \
+        _Pragma("unroll") for (int i = 0; i < (NA_); ++i)                                       \
             _Pragma("unroll") for (int b = 0; b < 2; ++b) acc[i][b] =                           \
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_[i], bf_[b], acc[i][b], 0, 0, 0);    \
     } while (0)
-// 8 MFMAs with the 6 fragment reads of the following step between them
-#define MOE_INTERLEAVE()                                                                        \
+// The MFMAs of a step with the fragment reads of the following step between
+// them: 8 MFMAs / 6 reads for 4 row blocks, 4 / 4 for 2.
+#define MOE_INTERLEAVE(NA_)                                                                     \
     do {                                                                                        \
-        _Pragma("unroll") for (int i_ = 0; i_ < 6; ++i_) {                                      \
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                  \
+        if ((NA_) == 4) {                                                                       \
+            _Pragma("unroll") for (int i_ = 0; i_ < 6; ++i_) {                                  \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                              \
+            }                                                                                   \
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                  \
+        } else if ((NA_) == 2) {                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                  \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                              \
+            }                                                                                   \
         }                                                                                       \
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                      \
     } while (0)
-// One K stage from buffer (sAc, sBc); afterwards that buffer is refilled with
-// stage kd_ of src_ (if fetch_) and the first fragments of (sAn, sBn) are read.
-#define MOE_STAGE(sAc, sBc, sAn, sBn, src_, kd_, fetch_)                                        \
+// One K stage from buffer (sAc, sBc) for NA_ row blocks; after the barrier
+// that buffer is refilled with stage kd_ of src_ (if fetch_) and the first
+// fragments of (sAn, sBn) are read for NN_ row blocks (at a tile boundary,
+// all 4: the next tile may have more live rows).
+#define MOE_STAGE(NA_, NN_, sAc, sBc, sAn, sBn, src_, kd_, fetch_)                              \
     do {                                                                                        \
-        MOE_LOAD_FRAGS(sAc, sBc, 1, fa1, fb1);                                                  \
-        MOE_MFMAS(fa0, fb0);                                                                    \
-        MOE_INTERLEAVE();                                                                       \
+        MOE_LOAD_FRAGS(sAc, sBc, 1, fa1, fb1, NA_);                                             \
+        MOE_MFMAS(fa0, fb0, NA_);                                                               \
+        MOE_INTERLEAVE(NA_);                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                      \
-        MOE_LOAD_FRAGS(sAc, sBc, 2, fa0, fb0);                                                  \
-        MOE_MFMAS(fa1, fb1);                                                                    \
-        MOE_INTERLEAVE();                                                                       \
+        MOE_LOAD_FRAGS(sAc, sBc, 2, fa0, fb0, NA_);                                             \
+        MOE_MFMAS(fa1, fb1, NA_);                                                               \
+        MOE_INTERLEAVE(NA_);                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                      \
-        MOE_LOAD_FRAGS(sAc, sBc, 3, fa1, fb1);                                                  \
-        MOE_MFMAS(fa0, fb0);                                                                    \
-        MOE_INTERLEAVE();                                                                       \
+        MOE_LOAD_FRAGS(sAc, sBc, 3, fa1, fb1, NA_);                                             \
+        MOE_MFMAS(fa0, fb0, NA_);                                                               \
+        MOE_INTERLEAVE(NA_);                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                      \
         __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);                                              \
         __builtin_amdgcn_s_barrier();                                                           \
         __builtin_amdgcn_sched_barrier(0);                                                      \
         if (fetch_) MOE_DMA(sAc, sBc, src_, kd_);                                               \
         __builtin_amdgcn_sched_barrier(0);                                                      \
-        MOE_LOAD_FRAGS(sAn, sBn, 0, fa0, fb0);                                                  \
-        MOE_MFMAS(fa1, fb1);                                                                    \
-        MOE_INTERLEAVE();                                                                       \
+        MOE_LOAD_FRAGS(sAn, sBn, 0, fa0, fb0, NN_);                                             \
+        MOE_MFMAS(fa1, fb1, NA_);                                                               \
+        MOE_INTERLEAVE((NN_) < (NA_) ? (NN_) : (NA_));                                          \
         __builtin_amdgcn_sched_barrier(0);                                                      \
+    } while (0)
+// The K stages of one tile for a wave with NA_ live row blocks.
+#define MOE_KLOOP(NA_)                                                                          \
+    do {                                                                                        \
+        for (int kt = 0; kt < KT - 2; kt += 2) {                                                \
+            MOE_STAGE(NA_, NA_, sA0, sB0, sA1, sB1, cur, kt + 2, true);                         \
+            MOE_STAGE(NA_, NA_, sA1, sB1, sA0, sB0, cur, kt + 3, true);                         \
+        }                                                                                       \
+        nxt = dma_src<DUAL, 8>(g, tn, gsrc, w, lane, KT * kBK);                                  \
+        MOE_STAGE(NA_, NA_, sA0, sB0, sA1, sB1, nxt, 0, more);                                  \
+        MOE_STAGE(NA_, 4, sA1, sB1, sA0, sB0, nxt, 1, more);                                    \
     } while (0)
 
     TileRef tr = split_tile_at<BM, BN>(s_tb, s_off, G, mt_total, tiles_n, wn_win, L);
-    DmaSrc<4> cur = dma_src<DUAL, 8>(g, tr, w, lane, KT * kBK);
+    int gsrc[4];
+    gather_rows<8>(g, tr, w, lane, gsrc);
+    DmaSrc<4> cur = dma_src<DUAL, 8>(g, tr, gsrc, w, lane, KT * kBK);
     bf16x8_t fa0[4], fb0[2], fa1[4], fb1[2];
-    // prologue: the first tile's stages 0 and 1; wait for this wave's stage 0
+    // prologue: the first tile's stages 0 and 1
     MOE_DMA(sA0, sB0, cur, 0);
     MOE_DMA(sA1, sB1, cur, 1);
-    __builtin_amdgcn_s_waitcnt(kWaitVm8);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    MOE_LOAD_FRAGS(sA0, sB0, 0, fa0, fb0);
+    MOE_LOAD_FRAGS(sA0, sB0, 0, fa0, fb0, 4);
 
     uint16_t* C = static_cast<uint16_t*>(g.C);
     for (;;) {
         const int Ln = L + nslot;
         const bool more = Ln < Lend;
         const TileRef tn = split_tile_at<BM, BN>(s_tb, s_off, G, mt_total, tiles_n, wn_win, more ? Ln : L);
-        const DmaSrc<4> nxt = dma_src<DUAL, 8>(g, tn, w, lane, KT * kBK);
+        // the next tile's gathered rows load now; their values are used after
+        // the K loop, whose stage waits have long covered them
+        gather_rows<8>(g, tn, w, lane, gsrc);
+        DmaSrc<4> nxt;
 
         f32x16_t acc[4][2];
 #pragma unroll
@@ -547,23 +602,23 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-        for (int kt = 0; kt < KT - 2; kt += 2) {
-            MOE_STAGE(sA0, sB0, sA1, sB1, cur, kt + 2, true);
-            MOE_STAGE(sA1, sB1, sA0, sB0, cur, kt + 3, true);
-        }
-        MOE_STAGE(sA0, sB0, sA1, sB1, nxt, 0, more);
-        MOE_STAGE(sA1, sB1, sA0, sB0, nxt, 1, more);
+        // live row blocks of this wave: 4 (3 or 4 with rows), 2 (1 or 2) or 0
+        const int blocks = min(4, max(0, (tr.nrows - wm * 128 + 31) >> 5));
+        if (blocks > 2) MOE_KLOOP(4);
+        else if (blocks > 0) MOE_KLOOP(2);
+        else MOE_KLOOP(0);
 
         // epilogue: the next tile's first two stages are in flight meanwhile
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            const int rb = wm * 128 + i * 32;
+            if (rb >= tr.nrows) break;
 #pragma unroll
             for (int bo = 0; bo < (DUAL ? 1 : 2); ++bo) {
                 float v[16];
 #pragma unroll
                 for (int q = 0; q < 16; ++q)
                     v[q] = DUAL ? silu_f32(acc[i][0][q]) * acc[i][1][q] : acc[i][bo][q];
-                const int rb = wm * 128 + i * 32;
                 const int cb = DUAL ? wn * 32 : wn * 64 + bo * 32;
                 store_block_bf16(C + tr.ks * g.part_stride + (int64_t)(tr.row0 + rb) * g.N + tr.n0 + cb, g.N,
                                  tr.nrows - rb, v, lane);
@@ -579,6 +634,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 #undef MOE_MFMAS
 #undef MOE_INTERLEAVE
 #undef MOE_STAGE
+#undef MOE_KLOOP
 }
 
 // fp32 grouped GEMM: 64x64 tiles, BK 16, 4x4 outputs per thread.
