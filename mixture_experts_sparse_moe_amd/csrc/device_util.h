@@ -37,4 +37,16 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// LDS destination operand of the direct-to-LDS loads (global_load_lds).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Swizzle of LDS rows of 128 bytes (8 chunks of 16 B): chunk c of row r sits
+// at c ^ swz(r), so 16-byte reads of one chunk in 32 consecutive rows hit
+// distinct banks.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]) waiting for vmcnt <= n only.
+constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 }  // namespace moe

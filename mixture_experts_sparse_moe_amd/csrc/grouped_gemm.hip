@@ -33,7 +33,6 @@ constexpr int kBK = 64;
 constexpr int kThreads = 256;
 constexpr int kWMW = 4;   // M tiles per window (share one weight panel)
 
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // Block-wide: map flattened M tile `mt` to (group, first row, rows).  Returns
 // false if mt is past the last real tile.
@@ -243,13 +242,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmGroup g, int ti
         }
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 // ---- persistent 256 x 256 kernel ---------------------------------------------
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
 // [6:4], lgkmcnt [11:8]).  The builtin, unlike inline asm, is seen by the
 // compiler's own wait insertion, so it adds no waits of its own after these.
-constexpr int kWaitVm8 = 8 | (7 << 4) | (15 << 8);      // vmcnt(8)
 constexpr int kWaitVm0Lgkm0 = (7 << 4);                 // vmcnt(0) lgkmcnt(0)
 
 // Per-workgroup tile table in LDS: s_tb[e] = M tiles (of BM rows) before

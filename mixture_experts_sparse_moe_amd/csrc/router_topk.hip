@@ -15,12 +15,14 @@
 // Workgroup = 256 threads (4 waves) owns 32 tokens and all E <= 256 experts.
 // bf16: the logits tile [32, E] is built with v_mfma_f32_32x32x16_bf16 (bf16
 // products are exact in fp32, so this is an fp32-accumulated dot product).
-// Each lane streams 64 contiguous bytes of its row per 64-wide K chunk: the
-// MFMA's 16 K slots in step s take actual k = 32*half + 8*s + i, a
-// permutation of the chunk shared by both operands, so the contraction is
-// unchanged while every load is a full 16-byte vector.  When E needs fewer
-// than four 32-expert blocks, the K chunks are split over waves and the
-// partial tiles are added in a fixed order (deterministic).
+// The K dimension streams through LDS in chunks of 64: the chunk of the 32 x
+// rows and of the E weight rows (E padded to 32 * NBLK, NBLK in {1, 2, 4, 8})
+// is fetched by direct-to-LDS DMA into one of NST stage buffers, NST - 1
+// chunks ahead of the MFMAs, one barrier per chunk.  Rows are 128 bytes with
+// 16-byte chunks XOR-swizzled.  With NBLK >= 4 each wave owns NBLK / 4
+// expert blocks; with fewer blocks 4 / NBLK waves share a block and split
+// the four 16-wide K steps of a chunk, their partial tiles added in a fixed
+// order (deterministic).
 // fp32: plain FMA dot products.
 // Top-k: one wave per token, 64-bit keys (orderable logit bits, inverted
 // expert index) reduced with a butterfly; k rounds.
@@ -33,10 +35,9 @@ namespace {
 
 constexpr int kBT = 32;          // tokens per workgroup
 constexpr int kMaxE = 256;
-constexpr int kPartStride = 97;  // row stride of a partial tile (E <= 96 when split)
 constexpr int kLogitStride = kMaxE + 1;
-constexpr int kLdsFloats = (4 * kBT * kPartStride > kBT * kLogitStride) ? 4 * kBT * kPartStride
-                                                                         : kBT * kLogitStride;
+constexpr int kLogitFloats = kBT * kLogitStride;
+constexpr int kChunk = 64;       // K elements per LDS stage
 
 __device__ __forceinline__ uint32_t ord_bits(float f) {
     f = f + 0.0f;  // -0 -> +0: equal logits compare equal
@@ -59,110 +60,144 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
     return v;
 }
 
-// Logits of 32 tokens x all experts into lds (bf16 inputs, MFMA).
-__device__ void logits_bf16(const RouteArgs& a, int t0, float* lds) {
-    const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    const int nb = (a.E + 31) / 32;
-    const int KS = nb >= 4 ? 1 : 4 / nb;    // K slices
-    const int WPS = 4 / KS;                 // waves per slice
-    const int ksl = w % KS, wsub = w / KS;
-    const int nchunks = a.d / 64;
+// Logits of 32 tokens x all experts (E <= 32 NBLK) into lds[32][kLogitStride]
+// (bf16 inputs, MFMA, LDS-staged K chunks).
+template <int NBLK>
+struct RouterStages {
+    static constexpr int NST = NBLK >= 8 ? 3 : 4;        // stage buffers
+    static constexpr int XS = kBT * kChunk;               // x stage (elements)
+    static constexpr int WS = NBLK * 32 * kChunk;         // weight stage (elements)
+};
+
+template <int NBLK>
+__device__ __forceinline__ void logits_bf16(const RouteArgs& a, int t0, float* lds, uint16_t* sX0,
+                                            uint16_t* sX1, uint16_t* sX2, uint16_t* sX3, uint16_t* sW0,
+                                            uint16_t* sW1, uint16_t* sW2, uint16_t* sW3) {
+    constexpr int NST = RouterStages<NBLK>::NST;
+    constexpr int KS = NBLK >= 4 ? 1 : 4 / NBLK;          // waves sharing an expert block
+    constexpr int BPW = NBLK >= 4 ? NBLK / 4 : 1;         // expert blocks per wave
+    constexpr int P = 1 + NBLK;                           // DMA instructions per wave per stage
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, r32 = lane & 31;
+    const int nchunks = a.d / kChunk;
+    const int64_t rowb = (int64_t)a.d * 2;               // bytes per row
 
-    const uint16_t* X = static_cast<const uint16_t*>(a.x);
-    const uint16_t* W = static_cast<const uint16_t*>(a.w);
-    int tok = t0 + r32;
-    if (tok >= a.T) tok = a.T - 1;          // clamp; rows past T are discarded
-    const uint4* xrow = reinterpret_cast<const uint4*>(X + (int64_t)tok * a.d + 32 * half);
-
-    // this wave's expert blocks: wsub and wsub + WPS (nb <= 8)
-    const int blk[2] = {wsub, wsub + WPS};
-    const int nmy = (blk[0] < nb) + (blk[1] < nb);
-    const uint4* wrow[2];
-    bool wvalid[2];
+    // DMA instruction j of wave w fills 8 rows of the stage, 8 (w + 4 j) ..:
+    // j = 0 the x rows 8 w .. 8 w + 7, j >= 1 weight rows 8 (w + 4 j - 4) ..
+    // Lane l fills physical chunk l % 8 of row l / 8 with logical chunk
+    // (l % 8) ^ swz(row).  Rows past T or E repeat the last one.
+    const char* src[P];
+    {
+        const int rx = 8 * w + (lane >> 3);
+        const int tok = min(t0 + rx, a.T - 1);
+        src[0] = static_cast<const char*>(a.x) + tok * rowb + (((lane & 7) ^ swz(rx)) * 16);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        int e = blk[i] * 32 + r32;
-        wvalid[i] = (i < nmy) && (e < a.E);
-        if (e >= a.E) e = a.E - 1;
-        wrow[i] = reinterpret_cast<const uint4*>(W + (int64_t)e * a.d + 32 * half);
+        for (int j = 1; j < P; ++j) {
+            const int rw = 8 * (w + 4 * j - 4) + (lane >> 3);
+            const int e = min(rw, a.E - 1);
+            src[j] = static_cast<const char*>(a.w) + e * rowb + (((lane & 7) ^ swz(rw)) * 16);
+        }
     }
+#define MOE_R_DMA(sX_, sW_, st_)                                                                \
+    do {                                                                                        \
+        const int64_t ko_ = (int64_t)min((st_), nchunks - 1) * (kChunk * 2);                    \
+        __builtin_amdgcn_global_load_lds((const void*)(src[0] + ko_),                           \
+                                         (lds_ptr_t)((sX_) + 8 * w * kChunk), 16, 0, 0);        \
+        _Pragma("unroll") for (int j = 1; j < P; ++j)                                           \
+            __builtin_amdgcn_global_load_lds((const void*)(src[j] + ko_),                       \
+                                             (lds_ptr_t)((sW_) + 8 * (w + 4 * j - 4) * kChunk), 16, 0, 0); \
+    } while (0)
 
-    f32x16_t acc[2];
+    // this wave's expert blocks and K steps
+    const int b0 = NBLK >= 4 ? w * BPW : w % NBLK;
+    const int s0 = NBLK >= 4 ? 0 : (w / NBLK) * (4 / KS);
+    constexpr int NS = 4 / KS;                            // K steps per chunk for this wave
+    f32x16_t acc[BPW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < BPW; ++i)
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
 
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
-    for (int c = ksl; c < nchunks; c += KS) {
-        uint4 av[4], bv[2][4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) av[s] = xrow[c * 8 + s];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) bv[i][s] = (i < nmy && wvalid[i]) ? wrow[i][c * 8 + s] : z4;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                if (i < nmy)
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(av[s]),
-                                                                     as_bf16x8(bv[i][s]), acc[i],
-                                                                     0, 0, 0);
+#define MOE_R_MFMA(sX_, sW_)                                                                    \
+    do {                                                                                        \
+        _Pragma("unroll") for (int s_ = 0; s_ < NS; ++s_) {                                     \
+            const int c_ = 2 * (s0 + s_) + half;                                                \
+            const bf16x8_t xa_ = as_bf16x8(*reinterpret_cast<const uint4*>(                     \
+                (sX_) + r32 * kChunk + ((c_ ^ swz(r32)) * 8)));                                 \
+            _Pragma("unroll") for (int i_ = 0; i_ < BPW; ++i_) {                                \
+                const int r_ = (b0 + i_) * 32 + r32;                                            \
+                const bf16x8_t wb_ = as_bf16x8(*reinterpret_cast<const uint4*>(                 \
+                    (sW_) + r_ * kChunk + ((c_ ^ swz(r_)) * 8)));                               \
+                acc[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa_, wb_, acc[i_], 0, 0, 0);  \
+            }                                                                                   \
+        }                                                                                       \
+    } while (0)
+// chunk st_ in buffer (sX_, sW_); the buffer of chunk st_ - 1 is refilled
+// with chunk st_ - 1 + NST once every wave is past this barrier
+#define MOE_R_STAGE(sX_, sW_, sXp_, sWp_, st_)                                                  \
+    do {                                                                                        \
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt((NST - 2) * P));                                  \
+        __builtin_amdgcn_s_barrier();                                                           \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        MOE_R_DMA(sXp_, sWp_, (st_) - 1 + NST);                                                 \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        if ((st_) < nchunks) MOE_R_MFMA(sX_, sW_);                                              \
+    } while (0)
+
+    MOE_R_DMA(sX0, sW0, 0);
+    MOE_R_DMA(sX1, sW1, 1);
+    MOE_R_DMA(sX2, sW2, 2);
+    if (NST > 3) MOE_R_DMA(sX3, sW3, 3);
+    for (int c = 0; c < nchunks; c += NST) {
+        if (NST > 3) {
+            MOE_R_STAGE(sX0, sW0, sX3, sW3, c);
+            MOE_R_STAGE(sX1, sW1, sX0, sW0, c + 1);
+            MOE_R_STAGE(sX2, sW2, sX1, sW1, c + 2);
+            MOE_R_STAGE(sX3, sW3, sX2, sW2, c + 3);
+        } else {
+            MOE_R_STAGE(sX0, sW0, sX2, sW2, c);
+            MOE_R_STAGE(sX1, sW1, sX0, sW0, c + 1);
+            MOE_R_STAGE(sX2, sW2, sX1, sW1, c + 2);
         }
     }
-    // D element (blk4, r): token row 8*blk4 + 4*half + r, expert col b*32 + r32
+#undef MOE_R_DMA
+#undef MOE_R_MFMA
+#undef MOE_R_STAGE
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));     // the repeated chunks past the end
+
+    // D element j of block i: token row 8 (j / 4) + 4 half + j % 4, expert r32
     if (KS == 1) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            if (i >= nmy) continue;
-            int e = blk[i] * 32 + r32;
+        for (int i = 0; i < BPW; ++i) {
+            const int e = (b0 + i) * 32 + r32;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                int row = 8 * (j >> 2) + 4 * half + (j & 3);
-                lds[row * kLogitStride + e] = acc[i][j];
-            }
+            for (int j = 0; j < 16; ++j) lds[(8 * (j >> 2) + 4 * half + (j & 3)) * kLogitStride + e] = acc[i][j];
         }
         __syncthreads();
     } else {
-        float* part = lds + ksl * kBT * kPartStride;
+        // partial tiles [KS][32][32 NBLK], then their sum in slice order
+        constexpr int EP = 32 * NBLK;
+        const int q = w / NBLK;
+        const int e = b0 * 32 + r32;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            if (i >= nmy) continue;
-            int e = blk[i] * 32 + r32;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                int row = 8 * (j >> 2) + 4 * half + (j & 3);
-                part[row * kPartStride + e] = acc[i][j];
-            }
-        }
+        for (int j = 0; j < 16; ++j) lds[q * kBT * EP + (8 * (j >> 2) + 4 * half + (j & 3)) * EP + e] = acc[0][j];
         __syncthreads();
-        // sum the K slices in slice order; result replaces slice 0
-        const int Epad = nb * 32;            // <= 64 when the K chunks are split
-        constexpr int kIt = kBT * 64 / 256;
+        constexpr int kIt = kBT * EP / 256;
         float vals[kIt];
 #pragma unroll
         for (int it = 0; it < kIt; ++it) {
-            const int idx = threadIdx.x + it * 256;
-            vals[it] = 0.0f;
-            if (idx < kBT * Epad) {
-                const int row = idx / Epad, e = idx % Epad;
-                float s = lds[row * kPartStride + e];
-                for (int q = 1; q < KS; ++q) s += lds[q * kBT * kPartStride + row * kPartStride + e];
-                vals[it] = s;
-            }
+            const int idx = tid + it * 256;
+            float v = lds[idx];
+            for (int qq = 1; qq < KS; ++qq) v += lds[qq * kBT * EP + idx];
+            vals[it] = v;
         }
         __syncthreads();
 #pragma unroll
         for (int it = 0; it < kIt; ++it) {
-            const int idx = threadIdx.x + it * 256;
-            if (idx < kBT * Epad) {
-                const int row = idx / Epad, e = idx % Epad;
-                lds[row * kLogitStride + e] = vals[it];
-            }
+            const int idx = tid + it * 256;
+            lds[(idx / EP) * kLogitStride + idx % EP] = vals[it];
         }
         __syncthreads();
     }
@@ -185,11 +220,18 @@ __device__ void logits_f32(const RouteArgs& a, int t0, float* lds) {
     __syncthreads();
 }
 
-template <bool BF16>
+// NBLK = 0: fp32 inputs; else bf16 with E <= 32 NBLK.
+template <int NBLK>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
-    __shared__ float lds[kLdsFloats];
+    constexpr int NB = NBLK ? NBLK : 1;
+    using St = RouterStages<NB>;
+    constexpr int XS = NBLK ? St::XS : 8, WS = NBLK ? St::WS : 8;
+    constexpr int X3 = St::NST > 3 ? XS : 8, W3 = St::NST > 3 ? WS : 8;
+    __shared__ float lds[kLogitFloats];
+    __shared__ __align__(16) uint16_t sX0[XS], sX1[XS], sX2[XS], sX3[X3];
+    __shared__ __align__(16) uint16_t sW0[WS], sW1[WS], sW2[WS], sW3[W3];
     const int t0 = blockIdx.x * kBT;
-    if (BF16) logits_bf16(a, t0, lds);
+    if (NBLK) logits_bf16<NB>(a, t0, lds, sX0, sX1, sX2, sX3, sW0, sW1, sW2, sW3);
     else logits_f32(a, t0, lds);
 
     const int lane = threadIdx.x & 63;
@@ -268,8 +310,12 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
 hipError_t launch_route(const RouteArgs& a, bool bf16, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
     dim3 grid((a.T + kBT - 1) / kBT), block(256);
-    if (bf16) hipLaunchKernelGGL(route_kernel<true>, grid, block, 0, s, a);
-    else hipLaunchKernelGGL(route_kernel<false>, grid, block, 0, s, a);
+    const int nb = (a.E + 31) / 32;
+    if (!bf16) hipLaunchKernelGGL(route_kernel<0>, grid, block, 0, s, a);
+    else if (nb <= 1) hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, s, a);
+    else if (nb <= 2) hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, s, a);
+    else if (nb <= 4) hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, s, a);
     return hipGetLastError();
 }
 
