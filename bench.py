@@ -125,6 +125,10 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": COPY_BYTES}), flush=True)
 
 
+# the gate/up GEMM kernel as rocprofv3 names it (bf16, dual mode)
+GATE_UP_KERNEL = "gemm_bf16_persistent_kernel<true>"
+
+
 def _pmc_rows(d):
     import csv
     import glob
@@ -150,12 +154,12 @@ def traffic_from(args):
              default=None)
     cw = max((float(r["Counter_Value"]) for r in copy_rows if r["Counter_Name"] == "WRITE_SIZE"),
              default=None)
-    f_kib = _per_dispatch(_pmc_rows(fetch_dir), "FETCH_SIZE", "gemm_bf16_256x8_kernel<true>")
-    w_kib = _per_dispatch(_pmc_rows(write_dir), "WRITE_SIZE", "gemm_bf16_256x8_kernel<true>")
+    f_kib = _per_dispatch(_pmc_rows(fetch_dir), "FETCH_SIZE", GATE_UP_KERNEL)
+    w_kib = _per_dispatch(_pmc_rows(write_dir), "WRITE_SIZE", GATE_UP_KERNEL)
     if None in (cf, cw, f_kib, w_kib):
         sys.exit(f"missing counters: copy {cf} {cw}, kernel {f_kib} {w_kib}")
     f_scale, w_scale = COPY_BYTES / cf, COPY_BYTES / cw
-    rec = {"kernel": "gemm_bf16_256x8_kernel<true> (gate/up)",
+    rec = {"kernel": GATE_UP_KERNEL + " (gate/up)",
            "fetch_kib": f_kib, "write_kib": w_kib,
            "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_scale_bytes_per_kib": f_scale, "write_scale_bytes_per_kib": w_scale,
