@@ -32,6 +32,7 @@ namespace {
 constexpr int kBK = 64;
 constexpr int kThreads = 256;
 constexpr int kWMW = 4;   // M tiles per window (share one weight panel)
+constexpr int kMaxBand = 6;   // most M tiles in one band of the expert-aligned order
 
 
 // Block-wide: map flattened M tile `mt` to (group, first row, rows).  Returns
@@ -318,14 +319,57 @@ __device__ __forceinline__ TileRef tile_at(const int* s_tb, const int* s_off, in
     return t;
 }
 
+// Expert-aligned order: the M tiles of each group form bands of near-equal
+// height, at most kMaxBand; a band's tiles come in windows of (nslot /
+// height) N tiles, M tile fastest, so a round's tiles share a few A panels
+// and the B panels of one group, and each group's weights are streamed about
+// once.  Band b covers logical tiles [first M tile * tiles_n, (first M tile +
+// height) * tiles_n), so the band holding L holds M tile L / tiles_n.
+template <int BM, int BN>
+__device__ __forceinline__ TileRef tile_at_aligned(const int* s_tb, const int* s_off, int G, int tiles_n,
+                                                   int nslot, int L) {
+    const int mt0 = L / tiles_n;
+    int lo = 0, hi = G;                              // s_tb[lo] <= mt0 < s_tb[lo + 1]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_tb[mid] <= mt0) lo = mid; else hi = mid;
+    }
+    const int gbase = s_tb[lo], m = s_tb[lo + 1] - gbase;   // the group's M tiles (>= 1)
+    const int nb = (m + kMaxBand - 1) / kMaxBand;           // its bands: r of q + 1, then q
+    const int q = m / nb, r = m - nb * q;
+    const int local = mt0 - gbase;
+    int j, start;
+    if (local < r * (q + 1)) {
+        j = local / (q + 1);
+        start = j * (q + 1);
+    } else {
+        j = r + (local - r * (q + 1)) / q;
+        start = r * (q + 1) + (j - r) * q;
+    }
+    const int mh = j < r ? q + 1 : q;
+    const int wn = max(1, min(tiles_n, nslot / mh));
+    const int rem = L - (gbase + start) * tiles_n;
+    const int nwin = rem / (mh * wn);
+    const int r2 = rem - nwin * mh * wn;             // the last window may be narrower
+    const int mt = gbase + start + r2 % mh;
+    TileRef t;
+    t.grp = lo;
+    t.row0 = s_off[lo] + (mt - gbase) * BM;
+    t.nrows = min(BM, s_off[lo + 1] - t.row0);
+    t.n0 = (nwin * wn + r2 / mh) * BN;
+    t.ks = 0;
+    return t;
+}
+
 // Logical tile L of a K-split GEMM: the split index is the slowest, so each
 // split walks the same windows of M x N tiles.
-template <int BM, int BN>
+template <int BM, int BN, bool ALIGNED>
 __device__ __forceinline__ TileRef split_tile_at(const int* s_tb, const int* s_off, int G, int mt_total,
                                                  int tiles_n, int wn_win, int L) {
     const int per_split = mt_total * tiles_n;
     const int ks = L / per_split;
-    TileRef t = tile_at<BM, BN>(s_tb, s_off, G, mt_total, tiles_n, wn_win, L - ks * per_split);
+    TileRef t = ALIGNED ? tile_at_aligned<BM, BN>(s_tb, s_off, G, tiles_n, wn_win * kWMW, L - ks * per_split)
+                        : tile_at<BM, BN>(s_tb, s_off, G, mt_total, tiles_n, wn_win, L - ks * per_split);
     // the same in every lane (read from LDS at uniform addresses): scalar registers
     t.grp = __builtin_amdgcn_readfirstlane(t.grp);
     t.row0 = __builtin_amdgcn_readfirstlane(t.row0);
@@ -432,6 +476,8 @@ __device__ __forceinline__ void store_block_bf16(uint16_t* Cb, int64_t ldc, int 
 // Inside a range the XCD's workgroups take consecutive tiles in rounds; a
 // round is a window of 4 M tiles x (workgroups / 4) N tiles, so its A and B
 // panels are shared in the XCD's L2 while its tiles advance through K together.
+// With ALIGNED the bands follow the groups instead (up to 6 M tiles of one
+// expert, whose weights are then streamed about once).
 // Waves form a 2 x 4 grid: wave (wm, wn) owns 128 rows and two 32-row blocks
 // of B (dual: gate columns 32 wn .. 32 wn + 31 and the same up columns, so
 // silu(g)*u stays in registers; single: B rows 64 wn .. 64 wn + 63), i.e.
@@ -445,7 +491,7 @@ __device__ __forceinline__ void store_block_bf16(uint16_t* Cb, int64_t ldc, int 
 // stages runs on across tiles: the last two stages of a tile fetch the first
 // two of the workgroup's next tile, whose loads are in flight during the
 // epilogue.
-template <bool DUAL>
+template <bool DUAL, bool ALIGNED>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup g, int tiles_n) {
     constexpr int BM = 256;
     constexpr int BN = DUAL ? 128 : 256;
@@ -567,7 +613,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
         MOE_STAGE(NA_, 4, sA1, sB1, sA0, sB0, nxt, 1, more);                                    \
     } while (0)
 
-    TileRef tr = split_tile_at<BM, BN>(s_tb, s_off, G, mt_total, tiles_n, wn_win, L);
+    TileRef tr = split_tile_at<BM, BN, ALIGNED>(s_tb, s_off, G, mt_total, tiles_n, wn_win, L);
     int gsrc[4];
     gather_rows<8>(g, tr, w, lane, gsrc);
     DmaSrc<4> cur = dma_src<DUAL, 8>(g, tr, gsrc, w, lane, KT * kBK);
@@ -584,7 +630,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     for (;;) {
         const int Ln = L + nslot;
         const bool more = Ln < Lend;
-        const TileRef tn = split_tile_at<BM, BN>(s_tb, s_off, G, mt_total, tiles_n, wn_win, more ? Ln : L);
+        const TileRef tn = split_tile_at<BM, BN, ALIGNED>(s_tb, s_off, G, mt_total, tiles_n, wn_win, more ? Ln : L);
         // the next tile's gathered rows load now; their values are used after
         // the K loop, whose stage waits have long covered them
         gather_rows<8>(g, tn, w, lane, gsrc);
@@ -737,7 +783,16 @@ int persistent_grid() {
 template <bool DUAL>
 hipError_t launch_bf16_persistent(const GemmGroup& g, hipStream_t s) {
     constexpr int BN = DUAL ? 128 : 256;
-    hipLaunchKernelGGL((gemm_bf16_persistent_kernel<DUAL>), dim3(persistent_grid()), dim3(512), 0, s,
+    // one instantiation per tile order: a runtime choice inside the kernel
+    // costs the K loop a compiler-inserted wait on the loads in flight
+    if constexpr (!DUAL) {
+        if (g.aligned_bands) {
+            hipLaunchKernelGGL((gemm_bf16_persistent_kernel<false, true>), dim3(persistent_grid()), dim3(512),
+                               0, s, g, g.N / BN);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((gemm_bf16_persistent_kernel<DUAL, false>), dim3(persistent_grid()), dim3(512), 0, s,
                        g, g.N / BN);
     return hipGetLastError();
 }

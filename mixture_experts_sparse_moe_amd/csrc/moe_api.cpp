@@ -145,8 +145,11 @@ int run_ffn(const moe_config* c, const void* x, const int32_t* sorted, const int
                      c->d_model};
         MOE_HIP(launch_grouped_gemm(up, true, bf16, s));
         MOE_TRY(mark(ev, 2, s));
+        // expert-aligned tile bands pay off when experts hold several M tiles
+        // (measured on the down GEMM: -6 % at ~4 tiles per expert, +2 % at ~1.5)
         GemmGroup down{H, nullptr, 1, offsets, c->num_experts, P, wd, nullptr, out, c->d_model,
-                       c->d_ff, sp.routed, (int64_t)P * c->d_model};
+                       c->d_ff, sp.routed, (int64_t)P * c->d_model,
+                       (int64_t)P >= (int64_t)640 * c->num_experts};
         MOE_HIP(launch_grouped_gemm(down, false, bf16, s));
         MOE_TRY(mark(ev, 3, s));
     }

@@ -53,6 +53,7 @@ struct GemmGroup {
     int N, K;
     int splitk = 1;         // single bf16 only: K cut into splitk ranges, one C slice each
     int64_t part_stride = 0;// elements between C slices when splitk > 1
+    bool aligned_bands = false; // single bf16: tile bands follow group boundaries
 };
 // Dual mode: C = silu(A B0^T) * (A B1^T).  Single: C = A B0^T, or with
 // splitk > 1 the partial products of the K ranges, C slice s = A[:, Ks] B0[:, Ks]^T.
