@@ -125,8 +125,9 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": COPY_BYTES}), flush=True)
 
 
-# the gate/up GEMM kernel as rocprofv3 names it (bf16, dual mode)
-GATE_UP_KERNEL = "gemm_bf16_persistent_kernel<true>"
+# the gate/up GEMM kernel as rocprofv3 names it (bf16, dual mode; prefix of
+# the template argument list)
+GATE_UP_KERNEL = "gemm_bf16_persistent_kernel<true"
 
 
 def _pmc_rows(d):
@@ -159,7 +160,7 @@ def traffic_from(args):
     if None in (cf, cw, f_kib, w_kib):
         sys.exit(f"missing counters: copy {cf} {cw}, kernel {f_kib} {w_kib}")
     f_scale, w_scale = COPY_BYTES / cf, COPY_BYTES / cw
-    rec = {"kernel": GATE_UP_KERNEL + " (gate/up)",
+    rec = {"kernel": "grouped gate/up GEMM (" + GATE_UP_KERNEL + ", ...>)",
            "fetch_kib": f_kib, "write_kib": w_kib,
            "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_scale_bytes_per_kib": f_scale, "write_scale_bytes_per_kib": w_scale,
