@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the CPU oracle sample")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the practical ceilings (device copy, torch.matmul yardstick)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of 1 GiB (the reference for HBM counters)")
     p.add_argument("--traffic-from", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_DIR"),
@@ -84,6 +86,40 @@ def algorithmic(sh, counts: np.ndarray) -> dict:
     down = dict(flops=2.0 * P * d * f, bytes=touched * d * f * w + P * f * w + P * d * w)
     return dict(layer_flops=layer_flops, layer_bytes=layer_bytes, gate_up=gate_up, down=down,
                 touched=touched)
+
+
+def practical_ceilings(torch, dev) -> dict:
+    """Measured ceilings on the same GPU, next to the nominal peaks: a 1 GiB
+    device copy (read + write bytes / time) and one bf16 4096 x 14336 x 4096
+    torch.matmul (a library yardstick only; nothing of the layer uses it)."""
+    out = {}
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    out["copy_gbs"] = 2 * COPY_BYTES * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    a = torch.randn(4096, 4096, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(4096, 14336, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        c = a @ b
+    e1.record()
+    e1.synchronize()
+    out["torch_matmul_bf16_tflops"] = 2.0 * 4096 * 14336 * 4096 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    out["torch_matmul_shape"] = "4096x14336x4096"
+    del a, b, c
+    return out
 
 
 def cpu_baseline(sh, inp, target_s: float) -> dict:
@@ -285,8 +321,19 @@ def main():
         "expert_load": {"max_over_mean": float(cnt.max() / max(cnt.mean(), 1e-9)),
                         "touched": alg["touched"], "min": int(cnt.min()), "max": int(cnt.max())},
         "roofline": roof,
+        # the prefill-shaped grouped GEMM: gate/up and down kernels together
+        "grouped_gemm": {"ms": gu_ms + float(stage_avg[3]),
+                         "tflops": (alg["gate_up"]["flops"] + alg["down"]["flops"]) /
+                                   ((gu_ms + float(stage_avg[3])) * 1e-3) / 1e12,
+                         "gbs": (alg["gate_up"]["bytes"] + alg["down"]["bytes"]) /
+                                ((gu_ms + float(stage_avg[3])) * 1e-3) / 1e9},
         "kernel_source_hash": src_hash,
     }
+    gg = out["grouped_gemm"]
+    gg["frac_bf16_peak"] = gg["tflops"] / PEAK_BF16_TFLOPS
+    gg["frac_hbm"] = gg["gbs"] / PEAK_HBM_GBS
+    if not args.no_ceilings:
+        out["practical_ceilings"] = practical_ceilings(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(sh, inp, args.cpu_seconds)
     else:

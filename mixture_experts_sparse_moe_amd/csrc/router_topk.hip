@@ -28,6 +28,7 @@
 // expert index) reduced with a butterfly; k rounds.
 #include "device_util.h"
 #include "moe_internal.h"
+#include "skinny.h"
 
 namespace moe {
 
@@ -37,7 +38,6 @@ constexpr int kBT = 32;          // tokens per workgroup
 constexpr int kMaxE = 256;
 constexpr int kLogitStride = kMaxE + 1;
 constexpr int kLogitFloats = kBT * kLogitStride;
-constexpr int kChunk = 64;       // K elements per LDS stage
 
 __device__ __forceinline__ uint32_t ord_bits(float f) {
     f = f + 0.0f;  // -0 -> +0: equal logits compare equal
@@ -63,31 +63,18 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 // Logits of 32 tokens x all experts (E <= 32 NBLK) into lds[32][kLogitStride]
 // (bf16 inputs, MFMA, LDS-staged K chunks).
 template <int NBLK>
-struct RouterStages {
-    static constexpr int NST = NBLK >= 8 ? 3 : 4;        // stage buffers
-    static constexpr int XS = kBT * kChunk;               // x stage (elements)
-    static constexpr int WS = NBLK * 32 * kChunk;         // weight stage (elements)
-};
-
-template <int NBLK>
 __device__ __forceinline__ void logits_bf16(const RouteArgs& a, int t0, float* lds, uint16_t* sX0,
                                             uint16_t* sX1, uint16_t* sX2, uint16_t* sX3, uint16_t* sW0,
                                             uint16_t* sW1, uint16_t* sW2, uint16_t* sW3) {
-    constexpr int NST = RouterStages<NBLK>::NST;
-    constexpr int KS = NBLK >= 4 ? 1 : 4 / NBLK;          // waves sharing an expert block
-    constexpr int BPW = NBLK >= 4 ? NBLK / 4 : 1;         // expert blocks per wave
-    constexpr int P = 1 + NBLK;                           // DMA instructions per wave per stage
-
+    using Sh = SkinnyShape<NBLK>;
+    constexpr int KS = Sh::KS, BPW = Sh::BPW, P = Sh::P;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, r32 = lane & 31;
-    const int nchunks = a.d / kChunk;
     const int64_t rowb = (int64_t)a.d * 2;               // bytes per row
 
-    // DMA instruction j of wave w fills 8 rows of the stage, 8 (w + 4 j) ..:
-    // j = 0 the x rows 8 w .. 8 w + 7, j >= 1 weight rows 8 (w + 4 j - 4) ..
-    // Lane l fills physical chunk l % 8 of row l / 8 with logical chunk
-    // (l % 8) ^ swz(row).  Rows past T or E repeat the last one.
+    // A rows: the 32 tokens (rows past T repeat the last); B rows: the experts
+    // (rows past E repeat the last)
     const char* src[P];
     {
         const int rx = 8 * w + (lane >> 3);
@@ -100,72 +87,13 @@ __device__ __forceinline__ void logits_bf16(const RouteArgs& a, int t0, float* l
             src[j] = static_cast<const char*>(a.w) + e * rowb + (((lane & 7) ^ swz(rw)) * 16);
         }
     }
-#define MOE_R_DMA(sX_, sW_, st_)                                                                \
-    do {                                                                                        \
-        const int64_t ko_ = (int64_t)min((st_), nchunks - 1) * (kChunk * 2);                    \
-        __builtin_amdgcn_global_load_lds((const void*)(src[0] + ko_),                           \
-                                         (lds_ptr_t)((sX_) + 8 * w * kChunk), 16, 0, 0);        \
-        _Pragma("unroll") for (int j = 1; j < P; ++j)                                           \
-            __builtin_amdgcn_global_load_lds((const void*)(src[j] + ko_),                       \
-                                             (lds_ptr_t)((sW_) + 8 * (w + 4 * j - 4) * kChunk), 16, 0, 0); \
-    } while (0)
-
-    // this wave's expert blocks and K steps
-    const int b0 = NBLK >= 4 ? w * BPW : w % NBLK;
-    const int s0 = NBLK >= 4 ? 0 : (w / NBLK) * (4 / KS);
-    constexpr int NS = 4 / KS;                            // K steps per chunk for this wave
     f32x16_t acc[BPW];
 #pragma unroll
     for (int i = 0; i < BPW; ++i)
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
-
-#define MOE_R_MFMA(sX_, sW_)                                                                    \
-    do {                                                                                        \
-        _Pragma("unroll") for (int s_ = 0; s_ < NS; ++s_) {                                     \
-            const int c_ = 2 * (s0 + s_) + half;                                                \
-            const bf16x8_t xa_ = as_bf16x8(*reinterpret_cast<const uint4*>(                     \
-                (sX_) + r32 * kChunk + ((c_ ^ swz(r32)) * 8)));                                 \
-            _Pragma("unroll") for (int i_ = 0; i_ < BPW; ++i_) {                                \
-                const int r_ = (b0 + i_) * 32 + r32;                                            \
-                const bf16x8_t wb_ = as_bf16x8(*reinterpret_cast<const uint4*>(                 \
-                    (sW_) + r_ * kChunk + ((c_ ^ swz(r_)) * 8)));                               \
-                acc[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa_, wb_, acc[i_], 0, 0, 0);  \
-            }                                                                                   \
-        }                                                                                       \
-    } while (0)
-// chunk st_ in buffer (sX_, sW_); the buffer of chunk st_ - 1 is refilled
-// with chunk st_ - 1 + NST once every wave is past this barrier
-#define MOE_R_STAGE(sX_, sW_, sXp_, sWp_, st_)                                                  \
-    do {                                                                                        \
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt((NST - 2) * P));                                  \
-        __builtin_amdgcn_s_barrier();                                                           \
-        __builtin_amdgcn_sched_barrier(0);                                                      \
-        MOE_R_DMA(sXp_, sWp_, (st_) - 1 + NST);                                                 \
-        __builtin_amdgcn_sched_barrier(0);                                                      \
-        if ((st_) < nchunks) MOE_R_MFMA(sX_, sW_);                                              \
-    } while (0)
-
-    MOE_R_DMA(sX0, sW0, 0);
-    MOE_R_DMA(sX1, sW1, 1);
-    MOE_R_DMA(sX2, sW2, 2);
-    if (NST > 3) MOE_R_DMA(sX3, sW3, 3);
-    for (int c = 0; c < nchunks; c += NST) {
-        if (NST > 3) {
-            MOE_R_STAGE(sX0, sW0, sX3, sW3, c);
-            MOE_R_STAGE(sX1, sW1, sX0, sW0, c + 1);
-            MOE_R_STAGE(sX2, sW2, sX1, sW1, c + 2);
-            MOE_R_STAGE(sX3, sW3, sX2, sW2, c + 3);
-        } else {
-            MOE_R_STAGE(sX0, sW0, sX2, sW2, c);
-            MOE_R_STAGE(sX1, sW1, sX0, sW0, c + 1);
-            MOE_R_STAGE(sX2, sW2, sX1, sW1, c + 2);
-        }
-    }
-#undef MOE_R_DMA
-#undef MOE_R_MFMA
-#undef MOE_R_STAGE
-    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));     // the repeated chunks past the end
+    skinny_mma<NBLK, false>(src, a.d / kSkChunk, sX0, sX1, sX2, sX3, sW0, sW1, sW2, sW3, acc);
+    const int b0 = skinny_block<NBLK, false>(w, 0);
 
     // D element j of block i: token row 8 (j / 4) + 4 half + j % 4, expert r32
     if (KS == 1) {
@@ -224,7 +152,7 @@ __device__ void logits_f32(const RouteArgs& a, int t0, float* lds) {
 template <int NBLK>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     constexpr int NB = NBLK ? NBLK : 1;
-    using St = RouterStages<NB>;
+    using St = SkinnyShape<NB>;
     constexpr int XS = NBLK ? St::XS : 8, WS = NBLK ? St::WS : 8;
     constexpr int X3 = St::NST > 3 ? XS : 8, W3 = St::NST > 3 ? WS : 8;
     __shared__ float lds[kLogitFloats];
