@@ -24,6 +24,7 @@
 // fp32 kernel: LDS-tiled FMA (the tiny fp32 layer only).
 #include "device_util.h"
 #include "moe_internal.h"
+#include "skinny.h"
 
 namespace moe {
 
@@ -389,6 +390,7 @@ struct DmaSrc {
     const char* a;
     const char* b;
     uint32_t ao[J], bo[J];
+    int rot;        // first K stage of the walk (stage s reads stage (s + rot) mod stages)
 };
 
 // NW waves; wave w stages rows (256 / NW) w .. (256 / NW)(w + 1) - 1 of the A
@@ -420,6 +422,12 @@ __device__ __forceinline__ DmaSrc<32 / NW> dma_src(const GemmGroup& g, const Til
     const uint32_t K2 = (uint32_t)g.K * 2;
     const int64_t k0 = (int64_t)t.ks * k_split * 2;    // first byte of the tile's K range
     DmaSrc<J> s;
+    // Tiles that run at the same time start their K walks at different
+    // stages: every workgroup reading the same offset of its 8 KB-strided
+    // weight rows at once crowds a few HBM channels.  Tiles of one group and
+    // N tile (the same weight panel) start together; N tiles of a window,
+    // which share an A panel, are a few stages apart.
+    s.rot = __builtin_amdgcn_readfirstlane((t.n0 / (DUAL ? 128 : 256) + 17 * t.grp) % (k_split / kBK));
     s.a = static_cast<const char*>(g.A) + (g.gather ? 0 : (int64_t)t.row0 * K2) + k0;
     // dual: the first half of the waves stage gate rows n0 .. n0 + 127, the
     // second half the same up rows
@@ -532,8 +540,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 // compiler waits for them before the next fragment reads.
 #define MOE_DMA(sA_, sB_, src_, kt_)                                                            \
     do {                                                                                        \
-        const char* ab_ = (src_).a + (kt_) * (kBK * 2);                                         \
-        const char* bb_ = (src_).b + (kt_) * (kBK * 2);                                         \
+        const int kr_ = (kt_) + (src_).rot;                                                     \
+        const int kp_ = kr_ >= KT ? kr_ - KT : kr_;                                             \
+        const char* ab_ = (src_).a + kp_ * (kBK * 2);                                           \
+        const char* bb_ = (src_).b + kp_ * (kBK * 2);                                           \
         _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                         \
             __builtin_amdgcn_global_load_lds(ab_ + (src_).ao[j],                                \
                                              (lds_ptr_t)((sA_) + (w * 32 + j * 8) * kBK), 16, 0, 0); \
@@ -679,6 +689,115 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 #undef MOE_KLOOP
 }
 
+// Few rows per group (decode): the weights are the stream and the MFMA work
+// is small, so the tile is 32 rows of one group x NBLK blocks of 32 weight
+// rows (dual: NBLK / 2 gate blocks and the same up blocks, so a tile yields
+// 16 NBLK columns of silu(g) * u; single: 32 NBLK columns) over one K range.
+// One workgroup of 4 waves per tile; the K chunks stream through LDS (the
+// shared 32-row product above).  With NST = 3 and NBLK = 4 a workgroup takes
+// 60 KB of LDS, so two run on a CU and one's set-up and epilogue overlap the
+// other's stream.  Logical tile L: N tile fastest, then the M tile (of 32
+// rows, by the prefix over the groups), then the K range.  The K walk of a
+// tile starts at a chunk that depends on its N tile and group, so tiles that
+// run together read different offsets of their weight rows.
+template <bool DUAL, int NBLK, int NST>
+__global__ __launch_bounds__(256, NBLK * NST <= 12 ? 2 : 1) void gemm_bf16_skinny_kernel(GemmGroup g, int tiles_n,
+                                                                                        int mt_upper) {
+    constexpr int KS = (DUAL && NBLK == 4) ? 2 : 1;
+    using Sh = SkinnyShape<NBLK, NST, KS>;
+    constexpr int COLS = DUAL ? 16 * NBLK : 32 * NBLK;   // output columns per tile
+    constexpr int X3 = NST > 3 ? Sh::XS : 8, W3 = NST > 3 ? Sh::WS : 8;
+    __shared__ __align__(16) uint16_t sX0[Sh::XS], sX1[Sh::XS], sX2[Sh::XS], sX3[X3];
+    __shared__ __align__(16) uint16_t sW0[Sh::WS], sW1[Sh::WS], sW2[Sh::WS], sW3[W3];
+
+    const int L = blockIdx.x;
+    const int nt = L % tiles_n;
+    const int mt = (L / tiles_n) % mt_upper;
+    const int ks = L / tiles_n / mt_upper;
+    int grp, row0, nrows;
+    if (!locate_tile<32>(g, mt, &grp, &row0, &nrows)) return;   // uniform over the workgroup
+    grp = __builtin_amdgcn_readfirstlane(grp);
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    nrows = __builtin_amdgcn_readfirstlane(nrows);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int S = DUAL ? 1 : g.splitk;
+    const int nchunks = g.K / kSkChunk / S;
+    const int64_t rowb = (int64_t)g.K * 2;
+    const int64_t k0b = (int64_t)ks * nchunks * (kSkChunk * 2);
+    const int n0 = nt * COLS;
+
+    const char* src[Sh::P];
+    {
+        const int r = 8 * w + (lane >> 3);
+        const int rr = row0 + min(r, nrows - 1);       // rows past the tile's end repeat its last row
+        const int64_t arow = g.gather ? g.gather[rr] / g.gather_div : rr;
+        src[0] = static_cast<const char*>(g.A) + arow * rowb + k0b + (((lane & 7) ^ swz(r)) * 16);
+#pragma unroll
+        for (int j = 1; j < Sh::P; ++j) {
+            const int rb = 8 * (w + 4 * j - 4) + (lane >> 3);          // B row of the tile
+            const char* base;
+            int n;
+            if (DUAL) {
+                base = static_cast<const char*>(rb < 16 * NBLK ? g.B0 : g.B1);
+                n = n0 + (rb < 16 * NBLK ? rb : rb - 16 * NBLK);
+            } else {
+                base = static_cast<const char*>(g.B0);
+                n = n0 + rb;
+            }
+            src[j] = base + ((int64_t)grp * g.N + n) * rowb + k0b + (((lane & 7) ^ swz(rb)) * 16);
+        }
+    }
+    const int rot = __builtin_amdgcn_readfirstlane((nt + 17 * grp) % nchunks);
+
+    f32x16_t acc[Sh::BPW];
+#pragma unroll
+    for (int i = 0; i < Sh::BPW; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
+    skinny_mma<Sh, DUAL>(src, nchunks, rot, sX0, sX1, sX2, sX3, sW0, sW1, sW2, sW3, acc);
+
+    const int gi = w % Sh::NG;
+    if (KS == 2) {
+        // waves 2, 3 hold the partial sums of K steps 2, 3 of groups 0, 1:
+        // handed to waves 0, 1 through LDS (after every wave's last reads
+        // and DMAs), added in that order
+        float* red = reinterpret_cast<float*>(sW0);
+        static_assert(KS != 2 || Sh::WS * 2 >= 2 * Sh::BPW * 16 * 64 * 4, "reduction space");
+        __syncthreads();
+        if (w >= 2) {
+#pragma unroll
+            for (int i = 0; i < Sh::BPW; ++i)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) red[((gi * Sh::BPW + i) * 16 + j) * 64 + lane] = acc[i][j];
+        }
+        __syncthreads();
+        if (w >= 2) return;
+#pragma unroll
+        for (int i = 0; i < Sh::BPW; ++i)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[i][j] += red[((gi * Sh::BPW + i) * 16 + j) * 64 + lane];
+    }
+    uint16_t* C = static_cast<uint16_t*>(g.C) + (int64_t)ks * g.part_stride + (int64_t)row0 * g.N + n0;
+    if (DUAL) {
+        // this wave: gate block gi (acc[0]) and up block gi + NG (acc[1]), columns 32 gi ..
+        static_assert(!DUAL || Sh::BPW == 2, "dual pairs one gate and one up block per wave");
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = silu_f32(acc[0][q]) * acc[1][q];
+        store_block_bf16(C + 32 * gi, g.N, nrows, v, lane);
+    } else {
+#pragma unroll
+        for (int i = 0; i < Sh::BPW; ++i) {
+            float v[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v[q] = acc[i][q];
+            store_block_bf16(C + 32 * skinny_block<Sh, false>(w, i), g.N, nrows, v, lane);
+        }
+    }
+}
+
 // fp32 grouped GEMM: 64x64 tiles, BK 16, 4x4 outputs per thread.
 template <bool DUAL>
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmGroup g, int tiles_n, int mt_upper) {
@@ -797,6 +916,22 @@ hipError_t launch_bf16_persistent(const GemmGroup& g, hipStream_t s) {
     return hipGetLastError();
 }
 
+constexpr int kSkNblk = 4, kSkNst = 3;
+
+template <bool DUAL>
+hipError_t launch_bf16_skinny(const GemmGroup& g, hipStream_t s) {
+    constexpr int COLS = DUAL ? 16 * kSkNblk : 32 * kSkNblk;
+    const int tiles_n = g.N / COLS;
+    const int64_t mtu = g.offsets ? grouped_m_tiles_upper(g.M, g.G, 32) : (g.M + 31) / 32;
+    const int S = DUAL ? 1 : g.splitk;
+    const int64_t grid = mtu * tiles_n * S;
+    if (grid == 0) return hipSuccess;
+    if (grid > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((gemm_bf16_skinny_kernel<DUAL, kSkNblk, kSkNst>), dim3((unsigned)grid), dim3(256), 0, s,
+                       g, tiles_n, (int)mtu);
+    return hipGetLastError();
+}
+
 template <bool DUAL>
 hipError_t launch_f32(const GemmGroup& g, hipStream_t s) {
     const int tiles_n = g.N / 64;
@@ -830,8 +965,35 @@ int choose_splitk(int64_t mt_expected, int N, int K) {
     return best;
 }
 
+bool skinny_rows(int64_t rows, int G) { return rows <= (int64_t)32 * G; }
+
+bool skinny_fits(int N, int K, bool dual, int splitk) {
+    const int cols = dual ? 16 * kSkNblk : 32 * kSkNblk;
+    return N % cols == 0 && splitk >= 1 && K % (kSkChunk * splitk) == 0 && (!dual || splitk == 1);
+}
+
+int choose_splitk_skinny(int64_t mt_expected, int N, int K) {
+    constexpr int kSlots = 2 * 256;            // workgroups in flight: two per CU
+    const int cols = 32 * kSkNblk;
+    if (N % cols || mt_expected <= 0) return 1;
+    const int64_t tiles = mt_expected * (N / cols);
+    int best = 1;
+    double best_cost = (double)((tiles + kSlots - 1) / kSlots);
+    for (int sk = 2; sk <= 8; sk *= 2) {
+        // at least 32 chunks of 64 per split
+        if (K % (kSkChunk * sk) || K / (kSkChunk * sk) < 32) break;
+        const double cost = (double)((tiles * sk + kSlots - 1) / kSlots) / sk;
+        if (cost < best_cost * 0.95) { best = sk; best_cost = cost; }
+    }
+    return best;
+}
+
 hipError_t launch_grouped_gemm(const GemmGroup& g, bool dual, bool bf16, hipStream_t s) {
     if (g.M == 0) return hipSuccess;
+    if (g.skinny) {
+        if (!bf16 || !skinny_fits(g.N, g.K, dual, g.splitk)) return hipErrorInvalidValue;
+        return dual ? launch_bf16_skinny<true>(g, s) : launch_bf16_skinny<false>(g, s);
+    }
     if (g.splitk != 1 && (dual || !bf16 || g.splitk < 1 || g.K % (128 * g.splitk) || g.N % 256))
         return hipErrorInvalidValue;
     if (!bf16) return dual ? launch_f32<true>(g, s) : launch_f32<false>(g, s);

@@ -41,10 +41,28 @@ int validate_cfg(const moe_config* c) {
 
 size_t elem(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 
+// Which bf16 GEMM kernel the routed and the shared expert GEMMs use: the
+// 32-row streaming kernel when groups hold about 32 rows or fewer on average
+// (decode), else the 256 x 256 tile kernel.
+struct Paths {
+    bool routed_skinny, shared_skinny;
+};
+
+Paths paths(const moe_config* c) {
+    const bool bf16 = c->dtype == MOE_BF16;
+    const int64_t P = (int64_t)c->num_tokens * c->top_k;
+    Paths p{bf16 && skinny_rows(P, c->num_experts) && skinny_fits(c->d_ff, c->d_model, true, 1) &&
+                skinny_fits(c->d_model, c->d_ff, false, 1),
+            bf16 && c->num_shared && skinny_rows(c->num_tokens, 1) &&
+                skinny_fits(c->d_ff_shared, c->d_model, true, 1) && skinny_fits(c->d_model, c->d_ff_shared, false, 1)};
+    return p;
+}
+
 // K splits of the down projections inside moe_forward (moe_expert_ffn never
-// splits: its expert_out is the finished product).  The routed GEMM has about
-// P / 256 + min(E, P) / 2 M tiles (each expert's last tile is partial); the
-// shared one T / 256.  Only bf16 layers split.
+// splits: its expert_out is the finished product).  For the 256-row kernel the
+// routed GEMM has about P / 256 + min(E, P) / 2 M tiles (each expert's last
+// tile is partial), the shared one T / 256; for the 32-row kernel about
+// P / 32 + min(E, P) / 2 and T / 32.  Only bf16 layers split.
 struct Splits {
     int routed, shared;
 };
@@ -52,11 +70,21 @@ struct Splits {
 Splits splits(const moe_config* c) {
     Splits sp{1, 1};
     if (c->dtype != MOE_BF16 || c->num_tokens == 0) return sp;
-    const int64_t P = (int64_t)c->num_tokens * c->top_k, E = c->num_experts;
-    const int64_t mt_upper = grouped_m_tiles_upper(P, (int)E, 256);
-    const int64_t mt_exp = std::min<int64_t>(mt_upper, (P + 255) / 256 + std::min<int64_t>(E, P) / 2);
-    sp.routed = choose_splitk(mt_exp, c->d_model, c->d_ff);
-    if (c->num_shared) sp.shared = choose_splitk(((int64_t)c->num_tokens + 255) / 256, c->d_model, c->d_ff_shared);
+    const Paths pa = paths(c);
+    const int64_t P = (int64_t)c->num_tokens * c->top_k, E = c->num_experts, T = c->num_tokens;
+    if (pa.routed_skinny) {
+        const int64_t mt_exp = std::min<int64_t>(grouped_m_tiles_upper(P, (int)E, 32),
+                                                 (P + 31) / 32 + std::min<int64_t>(E, P) / 2);
+        sp.routed = choose_splitk_skinny(mt_exp, c->d_model, c->d_ff);
+    } else {
+        const int64_t mt_upper = grouped_m_tiles_upper(P, (int)E, 256);
+        const int64_t mt_exp = std::min<int64_t>(mt_upper, (P + 255) / 256 + std::min<int64_t>(E, P) / 2);
+        sp.routed = choose_splitk(mt_exp, c->d_model, c->d_ff);
+    }
+    if (c->num_shared) {
+        sp.shared = pa.shared_skinny ? choose_splitk_skinny((T + 31) / 32, c->d_model, c->d_ff_shared)
+                                     : choose_splitk((T + 255) / 256, c->d_model, c->d_ff_shared);
+    }
     return sp;
 }
 
@@ -140,9 +168,11 @@ int run_ffn(const moe_config* c, const void* x, const int32_t* sorted, const int
             void* const* ev = nullptr, Splits sp = Splits{1, 1}) {
     const bool bf16 = c->dtype == MOE_BF16;
     const int P = c->num_tokens * c->top_k;
+    const Paths pa = paths(c);
     if (P > 0) {
         GemmGroup up{x, sorted, c->top_k, offsets, c->num_experts, P, wg, wu, H, c->d_ff,
                      c->d_model};
+        up.skinny = pa.routed_skinny;
         MOE_HIP(launch_grouped_gemm(up, true, bf16, s));
         MOE_TRY(mark(ev, 2, s));
         // expert-aligned tile bands pay off when experts hold several M tiles
@@ -150,16 +180,19 @@ int run_ffn(const moe_config* c, const void* x, const int32_t* sorted, const int
         GemmGroup down{H, nullptr, 1, offsets, c->num_experts, P, wd, nullptr, out, c->d_model,
                        c->d_ff, sp.routed, (int64_t)P * c->d_model,
                        (int64_t)P >= (int64_t)640 * c->num_experts};
+        down.skinny = pa.routed_skinny;
         MOE_HIP(launch_grouped_gemm(down, false, bf16, s));
         MOE_TRY(mark(ev, 3, s));
     }
     if (c->num_shared && c->num_tokens > 0) {
         GemmGroup up{x, nullptr, 1, nullptr, 1, c->num_tokens, sg, su, Hs, c->d_ff_shared,
                      c->d_model};
+        up.skinny = pa.shared_skinny;
         MOE_HIP(launch_grouped_gemm(up, true, bf16, s));
         MOE_TRY(mark(ev, 4, s));
         GemmGroup down{Hs, nullptr, 1, nullptr, 1, c->num_tokens, sd, nullptr, shared_out,
                        c->d_model, c->d_ff_shared, sp.shared, (int64_t)c->num_tokens * c->d_model};
+        down.skinny = pa.shared_skinny;
         MOE_HIP(launch_grouped_gemm(down, false, bf16, s));
         MOE_TRY(mark(ev, 5, s));
     } else {

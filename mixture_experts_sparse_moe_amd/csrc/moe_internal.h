@@ -54,6 +54,7 @@ struct GemmGroup {
     int splitk = 1;         // single bf16 only: K cut into splitk ranges, one C slice each
     int64_t part_stride = 0;// elements between C slices when splitk > 1
     bool aligned_bands = false; // single bf16: tile bands follow group boundaries
+    bool skinny = false;    // bf16, few rows per group: 32-row tiles streaming the weights
 };
 // Dual mode: C = silu(A B0^T) * (A B1^T).  Single: C = A B0^T, or with
 // splitk > 1 the partial products of the K ranges, C slice s = A[:, Ks] B0[:, Ks]^T.
@@ -63,6 +64,12 @@ hipError_t launch_grouped_gemm(const GemmGroup& g, bool dual, bool bf16, hipStre
 // least 24 stages of 64 per split) whose rounds of tiles over 256 CUs waste
 // the least.  Depends only on its arguments.
 int choose_splitk(int64_t mt_expected, int N, int K);
+// The 32-row kernel suits groups of about 32 rows or fewer on average.
+bool skinny_rows(int64_t rows, int G);
+// Shapes it takes: N a multiple of its tile width, K of 64 per range; dual unsplit.
+bool skinny_fits(int N, int K, bool dual, int splitk);
+// K split for its single GEMM with about mt_expected M tiles of 32 rows.
+int choose_splitk_skinny(int64_t mt_expected, int N, int K);
 // Upper bound of M-tiles over all groups for tile height bm.
 int64_t grouped_m_tiles_upper(int64_t rows, int G, int bm);
 

@@ -68,6 +68,7 @@ __device__ __forceinline__ void logits_bf16(const RouteArgs& a, int t0, float* l
                                             uint16_t* sW1, uint16_t* sW2, uint16_t* sW3) {
     using Sh = SkinnyShape<NBLK>;
     constexpr int KS = Sh::KS, BPW = Sh::BPW, P = Sh::P;
+    static_assert(KS == 1 || BPW == 1, "partial tiles of one block per wave");
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, r32 = lane & 31;
@@ -92,8 +93,8 @@ __device__ __forceinline__ void logits_bf16(const RouteArgs& a, int t0, float* l
     for (int i = 0; i < BPW; ++i)
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
-    skinny_mma<NBLK, false>(src, a.d / kSkChunk, sX0, sX1, sX2, sX3, sW0, sW1, sW2, sW3, acc);
-    const int b0 = skinny_block<NBLK, false>(w, 0);
+    skinny_mma<Sh, false>(src, a.d / kSkChunk, 0, sX0, sX1, sX2, sX3, sW0, sW1, sW2, sW3, acc);
+    const int b0 = skinny_block<Sh, false>(w, 0);
 
     // D element j of block i: token row 8 (j / 4) + 4 half + j % 4, expert r32
     if (KS == 1) {
@@ -107,7 +108,7 @@ __device__ __forceinline__ void logits_bf16(const RouteArgs& a, int t0, float* l
     } else {
         // partial tiles [KS][32][32 NBLK], then their sum in slice order
         constexpr int EP = 32 * NBLK;
-        const int q = w / NBLK;
+        const int q = w / Sh::NG;
         const int e = b0 * 32 + r32;
 #pragma unroll
         for (int j = 0; j < 16; ++j) lds[q * kBT * EP + (8 * (j >> 2) + 4 * half + (j & 3)) * EP + e] = acc[0][j];

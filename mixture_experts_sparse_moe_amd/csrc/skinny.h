@@ -1,20 +1,22 @@
 // A 32-row product streamed through LDS: C[32, 32 NBLK] = A[32, K] B[32 NBLK, K]^T
 // on v_mfma_f32_32x32x16_bf16 (bf16 in, fp32 accumulation).  Shared by the
 // router (32 tokens x all experts) and the grouped GEMM for few rows per
-// expert (decode), where the weights are the stream.
+// group (decode), where the weights are the stream.
 //
 // One workgroup of 4 waves.  K goes in chunks of 64 elements: the chunk of the
 // 32 A rows and of the 32 NBLK B rows is fetched by direct-to-LDS DMA into one
-// of NST stage buffers, NST - 2 chunks ahead of the one being multiplied, one
+// of NST stage buffers, NST - 1 chunks ahead of the one being multiplied, one
 // barrier per chunk.  LDS rows are 128 bytes with 16-byte chunks XOR-swizzled
 // (c ^ swz(row)).  The DMA instructions are unconditional: chunks past the end
-// repeat the last one, into buffers that are never read.
+// repeat the last one, into buffers that are never read.  The walk over the
+// chunks may start at any chunk `rot` and wrap around.
 //
-// Waves and blocks (32 B rows each): with NBLK >= 4 wave w owns NBLK / 4
-// blocks, w * NBLK / 4 + i, or w + 4 i when PAIRED (so a wave holds block w of
-// both halves, e.g. the gate and the up rows of the same columns).  With
-// NBLK < 4, 4 / NBLK waves share block w % NBLK and split the four 16-wide K
-// steps of each chunk; the caller adds their partial tiles.
+// Waves and blocks (32 B rows each): the 4 waves form NG = 4 / KS groups; the
+// KS waves of a group split the four 16-wide K steps of every chunk and each
+// holds partial sums of the group's BPW = NBLK / NG blocks: block i of group
+// gi is gi BPW + i, or gi + NG i when PAIRED (so one wave holds the same
+// columns of both halves of B, e.g. gate and up rows).  The caller adds the
+// partial tiles of a group's waves.
 #pragma once
 
 #include "device_util.h"
@@ -22,52 +24,53 @@
 namespace moe {
 
 constexpr int kSkChunk = 64;            // K elements per stage
-constexpr int kSkRows = 32;             // A rows
 
-template <int NBLK>
+template <int NBLK_, int NST_ = (NBLK_ >= 8 ? 3 : 4), int KS_ = (NBLK_ >= 4 ? 1 : 4 / NBLK_)>
 struct SkinnyShape {
-    static constexpr int NST = NBLK >= 8 ? 3 : 4;                  // stage buffers
-    static constexpr int XS = kSkRows * kSkChunk;                  // A stage (elements)
-    static constexpr int WS = NBLK * 32 * kSkChunk;                // B stage (elements)
-    static constexpr int KS = NBLK >= 4 ? 1 : 4 / NBLK;            // waves per block
-    static constexpr int BPW = NBLK >= 4 ? NBLK / 4 : 1;           // blocks per wave
-    static constexpr int P = 1 + NBLK;                             // DMA instructions per wave per chunk
+    static constexpr int NBLK = NBLK_, NST = NST_, KS = KS_;
+    static constexpr int XS = 32 * kSkChunk;                   // A stage (elements)
+    static constexpr int WS = NBLK * 32 * kSkChunk;            // B stage (elements)
+    static constexpr int NG = 4 / KS;                          // wave groups
+    static constexpr int BPW = NBLK / NG;                      // blocks per wave
+    static constexpr int NS = 4 / KS;                          // K steps per wave per chunk
+    static constexpr int P = 1 + NBLK;                         // DMA instructions per wave per chunk
+    static_assert(NST >= 3 && NST <= 4 && KS * NG == 4 && BPW * NG == NBLK, "shape");
 };
 
 // Block i of wave w.
-template <int NBLK, bool PAIRED>
+template <class Sh, bool PAIRED>
 __device__ __forceinline__ int skinny_block(int w, int i) {
-    if (NBLK < 4) return w % NBLK;
-    return PAIRED ? w + 4 * i : w * (NBLK / 4) + i;
+    const int gi = w % Sh::NG;
+    return PAIRED ? gi + Sh::NG * i : gi * Sh::BPW + i;
 }
 
-// src[0]: this lane's A row 8 w + lane / 8 at its swizzled chunk, first chunk
-// of the K range; src[j], j >= 1: B row 8 (w + 4 j - 4) + lane / 8 likewise.
-// Chunk st of the range is at byte offset 128 st.  Multiplies nchunks chunks
-// into acc (zeroed by the caller).  Every wave of the workgroup must call it.
-template <int NBLK, bool PAIRED>
-__device__ __forceinline__ void skinny_mma(const char* const* src, int nchunks, uint16_t* sX0, uint16_t* sX1,
-                                           uint16_t* sX2, uint16_t* sX3, uint16_t* sW0, uint16_t* sW1,
-                                           uint16_t* sW2, uint16_t* sW3, f32x16_t* acc) {
-    using Sh = SkinnyShape<NBLK>;
-    constexpr int NST = Sh::NST, KS = Sh::KS, BPW = Sh::BPW, P = Sh::P;
+// src[0]: this lane's A row 8 w + lane / 8 at its swizzled 16-byte chunk, in
+// the first chunk of the K range; src[j], j >= 1: B row 8 (w + 4 j - 4) +
+// lane / 8 likewise.  Chunk c of the range is at byte offset 128 c.  Adds
+// the products of nchunks chunks, walked from chunk rot (< nchunks), into
+// acc.  Every wave of the workgroup must call it; on return this wave's DMAs
+// have landed (other waves' only after a barrier).
+template <class Sh, bool PAIRED>
+__device__ __forceinline__ void skinny_mma(const char* const* src, int nchunks, int rot, uint16_t* sX0,
+                                           uint16_t* sX1, uint16_t* sX2, uint16_t* sX3, uint16_t* sW0,
+                                           uint16_t* sW1, uint16_t* sW2, uint16_t* sW3, f32x16_t* acc) {
+    constexpr int NST = Sh::NST, BPW = Sh::BPW, P = Sh::P, NS = Sh::NS;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5, r32 = lane & 31;
+    const int s0 = (w / Sh::NG) * NS;   // this wave's first K step in a chunk
 
 #define MOE_SK_DMA(sX_, sW_, st_)                                                               \
     do {                                                                                        \
-        const int64_t ko_ = (int64_t)min((st_), nchunks - 1) * (kSkChunk * 2);                  \
+        int c_ = min((st_), nchunks - 1) + rot;                                                 \
+        c_ = c_ >= nchunks ? c_ - nchunks : c_;                                                 \
+        const int64_t ko_ = (int64_t)c_ * (kSkChunk * 2);                                       \
         __builtin_amdgcn_global_load_lds((const void*)(src[0] + ko_),                           \
                                          (lds_ptr_t)((sX_) + 8 * w * kSkChunk), 16, 0, 0);      \
         _Pragma("unroll") for (int j = 1; j < P; ++j)                                           \
             __builtin_amdgcn_global_load_lds((const void*)(src[j] + ko_),                       \
                                              (lds_ptr_t)((sW_) + 8 * (w + 4 * j - 4) * kSkChunk), 16, 0, 0); \
     } while (0)
-
-    // this wave's K steps inside a chunk
-    const int s0 = NBLK >= 4 ? 0 : (w / NBLK) * (4 / KS);
-    constexpr int NS = 4 / KS;
 
 #define MOE_SK_MFMA(sX_, sW_)                                                                   \
     do {                                                                                        \
@@ -76,15 +79,17 @@ __device__ __forceinline__ void skinny_mma(const char* const* src, int nchunks, 
             const bf16x8_t xa_ = as_bf16x8(*reinterpret_cast<const uint4*>(                     \
                 (sX_) + r32 * kSkChunk + ((c_ ^ swz(r32)) * 8)));                               \
             _Pragma("unroll") for (int i_ = 0; i_ < BPW; ++i_) {                                \
-                const int r_ = skinny_block<NBLK, PAIRED>(w, i_) * 32 + r32;                    \
+                const int r_ = skinny_block<Sh, PAIRED>(w, i_) * 32 + r32;                      \
                 const bf16x8_t wb_ = as_bf16x8(*reinterpret_cast<const uint4*>(                 \
                     (sW_) + r_ * kSkChunk + ((c_ ^ swz(r_)) * 8)));                             \
                 acc[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa_, wb_, acc[i_], 0, 0, 0);  \
             }                                                                                   \
         }                                                                                       \
     } while (0)
-// chunk st_ in buffer (sX_, sW_); the buffer of chunk st_ - 1 is refilled
-// with chunk st_ - 1 + NST once every wave is past this barrier
+// Chunk st_ from buffer (sX_, sW_).  When every wave is past this barrier the
+// buffer of chunk st_ - 1 is free and takes chunk st_ - 1 + NST.  Issued
+// chunks are consecutive, so waiting until NST - 2 chunks (of P instructions
+// each) are outstanding means chunk st_ has landed.
 #define MOE_SK_STAGE(sX_, sW_, sXp_, sWp_, st_)                                                 \
     do {                                                                                        \
         __builtin_amdgcn_s_waitcnt(wait_vmcnt((NST - 2) * P));                                  \
@@ -97,8 +102,7 @@ __device__ __forceinline__ void skinny_mma(const char* const* src, int nchunks, 
 
     MOE_SK_DMA(sX0, sW0, 0);
     MOE_SK_DMA(sX1, sW1, 1);
-    MOE_SK_DMA(sX2, sW2, 2);
-    if (NST > 3) MOE_SK_DMA(sX3, sW3, 3);
+    if (NST > 3) MOE_SK_DMA(sX2, sW2, 2);
     for (int c = 0; c < nchunks; c += NST) {
         if (NST > 3) {
             MOE_SK_STAGE(sX0, sW0, sX3, sW3, c);
