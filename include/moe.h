@@ -162,6 +162,10 @@ int moe_combine(const moe_config* cfg, const void* expert_out, const float* topk
  *   topk_ids_out [T,k], topk_weights_out [T,k], expert_counts_out [E]:
  *   optional copies of the routing (nullable; the workspace is used when
  *   NULL).
+ * Same arithmetic as the entry points above, except that with few tokens the
+ * router logits and, in bf16, the down projections may be summed over K
+ * ranges (fixed order; deterministic), so results can differ from the
+ * step-by-step calls in the last bits and routing at near-ties.
  */
 int moe_forward(const moe_config* cfg, const void* x, const void* w_router, const void* w_gate,
                 const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,

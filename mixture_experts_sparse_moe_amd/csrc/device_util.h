@@ -48,5 +48,7 @@ __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // s_waitcnt immediate (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
 // [6:4], lgkmcnt [11:8]) waiting for vmcnt <= n only.
 constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// ... and for lgkmcnt == 0 as well (every LDS access of the wave done).
+constexpr int wait_vmcnt_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
 }  // namespace moe

@@ -90,7 +90,7 @@ Splits splits(const moe_config* c) {
 
 // Device workspace layout.  Every region starts on a 256-byte boundary.
 struct Layout {
-    size_t ids, wts, counts, offsets, chunk, sorted, pos, H, O, Hs, S, total;
+    size_t ids, wts, counts, offsets, chunk, sorted, pos, H, O, Hs, S, rpart, total;
     size_t dispatch_need, ffn_need;   // bytes used by moe_dispatch / moe_expert_ffn (from 0)
 };
 
@@ -114,6 +114,8 @@ Layout layout(const moe_config* c) {
     const Splits sp = splits(c);
     L.O = take(sp.routed * P * c->d_model * elem(c));
     L.S = take(c->num_shared ? sp.shared * T * c->d_model * elem(c) : 0);
+    const int rr = route_ranges(c->num_tokens, c->d_model, c->dtype == MOE_BF16);
+    L.rpart = take(rr > 1 ? (size_t)rr * T * E * sizeof(float) : 0);
     L.total = o;
     L.dispatch_need = align_up(nchunks * E * sizeof(int32_t));
     return L;
@@ -139,11 +141,16 @@ int check_ptr(const void* p, bool empty_ok) {
         if ((expr) != hipSuccess) return MOE_ERR_HIP;  \
     } while (0)
 
+// part: scratch for the partial logits of a K-split router (moe_forward,
+// batches of few token blocks), or nullptr for the one-kernel router.
 int run_route(const moe_config* c, const void* x, const void* w_router, int32_t* ids, float* wts,
-              float* gap, hipStream_t s) {
+              float* gap, hipStream_t s, float* part = nullptr) {
     RouteArgs a{x, w_router, ids, wts, gap, c->num_tokens, c->d_model, c->num_experts,
                 c->top_k, c->score_fn, c->renormalize};
-    MOE_HIP(launch_route(a, c->dtype == MOE_BF16, s));
+    const bool bf16 = c->dtype == MOE_BF16;
+    const int rr = route_ranges(c->num_tokens, c->d_model, bf16);
+    if (part && rr > 1) MOE_HIP(launch_route_split(a, rr, part, s));
+    else MOE_HIP(launch_route(a, bf16, s));
     return MOE_OK;
 }
 
@@ -351,7 +358,7 @@ int moe_forward_staged(const moe_config* cfg, const void* x, const void* w_route
         for (int i = 1; i < MOE_NUM_STAGES; ++i) MOE_TRY(mark(ev, i, s));
         return MOE_OK;
     }
-    MOE_TRY(run_route(cfg, x, w_router, ids, wts, nullptr, s));
+    MOE_TRY(run_route(cfg, x, w_router, ids, wts, nullptr, s, at<float>(ws, L.rpart)));
     MOE_TRY(mark(ev, 0, s));
     MOE_TRY(run_dispatch(cfg, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s));
     MOE_TRY(mark(ev, 1, s));

@@ -21,6 +21,11 @@ struct RouteArgs {
     int renorm;
 };
 hipError_t launch_route(const RouteArgs& a, bool bf16, hipStream_t s);
+// bf16 only: the K chunks in `ranges` ranges, one workgroup per (32 tokens,
+// range), partial logits in part [ranges, T, E] fp32, then a second kernel
+// adds them in range order and selects.  For batches of few token blocks.
+int route_ranges(int T, int d, bool bf16);
+hipError_t launch_route_split(const RouteArgs& a, int ranges, float* part, hipStream_t s);
 
 // ---- dispatch: histogram, scan, stable scatter ------------------------------
 constexpr int kDispatchChunk = 2048;   // pairs per chunk (one workgroup each)

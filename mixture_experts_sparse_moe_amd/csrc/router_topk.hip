@@ -26,6 +26,8 @@
 // fp32: plain FMA dot products.
 // Top-k: one wave per token, 64-bit keys (orderable logit bits, inverted
 // expert index) reduced with a butterfly; k rounds.
+#include <algorithm>
+
 #include "device_util.h"
 #include "moe_internal.h"
 #include "skinny.h"
@@ -61,11 +63,11 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 }
 
 // Logits of 32 tokens x all experts (E <= 32 NBLK) into lds[32][kLogitStride]
-// (bf16 inputs, MFMA, LDS-staged K chunks).
+// (bf16 inputs, MFMA, LDS-staged K chunks), over the K chunks [c0, c0 + nc).
 template <int NBLK>
-__device__ __forceinline__ void logits_bf16(const RouteArgs& a, int t0, float* lds, uint16_t* sX0,
-                                            uint16_t* sX1, uint16_t* sX2, uint16_t* sX3, uint16_t* sW0,
-                                            uint16_t* sW1, uint16_t* sW2, uint16_t* sW3) {
+__device__ __forceinline__ void logits_bf16(const RouteArgs& a, int t0, int c0, int nc, float* lds,
+                                            uint16_t* sX0, uint16_t* sX1, uint16_t* sX2, uint16_t* sX3,
+                                            uint16_t* sW0, uint16_t* sW1, uint16_t* sW2, uint16_t* sW3) {
     using Sh = SkinnyShape<NBLK>;
     constexpr int KS = Sh::KS, BPW = Sh::BPW, P = Sh::P;
     static_assert(KS == 1 || BPW == 1, "partial tiles of one block per wave");
@@ -78,14 +80,15 @@ __device__ __forceinline__ void logits_bf16(const RouteArgs& a, int t0, float* l
     // (rows past E repeat the last)
     const char* src[P];
     {
+        const int64_t kb = (int64_t)c0 * (kSkChunk * 2);
         const int rx = 8 * w + (lane >> 3);
         const int tok = min(t0 + rx, a.T - 1);
-        src[0] = static_cast<const char*>(a.x) + tok * rowb + (((lane & 7) ^ swz(rx)) * 16);
+        src[0] = static_cast<const char*>(a.x) + tok * rowb + kb + (((lane & 7) ^ swz(rx)) * 16);
 #pragma unroll
         for (int j = 1; j < P; ++j) {
             const int rw = 8 * (w + 4 * j - 4) + (lane >> 3);
             const int e = min(rw, a.E - 1);
-            src[j] = static_cast<const char*>(a.w) + e * rowb + (((lane & 7) ^ swz(rw)) * 16);
+            src[j] = static_cast<const char*>(a.w) + e * rowb + kb + (((lane & 7) ^ swz(rw)) * 16);
         }
     }
     f32x16_t acc[BPW];
@@ -93,7 +96,7 @@ __device__ __forceinline__ void logits_bf16(const RouteArgs& a, int t0, float* l
     for (int i = 0; i < BPW; ++i)
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
-    skinny_mma<Sh, false>(src, a.d / kSkChunk, 0, sX0, sX1, sX2, sX3, sW0, sW1, sW2, sW3, acc);
+    skinny_mma<Sh, false>(src, nc, 0, sX0, sX1, sX2, sX3, sW0, sW1, sW2, sW3, acc);
     const int b0 = skinny_block<Sh, false>(w, 0);
 
     // D element j of block i: token row 8 (j / 4) + 4 half + j % 4, expert r32
@@ -149,20 +152,9 @@ __device__ void logits_f32(const RouteArgs& a, int t0, float* lds) {
     __syncthreads();
 }
 
-// NBLK = 0: fp32 inputs; else bf16 with E <= 32 NBLK.
-template <int NBLK>
-__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
-    constexpr int NB = NBLK ? NBLK : 1;
-    using St = SkinnyShape<NB>;
-    constexpr int XS = NBLK ? St::XS : 8, WS = NBLK ? St::WS : 8;
-    constexpr int X3 = St::NST > 3 ? XS : 8, W3 = St::NST > 3 ? WS : 8;
-    __shared__ float lds[kLogitFloats];
-    __shared__ __align__(16) uint16_t sX0[XS], sX1[XS], sX2[XS], sX3[X3];
-    __shared__ __align__(16) uint16_t sW0[WS], sW1[WS], sW2[WS], sW3[W3];
-    const int t0 = blockIdx.x * kBT;
-    if (NBLK) logits_bf16<NB>(a, t0, lds, sX0, sX1, sX2, sX3, sW0, sW1, sW2, sW3);
-    else logits_f32(a, t0, lds);
-
+// Top-k selection and gates of tokens t0 .. t0 + 31 from their logits in
+// lds[32][kLogitStride].
+__device__ __forceinline__ void topk_rows(const RouteArgs& a, int t0, const float* lds) {
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     for (int row = w; row < kBT; row += 4) {
@@ -234,7 +226,79 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     }
 }
 
+// Stage buffers of the bf16 logits (NBLK = 0, fp32: none).
+#define MOE_ROUTE_LDS(NBLK_)                                                                    \
+    constexpr int NB = (NBLK_) ? (NBLK_) : 1;                                                   \
+    using St = SkinnyShape<NB>;                                                                 \
+    constexpr int XS = (NBLK_) ? St::XS : 8, WS = (NBLK_) ? St::WS : 8;                         \
+    constexpr int X3 = St::NST > 3 ? XS : 8, W3 = St::NST > 3 ? WS : 8;                         \
+    __shared__ float lds[kLogitFloats];                                                         \
+    __shared__ __align__(16) uint16_t sX0[XS], sX1[XS], sX2[XS], sX3[X3];                       \
+    __shared__ __align__(16) uint16_t sW0[WS], sW1[WS], sW2[WS], sW3[W3]
+
+// One workgroup per 32 tokens.  NBLK = 0: fp32 inputs; else bf16 with E <= 32 NBLK.
+template <int NBLK>
+__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
+    MOE_ROUTE_LDS(NBLK);
+    const int t0 = blockIdx.x * kBT;
+    if (NBLK) logits_bf16<NB>(a, t0, 0, a.d / kSkChunk, lds, sX0, sX1, sX2, sX3, sW0, sW1, sW2, sW3);
+    else logits_f32(a, t0, lds);
+    topk_rows(a, t0, lds);
+}
+
+// Few token blocks: the K chunks are cut into ks ranges, one workgroup per
+// (token block, range), whose fp32 logits go to part[range][T][E] ...
+template <int NBLK>
+__global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a, float* part) {
+    MOE_ROUTE_LDS(NBLK);
+    const int t0 = blockIdx.x * kBT;
+    const int r = blockIdx.y, nr = gridDim.y, n = a.d / kSkChunk;
+    const int c0 = (int)((int64_t)r * n / nr), c1 = (int)((int64_t)(r + 1) * n / nr);
+    logits_bf16<NB>(a, t0, c0, c1 - c0, lds, sX0, sX1, sX2, sX3, sW0, sW1, sW2, sW3);
+    float* out = part + (int64_t)r * a.T * a.E;
+    for (int idx = threadIdx.x; idx < kBT * a.E; idx += 256) {
+        const int row = idx / a.E, e = idx - row * a.E;
+        if (t0 + row < a.T) out[(int64_t)(t0 + row) * a.E + e] = lds[row * kLogitStride + e];
+    }
+}
+
+// ... and one workgroup per token block adds the ranges in order and selects.
+__global__ __launch_bounds__(256) void route_finish_kernel(RouteArgs a, const float* part, int nr) {
+    __shared__ float lds[kLogitFloats];
+    const int t0 = blockIdx.x * kBT;
+    for (int idx = threadIdx.x; idx < kBT * a.E; idx += 256) {
+        const int row = idx / a.E, e = idx - row * a.E;
+        const int t = min(t0 + row, a.T - 1);
+        float v = 0.0f;
+        for (int r = 0; r < nr; ++r) v += part[((int64_t)r * a.T + t) * a.E + e];
+        lds[row * kLogitStride + e] = v;
+    }
+    __syncthreads();
+    topk_rows(a, t0, lds);
+}
+
 }  // namespace
+
+int route_ranges(int T, int d, bool bf16) {
+    if (!bf16 || T <= 0) return 1;
+    const int blocks = (T + kBT - 1) / kBT;
+    // about 128 workgroups, each range at least 4 chunks of 64
+    const int r = std::min((128 + blocks - 1) / blocks, d / (4 * kSkChunk));
+    return std::max(r, 1);
+}
+
+hipError_t launch_route_split(const RouteArgs& a, int ranges, float* part, hipStream_t s) {
+    if (a.T == 0) return hipSuccess;
+    if (ranges < 1 || ranges > a.d / kSkChunk || a.E > 256) return hipErrorInvalidValue;
+    dim3 grid((a.T + kBT - 1) / kBT, ranges), block(256);
+    const int nb = (a.E + 31) / 32;
+    if (nb <= 1) hipLaunchKernelGGL(route_partial_kernel<1>, grid, block, 0, s, a, part);
+    else if (nb <= 2) hipLaunchKernelGGL(route_partial_kernel<2>, grid, block, 0, s, a, part);
+    else if (nb <= 4) hipLaunchKernelGGL(route_partial_kernel<4>, grid, block, 0, s, a, part);
+    else hipLaunchKernelGGL(route_partial_kernel<8>, grid, block, 0, s, a, part);
+    hipLaunchKernelGGL(route_finish_kernel, dim3(grid.x), block, 0, s, a, (const float*)part, ranges);
+    return hipGetLastError();
+}
 
 hipError_t launch_route(const RouteArgs& a, bool bf16, hipStream_t s) {
     if (a.T == 0) return hipSuccess;

@@ -89,10 +89,13 @@ __device__ __forceinline__ void skinny_mma(const char* const* src, int nchunks, 
 // Chunk st_ from buffer (sX_, sW_).  When every wave is past this barrier the
 // buffer of chunk st_ - 1 is free and takes chunk st_ - 1 + NST.  Issued
 // chunks are consecutive, so waiting until NST - 2 chunks (of P instructions
-// each) are outstanding means chunk st_ has landed.
+// each) are outstanding means chunk st_ has landed.  The wait also covers the
+// wave's LDS reads: a fragment read of chunk st_ - 1 still queued when the
+// refill is issued could otherwise see the new data (operands that hit in
+// the cache come back fast).
 #define MOE_SK_STAGE(sX_, sW_, sXp_, sWp_, st_)                                                 \
     do {                                                                                        \
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt((NST - 2) * P));                                  \
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt_lgkm0((NST - 2) * P));                            \
         __builtin_amdgcn_s_barrier();                                                           \
         __builtin_amdgcn_sched_barrier(0);                                                      \
         MOE_SK_DMA(sXp_, sWp_, (st_) - 1 + NST);                                                \

@@ -37,6 +37,11 @@ SMALL = {
     "bf16_e3_k2": S("c", T=97, d=64, E=3, k=2, d_ff=64),
     "bf16_e256_k16": S("c", T=100, d=128, E=256, k=16, d_ff=64),
     "fp32_e6_k6_dense": S("c", T=100, d=64, E=6, k=6, d_ff=128, dtype=synth.F32),
+    # few tokens, wide rows: K-split router and the 32-row expert GEMMs
+    "bf16_decode_e64_k6": S("c", T=40, d=1024, E=64, k=6, d_ff=192),
+    "bf16_decode_e256_k8_shared": S("c", T=8, d=2048, E=256, k=8, d_ff=64, num_shared=1,
+                                    d_ff_shared=128, score_fn=synth.SIGMOID),
+    "bf16_decode_e100_k3": S("c", T=70, d=512, E=100, k=3, d_ff=320),
     "fp32_e32_k4_sigmoid_shared": S("c", T=130, d=128, E=32, k=4, d_ff=192, num_shared=1,
                                     d_ff_shared=128, score_fn=synth.SIGMOID, dtype=synth.F32),
 }
@@ -65,14 +70,16 @@ def check_layer(sh, inp, sample=None, check_expert_out=True):
     ref = oracle_routing(inp, sh)
     gids = to_host(st["ids"])
     exempt = check_routing(gids, ref, sh.k)
-    # the whole-layer call routes exactly like the step-by-step calls; its y
-    # is checked against the oracle below (moe_forward may run the down
-    # projection in K ranges, which rounds differently from moe_expert_ffn)
-    np.testing.assert_array_equal(to_host(fw["ids"]), gids)
-    np.testing.assert_array_equal(to_host(fw["weights"]), to_host(st["weights"]))
+    # the whole-layer call may sum the router logits and the down projection
+    # over K ranges, which rounds differently from the step-by-step calls:
+    # its routing is checked against the oracle by the same rules
+    fids = to_host(fw["ids"])
+    fexempt = check_routing(fids, ref, sh.k)
     # gates for the GPU's ids
     rf = oracle.route(ref["logits"], sh.k, sh.score_fn, sh.renormalize, forced_ids=gids)
     np.testing.assert_allclose(to_host(st["weights"]), rf["gates"], atol=1e-5, rtol=0)
+    rff = oracle.route(ref["logits"], sh.k, sh.score_fn, sh.renormalize, forced_ids=fids)
+    np.testing.assert_allclose(to_host(fw["weights"]), rff["gates"], atol=1e-5, rtol=0)
     # logit margin of the k-th choice
     gap = to_host(st["gap"])
     if sh.k < sh.E:
@@ -84,7 +91,7 @@ def check_layer(sh, inp, sample=None, check_expert_out=True):
     d = oracle.dispatch(gids, sh.E)
     for n in ("counts", "offsets", "sorted_pairs", "pair_pos"):
         np.testing.assert_array_equal(to_host(st[n]), d[n], err_msg=n)
-    np.testing.assert_array_equal(to_host(fw["counts"]), d["counts"])
+    np.testing.assert_array_equal(to_host(fw["counts"]), oracle.dispatch(fids, sh.E)["counts"])
     tau = TAU[sh.dtype]
     widen = synth.bf16_to_f64 if sh.dtype == synth.BF16 else (lambda a: a.astype(np.float64))
     # expert outputs, per expert in grouped order
@@ -106,8 +113,10 @@ def check_layer(sh, inp, sample=None, check_expert_out=True):
     r = oracle.forward_tokens(inp, sh.k, toks, sh.score_fn, sh.renormalize, forced_ids=gids[toks])
     y = widen(to_host(st["y"]))[toks]
     rel = assert_close(y, r["y"], tau, "y of the step-by-step calls")
+    if not np.array_equal(fids[toks], gids[toks]):
+        r = oracle.forward_tokens(inp, sh.k, toks, sh.score_fn, sh.renormalize, forced_ids=fids[toks])
     rel = max(rel, assert_close(widen(to_host(fw["y"]))[toks], r["y"], tau, "y of moe_forward"))
-    say(f"[ok] max|err|/max|y| = {rel:.3e}, near-tie tokens {exempt.tolist()}, "
+    say(f"[ok] max|err|/max|y| = {rel:.3e}, near-tie tokens {exempt.tolist()} / {fexempt.tolist()}, "
         f"counts max/mean {d['counts'].max() / max(d['counts'].mean(), 1e-9):.2f}")
     return dict(rel=rel, exempt=exempt, counts=d["counts"])
 
@@ -187,3 +196,29 @@ def test_deterministic_and_stream_independent():
     t.cuda.synchronize()
     for n in ("y", "ids", "weights", "counts"):
         np.testing.assert_array_equal(to_host(a[n]), to_host(b[n]), err_msg=n)
+
+
+def test_decode_paths_deterministic():
+    """Few tokens (32-row expert GEMMs, K-split router): repeated whole-layer
+    and expert-FFN calls give bitwise identical outputs.  Every expert block
+    is checked against the oracle in test_small_layer; a race between a
+    stage buffer's last reads and its refill showed up here as run-to-run
+    differences in single row blocks."""
+    t = torch()
+    sh = SMALL["bf16_decode_e100_k3"]
+    L = DeviceLayer(sh, synth.make_inputs(sh, 7))
+    st = L.steps()
+    ys = [to_host(L.forward()["y"]) for _ in range(6)]
+    t.cuda.synchronize()
+    for y in ys[1:]:
+        np.testing.assert_array_equal(y, ys[0])
+    import mixture_experts_sparse_moe_amd as moe
+    outs = []
+    for _ in range(6):
+        out = L.empty_act(sh.T * sh.k, sh.d)
+        moe.moe_expert_ffn(L.cfg, L.d["x"], st["sorted_pairs"], st["offsets"], L.d["w_gate"], L.d["w_up"],
+                           L.d["w_down"], None, None, None, out, None, L.ws)
+        outs.append(out)
+    t.cuda.synchronize()
+    for o in outs:
+        np.testing.assert_array_equal(to_host(o), to_host(st["expert_out"]))
