@@ -181,7 +181,10 @@ int moe_forward(const moe_config* cfg, const void* x, const void* w_router, cons
  *                 right after stage i is enqueued:
  *                 0 route, 1 dispatch, 2 routed gate/up GEMM (+SiLU*up),
  *                 3 routed down GEMM, 4 shared gate/up, 5 shared down,
- *                 6 combine.  Stages 4-5 are empty when num_shared == 0.
+ *                 6 combine.  Stages 4-5 are empty when num_shared == 0;
+ *                 stage 1 is empty when the batch is at most 32 bf16
+ *                 tokens with a K-split router, whose last kernel then
+ *                 also groups the pairs (its time counts in stage 0).
  *   start_event:  recorded before stage 0 (nullable).
  * The elapsed time between consecutive events is the stage's device time.
  */

@@ -143,13 +143,19 @@ int check_ptr(const void* p, bool empty_ok) {
 
 // part: scratch for the partial logits of a K-split router (moe_forward,
 // batches of few token blocks), or nullptr for the one-kernel router.
+// disp (with part): the dispatch of these ids, run by the router's second
+// kernel when the batch is one block of at most 32 tokens.  Returns in
+// *dispatched whether it did.
 int run_route(const moe_config* c, const void* x, const void* w_router, int32_t* ids, float* wts,
-              float* gap, hipStream_t s, float* part = nullptr) {
+              float* gap, hipStream_t s, float* part = nullptr, const DispatchArgs* disp = nullptr,
+              bool* dispatched = nullptr) {
     RouteArgs a{x, w_router, ids, wts, gap, c->num_tokens, c->d_model, c->num_experts,
                 c->top_k, c->score_fn, c->renormalize};
     const bool bf16 = c->dtype == MOE_BF16;
     const int rr = route_ranges(c->num_tokens, c->d_model, bf16);
-    if (part && rr > 1) MOE_HIP(launch_route_split(a, rr, part, s));
+    const bool fuse = part && rr > 1 && disp && c->num_tokens <= 32;
+    if (dispatched) *dispatched = fuse;
+    if (part && rr > 1) MOE_HIP(launch_route_split(a, rr, part, fuse ? disp : nullptr, s));
     else MOE_HIP(launch_route(a, bf16, s));
     return MOE_OK;
 }
@@ -358,9 +364,12 @@ int moe_forward_staged(const moe_config* cfg, const void* x, const void* w_route
         for (int i = 1; i < MOE_NUM_STAGES; ++i) MOE_TRY(mark(ev, i, s));
         return MOE_OK;
     }
-    MOE_TRY(run_route(cfg, x, w_router, ids, wts, nullptr, s, at<float>(ws, L.rpart)));
+    const DispatchArgs disp{ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk),
+                            cfg->num_tokens * cfg->top_k, cfg->num_experts};
+    bool dispatched = false;
+    MOE_TRY(run_route(cfg, x, w_router, ids, wts, nullptr, s, at<float>(ws, L.rpart), &disp, &dispatched));
     MOE_TRY(mark(ev, 0, s));
-    MOE_TRY(run_dispatch(cfg, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s));
+    if (!dispatched) MOE_TRY(run_dispatch(cfg, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s));
     MOE_TRY(mark(ev, 1, s));
     void* O = at<void>(ws, L.O);
     void* S = cfg->num_shared ? at<void>(ws, L.S) : nullptr;

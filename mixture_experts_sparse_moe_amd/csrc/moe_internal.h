@@ -9,6 +9,20 @@ namespace moe {
 
 using bf16_t = uint16_t;  // bf16 storage: upper half of an IEEE fp32
 
+// ---- dispatch: histogram, scan, stable scatter ------------------------------
+constexpr int kDispatchChunk = 2048;   // pairs per chunk (one workgroup each)
+struct DispatchArgs {
+    const int32_t* ids;     // [P]
+    int32_t* counts;        // [E]
+    int32_t* offsets;       // [E+1]
+    int32_t* sorted_pairs;  // [P]
+    int32_t* pair_pos;      // [P]
+    int32_t* chunk_counts;  // [nchunks, E] scratch
+    int P, E;
+};
+int dispatch_num_chunks(int P);
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+
 // ---- router + top-k ---------------------------------------------------------
 struct RouteArgs {
     const void* x;          // [T, d]
@@ -24,22 +38,11 @@ hipError_t launch_route(const RouteArgs& a, bool bf16, hipStream_t s);
 // bf16 only: the K chunks in `ranges` ranges, one workgroup per (32 tokens,
 // range), partial logits in part [ranges, T, E] fp32, then a second kernel
 // adds them in range order and selects.  For batches of few token blocks.
+// With d (T <= 32 only; d->ids == a.ids) the second kernel also runs the
+// dispatch of the pairs.
 int route_ranges(int T, int d, bool bf16);
-hipError_t launch_route_split(const RouteArgs& a, int ranges, float* part, hipStream_t s);
-
-// ---- dispatch: histogram, scan, stable scatter ------------------------------
-constexpr int kDispatchChunk = 2048;   // pairs per chunk (one workgroup each)
-struct DispatchArgs {
-    const int32_t* ids;     // [P]
-    int32_t* counts;        // [E]
-    int32_t* offsets;       // [E+1]
-    int32_t* sorted_pairs;  // [P]
-    int32_t* pair_pos;      // [P]
-    int32_t* chunk_counts;  // [nchunks, E] scratch
-    int P, E;
-};
-int dispatch_num_chunks(int P);
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+hipError_t launch_route_split(const RouteArgs& a, int ranges, float* part, const DispatchArgs* d,
+                              hipStream_t s);
 
 // ---- grouped GEMMs ----------------------------------------------------------
 // One "problem group" of the grouped GEMM: rows of A (optionally gathered)

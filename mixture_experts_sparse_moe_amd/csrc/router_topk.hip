@@ -25,11 +25,14 @@
 // order (deterministic).
 // fp32: plain FMA dot products.
 // Top-k: one wave per token, 64-bit keys (orderable logit bits, inverted
-// expert index) reduced with a butterfly; k rounds.
+// expert index) reduced with DPP lane moves; k rounds.
+// Few tokens (moe_forward): the K chunks are split over workgroups, whose
+// partial logits a second kernel adds in a fixed order before selecting.
 #include <algorithm>
 
 #include "device_util.h"
 #include "moe_internal.h"
+#include "dispatch_block.h"
 #include "skinny.h"
 
 namespace moe {
@@ -47,19 +50,52 @@ __device__ __forceinline__ uint32_t ord_bits(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+// Wave reductions with DPP lane moves inside rows of 16 lanes (quad swaps,
+// half-row and row mirrors), then the four row results through scalar
+// registers, combined in row order.  No LDS round trips: selecting the top k
+// for a token takes k + 1 maxima and one or two sums, one after another.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ unsigned long long max_step(unsigned long long v) {
+    const unsigned long long w =
+        ((unsigned long long)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+    return w > v ? w : v;
 }
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+    v = max_step<0xB1>(v);       // quad_perm(1, 0, 3, 2)
+    v = max_step<0x4E>(v);       // quad_perm(2, 3, 0, 1)
+    v = max_step<0x141>(v);      // row_half_mirror
+    v = max_step<0x140>(v);      // row_mirror: every lane holds its row's maximum
+    unsigned long long m = 0;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        unsigned long long w = __shfl_xor(v, o, 64);
-        v = (w > v) ? w : v;
+    for (int r = 0; r < 4; ++r) {
+        const unsigned long long x =
+            ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), 16 * r) << 32) |
+            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+        m = x > m ? x : m;
     }
-    return v;
+    return m;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float sum_step(float v) {
+    return v + __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v = sum_step<0xB1>(v);
+    v = sum_step<0x4E>(v);
+    v = sum_step<0x141>(v);
+    v = sum_step<0x140>(v);
+    float t = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) t += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16 * r));
+    return t;
 }
 
 // Logits of 32 tokens x all experts (E <= 32 NBLK) into lds[32][kLogitStride]
@@ -154,10 +190,11 @@ __device__ void logits_f32(const RouteArgs& a, int t0, float* lds) {
 
 // Top-k selection and gates of tokens t0 .. t0 + 31 from their logits in
 // lds[32][kLogitStride].
-__device__ __forceinline__ void topk_rows(const RouteArgs& a, int t0, const float* lds) {
+// With s_ids the ids are also kept in LDS, s_ids[(t - t0) * k + j].
+__device__ __forceinline__ void topk_rows(const RouteArgs& a, int t0, const float* lds, int* s_ids = nullptr) {
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    for (int row = w; row < kBT; row += 4) {
+    const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    for (int row = w; row < kBT; row += nw) {
         const int t = t0 + row;
         if (t >= a.T) break;
         const float* lrow = lds + row * kLogitStride;
@@ -221,6 +258,7 @@ __device__ __forceinline__ void topk_rows(const RouteArgs& a, int t0, const floa
         if (mine) {
             a.ids[(int64_t)t * a.k + lane] = my_e;
             a.weights[(int64_t)t * a.k + lane] = g;
+            if (s_ids) s_ids[row * a.k + lane] = my_e;
         }
         if (lane == 0 && a.gap) a.gap[t] = gap;
     }
@@ -262,19 +300,48 @@ __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a, float* 
     }
 }
 
-// ... and one workgroup per token block adds the ranges in order and selects.
-__global__ __launch_bounds__(256) void route_finish_kernel(RouteArgs a, const float* part, int nr) {
+// ... and one workgroup per token block adds the ranges in order and selects,
+// kFinishThreads threads (two tokens per wave: the selection is a chain of
+// wave reductions, so few tokens per wave keep it short).  With DISPATCH
+// (one token block) the first 256 threads then group the pairs by expert
+// (waves that have ended no longer take part in barriers).
+constexpr int kFinishThreads = 1024;
+
+template <bool DISPATCH>
+__global__ __launch_bounds__(kFinishThreads) void route_finish_kernel(RouteArgs a, const float* part, int nr,
+                                                                      DispatchArgs d) {
     __shared__ float lds[kLogitFloats];
     const int t0 = blockIdx.x * kBT;
-    for (int idx = threadIdx.x; idx < kBT * a.E; idx += 256) {
+    for (int idx = threadIdx.x; idx < kBT * a.E; idx += kFinishThreads) {
         const int row = idx / a.E, e = idx - row * a.E;
         const int t = min(t0 + row, a.T - 1);
+        const float* p = part + (int64_t)t * a.E + e;
+        const int64_t stride = (int64_t)a.T * a.E;
+        // the ranges' values are loaded 8 at a time, then added in range order
         float v = 0.0f;
-        for (int r = 0; r < nr; ++r) v += part[((int64_t)r * a.T + t) * a.E + e];
+        for (int r0 = 0; r0 < nr; r0 += 8) {
+            float q[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[i] = r0 + i < nr ? p[(r0 + i) * stride] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (r0 + i < nr) v += q[i];
+        }
         lds[row * kLogitStride + e] = v;
     }
     __syncthreads();
-    topk_rows(a, t0, lds);
+    if (DISPATCH) {
+        // the ids of this one block of tokens, from LDS
+        __shared__ int s_ids[kBT * 16];
+        topk_rows(a, t0, lds, s_ids);
+        __syncthreads();
+        if (threadIdx.x >= kDispatchThreads) return;
+        DispatchArgs dl = d;
+        dl.ids = s_ids;
+        dispatch_in_block(dl);
+    } else {
+        topk_rows(a, t0, lds);
+    }
 }
 
 }  // namespace
@@ -287,16 +354,20 @@ int route_ranges(int T, int d, bool bf16) {
     return std::max(r, 1);
 }
 
-hipError_t launch_route_split(const RouteArgs& a, int ranges, float* part, hipStream_t s) {
+hipError_t launch_route_split(const RouteArgs& a, int ranges, float* part, const DispatchArgs* d,
+                              hipStream_t s) {
     if (a.T == 0) return hipSuccess;
-    if (ranges < 1 || ranges > a.d / kSkChunk || a.E > 256) return hipErrorInvalidValue;
+    if (ranges < 1 || ranges > a.d / kSkChunk || a.E > 256 || (d && a.T > kBT)) return hipErrorInvalidValue;
     dim3 grid((a.T + kBT - 1) / kBT, ranges), block(256);
     const int nb = (a.E + 31) / 32;
     if (nb <= 1) hipLaunchKernelGGL(route_partial_kernel<1>, grid, block, 0, s, a, part);
     else if (nb <= 2) hipLaunchKernelGGL(route_partial_kernel<2>, grid, block, 0, s, a, part);
     else if (nb <= 4) hipLaunchKernelGGL(route_partial_kernel<4>, grid, block, 0, s, a, part);
     else hipLaunchKernelGGL(route_partial_kernel<8>, grid, block, 0, s, a, part);
-    hipLaunchKernelGGL(route_finish_kernel, dim3(grid.x), block, 0, s, a, (const float*)part, ranges);
+    const dim3 fblock(kFinishThreads);
+    if (d) hipLaunchKernelGGL(route_finish_kernel<true>, dim3(grid.x), fblock, 0, s, a, (const float*)part, ranges, *d);
+    else hipLaunchKernelGGL(route_finish_kernel<false>, dim3(grid.x), fblock, 0, s, a, (const float*)part, ranges,
+                            DispatchArgs{});
     return hipGetLastError();
 }
 
