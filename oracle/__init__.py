@@ -57,13 +57,13 @@ def lib():
         i32, i64, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
         L.oracle_logits.argtypes = [i64, i64, i32, i32, vp, vp, i32, vp, i32]
         L.oracle_logits.restype = None
-        L.oracle_route.argtypes = [i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        L.oracle_route.argtypes = [i64, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32]
         L.oracle_route.restype = i32
-        L.oracle_dispatch.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp]
+        L.oracle_dispatch.argtypes = [i64, i32, i32, i64, vp, vp, vp, vp, vp]
         L.oracle_dispatch.restype = i32
         L.oracle_expert_rows.argtypes = [i32, i32, i32, vp, i32, vp, i64, vp, vp, vp, vp, vp, i32]
         L.oracle_expert_rows.restype = None
-        L.oracle_forward_tokens.argtypes = ([i32] * 9 + [vp] * 8 + [vp, vp, i64, vp, vp, vp, vp, i32])
+        L.oracle_forward_tokens.argtypes = ([i32] * 9 + [vp] * 8 + [vp, i32, vp, i64, vp, vp, vp, vp, vp, i32])
         L.oracle_forward_tokens.restype = i32
         L.oracle_forward_expert_loop.argtypes = ([i64] + [i32] * 7 + [vp] * 7 + [vp, vp, vp, i32])
         L.oracle_forward_expert_loop.restype = i32
@@ -102,9 +102,11 @@ def logits(x: np.ndarray, w_router: np.ndarray, rows: slice | None = None,
 
 def route(lg: np.ndarray, k: int, score_fn: int = SOFTMAX, renormalize: int = 1,
           bias: np.ndarray | None = None, forced_ids: np.ndarray | None = None,
-          nthreads: int | None = None) -> dict:
-    """Scores, top-k ids (descending logit, ties to the lower index), gates and
-    the k-th/(k+1)-th gaps in score and logit space."""
+          nthreads: int | None = None, bias_on_scores: int = 0) -> dict:
+    """Scores, top-k ids (descending selection key, ties to the lower index),
+    gates from the unbiased scores, and the k-th/(k+1)-th gaps in score space
+    and in selection-key space (``gap_logit``: the key is the logit, or with a
+    bias the logit + bias or the score + bias)."""
     lg = np.ascontiguousarray(lg, dtype=np.float64)
     n, E = lg.shape
     ids = np.empty((n, k), dtype=np.int32)
@@ -114,27 +116,60 @@ def route(lg: np.ndarray, k: int, score_fn: int = SOFTMAX, renormalize: int = 1,
     gl = np.empty(n, dtype=np.float64)
     b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64)
     fi = None if forced_ids is None else np.ascontiguousarray(forced_ids, dtype=np.int32)
-    rc = lib().oracle_route(n, E, k, score_fn, renormalize, lg.ctypes.data, _ptr(b), _ptr(fi),
-                            ids.ctypes.data, gates.ctypes.data, scores.ctypes.data,
+    rc = lib().oracle_route(n, E, k, score_fn, renormalize, lg.ctypes.data, _ptr(b), int(bias_on_scores),
+                            _ptr(fi), ids.ctypes.data, gates.ctypes.data, scores.ctypes.data,
                             gs.ctypes.data, gl.ctypes.data, nthreads or _nthreads())
     if rc:
         raise ValueError(f"oracle_route failed ({rc})")
     return dict(ids=ids, gates=gates, scores=scores, gap_score=gs, gap_logit=gl)
 
 
-def dispatch(ids: np.ndarray, E: int) -> dict:
-    """Pairs p = t*k + j grouped by expert (index order), ascending p inside."""
+def capacity(T: int, k: int, E: int, factor: float) -> int:
+    """Slots per expert: ceil(T * k / E * factor) ("8.6 Mixture of Experts",
+    sec. 3.2; the pages leave the rounding open)."""
+    return int(np.ceil(T * k / E * factor - 1e-9))
+
+
+def dispatch(ids: np.ndarray, E: int, cap: int | None = None) -> dict:
+    """Pairs p = t*k + j grouped by expert (index order), ascending p inside;
+    with ``cap`` each expert keeps its first ``cap`` pairs in that order and
+    the rest are dropped (pair_pos -1, sorted_pairs -1 past the kept pairs)."""
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     T, k = ids.shape
     counts = np.empty(E, dtype=np.int32)
     offsets = np.empty(E + 1, dtype=np.int32)
     sp = np.empty(T * k, dtype=np.int32)
     pp = np.empty(T * k, dtype=np.int32)
-    rc = lib().oracle_dispatch(T, k, E, ids.ctypes.data, counts.ctypes.data, offsets.ctypes.data,
-                               sp.ctypes.data, pp.ctypes.data)
+    rc = lib().oracle_dispatch(T, k, E, -1 if cap is None else int(cap), ids.ctypes.data,
+                               counts.ctypes.data, offsets.ctypes.data, sp.ctypes.data,
+                               pp.ctypes.data)
     if rc:
         raise ValueError(f"oracle_dispatch failed ({rc})")
     return dict(counts=counts, offsets=offsets, sorted_pairs=sp, pair_pos=pp)
+
+
+def router_stats(scores: np.ndarray, ids: np.ndarray, score_fn: int = SOFTMAX,
+                 alpha: float = 1.0) -> dict:
+    """Load-balancing statistics of one batch ("8.6 Mixture of Experts",
+    sec. 3.1; "from the router to the all-to-all", Load balancing):
+      f_e = n_e / T, with n_e the pairs routed to expert e (before any
+            capacity drop); sum_e f_e = k;
+      P_e = mean over tokens of the router probability of e: the softmax
+            score, or the sigmoid score normalised over all experts;
+      L_aux = alpha * E * sum_e f_e P_e (= alpha under uniform routing, k = 1);
+      max_over_mean = max_e n_e / mean_e n_e."""
+    scores = np.asarray(scores, dtype=np.float64)
+    T, E = scores.shape
+    ids = np.asarray(ids)
+    n = np.zeros(E, dtype=np.float64)
+    for t in range(ids.shape[0]):
+        for j in range(ids.shape[1]):
+            n[ids[t, j]] += 1.0
+    prob = scores if score_fn == SOFTMAX else scores / scores.sum(1, keepdims=True)
+    f = n / T
+    P = prob.sum(0) / T
+    l_aux = alpha * E * float(np.sum(f * P))
+    return dict(f=f, P=P, l_aux=l_aux, max_over_mean=float(n.max() / n.mean()), counts=n)
 
 
 def expert_rows(e: int, x: np.ndarray, rows: np.ndarray, w_gate, w_up, w_down,
@@ -155,8 +190,10 @@ def expert_rows(e: int, x: np.ndarray, rows: np.ndarray, w_gate, w_up, w_down,
 
 def forward_tokens(inp: dict, k: int, tokens, score_fn: int = SOFTMAX, renormalize: int = 1,
                    forced_ids: np.ndarray | None = None, bias: np.ndarray | None = None,
-                   nthreads: int | None = None) -> dict:
-    """y for the listed tokens, token by token: y = sum_j g_j f_{id_j}(x) (+ f_s(x))."""
+                   nthreads: int | None = None, bias_on_scores: int = 0,
+                   keep: np.ndarray | None = None) -> dict:
+    """y for the listed tokens, token by token: y = sum_j g_j f_{id_j}(x) (+ f_s(x)),
+    skipping the pairs that ``keep`` [n,k] marks 0 (dropped for capacity)."""
     x = _c(inp["x"])
     wr, wg, wu, wd = (_c(inp[n]) for n in ("w_router", "w_gate", "w_up", "w_down"))
     sg, su, sd = (_c(inp.get(n)) for n in ("ws_gate", "ws_up", "ws_down"))
@@ -174,11 +211,13 @@ def forward_tokens(inp: dict, k: int, tokens, score_fn: int = SOFTMAX, renormali
     gates = np.empty((n, k), dtype=np.float64)
     fi = None if forced_ids is None else np.ascontiguousarray(forced_ids, dtype=np.int32)
     b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64)
+    kp = None if keep is None else np.ascontiguousarray(keep, dtype=np.int32)
     rc = lib().oracle_forward_tokens(d, E, k, f, S, f_s, score_fn, renormalize, _dtype_of(x),
                                      x.ctypes.data, wr.ctypes.data, wg.ctypes.data,
                                      wu.ctypes.data, wd.ctypes.data, _ptr(sg), _ptr(su), _ptr(sd),
-                                     _ptr(b), tokens.ctypes.data, n, _ptr(fi), y.ctypes.data,
-                                     ids.ctypes.data, gates.ctypes.data, nthreads or _nthreads())
+                                     _ptr(b), int(bias_on_scores), tokens.ctypes.data, n, _ptr(fi),
+                                     _ptr(kp), y.ctypes.data, ids.ctypes.data, gates.ctypes.data,
+                                     nthreads or _nthreads())
     if rc:
         raise ValueError(f"oracle_forward_tokens failed ({rc})")
     return dict(y=y, ids=ids, gates=gates)

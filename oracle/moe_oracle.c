@@ -93,18 +93,25 @@ static int before(const double* l, int a, int b) {
  *   ids   [n,k]  chosen experts, in selection order
  *   gates [n,k]  gate of each chosen expert
  *   scores [n,E] (nullable) all scores
- *   gap_score, gap_logit [n] (nullable): s_(k)-s_(k+1) and l_(k)-l_(k+1) in
- *       selection order; +inf when k == E.
- *   bias [E] (nullable): added to the logits for choosing only; the gates use
- *       the unbiased scores ("Mixture-of-Experts Internals", sec. 3.3).
+ *   gap_score, gap_key [n] (nullable): s_(k)-s_(k+1) and key_(k)-key_(k+1)
+ *       in selection order (key = the selection value below); +inf when
+ *       k == E.
+ *   bias [E] (nullable): a per-expert bias for choosing only; the gates use
+ *       the unbiased scores.  bias_on_scores = 0: key = logit + bias
+ *       ("Mixture-of-Experts Internals", sec. 3.3: top-k over the modified
+ *       routing logits); 1: key = score + bias ("Mixture-of-Experts, from the
+ *       router to the all-to-all", Load balancing: the bias is added to the
+ *       scores for choosing).  Without a bias, key = logit.
  *   forced_ids [n,k] (nullable): skip selection and use these ids.
  */
 static int route_one(int E, int k, int score_fn, int renorm, const double* l, const double* bias,
-                     const int32_t* forced, int32_t* id, double* gates, double* scores,
-                     double* gap_score, double* gap_logit, double* s, double* key, int* order) {
+                     int bias_on_scores, const int32_t* forced, int32_t* id, double* gates,
+                     double* scores, double* gap_score, double* gap_key, double* s, double* key,
+                     int* order) {
     scores_of(l, E, score_fn, s);
     if (scores) memcpy(scores, s, sizeof(double) * E);
-    for (int e = 0; e < E; ++e) key[e] = l[e] + (bias ? bias[e] : 0.0);
+    for (int e = 0; e < E; ++e)
+        key[e] = bias ? (bias_on_scores ? s[e] : l[e]) + bias[e] : l[e];
     /* full selection order by insertion: plain and obviously correct */
     for (int e = 0; e < E; ++e) {
         int p = e;
@@ -120,7 +127,7 @@ static int route_one(int E, int k, int score_fn, int renorm, const double* l, co
         for (int j = 0; j < k; ++j) id[j] = order[j];
     }
     if (gap_score) *gap_score = (k < E) ? s[order[k - 1]] - s[order[k]] : INFINITY;
-    if (gap_logit) *gap_logit = (k < E) ? key[order[k - 1]] - key[order[k]] : INFINITY;
+    if (gap_key) *gap_key = (k < E) ? key[order[k - 1]] - key[order[k]] : INFINITY;
     double denom = 0.0;
     for (int j = 0; j < k; ++j) denom += s[id[j]];
     for (int j = 0; j < k; ++j) gates[j] = renorm ? s[id[j]] / denom : s[id[j]];
@@ -128,8 +135,8 @@ static int route_one(int E, int k, int score_fn, int renorm, const double* l, co
 }
 
 int oracle_route(int64_t n, int E, int k, int score_fn, int renorm, const double* logits,
-                 const double* bias, const int32_t* forced_ids, int32_t* ids, double* gates,
-                 double* scores, double* gap_score, double* gap_logit, int nthreads) {
+                 const double* bias, int bias_on_scores, const int32_t* forced_ids, int32_t* ids,
+                 double* gates, double* scores, double* gap_score, double* gap_key, int nthreads) {
     if (k < 1 || k > E) return -2;
     int err = 0;
 #pragma omp parallel num_threads(nthreads)
@@ -139,10 +146,10 @@ int oracle_route(int64_t n, int E, int k, int score_fn, int renorm, const double
         int* order = (int*)malloc(sizeof(int) * E);
 #pragma omp for schedule(static)
         for (int64_t t = 0; t < n; ++t) {
-            int rc = route_one(E, k, score_fn, renorm, logits + t * E, bias,
+            int rc = route_one(E, k, score_fn, renorm, logits + t * E, bias, bias_on_scores,
                                forced_ids ? forced_ids + t * k : NULL, ids + t * k, gates + t * k,
                                scores ? scores + t * E : NULL, gap_score ? gap_score + t : NULL,
-                               gap_logit ? gap_logit + t : NULL, s, key, order);
+                               gap_key ? gap_key + t : NULL, s, key, order);
             if (rc) {
 #pragma omp atomic write
                 err = rc;
@@ -155,20 +162,30 @@ int oracle_route(int64_t n, int E, int k, int score_fn, int renorm, const double
 
 /*
  * Group the T*k (token, slot) pairs by expert: expert 0's pairs first, then
- * expert 1's, ...; inside a group, pairs in ascending pair index p = t*k + j.
- *   counts [E], offsets [E+1], sorted_pairs [T*k] (pair index at each
- *   grouped position), pair_pos [T*k] (grouped position of each pair).
+ * expert 1's, ...; inside a group, pairs in ascending pair index p = t*k + j
+ * ("What Actually Happens...", Step 3).
+ *   cap: each expert keeps at most cap pairs, the first ones in that order;
+ *       the others are dropped ("8.6 Mixture of Experts", sec. 3.2; "from the
+ *       router to the all-to-all", Capacity and token dropping).  cap < 0:
+ *       no limit.
+ *   counts [E] (pairs kept), offsets [E+1], sorted_pairs [T*k] (pair index at
+ *   each grouped position; -1 past the kept pairs), pair_pos [T*k] (grouped
+ *   position of each pair, -1 if dropped).
  */
-int oracle_dispatch(int64_t T, int k, int E, const int32_t* ids, int32_t* counts,
+int oracle_dispatch(int64_t T, int k, int E, int64_t cap, const int32_t* ids, int32_t* counts,
                     int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_pos) {
     int64_t P = T * k;
     int64_t pos = 0;
+    for (int64_t p = 0; p < P; ++p) {
+        if (ids[p] < 0 || ids[p] >= E) return -2;
+        pair_pos[p] = -1;
+        sorted_pairs[p] = -1;
+    }
     for (int e = 0; e < E; ++e) {
         offsets[e] = (int32_t)pos;
         int32_t c = 0;
         for (int64_t p = 0; p < P; ++p) {
-            if (ids[p] < 0 || ids[p] >= E) return -2;
-            if (ids[p] == e) {
+            if (ids[p] == e && (cap < 0 || c < cap)) {
                 sorted_pairs[pos] = (int32_t)p;
                 pair_pos[p] = (int32_t)pos;
                 ++pos; ++c;
@@ -177,7 +194,7 @@ int oracle_dispatch(int64_t T, int k, int E, const int32_t* ids, int32_t* counts
         counts[e] = c;
     }
     offsets[E] = (int32_t)pos;
-    return pos == P ? 0 : -2;
+    return 0;
 }
 
 /*
@@ -229,15 +246,18 @@ void oracle_expert_rows(int d, int f, int e, const void* x, int dtype, const int
  * Layer output for the tokens listed in `tokens[0..n)`, token by token, in
  * the per-token form y = sum_j g_j f_{ids_j}(x) + f_shared(x).
  *   forced_ids [n,k] (nullable): use these ids instead of selecting.
- *   bias [E] (nullable): selection-only bias.
+ *   bias [E] (nullable), bias_on_scores: selection-only bias (route_one).
+ *   keep [n,k] (nullable): 0 marks a pair dropped for capacity; a dropped
+ *       pair contributes nothing ("8.6 Mixture of Experts", sec. 3.2).
  *   y [n,d]; ids_out [n,k], gates_out [n,k] (both nullable).
  */
 int oracle_forward_tokens(int d, int E, int k, int f, int num_shared, int f_s, int score_fn,
                           int renorm, int dtype, const void* x, const void* w_r, const void* wg,
                           const void* wu, const void* wd, const void* sg, const void* su,
-                          const void* sd, const double* bias, const int32_t* tokens, int64_t n,
-                          const int32_t* forced_ids, double* y, int32_t* ids_out,
-                          double* gates_out, int nthreads) {
+                          const void* sd, const double* bias, int bias_on_scores,
+                          const int32_t* tokens, int64_t n, const int32_t* forced_ids,
+                          const int32_t* keep, double* y, int32_t* ids_out, double* gates_out,
+                          int nthreads) {
     if (k < 1 || k > E || num_shared < 0 || num_shared > 1) return -2;
     int err = 0;
 #pragma omp parallel num_threads(nthreads)
@@ -260,7 +280,7 @@ int oracle_forward_tokens(int d, int E, int k, int f, int num_shared, int f_s, i
                     acc += widen(x, dtype, t * d + c) * widen(w_r, dtype, (int64_t)e * d + c);
                 l[e] = acc;
             }
-            int rc = route_one(E, k, score_fn, renorm, l, bias,
+            int rc = route_one(E, k, score_fn, renorm, l, bias, bias_on_scores,
                                forced_ids ? forced_ids + i * k : NULL, id, g, NULL, NULL, NULL,
                                s, key, order);
             if (rc) {
@@ -271,6 +291,7 @@ int oracle_forward_tokens(int d, int E, int k, int f, int num_shared, int f_s, i
             double* yt = y + i * d;
             for (int c = 0; c < d; ++c) yt[c] = 0.0;
             for (int j = 0; j < k; ++j) {
+                if (keep && !keep[i * k + j]) continue;
                 swiglu_one(d, f, x, t * d, dtype, wg, wu, (int64_t)id[j] * f * d, wd,
                            (int64_t)id[j] * d * f, h, o);
                 for (int c = 0; c < d; ++c) yt[c] += g[j] * o[c];

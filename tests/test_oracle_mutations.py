@@ -25,7 +25,13 @@ MUTATIONS = {
     "dispatch_unstable": ("for (int64_t p = 0; p < P; ++p) {", "for (int64_t p = P - 1; p >= 0; --p) {"),
     "softmax_denominator": ("s[e] = exp(l[e] - m); z += s[e];", "s[e] = exp(l[e] - m); z += s[e] * 1.0000001;"),
     "logit_index": ("widen(w_r, dtype, (int64_t)e * d + c)", "widen(w_r, dtype, (int64_t)c * E + e)"),
+    "bias_space_ignored": ("key[e] = bias ? (bias_on_scores ? s[e] : l[e]) + bias[e] : l[e];",
+                           "key[e] = bias ? l[e] + bias[e] : l[e];"),
+    "capacity_off_by_one": ("(cap < 0 || c < cap)", "(cap < 0 || c <= cap)"),
+    "dropped_pair_counted": ("if (keep && !keep[i * k + j]) continue;", ";"),
+    "gate_from_key": ("denom += s[id[j]];", "denom += key[id[j]];"),
 }
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_next.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
@@ -39,6 +45,6 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                            "-o", str(lib), "-lm"])
     env = dict(os.environ, ORACLE_LIB_OVERRIDE=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        *(os.path.join(ROOT, "tests", f) for f in PIN_FILES)],
                        env=env, capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert r.returncode != 0, f"no pin failed for planted mistake {name}:\n{r.stdout[-2000:]}"
