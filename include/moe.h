@@ -150,7 +150,8 @@ int moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* sorted_p
  *   y[t] = sum_{j=0..k-1} topk_weights[t,j] * expert_out[pair_pos[t*k+j]]
  *          (+ shared_out[t])
  * summed in fp32 in slot order j = 0..k-1, then rounded to cfg->dtype.  No
- * atomics: every y row is written once.
+ * atomics: every y row is written once.  A slot whose pair_pos is -1 (a pair
+ * dropped for capacity, see moe_options) contributes nothing.
  *   shared_out nullable iff num_shared == 0.
  */
 int moe_combine(const moe_config* cfg, const void* expert_out, const float* topk_weights,
@@ -195,6 +196,63 @@ int moe_forward_staged(const moe_config* cfg, const void* x, const void* w_route
                        int32_t* topk_ids_out, float* topk_weights_out,
                        int32_t* expert_counts_out, void* ws, size_t ws_bytes, void* start_event,
                        void* const* stage_events, void* stream);
+
+/*
+ * Optional routing features.  A NULL moe_options*, or one with every field
+ * zero, is the plain layer above.
+ *   expert_bias [E] fp32 (device, nullable): a per-expert bias used only to
+ *       choose the experts; the gates stay the unbiased scores, renormalised
+ *       over the chosen set when cfg->renormalize ("Mixture-of-Experts
+ *       Internals", sec. 3.3, auxiliary-loss-free balancing; "from the router
+ *       to the all-to-all", Load balancing).
+ *   bias_on_scores: 0 = choose on logit + bias (the first page's form),
+ *       1 = on score + bias (the second page's form; the score is the
+ *       softmax probability or the sigmoid).  topk_gap is then the margin in
+ *       that selection space.
+ *   expert_capacity (> 0): each expert keeps at most this many pairs, the
+ *       first ones in pair order; the others are dropped and contribute
+ *       nothing ("8.6 Mixture of Experts", sec. 3.2; "from the router to the
+ *       all-to-all", Capacity and token dropping: capacity = T k / E times
+ *       the capacity factor, rounded as the caller chooses).  expert_counts
+ *       and expert_offsets then count the kept pairs, pair_pos is -1 for a
+ *       dropped pair, and sorted_pairs holds offsets[E] entries (the rest
+ *       are unspecified).  <= 0: no limit.
+ *   router_stats [2E + 2] fp32 (device, nullable): load statistics of the
+ *       batch ("8.6 Mixture of Experts", sec. 3.1; "from the router to the
+ *       all-to-all", Load balancing):
+ *         [0, E)   f_e = (pairs routed to e, before any capacity drop) / T
+ *         [E, 2E)  P_e = mean over tokens of e's router probability (softmax
+ *                  score; sigmoid scores normalised over all experts)
+ *         [2E]     L_aux = aux_alpha * E * sum_e f_e P_e  (sum_e f_e = k, so
+ *                  uniform routing gives aux_alpha * k)
+ *         [2E+1]   max_e n_e / mean_e n_e
+ *       Needs the workspace.  Sums are taken in a fixed order.
+ */
+typedef struct moe_options {
+    const float* expert_bias;
+    int32_t bias_on_scores;
+    int32_t expert_capacity;
+    float* router_stats;
+    float aux_alpha;
+} moe_options;
+
+/* moe_route with options.  ws: scratch of at least moe_workspace_bytes
+ * bytes when router_stats is set, else unused (nullable). */
+int moe_route_ex(const moe_config* cfg, const moe_options* opts, const void* x, const void* w_router,
+                 int32_t* topk_ids, float* topk_weights, float* topk_gap, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/* moe_dispatch with options (expert_capacity). */
+int moe_dispatch_ex(const moe_config* cfg, const moe_options* opts, const int32_t* topk_ids,
+                    int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_pairs,
+                    int32_t* pair_pos, void* ws, size_t ws_bytes, void* stream);
+
+/* moe_forward with options (bias, capacity, statistics). */
+int moe_forward_ex(const moe_config* cfg, const moe_options* opts, const void* x, const void* w_router,
+                   const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
+                   const void* ws_up, const void* ws_down, void* y, int32_t* topk_ids_out,
+                   float* topk_weights_out, int32_t* expert_counts_out, void* ws, size_t ws_bytes,
+                   void* stream);
 
 #ifdef __cplusplus
 }

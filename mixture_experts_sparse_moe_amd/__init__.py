@@ -8,7 +8,8 @@ library is missing, importing works but every call raises.
 
 Entry points (same names as the C ABI):
     moe_workspace_bytes, moe_route, moe_dispatch, moe_expert_ffn,
-    moe_combine, moe_forward, moe_forward_staged, moe_status_str
+    moe_combine, moe_forward, moe_forward_staged, moe_status_str,
+    moe_route_ex, moe_dispatch_ex, moe_forward_ex (with MoeOptions)
 """
 from __future__ import annotations
 
@@ -27,7 +28,8 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
 
 EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
-           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_staged")
+           "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_staged",
+           "moe_route_ex", "moe_dispatch_ex", "moe_forward_ex")
 MOE_NUM_STAGES = 7
 STAGE_NAMES = ("route", "dispatch", "gate_up_gemm", "down_gemm", "shared_gate_up", "shared_down",
                "combine")
@@ -52,6 +54,28 @@ class MoeConfig(ctypes.Structure):
     def of(cls, T, d, E, k, d_ff, num_shared=0, d_ff_shared=0, score_fn=MOE_SCORE_SOFTMAX,
            renormalize=1, dtype=MOE_BF16):
         return cls(T, d, E, k, d_ff, num_shared, d_ff_shared, score_fn, renormalize, dtype)
+
+
+class MoeOptions(ctypes.Structure):
+    """Mirror of ``moe_options``: selection-only expert bias, per-expert
+    capacity, router statistics.  Build with ``MoeOptions.of(...)``; the
+    tensors it points to must stay alive while the call runs."""
+    _fields_ = [("expert_bias", ctypes.c_void_p), ("bias_on_scores", ctypes.c_int32),
+                ("expert_capacity", ctypes.c_int32), ("router_stats", ctypes.c_void_p),
+                ("aux_alpha", ctypes.c_float)]
+
+    @classmethod
+    def of(cls, expert_bias=None, bias_on_scores=0, expert_capacity=0, router_stats=None, aux_alpha=0.0):
+        o = cls(_ptr(expert_bias), int(bias_on_scores), int(expert_capacity), _ptr(router_stats),
+                float(aux_alpha))
+        o._keep = (expert_bias, router_stats)
+        return o
+
+
+def capacity(T: int, k: int, E: int, factor: float) -> int:
+    """Slots per expert, ceil(T k / E * factor) (the pages leave the rounding open)."""
+    import math
+    return int(math.ceil(T * k / E * factor - 1e-9))
 
 
 _lib = None
@@ -82,6 +106,13 @@ def lib():
         L.moe_forward.restype = i32
         L.moe_forward_staged.argtypes = [cfgp] + [vp] * 12 + [vp, sz, vp, vp, vp]
         L.moe_forward_staged.restype = i32
+        optp = ctypes.POINTER(MoeOptions)
+        L.moe_route_ex.argtypes = [cfgp, optp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_route_ex.restype = i32
+        L.moe_dispatch_ex.argtypes = [cfgp, optp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_dispatch_ex.restype = i32
+        L.moe_forward_ex.argtypes = [cfgp, optp] + [vp] * 12 + [vp, sz, vp]
+        L.moe_forward_ex.restype = i32
         _lib = L
     return _lib
 
@@ -264,6 +295,69 @@ def moe_forward_staged(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, w
                                  _ptr(expert_counts), _ptr(ws), _ws_bytes(ws),
                                  ev_handle(start_event), evs, _stream(stream)),
         "moe_forward_staged")
+
+
+def _opts(opts):
+    return None if opts is None else ctypes.byref(opts)
+
+
+def _check_opts(cfg, opts, dev):
+    if opts is None:
+        return
+    torch = _torch()
+    b, st = opts._keep if hasattr(opts, "_keep") else (None, None)
+    _check(b, "expert_bias", (cfg.num_experts,), torch.float32, dev, optional=True)
+    _check(st, "router_stats", (2 * cfg.num_experts + 2,), torch.float32, dev, optional=True)
+
+
+def moe_route_ex(cfg, opts, x, w_router, topk_ids, topk_weights, topk_gap=None, ws=None, stream=None):
+    torch = _torch()
+    T, d, E, k = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k
+    dt, dev = _act_dtype(cfg), x.device
+    _check(x, "x", (T, d), dt, dev)
+    _check(w_router, "w_router", (E, d), dt, dev)
+    _check(topk_ids, "topk_ids", (T, k), torch.int32, dev)
+    _check(topk_weights, "topk_weights", (T, k), torch.float32, dev)
+    _check(topk_gap, "topk_gap", (T,), torch.float32, dev, optional=True)
+    _check_opts(cfg, opts, dev)
+    _rc(lib().moe_route_ex(ctypes.byref(cfg), _opts(opts), _ptr(x), _ptr(w_router), _ptr(topk_ids),
+                           _ptr(topk_weights), _ptr(topk_gap), _ptr(ws), _ws_bytes(ws), _stream(stream)),
+        "moe_route_ex")
+
+
+def moe_dispatch_ex(cfg, opts, topk_ids, expert_counts, expert_offsets, sorted_pairs, pair_pos, ws,
+                    stream=None):
+    torch = _torch()
+    T, E, k = cfg.num_tokens, cfg.num_experts, cfg.top_k
+    dev = topk_ids.device
+    _check(topk_ids, "topk_ids", (T, k), torch.int32, dev)
+    _check(expert_counts, "expert_counts", (E,), torch.int32, dev)
+    _check(expert_offsets, "expert_offsets", (E + 1,), torch.int32, dev)
+    _check(sorted_pairs, "sorted_pairs", (T * k,), torch.int32, dev)
+    _check(pair_pos, "pair_pos", (T * k,), torch.int32, dev)
+    _check_opts(cfg, opts, dev)
+    _rc(lib().moe_dispatch_ex(ctypes.byref(cfg), _opts(opts), _ptr(topk_ids), _ptr(expert_counts),
+                              _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(pair_pos), _ptr(ws),
+                              _ws_bytes(ws), _stream(stream)), "moe_dispatch_ex")
+
+
+def moe_forward_ex(cfg, opts, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
+                   topk_ids=None, topk_weights=None, expert_counts=None, ws=None, stream=None):
+    torch = _torch()
+    T, d, E, k = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k
+    dt, dev = _act_dtype(cfg), x.device
+    _check(x, "x", (T, d), dt, dev)
+    _check(w_router, "w_router", (E, d), dt, dev)
+    _check_experts(cfg, dev, w_gate, w_up, w_down, ws_gate, ws_up, ws_down)
+    _check(y, "y", (T, d), dt, dev)
+    _check(topk_ids, "topk_ids", (T, k), torch.int32, dev, optional=True)
+    _check(topk_weights, "topk_weights", (T, k), torch.float32, dev, optional=True)
+    _check(expert_counts, "expert_counts", (E,), torch.int32, dev, optional=True)
+    _check_opts(cfg, opts, dev)
+    _rc(lib().moe_forward_ex(ctypes.byref(cfg), _opts(opts), _ptr(x), _ptr(w_router), _ptr(w_gate),
+                             _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(y),
+                             _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_counts), _ptr(ws),
+                             _ws_bytes(ws), _stream(stream)), "moe_forward_ex")
 
 
 def alloc_workspace(cfg, device="cuda"):

@@ -8,7 +8,8 @@
 // vectors (8 elements per lane).
 // When the down projection was computed in K ranges, expert_out (and shared)
 // hold one bf16 slice per range; a row is the fp32 sum of its slices in slice
-// order, taken before the gate weight.
+// order, taken before the gate weight.  A pair with pair_pos -1 (dropped for
+// capacity, "8.6 Mixture of Experts", sec. 3.2) contributes nothing.
 #include "device_util.h"
 #include "moe_internal.h"
 
@@ -61,12 +62,13 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(CombineArgs a) {
         for (int jj = 0; jj < JB; ++jj)
 #pragma unroll
             for (int sl = 0; sl < S; ++sl)
-                if (j0 + jj < a.k)
+                if (j0 + jj < a.k && s_pos[j0 + jj] >= 0)
                     q[jj][sl] = *reinterpret_cast<const uint4*>(O + sl * a.part_stride +
                                                                 (int64_t)s_pos[j0 + jj] * a.d + v * 8);
 #pragma unroll
         for (int jj = 0; jj < JB; ++jj) {
             if (j0 + jj >= a.k) break;
+            if (s_pos[j0 + jj] < 0) continue;       // dropped for capacity: contributes nothing
             float row[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
             for (int sl = 0; sl < S; ++sl) add_bf16x8(q[jj][sl], row);
@@ -98,6 +100,7 @@ __global__ __launch_bounds__(kThreads) void combine_f32_kernel(CombineArgs a) {
         float acc = 0.0f;
         for (int j = 0; j < a.k; ++j) {
             const int pos = a.pair_pos[(int64_t)t * a.k + j];
+            if (pos < 0) continue;                  // dropped for capacity
             acc = fmaf(a.weights[(int64_t)t * a.k + j], O[(int64_t)pos * a.d + c], acc);
         }
         if (S) acc += S[(int64_t)t * a.d + c];

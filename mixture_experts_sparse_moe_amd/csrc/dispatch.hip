@@ -9,7 +9,10 @@
 //               histogram (integer LDS atomics) -> chunk_counts[chunk][e].
 //   2. scan:    one workgroup: per-expert totals over chunks, exclusive scan
 //               over experts -> counts, offsets; chunk_counts becomes each
-//               chunk's first grouped row per expert.
+//               chunk's first rank inside each expert.
+// With a capacity C ("8.6 Mixture of Experts", sec. 3.2) an expert keeps its
+// first C pairs in pair order: counts and offsets are of the kept pairs, and
+// a pair of rank >= C inside its expert gets pair_pos -1.
 //   3. scatter: one workgroup per chunk walks its pairs in order, 256 at a
 //               time.  A pair's rank among equal ids in its wave comes from a
 //               match mask built with 8 ballots over the id bits (E <= 256);
@@ -50,24 +53,25 @@ __global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(DispatchArgs a,
             a.chunk_counts[(int64_t)c * a.E + e] = run;   // exclusive within expert
             run += v;
         }
+        run = min(run, a.cap);
         a.counts[e] = run;
     }
     expert_scan(a, run, tot, wsum);
-    if (e < a.E)
-        for (int c = 0; c < nchunks; ++c) a.chunk_counts[(int64_t)c * a.E + e] += tot[e];
 }
 
 __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(DispatchArgs a) {
-    __shared__ int running[256];          // rows handed out so far in this chunk, per expert
+    __shared__ int running[256];          // pairs of each expert before this one (earlier chunks and rounds)
+    __shared__ int base[256];             // first grouped row of each expert
     __shared__ int wcount[kWaves][256];   // per-wave counts of the current round
     for (int e = threadIdx.x; e < a.E; e += kThreads) {
         running[e] = a.chunk_counts[(int64_t)blockIdx.x * a.E + e];
+        base[e] = a.offsets[e];
         for (int q = 0; q < kWaves; ++q) wcount[q][e] = 0;
     }
     __syncthreads();
     const int64_t p0 = (int64_t)blockIdx.x * kDispatchChunk;
     const int64_t p1 = min((int64_t)a.P, p0 + kDispatchChunk);
-    scatter_range(a, p0, p1, running, wcount);
+    scatter_range(a, p0, p1, running, base, wcount);
 }
 
 // All pairs in one chunk: count, scan and scatter in one workgroup.

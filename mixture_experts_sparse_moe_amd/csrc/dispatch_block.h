@@ -10,9 +10,9 @@ namespace moe {
 
 constexpr int kDispatchThreads = 256;
 
-// Exclusive scan of `run` (thread e's expert total, 0 past E) over the
-// experts: offsets[e] and tot[e] = first grouped row of expert e,
-// offsets[E] = P.  Ends with a barrier.
+// Exclusive scan of `run` (thread e's expert's kept pairs, 0 past E) over
+// the experts: offsets[e] and tot[e] = first grouped row of expert e,
+// offsets[E] = all kept pairs.  Ends with a barrier.
 __device__ __forceinline__ void expert_scan(const DispatchArgs& a, int run, int* tot, int* wsum) {
     const int e = threadIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int v = run;
@@ -29,19 +29,21 @@ __device__ __forceinline__ void expert_scan(const DispatchArgs& a, int run, int*
     const int excl = incl - run;
     tot[e] = excl;
     if (e < a.E) a.offsets[e] = excl;
-    if (e == kDispatchThreads - 1) a.offsets[a.E] = incl;   // total = P
+    if (e == kDispatchThreads - 1) a.offsets[a.E] = incl;   // all kept pairs
     __syncthreads();
 }
 
-// Pairs [p0, p1) in order: each gets row running[e] + (its rank among the
-// earlier pairs of this range with the same expert).  running[] advances.
-// wcount[][] must be zero on entry and is zero on exit.
+// Pairs [p0, p1) in order.  A pair's rank w inside its expert e is
+// running[e] + (its rank among the earlier pairs of this range with expert
+// e); it gets row base[e] + w if w < a.cap, else it is dropped (pair_pos
+// -1).  running[] advances.  wcount[][] must be zero on entry and is zero on
+// exit.
 __device__ __forceinline__ void scatter_range(const DispatchArgs& a, int64_t p0, int64_t p1, int* running,
-                                              int (*wcount)[256]) {
+                                              const int* base, int (*wcount)[256]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int64_t base = p0; base < p1; base += kDispatchThreads) {
-        const int64_t p = base + threadIdx.x;
+    for (int64_t q0 = p0; q0 < p1; q0 += kDispatchThreads) {
+        const int64_t p = q0 + threadIdx.x;
         const bool valid = p < p1;
         const int e = valid ? a.ids[p] : 0;
         // lanes of this wave holding the same expert id
@@ -58,8 +60,12 @@ __device__ __forceinline__ void scatter_range(const DispatchArgs& a, int64_t p0,
         if (valid) {
             int r = running[e] + rank_in_wave;
             for (int q = 0; q < w; ++q) r += wcount[q][e];
-            a.sorted_pairs[r] = (int32_t)p;
-            a.pair_pos[p] = r;
+            if (r < a.cap) {
+                a.sorted_pairs[base[e] + r] = (int32_t)p;
+                a.pair_pos[p] = base[e] + r;
+            } else {
+                a.pair_pos[p] = -1;
+            }
         }
         __syncthreads();
         for (int ee = threadIdx.x; ee < a.E; ee += kDispatchThreads) {
@@ -72,12 +78,12 @@ __device__ __forceinline__ void scatter_range(const DispatchArgs& a, int64_t p0,
 }
 
 // The whole dispatch of a.P <= kDispatchChunk pairs in one workgroup: count
-// (LDS histogram), exclusive scan over the experts, stable scatter.  a.ids
-// must be visible to every thread of the workgroup.
+// (LDS histogram), exclusive scan over the experts' kept counts, stable
+// scatter.  a.ids must be visible to every thread of the workgroup.
 __device__ __forceinline__ void dispatch_in_block(const DispatchArgs& a) {
     __shared__ int hist[256];
     __shared__ int wsum[kDispatchThreads / 64];
-    __shared__ int running[256];
+    __shared__ int base[256];
     __shared__ int wcount[kDispatchThreads / 64][256];
     const int e = threadIdx.x;
     hist[e] = 0;
@@ -85,10 +91,12 @@ __device__ __forceinline__ void dispatch_in_block(const DispatchArgs& a) {
     __syncthreads();
     for (int p = threadIdx.x; p < a.P; p += kDispatchThreads) atomicAdd(&hist[a.ids[p]], 1);
     __syncthreads();
-    const int run = e < a.E ? hist[e] : 0;
-    if (e < a.E) a.counts[e] = run;
-    expert_scan(a, run, running, wsum);
-    scatter_range(a, 0, a.P, running, wcount);
+    const int kept = e < a.E ? min(hist[e], a.cap) : 0;
+    if (e < a.E) a.counts[e] = kept;
+    expert_scan(a, kept, base, wsum);
+    hist[e] = 0;                   // now: rank inside the expert so far
+    __syncthreads();
+    scatter_range(a, 0, a.P, hist, base, wcount);
 }
 
 }  // namespace moe

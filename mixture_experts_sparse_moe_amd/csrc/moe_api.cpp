@@ -41,6 +41,22 @@ int validate_cfg(const moe_config* c) {
 
 size_t elem(const moe_config* c) { return c->dtype == MOE_BF16 ? 2 : 4; }
 
+bool misaligned(const void* p);
+
+// Options: NULL or all fields zero is the plain layer.
+int validate_opts(const moe_options* o) {
+    if (!o) return MOE_OK;
+    if (o->bias_on_scores != 0 && o->bias_on_scores != 1) return MOE_ERR_UNSUPPORTED;
+    if (o->expert_bias && misaligned(o->expert_bias)) return MOE_ERR_ALIGN;
+    if (o->router_stats && misaligned(o->router_stats)) return MOE_ERR_ALIGN;
+    if (!(o->aux_alpha == o->aux_alpha)) return MOE_ERR_SHAPE;      // NaN
+    return MOE_OK;
+}
+
+int capacity_of(const moe_options* o) {
+    return (o && o->expert_capacity > 0) ? o->expert_capacity : 0x7FFFFFFF;
+}
+
 // Which bf16 GEMM kernel the routed and the shared expert GEMMs use: the
 // 32-row streaming kernel when groups hold about 32 rows or fewer on average
 // (decode), else the 256 x 256 tile kernel.
@@ -90,7 +106,7 @@ Splits splits(const moe_config* c) {
 
 // Device workspace layout.  Every region starts on a 256-byte boundary.
 struct Layout {
-    size_t ids, wts, counts, offsets, chunk, sorted, pos, H, O, Hs, S, rpart, total;
+    size_t ids, wts, counts, offsets, chunk, sorted, pos, H, O, Hs, S, rpart, spart, total;
     size_t dispatch_need, ffn_need;   // bytes used by moe_dispatch / moe_expert_ffn (from 0)
 };
 
@@ -116,6 +132,7 @@ Layout layout(const moe_config* c) {
     L.S = take(c->num_shared ? sp.shared * T * c->d_model * elem(c) : 0);
     const int rr = route_ranges(c->num_tokens, c->d_model, c->dtype == MOE_BF16);
     L.rpart = take(rr > 1 ? (size_t)rr * T * E * sizeof(float) : 0);
+    L.spart = take(((T + 31) / 32) * 2 * E * sizeof(float));
     L.total = o;
     L.dispatch_need = align_up(nchunks * E * sizeof(int32_t));
     return L;
@@ -146,24 +163,35 @@ int check_ptr(const void* p, bool empty_ok) {
 // disp (with part): the dispatch of these ids, run by the router's second
 // kernel when the batch is one block of at most 32 tokens.  Returns in
 // *dispatched whether it did.
+// opts (nullable): selection bias; router statistics into opts->router_stats,
+// with per-block sums in spart (required then).
 int run_route(const moe_config* c, const void* x, const void* w_router, int32_t* ids, float* wts,
               float* gap, hipStream_t s, float* part = nullptr, const DispatchArgs* disp = nullptr,
-              bool* dispatched = nullptr) {
+              bool* dispatched = nullptr, const moe_options* opts = nullptr, float* spart = nullptr) {
     RouteArgs a{x, w_router, ids, wts, gap, c->num_tokens, c->d_model, c->num_experts,
                 c->top_k, c->score_fn, c->renormalize};
+    const bool stats = opts && opts->router_stats;
+    if (opts) {
+        a.bias = opts->expert_bias;
+        a.bias_on_scores = opts->bias_on_scores;
+        a.stats_part = stats ? spart : nullptr;
+    }
     const bool bf16 = c->dtype == MOE_BF16;
     const int rr = route_ranges(c->num_tokens, c->d_model, bf16);
     const bool fuse = part && rr > 1 && disp && c->num_tokens <= 32;
     if (dispatched) *dispatched = fuse;
     if (part && rr > 1) MOE_HIP(launch_route_split(a, rr, part, fuse ? disp : nullptr, s));
     else MOE_HIP(launch_route(a, bf16, s));
+    if (stats)
+        MOE_HIP(launch_router_stats(spart, (c->num_tokens + 31) / 32, c->num_experts, c->num_tokens,
+                                    opts->aux_alpha, opts->router_stats, s));
     return MOE_OK;
 }
 
 int run_dispatch(const moe_config* c, const int32_t* ids, int32_t* counts, int32_t* offsets,
-                 int32_t* sorted, int32_t* pos, int32_t* chunk, hipStream_t s) {
+                 int32_t* sorted, int32_t* pos, int32_t* chunk, hipStream_t s, int cap = 0x7FFFFFFF) {
     DispatchArgs a{ids, counts, offsets, sorted, pos, chunk, c->num_tokens * c->top_k,
-                   c->num_experts};
+                   c->num_experts, cap};
     MOE_HIP(launch_dispatch(a, s));
     return MOE_OK;
 }
@@ -224,6 +252,65 @@ int run_combine(const moe_config* c, const void* out, const float* wts, const in
     return MOE_OK;
 }
 
+int forward_impl(const moe_config* cfg, const moe_options* opts, const void* x, const void* w_router,
+                 const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
+                 const void* ws_up, const void* ws_down, void* y, int32_t* topk_ids_out,
+                 float* topk_weights_out, int32_t* expert_counts_out, void* ws, size_t ws_bytes,
+                 void* start_event, void* const* ev, void* stream) {
+    MOE_TRY(validate_cfg(cfg));
+    MOE_TRY(validate_opts(opts));
+    const bool empty = cfg->num_tokens == 0;
+    MOE_TRY(check_ptr(x, empty));
+    MOE_TRY(check_ptr(w_router, false));
+    MOE_TRY(check_ptr(w_gate, false));
+    MOE_TRY(check_ptr(w_up, false));
+    MOE_TRY(check_ptr(w_down, false));
+    if (cfg->num_shared) {
+        MOE_TRY(check_ptr(ws_gate, false));
+        MOE_TRY(check_ptr(ws_up, false));
+        MOE_TRY(check_ptr(ws_down, false));
+    }
+    MOE_TRY(check_ptr(y, empty));
+    if (topk_ids_out) MOE_TRY(check_ptr(topk_ids_out, true));
+    if (topk_weights_out) MOE_TRY(check_ptr(topk_weights_out, true));
+    if (expert_counts_out) MOE_TRY(check_ptr(expert_counts_out, true));
+    const Layout L = layout(cfg);
+    if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    MOE_TRY(check_ptr(ws, false));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+    float* wts = topk_weights_out ? topk_weights_out : at<float>(ws, L.wts);
+    int32_t* counts = expert_counts_out ? expert_counts_out : at<int32_t>(ws, L.counts);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    int32_t* sorted = at<int32_t>(ws, L.sorted);
+    int32_t* pos = at<int32_t>(ws, L.pos);
+    if (start_event) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(start_event), s));
+    const int cap = capacity_of(opts);
+    if (empty) {
+        // routing outputs are empty; expert counts are all zero
+        MOE_TRY(mark(ev, 0, s));
+        MOE_TRY(run_dispatch(cfg, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s, cap));
+        for (int i = 1; i < MOE_NUM_STAGES; ++i) MOE_TRY(mark(ev, i, s));
+        return MOE_OK;
+    }
+    const DispatchArgs disp{ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk),
+                            cfg->num_tokens * cfg->top_k, cfg->num_experts, cap};
+    bool dispatched = false;
+    MOE_TRY(run_route(cfg, x, w_router, ids, wts, nullptr, s, at<float>(ws, L.rpart), &disp, &dispatched, opts,
+                      at<float>(ws, L.spart)));
+    MOE_TRY(mark(ev, 0, s));
+    if (!dispatched)
+        MOE_TRY(run_dispatch(cfg, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s, cap));
+    MOE_TRY(mark(ev, 1, s));
+    void* O = at<void>(ws, L.O);
+    void* S = cfg->num_shared ? at<void>(ws, L.S) : nullptr;
+    const Splits sp = splits(cfg);
+    MOE_TRY(run_ffn(cfg, x, sorted, offsets, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, O, S,
+                    at<void>(ws, L.H), at<void>(ws, L.Hs), s, ev, sp));
+    MOE_TRY(run_combine(cfg, O, wts, pos, S, y, s, sp));
+    return mark(ev, 6, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -248,22 +335,44 @@ const char* moe_status_str(int status) {
 
 int moe_route(const moe_config* cfg, const void* x, const void* w_router, int32_t* topk_ids,
               float* topk_weights, float* topk_gap, void* stream) {
+    return moe_route_ex(cfg, nullptr, x, w_router, topk_ids, topk_weights, topk_gap, nullptr, 0, stream);
+}
+
+int moe_route_ex(const moe_config* cfg, const moe_options* opts, const void* x, const void* w_router,
+                 int32_t* topk_ids, float* topk_weights, float* topk_gap, void* ws, size_t ws_bytes,
+                 void* stream) {
     MOE_TRY(validate_cfg(cfg));
+    MOE_TRY(validate_opts(opts));
     const bool empty = cfg->num_tokens == 0;
     MOE_TRY(check_ptr(x, empty));
     MOE_TRY(check_ptr(w_router, false));
     MOE_TRY(check_ptr(topk_ids, empty));
     MOE_TRY(check_ptr(topk_weights, empty));
     if (topk_gap) MOE_TRY(check_ptr(topk_gap, true));
+    const bool stats = opts && opts->router_stats;
+    const Layout L = layout(cfg);
+    if (stats) {
+        if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+        MOE_TRY(check_ptr(ws, false));
+    }
     if (empty) return MOE_OK;
     return run_route(cfg, x, w_router, topk_ids, topk_weights, topk_gap,
-                     static_cast<hipStream_t>(stream));
+                     static_cast<hipStream_t>(stream), nullptr, nullptr, nullptr, opts,
+                     stats ? at<float>(ws, L.spart) : nullptr);
 }
 
 int moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t* expert_counts,
                  int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos, void* ws,
                  size_t ws_bytes, void* stream) {
+    return moe_dispatch_ex(cfg, nullptr, topk_ids, expert_counts, expert_offsets, sorted_pairs, pair_pos,
+                           ws, ws_bytes, stream);
+}
+
+int moe_dispatch_ex(const moe_config* cfg, const moe_options* opts, const int32_t* topk_ids,
+                    int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_pairs,
+                    int32_t* pair_pos, void* ws, size_t ws_bytes, void* stream) {
     MOE_TRY(validate_cfg(cfg));
+    MOE_TRY(validate_opts(opts));
     const bool empty = cfg->num_tokens == 0;
     MOE_TRY(check_ptr(topk_ids, empty));
     MOE_TRY(check_ptr(expert_counts, false));
@@ -276,7 +385,7 @@ int moe_dispatch(const moe_config* cfg, const int32_t* topk_ids, int32_t* expert
         MOE_TRY(check_ptr(ws, false));
     }
     return run_dispatch(cfg, topk_ids, expert_counts, expert_offsets, sorted_pairs, pair_pos,
-                        static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream));
+                        static_cast<int32_t*>(ws), static_cast<hipStream_t>(stream), capacity_of(opts));
 }
 
 int moe_expert_ffn(const moe_config* cfg, const void* x, const int32_t* sorted_pairs,
@@ -330,54 +439,19 @@ int moe_forward_staged(const moe_config* cfg, const void* x, const void* w_route
                        int32_t* topk_ids_out, float* topk_weights_out,
                        int32_t* expert_counts_out, void* ws, size_t ws_bytes, void* start_event,
                        void* const* ev, void* stream) {
-    MOE_TRY(validate_cfg(cfg));
-    const bool empty = cfg->num_tokens == 0;
-    MOE_TRY(check_ptr(x, empty));
-    MOE_TRY(check_ptr(w_router, false));
-    MOE_TRY(check_ptr(w_gate, false));
-    MOE_TRY(check_ptr(w_up, false));
-    MOE_TRY(check_ptr(w_down, false));
-    if (cfg->num_shared) {
-        MOE_TRY(check_ptr(ws_gate, false));
-        MOE_TRY(check_ptr(ws_up, false));
-        MOE_TRY(check_ptr(ws_down, false));
-    }
-    MOE_TRY(check_ptr(y, empty));
-    if (topk_ids_out) MOE_TRY(check_ptr(topk_ids_out, true));
-    if (topk_weights_out) MOE_TRY(check_ptr(topk_weights_out, true));
-    if (expert_counts_out) MOE_TRY(check_ptr(expert_counts_out, true));
-    const Layout L = layout(cfg);
-    if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-    MOE_TRY(check_ptr(ws, false));
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    int32_t* ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
-    float* wts = topk_weights_out ? topk_weights_out : at<float>(ws, L.wts);
-    int32_t* counts = expert_counts_out ? expert_counts_out : at<int32_t>(ws, L.counts);
-    int32_t* offsets = at<int32_t>(ws, L.offsets);
-    int32_t* sorted = at<int32_t>(ws, L.sorted);
-    int32_t* pos = at<int32_t>(ws, L.pos);
-    if (start_event) MOE_HIP(hipEventRecord(static_cast<hipEvent_t>(start_event), s));
-    if (empty) {
-        // routing outputs are empty; expert counts are all zero
-        MOE_TRY(mark(ev, 0, s));
-        MOE_TRY(run_dispatch(cfg, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s));
-        for (int i = 1; i < MOE_NUM_STAGES; ++i) MOE_TRY(mark(ev, i, s));
-        return MOE_OK;
-    }
-    const DispatchArgs disp{ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk),
-                            cfg->num_tokens * cfg->top_k, cfg->num_experts};
-    bool dispatched = false;
-    MOE_TRY(run_route(cfg, x, w_router, ids, wts, nullptr, s, at<float>(ws, L.rpart), &disp, &dispatched));
-    MOE_TRY(mark(ev, 0, s));
-    if (!dispatched) MOE_TRY(run_dispatch(cfg, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s));
-    MOE_TRY(mark(ev, 1, s));
-    void* O = at<void>(ws, L.O);
-    void* S = cfg->num_shared ? at<void>(ws, L.S) : nullptr;
-    const Splits sp = splits(cfg);
-    MOE_TRY(run_ffn(cfg, x, sorted, offsets, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, O, S,
-                    at<void>(ws, L.H), at<void>(ws, L.Hs), s, ev, sp));
-    MOE_TRY(run_combine(cfg, O, wts, pos, S, y, s, sp));
-    return mark(ev, 6, s);
+    return forward_impl(cfg, nullptr, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
+                        topk_ids_out, topk_weights_out, expert_counts_out, ws, ws_bytes, start_event, ev,
+                        stream);
+}
+
+int moe_forward_ex(const moe_config* cfg, const moe_options* opts, const void* x, const void* w_router,
+                   const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
+                   const void* ws_up, const void* ws_down, void* y, int32_t* topk_ids_out,
+                   float* topk_weights_out, int32_t* expert_counts_out, void* ws, size_t ws_bytes,
+                   void* stream) {
+    return forward_impl(cfg, opts, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
+                        topk_ids_out, topk_weights_out, expert_counts_out, ws, ws_bytes, nullptr, nullptr,
+                        stream);
 }
 
 int moe_forward(const moe_config* cfg, const void* x, const void* w_router, const void* w_gate,

@@ -19,6 +19,7 @@ struct DispatchArgs {
     int32_t* pair_pos;      // [P]
     int32_t* chunk_counts;  // [nchunks, E] scratch
     int P, E;
+    int cap = 0x7FFFFFFF;   // pairs kept per expert (the first ones); the rest get pair_pos -1
 };
 int dispatch_num_chunks(int P);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
@@ -33,8 +34,15 @@ struct RouteArgs {
     int T, d, E, k;
     int score_fn;           // 0 softmax, 1 sigmoid
     int renorm;
+    const float* bias = nullptr;  // [E] selection-only bias, or nullptr
+    int bias_on_scores = 0;       // 0: key = logit + bias; 1: key = score + bias
+    float* stats_part = nullptr;  // [token blocks of 32][2E] per-block sums, or nullptr
 };
 hipError_t launch_route(const RouteArgs& a, bool bf16, hipStream_t s);
+// Router statistics from the per-block sums of a routing call:
+// out [2E + 2] = f_e (E), P_e (E), L_aux = alpha E sum_e f_e P_e, max_e n_e / mean_e n_e.
+hipError_t launch_router_stats(const float* stats_part, int blocks, int E, int T, float alpha, float* out,
+                               hipStream_t s);
 // bf16 only: the K chunks in `ranges` ranges, one workgroup per (32 tokens,
 // range), partial logits in part [ranges, T, E] fp32, then a second kernel
 // adds them in range order and selects.  For batches of few token blocks.

@@ -188,31 +188,77 @@ __device__ void logits_f32(const RouteArgs& a, int t0, float* lds) {
     __syncthreads();
 }
 
+// The float whose ord_bits are the upper half of a selection key.
+__device__ __forceinline__ float key_value(unsigned long long m) {
+    const uint32_t u = (uint32_t)(m >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// Largest float over the wave (every lane gets it).
+__device__ __forceinline__ float wave_max_f32(float v) {
+    return key_value(wave_max_u64((unsigned long long)ord_bits(v) << 32));
+}
+
 // Top-k selection and gates of tokens t0 .. t0 + 31 from their logits in
-// lds[32][kLogitStride].
-// With s_ids the ids are also kept in LDS, s_ids[(t - t0) * k + j].
-__device__ __forceinline__ void topk_rows(const RouteArgs& a, int t0, const float* lds, int* s_ids = nullptr) {
+// lds[32][kLogitStride]; one wave per token.  Lane owns experts lane + 64 q.
+//   key (what is selected on): the logit; with a bias, logit + bias or
+//       score + bias ("Mixture-of-Experts Internals", sec. 3.3; "from the
+//       router to the all-to-all", Load balancing).  Ties: lower index.
+//   gates: from the unbiased scores, renormalised over the chosen set or not.
+//   gap: key_(k) - key_(k+1).
+// With a.stats_part the block's per-expert sums of the chosen count and of
+// the router probability (softmax score, or sigmoid score normalised over all
+// experts) go to a.stats_part[blockIdx.x][2E], summed over the block's tokens
+// in a fixed order.  With s_ids the ids are also kept in LDS,
+// s_ids[(t - t0) * k + j].  Every thread of the workgroup must call it.
+__device__ __forceinline__ void topk_rows(const RouteArgs& a, int t0, float* lds, int* s_ids = nullptr) {
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const bool stats = a.stats_part != nullptr;
+    float bias[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bias[q] = (a.bias && lane + 64 * q < a.E) ? a.bias[lane + 64 * q] : 0.0f;
+    float pacc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int row = w; row < kBT; row += nw) {
         const int t = t0 + row;
         if (t >= a.T) break;
         const float* lrow = lds + row * kLogitStride;
-        unsigned long long key[4];
         float lv[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            int e = lane + 64 * q;
-            if (e < a.E) {
-                lv[q] = lrow[e];
-                key[q] = ((unsigned long long)ord_bits(lv[q]) << 32) | (0xFFFFFFFFu - (uint32_t)e);
-            } else {
-                lv[q] = 0.0f;
-                key[q] = 0ull;
+        for (int q = 0; q < 4; ++q) lv[q] = lane + 64 * q < a.E ? lrow[lane + 64 * q] : -__builtin_inff();
+        // full scores, when the key or the statistics need them
+        const bool need_s = (a.bias && a.bias_on_scores) || stats;
+        float sv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, mx = 0.0f;
+        if (need_s || a.bias) mx = wave_max_f32(fmaxf(fmaxf(lv[0], lv[1]), fmaxf(lv[2], lv[3])));
+        if (need_s) {
+            float part = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (lane + 64 * q < a.E) {
+                    sv[q] = a.score_fn == 0 ? expf(lv[q] - mx) : 1.0f / (1.0f + expf(-lv[q]));
+                    part += sv[q];
+                }
+            }
+            const float z = wave_sum(part);
+            if (a.score_fn == 0) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sv[q] /= z;
+            }
+            if (stats) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) pacc[q] += a.score_fn == 0 ? sv[q] : sv[q] / z;
             }
         }
+        unsigned long long key[4];
+        float kv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = lane + 64 * q;
+            kv[q] = a.bias ? (a.bias_on_scores ? sv[q] : lv[q]) + bias[q] : lv[q];
+            key[q] = e < a.E ? ((unsigned long long)ord_bits(kv[q]) << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
+        }
         int my_e = 0;
-        float my_l = 0.0f, first_l = 0.0f, last_l = 0.0f;
+        float my_l = 0.0f, first_l = 0.0f, last_k = 0.0f;
         for (int j = 0; j < a.k; ++j) {
             unsigned long long m = key[0];
 #pragma unroll
@@ -222,32 +268,36 @@ __device__ __forceinline__ void topk_rows(const RouteArgs& a, int t0, const floa
             const float l = lrow[e];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if (key[q] == m) key[q] = 0ull;
+                if (key[q] == m) {
+                    key[q] = 0ull;
+                    cacc[q] += 1.0f;
+                }
             if (lane == j) { my_e = e; my_l = l; }
             if (j == 0) first_l = l;
-            last_l = l;
+            last_k = key_value(m);
         }
         float gap = __builtin_inff();
         if (a.k < a.E) {
             unsigned long long m = key[0];
 #pragma unroll
             for (int q = 1; q < 4; ++q) m = key[q] > m ? key[q] : m;
-            m = wave_max_u64(m);
-            const int e = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
-            gap = last_l - lrow[e];
+            gap = last_k - key_value(wave_max_u64(m));
         }
         const bool mine = lane < a.k;
+        // largest logit among the chosen (the first chosen unless biased)
+        const float top = a.bias ? wave_max_f32(mine ? my_l : -__builtin_inff()) : first_l;
         float g;
         if (a.score_fn == 0) {
-            const float ex = mine ? expf(my_l - first_l) : 0.0f;
+            const float ex = mine ? expf(my_l - (a.renorm ? top : (a.bias ? mx : first_l))) : 0.0f;
             float z;
             if (a.renorm) {
                 z = wave_sum(ex);
             } else {
+                const float sh = a.bias ? mx : first_l;
                 float part = 0.0f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    if (lane + 64 * q < a.E) part += expf(lv[q] - first_l);
+                    if (lane + 64 * q < a.E) part += expf(lv[q] - sh);
                 z = wave_sum(part);
             }
             g = ex / z;
@@ -261,6 +311,25 @@ __device__ __forceinline__ void topk_rows(const RouteArgs& a, int t0, const floa
             if (s_ids) s_ids[row * a.k + lane] = my_e;
         }
         if (lane == 0 && a.gap) a.gap[t] = gap;
+    }
+    if (stats) {
+        // waves' sums in LDS (the logit tile is no longer read), then added
+        // in wave order: [wave][0, E) counts, [wave][E, 2E) probabilities
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = lane + 64 * q;
+            if (e < a.E) {
+                lds[w * 2 * a.E + e] = cacc[q];
+                lds[w * 2 * a.E + a.E + e] = pacc[q];
+            }
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < 2 * a.E; i += blockDim.x) {
+            float v = 0.0f;
+            for (int q = 0; q < nw; ++q) v += lds[q * 2 * a.E + i];
+            a.stats_part[(int64_t)blockIdx.x * 2 * a.E + i] = v;
+        }
     }
 }
 
@@ -344,7 +413,48 @@ __global__ __launch_bounds__(kFinishThreads) void route_finish_kernel(RouteArgs 
     }
 }
 
+// Statistics of the whole batch from the per-block sums, added in block
+// order: f_e = n_e / T, P_e = (sum of probabilities) / T, then (thread 0, in
+// expert order) L_aux = alpha E sum_e f_e P_e and max_e n_e / mean_e n_e
+// ("8.6 Mixture of Experts", sec. 3.1; "from the router to the all-to-all",
+// Load balancing).
+__global__ __launch_bounds__(256) void router_stats_kernel(const float* part, int blocks, int E, int T,
+                                                           float alpha, float* out) {
+    __shared__ float s_fp[256], s_n[256];
+    const int e = threadIdx.x;
+    if (e < E) {
+        float n = 0.0f, p = 0.0f;
+        for (int b = 0; b < blocks; ++b) {
+            n += part[(int64_t)b * 2 * E + e];
+            p += part[(int64_t)b * 2 * E + E + e];
+        }
+        const float f = n / (float)T, P = p / (float)T;
+        out[e] = f;
+        out[E + e] = P;
+        s_fp[e] = f * P;
+        s_n[e] = n;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float acc = 0.0f, mx = 0.0f, tot = 0.0f;
+        for (int i = 0; i < E; ++i) {
+            acc += s_fp[i];
+            mx = fmaxf(mx, s_n[i]);
+            tot += s_n[i];
+        }
+        out[2 * E] = alpha * (float)E * acc;
+        out[2 * E + 1] = tot > 0.0f ? mx / (tot / (float)E) : 0.0f;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_router_stats(const float* stats_part, int blocks, int E, int T, float alpha, float* out,
+                               hipStream_t s) {
+    if (E < 1 || E > 256 || blocks < 1 || T < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(router_stats_kernel, dim3(1), dim3(256), 0, s, stats_part, blocks, E, T, alpha, out);
+    return hipGetLastError();
+}
 
 int route_ranges(int T, int d, bool bf16) {
     if (!bf16 || T <= 0) return 1;

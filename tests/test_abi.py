@@ -154,3 +154,29 @@ def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert moe.moe_status_str(s).startswith("MOE_")
     assert "unknown" in moe.moe_status_str(42)
+
+
+def route_ex(c, opts, ws=None, ws_bytes=0):
+    return moe.lib().moe_route_ex(ctypes.byref(c), ctypes.byref(opts) if opts is not None else None,
+                                  FAKE, FAKE, FAKE, FAKE, None, ws, ws_bytes, None)
+
+
+def test_options_are_validated_before_launch():
+    c = cfg()
+    O = moe.MoeOptions
+    assert route_ex(c, O(None, 2, 0, None, 0.0)) == moe.MOE_ERR_UNSUPPORTED       # bias space 0/1
+    assert route_ex(c, O(FAKE + 4, 0, 0, None, 0.0)) == moe.MOE_ERR_ALIGN        # bias alignment
+    assert route_ex(c, O(None, 0, 0, FAKE + 8, 0.0)) == moe.MOE_ERR_ALIGN        # stats alignment
+    assert route_ex(c, O(None, 0, 0, None, float("nan"))) == moe.MOE_ERR_SHAPE   # alpha
+    # statistics need the workspace
+    assert route_ex(c, O(None, 0, 0, FAKE, 0.01)) == moe.MOE_ERR_WORKSPACE
+    assert route_ex(c, O(None, 0, 0, FAKE, 0.01), FAKE, 64) == moe.MOE_ERR_WORKSPACE
+    # a bad config is still reported first
+    assert route_ex(cfg(k=0), O(None, 0, 0, None, 0.0)) == moe.MOE_ERR_SHAPE
+
+
+def test_capacity_helper_matches_page():
+    # 4,096 tokens, 64 experts, top-8, factor 1.0 -> 512 slots
+    assert moe.capacity(4096, 8, 64, 1.0) == 512
+    assert moe.capacity(4096, 8, 64, 1.25) == 640
+    assert moe.capacity(10, 2, 3, 1.0) == 7
