@@ -10,9 +10,10 @@ shaped prefill layer (T=4096, d=4096, E=8, k=2, d_ff=14336, bf16).
 Prints one JSON line with the throughput (tokens/s), the roofline of the
 dominant kernel measured live with HIP events on the launch stream, and the
 CPU oracle timed on a bounded sample of the same workload on the host cores.
-The timed region records two events per step, around the dominant kernel;
-the per-stage breakdown comes from a separate pass with an event after every
-stage (each event between kernels costs a few microseconds).
+The timed region records two timing events per step, around the dominant
+kernel (created without the system-scope fence, so recording them costs the
+next kernel nothing measurable); the per-stage breakdown comes from a
+separate pass with an event after every stage.
 """
 from __future__ import annotations
 
@@ -46,6 +47,8 @@ def parse():
                    help="target wall time of the CPU oracle sample")
     p.add_argument("--no-ceilings", action="store_true",
                    help="skip the practical ceilings (device copy, torch.matmul yardstick)")
+    p.add_argument("--no-options", action="store_true",
+                   help="skip timing the layer with its optional routing features")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of 1 GiB (the reference for HBM counters)")
     p.add_argument("--traffic-from", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_DIR"),
@@ -53,6 +56,44 @@ def parse():
                         "of the bench, FETCH_SIZE+WRITE_SIZE runs of --copy-calibration); writes "
                         "profiles/traffic.json for --workload")
     return p.parse_args()
+
+
+class TimingEvents:
+    """HIP events for timing only, created with hipEventDisableSystemFence:
+    recording one skips the system-scope cache write-back and invalidation
+    that a default event performs, which would otherwise slow the next
+    kernel.  Uses the HIP runtime already loaded in this process."""
+    FLAG = 0x20000000   # hipEventDisableSystemFence
+
+    def __init__(self):
+        import ctypes
+        path = next(ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln)
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path)
+        self.made = []
+
+    def make(self, n, stream):
+        out = []
+        for _ in range(n):
+            ev = self.ct.c_void_p()
+            if self.hip.hipEventCreateWithFlags(self.ct.byref(ev), self.FLAG) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            # record once outside any timed region
+            self.hip.hipEventRecord(ev, self.ct.c_void_p(stream.cuda_stream))
+            out.append(ev.value)
+        self.made += out
+        return out
+
+    def ms(self, a, b) -> float:
+        t = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(t), self.ct.c_void_p(a), self.ct.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(self.ct.c_void_p(e))
+        self.made = []
 
 
 def kernel_source_hash() -> str:
@@ -89,6 +130,43 @@ def algorithmic(sh, counts: np.ndarray) -> dict:
     down = dict(flops=2.0 * P * d * f, bytes=touched * d * f * w + P * f * w + P * d * w)
     return dict(layer_flops=layer_flops, layer_bytes=layer_bytes, gate_up=gate_up, down=down,
                 touched=touched)
+
+
+def options_cost(torch, moe, cfg, d, y, ws, stream, sh, steps: int) -> dict:
+    """ms per layer (moe_forward_ex, no per-stage events) with each optional
+    routing feature on: a selection-only bias on the scores (N(0, 0.01)),
+    capacity factor 1.25, router statistics, and all three; next to the plain
+    layer through the same entry point."""
+    g = torch.Generator().manual_seed(0)
+    bias = (torch.randn(sh.E, generator=g, dtype=torch.float32) * 0.01).to(d["x"].device)
+    stats = torch.empty(2 * sh.E + 2, dtype=torch.float32, device=d["x"].device)
+    cap = moe.capacity(sh.T, sh.k, sh.E, 1.25)
+    variants = {
+        "plain": moe.MoeOptions.of(),
+        "bias_on_scores": moe.MoeOptions.of(expert_bias=bias, bias_on_scores=1),
+        "capacity_1.25": moe.MoeOptions.of(expert_capacity=cap),
+        "router_stats": moe.MoeOptions.of(router_stats=stats, aux_alpha=0.01),
+        "all": moe.MoeOptions.of(expert_bias=bias, bias_on_scores=1, expert_capacity=cap,
+                                 router_stats=stats, aux_alpha=0.01),
+    }
+    out = {}
+    for name, o in variants.items():
+        run = lambda: moe.moe_forward_ex(cfg, o, d["x"], d["w_router"], d["w_gate"], d["w_up"],
+                                         d["w_down"], d["ws_gate"], d["ws_up"], d["ws_down"], y,
+                                         ws=ws, stream=stream)
+        for _ in range(2):
+            run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run()
+        torch.cuda.synchronize()
+        out[name] = round((time.perf_counter() - t0) / steps * 1e3, 4)
+    out["capacity"] = cap
+    st = stats.cpu().numpy()
+    out["l_aux_alpha_0.01"] = float(st[2 * sh.E])
+    out["max_over_mean_load"] = float(st[2 * sh.E + 1])
+    return out
 
 
 def practical_ceilings(torch, dev) -> dict:
@@ -251,21 +329,15 @@ def main():
                                d["ws_gate"], d["ws_up"], d["ws_down"], y, expert_counts=counts,
                                ws=ws, start_event=start, stage_events=evs, stream=stream)
 
-    mk = lambda: torch.cuda.Event(enable_timing=True)
-
-    def made(n):
-        evs = [mk() for _ in range(n)]
-        for e in evs:                 # created before any timed region
-            e.record(stream)
-        return evs
+    tev = TimingEvents()
 
     for _ in range(args.warmup):
         step(None, None)
     torch.cuda.synchronize()
-    # Timed region: the whole layer, with two events per step around the
-    # dominant kernel (the routed gate/up GEMM, stage 2) on the layer's stream;
-    # recording an event between every stage costs a few microseconds each.
-    gu_ev = [made(2) for _ in range(args.steps)]
+    # Timed region: the whole layer, with two timing events per step around
+    # the dominant kernel (the routed gate/up GEMM, stage 2) on the layer's
+    # stream.
+    gu_ev = [tev.make(2, stream) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -275,11 +347,11 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
-    gu_ms = float(np.mean([a.elapsed_time(b) for a, b in gu_ev]))
+    gu_ms = float(np.mean([tev.ms(a, b) for a, b in gu_ev]))
 
     # Stage breakdown: a separate pass with an event after every stage.
-    starts = made(args.steps)
-    stages = [made(moe.MOE_NUM_STAGES) for _ in range(args.steps)]
+    starts = tev.make(args.steps, stream)
+    stages = [tev.make(moe.MOE_NUM_STAGES, stream) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(starts[i], stages[i])
@@ -288,9 +360,10 @@ def main():
     for i in range(args.steps):
         prev = starts[i]
         for j, e in enumerate(stages[i]):
-            stage_ms[i, j] = prev.elapsed_time(e)
+            stage_ms[i, j] = tev.ms(prev, e)
             prev = e
     stage_avg = stage_ms.mean(0)
+    tev.close()
     cnt = counts.cpu().numpy()
     alg = algorithmic(sh, cnt)
     decode = sh.T * sh.k < 64 * sh.E          # under 64 rows per expert: weight-read bound
@@ -333,7 +406,7 @@ def main():
         "layer_pct_bf16_peak": alg["layer_flops"] / layer_s / 1e12 / PEAK_BF16_TFLOPS,
         "layer_gbs": alg["layer_bytes"] / layer_s / 1e9,
         "layer_pct_hbm": alg["layer_bytes"] / layer_s / 1e9 / PEAK_HBM_GBS,
-        # separate pass, an event after every stage (each adds a few microseconds)
+        # separate pass with an event after every stage
         "stages_ms": {n: round(float(v), 4) for n, v in zip(moe.STAGE_NAMES, stage_avg)},
         "staged_ms_per_step": round(float(stage_ms.sum(1).mean()), 4),
         "expert_load": {"max_over_mean": float(cnt.max() / max(cnt.mean(), 1e-9)),
@@ -350,6 +423,9 @@ def main():
     gg = out["grouped_gemm"]
     gg["frac_bf16_peak"] = gg["tflops"] / PEAK_BF16_TFLOPS
     gg["frac_hbm"] = gg["gbs"] / PEAK_HBM_GBS
+    if not args.no_options:
+        out["options_ms_per_step"] = options_cost(torch, moe, cfg, d, y, ws, stream, sh,
+                                                  max(3, min(args.steps, 20)))
     if not args.no_ceilings:
         out["practical_ceilings"] = practical_ceilings(torch, dev)
     if not args.no_cpu_baseline:

@@ -178,8 +178,11 @@ int moe_forward(const moe_config* cfg, const void* x, const void* w_router, cons
  * Changes", In practice: watch per-expert counts and expert compute time;
  * profile each stage).  Same arguments and results as moe_forward, plus
  *   stage_events: MOE_NUM_STAGES hipEvent_t handles (passed as void*),
- *                 created by the caller; event i is recorded on `stream`
- *                 right after stage i is enqueued:
+ *                 created by the caller, entries nullable; event i is
+ *                 recorded on `stream` right after stage i is enqueued,
+ *                 except events 1 and 2, which the routed gate/up kernel's
+ *                 launch records at its start and at its end (so 1 -> 2 is
+ *                 that kernel's own duration):
  *                 0 route, 1 dispatch, 2 routed gate/up GEMM (+SiLU*up),
  *                 3 routed down GEMM, 4 shared gate/up, 5 shared down,
  *                 6 combine.  Stages 4-5 are empty when num_shared == 0;

@@ -265,7 +265,7 @@ def moe_forward_staged(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, w
                        topk_ids=None, topk_weights=None, expert_counts=None, ws=None,
                        start_event=None, stage_events=None, stream=None):
     """moe_forward recording ``start_event`` and one event per stage (torch.cuda.Event
-    objects created with enable_timing=True) on the stream."""
+    objects created with enable_timing=True, or raw hipEvent_t handles) on the stream."""
     torch = _torch()
     T, d, E, k = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k
     dt, dev = _act_dtype(cfg), x.device
@@ -280,8 +280,8 @@ def moe_forward_staged(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, w
         raise ValueError(f"stage_events needs {MOE_NUM_STAGES} events")
 
     def ev_handle(e):
-        if e is None:
-            return None
+        if e is None or isinstance(e, int):     # a raw hipEvent_t handle
+            return e
         if not e.cuda_event:        # torch creates its events on first record
             e.record()
         return e.cuda_event

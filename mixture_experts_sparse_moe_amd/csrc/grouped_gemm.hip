@@ -26,6 +26,8 @@
 #include "moe_internal.h"
 #include "skinny.h"
 
+#include <hip/hip_ext.h>
+
 namespace moe {
 
 namespace {
@@ -883,7 +885,8 @@ hipError_t launch_bf16(const GemmGroup& g, hipStream_t s) {
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(kThreads), lds, s, g, tiles_n, (int)mtu);
+    hipExtLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(kThreads), lds, s, g.t_start, g.t_stop, 0, g, tiles_n,
+                          (int)mtu);
     return hipGetLastError();
 }
 
@@ -906,13 +909,13 @@ hipError_t launch_bf16_persistent(const GemmGroup& g, hipStream_t s) {
     // costs the K loop a compiler-inserted wait on the loads in flight
     if constexpr (!DUAL) {
         if (g.aligned_bands) {
-            hipLaunchKernelGGL((gemm_bf16_persistent_kernel<false, true>), dim3(persistent_grid()), dim3(512),
-                               0, s, g, g.N / BN);
+            hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<false, true>), dim3(persistent_grid()), dim3(512),
+                                  0, s, g.t_start, g.t_stop, 0, g, g.N / BN);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((gemm_bf16_persistent_kernel<DUAL, false>), dim3(persistent_grid()), dim3(512), 0, s,
-                       g, g.N / BN);
+    hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<DUAL, false>), dim3(persistent_grid()), dim3(512), 0, s,
+                          g.t_start, g.t_stop, 0, g, g.N / BN);
     return hipGetLastError();
 }
 
@@ -927,7 +930,8 @@ hipError_t launch_bf16_skinny(const GemmGroup& g, hipStream_t s) {
     const int64_t grid = mtu * tiles_n * S;
     if (grid == 0) return hipSuccess;
     if (grid > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_bf16_skinny_kernel<DUAL, kSkNblk, kSkNst>), dim3((unsigned)grid), dim3(256), 0, s,
+    hipExtLaunchKernelGGL((gemm_bf16_skinny_kernel<DUAL, kSkNblk, kSkNst>), dim3((unsigned)grid), dim3(256), 0, s,
+                          g.t_start, g.t_stop, 0,
                        g, tiles_n, (int)mtu);
     return hipGetLastError();
 }
@@ -937,7 +941,8 @@ hipError_t launch_f32(const GemmGroup& g, hipStream_t s) {
     const int tiles_n = g.N / 64;
     const int64_t mtu = g.offsets ? grouped_m_tiles_upper(g.M, g.G, 64) : (g.M + 63) / 64;
     if (mtu == 0) return hipSuccess;
-    hipLaunchKernelGGL(gemm_f32_kernel<DUAL>, dim3((unsigned)(mtu * tiles_n)), dim3(kThreads), 0, s,
+    hipExtLaunchKernelGGL(gemm_f32_kernel<DUAL>, dim3((unsigned)(mtu * tiles_n)), dim3(kThreads), 0, s,
+                          g.t_start, g.t_stop, 0,
                        g, tiles_n, (int)mtu);
     return hipGetLastError();
 }

@@ -214,8 +214,13 @@ int run_ffn(const moe_config* c, const void* x, const int32_t* sorted, const int
         GemmGroup up{x, sorted, c->top_k, offsets, c->num_experts, P, wg, wu, H, c->d_ff,
                      c->d_model};
         up.skinny = pa.routed_skinny;
+        // stage events 1 and 2 are the routed gate/up kernel's own start and
+        // end timestamps: no separate records around the dominant kernel
+        if (ev) {
+            up.t_start = static_cast<hipEvent_t>(ev[1]);
+            up.t_stop = static_cast<hipEvent_t>(ev[2]);
+        }
         MOE_HIP(launch_grouped_gemm(up, true, bf16, s));
-        MOE_TRY(mark(ev, 2, s));
         // expert-aligned tile bands pay off when experts hold several M tiles
         // (measured on the down GEMM: -6 % at ~4 tiles per expert, +2 % at ~1.5)
         GemmGroup down{H, nullptr, 1, offsets, c->num_experts, P, wd, nullptr, out, c->d_model,
@@ -223,6 +228,10 @@ int run_ffn(const moe_config* c, const void* x, const int32_t* sorted, const int
                        (int64_t)P >= (int64_t)640 * c->num_experts};
         down.skinny = pa.routed_skinny;
         MOE_HIP(launch_grouped_gemm(down, false, bf16, s));
+        MOE_TRY(mark(ev, 3, s));
+    } else {
+        MOE_TRY(mark(ev, 1, s));
+        MOE_TRY(mark(ev, 2, s));
         MOE_TRY(mark(ev, 3, s));
     }
     if (c->num_shared && c->num_tokens > 0) {
@@ -301,7 +310,6 @@ int forward_impl(const moe_config* cfg, const moe_options* opts, const void* x, 
     MOE_TRY(mark(ev, 0, s));
     if (!dispatched)
         MOE_TRY(run_dispatch(cfg, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s, cap));
-    MOE_TRY(mark(ev, 1, s));
     void* O = at<void>(ws, L.O);
     void* S = cfg->num_shared ? at<void>(ws, L.S) : nullptr;
     const Splits sp = splits(cfg);

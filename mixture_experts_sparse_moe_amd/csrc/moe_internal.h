@@ -71,6 +71,7 @@ struct GemmGroup {
     int64_t part_stride = 0;// elements between C slices when splitk > 1
     bool aligned_bands = false; // single bf16: tile bands follow group boundaries
     bool skinny = false;    // bf16, few rows per group: 32-row tiles streaming the weights
+    hipEvent_t t_start = nullptr, t_stop = nullptr;  // recorded when the kernel starts / ends
 };
 // Dual mode: C = silu(A B0^T) * (A B1^T).  Single: C = A B0^T, or with
 // splitk > 1 the partial products of the K ranges, C slice s = A[:, Ks] B0[:, Ks]^T.
