@@ -244,7 +244,9 @@ def copy_calibration():
 
 # the gate/up GEMM kernel as rocprofv3 names it (bf16, dual mode; prefix of
 # the template argument list)
-GATE_UP_KERNEL = "gemm_bf16_persistent_kernel<true"
+# the routed gate/up GEMM: the 256-row tile kernel, or the 32-row one for
+# decode-sized batches (one of them runs per workload)
+GATE_UP_KERNELS = ("gemm_bf16_persistent_kernel<true", "gemm_bf16_skinny_kernel<true")
 
 
 def _pmc_rows(d):
@@ -256,9 +258,9 @@ def _pmc_rows(d):
     return rows
 
 
-def _per_dispatch(rows, counter, name_has):
+def _per_dispatch(rows, counter, names):
     vals = [float(r["Counter_Value"]) for r in rows
-            if r["Counter_Name"] == counter and name_has in r["Kernel_Name"]]
+            if r["Counter_Name"] == counter and any(n in r["Kernel_Name"] for n in names)]
     return sum(vals) / len(vals) if vals else None
 
 
@@ -272,12 +274,12 @@ def traffic_from(args):
              default=None)
     cw = max((float(r["Counter_Value"]) for r in copy_rows if r["Counter_Name"] == "WRITE_SIZE"),
              default=None)
-    f_kib = _per_dispatch(_pmc_rows(fetch_dir), "FETCH_SIZE", GATE_UP_KERNEL)
-    w_kib = _per_dispatch(_pmc_rows(write_dir), "WRITE_SIZE", GATE_UP_KERNEL)
+    f_kib = _per_dispatch(_pmc_rows(fetch_dir), "FETCH_SIZE", GATE_UP_KERNELS)
+    w_kib = _per_dispatch(_pmc_rows(write_dir), "WRITE_SIZE", GATE_UP_KERNELS)
     if None in (cf, cw, f_kib, w_kib):
         sys.exit(f"missing counters: copy {cf} {cw}, kernel {f_kib} {w_kib}")
     f_scale, w_scale = COPY_BYTES / cf, COPY_BYTES / cw
-    rec = {"kernel": "grouped gate/up GEMM (" + GATE_UP_KERNEL + ", ...>)",
+    rec = {"kernel": "grouped gate/up GEMM (" + " or ".join(GATE_UP_KERNELS) + ", ...>)",
            "fetch_kib": f_kib, "write_kib": w_kib,
            "copy_fetch_kib": cf, "copy_write_kib": cw,
            "fetch_scale_bytes_per_kib": f_scale, "write_scale_bytes_per_kib": w_scale,
