@@ -39,9 +39,9 @@ constexpr int kMaxBand = 6;   // most M tiles in one band of the expert-aligned 
 
 
 // Block-wide: map flattened M tile `mt` to (group, first row, rows).  Returns
-// false if mt is past the last real tile.
+// false if mt is past the last real tile.  scratch: 11 ints of LDS.
 template <int BM>
-__device__ bool locate_tile(const GemmGroup& g, int mt, int* grp, int* row0, int* nrows) {
+__device__ bool locate_tile_in(const GemmGroup& g, int mt, int* grp, int* row0, int* nrows, int* scratch) {
     if (g.offsets == nullptr) {
         const int r0 = mt * BM;
         if (r0 >= g.M) return false;
@@ -50,8 +50,8 @@ __device__ bool locate_tile(const GemmGroup& g, int mt, int* grp, int* row0, int
         *nrows = min(BM, g.M - r0);
         return true;
     }
-    __shared__ int s_wsum[8];      // one slot per wave, up to 512 threads
-    __shared__ int s_res[3];
+    int* s_wsum = scratch;         // one slot per wave, up to 512 threads
+    int* s_res = scratch + 8;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     if (threadIdx.x == 0) s_res[0] = -1;
     int nt = 0, cnt = 0, off = 0;
@@ -83,6 +83,12 @@ __device__ bool locate_tile(const GemmGroup& g, int mt, int* grp, int* row0, int
     *row0 = s_res[1];
     *nrows = s_res[2];
     return true;
+}
+
+template <int BM>
+__device__ bool locate_tile(const GemmGroup& g, int mt, int* grp, int* row0, int* nrows) {
+    __shared__ int s_scratch[11];
+    return locate_tile_in<BM>(g, mt, grp, row0, nrows, s_scratch);
 }
 
 // Logical tile of this workgroup: XCD-contiguous, then windows of kWMW M tiles
@@ -703,7 +709,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 // tile starts at a chunk that depends on its N tile and group, so tiles that
 // run together read different offsets of their weight rows.
 template <bool DUAL, int NBLK, int NST>
-__global__ __launch_bounds__(256, NBLK * NST <= 12 ? 2 : 1) void gemm_bf16_skinny_kernel(GemmGroup g, int tiles_n,
+__global__ __launch_bounds__(256, NBLK * NST <= 16 ? 2 : 1) void gemm_bf16_skinny_kernel(GemmGroup g, int tiles_n,
                                                                                         int mt_upper) {
     constexpr int KS = (DUAL && NBLK == 4) ? 2 : 1;
     using Sh = SkinnyShape<NBLK, NST, KS>;
@@ -717,7 +723,10 @@ __global__ __launch_bounds__(256, NBLK * NST <= 12 ? 2 : 1) void gemm_bf16_skinn
     const int mt = (L / tiles_n) % mt_upper;
     const int ks = L / tiles_n / mt_upper;
     int grp, row0, nrows;
-    if (!locate_tile<32>(g, mt, &grp, &row0, &nrows)) return;   // uniform over the workgroup
+    // the tile lookup's scratch: the last stage buffer, first written after
+    // the first barrier of the K loop
+    if (!locate_tile_in<32>(g, mt, &grp, &row0, &nrows, reinterpret_cast<int*>(NST > 3 ? sX3 : sX2)))
+        return;   // uniform over the workgroup
     grp = __builtin_amdgcn_readfirstlane(grp);
     row0 = __builtin_amdgcn_readfirstlane(row0);
     nrows = __builtin_amdgcn_readfirstlane(nrows);
@@ -919,7 +928,7 @@ hipError_t launch_bf16_persistent(const GemmGroup& g, hipStream_t s) {
     return hipGetLastError();
 }
 
-constexpr int kSkNblk = 4, kSkNst = 3;
+constexpr int kSkNblk = 4, kSkNst = 4;
 
 template <bool DUAL>
 hipError_t launch_bf16_skinny(const GemmGroup& g, hipStream_t s) {

@@ -211,29 +211,40 @@ __device__ __forceinline__ float wave_max_f32(float v) {
 // experts) go to a.stats_part[blockIdx.x][2E], summed over the block's tokens
 // in a fixed order.  With s_ids the ids are also kept in LDS,
 // s_ids[(t - t0) * k + j].  Every thread of the workgroup must call it.
-__device__ __forceinline__ void topk_rows(const RouteArgs& a, int t0, float* lds, int* s_ids = nullptr) {
+template <int QN, bool OPT>
+__device__ __forceinline__ void topk_rows_q(const RouteArgs& a, int t0, float* lds, int* s_ids) {
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    const bool stats = a.stats_part != nullptr;
-    float bias[4];
+    const bool stats = OPT && a.stats_part != nullptr;
+    const float* abias = OPT ? a.bias : nullptr;
+    float bias[QN];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) bias[q] = (a.bias && lane + 64 * q < a.E) ? a.bias[lane + 64 * q] : 0.0f;
-    float pacc[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int q = 0; q < QN; ++q) bias[q] = (abias && lane + 64 * q < a.E) ? abias[lane + 64 * q] : 0.0f;
+    float pacc[QN], cacc[QN];
+#pragma unroll
+    for (int q = 0; q < QN; ++q) pacc[q] = cacc[q] = 0.0f;
     for (int row = w; row < kBT; row += nw) {
         const int t = t0 + row;
         if (t >= a.T) break;
         const float* lrow = lds + row * kLogitStride;
-        float lv[4];
+        float lv[QN];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) lv[q] = lane + 64 * q < a.E ? lrow[lane + 64 * q] : -__builtin_inff();
+        for (int q = 0; q < QN; ++q) lv[q] = lane + 64 * q < a.E ? lrow[lane + 64 * q] : -__builtin_inff();
         // full scores, when the key or the statistics need them
-        const bool need_s = (a.bias && a.bias_on_scores) || stats;
-        float sv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, mx = 0.0f;
-        if (need_s || a.bias) mx = wave_max_f32(fmaxf(fmaxf(lv[0], lv[1]), fmaxf(lv[2], lv[3])));
+        const bool need_s = (abias && a.bias_on_scores) || stats;
+        float sv[QN], mx = 0.0f;
+#pragma unroll
+        for (int q = 0; q < QN; ++q) sv[q] = 0.0f;
+        if (need_s || abias) {
+            float m = lv[0];
+#pragma unroll
+            for (int q = 1; q < QN; ++q) m = fmaxf(m, lv[q]);
+            mx = wave_max_f32(m);
+        }
         if (need_s) {
             float part = 0.0f;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < QN; ++q) {
                 if (lane + 64 * q < a.E) {
                     sv[q] = a.score_fn == 0 ? expf(lv[q] - mx) : 1.0f / (1.0f + expf(-lv[q]));
                     part += sv[q];
@@ -242,19 +253,19 @@ __device__ __forceinline__ void topk_rows(const RouteArgs& a, int t0, float* lds
             const float z = wave_sum(part);
             if (a.score_fn == 0) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) sv[q] /= z;
+                for (int q = 0; q < QN; ++q) sv[q] /= z;
             }
             if (stats) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) pacc[q] += a.score_fn == 0 ? sv[q] : sv[q] / z;
+                for (int q = 0; q < QN; ++q) pacc[q] += a.score_fn == 0 ? sv[q] : sv[q] / z;
             }
         }
-        unsigned long long key[4];
-        float kv[4];
+        unsigned long long key[QN];
+        float kv[QN];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < QN; ++q) {
             const int e = lane + 64 * q;
-            kv[q] = a.bias ? (a.bias_on_scores ? sv[q] : lv[q]) + bias[q] : lv[q];
+            kv[q] = abias ? (a.bias_on_scores ? sv[q] : lv[q]) + bias[q] : lv[q];
             key[q] = e < a.E ? ((unsigned long long)ord_bits(kv[q]) << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
         }
         int my_e = 0;
@@ -262,12 +273,12 @@ __device__ __forceinline__ void topk_rows(const RouteArgs& a, int t0, float* lds
         for (int j = 0; j < a.k; ++j) {
             unsigned long long m = key[0];
 #pragma unroll
-            for (int q = 1; q < 4; ++q) m = key[q] > m ? key[q] : m;
+            for (int q = 1; q < QN; ++q) m = key[q] > m ? key[q] : m;
             m = wave_max_u64(m);
             const int e = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
             const float l = lrow[e];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < QN; ++q)
                 if (key[q] == m) {
                     key[q] = 0ull;
                     cacc[q] += 1.0f;
@@ -280,23 +291,23 @@ __device__ __forceinline__ void topk_rows(const RouteArgs& a, int t0, float* lds
         if (a.k < a.E) {
             unsigned long long m = key[0];
 #pragma unroll
-            for (int q = 1; q < 4; ++q) m = key[q] > m ? key[q] : m;
+            for (int q = 1; q < QN; ++q) m = key[q] > m ? key[q] : m;
             gap = last_k - key_value(wave_max_u64(m));
         }
         const bool mine = lane < a.k;
         // largest logit among the chosen (the first chosen unless biased)
-        const float top = a.bias ? wave_max_f32(mine ? my_l : -__builtin_inff()) : first_l;
+        const float top = abias ? wave_max_f32(mine ? my_l : -__builtin_inff()) : first_l;
         float g;
         if (a.score_fn == 0) {
-            const float ex = mine ? expf(my_l - (a.renorm ? top : (a.bias ? mx : first_l))) : 0.0f;
+            const float ex = mine ? expf(my_l - (a.renorm ? top : (abias ? mx : first_l))) : 0.0f;
             float z;
             if (a.renorm) {
                 z = wave_sum(ex);
             } else {
-                const float sh = a.bias ? mx : first_l;
+                const float sh = abias ? mx : first_l;
                 float part = 0.0f;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+                for (int q = 0; q < QN; ++q)
                     if (lane + 64 * q < a.E) part += expf(lv[q] - sh);
                 z = wave_sum(part);
             }
@@ -317,7 +328,7 @@ __device__ __forceinline__ void topk_rows(const RouteArgs& a, int t0, float* lds
         // in wave order: [wave][0, E) counts, [wave][E, 2E) probabilities
         __syncthreads();
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < QN; ++q) {
             const int e = lane + 64 * q;
             if (e < a.E) {
                 lds[w * 2 * a.E + e] = cacc[q];
@@ -331,6 +342,15 @@ __device__ __forceinline__ void topk_rows(const RouteArgs& a, int t0, float* lds
             a.stats_part[(int64_t)blockIdx.x * 2 * a.E + i] = v;
         }
     }
+}
+
+// Expert slots per lane QN = ceil(E / 64); the optional bias and statistics
+// code only in the variant that needs it (the selection runs once per launch,
+// so the instructions it fetches are a large part of its time).
+template <int QN>
+__device__ __forceinline__ void topk_rows(const RouteArgs& a, int t0, float* lds, int* s_ids = nullptr) {
+    if (a.bias || a.stats_part) topk_rows_q<QN, true>(a, t0, lds, s_ids);
+    else topk_rows_q<QN, false>(a, t0, lds, s_ids);
 }
 
 // Stage buffers of the bf16 logits (NBLK = 0, fp32: none).
@@ -350,7 +370,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     const int t0 = blockIdx.x * kBT;
     if (NBLK) logits_bf16<NB>(a, t0, 0, a.d / kSkChunk, lds, sX0, sX1, sX2, sX3, sW0, sW1, sW2, sW3);
     else logits_f32(a, t0, lds);
-    topk_rows(a, t0, lds);
+    topk_rows<NBLK == 0 || NBLK >= 8 ? 4 : (NBLK == 4 ? 2 : 1)>(a, t0, lds);
 }
 
 // Few token blocks: the K chunks are cut into ks ranges, one workgroup per
@@ -376,7 +396,7 @@ __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a, float* 
 // (waves that have ended no longer take part in barriers).
 constexpr int kFinishThreads = 1024;
 
-template <bool DISPATCH>
+template <bool DISPATCH, int QN>
 __global__ __launch_bounds__(kFinishThreads) void route_finish_kernel(RouteArgs a, const float* part, int nr,
                                                                       DispatchArgs d) {
     __shared__ float lds[kLogitFloats];
@@ -402,14 +422,14 @@ __global__ __launch_bounds__(kFinishThreads) void route_finish_kernel(RouteArgs 
     if (DISPATCH) {
         // the ids of this one block of tokens, from LDS
         __shared__ int s_ids[kBT * 16];
-        topk_rows(a, t0, lds, s_ids);
+        topk_rows<QN>(a, t0, lds, s_ids);
         __syncthreads();
         if (threadIdx.x >= kDispatchThreads) return;
         DispatchArgs dl = d;
         dl.ids = s_ids;
         dispatch_in_block(dl);
     } else {
-        topk_rows(a, t0, lds);
+        topk_rows<QN>(a, t0, lds);
     }
 }
 
@@ -475,9 +495,17 @@ hipError_t launch_route_split(const RouteArgs& a, int ranges, float* part, const
     else if (nb <= 4) hipLaunchKernelGGL(route_partial_kernel<4>, grid, block, 0, s, a, part);
     else hipLaunchKernelGGL(route_partial_kernel<8>, grid, block, 0, s, a, part);
     const dim3 fblock(kFinishThreads);
-    if (d) hipLaunchKernelGGL(route_finish_kernel<true>, dim3(grid.x), fblock, 0, s, a, (const float*)part, ranges, *d);
-    else hipLaunchKernelGGL(route_finish_kernel<false>, dim3(grid.x), fblock, 0, s, a, (const float*)part, ranges,
-                            DispatchArgs{});
+    const DispatchArgs dd = d ? *d : DispatchArgs{};
+#define MOE_FINISH(D_, Q_) \
+    hipLaunchKernelGGL((route_finish_kernel<D_, Q_>), dim3(grid.x), fblock, 0, s, a, (const float*)part, ranges, dd)
+    if (a.E <= 64) {
+        if (d) MOE_FINISH(true, 1); else MOE_FINISH(false, 1);
+    } else if (a.E <= 128) {
+        if (d) MOE_FINISH(true, 2); else MOE_FINISH(false, 2);
+    } else {
+        if (d) MOE_FINISH(true, 4); else MOE_FINISH(false, 4);
+    }
+#undef MOE_FINISH
     return hipGetLastError();
 }
 
