@@ -27,7 +27,7 @@ _LIB_PATH = os.environ.get("ORACLE_LIB_OVERRIDE") or os.path.join(_HERE, "libora
 _lib = None
 
 SOFTMAX, SIGMOID = 0, 1
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 
 def build(verbose: bool = False) -> str:
@@ -67,6 +67,8 @@ def lib():
         L.oracle_forward_tokens.restype = i32
         L.oracle_forward_expert_loop.argtypes = ([i64] + [i32] * 7 + [vp] * 7 + [vp, vp, vp, i32])
         L.oracle_forward_expert_loop.restype = i32
+        L.oracle_backward.argtypes = [i64] + [i32] * 9 + [vp] * 8 + [vp, vp] + [vp] * 8
+        L.oracle_backward.restype = i32
         _lib = L
     return _lib
 
@@ -80,7 +82,9 @@ def _dtype_of(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:
         return BF16
-    raise TypeError(f"oracle inputs are fp32 or bf16 bit patterns (uint16), got {a.dtype}")
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"oracle inputs are fp32, bf16 bit patterns (uint16) or fp64, got {a.dtype}")
 
 
 def _c(a):
@@ -253,3 +257,32 @@ def forward(inp: dict, k: int, score_fn: int = SOFTMAX, renormalize: int = 1,
     disp = dispatch(r["ids"], E)
     y = forward_expert_loop(inp, r["ids"], r["gates"], nthreads=nthreads)
     return dict(logits=lg, y=y, **r, **disp)
+
+
+def backward(inp: dict, ids: np.ndarray, dy: np.ndarray, score_fn: int = SOFTMAX,
+             renormalize: int = 1) -> dict:
+    """Gradients of L = sum(dy * y) for the routing ``ids`` [T,k] (held fixed):
+    dx, dw_router, dw_gate, dw_up, dw_down (and ds_gate, ds_up, ds_down with a
+    shared expert), fp64, by the chain rule written out per token."""
+    x = _c(inp["x"])
+    wr, wg, wu, wd = (_c(inp[n]) for n in ("w_router", "w_gate", "w_up", "w_down"))
+    sg, su, sd = (_c(inp.get(n)) for n in ("ws_gate", "ws_up", "ws_down"))
+    T, d = x.shape
+    E, f = wg.shape[0], wg.shape[1]
+    k = ids.shape[1]
+    S = 0 if sg is None else 1
+    f_s = 0 if sg is None else sg.shape[0]
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    out = dict(dx=np.empty((T, d)), dw_router=np.empty((E, d)), dw_gate=np.empty((E, f, d)),
+               dw_up=np.empty((E, f, d)), dw_down=np.empty((E, d, f)))
+    if S:
+        out.update(ds_gate=np.empty((f_s, d)), ds_up=np.empty((f_s, d)), ds_down=np.empty((d, f_s)))
+    rc = lib().oracle_backward(T, d, E, k, f, S, f_s, score_fn, renormalize, _dtype_of(x), x.ctypes.data,
+                               wr.ctypes.data, wg.ctypes.data, wu.ctypes.data, wd.ctypes.data, _ptr(sg),
+                               _ptr(su), _ptr(sd), ids.ctypes.data, dy.ctypes.data,
+                               *(out[n].ctypes.data for n in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down")),
+                               *((out[n].ctypes.data for n in ("ds_gate", "ds_up", "ds_down")) if S else (None,) * 3))
+    if rc:
+        raise ValueError(f"oracle_backward failed ({rc})")
+    return out

@@ -40,10 +40,12 @@
 
 #define OR_F32 0
 #define OR_BF16 1
+#define OR_F64 2   /* fp64 inputs: only for finite-difference checks of the gradients */
 #define OR_SOFTMAX 0
 #define OR_SIGMOID 1
 
 static double widen(const void* base, int dtype, int64_t i) {
+    if (dtype == OR_F64) return ((const double*)base)[i];
     if (dtype == OR_F32) return (double)((const float*)base)[i];
     uint32_t u = (uint32_t)((const uint16_t*)base)[i] << 16;
     float f;
@@ -351,4 +353,182 @@ int oracle_forward_expert_loop(int64_t T, int d, int E, int k, int f, int num_sh
         }
     }
     return 0;
+}
+
+/*
+ * Backward pass of the layer for a fixed routing (the selection is piecewise
+ * constant, so its ids are an input), by the chain rule on the forward above.
+ * With L = sum_t <dy_t, y_t>:
+ *   pair (t, j), expert e = ids[t,j], gate g_j:
+ *     a = W_gate,e x, u = W_up,e x, h = silu(a) * u, o = W_down,e h
+ *     dL/dg_j = <dy, o>,  dL/do = g_j dy
+ *     dh = W_down,e^T (g_j dy); da = dh * u * silu'(a); du = dh * silu(a)
+ *     dW_down,e += (g_j dy) h^T; dW_gate,e += da x^T; dW_up,e += du x^T
+ *     dx += W_gate,e^T da + W_up,e^T du
+ *   gates -> logits: dL/dl_m = sum_j dL/dg_j * dg_j/dl_m, with g_j the
+ *     renormalised (or raw) score of the chosen expert j, the scores a
+ *     softmax over all E or per-expert sigmoids; the Jacobian entries are
+ *     written out term by term below.
+ *   router: dW_r += dl x^T; dx += W_r^T dl
+ *   shared expert (weight 1): as a pair with g = 1 and its own weights.
+ * ("8.6 Mixture of Experts", sec. 2: the gate and expert paths; the router
+ * receives gradient only through the gates of the chosen experts,
+ * "Mixture-of-Experts Internals", sec. 2.2.)
+ * Outputs (fp64, overwritten): dx [T,d], dwr [E,d], dwg, dwu [E,f,d],
+ * dwd [E,d,f], dsg, dsu [f_s,d], dsd [d,f_s] (the last three when
+ * num_shared).  Serial over tokens (the weight gradients are sums over them).
+ */
+int oracle_backward(int64_t T, int d, int E, int k, int f, int num_shared, int f_s, int score_fn,
+                    int renorm, int dtype, const void* x, const void* w_r, const void* wg,
+                    const void* wu, const void* wd, const void* sg, const void* su, const void* sd,
+                    const int32_t* ids, const double* dy, double* dx, double* dwr, double* dwg,
+                    double* dwu, double* dwd, double* dsg, double* dsu, double* dsd) {
+    if (k < 1 || k > E) return -2;
+    memset(dx, 0, sizeof(double) * T * d);
+    memset(dwr, 0, sizeof(double) * E * d);
+    memset(dwg, 0, sizeof(double) * E * f * d);
+    memset(dwu, 0, sizeof(double) * E * f * d);
+    memset(dwd, 0, sizeof(double) * E * d * f);
+    if (num_shared) {
+        memset(dsg, 0, sizeof(double) * f_s * d);
+        memset(dsu, 0, sizeof(double) * f_s * d);
+        memset(dsd, 0, sizeof(double) * d * f_s);
+    }
+    int fm = f > f_s ? f : f_s;
+    double* l = (double*)malloc(sizeof(double) * E);
+    double* s = (double*)malloc(sizeof(double) * E);
+    double* dl = (double*)malloc(sizeof(double) * E);
+    double* g = (double*)malloc(sizeof(double) * k);
+    double* dg = (double*)malloc(sizeof(double) * k);
+    double* a = (double*)malloc(sizeof(double) * fm);
+    double* u = (double*)malloc(sizeof(double) * fm);
+    double* h = (double*)malloc(sizeof(double) * fm);
+    double* dh = (double*)malloc(sizeof(double) * fm);
+    double* o = (double*)malloc(sizeof(double) * d);
+    int err = 0;
+    for (int64_t t = 0; t < T && !err; ++t) {
+        const double* dyt = dy + t * d;
+        double* dxt = dx + t * d;
+        /* logits, scores, gates of the given ids */
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c) acc += widen(x, dtype, t * d + c) * widen(w_r, dtype, (int64_t)e * d + c);
+            l[e] = acc;
+        }
+        scores_of(l, E, score_fn, s);
+        double S = 0.0;
+        for (int j = 0; j < k; ++j) {
+            int e = ids[t * k + j];
+            if (e < 0 || e >= E) { err = -2; break; }
+            S += s[e];
+        }
+        if (err) break;
+        for (int j = 0; j < k; ++j) g[j] = renorm ? s[ids[t * k + j]] / S : s[ids[t * k + j]];
+        /* experts */
+        for (int j = 0; j < k; ++j) {
+            int e = ids[t * k + j];
+            int64_t win = (int64_t)e * f * d, wdn = (int64_t)e * d * f;
+            for (int r = 0; r < f; ++r) {
+                double aa = 0.0, bb = 0.0;
+                for (int c = 0; c < d; ++c) {
+                    double xc = widen(x, dtype, t * d + c);
+                    aa += widen(wg, dtype, win + (int64_t)r * d + c) * xc;
+                    bb += widen(wu, dtype, win + (int64_t)r * d + c) * xc;
+                }
+                a[r] = aa; u[r] = bb; h[r] = silu(aa) * bb;
+            }
+            double dgj = 0.0;
+            for (int c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (int r = 0; r < f; ++r) acc += widen(wd, dtype, wdn + (int64_t)c * f + r) * h[r];
+                o[c] = acc;
+                dgj += dyt[c] * acc;
+            }
+            dg[j] = dgj;
+            for (int r = 0; r < f; ++r) {
+                double acc = 0.0;
+                for (int c = 0; c < d; ++c) acc += widen(wd, dtype, wdn + (int64_t)c * f + r) * g[j] * dyt[c];
+                dh[r] = acc;
+            }
+            for (int c = 0; c < d; ++c)
+                for (int r = 0; r < f; ++r) dwd[wdn + (int64_t)c * f + r] += g[j] * dyt[c] * h[r];
+            for (int r = 0; r < f; ++r) {
+                double sig = 1.0 / (1.0 + exp(-a[r]));
+                double dsilu = sig * (1.0 + a[r] * (1.0 - sig));        /* d/da of a * sigmoid(a) */
+                double da = dh[r] * u[r] * dsilu;
+                double du = dh[r] * a[r] * sig;
+                for (int c = 0; c < d; ++c) {
+                    double xc = widen(x, dtype, t * d + c);
+                    dwg[win + (int64_t)r * d + c] += da * xc;
+                    dwu[win + (int64_t)r * d + c] += du * xc;
+                    dxt[c] += widen(wg, dtype, win + (int64_t)r * d + c) * da +
+                              widen(wu, dtype, win + (int64_t)r * d + c) * du;
+                }
+            }
+        }
+        /* gates -> logits */
+        for (int m = 0; m < E; ++m) {
+            double acc = 0.0;
+            for (int j = 0; j < k; ++j) {
+                int e = ids[t * k + j];
+                /* ds_e / dl_m */
+                double dse_dlm;
+                if (score_fn == OR_SOFTMAX) dse_dlm = s[e] * ((e == m ? 1.0 : 0.0) - s[m]);
+                else dse_dlm = (e == m) ? s[e] * (1.0 - s[e]) : 0.0;
+                double dgj_dlm;
+                if (renorm) {
+                    /* g_j = s_e / S, S = sum over the chosen of s */
+                    double dS_dlm = 0.0;
+                    for (int i = 0; i < k; ++i) {
+                        int ei = ids[t * k + i];
+                        if (score_fn == OR_SOFTMAX) dS_dlm += s[ei] * ((ei == m ? 1.0 : 0.0) - s[m]);
+                        else dS_dlm += (ei == m) ? s[ei] * (1.0 - s[ei]) : 0.0;
+                    }
+                    dgj_dlm = dse_dlm / S - s[e] * dS_dlm / (S * S);
+                } else {
+                    dgj_dlm = dse_dlm;
+                }
+                acc += dg[j] * dgj_dlm;
+            }
+            dl[m] = acc;
+        }
+        for (int m = 0; m < E; ++m)
+            for (int c = 0; c < d; ++c) {
+                dwr[(int64_t)m * d + c] += dl[m] * widen(x, dtype, t * d + c);
+                dxt[c] += widen(w_r, dtype, (int64_t)m * d + c) * dl[m];
+            }
+        /* shared expert */
+        if (num_shared) {
+            for (int r = 0; r < f_s; ++r) {
+                double aa = 0.0, bb = 0.0;
+                for (int c = 0; c < d; ++c) {
+                    double xc = widen(x, dtype, t * d + c);
+                    aa += widen(sg, dtype, (int64_t)r * d + c) * xc;
+                    bb += widen(su, dtype, (int64_t)r * d + c) * xc;
+                }
+                a[r] = aa; u[r] = bb; h[r] = silu(aa) * bb;
+            }
+            for (int r = 0; r < f_s; ++r) {
+                double acc = 0.0;
+                for (int c = 0; c < d; ++c) acc += widen(sd, dtype, (int64_t)c * f_s + r) * dyt[c];
+                dh[r] = acc;
+            }
+            for (int c = 0; c < d; ++c)
+                for (int r = 0; r < f_s; ++r) dsd[(int64_t)c * f_s + r] += dyt[c] * h[r];
+            for (int r = 0; r < f_s; ++r) {
+                double sig = 1.0 / (1.0 + exp(-a[r]));
+                double dsilu = sig * (1.0 + a[r] * (1.0 - sig));
+                double da = dh[r] * u[r] * dsilu;
+                double du = dh[r] * a[r] * sig;
+                for (int c = 0; c < d; ++c) {
+                    double xc = widen(x, dtype, t * d + c);
+                    dsg[(int64_t)r * d + c] += da * xc;
+                    dsu[(int64_t)r * d + c] += du * xc;
+                    dxt[c] += widen(sg, dtype, (int64_t)r * d + c) * da + widen(su, dtype, (int64_t)r * d + c) * du;
+                }
+            }
+        }
+    }
+    free(l); free(s); free(dl); free(g); free(dg); free(a); free(u); free(h); free(dh); free(o);
+    return err;
 }

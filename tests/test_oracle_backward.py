@@ -1,0 +1,95 @@
+"""Pins of the oracle's backward pass: central finite differences of the
+oracle's own forward (fp64 inputs, routing held fixed) in random directions
+of every input and weight tensor, and closed forms.  No GPU."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+RNG = np.random.default_rng(2024)
+
+
+def _inputs(T, d, E, k, f, S=0, f_s=0, seed=0):
+    sh = synth.LayerShape("t", T=T, d=d, E=E, k=k, d_ff=f, num_shared=S, d_ff_shared=f_s, dtype=synth.F32)
+    inp = synth.make_inputs(sh, seed)
+    return {n: (None if a is None else a.astype(np.float64)) for n, a in inp.items()}
+
+
+def _loss(inp, ids, dy, score_fn, renorm):
+    T = inp["x"].shape[0]
+    y = oracle.forward_tokens(inp, ids.shape[1], np.arange(T), score_fn, renorm, forced_ids=ids)["y"]
+    return float(np.sum(dy * y))
+
+
+GRAD_OF = {"x": "dx", "w_router": "dw_router", "w_gate": "dw_gate", "w_up": "dw_up", "w_down": "dw_down",
+           "ws_gate": "ds_gate", "ws_up": "ds_up", "ws_down": "ds_down"}
+
+
+@pytest.mark.parametrize("score_fn,renorm,S", [(oracle.SOFTMAX, 1, 0), (oracle.SOFTMAX, 0, 1),
+                                               (oracle.SIGMOID, 1, 1), (oracle.SIGMOID, 0, 0)])
+def test_gradients_match_finite_differences(score_fn, renorm, S):
+    T, d, E, k, f = 5, 8, 6, 2, 12
+    inp = _inputs(T, d, E, k, f, S, 4 if S else 0, seed=3)
+    for n in ("x", "w_router"):
+        inp[n] = inp[n] * 2.0            # livelier gates
+    lg = oracle.logits(inp["x"], inp["w_router"])
+    ids = oracle.route(lg, k, score_fn, renorm)["ids"]
+    dy = RNG.normal(size=(T, d))
+    g = oracle.backward(inp, ids, dy, score_fn, renorm)
+    eps = 1e-6
+    for name, gname in GRAD_OF.items():
+        if inp.get(name) is None:
+            continue
+        v = RNG.normal(size=inp[name].shape)
+        plus, minus = dict(inp), dict(inp)
+        plus[name] = inp[name] + eps * v
+        minus[name] = inp[name] - eps * v
+        fd = (_loss(plus, ids, dy, score_fn, renorm) - _loss(minus, ids, dy, score_fn, renorm)) / (2 * eps)
+        an = float(np.sum(g[gname] * v))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), f"{name}: finite difference {fd} vs gradient {an}"
+
+
+def test_single_renormalised_choice_gives_no_router_gradient():
+    """k = 1 with renormalisation: the gate is 1 whatever the logits, so the
+    router gets no gradient and dx has only the expert path."""
+    inp = _inputs(7, 8, 4, 1, 12, seed=5)
+    lg = oracle.logits(inp["x"], inp["w_router"])
+    ids = oracle.route(lg, 1)["ids"]
+    dy = RNG.normal(size=(7, 8))
+    g = oracle.backward(inp, ids, dy, oracle.SOFTMAX, 1)
+    np.testing.assert_allclose(g["dw_router"], 0.0, atol=1e-14)   # the Jacobian terms cancel
+    # the expert path alone: dx = W_gate^T da + W_up^T du for the chosen expert
+    x, wg, wu, wd = (inp[n] for n in ("x", "w_gate", "w_up", "w_down"))
+    for t in range(7):
+        e = ids[t, 0]
+        a, u = wg[e] @ x[t], wu[e] @ x[t]
+        sig = 1 / (1 + np.exp(-a))
+        dh = wd[e].T @ dy[t]
+        da = dh * u * (sig + a * sig * (1 - sig))
+        du = dh * a * sig
+        np.testing.assert_allclose(g["dx"][t], wg[e].T @ da + wu[e].T @ du, rtol=1e-12, atol=1e-14)
+
+
+def test_weight_gradients_are_outer_product_sums():
+    """dW_down of an expert is the sum over its pairs of (g dy) h^T: with all
+    tokens sent to one expert and k = 1, renorm = 0 (Switch), it equals
+    (g * dy)^T H computed with plain matmuls."""
+    inp = _inputs(9, 8, 3, 1, 10, seed=8)
+    inp["w_router"] = inp["w_router"] * 0.0
+    inp["w_router"][1] = 1.0              # expert 1 wins only where sum(x) > 0 ...
+    inp["w_router"][:, 0] += np.array([0.0, 50.0, 0.0])   # ... so force it through x[:, 0]
+    x = inp["x"]
+    x[:, 0] = 1.0
+    lg = oracle.logits(x, inp["w_router"])
+    ids = oracle.route(lg, 1, oracle.SOFTMAX, 0)["ids"]
+    assert (ids == 1).all()
+    dy = RNG.normal(size=(9, 8))
+    g = oracle.backward(inp, ids, dy, oracle.SOFTMAX, 0)
+    s = np.exp(lg - lg.max(1, keepdims=True))
+    s /= s.sum(1, keepdims=True)
+    gate = s[:, 1]
+    a, u = x @ inp["w_gate"][1].T, x @ inp["w_up"][1].T
+    H = a / (1 + np.exp(-a)) * u
+    np.testing.assert_allclose(g["dw_down"][1], (gate[:, None] * dy).T @ H, rtol=1e-12, atol=1e-14)
+    assert np.all(g["dw_down"][0] == 0.0) and np.all(g["dw_down"][2] == 0.0)

@@ -30,8 +30,16 @@ MUTATIONS = {
     "capacity_off_by_one": ("(cap < 0 || c < cap)", "(cap < 0 || c <= cap)"),
     "dropped_pair_counted": ("if (keep && !keep[i * k + j]) continue;", ";"),
     "gate_from_key": ("denom += s[id[j]];", "denom += key[id[j]];"),
+    "dsilu_dropped_term": ("double dsilu = sig * (1.0 + a[r] * (1.0 - sig));        /* d/da of a * sigmoid(a) */",
+                           "double dsilu = sig;"),
+    "renorm_jacobian_sign": ("dgj_dlm = dse_dlm / S - s[e] * dS_dlm / (S * S);",
+                             "dgj_dlm = dse_dlm / S + s[e] * dS_dlm / (S * S);"),
+    "router_grad_transposed": ("dxt[c] += widen(w_r, dtype, (int64_t)m * d + c) * dl[m];",
+                               "dxt[c] += widen(w_r, dtype, (int64_t)c * E + m) * dl[m];"),
+    "shared_grad_ungated_missing": ("for (int r = 0; r < f_s; ++r) dsd[(int64_t)c * f_s + r] += dyt[c] * h[r];",
+                                    "for (int r = 0; r < f_s; ++r) dsd[(int64_t)c * f_s + r] += 0.5 * dyt[c] * h[r];"),
 }
-PIN_FILES = ["test_oracle_pins.py", "test_oracle_next.py"]
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_next.py", "test_oracle_backward.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
