@@ -201,6 +201,32 @@ int moe_forward_staged(const moe_config* cfg, const void* x, const void* w_route
                        void* const* stage_events, void* stream);
 
 /*
+ * Backward pass of the layer for the routing of a forward call ("8.6 Mixture
+ * of Experts", sec. 2; the router learns only through the gates of the
+ * chosen experts, "Mixture-of-Experts Internals", sec. 2.2).  With L the
+ * loss and dy = dL/dy [T,d] (cfg->dtype):
+ *   topk_ids, topk_weights [T,k]     in: the forward's routing (held fixed;
+ *                                    the selection itself has no gradient)
+ *   dx [T,d]                         out: dL/dx, through the experts, the
+ *                                    gates and the shared expert
+ *   dw_router [E,d]                  out: through the gates only
+ *   dw_gate, dw_up [E,d_ff,d]; dw_down [E,d,d_ff]   out (0 for unused experts)
+ *   dws_gate, dws_up [d_ff_s,d]; dws_down [d,d_ff_s] out, nullable iff
+ *                                    num_shared == 0
+ * All gradients are fp32 and overwritten (not accumulated).  The plain layer
+ * only (no moe_options).  The expert pre-activations are recomputed, nothing
+ * is kept from the forward but its routing.  Sums run in a fixed order, no
+ * atomics: the result is deterministic.  ws: at least
+ * moe_backward_workspace_bytes(cfg) bytes.
+ */
+size_t moe_backward_workspace_bytes(const moe_config* cfg);
+int moe_backward(const moe_config* cfg, const void* x, const void* w_router, const void* w_gate,
+                 const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,
+                 const void* ws_down, const void* dy, const int32_t* topk_ids, const float* topk_weights,
+                 float* dx, float* dw_router, float* dw_gate, float* dw_up, float* dw_down, float* dws_gate,
+                 float* dws_up, float* dws_down, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Optional routing features.  A NULL moe_options*, or one with every field
  * zero, is the plain layer above.
  *   expert_bias [E] fp32 (device, nullable): a per-expert bias used only to

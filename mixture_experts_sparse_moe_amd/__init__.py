@@ -9,7 +9,8 @@ library is missing, importing works but every call raises.
 Entry points (same names as the C ABI):
     moe_workspace_bytes, moe_route, moe_dispatch, moe_expert_ffn,
     moe_combine, moe_forward, moe_forward_staged, moe_status_str,
-    moe_route_ex, moe_dispatch_ex, moe_forward_ex (with MoeOptions)
+    moe_route_ex, moe_dispatch_ex, moe_forward_ex (with MoeOptions),
+    moe_backward_workspace_bytes, moe_backward
 """
 from __future__ import annotations
 
@@ -29,7 +30,8 @@ MOE_F32, MOE_BF16 = 0, 1
 
 EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_staged",
-           "moe_route_ex", "moe_dispatch_ex", "moe_forward_ex")
+           "moe_route_ex", "moe_dispatch_ex", "moe_forward_ex", "moe_backward_workspace_bytes",
+           "moe_backward")
 MOE_NUM_STAGES = 7
 STAGE_NAMES = ("route", "dispatch", "gate_up_gemm", "down_gemm", "shared_gate_up", "shared_down",
                "combine")
@@ -113,6 +115,10 @@ def lib():
         L.moe_dispatch_ex.restype = i32
         L.moe_forward_ex.argtypes = [cfgp, optp] + [vp] * 12 + [vp, sz, vp]
         L.moe_forward_ex.restype = i32
+        L.moe_backward_workspace_bytes.argtypes = [cfgp]
+        L.moe_backward_workspace_bytes.restype = sz
+        L.moe_backward.argtypes = [cfgp] + [vp] * 20 + [sz, vp]
+        L.moe_backward.restype = i32
         _lib = L
     return _lib
 
@@ -358,6 +364,48 @@ def moe_forward_ex(cfg, opts, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up,
                              _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(y),
                              _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_counts), _ptr(ws),
                              _ws_bytes(ws), _stream(stream)), "moe_forward_ex")
+
+
+def moe_backward_workspace_bytes(cfg: MoeConfig) -> int:
+    return int(lib().moe_backward_workspace_bytes(ctypes.byref(cfg)))
+
+
+def moe_backward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, dy, topk_ids,
+                 topk_weights, dx, dw_router, dw_gate, dw_up, dw_down, dws_gate=None, dws_up=None,
+                 dws_down=None, ws=None, stream=None):
+    """Gradients (fp32) of the layer for the forward's routing."""
+    torch = _torch()
+    T, d, E, k, f, fs = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k, cfg.d_ff, cfg.d_ff_shared
+    dt, dev = _act_dtype(cfg), x.device
+    f32 = torch.float32
+    _check(x, "x", (T, d), dt, dev)
+    _check(w_router, "w_router", (E, d), dt, dev)
+    _check_experts(cfg, dev, w_gate, w_up, w_down, ws_gate, ws_up, ws_down)
+    _check(dy, "dy", (T, d), dt, dev)
+    _check(topk_ids, "topk_ids", (T, k), torch.int32, dev)
+    _check(topk_weights, "topk_weights", (T, k), f32, dev)
+    _check(dx, "dx", (T, d), f32, dev)
+    _check(dw_router, "dw_router", (E, d), f32, dev)
+    _check(dw_gate, "dw_gate", (E, f, d), f32, dev)
+    _check(dw_up, "dw_up", (E, f, d), f32, dev)
+    _check(dw_down, "dw_down", (E, d, f), f32, dev)
+    if cfg.num_shared:
+        _check(dws_gate, "dws_gate", (fs, d), f32, dev)
+        _check(dws_up, "dws_up", (fs, d), f32, dev)
+        _check(dws_down, "dws_down", (d, fs), f32, dev)
+    _rc(lib().moe_backward(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                           _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(dy), _ptr(topk_ids),
+                           _ptr(topk_weights), _ptr(dx), _ptr(dw_router), _ptr(dw_gate), _ptr(dw_up),
+                           _ptr(dw_down), _ptr(dws_gate), _ptr(dws_up), _ptr(dws_down), _ptr(ws),
+                           _ws_bytes(ws), _stream(stream)), "moe_backward")
+
+
+def alloc_backward_workspace(cfg, device="cuda"):
+    """A device byte buffer of moe_backward_workspace_bytes(cfg) bytes."""
+    n = moe_backward_workspace_bytes(cfg)
+    if n == 0:
+        raise ValueError(f"invalid config {cfg}")
+    return _torch().empty(n, dtype=_torch().uint8, device=device)
 
 
 def alloc_workspace(cfg, device="cuda"):

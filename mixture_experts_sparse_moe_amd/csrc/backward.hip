@@ -1,0 +1,343 @@
+// Backward pass of the layer for a given routing ("8.6 Mixture of Experts",
+// sec. 2: y = sum_i g_i f_i(x); the router learns only through the gates of
+// the chosen experts, "Mixture-of-Experts Internals", sec. 2.2).  With dy the
+// gradient of the output and the routing (ids, gates) of the forward:
+//   pair p (token t, expert e, gate g):  dO_p = g dy_t,  dg_p = <dy_t, f_e(x_t)>
+//   dH'_p = dy_t W_down,e        (so dg_p = <dH'_p, h_p> and dH_p = g dH'_p)
+//   da = g dH' * u * silu'(a),  du = g dH' * silu(a)   (a, u recomputed)
+//   dx_t  = sum over its pairs of (da W_gate,e + du W_up,e) + dl_t W_r (+ shared)
+//   dW_down,e = sum_p dO_p h_p^T;  dW_gate,e = sum_p da_p x^T;  dW_up,e likewise
+//   dl_t: the gates' Jacobian with respect to the logits times dg; dW_r = dl^T x.
+// Gradients are fp32.  Every sum is taken in a fixed order (no atomics).
+//
+// The GEMMs of the backward are NN (dgrad: the weights are contracted over
+// their output dimension) and TN (weight gradients: a sum over each expert's
+// rows).  They run on one generic LDS-tiled kernel with fp32 FMA, any operand
+// layout, gathered rows and per-group row ranges: correct for every shape,
+// not tuned.  The recomputation of a and u uses the forward's grouped GEMM.
+#include "device_util.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kGT = 256;                  // threads
+constexpr int kGBM = 64, kGBN = 64, kGBK = 16;
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+template <>
+__device__ __forceinline__ float ld<float>(const float* p, int64_t i) { return p[i]; }
+
+template <typename T>
+__device__ __forceinline__ void st(T* p, int64_t i, float v);
+template <>
+__device__ __forceinline__ void st<uint16_t>(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+template <>
+__device__ __forceinline__ void st<float>(float* p, int64_t i, float v) { p[i] = v; }
+
+// Output rows of group g in ROWS mode: the M tiles of 64 rows over the groups
+// (prefix in LDS, as in the forward GEMM).
+__device__ __forceinline__ bool rows_tile(const GradGemm& a, int mt, int* grp, int* r0, int* nr) {
+    if (!a.offsets) {
+        *grp = 0;
+        *r0 = mt * kGBM;
+        *nr = min(kGBM, a.M - *r0);
+        return *r0 < a.M;
+    }
+    __shared__ int s_wsum[4], s_res[3];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (threadIdx.x == 0) s_res[0] = -1;
+    int nt = 0, cnt = 0, off = 0;
+    const int e = threadIdx.x;
+    if (e < a.G) {
+        off = a.offsets[e];
+        cnt = a.offsets[e + 1] - off;
+        nt = (cnt + kGBM - 1) / kGBM;
+    }
+    int v = nt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) s_wsum[w] = v;
+    __syncthreads();
+    int before = 0;
+    for (int q = 0; q < w; ++q) before += s_wsum[q];
+    const int incl = v + before, excl = incl - nt;
+    if (e < a.G && mt >= excl && mt < incl) {
+        s_res[0] = e;
+        s_res[1] = off + (mt - excl) * kGBM;
+        s_res[2] = min(kGBM, cnt - (mt - excl) * kGBM);
+    }
+    __syncthreads();
+    if (s_res[0] < 0) return false;
+    *grp = s_res[0];
+    *r0 = s_res[1];
+    *nr = s_res[2];
+    return true;
+}
+
+// C (+)= A B over one 64 x 64 tile; see GradGemm.  Thread (tm, tn) owns a
+// 4 x 4 block of outputs; K in steps of 16 through LDS (fp32).
+template <typename TA, typename TB, bool KROWS, bool B_KCONT>
+__global__ __launch_bounds__(kGT) void grad_gemm_kernel(GradGemm a, int tiles_m, int tiles_n) {
+    __shared__ float As[kGBK][kGBM + 4];
+    __shared__ float Bs[kGBK][kGBN + 4];
+    const int tid = threadIdx.x;
+    const int nt = blockIdx.x % tiles_n;
+    const int mt = (blockIdx.x / tiles_n) % tiles_m;
+    const int gz = blockIdx.x / tiles_n / tiles_m;       // KROWS: the group
+    int grp, r0, nr, k0, k1;
+    if (KROWS) {
+        grp = gz;
+        r0 = mt * kGBM;
+        nr = min(kGBM, a.M - r0);
+        k0 = a.offsets ? a.offsets[grp] : 0;
+        k1 = a.offsets ? a.offsets[grp + 1] : a.K;
+        if (nr <= 0) return;
+    } else {
+        if (!rows_tile(a, mt, &grp, &r0, &nr)) return;
+        k0 = 0;
+        k1 = a.K;
+    }
+    const int n0 = nt * kGBN;
+    const TA* A = static_cast<const TA*>(a.A);
+    const TB* B = static_cast<const TB*>(a.B) + (int64_t)grp * a.b_gstride;
+    const int tm = tid >> 4, tn = tid & 15;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+
+    for (int kb = k0; kb < k1; kb += kGBK) {
+        // A tile -> As[k][m]
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int idx = tid + q * kGT;             // 0 .. 1023
+            int m, kk;
+            if (KROWS) { kk = idx >> 6; m = idx & 63; }   // M contiguous: consecutive threads, consecutive m
+            else { m = idx >> 4; kk = idx & 15; }         // K contiguous
+            const int k = kb + kk;
+            float v = 0.0f;
+            if (m < nr && k < k1) {
+                if (KROWS) {
+                    v = ld<TA>(A, (int64_t)k * a.lda + r0 + m);
+                } else {
+                    const int r = r0 + m;
+                    const int64_t src = a.a_gather ? a.a_gather[r] / a.a_div : r;
+                    v = ld<TA>(A, src * a.lda + k);
+                }
+            }
+            As[kk][m] = v;
+        }
+        // B tile -> Bs[k][n]
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int idx = tid + q * kGT;
+            int n, kk;
+            if (B_KCONT) { n = idx >> 4; kk = idx & 15; }
+            else { kk = idx >> 6; n = idx & 63; }
+            const int k = kb + kk;
+            float v = 0.0f;
+            if (n0 + n < a.N && k < k1) {
+                if (B_KCONT) {
+                    v = ld<TB>(B, (int64_t)(n0 + n) * a.ldb + k);
+                } else {
+                    const int64_t src = (KROWS && a.b_gather) ? a.b_gather[k] / a.b_div : k;
+                    v = ld<TB>(B, src * a.ldb + n0 + n);
+                }
+            }
+            Bs[kk][n] = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kGBK; ++kk) {
+            float x4[4], y4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x4[i] = As[kk][tm * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y4[j] = Bs[kk][tn * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(x4[i], y4[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+    float* C = a.C + (KROWS ? (int64_t)grp * a.c_gstride : 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = tm * 4 + i;
+        if (m >= nr) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + tn * 4 + j;
+            if (n >= a.N) continue;
+            float* c = C + (int64_t)(r0 + m) * a.ldc + n;
+            *c = a.accumulate ? *c + acc[i][j] : acc[i][j];
+        }
+    }
+}
+
+// One workgroup per grouped row r (pair p = sorted[r], or token r when there
+// is no grouping): h = silu(a) u; dg = <dH', h>; da, du; dO = g dy.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_pair_kernel(BwdPairArgs b) {
+    const int r = blockIdx.x;
+    if (b.offsets && r >= b.offsets[b.G]) return;
+    const int p = b.sorted ? b.sorted[r] : r;
+    const int t = b.sorted ? p / b.k : r;
+    const float g = b.gates ? b.gates[p] : 1.0f;
+    const T* A = static_cast<const T*>(b.a) + (int64_t)r * b.f;
+    const T* U = static_cast<const T*>(b.u) + (int64_t)r * b.f;
+    const float* dHp = b.dhp + (int64_t)r * b.f;
+    T* H = static_cast<T*>(b.h) + (int64_t)r * b.f;
+    T* DA = static_cast<T*>(b.da) + (int64_t)r * b.f;
+    T* DU = static_cast<T*>(b.du) + (int64_t)r * b.f;
+    float part = 0.0f;
+    for (int i = threadIdx.x; i < b.f; i += 256) {
+        const float av = ld<T>(A, i), uv = ld<T>(U, i), d = dHp[i];
+        const float sg = 1.0f / (1.0f + expf(-av));
+        const float hv = av * sg * uv;
+        st<T>(H, i, hv);
+        part = fmaf(d, hv, part);
+        const float dh = g * d;
+        st<T>(DA, i, dh * uv * (sg * (1.0f + av * (1.0f - sg))));
+        st<T>(DU, i, dh * av * sg);
+    }
+    if (b.dgate) {
+        // fixed-order sum: per thread, then threads in index order
+        __shared__ float s_part[256];
+        s_part[threadIdx.x] = part;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            float v = 0.0f;
+            for (int i = 0; i < 256; ++i) v += s_part[i];
+            b.dgate[p] = v;
+        }
+    }
+    if (b.d_o) {
+        const T* dy = static_cast<const T*>(b.dy) + (int64_t)t * b.dm;
+        T* dO = static_cast<T*>(b.d_o) + (int64_t)r * b.dm;
+        for (int i = threadIdx.x; i < b.dm; i += 256) st<T>(dO, i, g * ld<T>(dy, i));
+    }
+}
+
+// One wave per token: dl[t, :] from dg of its k pairs (pair p = t k + j) and,
+// when needed, the recomputed logits.
+__global__ __launch_bounds__(256) void bwd_router_kernel(BwdRouterArgs b) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= b.T) return;
+    float* dl = b.dl + (int64_t)t * b.E;
+    const int32_t* id = b.ids + (int64_t)t * b.k;
+    const float* gate = b.gates + (int64_t)t * b.k;
+    const float* dg = b.dgate + (int64_t)t * b.k;
+    const float* l = b.logits ? b.logits + (int64_t)t * b.E : nullptr;
+    // sum_j g_j dg_j over the chosen (the gates as the forward computed them)
+    float gdg = 0.0f;
+    for (int j = 0; j < b.k; ++j) gdg = fmaf(gate[j], dg[j], gdg);
+    // each lane writes its own experts' entries (0 for experts not chosen,
+    // except for softmax without renormalisation, where every logit matters)
+    float mx = 0.0f, z = 1.0f, ssum = 0.0f;
+    if (b.score_fn == 0 && !b.renorm) {
+        mx = -__builtin_inff();
+        for (int e = 0; e < b.E; ++e) mx = fmaxf(mx, l[e]);
+        z = 0.0f;
+        for (int e = 0; e < b.E; ++e) z += expf(l[e] - mx);
+    }
+    if (b.score_fn == 1)
+        for (int j = 0; j < b.k; ++j) ssum += 1.0f / (1.0f + expf(-l[id[j]]));
+    for (int e = lane; e < b.E; e += 64) {
+        int j = -1;
+        for (int q = 0; q < b.k; ++q)
+            if (id[q] == e) j = q;
+        float v = 0.0f;
+        if (b.score_fn == 0 && b.renorm) {
+            // g = softmax over the chosen logits: dl_i = g_i (dg_i - sum_j g_j dg_j)
+            if (j >= 0) v = gate[j] * (dg[j] - gdg);
+        } else if (b.score_fn == 0) {
+            // g_i = s_i, the softmax over all E: dl_e = s_e (dg_e - sum_j s_{e_j} dg_j)
+            v = expf(l[e] - mx) / z * ((j >= 0 ? dg[j] : 0.0f) - gdg);
+        } else if (j >= 0) {
+            // sigmoid s_i; renormalised: g_i = s_i / S, ds_i = (dg_i - sum_j g_j dg_j) / S
+            const float sg = 1.0f / (1.0f + expf(-l[e]));
+            const float ds = b.renorm ? (dg[j] - gdg) / ssum : dg[j];
+            v = ds * sg * (1.0f - sg);
+        }
+        dl[e] = v;
+    }
+}
+
+// dx[t, :] = sum over the token's pairs, in slot order, of dXp[pair_pos].
+__global__ __launch_bounds__(256) void bwd_token_sum_kernel(const float* dxp, const int32_t* pair_pos, int k, int d,
+                                                            float* dx) {
+    const int t = blockIdx.x;
+    for (int c = threadIdx.x; c < d; c += 256) {
+        float v = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const int pos = pair_pos[(int64_t)t * k + j];
+            if (pos >= 0) v += dxp[(int64_t)pos * d + c];
+        }
+        dx[(int64_t)t * d + c] = v;
+    }
+}
+
+template <typename TA, typename TB>
+hipError_t launch_grad_gemm_t(const GradGemm& a, bool krows, bool b_kcont, hipStream_t s) {
+    const int tiles_n = (a.N + kGBN - 1) / kGBN;
+    int tiles_m, groups;
+    if (krows) {
+        tiles_m = (a.M + kGBM - 1) / kGBM;
+        groups = a.offsets ? a.G : 1;
+    } else {
+        tiles_m = (int)(a.offsets ? grouped_m_tiles_upper(a.M, a.G, kGBM) : (a.M + kGBM - 1) / kGBM);
+        groups = 1;
+    }
+    const int64_t grid = (int64_t)tiles_m * tiles_n * groups;
+    if (grid == 0) return hipSuccess;
+    if (grid > INT32_MAX || (krows && b_kcont)) return hipErrorInvalidValue;
+    const dim3 g3((unsigned)grid), b3(kGT);
+    if (krows) hipLaunchKernelGGL((grad_gemm_kernel<TA, TB, true, false>), g3, b3, 0, s, a, tiles_m, tiles_n);
+    else if (b_kcont) hipLaunchKernelGGL((grad_gemm_kernel<TA, TB, false, true>), g3, b3, 0, s, a, tiles_m, tiles_n);
+    else hipLaunchKernelGGL((grad_gemm_kernel<TA, TB, false, false>), g3, b3, 0, s, a, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_grad_gemm(const GradGemm& a, bool krows, bool b_kcont, bool a_bf16, bool b_bf16, hipStream_t s) {
+    if (a.G > 256) return hipErrorInvalidValue;
+    if (a_bf16 && b_bf16) return launch_grad_gemm_t<uint16_t, uint16_t>(a, krows, b_kcont, s);
+    if (!a_bf16 && b_bf16) return launch_grad_gemm_t<float, uint16_t>(a, krows, b_kcont, s);
+    if (!a_bf16 && !b_bf16) return launch_grad_gemm_t<float, float>(a, krows, b_kcont, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_pair(const BwdPairArgs& b, int rows, bool bf16, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if (bf16) hipLaunchKernelGGL(bwd_pair_kernel<uint16_t>, dim3(rows), dim3(256), 0, s, b);
+    else hipLaunchKernelGGL(bwd_pair_kernel<float>, dim3(rows), dim3(256), 0, s, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_router(const BwdRouterArgs& b, hipStream_t s) {
+    if (b.T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_router_kernel, dim3((b.T + 3) / 4), dim3(256), 0, s, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_token_sum(const float* dxp, const int32_t* pair_pos, int T, int k, int d, float* dx,
+                                hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_token_sum_kernel, dim3(T), dim3(256), 0, s, dxp, pair_pos, k, d, dx);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -319,6 +319,144 @@ int forward_impl(const moe_config* cfg, const moe_options* opts, const void* x, 
     return mark(ev, 6, s);
 }
 
+
+// Backward workspace, 256-byte aligned regions.
+struct BwdLayout {
+    size_t counts, offsets, sorted, pos, chunk, A, U, H, DA, DU, dHp, dO, dXp, dgate, logits, dl;
+    size_t As, Us, Hs, DAs, DUs, dHs, total;
+};
+
+BwdLayout bwd_layout(const moe_config* c) {
+    const size_t T = (size_t)c->num_tokens, P = T * c->top_k, E = c->num_experts;
+    const size_t d = c->d_model, f = c->d_ff, fs = c->num_shared ? c->d_ff_shared : 0, w = elem(c);
+    BwdLayout L{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+    L.chunk = take((size_t)dispatch_num_chunks((int)P) * E * 4);
+    L.counts = take(E * 4);
+    L.offsets = take((E + 1) * 4);
+    L.sorted = take(P * 4);
+    L.pos = take(P * 4);
+    L.A = take(P * f * w);
+    L.U = take(P * f * w);
+    L.H = take(P * f * w);
+    L.DA = take(P * f * w);
+    L.DU = take(P * f * w);
+    L.dHp = take(P * f * 4);
+    L.dO = take(P * d * w);
+    L.dXp = take(P * d * 4);
+    L.dgate = take(P * 4);
+    L.logits = take(T * E * 4);
+    L.dl = take(T * E * 4);
+    L.As = take(T * fs * w);
+    L.Us = take(T * fs * w);
+    L.Hs = take(T * fs * w);
+    L.DAs = take(T * fs * w);
+    L.DUs = take(T * fs * w);
+    L.dHs = take(T * fs * 4);
+    L.total = o;
+    return L;
+}
+
+GradGemm grad_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc, int M, int N,
+                   int K) {
+    GradGemm g{};
+    g.A = A; g.lda = lda; g.a_div = 1;
+    g.B = B; g.ldb = ldb; g.b_div = 1;
+    g.C = C; g.ldc = ldc;
+    g.G = 1; g.M = M; g.N = N; g.K = K;
+    return g;
+}
+
+int run_backward(const moe_config* c, const void* x, const void* wr, const void* wg, const void* wu,
+                 const void* wd, const void* sg, const void* su, const void* sd, const void* dy,
+                 const int32_t* ids, const float* gates, float* dx, float* dwr, float* dwg, float* dwu,
+                 float* dwd, float* dsg, float* dsu, float* dsd, void* ws, hipStream_t s) {
+    const BwdLayout L = bwd_layout(c);
+    const bool bf16 = c->dtype == MOE_BF16;
+    const int T = c->num_tokens, k = c->top_k, E = c->num_experts, P = T * k;
+    const int d = c->d_model, f = c->d_ff;
+    int32_t* counts = at<int32_t>(ws, L.counts);
+    int32_t* offsets = at<int32_t>(ws, L.offsets);
+    int32_t* sorted = at<int32_t>(ws, L.sorted);
+    int32_t* pos = at<int32_t>(ws, L.pos);
+    void *A = at<void>(ws, L.A), *U = at<void>(ws, L.U), *H = at<void>(ws, L.H);
+    void *DA = at<void>(ws, L.DA), *DU = at<void>(ws, L.DU), *dO = at<void>(ws, L.dO);
+    float *dHp = at<float>(ws, L.dHp), *dXp = at<float>(ws, L.dXp), *dgate = at<float>(ws, L.dgate);
+    float *logits = at<float>(ws, L.logits), *dl = at<float>(ws, L.dl);
+
+    // routing groups of the forward's ids
+    MOE_TRY(run_dispatch(c, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s));
+    // a = x W_gate^T, u = x W_up^T on the grouped rows (the forward's GEMM)
+    GemmGroup ga{x, sorted, k, offsets, E, P, wg, nullptr, A, f, d};
+    MOE_HIP(launch_grouped_gemm(ga, false, bf16, s));
+    GemmGroup gu{x, sorted, k, offsets, E, P, wu, nullptr, U, f, d};
+    MOE_HIP(launch_grouped_gemm(gu, false, bf16, s));
+    // dH' = dy W_down (rows gathered by pair)
+    GradGemm g1 = grad_gemm(dy, d, wd, f, dHp, f, P, f, d);
+    g1.a_gather = sorted; g1.a_div = k; g1.b_gstride = (int64_t)d * f; g1.offsets = offsets; g1.G = E;
+    MOE_HIP(launch_grad_gemm(g1, false, false, bf16, bf16, s));
+    // h, dg, da, du, dO per pair
+    BwdPairArgs pa{sorted, offsets, E, k, gates, A, U, dHp, H, DA, DU, dgate, dy, dO, f, d};
+    MOE_HIP(launch_bwd_pair(pa, P, bf16, s));
+    // dx of each pair = da W_gate + du W_up, then summed per token in slot order
+    GradGemm g2 = grad_gemm(DA, f, wg, d, dXp, d, P, d, f);
+    g2.b_gstride = (int64_t)f * d; g2.offsets = offsets; g2.G = E;
+    MOE_HIP(launch_grad_gemm(g2, false, false, bf16, bf16, s));
+    g2.A = DU; g2.B = wu; g2.accumulate = true;
+    MOE_HIP(launch_grad_gemm(g2, false, false, bf16, bf16, s));
+    MOE_HIP(launch_bwd_token_sum(dXp, pos, T, k, d, dx, s));
+    // weight gradients: sums over each expert's rows
+    GradGemm w1 = grad_gemm(dO, d, H, f, dwd, f, d, f, P);
+    w1.c_gstride = (int64_t)d * f; w1.offsets = offsets; w1.G = E;
+    MOE_HIP(launch_grad_gemm(w1, true, false, bf16, bf16, s));
+    GradGemm w2 = grad_gemm(DA, f, x, d, dwg, d, f, d, P);
+    w2.b_gather = sorted; w2.b_div = k; w2.c_gstride = (int64_t)f * d; w2.offsets = offsets; w2.G = E;
+    MOE_HIP(launch_grad_gemm(w2, true, false, bf16, bf16, s));
+    w2.A = DU; w2.C = dwu;
+    MOE_HIP(launch_grad_gemm(w2, true, false, bf16, bf16, s));
+    // router: dl from dg (logits recomputed when the gates need them)
+    const bool need_logits = !(c->score_fn == MOE_SCORE_SOFTMAX && c->renormalize);
+    if (need_logits) {
+        GradGemm gl = grad_gemm(x, d, wr, d, logits, E, T, E, d);
+        MOE_HIP(launch_grad_gemm(gl, false, true, bf16, bf16, s));
+    }
+    BwdRouterArgs ra{ids, gates, dgate, need_logits ? logits : nullptr, dl, T, E, k, c->score_fn, c->renormalize};
+    MOE_HIP(launch_bwd_router(ra, s));
+    GradGemm gr = grad_gemm(dl, E, x, d, dwr, d, E, d, T);
+    MOE_HIP(launch_grad_gemm(gr, true, false, false, bf16, s));
+    GradGemm gx = grad_gemm(dl, E, wr, d, dx, d, T, d, E);
+    gx.accumulate = true;
+    MOE_HIP(launch_grad_gemm(gx, false, false, false, bf16, s));
+    // shared expert: a pair per token with gate 1
+    if (c->num_shared) {
+        const int fs = c->d_ff_shared;
+        void *As = at<void>(ws, L.As), *Us = at<void>(ws, L.Us), *Hs = at<void>(ws, L.Hs);
+        void *DAs = at<void>(ws, L.DAs), *DUs = at<void>(ws, L.DUs);
+        float* dHs = at<float>(ws, L.dHs);
+        GemmGroup sa{x, nullptr, 1, nullptr, 1, T, sg, nullptr, As, fs, d};
+        MOE_HIP(launch_grouped_gemm(sa, false, bf16, s));
+        GemmGroup su_{x, nullptr, 1, nullptr, 1, T, su, nullptr, Us, fs, d};
+        MOE_HIP(launch_grouped_gemm(su_, false, bf16, s));
+        GradGemm s1 = grad_gemm(dy, d, sd, fs, dHs, fs, T, fs, d);
+        MOE_HIP(launch_grad_gemm(s1, false, false, bf16, bf16, s));
+        BwdPairArgs sp{nullptr, nullptr, 1, 1, nullptr, As, Us, dHs, Hs, DAs, DUs, nullptr, dy, nullptr, fs, d};
+        MOE_HIP(launch_bwd_pair(sp, T, bf16, s));
+        GradGemm s2 = grad_gemm(DAs, fs, sg, d, dx, d, T, d, fs);
+        s2.accumulate = true;
+        MOE_HIP(launch_grad_gemm(s2, false, false, bf16, bf16, s));
+        s2.A = DUs; s2.B = su;
+        MOE_HIP(launch_grad_gemm(s2, false, false, bf16, bf16, s));
+        GradGemm s3 = grad_gemm(dy, d, Hs, fs, dsd, fs, d, fs, T);
+        MOE_HIP(launch_grad_gemm(s3, true, false, bf16, bf16, s));
+        GradGemm s4 = grad_gemm(DAs, fs, x, d, dsg, d, fs, d, T);
+        MOE_HIP(launch_grad_gemm(s4, true, false, bf16, bf16, s));
+        s4.A = DUs; s4.C = dsu;
+        MOE_HIP(launch_grad_gemm(s4, true, false, bf16, bf16, s));
+    }
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -460,6 +598,36 @@ int moe_forward_ex(const moe_config* cfg, const moe_options* opts, const void* x
     return forward_impl(cfg, opts, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
                         topk_ids_out, topk_weights_out, expert_counts_out, ws, ws_bytes, nullptr, nullptr,
                         stream);
+}
+
+size_t moe_backward_workspace_bytes(const moe_config* cfg) {
+    if (validate_cfg(cfg) != MOE_OK) return 0;
+    return bwd_layout(cfg).total;
+}
+
+int moe_backward(const moe_config* cfg, const void* x, const void* w_router, const void* w_gate,
+                 const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,
+                 const void* ws_down, const void* dy, const int32_t* topk_ids, const float* topk_weights,
+                 float* dx, float* dw_router, float* dw_gate, float* dw_up, float* dw_down, float* dws_gate,
+                 float* dws_up, float* dws_down, void* ws, size_t ws_bytes, void* stream) {
+    MOE_TRY(validate_cfg(cfg));
+    const bool empty = cfg->num_tokens == 0;
+    for (const void* p : {x, dy, (const void*)topk_ids, (const void*)topk_weights, (const void*)dx})
+        MOE_TRY(check_ptr(p, empty));
+    for (const void* p : {w_router, w_gate, w_up, w_down, (const void*)dw_router, (const void*)dw_gate,
+                          (const void*)dw_up, (const void*)dw_down})
+        MOE_TRY(check_ptr(p, false));
+    if (cfg->num_shared)
+        for (const void* p : {ws_gate, ws_up, ws_down, (const void*)dws_gate, (const void*)dws_up,
+                              (const void*)dws_down})
+            MOE_TRY(check_ptr(p, false));
+    const BwdLayout L = bwd_layout(cfg);
+    if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    MOE_TRY(check_ptr(ws, false));
+    // T = 0 still runs: the weight gradients are written as zeros
+    return run_backward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, dy, topk_ids,
+                        topk_weights, dx, dw_router, dw_gate, dw_up, dw_down, dws_gate, dws_up, dws_down, ws,
+                        static_cast<hipStream_t>(stream));
 }
 
 int moe_forward(const moe_config* cfg, const void* x, const void* w_router, const void* w_gate,

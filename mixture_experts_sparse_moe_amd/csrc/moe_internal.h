@@ -90,6 +90,68 @@ int choose_splitk_skinny(int64_t mt_expected, int N, int K);
 // Upper bound of M-tiles over all groups for tile height bm.
 int64_t grouped_m_tiles_upper(int64_t rows, int G, int bm);
 
+// ---- backward -------------------------------------------------------------------
+// Generic grouped GEMM for the backward, fp32 FMA, C fp32:
+//   C(m, n) (+)= sum_k A(m, k) B(n, k)
+// rows mode (krows = false): group g owns output rows [offsets[g], offsets[g+1])
+//   (or [0, M) without offsets); A(m, k) = A[src(m) lda + k] with src(m) =
+//   a_gather[m] / a_div (or m); B(n, k) = Bg[k ldb + n], or Bg[n ldb + k]
+//   with b_kcont; Bg = B + g b_gstride; C(m, n) at C[m ldc + n].
+// krows mode: group g sums over k in [offsets[g], offsets[g+1]) (or [0, K));
+//   A(m, k) = A[k lda + m]; B(n, k) = B[src(k) ldb + n] with src(k) =
+//   b_gather[k] / b_div (or k); C(m, n) at C[g c_gstride + m ldc + n].
+struct GradGemm {
+    const void* A;
+    int64_t lda;
+    const int32_t* a_gather;
+    int a_div;
+    const void* B;
+    int64_t ldb, b_gstride;
+    const int32_t* b_gather;
+    int b_div;
+    float* C;
+    int64_t ldc, c_gstride;
+    bool accumulate;
+    const int32_t* offsets;
+    int G, M, N, K;
+};
+// a_bf16 / b_bf16: element type of A / B (bf16, or fp32); bf16 A needs bf16 B.
+hipError_t launch_grad_gemm(const GradGemm& a, bool krows, bool b_kcont, bool a_bf16, bool b_bf16, hipStream_t s);
+
+// Per grouped row r: h = silu(a) u, dg = <dH', h> (to dgate[pair], nullable),
+// da = g dH' u silu'(a), du = g dH' silu(a), dO = g dy[token] (nullable).
+struct BwdPairArgs {
+    const int32_t* sorted;  // grouped row -> pair (nullptr: rows are tokens)
+    const int32_t* offsets; // [G+1] or nullptr
+    int G, k;
+    const float* gates;     // [P] by pair, or nullptr (gate 1)
+    const void* a;          // [rows, f]
+    const void* u;          // [rows, f]
+    const float* dhp;       // [rows, f] dy W_down
+    void* h;                // [rows, f] out
+    void* da;               // [rows, f] out
+    void* du;               // [rows, f] out
+    float* dgate;           // [P] out, or nullptr
+    const void* dy;         // [T, dm]
+    void* d_o;              // [rows, dm] out, or nullptr
+    int f, dm;
+};
+hipError_t launch_bwd_pair(const BwdPairArgs& b, int rows, bool bf16, hipStream_t s);
+
+// dl [T, E] from the pairs' dg, the forward's gates and (sigmoid or softmax
+// without renormalisation) the logits.
+struct BwdRouterArgs {
+    const int32_t* ids;     // [T, k]
+    const float* gates;     // [T, k]
+    const float* dgate;     // [T, k] by pair
+    const float* logits;    // [T, E] or nullptr (softmax + renormalise)
+    float* dl;              // [T, E] out
+    int T, E, k, score_fn, renorm;
+};
+hipError_t launch_bwd_router(const BwdRouterArgs& b, hipStream_t s);
+hipError_t launch_bwd_token_sum(const float* dxp, const int32_t* pair_pos, int T, int k, int d, float* dx,
+                                hipStream_t s);
+
 // ---- combine ------------------------------------------------------------------
 struct CombineArgs {
     const void* expert_out; // [P, d]

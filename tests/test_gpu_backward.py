@@ -1,0 +1,99 @@
+"""GPU parity of the backward pass (moe_backward) against the oracle's
+chain-rule backward, for the GPU's own routing.  Every gradient must satisfy
+max|err| <= tau * max|ref|: tau = 1e-4 for fp32 layers; 2e-2 for bf16 layers
+(the recomputed a, u, h and the intermediate da, du, dO are rounded to bf16,
+about five roundings of 2^-9 along any path)."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_harness import TAU, DeviceLayer, assert_close, to_dev, to_host, torch
+
+pytestmark = pytest.mark.gpu
+S = synth.LayerShape
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch().cuda.is_available():
+        pytest.fail("GPU tests need an MI355X; torch.cuda.is_available() is False")
+    import mixture_experts_sparse_moe_amd as moe
+    moe.lib()
+
+
+CASES = {
+    "fp32_e8_k2": S("b", T=64, d=64, E=8, k=2, d_ff=128, dtype=synth.F32),
+    "fp32_e6_k3_sigmoid_raw_shared": S("b", T=40, d=64, E=6, k=3, d_ff=64, num_shared=1, d_ff_shared=64,
+                                       score_fn=synth.SIGMOID, renormalize=0, dtype=synth.F32),
+    "fp32_e6_k4_softmax_raw": S("b", T=50, d=64, E=6, k=4, d_ff=128, renormalize=0, dtype=synth.F32),
+    "bf16_e8_k2": S("b", T=200, d=256, E=8, k=2, d_ff=384),
+    "bf16_e32_k4_sigmoid_shared": S("b", T=150, d=128, E=32, k=4, d_ff=128, num_shared=1, d_ff_shared=192,
+                                    score_fn=synth.SIGMOID),
+    "bf16_e64_k8_zipf": S("b", T=300, d=256, E=64, k=8, d_ff=128, zipf_s=1.1),
+    "bf16_decode_e8_k2": S("b", T=16, d=512, E=8, k=2, d_ff=256),
+    "bf16_e4_k1": S("b", T=90, d=128, E=4, k=1, d_ff=128),
+}
+
+NAMES = [("dx", "dx"), ("dw_router", "dw_router"), ("dw_gate", "dw_gate"), ("dw_up", "dw_up"),
+         ("dw_down", "dw_down"), ("dws_gate", "ds_gate"), ("dws_up", "ds_up"), ("dws_down", "ds_down")]
+
+
+def run_backward(L, ids, wts, dy_d):
+    import mixture_experts_sparse_moe_amd as moe
+    t = torch()
+    sh, dv = L.sh, L.d
+    f32 = dict(dtype=t.float32, device="cuda")
+    out = dict(dx=t.full((sh.T, sh.d), 7.0, **f32), dw_router=t.full((sh.E, sh.d), 7.0, **f32),
+               dw_gate=t.full((sh.E, sh.d_ff, sh.d), 7.0, **f32), dw_up=t.full((sh.E, sh.d_ff, sh.d), 7.0, **f32),
+               dw_down=t.full((sh.E, sh.d, sh.d_ff), 7.0, **f32))
+    if sh.num_shared:
+        fs = sh.d_ff_shared
+        out.update(dws_gate=t.full((fs, sh.d), 7.0, **f32), dws_up=t.full((fs, sh.d), 7.0, **f32),
+                   dws_down=t.full((sh.d, fs), 7.0, **f32))
+    ws = moe.alloc_backward_workspace(L.cfg)
+    moe.moe_backward(L.cfg, dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], dv["ws_gate"],
+                     dv["ws_up"], dv["ws_down"], dy_d, ids, wts, out["dx"], out["dw_router"], out["dw_gate"],
+                     out["dw_up"], out["dw_down"], out.get("dws_gate"), out.get("dws_up"), out.get("dws_down"),
+                     ws=ws)
+    return out
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_backward_matches_oracle(name):
+    sh = CASES[name]
+    say(f"[case] backward {name} {sh}")
+    inp = synth.make_inputs(sh, 21)
+    L = DeviceLayer(sh, inp)
+    st = L.steps()
+    # dy: seeded normals in the layer's dtype (tensor id 99: not used by the inputs)
+    dy_h = synth.normal(21, 99, sh.T * sh.d, 1.0, sh.dtype).reshape(sh.T, sh.d)
+    dy_ref = synth.bf16_to_f64(dy_h) if sh.dtype == synth.BF16 else dy_h.astype(np.float64)
+    out = run_backward(L, st["ids"], st["weights"], to_dev(dy_h))
+    out2 = run_backward(L, st["ids"], st["weights"], to_dev(dy_h))
+    torch().cuda.synchronize()
+    gids = to_host(st["ids"])
+    ref = oracle.backward(inp, gids, dy_ref, sh.score_fn, sh.renormalize)
+    tau = TAU[sh.dtype]
+    worst = 0.0
+    for gname, rname in NAMES:
+        if gname not in out:
+            continue
+        got = to_host(out[gname]).astype(np.float64)
+        np.testing.assert_array_equal(got, to_host(out2[gname]), err_msg=f"{gname} not deterministic")
+        want = ref[rname]
+        if np.abs(want).max() < 1e-10:       # zero up to the oracle's rounding (k = 1, renormalised)
+            assert np.abs(got).max() <= 1e-6, f"{gname} should be zero"
+            continue
+        worst = max(worst, assert_close(got, want, tau, gname))
+    # experts that no pair chose get exactly zero weight gradients
+    unused = np.setdiff1d(np.arange(sh.E), gids.ravel())
+    for gname in ("dw_gate", "dw_up", "dw_down"):
+        assert not np.any(to_host(out[gname])[unused]), gname
+    say(f"[ok] worst max|err|/max|ref| = {worst:.2e}, unused experts {unused.tolist()}")
