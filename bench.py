@@ -49,6 +49,8 @@ def parse():
                    help="skip the practical ceilings (device copy, torch.matmul yardstick)")
     p.add_argument("--no-options", action="store_true",
                    help="skip timing the layer with its optional routing features")
+    p.add_argument("--no-backward", action="store_true",
+                   help="skip timing the backward pass (moe_backward)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of 1 GiB (the reference for HBM counters)")
     p.add_argument("--traffic-from", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_DIR"),
@@ -166,6 +168,48 @@ def options_cost(torch, moe, cfg, d, y, ws, stream, sh, steps: int) -> dict:
     st = stats.cpu().numpy()
     out["l_aux_alpha_0.01"] = float(st[2 * sh.E])
     out["max_over_mean_load"] = float(st[2 * sh.E + 1])
+    return out
+
+
+def backward_cost(torch, moe, cfg, d, sh, stream, steps: int) -> dict:
+    """ms per moe_backward for the layer's routing (dy seeded normal), and its
+    algorithmic FLOPs: 12 d d_ff per routed pair (data and weight gradients of
+    the three expert matrices), 4 d E per token for the router, 12 d d_ff_s per
+    token for the shared expert.  The recomputation of the expert
+    pre-activations (4 d d_ff per pair) is an implementation cost, not
+    counted.  Its GEMMs run on fp32 FMA, so the roofline is the fp32 vector
+    peak."""
+    import synth
+    dev = d["x"].device
+    T, E, k, dm, f, fs = sh.T, sh.E, sh.k, sh.d, sh.d_ff, sh.d_ff_shared
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    wts = torch.empty(T, k, dtype=torch.float32, device=dev)
+    moe.moe_route(cfg, d["x"], d["w_router"], ids, wts, stream=stream)
+    dy = upload(synth.normal(7, 99, T * dm, 1.0, sh.dtype).reshape(T, dm), torch, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dx=torch.empty(T, dm, **f32), dw_router=torch.empty(E, dm, **f32),
+             dw_gate=torch.empty(E, f, dm, **f32), dw_up=torch.empty(E, f, dm, **f32),
+             dw_down=torch.empty(E, dm, f, **f32))
+    if sh.num_shared:
+        g.update(dws_gate=torch.empty(fs, dm, **f32), dws_up=torch.empty(fs, dm, **f32),
+                 dws_down=torch.empty(dm, fs, **f32))
+    ws = moe.alloc_backward_workspace(cfg, dev)
+    run = lambda: moe.moe_backward(cfg, d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"],
+                                   d["ws_gate"], d["ws_up"], d["ws_down"], dy, ids, wts, g["dx"],
+                                   g["dw_router"], g["dw_gate"], g["dw_up"], g["dw_down"], g.get("dws_gate"),
+                                   g.get("dws_up"), g.get("dws_down"), ws=ws, stream=stream)
+    run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    flops = 12.0 * T * k * dm * f + 4.0 * T * dm * E + 12.0 * sh.num_shared * T * dm * fs
+    out = {"ms": round(ms, 3), "steps": steps, "alg_flops": flops, "tflops": flops / (ms * 1e-3) / 1e12,
+           "bound": "alu", "peak_tflops": PEAK_F32_TFLOPS}
+    out["frac"] = out["tflops"] / PEAK_F32_TFLOPS
+    del g, ws
     return out
 
 
@@ -428,6 +472,8 @@ def main():
     if not args.no_options:
         out["options_ms_per_step"] = options_cost(torch, moe, cfg, d, y, ws, stream, sh,
                                                   max(3, min(args.steps, 20)))
+    if not args.no_backward:
+        out["backward"] = backward_cost(torch, moe, cfg, d, sh, stream, 3)
     if not args.no_ceilings:
         out["practical_ceilings"] = practical_ceilings(torch, dev)
     if not args.no_cpu_baseline:
