@@ -177,8 +177,8 @@ def backward_cost(torch, moe, cfg, d, sh, stream, steps: int) -> dict:
     the three expert matrices), 4 d E per token for the router, 12 d d_ff_s per
     token for the shared expert.  The recomputation of the expert
     pre-activations (4 d d_ff per pair) is an implementation cost, not
-    counted.  Its GEMMs run on fp32 FMA, so the roofline is the fp32 vector
-    peak."""
+    counted.  bf16 layers run its GEMMs on bf16 MFMA (roofline: the dense
+    bf16 peak), fp32 layers on fp32 FMA (the fp32 vector peak)."""
     import synth
     dev = d["x"].device
     T, E, k, dm, f, fs = sh.T, sh.E, sh.k, sh.d, sh.d_ff, sh.d_ff_shared
@@ -206,9 +206,11 @@ def backward_cost(torch, moe, cfg, d, sh, stream, steps: int) -> dict:
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / steps * 1e3
     flops = 12.0 * T * k * dm * f + 4.0 * T * dm * E + 12.0 * sh.num_shared * T * dm * fs
+    bf16 = sh.dtype == synth.BF16
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     out = {"ms": round(ms, 3), "steps": steps, "alg_flops": flops, "tflops": flops / (ms * 1e-3) / 1e12,
-           "bound": "alu", "peak_tflops": PEAK_F32_TFLOPS}
-    out["frac"] = out["tflops"] / PEAK_F32_TFLOPS
+           "bound": "mfma" if bf16 else "alu", "peak_tflops": peak}
+    out["frac"] = out["tflops"] / peak
     del g, ws
     return out
 

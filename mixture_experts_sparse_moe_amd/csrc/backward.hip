@@ -41,11 +41,12 @@ __device__ __forceinline__ void st<float>(float* p, int64_t i, float v) { p[i] =
 
 // Output rows of group g in ROWS mode: the M tiles of 64 rows over the groups
 // (prefix in LDS, as in the forward GEMM).
+template <int BM>
 __device__ __forceinline__ bool rows_tile(const GradGemm& a, int mt, int* grp, int* r0, int* nr) {
     if (!a.offsets) {
         *grp = 0;
-        *r0 = mt * kGBM;
-        *nr = min(kGBM, a.M - *r0);
+        *r0 = mt * BM;
+        *nr = min(BM, a.M - *r0);
         return *r0 < a.M;
     }
     __shared__ int s_wsum[4], s_res[3];
@@ -56,7 +57,7 @@ __device__ __forceinline__ bool rows_tile(const GradGemm& a, int mt, int* grp, i
     if (e < a.G) {
         off = a.offsets[e];
         cnt = a.offsets[e + 1] - off;
-        nt = (cnt + kGBM - 1) / kGBM;
+        nt = (cnt + BM - 1) / BM;
     }
     int v = nt;
 #pragma unroll
@@ -71,8 +72,8 @@ __device__ __forceinline__ bool rows_tile(const GradGemm& a, int mt, int* grp, i
     const int incl = v + before, excl = incl - nt;
     if (e < a.G && mt >= excl && mt < incl) {
         s_res[0] = e;
-        s_res[1] = off + (mt - excl) * kGBM;
-        s_res[2] = min(kGBM, cnt - (mt - excl) * kGBM);
+        s_res[1] = off + (mt - excl) * BM;
+        s_res[2] = min(BM, cnt - (mt - excl) * BM);
     }
     __syncthreads();
     if (s_res[0] < 0) return false;
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(kGT) void grad_gemm_kernel(GradGemm a, int tiles_m,
         k1 = a.offsets ? a.offsets[grp + 1] : a.K;
         if (nr <= 0) return;
     } else {
-        if (!rows_tile(a, mt, &grp, &r0, &nr)) return;
+        if (!rows_tile<kGBM>(a, mt, &grp, &r0, &nr)) return;
         k0 = 0;
         k1 = a.K;
     }
@@ -183,6 +184,167 @@ __global__ __launch_bounds__(kGT) void grad_gemm_kernel(GradGemm a, int tiles_m,
             *c = a.accumulate ? *c + acc[i][j] : acc[i][j];
         }
     }
+}
+
+
+// The same GEMM on bf16 MFMA for bf16 operands whose contiguous dimension is
+// a multiple of 8 elements: 128 x 128 tiles, 4 waves of 64 x 64 (2 x 2 blocks
+// of v_mfma_f32_32x32x16_bf16), K in steps of 32.  Operands are loaded 16
+// bytes at a time along their contiguous dimension into registers (the next
+// K step's loads in flight during this one's MFMAs) and stored to LDS as
+// rows of K: directly when K is contiguous, element by element (a transpose)
+// when M or N is.  LDS rows are padded to 40 elements against bank conflicts.
+constexpr int kMBM = 128, kMBN = 128, kMBK = 32, kMLD = 40;
+
+template <bool KROWS, bool B_KCONT>
+__global__ __launch_bounds__(256) void grad_gemm_mfma_kernel(GradGemm a, int tiles_m, int tiles_n) {
+    __shared__ __align__(16) uint16_t As[2][kMBM * kMLD];
+    __shared__ __align__(16) uint16_t Bs[2][kMBN * kMLD];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+    const int nt = blockIdx.x % tiles_n;
+    const int mt = (blockIdx.x / tiles_n) % tiles_m;
+    const int gz = blockIdx.x / tiles_n / tiles_m;
+    int grp, r0, nr, k0, k1;
+    if (KROWS) {
+        grp = gz;
+        r0 = mt * kMBM;
+        nr = min(kMBM, a.M - r0);
+        k0 = a.offsets ? a.offsets[grp] : 0;
+        k1 = a.offsets ? a.offsets[grp + 1] : a.K;
+        if (nr <= 0) return;
+    } else {
+        if (!rows_tile<kMBM>(a, mt, &grp, &r0, &nr)) return;
+        k0 = 0;
+        k1 = a.K;
+    }
+    const int n0 = nt * kMBN;
+    const int nn = min(kMBN, a.N - n0);
+    const uint16_t* A = static_cast<const uint16_t*>(a.A);
+    const uint16_t* B = static_cast<const uint16_t*>(a.B) + (int64_t)grp * a.b_gstride;
+
+    // this thread's two 16-byte pieces of each operand per K step
+    uint4 ra0, ra1, rb0, rb1;
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+#define MOE_G_LOAD_A(ra_, i_, kb_)                                                                  \
+    do {                                                                                           \
+        if (KROWS) {        /* A(m, k) = A[k lda + m]: 8 m at one k */                             \
+            const int k_ = (kb_) + (tid >> 4) + 16 * (i_), m_ = (tid & 15) * 8;                    \
+            ra_ = zero;                                                                            \
+            if (k_ < k1 && m_ < nr) ra_ = *reinterpret_cast<const uint4*>(A + (int64_t)k_ * a.lda + r0 + m_); \
+        } else {            /* A(m, k) = A[src(m) lda + k]: 8 k at one m */                        \
+            const int m_ = (tid >> 2) + 64 * (i_), k_ = (kb_) + (tid & 3) * 8;                     \
+            ra_ = zero;                                                                            \
+            if (m_ < nr && k_ < k1) {                                                              \
+                const int r_ = r0 + m_;                                                            \
+                const int64_t src_ = a.a_gather ? a.a_gather[r_] / a.a_div : r_;                   \
+                ra_ = *reinterpret_cast<const uint4*>(A + src_ * a.lda + k_);                      \
+            }                                                                                      \
+        }                                                                                          \
+    } while (0)
+#define MOE_G_LOAD_B(rb_, i_, kb_)                                                                  \
+    do {                                                                                           \
+        if (B_KCONT) {      /* B(n, k) = B[n ldb + k] */                                           \
+            const int n_ = (tid >> 2) + 64 * (i_), k_ = (kb_) + (tid & 3) * 8;                     \
+            rb_ = zero;                                                                            \
+            if (n_ < nn && k_ < k1) rb_ = *reinterpret_cast<const uint4*>(B + (int64_t)(n0 + n_) * a.ldb + k_); \
+        } else {            /* B(n, k) = B[src(k) ldb + n]: 8 n at one k */                        \
+            const int k_ = (kb_) + (tid >> 4) + 16 * (i_), n_ = (tid & 15) * 8;                    \
+            rb_ = zero;                                                                            \
+            if (k_ < k1 && n_ < nn) {                                                              \
+                const int64_t src_ = (KROWS && a.b_gather) ? a.b_gather[k_] / a.b_div : k_;        \
+                rb_ = *reinterpret_cast<const uint4*>(B + src_ * a.ldb + n0 + n_);                 \
+            }                                                                                      \
+        }                                                                                          \
+    } while (0)
+// 8 elements of a 16-byte piece to 8 LDS rows (one column of K)
+#define MOE_G_SCATTER(dst_, row_, kk_, v_)                                                          \
+    do {                                                                                           \
+        uint16_t* d_ = (dst_) + (row_) * kMLD + (kk_);                                             \
+        d_[0 * kMLD] = (uint16_t)(v_).x; d_[1 * kMLD] = (uint16_t)((v_).x >> 16);                  \
+        d_[2 * kMLD] = (uint16_t)(v_).y; d_[3 * kMLD] = (uint16_t)((v_).y >> 16);                  \
+        d_[4 * kMLD] = (uint16_t)(v_).z; d_[5 * kMLD] = (uint16_t)((v_).z >> 16);                  \
+        d_[6 * kMLD] = (uint16_t)(v_).w; d_[7 * kMLD] = (uint16_t)((v_).w >> 16);                  \
+    } while (0)
+#define MOE_G_STORE_A(ra_, i_, buf_)                                                                \
+    do {                                                                                           \
+        if (KROWS) MOE_G_SCATTER(As[buf_], (tid & 15) * 8, (tid >> 4) + 16 * (i_), ra_);            \
+        else *reinterpret_cast<uint4*>(&As[buf_][((tid >> 2) + 64 * (i_)) * kMLD + (tid & 3) * 8]) = ra_; \
+    } while (0)
+#define MOE_G_STORE_B(rb_, i_, buf_)                                                                \
+    do {                                                                                           \
+        if (B_KCONT) *reinterpret_cast<uint4*>(&Bs[buf_][((tid >> 2) + 64 * (i_)) * kMLD + (tid & 3) * 8]) = rb_; \
+        else MOE_G_SCATTER(Bs[buf_], (tid & 15) * 8, (tid >> 4) + 16 * (i_), rb_);                  \
+    } while (0)
+#define MOE_G_LOAD(kb_)                                                                             \
+    do {                                                                                           \
+        MOE_G_LOAD_A(ra0, 0, kb_); MOE_G_LOAD_A(ra1, 1, kb_);                                     \
+        MOE_G_LOAD_B(rb0, 0, kb_); MOE_G_LOAD_B(rb1, 1, kb_);                                     \
+    } while (0)
+#define MOE_G_STORE(buf_)                                                                           \
+    do {                                                                                           \
+        MOE_G_STORE_A(ra0, 0, buf_); MOE_G_STORE_A(ra1, 1, buf_);                                 \
+        MOE_G_STORE_B(rb0, 0, buf_); MOE_G_STORE_B(rb1, 1, buf_);                                 \
+    } while (0)
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    const int half = lane >> 5, r32 = lane & 31;
+    int buf = 0;
+    MOE_G_LOAD(k0);
+    MOE_G_STORE(0);
+    __syncthreads();
+    for (int kb = k0; kb < k1; kb += kMBK) {
+        const bool more = kb + kMBK < k1;
+        if (more) MOE_G_LOAD(kb + kMBK);
+#pragma unroll
+        for (int st = 0; st < kMBK / 16; ++st) {
+            const int c = (2 * st + half) * 8;
+            bf16x8_t af[2], bfr[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                af[i] = as_bf16x8(*reinterpret_cast<const uint4*>(&As[buf][(wm * 64 + i * 32 + r32) * kMLD + c]));
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bfr[j] = as_bf16x8(*reinterpret_cast<const uint4*>(&Bs[buf][(wn * 64 + j * 32 + r32) * kMLD + c]));
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+        if (more) MOE_G_STORE(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+    }
+#undef MOE_G_LOAD_A
+#undef MOE_G_LOAD_B
+#undef MOE_G_SCATTER
+#undef MOE_G_STORE_A
+#undef MOE_G_STORE_B
+#undef MOE_G_LOAD
+#undef MOE_G_STORE
+    float* C = a.C + (KROWS ? (int64_t)grp * a.c_gstride : 0);
+    // element q of block (i, j): row 8 (q / 4) + 4 half + q % 4, column r32
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = wn * 64 + j * 32 + r32;
+            if (n >= nn) continue;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int m = wm * 64 + i * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
+                if (m >= nr) continue;
+                float* cp = C + (int64_t)(r0 + m) * a.ldc + n0 + n;
+                *cp = a.accumulate ? *cp + acc[i][j][q] : acc[i][j][q];
+            }
+        }
 }
 
 // One workgroup per grouped row r (pair p = sorted[r], or token r when there
@@ -310,10 +472,41 @@ hipError_t launch_grad_gemm_t(const GradGemm& a, bool krows, bool b_kcont, hipSt
     return hipGetLastError();
 }
 
+// bf16 operands whose contiguous dimensions and strides are multiples of 8
+// elements (16-byte pieces) go to the MFMA kernel.
+bool mfma_fits(const GradGemm& a, bool krows, bool b_kcont) {
+    auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    if (!al(a.A) || !al(a.B) || a.lda % 8 || a.ldb % 8 || a.b_gstride % 8) return false;
+    const bool a_ok = krows ? a.M % 8 == 0 : a.K % 8 == 0;
+    const bool b_ok = b_kcont ? a.K % 8 == 0 : a.N % 8 == 0;
+    return a_ok && b_ok;
+}
+
+hipError_t launch_grad_gemm_mfma(const GradGemm& a, bool krows, bool b_kcont, hipStream_t s) {
+    const int tiles_n = (a.N + kMBN - 1) / kMBN;
+    int tiles_m, groups;
+    if (krows) {
+        tiles_m = (a.M + kMBM - 1) / kMBM;
+        groups = a.offsets ? a.G : 1;
+    } else {
+        tiles_m = (int)(a.offsets ? grouped_m_tiles_upper(a.M, a.G, kMBM) : (a.M + kMBM - 1) / kMBM);
+        groups = 1;
+    }
+    const int64_t grid = (int64_t)tiles_m * tiles_n * groups;
+    if (grid == 0) return hipSuccess;
+    if (grid > INT32_MAX || (krows && b_kcont)) return hipErrorInvalidValue;
+    const dim3 g3((unsigned)grid), b3(256);
+    if (krows) hipLaunchKernelGGL((grad_gemm_mfma_kernel<true, false>), g3, b3, 0, s, a, tiles_m, tiles_n);
+    else if (b_kcont) hipLaunchKernelGGL((grad_gemm_mfma_kernel<false, true>), g3, b3, 0, s, a, tiles_m, tiles_n);
+    else hipLaunchKernelGGL((grad_gemm_mfma_kernel<false, false>), g3, b3, 0, s, a, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_grad_gemm(const GradGemm& a, bool krows, bool b_kcont, bool a_bf16, bool b_bf16, hipStream_t s) {
     if (a.G > 256) return hipErrorInvalidValue;
+    if (a_bf16 && b_bf16 && mfma_fits(a, krows, b_kcont)) return launch_grad_gemm_mfma(a, krows, b_kcont, s);
     if (a_bf16 && b_bf16) return launch_grad_gemm_t<uint16_t, uint16_t>(a, krows, b_kcont, s);
     if (!a_bf16 && b_bf16) return launch_grad_gemm_t<float, uint16_t>(a, krows, b_kcont, s);
     if (!a_bf16 && !b_bf16) return launch_grad_gemm_t<float, float>(a, krows, b_kcont, s);
