@@ -98,10 +98,16 @@ class TimingEvents:
         self.made = []
 
 
+# The sources of the gate/up GEMM kernel and of its launch (tile path, K split).
+GATE_UP_SOURCES = ("grouped_gemm.hip", "skinny.h", "device_util.h", "moe_internal.h", "moe_api.cpp")
+
+
 def kernel_source_hash() -> str:
+    """Hash of the gate/up kernel's sources: the traffic counters stay valid
+    while it is unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mixture_experts_sparse_moe_amd", "csrc")
-    for n in sorted(os.listdir(csrc)):
+    for n in GATE_UP_SOURCES:
         with open(os.path.join(csrc, n), "rb") as f:
             h.update(n.encode() + f.read())
     return h.hexdigest()[:16]

@@ -217,7 +217,9 @@ int moe_forward_staged(const moe_config* cfg, const void* x, const void* w_route
  * only (no moe_options).  The expert pre-activations are recomputed, nothing
  * is kept from the forward but its routing.  Sums run in a fixed order, no
  * atomics: the result is deterministic.  ws: at least
- * moe_backward_workspace_bytes(cfg) bytes.
+ * moe_backward_workspace_bytes(cfg) bytes; for bf16 layers whose d and d_ff
+ * are multiples of 256 that includes transposed copies of the expert weights
+ * (3 E d d_ff bf16) and of the pairs' activations.
  */
 size_t moe_backward_workspace_bytes(const moe_config* cfg);
 int moe_backward(const moe_config* cfg, const void* x, const void* w_router, const void* w_gate,

@@ -12,9 +12,16 @@
 //
 // The GEMMs of the backward are NN (dgrad: the weights are contracted over
 // their output dimension) and TN (weight gradients: a sum over each expert's
-// rows).  They run on one generic LDS-tiled kernel with fp32 FMA, any operand
-// layout, gathered rows and per-group row ranges: correct for every shape,
-// not tuned.  The recomputation of a and u uses the forward's grouped GEMM.
+// rows).  bf16 layers whose widths are multiples of 256 run them on the
+// forward's persistent MFMA kernel: the weights are transposed once per call
+// so the data gradients read them along K, and each expert's rows become a
+// range of columns (padded to 128 with zeros) of transposed activations, over
+// which the kernel's grouped-K mode sums.  Other shapes use the generic
+// grouped GEMMs here (bf16 MFMA with operands transposed on their way into
+// LDS, or fp32 FMA), which take any layout.  The recomputation of a and u
+// uses the forward's grouped GEMM.
+#include <algorithm>
+
 #include "device_util.h"
 #include "moe_internal.h"
 
@@ -360,8 +367,9 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdPairArgs b) {
     const T* U = static_cast<const T*>(b.u) + (int64_t)r * b.f;
     const float* dHp = b.dhp + (int64_t)r * b.f;
     T* H = static_cast<T*>(b.h) + (int64_t)r * b.f;
-    T* DA = static_cast<T*>(b.da) + (int64_t)r * b.f;
-    T* DU = static_cast<T*>(b.du) + (int64_t)r * b.f;
+    const int64_t ldd = b.ld_dadu ? b.ld_dadu : b.f;
+    T* DA = static_cast<T*>(b.da) + (int64_t)r * ldd;
+    T* DU = static_cast<T*>(b.du) + (int64_t)r * ldd;
     float part = 0.0f;
     for (int i = threadIdx.x; i < b.f; i += 256) {
         const float av = ld<T>(A, i), uv = ld<T>(U, i), d = dHp[i];
@@ -438,17 +446,194 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(BwdRouterArgs b) {
 }
 
 // dx[t, :] = sum over the token's pairs, in slot order, of dXp[pair_pos].
+// dx[t] = sum over the token's slots j (and K slices s, in that order) of
+// dxp[s][pair_pos[t k + j]].
 __global__ __launch_bounds__(256) void bwd_token_sum_kernel(const float* dxp, const int32_t* pair_pos, int k, int d,
-                                                            float* dx) {
+                                                            float* dx, int splitk, int64_t part_stride) {
     const int t = blockIdx.x;
     for (int c = threadIdx.x; c < d; c += 256) {
         float v = 0.0f;
         for (int j = 0; j < k; ++j) {
             const int pos = pair_pos[(int64_t)t * k + j];
-            if (pos >= 0) v += dxp[(int64_t)pos * d + c];
+            if (pos < 0) continue;
+            for (int sl = 0; sl < splitk; ++sl) v += dxp[sl * part_stride + (int64_t)pos * d + c];
         }
         dx[(int64_t)t * d + c] = v;
     }
+}
+
+// Router weight gradient dW_r[e][i] = sum_t dl[t][e] x[t][i] (E rows only, so a
+// GEMM tile would sit mostly idle): workgroup (column block, token chunk)
+// gives each thread one column and 16 experts at a time in registers, the
+// chunk's dl rows staged 32 tokens at a time in LDS.  out: the chunk's
+// partial sums [chunk][E][d] (or dW_r itself with one chunk).
+constexpr int kRwE = 16, kRwTok = 32;
+template <typename TX>
+__global__ __launch_bounds__(256) void router_wgrad_kernel(const float* dl, const TX* x, int T, int E, int d,
+                                                           int chunk_tokens, float* out) {
+    __shared__ float s_dl[kRwTok][kRwE];
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int c = blockIdx.y;
+    const int t0 = c * chunk_tokens, t1 = min(T, t0 + chunk_tokens);
+    for (int eg = 0; eg < E; eg += kRwE) {
+        float acc[kRwE];
+#pragma unroll
+        for (int j = 0; j < kRwE; ++j) acc[j] = 0.0f;
+        for (int tb = t0; tb < t1; tb += kRwTok) {
+            for (int q = threadIdx.x; q < kRwTok * kRwE; q += 256) {
+                const int tt = q / kRwE, j = q % kRwE;
+                s_dl[tt][j] = (tb + tt < t1 && eg + j < E) ? dl[(int64_t)(tb + tt) * E + eg + j] : 0.0f;
+            }
+            __syncthreads();
+            const int nt = min(kRwTok, t1 - tb);
+            if (i < d) {
+                for (int tt = 0; tt < nt; ++tt) {
+                    const float xv = ld<TX>(x, (int64_t)(tb + tt) * d + i);
+#pragma unroll
+                    for (int j = 0; j < kRwE; ++j) acc[j] = fmaf(s_dl[tt][j], xv, acc[j]);
+                }
+            }
+            __syncthreads();
+        }
+        if (i < d) {
+#pragma unroll
+            for (int j = 0; j < kRwE; ++j)
+                if (eg + j < E) out[((int64_t)c * E + eg + j) * d + i] = acc[j];
+        }
+    }
+}
+
+// dst[j] = sum over chunks c (in order) of part[c * n + j].
+__global__ __launch_bounds__(256) void sum_chunks_kernel(const float* part, int chunks, int64_t n, float* dst) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= n) return;
+    float v = 0.0f;
+    for (int c = 0; c < chunks; ++c) v += part[c * n + j];
+    dst[j] = v;
+}
+
+// ---- transposes feeding the backward's GEMMs on the forward kernel ----------------
+// That kernel reads both operands along K.  The data gradients contract the
+// weights over their output dimension and the weight gradients sum over rows,
+// so those operands are transposed first (HBM-bound copies, 64 x 64 tiles
+// through LDS, 16-byte loads and stores).
+
+constexpr int kTT = 64;   // transpose tile edge
+
+// dst[b][c][col0 + r] = src[b][r][c] for r < R, c < C (multiples of 64).
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* src, int64_t s_bstride, int64_t ld_src,
+                                                             uint16_t* dst, int64_t d_bstride, int64_t ld_dst,
+                                                             int col0) {
+    __shared__ uint16_t tile[kTT][kTT + 2];
+    const int c0 = blockIdx.x * kTT, r0 = blockIdx.y * kTT;
+    const uint16_t* S = src + blockIdx.z * s_bstride;
+    uint16_t* D = dst + blockIdx.z * d_bstride;
+    const int t = threadIdx.x, cc = (t & 7) * 8;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r = (t >> 3) + 32 * h;
+        const uint4 v = *reinterpret_cast<const uint4*>(S + (int64_t)(r0 + r) * ld_src + c0 + cc);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            tile[r][cc + 2 * i] = (uint16_t)(w4[i] & 0xFFFFu);
+            tile[r][cc + 2 * i + 1] = (uint16_t)(w4[i] >> 16);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = (t >> 3) + 32 * h;
+        uint32_t w4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w4[i] = (uint32_t)tile[cc + 2 * i][c] | ((uint32_t)tile[cc + 2 * i + 1][c] << 16);
+        *reinterpret_cast<uint4*>(D + (int64_t)(c0 + c) * ld_dst + col0 + r0 + cc) =
+            make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+}
+
+// Rows of each group as columns: for q < kofs[G] (one group: q < kpad), in the
+// group e with kofs[e] <= q < kofs[e + 1] and j = q - kofs[e]:
+//   dst[c][q] = scale(p) src[row][c] if j < n_e (grouped row r = off[e] + j,
+//   p = gather[r] or r, row = p / div or r), else 0.
+// kofs values are multiples of 128, so a 64-column tile lies in one group.
+__global__ __launch_bounds__(256) void transpose_rows_kernel(TransposeRowsArgs a) {
+    __shared__ uint16_t tile[kTT][kTT + 2];
+    const int q0 = blockIdx.x * kTT, c0 = blockIdx.y * kTT;
+    const int total = a.offsets ? a.kofs[a.G] : a.kpad;
+    if (q0 >= total) return;
+    int e = 0;
+    if (a.offsets) {
+        int lo = 0, hi = a.G;                        // kofs[lo] <= q0 < kofs[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (a.kofs[mid] <= q0) lo = mid; else hi = mid;
+        }
+        e = lo;
+    }
+    const int kbeg = a.offsets ? a.kofs[e] : 0;
+    const int roff = a.offsets ? a.offsets[e] : 0;
+    const int n = a.offsets ? a.offsets[e + 1] - roff : a.M;
+    const int t = threadIdx.x, cc = (t & 7) * 8;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int ql = (t >> 3) + 32 * h;
+        const int j = q0 + ql - kbeg;
+        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+        if (j < n) {
+            const int r = roff + j;
+            const int p = a.gather ? a.gather[r] : r;
+            const int row = a.gather ? p / a.div : r;
+            const uint4 v = *reinterpret_cast<const uint4*>(a.src + (int64_t)row * a.ld_src + c0 + cc);
+            w4[0] = v.x; w4[1] = v.y; w4[2] = v.z; w4[3] = v.w;
+            if (a.scale) {
+                const float g = a.scale[p];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    w4[i] = pack_bf16x2(g * bf16_to_f32((uint16_t)(w4[i] & 0xFFFFu)),
+                                        g * bf16_to_f32((uint16_t)(w4[i] >> 16)));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            tile[ql][cc + 2 * i] = (uint16_t)(w4[i] & 0xFFFFu);
+            tile[ql][cc + 2 * i + 1] = (uint16_t)(w4[i] >> 16);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = (t >> 3) + 32 * h;
+        uint32_t w4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w4[i] = (uint32_t)tile[cc + 2 * i][c] | ((uint32_t)tile[cc + 2 * i + 1][c] << 16);
+        *reinterpret_cast<uint4*>(a.dst + (int64_t)(c0 + c) * a.ld_dst + q0 + cc) =
+            make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+}
+
+// kofs[e] = sum over e' < e of n_e' rounded up to 128 (an expert with no rows
+// takes 128 zero columns, so its weight gradients come out zero).  One block.
+__global__ __launch_bounds__(256) void kgroup_offsets_kernel(const int32_t* offsets, int G, int32_t* kofs) {
+    __shared__ int s_w[4];
+    const int e = threadIdx.x, lane = e & 63, w = e >> 6;
+    int v = 0;
+    if (e < G) {
+        const int n = offsets[e + 1] - offsets[e];
+        v = n > 0 ? (n + 127) / 128 * 128 : 128;
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o, 64);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) s_w[w] = v;
+    __syncthreads();
+    for (int q = 0; q < w; ++q) v += s_w[q];
+    if (e < G) kofs[e + 1] = v;
+    if (e == 0) kofs[0] = 0;
 }
 
 template <typename TA, typename TB>
@@ -527,9 +712,68 @@ hipError_t launch_bwd_router(const BwdRouterArgs& b, hipStream_t s) {
 }
 
 hipError_t launch_bwd_token_sum(const float* dxp, const int32_t* pair_pos, int T, int k, int d, float* dx,
-                                hipStream_t s) {
+                                hipStream_t s, int splitk, int64_t part_stride) {
     if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_token_sum_kernel, dim3(T), dim3(256), 0, s, dxp, pair_pos, k, d, dx);
+    hipLaunchKernelGGL(bwd_token_sum_kernel, dim3(T), dim3(256), 0, s, dxp, pair_pos, k, d, dx, splitk, part_stride);
+    return hipGetLastError();
+}
+
+int router_wgrad_chunks(int T, int d, int E) {
+    const int col_blocks = (d + 255) / 256;
+    const int want = (1024 + col_blocks - 1) / col_blocks;       // about 1024 workgroups
+    const int most = std::max(1, (T + 31) / 32);                 // at least 32 tokens a chunk
+    const int64_t cap = std::max<int64_t>(1, (int64_t(64) << 20) / ((int64_t)E * d * 4));   // partials <= 64 MB
+    return (int)std::max<int64_t>(1, std::min<int64_t>(std::min(want, most), cap));
+}
+
+hipError_t launch_router_wgrad(const float* dl, const void* x, bool x_bf16, int T, int E, int d, float* part,
+                               float* dwr, hipStream_t s) {
+    if (E <= 0 || d <= 0) return hipSuccess;
+    const int chunks = router_wgrad_chunks(T, d, E);
+    const int per = chunks > 1 ? ((T + chunks - 1) / chunks + kRwTok - 1) / kRwTok * kRwTok : std::max(T, 1);
+    const int used = std::max(1, (T + per - 1) / per);            // chunks that hold tokens
+    float* out = used > 1 ? part : dwr;
+    const dim3 grid((d + 255) / 256, used);
+    if (x_bf16)
+        hipLaunchKernelGGL(router_wgrad_kernel<uint16_t>, grid, dim3(256), 0, s, dl,
+                           static_cast<const uint16_t*>(x), T, E, d, per, out);
+    else
+        hipLaunchKernelGGL(router_wgrad_kernel<float>, grid, dim3(256), 0, s, dl, static_cast<const float*>(x), T, E,
+                           d, per, out);
+    if (used > 1) {
+        const int64_t n = (int64_t)E * d;
+        hipLaunchKernelGGL(sum_chunks_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, used, n, dwr);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const void* src, int64_t s_bstride, int64_t ld_src, int R, int C, int batch,
+                                 void* dst, int64_t d_bstride, int64_t ld_dst, int col0, hipStream_t s) {
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    if (R % kTT || C % kTT || ld_src % 8 || ld_dst % 8 || col0 % 8 || s_bstride % 8 || d_bstride % 8 ||
+        !al16(src) || !al16(dst) || ld_src < C || ld_dst < col0 + R)
+        return hipErrorInvalidValue;
+    if (R == 0 || C == 0 || batch == 0) return hipSuccess;
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3(C / kTT, R / kTT, batch), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(src), s_bstride, ld_src, static_cast<uint16_t*>(dst), d_bstride,
+                       ld_dst, col0);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_rows(const TransposeRowsArgs& a, int64_t cols_upper, hipStream_t s) {
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    if (a.C % kTT || a.ld_src % 8 || a.ld_dst % 8 || !al16(a.src) || !al16(a.dst) || cols_upper % 128 ||
+        cols_upper > a.ld_dst || (a.offsets && (!a.kofs || a.G < 1 || a.G > 256)) ||
+        (!a.offsets && (a.kpad % 128 || a.kpad < a.M || a.kpad > cols_upper)))
+        return hipErrorInvalidValue;
+    if (a.C == 0 || cols_upper == 0) return hipSuccess;
+    hipLaunchKernelGGL(transpose_rows_kernel, dim3((unsigned)(cols_upper / kTT), a.C / kTT), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_kgroup_offsets(const int32_t* offsets, int G, int32_t* kofs, hipStream_t s) {
+    if (G < 1 || G > 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kgroup_offsets_kernel, dim3(1), dim3(256), 0, s, offsets, G, kofs);
     return hipGetLastError();
 }
 

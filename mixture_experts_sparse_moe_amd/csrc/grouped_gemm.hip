@@ -299,21 +299,28 @@ __device__ __forceinline__ int tile_prefix(const GemmGroup& g, int* s_tb, int* s
 
 struct TileRef {
     int grp, row0, nrows, n0, ks;
+    int kbeg, kt;   // grouped K: first K column and K stages of the tile
 };
 
-// Logical tile L -> (group, rows, first column).  Bands of kWMW M tiles; in a
-// band, windows of wn_win N tiles; inside a window, M-tile-fastest order.
-template <int BM, int BN>
-__device__ __forceinline__ TileRef tile_at(const int* s_tb, const int* s_off, int G, int mt_total,
-                                           int tiles_n, int wn_win, int L) {
+// Logical tile L -> (M tile, N tile).  Bands of kWMW M tiles; in a band,
+// windows of wn_win N tiles; inside a window, M-tile-fastest order.
+__device__ __forceinline__ void band_window(int mt_total, int tiles_n, int wn_win, int L, int& mt, int& ntile) {
     const int band = L / (kWMW * tiles_n);
     const int mb0 = band * kWMW;
     const int mh = min(kWMW, mt_total - mb0);
     const int rem = L - band * kWMW * tiles_n;
     const int nwin = rem / (mh * wn_win);
     const int r2 = rem - nwin * mh * wn_win;
-    const int mt = mb0 + r2 % mh;
-    const int ntile = nwin * wn_win + r2 / mh;
+    mt = mb0 + r2 % mh;
+    ntile = nwin * wn_win + r2 / mh;
+}
+
+// Logical tile L -> (group, rows, first column), in band_window order.
+template <int BM, int BN>
+__device__ __forceinline__ TileRef tile_at(const int* s_tb, const int* s_off, int G, int mt_total,
+                                           int tiles_n, int wn_win, int L) {
+    int mt, ntile;
+    band_window(mt_total, tiles_n, wn_win, L, mt, ntile);
     int lo = 0, hi = G;                              // s_tb[lo] <= mt < s_tb[hi]
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -388,6 +395,33 @@ __device__ __forceinline__ TileRef split_tile_at(const int* s_tb, const int* s_o
     return t;
 }
 
+// Grouped K: group g owns M tiles [g mtiles, (g + 1) mtiles) of the
+// band_window order, all N tiles, and K columns [s_off[g], s_off[g + 1]).
+template <int BM, int BN>
+__device__ __forceinline__ TileRef kgroup_tile_at(const int* s_off, int mtiles, int mt_total, int tiles_n,
+                                                  int wn_win, int L) {
+    int mt, ntile;
+    band_window(mt_total, tiles_n, wn_win, L, mt, ntile);
+    TileRef t;
+    t.grp = __builtin_amdgcn_readfirstlane(mt / mtiles);
+    t.row0 = __builtin_amdgcn_readfirstlane((mt - t.grp * mtiles) * BM);
+    t.nrows = BM;
+    t.n0 = __builtin_amdgcn_readfirstlane(ntile * BN);
+    t.ks = 0;
+    t.kbeg = __builtin_amdgcn_readfirstlane(s_off[t.grp]);
+    t.kt = __builtin_amdgcn_readfirstlane((s_off[t.grp + 1] - t.kbeg) / kBK);
+    return t;
+}
+
+// Grouped K: s_off[g] = first K column of group g, g <= G.  Returns G.
+__device__ __forceinline__ int kgroup_prefix(const GemmGroup& g, int* s_off) {
+    const int G = g.kofs ? g.G : 1;
+    const int tid = threadIdx.x;
+    if (tid <= G) s_off[tid] = g.kofs ? g.kofs[tid] : (tid ? g.K : 0);
+    __syncthreads();
+    return G;
+}
+
 // DMA sources of one tile for one wave: wave-uniform bases and 32-bit per-lane
 // byte offsets.  Instruction j (0..3) of wave w fills LDS rows 32 w + 8 j +
 // lane / 8 at physical 16-byte chunk lane % 8, which holds logical chunk
@@ -399,6 +433,7 @@ struct DmaSrc {
     const char* b;
     uint32_t ao[J], bo[J];
     int rot;        // first K stage of the walk (stage s reads stage (s + rot) mod stages)
+    int kt;         // grouped K: stages of the tile
 };
 
 // NW waves; wave w stages rows (256 / NW) w .. (256 / NW)(w + 1) - 1 of the A
@@ -423,10 +458,28 @@ __device__ __forceinline__ void gather_rows(const GemmGroup& g, const TileRef& t
     }
 }
 
-template <bool DUAL, int NW>
+template <bool DUAL, int NW, bool KG = false>
 __device__ __forceinline__ DmaSrc<32 / NW> dma_src(const GemmGroup& g, const TileRef& t, const int* src,
                                                   int w, int lane, int k_split) {
     constexpr int J = 32 / NW;
+    if constexpr (KG) {
+        // A rows t.row0 .., B rows t.n0 .., both from K column t.kbeg, strides lda / ldb
+        static_assert(!DUAL, "grouped K is a single GEMM");
+        const uint32_t A2 = (uint32_t)g.lda * 2, B2 = (uint32_t)g.ldb * 2;
+        DmaSrc<J> s;
+        s.kt = t.kt;
+        s.rot = __builtin_amdgcn_readfirstlane((t.n0 / 256 + 17 * t.grp) % t.kt);
+        s.a = static_cast<const char*>(g.A) + ((int64_t)t.row0 * g.lda + t.kbeg) * 2;
+        s.b = static_cast<const char*>(g.B0) + ((int64_t)t.n0 * g.ldb + t.kbeg) * 2;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int r = w * (256 / NW) + j * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ swz(r);
+            s.ao[j] = (uint32_t)src[j] * A2 + c * 16;
+            s.bo[j] = (uint32_t)r * B2 + c * 16;
+        }
+        return s;
+    }
     const uint32_t K2 = (uint32_t)g.K * 2;
     const int64_t k0 = (int64_t)t.ks * k_split * 2;    // first byte of the tile's K range
     DmaSrc<J> s;
@@ -481,6 +534,26 @@ __device__ __forceinline__ void store_block_bf16(uint16_t* Cb, int64_t ldc, int 
     }
 }
 
+// Stores (or adds to) one 32 x 32 block of MFMA results as fp32: lane (half,
+// r32) holds column r32 of block rows 8 a + 4 half + b in v[4 a + b]; each
+// store instruction writes two 128-byte row pieces.  Rows at or past
+// rows_left are not written.
+__device__ __forceinline__ void store_block_f32(float* Cf, int64_t ldc, int rows_left, const f32x16_t& v,
+                                                int lane, bool accumulate) {
+    const int half = lane >> 5, r32 = lane & 31;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int row = 8 * (q >> 2) + 4 * half + (q & 3);
+        if (row < rows_left) {
+            float* p = Cf + row * ldc + r32;
+            *p = accumulate ? *p + v[q] : v[q];
+        }
+    }
+}
+
+// Kernel modes: forward (bf16 C), fp32 C over grouped rows, fp32 C over grouped K.
+constexpr int kModeFwd = 0, kModeF32 = 1, kModeKgroup = 2;
+
 // Main bf16 kernel, persistent: one workgroup of 8 waves per CU walks a list
 // of 256 x 256 tiles of MFMA work.
 //   single: C tile 256 rows x 256 cols of one weight matrix;
@@ -507,10 +580,16 @@ __device__ __forceinline__ void store_block_bf16(uint16_t* Cb, int64_t ldc, int 
 // stages runs on across tiles: the last two stages of a tile fetch the first
 // two of the workgroup's next tile, whose loads are in flight during the
 // epilogue.
-template <bool DUAL, bool ALIGNED>
+// MODE kModeF32 (single): the same tiles, C stored as fp32 (or added to C).
+// MODE kModeKgroup (single): every group has all M x N tiles and walks its own
+// K columns (the weight gradients of the backward: sums over each expert's
+// rows, with both operands transposed so that K is contiguous).
+template <bool DUAL, bool ALIGNED, int MODE = kModeFwd>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup g, int tiles_n) {
     constexpr int BM = 256;
     constexpr int BN = DUAL ? 128 : 256;
+    constexpr bool KG = MODE == kModeKgroup;
+    static_assert(MODE == kModeFwd || !DUAL, "fp32 products are single GEMMs");
     constexpr int STG = 256 * kBK;    // elements of one A or B stage (32 KB)
     __shared__ __align__(16) uint16_t sA0[STG], sA1[STG];
     __shared__ __align__(16) uint16_t sB0[STG], sB1[STG];
@@ -520,11 +599,17 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w >> 2, wn = w & 3;
-    const int S = DUAL ? 1 : g.splitk;  // K ranges (single GEMM only)
-    const int KT = g.K / kBK / S;       // stages per tile: even, >= 2
+    const int S = DUAL || KG ? 1 : g.splitk;  // K ranges (single GEMM only)
+    const int KT = g.K / kBK / S;       // stages per tile: even, >= 2 (grouped K: per tile)
 
-    const int G = tile_prefix<BM>(g, s_tb, s_off, s_wsum);
-    const int mt_total = s_tb[G];
+    int G, mt_total;
+    if constexpr (KG) {
+        G = kgroup_prefix(g, s_off);
+        mt_total = G * (g.M / BM);
+    } else {
+        G = tile_prefix<BM>(g, s_tb, s_off, s_wsum);
+        mt_total = s_tb[G];
+    }
     const int TL = mt_total * tiles_n * S;
     const int nslot = gridDim.x >> 3;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -549,7 +634,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 #define MOE_DMA(sA_, sB_, src_, kt_)                                                            \
     do {                                                                                        \
         const int kr_ = (kt_) + (src_).rot;                                                     \
-        const int kp_ = kr_ >= KT ? kr_ - KT : kr_;                                             \
+        const int kw_ = KG ? (src_).kt : KT;                                                    \
+        const int kp_ = kr_ >= kw_ ? kr_ - kw_ : kr_;                                           \
         const char* ab_ = (src_).a + kp_ * (kBK * 2);                                           \
         const char* bb_ = (src_).b + kp_ * (kBK * 2);                                           \
         _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                         \
@@ -622,19 +708,25 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 // The K stages of one tile for a wave with NA_ live row blocks.
 #define MOE_KLOOP(NA_)                                                                          \
     do {                                                                                        \
-        for (int kt = 0; kt < KT - 2; kt += 2) {                                                \
+        const int kl_ = KG ? cur.kt : KT;                                                       \
+        for (int kt = 0; kt < kl_ - 2; kt += 2) {                                               \
             MOE_STAGE(NA_, NA_, sA0, sB0, sA1, sB1, cur, kt + 2, true);                         \
             MOE_STAGE(NA_, NA_, sA1, sB1, sA0, sB0, cur, kt + 3, true);                         \
         }                                                                                       \
-        nxt = dma_src<DUAL, 8>(g, tn, gsrc, w, lane, KT * kBK);                                  \
+        nxt = dma_src<DUAL, 8, KG>(g, tn, gsrc, w, lane, KT * kBK);                              \
         MOE_STAGE(NA_, NA_, sA0, sB0, sA1, sB1, nxt, 0, more);                                  \
         MOE_STAGE(NA_, 4, sA1, sB1, sA0, sB0, nxt, 1, more);                                    \
     } while (0)
 
-    TileRef tr = split_tile_at<BM, BN, ALIGNED>(s_tb, s_off, G, mt_total, tiles_n, wn_win, L);
+    const int mtiles = KG ? g.M / BM : 0;
+    auto tile_of = [&](int Lt) {
+        if constexpr (KG) return kgroup_tile_at<BM, BN>(s_off, mtiles, mt_total, tiles_n, wn_win, Lt);
+        else return split_tile_at<BM, BN, ALIGNED>(s_tb, s_off, G, mt_total, tiles_n, wn_win, Lt);
+    };
+    TileRef tr = tile_of(L);
     int gsrc[4];
     gather_rows<8>(g, tr, w, lane, gsrc);
-    DmaSrc<4> cur = dma_src<DUAL, 8>(g, tr, gsrc, w, lane, KT * kBK);
+    DmaSrc<4> cur = dma_src<DUAL, 8, KG>(g, tr, gsrc, w, lane, KT * kBK);
     bf16x8_t fa0[4], fb0[2], fa1[4], fb1[2];
     // prologue: the first tile's stages 0 and 1
     MOE_DMA(sA0, sB0, cur, 0);
@@ -648,7 +740,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     for (;;) {
         const int Ln = L + nslot;
         const bool more = Ln < Lend;
-        const TileRef tn = split_tile_at<BM, BN, ALIGNED>(s_tb, s_off, G, mt_total, tiles_n, wn_win, more ? Ln : L);
+        const TileRef tn = tile_of(more ? Ln : L);
         // the next tile's gathered rows load now; their values are used after
         // the K loop, whose stage waits have long covered them
         gather_rows<8>(g, tn, w, lane, gsrc);
@@ -675,13 +767,20 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
             if (rb >= tr.nrows) break;
 #pragma unroll
             for (int bo = 0; bo < (DUAL ? 1 : 2); ++bo) {
-                float v[16];
-#pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    v[q] = DUAL ? silu_f32(acc[i][0][q]) * acc[i][1][q] : acc[i][bo][q];
                 const int cb = DUAL ? wn * 32 : wn * 64 + bo * 32;
-                store_block_bf16(C + tr.ks * g.part_stride + (int64_t)(tr.row0 + rb) * g.N + tr.n0 + cb, g.N,
-                                 tr.nrows - rb, v, lane);
+                if constexpr (MODE == kModeFwd) {
+                    float v[16];
+#pragma unroll
+                    for (int q = 0; q < 16; ++q)
+                        v[q] = DUAL ? silu_f32(acc[i][0][q]) * acc[i][1][q] : acc[i][bo][q];
+                    store_block_bf16(C + tr.ks * g.part_stride + (int64_t)(tr.row0 + rb) * g.N + tr.n0 + cb, g.N,
+                                     tr.nrows - rb, v, lane);
+                } else {
+                    float* Cf = static_cast<float*>(g.C) +
+                                (KG ? (int64_t)tr.grp * g.c_gstride : (int64_t)tr.ks * g.part_stride) +
+                                (int64_t)(tr.row0 + rb) * g.ldc + tr.n0 + cb;
+                    store_block_f32(Cf, g.ldc, tr.nrows - rb, acc[i][bo], lane, g.accumulate);
+                }
             }
         }
         if (!more) break;
@@ -928,6 +1027,35 @@ hipError_t launch_bf16_persistent(const GemmGroup& g, hipStream_t s) {
     return hipGetLastError();
 }
 
+// fp32 products on the persistent kernel (the backward's GEMMs).
+hipError_t launch_bf16_f32out(const GemmGroup& g, hipStream_t s) {
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    if (!al16(g.A) || !al16(g.B0) || g.ldc < g.N || g.N % 256 || g.N <= 0) return hipErrorInvalidValue;
+    const dim3 grid(persistent_grid()), block(512);
+    if (g.kgrouped) {
+        const int G = g.kofs ? g.G : 1;
+        // 32-bit DMA offsets: 256 rows of A or B from the tile's first row
+        const bool ok = g.M > 0 && g.M % 256 == 0 && G >= 1 && G <= 256 && g.splitk == 1 && !g.accumulate &&
+                        !g.gather && g.lda % 8 == 0 && g.ldb % 8 == 0 && (int64_t)256 * g.lda * 2 < (int64_t(1) << 32) &&
+                        (int64_t)256 * g.ldb * 2 < (int64_t(1) << 32) && (g.kofs || (g.K % 128 == 0 && g.K >= 128));
+        if (!ok) return hipErrorInvalidValue;
+        hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<false, false, kModeKgroup>), grid, block, 0, s,
+                              g.t_start, g.t_stop, 0, g, g.N / 256);
+        return hipGetLastError();
+    }
+    const int64_t a_rows = g.gather ? ((int64_t)g.M + g.gather_div - 1) / g.gather_div : 0;
+    if (g.splitk < 1 || g.K % (128 * g.splitk) || (g.accumulate && g.splitk != 1) ||
+        a_rows * g.K * 2 >= (int64_t(1) << 32))
+        return hipErrorInvalidValue;
+    if (g.aligned_bands)
+        hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<false, true, kModeF32>), grid, block, 0, s, g.t_start,
+                              g.t_stop, 0, g, g.N / 256);
+    else
+        hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<false, false, kModeF32>), grid, block, 0, s, g.t_start,
+                              g.t_stop, 0, g, g.N / 256);
+    return hipGetLastError();
+}
+
 constexpr int kSkNblk = 4, kSkNst = 4;
 
 template <bool DUAL>
@@ -1004,6 +1132,10 @@ int choose_splitk_skinny(int64_t mt_expected, int N, int K) {
 
 hipError_t launch_grouped_gemm(const GemmGroup& g, bool dual, bool bf16, hipStream_t s) {
     if (g.M == 0) return hipSuccess;
+    if (g.f32_out || g.kgrouped) {
+        if (dual || !bf16 || g.skinny) return hipErrorInvalidValue;
+        return launch_bf16_f32out(g, s);
+    }
     if (g.skinny) {
         if (!bf16 || !skinny_fits(g.N, g.K, dual, g.splitk)) return hipErrorInvalidValue;
         return dual ? launch_bf16_skinny<true>(g, s) : launch_bf16_skinny<false>(g, s);

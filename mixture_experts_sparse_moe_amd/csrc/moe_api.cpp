@@ -321,14 +321,53 @@ int forward_impl(const moe_config* cfg, const moe_options* opts, const void* x, 
 
 
 // Backward workspace, 256-byte aligned regions.
+// The backward's bf16 GEMMs run on the forward's persistent kernel when the
+// widths are multiples of its 256-wide tiles (fast); otherwise, and for fp32
+// layers, on the generic grouped GEMM.
+struct BwdPlan {
+    bool fast = false;          // routed experts on the persistent kernel
+    bool shared_fast = false;   // shared expert likewise
+    int64_t Q = 0;              // columns of the transposed pair operands (rows padded per expert)
+    int64_t Tq = 0;             // columns of the transposed token operands
+    int xsplit = 1;             // K split of dx per pair (dXp slices)
+};
+
+BwdPlan bwd_plan(const moe_config* c) {
+    BwdPlan p;
+    if (c->dtype != MOE_BF16) return p;
+    const int64_t T = c->num_tokens, P = T * c->top_k, E = c->num_experts;
+    const int64_t d = c->d_model, f = c->d_ff;
+    auto round128 = [](int64_t v) { return (v + 127) / 128 * 128; };
+    p.Q = round128(P + 128 * E);
+    p.Tq = std::max<int64_t>(128, round128(T));
+    const int64_t lim = int64_t(1) << 32;
+    // 32-bit DMA offsets: gathered rows of dy from its start; 256 rows of a transposed operand
+    p.fast = d % 256 == 0 && f % 256 == 0 && T * d * 2 < lim && 256 * p.Q * 2 < lim;
+    if (p.fast) {
+        const int64_t mt_upper = grouped_m_tiles_upper(P, (int)E, 256);
+        const int64_t mt_exp = std::min<int64_t>(mt_upper, (P + 255) / 256 + std::min<int64_t>(E, P) / 2);
+        p.xsplit = choose_splitk(mt_exp, (int)d, (int)(2 * f));
+    }
+    if (c->num_shared) {
+        const int64_t fs = c->d_ff_shared;
+        p.shared_fast = d % 256 == 0 && fs % 256 == 0 && 256 * p.Tq * 2 < lim;
+    }
+    return p;
+}
+
 struct BwdLayout {
-    size_t counts, offsets, sorted, pos, chunk, A, U, H, DA, DU, dHp, dO, dXp, dgate, logits, dl;
-    size_t As, Us, Hs, DAs, DUs, dHs, total;
+    size_t counts, offsets, sorted, pos, chunk, A, U, H, DA, DU, dHp, dO, dXp, dgate, logits, dl, rw;
+    size_t As, Us, Hs, DAs, DUs, dHs;
+    // fast path: DA and DU share rows [da | du] (DA), transposed operands
+    size_t kofs, WdT, WguT, dOT, HT, DADUT, XgT, WsdT, WsguT, dyT, HsT, DADUsT, xT;
+    size_t total;
 };
 
 BwdLayout bwd_layout(const moe_config* c) {
+    const BwdPlan pl = bwd_plan(c);
     const size_t T = (size_t)c->num_tokens, P = T * c->top_k, E = c->num_experts;
     const size_t d = c->d_model, f = c->d_ff, fs = c->num_shared ? c->d_ff_shared : 0, w = elem(c);
+    const size_t Q = (size_t)pl.Q, Tq = (size_t)pl.Tq;
     BwdLayout L{};
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
@@ -340,20 +379,43 @@ BwdLayout bwd_layout(const moe_config* c) {
     L.A = take(P * f * w);
     L.U = take(P * f * w);
     L.H = take(P * f * w);
-    L.DA = take(P * f * w);
-    L.DU = take(P * f * w);
     L.dHp = take(P * f * 4);
-    L.dO = take(P * d * w);
-    L.dXp = take(P * d * 4);
     L.dgate = take(P * 4);
     L.logits = take(T * E * 4);
     L.dl = take(T * E * 4);
+    L.rw = take((size_t)router_wgrad_chunks((int)T, (int)d, (int)E) * E * d * 4);
+    if (pl.fast) {
+        L.DA = take(P * 2 * f * w);
+        L.dXp = take((size_t)pl.xsplit * P * d * 4);
+        L.kofs = take((E + 1) * 4);
+        L.WdT = take(E * f * d * w);
+        L.WguT = take(E * d * 2 * f * w);
+        L.dOT = take(d * Q * w);
+        L.HT = take(f * Q * w);
+        L.DADUT = take(2 * f * Q * w);
+        L.XgT = take(d * Q * w);
+    } else {
+        L.DA = take(P * f * w);
+        L.DU = take(P * f * w);
+        L.dO = take(P * d * w);
+        L.dXp = take(P * d * 4);
+    }
     L.As = take(T * fs * w);
     L.Us = take(T * fs * w);
     L.Hs = take(T * fs * w);
-    L.DAs = take(T * fs * w);
-    L.DUs = take(T * fs * w);
     L.dHs = take(T * fs * 4);
+    if (pl.shared_fast) {
+        L.DAs = take(T * 2 * fs * w);
+        L.WsdT = take(fs * d * w);
+        L.WsguT = take(d * 2 * fs * w);
+        L.dyT = take(d * Tq * w);
+        L.HsT = take(fs * Tq * w);
+        L.DADUsT = take(2 * fs * Tq * w);
+        L.xT = take(d * Tq * w);
+    } else {
+        L.DAs = take(T * fs * w);
+        L.DUs = take(T * fs * w);
+    }
     L.total = o;
     return L;
 }
@@ -368,20 +430,49 @@ GradGemm grad_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, float
     return g;
 }
 
+// fp32 product on the persistent kernel: C [rows, ldc] = A B0^T over grouped rows.
+GemmGroup f32_gemm(const void* A, const int32_t* gather, int div, const int32_t* offsets, int G, int M,
+                   const void* B0, float* C, int64_t ldc, int N, int K) {
+    GemmGroup g{A, gather, div, offsets, G, M, B0, nullptr, C, N, K};
+    g.f32_out = true;
+    g.ldc = ldc;
+    return g;
+}
+
+// Weight gradients on the persistent kernel: C[g] (M x N) = sum over group g's
+// columns of A (M rows, stride lda) times B (N rows, stride ldb).
+GemmGroup kgroup_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, const int32_t* kofs, int G, int M,
+                      int N, int K, float* C, int64_t ldc, int64_t c_gstride) {
+    GemmGroup g{A, nullptr, 1, nullptr, G, M, B, nullptr, C, N, K};
+    g.kgrouped = true;
+    g.kofs = kofs;
+    g.lda = lda; g.ldb = ldb; g.ldc = ldc; g.c_gstride = c_gstride;
+    return g;
+}
+
+TransposeRowsArgs rows_t(const void* src, int64_t ld_src, int C, const int32_t* gather, int div, const float* scale,
+                         const int32_t* offsets, const int32_t* kofs, int G, int M, int kpad, void* dst,
+                         int64_t ld_dst) {
+    return TransposeRowsArgs{static_cast<const uint16_t*>(src), ld_src, C, gather, div, scale, offsets, kofs,
+                             G, M, kpad, static_cast<uint16_t*>(dst), ld_dst};
+}
+
 int run_backward(const moe_config* c, const void* x, const void* wr, const void* wg, const void* wu,
                  const void* wd, const void* sg, const void* su, const void* sd, const void* dy,
                  const int32_t* ids, const float* gates, float* dx, float* dwr, float* dwg, float* dwu,
                  float* dwd, float* dsg, float* dsu, float* dsd, void* ws, hipStream_t s) {
+    const BwdPlan pl = bwd_plan(c);
     const BwdLayout L = bwd_layout(c);
     const bool bf16 = c->dtype == MOE_BF16;
     const int T = c->num_tokens, k = c->top_k, E = c->num_experts, P = T * k;
     const int d = c->d_model, f = c->d_ff;
+    const size_t w = elem(c);
     int32_t* counts = at<int32_t>(ws, L.counts);
     int32_t* offsets = at<int32_t>(ws, L.offsets);
     int32_t* sorted = at<int32_t>(ws, L.sorted);
     int32_t* pos = at<int32_t>(ws, L.pos);
     void *A = at<void>(ws, L.A), *U = at<void>(ws, L.U), *H = at<void>(ws, L.H);
-    void *DA = at<void>(ws, L.DA), *DU = at<void>(ws, L.DU), *dO = at<void>(ws, L.dO);
+    void* DA = at<void>(ws, L.DA);
     float *dHp = at<float>(ws, L.dHp), *dXp = at<float>(ws, L.dXp), *dgate = at<float>(ws, L.dgate);
     float *logits = at<float>(ws, L.logits), *dl = at<float>(ws, L.dl);
 
@@ -392,29 +483,70 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
     MOE_HIP(launch_grouped_gemm(ga, false, bf16, s));
     GemmGroup gu{x, sorted, k, offsets, E, P, wu, nullptr, U, f, d};
     MOE_HIP(launch_grouped_gemm(gu, false, bf16, s));
-    // dH' = dy W_down (rows gathered by pair)
-    GradGemm g1 = grad_gemm(dy, d, wd, f, dHp, f, P, f, d);
-    g1.a_gather = sorted; g1.a_div = k; g1.b_gstride = (int64_t)d * f; g1.offsets = offsets; g1.G = E;
-    MOE_HIP(launch_grad_gemm(g1, false, false, bf16, bf16, s));
-    // h, dg, da, du, dO per pair
-    BwdPairArgs pa{sorted, offsets, E, k, gates, A, U, dHp, H, DA, DU, dgate, dy, dO, f, d};
-    MOE_HIP(launch_bwd_pair(pa, P, bf16, s));
-    // dx of each pair = da W_gate + du W_up, then summed per token in slot order
-    GradGemm g2 = grad_gemm(DA, f, wg, d, dXp, d, P, d, f);
-    g2.b_gstride = (int64_t)f * d; g2.offsets = offsets; g2.G = E;
-    MOE_HIP(launch_grad_gemm(g2, false, false, bf16, bf16, s));
-    g2.A = DU; g2.B = wu; g2.accumulate = true;
-    MOE_HIP(launch_grad_gemm(g2, false, false, bf16, bf16, s));
-    MOE_HIP(launch_bwd_token_sum(dXp, pos, T, k, d, dx, s));
-    // weight gradients: sums over each expert's rows
-    GradGemm w1 = grad_gemm(dO, d, H, f, dwd, f, d, f, P);
-    w1.c_gstride = (int64_t)d * f; w1.offsets = offsets; w1.G = E;
-    MOE_HIP(launch_grad_gemm(w1, true, false, bf16, bf16, s));
-    GradGemm w2 = grad_gemm(DA, f, x, d, dwg, d, f, d, P);
-    w2.b_gather = sorted; w2.b_div = k; w2.c_gstride = (int64_t)f * d; w2.offsets = offsets; w2.G = E;
-    MOE_HIP(launch_grad_gemm(w2, true, false, bf16, bf16, s));
-    w2.A = DU; w2.C = dwu;
-    MOE_HIP(launch_grad_gemm(w2, true, false, bf16, bf16, s));
+    if (pl.fast) {
+        const int64_t Q = pl.Q;
+        int32_t* kofs = at<int32_t>(ws, L.kofs);
+        void *WdT = at<void>(ws, L.WdT), *WguT = at<void>(ws, L.WguT);
+        void *dOT = at<void>(ws, L.dOT), *HT = at<void>(ws, L.HT), *DADUT = at<void>(ws, L.DADUT);
+        void* XgT = at<void>(ws, L.XgT);
+        // dH' = dy W_down: W_down^T [E, f, d] makes the contraction K-contiguous
+        MOE_HIP(launch_transpose_bf16(wd, (int64_t)d * f, f, d, f, E, WdT, (int64_t)f * d, d, 0, s));
+        GemmGroup g1 = f32_gemm(dy, sorted, k, offsets, E, P, WdT, dHp, f, f, d);
+        MOE_HIP(launch_grouped_gemm(g1, false, true, s));
+        // h, dg, [da | du] per pair
+        BwdPairArgs pa{sorted, offsets, E, k, gates, A, U, dHp, H, DA, static_cast<char*>(DA) + f * w, dgate,
+                       dy, nullptr, f, d};
+        pa.ld_dadu = 2 * (int64_t)f;
+        MOE_HIP(launch_bwd_pair(pa, P, true, s));
+        // dx of each pair = [da | du] [W_gate^T | W_up^T]^T (one K walk of 2 f)
+        MOE_HIP(launch_transpose_bf16(wg, (int64_t)f * d, d, f, d, E, WguT, (int64_t)d * 2 * f, 2 * f, 0, s));
+        MOE_HIP(launch_transpose_bf16(wu, (int64_t)f * d, d, f, d, E, WguT, (int64_t)d * 2 * f, 2 * f, f, s));
+        GemmGroup g2 = f32_gemm(DA, nullptr, 1, offsets, E, P, WguT, dXp, d, d, 2 * f);
+        g2.splitk = pl.xsplit;
+        g2.part_stride = (int64_t)P * d;
+        g2.aligned_bands = true;
+        MOE_HIP(launch_grouped_gemm(g2, false, true, s));
+        MOE_HIP(launch_bwd_token_sum(dXp, pos, T, k, d, dx, s, pl.xsplit, (int64_t)P * d));
+        // weight gradients: each expert's rows as a K range of transposed operands
+        MOE_HIP(launch_kgroup_offsets(offsets, E, kofs, s));
+        MOE_HIP(launch_transpose_rows(rows_t(dy, d, d, sorted, k, gates, offsets, kofs, E, P, 0, dOT, Q), Q, s));
+        MOE_HIP(launch_transpose_rows(rows_t(H, f, f, nullptr, 1, nullptr, offsets, kofs, E, P, 0, HT, Q), Q, s));
+        MOE_HIP(launch_transpose_rows(
+            rows_t(DA, 2 * (int64_t)f, 2 * f, nullptr, 1, nullptr, offsets, kofs, E, P, 0, DADUT, Q), Q, s));
+        MOE_HIP(launch_transpose_rows(rows_t(x, d, d, sorted, k, nullptr, offsets, kofs, E, P, 0, XgT, Q), Q, s));
+        GemmGroup w1 = kgroup_gemm(dOT, Q, HT, Q, kofs, E, d, f, 0, dwd, f, (int64_t)d * f);
+        MOE_HIP(launch_grouped_gemm(w1, false, true, s));
+        GemmGroup w2 = kgroup_gemm(DADUT, Q, XgT, Q, kofs, E, f, d, 0, dwg, d, (int64_t)f * d);
+        MOE_HIP(launch_grouped_gemm(w2, false, true, s));
+        w2.A = static_cast<const char*>(DADUT) + (size_t)f * Q * w;
+        w2.C = dwu;
+        MOE_HIP(launch_grouped_gemm(w2, false, true, s));
+    } else {
+        void *DU = at<void>(ws, L.DU), *dO = at<void>(ws, L.dO);
+        // dH' = dy W_down (rows gathered by pair)
+        GradGemm g1 = grad_gemm(dy, d, wd, f, dHp, f, P, f, d);
+        g1.a_gather = sorted; g1.a_div = k; g1.b_gstride = (int64_t)d * f; g1.offsets = offsets; g1.G = E;
+        MOE_HIP(launch_grad_gemm(g1, false, false, bf16, bf16, s));
+        // h, dg, da, du, dO per pair
+        BwdPairArgs pa{sorted, offsets, E, k, gates, A, U, dHp, H, DA, DU, dgate, dy, dO, f, d};
+        MOE_HIP(launch_bwd_pair(pa, P, bf16, s));
+        // dx of each pair = da W_gate + du W_up, then summed per token in slot order
+        GradGemm g2 = grad_gemm(DA, f, wg, d, dXp, d, P, d, f);
+        g2.b_gstride = (int64_t)f * d; g2.offsets = offsets; g2.G = E;
+        MOE_HIP(launch_grad_gemm(g2, false, false, bf16, bf16, s));
+        g2.A = DU; g2.B = wu; g2.accumulate = true;
+        MOE_HIP(launch_grad_gemm(g2, false, false, bf16, bf16, s));
+        MOE_HIP(launch_bwd_token_sum(dXp, pos, T, k, d, dx, s));
+        // weight gradients: sums over each expert's rows
+        GradGemm w1 = grad_gemm(dO, d, H, f, dwd, f, d, f, P);
+        w1.c_gstride = (int64_t)d * f; w1.offsets = offsets; w1.G = E;
+        MOE_HIP(launch_grad_gemm(w1, true, false, bf16, bf16, s));
+        GradGemm w2 = grad_gemm(DA, f, x, d, dwg, d, f, d, P);
+        w2.b_gather = sorted; w2.b_div = k; w2.c_gstride = (int64_t)f * d; w2.offsets = offsets; w2.G = E;
+        MOE_HIP(launch_grad_gemm(w2, true, false, bf16, bf16, s));
+        w2.A = DU; w2.C = dwu;
+        MOE_HIP(launch_grad_gemm(w2, true, false, bf16, bf16, s));
+    }
     // router: dl from dg (logits recomputed when the gates need them)
     const bool need_logits = !(c->score_fn == MOE_SCORE_SOFTMAX && c->renormalize);
     if (need_logits) {
@@ -423,8 +555,7 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
     }
     BwdRouterArgs ra{ids, gates, dgate, need_logits ? logits : nullptr, dl, T, E, k, c->score_fn, c->renormalize};
     MOE_HIP(launch_bwd_router(ra, s));
-    GradGemm gr = grad_gemm(dl, E, x, d, dwr, d, E, d, T);
-    MOE_HIP(launch_grad_gemm(gr, true, false, false, bf16, s));
+    MOE_HIP(launch_router_wgrad(dl, x, bf16, T, E, d, at<float>(ws, L.rw), dwr, s));
     GradGemm gx = grad_gemm(dl, E, wr, d, dx, d, T, d, E);
     gx.accumulate = true;
     MOE_HIP(launch_grad_gemm(gx, false, false, false, bf16, s));
@@ -432,27 +563,63 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
     if (c->num_shared) {
         const int fs = c->d_ff_shared;
         void *As = at<void>(ws, L.As), *Us = at<void>(ws, L.Us), *Hs = at<void>(ws, L.Hs);
-        void *DAs = at<void>(ws, L.DAs), *DUs = at<void>(ws, L.DUs);
+        void* DAs = at<void>(ws, L.DAs);
         float* dHs = at<float>(ws, L.dHs);
         GemmGroup sa{x, nullptr, 1, nullptr, 1, T, sg, nullptr, As, fs, d};
         MOE_HIP(launch_grouped_gemm(sa, false, bf16, s));
         GemmGroup su_{x, nullptr, 1, nullptr, 1, T, su, nullptr, Us, fs, d};
         MOE_HIP(launch_grouped_gemm(su_, false, bf16, s));
-        GradGemm s1 = grad_gemm(dy, d, sd, fs, dHs, fs, T, fs, d);
-        MOE_HIP(launch_grad_gemm(s1, false, false, bf16, bf16, s));
-        BwdPairArgs sp{nullptr, nullptr, 1, 1, nullptr, As, Us, dHs, Hs, DAs, DUs, nullptr, dy, nullptr, fs, d};
-        MOE_HIP(launch_bwd_pair(sp, T, bf16, s));
-        GradGemm s2 = grad_gemm(DAs, fs, sg, d, dx, d, T, d, fs);
-        s2.accumulate = true;
-        MOE_HIP(launch_grad_gemm(s2, false, false, bf16, bf16, s));
-        s2.A = DUs; s2.B = su;
-        MOE_HIP(launch_grad_gemm(s2, false, false, bf16, bf16, s));
-        GradGemm s3 = grad_gemm(dy, d, Hs, fs, dsd, fs, d, fs, T);
-        MOE_HIP(launch_grad_gemm(s3, true, false, bf16, bf16, s));
-        GradGemm s4 = grad_gemm(DAs, fs, x, d, dsg, d, fs, d, T);
-        MOE_HIP(launch_grad_gemm(s4, true, false, bf16, bf16, s));
-        s4.A = DUs; s4.C = dsu;
-        MOE_HIP(launch_grad_gemm(s4, true, false, bf16, bf16, s));
+        if (pl.shared_fast) {
+            const int64_t Tq = pl.Tq;
+            void *WsdT = at<void>(ws, L.WsdT), *WsguT = at<void>(ws, L.WsguT), *dyT = at<void>(ws, L.dyT);
+            void *HsT = at<void>(ws, L.HsT), *DADUsT = at<void>(ws, L.DADUsT), *xT = at<void>(ws, L.xT);
+            MOE_HIP(launch_transpose_bf16(sd, 0, fs, d, fs, 1, WsdT, 0, d, 0, s));
+            GemmGroup s1 = f32_gemm(dy, nullptr, 1, nullptr, 1, T, WsdT, dHs, fs, fs, d);
+            MOE_HIP(launch_grouped_gemm(s1, false, true, s));
+            BwdPairArgs sp{nullptr, nullptr, 1, 1, nullptr, As, Us, dHs, Hs, DAs, static_cast<char*>(DAs) + fs * w,
+                           nullptr, dy, nullptr, fs, d};
+            sp.ld_dadu = 2 * (int64_t)fs;
+            MOE_HIP(launch_bwd_pair(sp, T, true, s));
+            MOE_HIP(launch_transpose_bf16(sg, 0, d, fs, d, 1, WsguT, 0, 2 * fs, 0, s));
+            MOE_HIP(launch_transpose_bf16(su, 0, d, fs, d, 1, WsguT, 0, 2 * fs, fs, s));
+            GemmGroup s2 = f32_gemm(DAs, nullptr, 1, nullptr, 1, T, WsguT, dx, d, d, 2 * fs);
+            s2.accumulate = true;
+            MOE_HIP(launch_grouped_gemm(s2, false, true, s));
+            const int tq = (int)Tq;
+            MOE_HIP(launch_transpose_rows(rows_t(dy, d, d, nullptr, 1, nullptr, nullptr, nullptr, 1, T, tq, dyT, Tq),
+                                          Tq, s));
+            MOE_HIP(launch_transpose_rows(rows_t(Hs, fs, fs, nullptr, 1, nullptr, nullptr, nullptr, 1, T, tq, HsT, Tq),
+                                          Tq, s));
+            MOE_HIP(launch_transpose_rows(
+                rows_t(DAs, 2 * (int64_t)fs, 2 * fs, nullptr, 1, nullptr, nullptr, nullptr, 1, T, tq, DADUsT, Tq), Tq,
+                s));
+            MOE_HIP(launch_transpose_rows(rows_t(x, d, d, nullptr, 1, nullptr, nullptr, nullptr, 1, T, tq, xT, Tq),
+                                          Tq, s));
+            GemmGroup s3 = kgroup_gemm(dyT, Tq, HsT, Tq, nullptr, 1, d, fs, tq, dsd, fs, 0);
+            MOE_HIP(launch_grouped_gemm(s3, false, true, s));
+            GemmGroup s4 = kgroup_gemm(DADUsT, Tq, xT, Tq, nullptr, 1, fs, d, tq, dsg, d, 0);
+            MOE_HIP(launch_grouped_gemm(s4, false, true, s));
+            s4.A = static_cast<const char*>(DADUsT) + (size_t)fs * Tq * w;
+            s4.C = dsu;
+            MOE_HIP(launch_grouped_gemm(s4, false, true, s));
+        } else {
+            void* DUs = at<void>(ws, L.DUs);
+            GradGemm s1 = grad_gemm(dy, d, sd, fs, dHs, fs, T, fs, d);
+            MOE_HIP(launch_grad_gemm(s1, false, false, bf16, bf16, s));
+            BwdPairArgs sp{nullptr, nullptr, 1, 1, nullptr, As, Us, dHs, Hs, DAs, DUs, nullptr, dy, nullptr, fs, d};
+            MOE_HIP(launch_bwd_pair(sp, T, bf16, s));
+            GradGemm s2 = grad_gemm(DAs, fs, sg, d, dx, d, T, d, fs);
+            s2.accumulate = true;
+            MOE_HIP(launch_grad_gemm(s2, false, false, bf16, bf16, s));
+            s2.A = DUs; s2.B = su;
+            MOE_HIP(launch_grad_gemm(s2, false, false, bf16, bf16, s));
+            GradGemm s3 = grad_gemm(dy, d, Hs, fs, dsd, fs, d, fs, T);
+            MOE_HIP(launch_grad_gemm(s3, true, false, bf16, bf16, s));
+            GradGemm s4 = grad_gemm(DAs, fs, x, d, dsg, d, fs, d, T);
+            MOE_HIP(launch_grad_gemm(s4, true, false, bf16, bf16, s));
+            s4.A = DUs; s4.C = dsu;
+            MOE_HIP(launch_grad_gemm(s4, true, false, bf16, bf16, s));
+        }
     }
     return MOE_OK;
 }

@@ -72,6 +72,19 @@ struct GemmGroup {
     bool aligned_bands = false; // single bf16: tile bands follow group boundaries
     bool skinny = false;    // bf16, few rows per group: 32-row tiles streaming the weights
     hipEvent_t t_start = nullptr, t_stop = nullptr;  // recorded when the kernel starts / ends
+    // fp32 products (single bf16 GEMM on the persistent kernel):
+    //   f32_out: C fp32 [rows, ldc] (split K: slices part_stride apart);
+    //     accumulate (splitk 1): C += product.
+    //   kgrouped: every group has the whole M x N output and sums over its own
+    //     K columns [kofs[g], kofs[g+1]) (multiples of 128, at least 128;
+    //     kofs == nullptr: one group over [0, K)): A(m, k) = A[m lda + k],
+    //     B(n, k) = B0[n ldb + k], C(g, m, n) = C[g c_gstride + m ldc + n];
+    //     M and N multiples of 256.
+    bool f32_out = false;
+    bool accumulate = false;
+    bool kgrouped = false;
+    const int32_t* kofs = nullptr;
+    int64_t lda = 0, ldb = 0, ldc = 0, c_gstride = 0;
 };
 // Dual mode: C = silu(A B0^T) * (A B1^T).  Single: C = A B0^T, or with
 // splitk > 1 the partial products of the K ranges, C slice s = A[:, Ks] B0[:, Ks]^T.
@@ -135,6 +148,7 @@ struct BwdPairArgs {
     const void* dy;         // [T, dm]
     void* d_o;              // [rows, dm] out, or nullptr
     int f, dm;
+    int64_t ld_dadu = 0;    // row stride of da and du (0: f)
 };
 hipError_t launch_bwd_pair(const BwdPairArgs& b, int rows, bool bf16, hipStream_t s);
 
@@ -149,8 +163,38 @@ struct BwdRouterArgs {
     int T, E, k, score_fn, renorm;
 };
 hipError_t launch_bwd_router(const BwdRouterArgs& b, hipStream_t s);
+// dx[t] = sum over slots j, then K slices, of dxp[slice][pair_pos[t k + j]] (pos -1 skipped).
 hipError_t launch_bwd_token_sum(const float* dxp, const int32_t* pair_pos, int T, int k, int d, float* dx,
-                                hipStream_t s);
+                                hipStream_t s, int splitk = 1, int64_t part_stride = 0);
+
+// dW_r [E, d] = dl^T x (x bf16 or fp32) over token chunks; part holds
+// router_wgrad_chunks(T, d, E) x E x d floats.
+int router_wgrad_chunks(int T, int d, int E);
+hipError_t launch_router_wgrad(const float* dl, const void* x, bool x_bf16, int T, int E, int d, float* part,
+                               float* dwr, hipStream_t s);
+
+// bf16 transposes for the backward's GEMMs on the forward kernel.
+// dst[b][c][col0 + r] = src[b][r][c]; R, C multiples of 64; strides multiples of 8.
+hipError_t launch_transpose_bf16(const void* src, int64_t s_bstride, int64_t ld_src, int R, int C, int batch,
+                                 void* dst, int64_t d_bstride, int64_t ld_dst, int col0, hipStream_t s);
+// Grouped rows as columns, each group's columns starting at kofs[g] (zero past its rows).
+struct TransposeRowsArgs {
+    const uint16_t* src;    // source rows [*, ld_src], columns c < C (C multiple of 64)
+    int64_t ld_src;
+    int C;
+    const int32_t* gather;  // grouped row -> pair id, or nullptr (source row = grouped row)
+    int div;                // source row = pair id / div
+    const float* scale;     // [pairs] factor by pair id, or nullptr
+    const int32_t* offsets; // [G+1] grouped rows per group, or nullptr (one group of M rows)
+    const int32_t* kofs;    // [G+1] first column of each group (multiples of 128)
+    int G, M, kpad;         // one group: M rows, kpad columns (multiple of 128)
+    uint16_t* dst;          // [C, ld_dst]
+    int64_t ld_dst;
+};
+// cols_upper: a multiple of 128 at least the columns written (kofs[G] or kpad).
+hipError_t launch_transpose_rows(const TransposeRowsArgs& a, int64_t cols_upper, hipStream_t s);
+// kofs[0..G] from offsets: each group's rows rounded up to 128 (empty: 128).
+hipError_t launch_kgroup_offsets(const int32_t* offsets, int G, int32_t* kofs, hipStream_t s);
 
 // ---- combine ------------------------------------------------------------------
 struct CombineArgs {

@@ -39,6 +39,15 @@ CASES = {
     "bf16_e64_k8_zipf": S("b", T=300, d=256, E=64, k=8, d_ff=128, zipf_s=1.1),
     "bf16_decode_e8_k2": S("b", T=16, d=512, E=8, k=2, d_ff=256),
     "bf16_e4_k1": S("b", T=90, d=128, E=4, k=1, d_ff=128),
+    # widths in multiples of 256: the GEMMs run on the forward's kernel over
+    # transposed operands (per-expert K ranges padded to 128 for the weights)
+    "bf16_w256_e8_k2": S("b", T=300, d=256, E=8, k=2, d_ff=512),
+    "bf16_w256_e16_k4_sigmoid_shared": S("b", T=260, d=512, E=16, k=4, d_ff=256, num_shared=1, d_ff_shared=256,
+                                         score_fn=synth.SIGMOID),
+    "bf16_w256_e32_k2_zipf": S("b", T=100, d=256, E=32, k=2, d_ff=256, zipf_s=1.5),
+    "bf16_w256_e4_k2_long_groups": S("b", T=1200, d=256, E=4, k=2, d_ff=256),
+    # dx per pair with its K (2 d_ff = 3072) cut in two slices
+    "bf16_w256_e8_k2_dx_split": S("b", T=200, d=256, E=8, k=2, d_ff=1536),
 }
 
 NAMES = [("dx", "dx"), ("dw_router", "dw_router"), ("dw_gate", "dw_gate"), ("dw_up", "dw_up"),
@@ -97,3 +106,22 @@ def test_backward_matches_oracle(name):
     for gname in ("dw_gate", "dw_up", "dw_down"):
         assert not np.any(to_host(out[gname])[unused]), gname
     say(f"[ok] worst max|err|/max|ref| = {worst:.2e}, unused experts {unused.tolist()}")
+
+
+@pytest.mark.parametrize("name", ["bf16_w256_e16_k4_sigmoid_shared", "bf16_e32_k4_sigmoid_shared", "fp32_e8_k2"])
+def test_backward_empty_batch_zeroes_weight_grads(name):
+    """T = 0: nothing routed, every weight gradient is written as exact zeros."""
+    import dataclasses
+    sh = dataclasses.replace(CASES[name], T=0)
+    say(f"[case] backward empty batch {name}")
+    inp = synth.make_inputs(sh, 21)
+    L = DeviceLayer(sh, inp)
+    t = torch()
+    ids = t.empty((0, sh.k), dtype=t.int32, device="cuda")
+    wts = t.empty((0, sh.k), dtype=t.float32, device="cuda")
+    dy = t.empty((0, sh.d), dtype=t.bfloat16 if sh.dtype == synth.BF16 else t.float32, device="cuda")
+    out = run_backward(L, ids, wts, dy)
+    t.cuda.synchronize()
+    for gname, _ in NAMES:
+        if gname in out and gname != "dx":
+            assert not np.any(to_host(out[gname])), gname
