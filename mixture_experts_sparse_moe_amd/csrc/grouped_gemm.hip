@@ -534,19 +534,50 @@ __device__ __forceinline__ void store_block_bf16(uint16_t* Cb, int64_t ldc, int 
     }
 }
 
-// Stores (or adds to) one 32 x 32 block of MFMA results as fp32: lane (half,
-// r32) holds column r32 of block rows 8 a + 4 half + b in v[4 a + b]; each
-// store instruction writes two 128-byte row pieces.  Rows at or past
-// rows_left are not written.
+// Stores (or adds to) one 32 x 32 block of MFMA results as fp32.  Lane (half,
+// r32) holds column r32 of block rows 8 a + 4 half + b in v[4 a + b].
+// VEC: inside each quad of lanes a 4 x 4 transpose (exchanges with lane j ^ 1,
+// then j ^ 2) gives lane j = r32 % 4 row 8 a + 4 half + j, columns r32 - j ..
+// r32 - j + 3, written as one 16-byte store per a.  Otherwise each store
+// instruction writes two 128-byte row pieces (measured faster for the short
+// tiles of the grouped-K mode).  Rows at or past rows_left are not written.
+template <bool VEC>
 __device__ __forceinline__ void store_block_f32(float* Cf, int64_t ldc, int rows_left, const f32x16_t& v,
                                                 int lane, bool accumulate) {
-    const int half = lane >> 5, r32 = lane & 31;
+    if constexpr (!VEC) {
+        const int half = lane >> 5, r32 = lane & 31;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const int row = 8 * (q >> 2) + 4 * half + (q & 3);
+        for (int q = 0; q < 16; ++q) {
+            const int row = 8 * (q >> 2) + 4 * half + (q & 3);
+            if (row < rows_left) {
+                float* p = Cf + row * ldc + r32;
+                *p = accumulate ? *p + v[q] : v[q];
+            }
+        }
+        return;
+    }
+    const int half = lane >> 5, r32 = lane & 31, j = r32 & 3;
+    const bool odd = j & 1, upper = j & 2;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const float c0 = v[4 * a + 0], c1 = v[4 * a + 1], c2 = v[4 * a + 2], c3 = v[4 * a + 3];
+        // j ^ 1: even lanes keep rows 0 and 2 of columns (j, j + 1), odd lanes rows 1 and 3 of (j - 1, j)
+        const float r0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(odd ? c0 : c1), 0xB1, 0xF, 0xF, true));
+        const float r1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(odd ? c2 : c3), 0xB1, 0xF, 0xF, true));
+        const float p0 = odd ? r0 : c0, p1 = odd ? c1 : r0;   // row j & 1, column pair of the lane
+        const float q0 = odd ? r1 : c2, q1 = odd ? c3 : r1;   // row 2 + (j & 1), same columns
+        // j ^ 2: lanes 0, 1 keep their first row and take columns 2, 3 of it; lanes 2, 3 the second row
+        const float t0 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(upper ? p0 : q0), 0x4E, 0xF, 0xF, true));
+        const float t1 = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(upper ? p1 : q1), 0x4E, 0xF, 0xF, true));
+        float4 out = upper ? make_float4(t0, t1, q0, q1) : make_float4(p0, p1, t0, t1);
+        const int row = 8 * a + 4 * half + j;
         if (row < rows_left) {
-            float* p = Cf + row * ldc + r32;
-            *p = accumulate ? *p + v[q] : v[q];
+            float4* p = reinterpret_cast<float4*>(Cf + row * ldc + (r32 - j));
+            if (accumulate) {
+                const float4 o = *p;
+                out.x += o.x; out.y += o.y; out.z += o.z; out.w += o.w;
+            }
+            *p = out;
         }
     }
 }
@@ -779,7 +810,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
                     float* Cf = static_cast<float*>(g.C) +
                                 (KG ? (int64_t)tr.grp * g.c_gstride : (int64_t)tr.ks * g.part_stride) +
                                 (int64_t)(tr.row0 + rb) * g.ldc + tr.n0 + cb;
-                    store_block_f32(Cf, g.ldc, tr.nrows - rb, acc[i][bo], lane, g.accumulate);
+                    store_block_f32<!KG>(Cf, g.ldc, tr.nrows - rb, acc[i][bo], lane, g.accumulate);
                 }
             }
         }
@@ -1030,7 +1061,10 @@ hipError_t launch_bf16_persistent(const GemmGroup& g, hipStream_t s) {
 // fp32 products on the persistent kernel (the backward's GEMMs).
 hipError_t launch_bf16_f32out(const GemmGroup& g, hipStream_t s) {
     auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-    if (!al16(g.A) || !al16(g.B0) || g.ldc < g.N || g.N % 256 || g.N <= 0) return hipErrorInvalidValue;
+    // 16-byte fp32 stores: C, its row stride and slice / group strides in whole 4-float pieces
+    if (!al16(g.A) || !al16(g.B0) || !al16(g.C) || g.ldc < g.N || g.ldc % 4 || g.part_stride % 4 ||
+        g.c_gstride % 4 || g.N % 256 || g.N <= 0)
+        return hipErrorInvalidValue;
     const dim3 grid(persistent_grid()), block(512);
     if (g.kgrouped) {
         const int G = g.kofs ? g.G : 1;
