@@ -10,7 +10,10 @@
 // bf16 kernels (gfx950), fp32 accumulation on v_mfma_f32_32x32x16_bf16:
 //   - gemm_bf16_persistent_kernel: the main path.  One workgroup of 8 waves
 //     per CU walks 256 x 256 tiles of MFMA work with a direct-to-LDS DMA
-//     pipeline that runs on across tiles; described at the kernel.
+//     pipeline that runs on across tiles; described at the kernel.  Two more
+//     modes serve the backward pass: fp32 products over the grouped rows, and
+//     grouped K (each group sums over its own range of K columns: the weight
+//     gradients, over transposed activations).
 //   - gemm_bf16_kernel: the general fallback for N or K that the persistent
 //     kernel does not take (N % 128, K % 128 != 0): 4 waves, BM x BN tiles,
 //     global -> registers -> LDS, double-buffered, one workgroup per tile.
