@@ -69,6 +69,8 @@ def lib():
         L.oracle_forward_expert_loop.restype = i32
         L.oracle_backward.argtypes = [i64] + [i32] * 9 + [vp] * 8 + [vp, vp] + [vp] * 8
         L.oracle_backward.restype = i32
+        L.oracle_backward_weight_samples.argtypes = ([i64] + [i32] * 8 + [vp] * 8 + [vp, vp, i32] + [vp] * 5)
+        L.oracle_backward_weight_samples.restype = i32
         _lib = L
     return _lib
 
@@ -260,10 +262,11 @@ def forward(inp: dict, k: int, score_fn: int = SOFTMAX, renormalize: int = 1,
 
 
 def backward(inp: dict, ids: np.ndarray, dy: np.ndarray, score_fn: int = SOFTMAX,
-             renormalize: int = 1) -> dict:
+             renormalize: int = 1, weights: bool = True) -> dict:
     """Gradients of L = sum(dy * y) for the routing ``ids`` [T,k] (held fixed):
     dx, dw_router, dw_gate, dw_up, dw_down (and ds_gate, ds_up, ds_down with a
-    shared expert), fp64, by the chain rule written out per token."""
+    shared expert), fp64, by the chain rule written out per token.  With
+    weights=False only dx (each token's row depends on that token alone)."""
     x = _c(inp["x"])
     wr, wg, wu, wd = (_c(inp[n]) for n in ("w_router", "w_gate", "w_up", "w_down"))
     sg, su, sd = (_c(inp.get(n)) for n in ("ws_gate", "ws_up", "ws_down"))
@@ -274,15 +277,58 @@ def backward(inp: dict, ids: np.ndarray, dy: np.ndarray, score_fn: int = SOFTMAX
     f_s = 0 if sg is None else sg.shape[0]
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     dy = np.ascontiguousarray(dy, dtype=np.float64)
-    out = dict(dx=np.empty((T, d)), dw_router=np.empty((E, d)), dw_gate=np.empty((E, f, d)),
-               dw_up=np.empty((E, f, d)), dw_down=np.empty((E, d, f)))
-    if S:
+    out = dict(dx=np.empty((T, d)))
+    if weights:
+        out.update(dw_router=np.empty((E, d)), dw_gate=np.empty((E, f, d)), dw_up=np.empty((E, f, d)),
+                   dw_down=np.empty((E, d, f)))
+    if S and weights:
         out.update(ds_gate=np.empty((f_s, d)), ds_up=np.empty((f_s, d)), ds_down=np.empty((d, f_s)))
+    wp = (lambda n: out[n].ctypes.data) if weights else (lambda n: None)
     rc = lib().oracle_backward(T, d, E, k, f, S, f_s, score_fn, renormalize, _dtype_of(x), x.ctypes.data,
                                wr.ctypes.data, wg.ctypes.data, wu.ctypes.data, wd.ctypes.data, _ptr(sg),
                                _ptr(su), _ptr(sd), ids.ctypes.data, dy.ctypes.data,
-                               *(out[n].ctypes.data for n in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down")),
-                               *((out[n].ctypes.data for n in ("ds_gate", "ds_up", "ds_down")) if S else (None,) * 3))
+                               out["dx"].ctypes.data, *(wp(n) for n in ("dw_router", "dw_gate", "dw_up", "dw_down")),
+                               *((wp(n) for n in ("ds_gate", "ds_up", "ds_down")) if S else (None,) * 3))
     if rc:
         raise ValueError(f"oracle_backward failed ({rc})")
+    return out
+
+
+WEIGHT_SAMPLE_KINDS = ("dw_gate", "dw_up", "dw_down", "ds_gate", "ds_up", "ds_down")
+
+
+def backward_weight_samples(inp: dict, ids: np.ndarray, dy: np.ndarray, samples, score_fn: int = SOFTMAX,
+                            renormalize: int = 1) -> np.ndarray:
+    """Single elements of the weight gradients of ``backward``, each summed over
+    its expert's pairs (all tokens for the shared expert), for checking
+    full-size layers on a sample.  samples: (name, e, i, j) with name in
+    WEIGHT_SAMPLE_KINDS, the element being grad[name][e][i][j] (routed) or
+    grad[name][i][j] (shared; e ignored)."""
+    x = _c(inp["x"])
+    wr, wg, wu, wd = (_c(inp[n]) for n in ("w_router", "w_gate", "w_up", "w_down"))
+    sg, su, sd = (_c(inp.get(n)) for n in ("ws_gate", "ws_up", "ws_down"))
+    T, d = x.shape
+    E, f = wg.shape[0], wg.shape[1]
+    k = ids.shape[1]
+    f_s = 0 if sg is None else sg.shape[0]
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    dy = np.ascontiguousarray(dy, dtype=np.float64)
+    kind, eidx, ridx, cidx = [], [], [], []
+    for name, e, i, j in samples:
+        kd = WEIGHT_SAMPLE_KINDS.index(name)
+        if kd >= 3 and sg is None:
+            raise ValueError(f"{name}: the layer has no shared expert")
+        # the oracle takes (row r of the inner width, column c of the model width)
+        down = name in ("dw_down", "ds_down")
+        r, c = (j, i) if down else (i, j)
+        kind.append(kd); eidx.append(e); ridx.append(r); cidx.append(c)
+    arr = [np.ascontiguousarray(v, dtype=np.int32) for v in (kind, eidx, ridx, cidx)]
+    out = np.empty(len(kind))
+    rc = lib().oracle_backward_weight_samples(T, d, E, k, f, f_s, score_fn, renormalize, _dtype_of(x),
+                                              x.ctypes.data, wr.ctypes.data, wg.ctypes.data, wu.ctypes.data,
+                                              wd.ctypes.data, _ptr(sg), _ptr(su), _ptr(sd), ids.ctypes.data,
+                                              dy.ctypes.data, len(kind), *(a.ctypes.data for a in arr),
+                                              out.ctypes.data)
+    if rc:
+        raise ValueError(f"oracle_backward_weight_samples failed ({rc})")
     return out

@@ -384,12 +384,16 @@ int oracle_backward(int64_t T, int d, int E, int k, int f, int num_shared, int f
                     const int32_t* ids, const double* dy, double* dx, double* dwr, double* dwg,
                     double* dwu, double* dwd, double* dsg, double* dsu, double* dsd) {
     if (k < 1 || k > E) return -2;
+    /* dwr == NULL: dx only (every weight gradient pointer ignored, nothing summed into them) */
+    const int wgrads = dwr != NULL;
     memset(dx, 0, sizeof(double) * T * d);
-    memset(dwr, 0, sizeof(double) * E * d);
-    memset(dwg, 0, sizeof(double) * E * f * d);
-    memset(dwu, 0, sizeof(double) * E * f * d);
-    memset(dwd, 0, sizeof(double) * E * d * f);
-    if (num_shared) {
+    if (wgrads) {
+        memset(dwr, 0, sizeof(double) * E * d);
+        memset(dwg, 0, sizeof(double) * E * f * d);
+        memset(dwu, 0, sizeof(double) * E * f * d);
+        memset(dwd, 0, sizeof(double) * E * d * f);
+    }
+    if (num_shared && wgrads) {
         memset(dsg, 0, sizeof(double) * f_s * d);
         memset(dsu, 0, sizeof(double) * f_s * d);
         memset(dsd, 0, sizeof(double) * d * f_s);
@@ -450,8 +454,9 @@ int oracle_backward(int64_t T, int d, int E, int k, int f, int num_shared, int f
                 for (int c = 0; c < d; ++c) acc += widen(wd, dtype, wdn + (int64_t)c * f + r) * g[j] * dyt[c];
                 dh[r] = acc;
             }
-            for (int c = 0; c < d; ++c)
-                for (int r = 0; r < f; ++r) dwd[wdn + (int64_t)c * f + r] += g[j] * dyt[c] * h[r];
+            if (wgrads)
+                for (int c = 0; c < d; ++c)
+                    for (int r = 0; r < f; ++r) dwd[wdn + (int64_t)c * f + r] += g[j] * dyt[c] * h[r];
             for (int r = 0; r < f; ++r) {
                 double sig = 1.0 / (1.0 + exp(-a[r]));
                 double dsilu = sig * (1.0 + a[r] * (1.0 - sig));        /* d/da of a * sigmoid(a) */
@@ -459,8 +464,10 @@ int oracle_backward(int64_t T, int d, int E, int k, int f, int num_shared, int f
                 double du = dh[r] * a[r] * sig;
                 for (int c = 0; c < d; ++c) {
                     double xc = widen(x, dtype, t * d + c);
-                    dwg[win + (int64_t)r * d + c] += da * xc;
-                    dwu[win + (int64_t)r * d + c] += du * xc;
+                    if (wgrads) {
+                        dwg[win + (int64_t)r * d + c] += da * xc;
+                        dwu[win + (int64_t)r * d + c] += du * xc;
+                    }
                     dxt[c] += widen(wg, dtype, win + (int64_t)r * d + c) * da +
                               widen(wu, dtype, win + (int64_t)r * d + c) * du;
                 }
@@ -494,7 +501,7 @@ int oracle_backward(int64_t T, int d, int E, int k, int f, int num_shared, int f
         }
         for (int m = 0; m < E; ++m)
             for (int c = 0; c < d; ++c) {
-                dwr[(int64_t)m * d + c] += dl[m] * widen(x, dtype, t * d + c);
+                if (wgrads) dwr[(int64_t)m * d + c] += dl[m] * widen(x, dtype, t * d + c);
                 dxt[c] += widen(w_r, dtype, (int64_t)m * d + c) * dl[m];
             }
         /* shared expert */
@@ -513,8 +520,9 @@ int oracle_backward(int64_t T, int d, int E, int k, int f, int num_shared, int f
                 for (int c = 0; c < d; ++c) acc += widen(sd, dtype, (int64_t)c * f_s + r) * dyt[c];
                 dh[r] = acc;
             }
-            for (int c = 0; c < d; ++c)
-                for (int r = 0; r < f_s; ++r) dsd[(int64_t)c * f_s + r] += dyt[c] * h[r];
+            if (wgrads)
+                for (int c = 0; c < d; ++c)
+                    for (int r = 0; r < f_s; ++r) dsd[(int64_t)c * f_s + r] += dyt[c] * h[r];
             for (int r = 0; r < f_s; ++r) {
                 double sig = 1.0 / (1.0 + exp(-a[r]));
                 double dsilu = sig * (1.0 + a[r] * (1.0 - sig));
@@ -522,8 +530,10 @@ int oracle_backward(int64_t T, int d, int E, int k, int f, int num_shared, int f
                 double du = dh[r] * a[r] * sig;
                 for (int c = 0; c < d; ++c) {
                     double xc = widen(x, dtype, t * d + c);
-                    dsg[(int64_t)r * d + c] += da * xc;
-                    dsu[(int64_t)r * d + c] += du * xc;
+                    if (wgrads) {
+                        dsg[(int64_t)r * d + c] += da * xc;
+                        dsu[(int64_t)r * d + c] += du * xc;
+                    }
                     dxt[c] += widen(sg, dtype, (int64_t)r * d + c) * da + widen(su, dtype, (int64_t)r * d + c) * du;
                 }
             }
@@ -531,4 +541,88 @@ int oracle_backward(int64_t T, int d, int E, int k, int f, int num_shared, int f
     }
     free(l); free(s); free(dl); free(g); free(dg); free(a); free(u); free(h); free(dh); free(o);
     return err;
+}
+
+/*
+ * Single elements of the expert weight gradients of oracle_backward, each a
+ * sum over the pairs routed to its expert (or over all tokens for the shared
+ * expert, gate 1), so that full-size layers can be checked on a sample:
+ *   kind 0: dW_gate[e][r][c] = sum_p da_p[r] x_t[c]
+ *   kind 1: dW_up[e][r][c]   = sum_p du_p[r] x_t[c]
+ *   kind 2: dW_down[e][c][r] = sum_p g_p dy_t[c] h_p[r]
+ *   kind 3, 4, 5: the same for the shared expert (e ignored, g = 1)
+ * with, for pair p = (t, j) of expert e and row r of its inner width:
+ *   a = <W_gate,e[r], x_t>, u = <W_up,e[r], x_t>, h = silu(a) u,
+ *   dh = g <W_down,e[:, r], dy_t>, da = dh u silu'(a), du = dh silu(a),
+ * the gates g of the given ids as in oracle_backward ("8.6 Mixture of
+ * Experts", sec. 2).  Pairs are visited in token order.  Returns 0, or -2 for
+ * an invalid id or kind.
+ */
+int oracle_backward_weight_samples(int64_t T, int d, int E, int k, int f, int f_s, int score_fn, int renorm,
+                                   int dtype, const void* x, const void* w_r, const void* wg, const void* wu,
+                                   const void* wd, const void* sg, const void* su, const void* sd,
+                                   const int32_t* ids, const double* dy, int n, const int32_t* kind,
+                                   const int32_t* eidx, const int32_t* ridx, const int32_t* cidx, double* out) {
+    if (k < 1 || k > E) return -2;
+    for (int64_t i = 0; i < T * k; ++i)
+        if (ids[i] < 0 || ids[i] >= E) return -2;
+    for (int q = 0; q < n; ++q)
+        if (kind[q] < 0 || kind[q] > 5 || (kind[q] < 3 && (eidx[q] < 0 || eidx[q] >= E))) return -2;
+    /* the gates of every pair, from the recomputed logits */
+    double* gates = (double*)malloc(sizeof(double) * T * k);
+#pragma omp parallel
+    {
+        double* l = (double*)malloc(sizeof(double) * E);
+        double* s = (double*)malloc(sizeof(double) * E);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < T; ++t) {
+            for (int e = 0; e < E; ++e) {
+                double acc = 0.0;
+                for (int c = 0; c < d; ++c) acc += widen(x, dtype, t * d + c) * widen(w_r, dtype, (int64_t)e * d + c);
+                l[e] = acc;
+            }
+            scores_of(l, E, score_fn, s);
+            double S = 0.0;
+            for (int j = 0; j < k; ++j) S += s[ids[t * k + j]];
+            for (int j = 0; j < k; ++j) gates[t * k + j] = renorm ? s[ids[t * k + j]] / S : s[ids[t * k + j]];
+        }
+        free(l); free(s);
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int q = 0; q < n; ++q) {
+        const int shared = kind[q] >= 3, kd = kind[q] % 3, e = eidx[q], r = ridx[q], c = cidx[q];
+        const int fw = shared ? f_s : f;
+        const void* G = shared ? sg : wg;
+        const void* U = shared ? su : wu;
+        const void* D = shared ? sd : wd;
+        const int64_t win = shared ? 0 : (int64_t)e * f * d, wdn = shared ? 0 : (int64_t)e * d * f;
+        double acc = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            for (int j = 0; j < (shared ? 1 : k); ++j) {
+                if (!shared && ids[t * k + j] != e) continue;
+                const double g = shared ? 1.0 : gates[t * k + j];
+                const double* dyt = dy + t * d;
+                double aa = 0.0, bb = 0.0;
+                for (int i = 0; i < d; ++i) {
+                    const double xi = widen(x, dtype, t * d + i);
+                    aa += widen(G, dtype, win + (int64_t)r * d + i) * xi;
+                    bb += widen(U, dtype, win + (int64_t)r * d + i) * xi;
+                }
+                if (kd == 2) {
+                    acc += g * dyt[c] * silu(aa) * bb;
+                    continue;
+                }
+                double dh = 0.0;
+                for (int i = 0; i < d; ++i) dh += widen(D, dtype, wdn + (int64_t)i * fw + r) * dyt[i];
+                dh *= g;
+                const double sig = 1.0 / (1.0 + exp(-aa));
+                const double xc = widen(x, dtype, t * d + c);
+                if (kd == 0) acc += dh * bb * (sig * (1.0 + aa * (1.0 - sig))) * xc;
+                else acc += dh * aa * sig * xc;
+            }
+        }
+        out[q] = acc;
+    }
+    free(gates);
+    return 0;
 }

@@ -4,6 +4,7 @@ max|err| <= tau * max|ref|: tau = 1e-4 for fp32 layers; 2e-2 for bf16 layers
 (the recomputed a, u, h and the intermediate da, du, dO are rounded to bf16,
 about five roundings of 2^-9 along any path)."""
 import sys
+import types
 
 import numpy as np
 import pytest
@@ -125,3 +126,59 @@ def test_backward_empty_batch_zeroes_weight_grads(name):
     for gname, _ in NAMES:
         if gname in out and gname != "dx":
             assert not np.any(to_host(out[gname])), gname
+
+
+@pytest.mark.parametrize("name", ["mixtral_prefill", "deepseek_v3"])
+def test_backward_full_size_sampled(name):
+    """Full-size layers in the configuration the benchmark times: dx on
+    sampled tokens (each depends on its own token only) and sampled elements
+    of every expert weight gradient, each summed by the oracle over its
+    expert's pairs; bound tau * (max |ref| over the tensor's samples).  The
+    router weight gradient needs every token's expert outputs, so it is
+    checked at the small shapes only."""
+    import mixture_experts_sparse_moe_amd as moe
+    t = torch()
+    sh = synth.SHAPES[name]
+    say(f"[gen] backward full size {name}")
+    inp = synth.make_inputs(sh, 0)
+    dv = {n: (None if a is None else to_dev(a)) for n, a in inp.items()}
+    cfg = moe.MoeConfig.of(sh.T, sh.d, sh.E, sh.k, sh.d_ff, sh.num_shared, sh.d_ff_shared, sh.score_fn,
+                           sh.renormalize)
+    ids = t.empty(sh.T, sh.k, dtype=t.int32, device="cuda")
+    wts = t.empty(sh.T, sh.k, dtype=t.float32, device="cuda")
+    moe.moe_route(cfg, dv["x"], dv["w_router"], ids, wts)
+    dy_h = synth.normal(0, 99, sh.T * sh.d, 1.0, sh.dtype).reshape(sh.T, sh.d)
+    say(f"[gpu] backward {name}")
+    out = run_backward(types.SimpleNamespace(sh=sh, d=dv, cfg=cfg), ids, wts, to_dev(dy_h))
+    t.cuda.synchronize()
+    gids = to_host(ids)
+    dy_ref = synth.bf16_to_f64(dy_h)
+    rng = np.random.default_rng(1)
+    tau = TAU[sh.dtype]
+    # dx on sampled tokens: the oracle's backward restricted to those tokens
+    toks = np.unique(np.concatenate([[0, sh.T - 1], rng.integers(0, sh.T, 4)]))
+    sub = dict(inp)
+    sub["x"] = inp["x"][toks]
+    say(f"[oracle] dx of tokens {toks.tolist()}")
+    ref_dx = oracle.backward(sub, gids[toks], dy_ref[toks], sh.score_fn, sh.renormalize, weights=False)["dx"]
+    got_dx = to_host(out["dx"][t.from_numpy(toks).cuda()]).astype(np.float64)
+    assert_close(got_dx, ref_dx, tau, "dx (sampled tokens)")
+    # weight gradients: 8 elements of each, experts and positions seeded
+    kinds = [("dw_gate", sh.d_ff, sh.d), ("dw_up", sh.d_ff, sh.d), ("dw_down", sh.d, sh.d_ff)]
+    if sh.num_shared:
+        kinds += [("ds_gate", sh.d_ff_shared, sh.d), ("ds_up", sh.d_ff_shared, sh.d),
+                  ("ds_down", sh.d, sh.d_ff_shared)]
+    samples = [(n, int(rng.integers(sh.E)), int(rng.integers(a)), int(rng.integers(b)))
+               for n, a, b in kinds for _ in range(8)]
+    say(f"[oracle] {len(samples)} weight-gradient elements")
+    ref = oracle.backward_weight_samples(inp, gids, dy_ref, samples, sh.score_fn, sh.renormalize)
+    gpu_name = {"ds_gate": "dws_gate", "ds_up": "dws_up", "ds_down": "dws_down"}
+    for n, _, _ in kinds:
+        sel = [q for q, s in enumerate(samples) if s[0] == n]
+        got = np.array([float(out[gpu_name.get(n, n)][s[2], s[3]] if n.startswith("ds_")
+                              else out[n][s[1], s[2], s[3]]) for s in (samples[q] for q in sel)])
+        want = ref[sel]
+        scale = np.abs(want).max()
+        err = np.abs(got - want).max()
+        say(f"[{n}] max|err| {err:.3e}, max|ref| {scale:.3e}")
+        assert err <= tau * scale, f"{n}: max|err| {err} > {tau} * {scale}"

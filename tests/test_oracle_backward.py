@@ -93,3 +93,37 @@ def test_weight_gradients_are_outer_product_sums():
     H = a / (1 + np.exp(-a)) * u
     np.testing.assert_allclose(g["dw_down"][1], (gate[:, None] * dy).T @ H, rtol=1e-12, atol=1e-14)
     assert np.all(g["dw_down"][0] == 0.0) and np.all(g["dw_down"][2] == 0.0)
+
+
+@pytest.mark.parametrize("score_fn,renorm", [(oracle.SOFTMAX, 1), (oracle.SIGMOID, 1), (oracle.SOFTMAX, 0)])
+def test_weight_samples_equal_full_backward(score_fn, renorm):
+    """The element-wise weight gradients (for checking full-size layers on a
+    sample) equal the entries of the whole backward, which the finite
+    differences above pin; routed and shared, every kind."""
+    T, d, E, k, f, f_s = 9, 8, 5, 2, 12, 6
+    inp = _inputs(T, d, E, k, f, 1, f_s, seed=7)
+    inp["x"] = inp["x"] * 2.0
+    ids = oracle.route(oracle.logits(inp["x"], inp["w_router"]), k, score_fn, renorm)["ids"]
+    dy = RNG.normal(size=(T, d))
+    g = oracle.backward(inp, ids, dy, score_fn, renorm)
+    samples = []
+    for e in range(E):
+        samples += [("dw_gate", e, int(RNG.integers(f)), int(RNG.integers(d))),
+                    ("dw_up", e, int(RNG.integers(f)), int(RNG.integers(d))),
+                    ("dw_down", e, int(RNG.integers(d)), int(RNG.integers(f)))]
+    samples += [("ds_gate", 0, 1, 2), ("ds_up", 0, 5, 7), ("ds_down", 0, 3, 4), ("ds_down", 0, 7, 0)]
+    got = oracle.backward_weight_samples(inp, ids, dy, samples, score_fn, renorm)
+    for (name, e, i, j), v in zip(samples, got):
+        want = g[name][i, j] if name.startswith("ds_") else g[name][e, i, j]
+        assert abs(v - want) <= 1e-12 * max(1.0, abs(want)), (name, e, i, j, v, want)
+
+
+def test_dx_only_equals_full_backward():
+    """weights=False (dx only, for full-size samples) gives the same dx."""
+    inp = _inputs(6, 8, 5, 2, 12, 1, 6, seed=9)
+    ids = oracle.route(oracle.logits(inp["x"], inp["w_router"]), 2, oracle.SIGMOID, 1)["ids"]
+    dy = RNG.normal(size=(6, 8))
+    full = oracle.backward(inp, ids, dy, oracle.SIGMOID, 1)
+    only = oracle.backward(inp, ids, dy, oracle.SIGMOID, 1, weights=False)
+    assert set(only) == {"dx"}
+    np.testing.assert_array_equal(only["dx"], full["dx"])
