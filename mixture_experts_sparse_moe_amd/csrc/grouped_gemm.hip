@@ -1049,12 +1049,10 @@ hipError_t launch_bf16_persistent(const GemmGroup& g, hipStream_t s) {
     constexpr int BN = DUAL ? 128 : 256;
     // one instantiation per tile order: a runtime choice inside the kernel
     // costs the K loop a compiler-inserted wait on the loads in flight
-    if constexpr (!DUAL) {
-        if (g.aligned_bands) {
-            hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<false, true>), dim3(persistent_grid()), dim3(512),
-                                  0, s, g.t_start, g.t_stop, 0, g, g.N / BN);
-            return hipGetLastError();
-        }
+    if (g.aligned_bands) {
+        hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<DUAL, true>), dim3(persistent_grid()), dim3(512),
+                              0, s, g.t_start, g.t_stop, 0, g, g.N / BN);
+        return hipGetLastError();
     }
     hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<DUAL, false>), dim3(persistent_grid()), dim3(512), 0, s,
                           g.t_start, g.t_stop, 0, g, g.N / BN);

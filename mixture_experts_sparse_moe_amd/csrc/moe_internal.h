@@ -69,7 +69,7 @@ struct GemmGroup {
     int N, K;
     int splitk = 1;         // single bf16 only: K cut into splitk ranges, one C slice each
     int64_t part_stride = 0;// elements between C slices when splitk > 1
-    bool aligned_bands = false; // single bf16: tile bands follow group boundaries
+    bool aligned_bands = false; // bf16 persistent kernel: tile bands follow group boundaries
     bool skinny = false;    // bf16, few rows per group: 32-row tiles streaming the weights
     hipEvent_t t_start = nullptr, t_stop = nullptr;  // recorded when the kernel starts / ends
     // fp32 products (single bf16 GEMM on the persistent kernel):
