@@ -480,10 +480,14 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
 
     // routing groups of the forward's ids
     MOE_TRY(run_dispatch(c, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s));
-    // a = x W_gate^T, u = x W_up^T on the grouped rows (the forward's GEMM)
+    // a = x W_gate^T, u = x W_up^T on the grouped rows (the forward's GEMM, with
+    // its expert-aligned tile order when experts hold several M tiles)
+    const bool aligned = (int64_t)P >= (int64_t)640 * E;
     GemmGroup ga{x, sorted, k, offsets, E, P, wg, nullptr, A, f, d};
+    ga.aligned_bands = aligned;
     MOE_HIP(launch_grouped_gemm(ga, false, bf16, s));
     GemmGroup gu{x, sorted, k, offsets, E, P, wu, nullptr, U, f, d};
+    gu.aligned_bands = aligned;
     MOE_HIP(launch_grouped_gemm(gu, false, bf16, s));
     if (pl.fast) {
         const int64_t Q = pl.Q;
@@ -494,6 +498,7 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
         // dH' = dy W_down: W_down^T [E, f, d] makes the contraction K-contiguous
         MOE_HIP(launch_transpose_bf16(wd, (int64_t)d * f, f, d, f, E, WdT, (int64_t)f * d, d, 0, s));
         GemmGroup g1 = f32_gemm(dy, sorted, k, offsets, E, P, WdT, dHp, f, f, d);
+        g1.aligned_bands = aligned;
         MOE_HIP(launch_grouped_gemm(g1, false, true, s));
         // h, dg, [da | du] per pair
         BwdPairArgs pa{sorted, offsets, E, k, gates, A, U, dHp, H, DA, static_cast<char*>(DA) + f * w, dgate,
