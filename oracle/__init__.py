@@ -67,7 +67,7 @@ def lib():
         L.oracle_forward_tokens.restype = i32
         L.oracle_forward_expert_loop.argtypes = ([i64] + [i32] * 7 + [vp] * 7 + [vp, vp, vp, i32])
         L.oracle_forward_expert_loop.restype = i32
-        L.oracle_backward.argtypes = [i64] + [i32] * 9 + [vp] * 8 + [vp, vp] + [vp] * 8
+        L.oracle_backward.argtypes = [i64] + [i32] * 9 + [vp] * 8 + [vp, vp] + [vp] * 8 + [vp]
         L.oracle_backward.restype = i32
         L.oracle_backward_weight_samples.argtypes = ([i64] + [i32] * 8 + [vp] * 8 + [vp, vp, i32] + [vp] * 5)
         L.oracle_backward_weight_samples.restype = i32
@@ -262,11 +262,13 @@ def forward(inp: dict, k: int, score_fn: int = SOFTMAX, renormalize: int = 1,
 
 
 def backward(inp: dict, ids: np.ndarray, dy: np.ndarray, score_fn: int = SOFTMAX,
-             renormalize: int = 1, weights: bool = True) -> dict:
+             renormalize: int = 1, weights: bool = True, keep=None) -> dict:
     """Gradients of L = sum(dy * y) for the routing ``ids`` [T,k] (held fixed):
     dx, dw_router, dw_gate, dw_up, dw_down (and ds_gate, ds_up, ds_down with a
     shared expert), fp64, by the chain rule written out per token.  With
-    weights=False only dx (each token's row depends on that token alone)."""
+    weights=False only dx (each token's row depends on that token alone).
+    keep [T,k] (bool, optional): False marks pairs an expert capacity dropped
+    (as in forward_tokens), which add nothing to y."""
     x = _c(inp["x"])
     wr, wg, wu, wd = (_c(inp[n]) for n in ("w_router", "w_gate", "w_up", "w_down"))
     sg, su, sd = (_c(inp.get(n)) for n in ("ws_gate", "ws_up", "ws_down"))
@@ -284,11 +286,13 @@ def backward(inp: dict, ids: np.ndarray, dy: np.ndarray, score_fn: int = SOFTMAX
     if S and weights:
         out.update(ds_gate=np.empty((f_s, d)), ds_up=np.empty((f_s, d)), ds_down=np.empty((d, f_s)))
     wp = (lambda n: out[n].ctypes.data) if weights else (lambda n: None)
+    kp = None if keep is None else np.ascontiguousarray(np.asarray(keep).reshape(T, k), dtype=np.int32)
     rc = lib().oracle_backward(T, d, E, k, f, S, f_s, score_fn, renormalize, _dtype_of(x), x.ctypes.data,
                                wr.ctypes.data, wg.ctypes.data, wu.ctypes.data, wd.ctypes.data, _ptr(sg),
                                _ptr(su), _ptr(sd), ids.ctypes.data, dy.ctypes.data,
                                out["dx"].ctypes.data, *(wp(n) for n in ("dw_router", "dw_gate", "dw_up", "dw_down")),
-                               *((wp(n) for n in ("ds_gate", "ds_up", "ds_down")) if S else (None,) * 3))
+                               *((wp(n) for n in ("ds_gate", "ds_up", "ds_down")) if S else (None,) * 3),
+                               None if kp is None else kp.ctypes.data)
     if rc:
         raise ValueError(f"oracle_backward failed ({rc})")
     return out

@@ -376,13 +376,15 @@ int oracle_forward_expert_loop(int64_t T, int d, int E, int k, int f, int num_sh
  * "Mixture-of-Experts Internals", sec. 2.2.)
  * Outputs (fp64, overwritten): dx [T,d], dwr [E,d], dwg, dwu [E,f,d],
  * dwd [E,d,f], dsg, dsu [f_s,d], dsd [d,f_s] (the last three when
- * num_shared).  Serial over tokens (the weight gradients are sums over them).
+ * num_shared).  keep [T*k] (nullable): 0 marks a pair an expert capacity
+ * dropped, as in oracle_forward_tokens.  Serial over tokens (the weight
+ * gradients are sums over them).
  */
 int oracle_backward(int64_t T, int d, int E, int k, int f, int num_shared, int f_s, int score_fn,
                     int renorm, int dtype, const void* x, const void* w_r, const void* wg,
                     const void* wu, const void* wd, const void* sg, const void* su, const void* sd,
                     const int32_t* ids, const double* dy, double* dx, double* dwr, double* dwg,
-                    double* dwu, double* dwd, double* dsg, double* dsu, double* dsd) {
+                    double* dwu, double* dwd, double* dsg, double* dsu, double* dsd, const int32_t* keep) {
     if (k < 1 || k > E) return -2;
     /* dwr == NULL: dx only (every weight gradient pointer ignored, nothing summed into them) */
     const int wgrads = dwr != NULL;
@@ -428,10 +430,15 @@ int oracle_backward(int64_t T, int d, int E, int k, int f, int num_shared, int f
         }
         if (err) break;
         for (int j = 0; j < k; ++j) g[j] = renorm ? s[ids[t * k + j]] / S : s[ids[t * k + j]];
-        /* experts */
+        /* experts; a pair the capacity dropped adds nothing to y, so its gate
+           gets no gradient and its expert none from it */
         for (int j = 0; j < k; ++j) {
             int e = ids[t * k + j];
             int64_t win = (int64_t)e * f * d, wdn = (int64_t)e * d * f;
+            if (keep && !keep[t * k + j]) {
+                dg[j] = 0.0;
+                continue;
+            }
             for (int r = 0; r < f; ++r) {
                 double aa = 0.0, bb = 0.0;
                 for (int c = 0; c < d; ++c) {

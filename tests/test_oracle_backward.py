@@ -127,3 +127,47 @@ def test_dx_only_equals_full_backward():
     only = oracle.backward(inp, ids, dy, oracle.SIGMOID, 1, weights=False)
     assert set(only) == {"dx"}
     np.testing.assert_array_equal(only["dx"], full["dx"])
+
+
+def _loss_keep(inp, ids, dy, score_fn, renorm, keep):
+    T = inp["x"].shape[0]
+    y = oracle.forward_tokens(inp, ids.shape[1], np.arange(T), score_fn, renorm, forced_ids=ids, keep=keep)["y"]
+    return float(np.sum(dy * y))
+
+
+@pytest.mark.parametrize("score_fn,renorm,S", [(oracle.SOFTMAX, 1, 1), (oracle.SIGMOID, 1, 0), (oracle.SOFTMAX, 0, 0)])
+def test_capacity_drops_match_finite_differences(score_fn, renorm, S):
+    """Pairs an expert capacity dropped add nothing to y: the backward with
+    the same keep mask matches central finite differences of the forward
+    with that mask, for every input and weight tensor."""
+    T, d, E, k, f = 8, 8, 4, 2, 12
+    inp = _inputs(T, d, E, k, f, S, 4 if S else 0, seed=11)
+    for n in ("x", "w_router"):
+        inp[n] = inp[n] * 2.0
+    ids = oracle.route(oracle.logits(inp["x"], inp["w_router"]), k, score_fn, renorm)["ids"]
+    keep = (oracle.dispatch(ids, E, 3)["pair_pos"] >= 0).reshape(T, k)
+    assert 0 < keep.sum() < T * k            # some pairs dropped, some kept
+    dy = RNG.normal(size=(T, d))
+    g = oracle.backward(inp, ids, dy, score_fn, renorm, keep=keep)
+    eps = 1e-6
+    for name, gname in GRAD_OF.items():
+        if inp.get(name) is None:
+            continue
+        v = RNG.normal(size=inp[name].shape)
+        plus, minus = dict(inp), dict(inp)
+        plus[name] = inp[name] + eps * v
+        minus[name] = inp[name] - eps * v
+        fd = (_loss_keep(plus, ids, dy, score_fn, renorm, keep) -
+              _loss_keep(minus, ids, dy, score_fn, renorm, keep)) / (2 * eps)
+        an = float(np.sum(g[gname] * v))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), f"{name}: finite difference {fd} vs gradient {an}"
+
+
+def test_keep_all_equals_plain_backward():
+    inp = _inputs(6, 8, 5, 2, 12, 1, 6, seed=12)
+    ids = oracle.route(oracle.logits(inp["x"], inp["w_router"]), 2)["ids"]
+    dy = RNG.normal(size=(6, 8))
+    a = oracle.backward(inp, ids, dy)
+    b = oracle.backward(inp, ids, dy, keep=np.ones((6, 2), bool))
+    for n in a:
+        np.testing.assert_array_equal(a[n], b[n])

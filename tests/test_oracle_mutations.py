@@ -36,6 +36,7 @@ MUTATIONS = {
                              "dgj_dlm = dse_dlm / S + s[e] * dS_dlm / (S * S);"),
     "router_grad_transposed": ("dxt[c] += widen(w_r, dtype, (int64_t)m * d + c) * dl[m];",
                                "dxt[c] += widen(w_r, dtype, (int64_t)c * E + m) * dl[m];"),
+    "backward_ignores_drops": ("            if (keep && !keep[t * k + j]) {", "            if (0) {"),
     "shared_grad_ungated_missing": ("for (int r = 0; r < f_s; ++r) dsd[(int64_t)c * f_s + r] += dyt[c] * h[r];",
                                     "for (int r = 0; r < f_s; ++r) dsd[(int64_t)c * f_s + r] += 0.5 * dyt[c] * h[r];"),
 }
