@@ -214,7 +214,7 @@ int moe_forward_staged(const moe_config* cfg, const void* x, const void* w_route
  *   dws_gate, dws_up [d_ff_s,d]; dws_down [d,d_ff_s] out, nullable iff
  *                                    num_shared == 0
  * All gradients are fp32 and overwritten (not accumulated).  The plain layer
- * only (no moe_options).  The expert pre-activations are recomputed, nothing
+ * (moe_backward_ex below adds an expert capacity).  The expert pre-activations are recomputed, nothing
  * is kept from the forward but its routing.  Sums run in a fixed order, no
  * atomics: the result is deterministic.  ws: at least
  * moe_backward_workspace_bytes(cfg) bytes; for bf16 layers whose d and d_ff
@@ -284,6 +284,22 @@ int moe_forward_ex(const moe_config* cfg, const moe_options* opts, const void* x
                    const void* ws_up, const void* ws_down, void* y, int32_t* topk_ids_out,
                    float* topk_weights_out, int32_t* expert_counts_out, void* ws, size_t ws_bytes,
                    void* stream);
+
+/* moe_backward with options, for training with an expert capacity ("8.6
+ * Mixture of Experts", sec. 3.2; "Mixture-of-Experts, from the router to the
+ * all-to-all", Capacity and token dropping): with expert_capacity > 0 the pairs past each
+ * expert's first expert_capacity (in pair order, as moe_forward_ex dropped
+ * them) added nothing to y, so they get no gradient: their gates' dL/dg is 0
+ * and their experts get nothing from them; the router still gets the gates'
+ * full Jacobian.  expert_bias and bias_on_scores have no effect (the routing
+ * is an input); router_stats must be NULL (MOE_ERR_UNSUPPORTED).  Same
+ * arguments, workspace and errors as moe_backward; NULL opts is moe_backward. */
+int moe_backward_ex(const moe_config* cfg, const moe_options* opts, const void* x, const void* w_router,
+                    const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
+                    const void* ws_up, const void* ws_down, const void* dy, const int32_t* topk_ids,
+                    const float* topk_weights, float* dx, float* dw_router, float* dw_gate, float* dw_up,
+                    float* dw_down, float* dws_gate, float* dws_up, float* dws_down, void* ws, size_t ws_bytes,
+                    void* stream);
 
 #ifdef __cplusplus
 }

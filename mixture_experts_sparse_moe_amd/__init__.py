@@ -31,7 +31,7 @@ MOE_F32, MOE_BF16 = 0, 1
 EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_staged",
            "moe_route_ex", "moe_dispatch_ex", "moe_forward_ex", "moe_backward_workspace_bytes",
-           "moe_backward")
+           "moe_backward", "moe_backward_ex")
 MOE_NUM_STAGES = 7
 STAGE_NAMES = ("route", "dispatch", "gate_up_gemm", "down_gemm", "shared_gate_up", "shared_down",
                "combine")
@@ -119,6 +119,8 @@ def lib():
         L.moe_backward_workspace_bytes.restype = sz
         L.moe_backward.argtypes = [cfgp] + [vp] * 20 + [sz, vp]
         L.moe_backward.restype = i32
+        L.moe_backward_ex.argtypes = [cfgp, optp] + [vp] * 20 + [sz, vp]
+        L.moe_backward_ex.restype = i32
         _lib = L
     return _lib
 
@@ -370,10 +372,8 @@ def moe_backward_workspace_bytes(cfg: MoeConfig) -> int:
     return int(lib().moe_backward_workspace_bytes(ctypes.byref(cfg)))
 
 
-def moe_backward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, dy, topk_ids,
-                 topk_weights, dx, dw_router, dw_gate, dw_up, dw_down, dws_gate=None, dws_up=None,
-                 dws_down=None, ws=None, stream=None):
-    """Gradients (fp32) of the layer for the forward's routing."""
+def _check_backward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, dy, topk_ids,
+                    topk_weights, dx, dw_router, dw_gate, dw_up, dw_down, dws_gate, dws_up, dws_down):
     torch = _torch()
     T, d, E, k, f, fs = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k, cfg.d_ff, cfg.d_ff_shared
     dt, dev = _act_dtype(cfg), x.device
@@ -393,11 +393,36 @@ def moe_backward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down
         _check(dws_gate, "dws_gate", (fs, d), f32, dev)
         _check(dws_up, "dws_up", (fs, d), f32, dev)
         _check(dws_down, "dws_down", (d, fs), f32, dev)
+    return dev
+
+
+def moe_backward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, dy, topk_ids,
+                 topk_weights, dx, dw_router, dw_gate, dw_up, dw_down, dws_gate=None, dws_up=None,
+                 dws_down=None, ws=None, stream=None):
+    """Gradients (fp32) of the layer for the forward's routing."""
+    _check_backward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, dy, topk_ids, topk_weights,
+                    dx, dw_router, dw_gate, dw_up, dw_down, dws_gate, dws_up, dws_down)
     _rc(lib().moe_backward(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                            _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(dy), _ptr(topk_ids),
                            _ptr(topk_weights), _ptr(dx), _ptr(dw_router), _ptr(dw_gate), _ptr(dw_up),
                            _ptr(dw_down), _ptr(dws_gate), _ptr(dws_up), _ptr(dws_down), _ptr(ws),
                            _ws_bytes(ws), _stream(stream)), "moe_backward")
+
+
+def moe_backward_ex(cfg, opts, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, dy, topk_ids,
+                    topk_weights, dx, dw_router, dw_gate, dw_up, dw_down, dws_gate=None, dws_up=None,
+                    dws_down=None, ws=None, stream=None):
+    """moe_backward for a forward that ran with options: an expert capacity
+    leaves the dropped pairs without gradient (opts.expert_capacity is the one
+    field it reads; router_stats must be unset)."""
+    dev = _check_backward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, dy, topk_ids,
+                          topk_weights, dx, dw_router, dw_gate, dw_up, dw_down, dws_gate, dws_up, dws_down)
+    _check_opts(cfg, opts, dev)
+    _rc(lib().moe_backward_ex(ctypes.byref(cfg), _opts(opts), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up),
+                              _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(dy), _ptr(topk_ids),
+                              _ptr(topk_weights), _ptr(dx), _ptr(dw_router), _ptr(dw_gate), _ptr(dw_up),
+                              _ptr(dw_down), _ptr(dws_gate), _ptr(dws_up), _ptr(dws_down), _ptr(ws),
+                              _ws_bytes(ws), _stream(stream)), "moe_backward_ex")
 
 
 def alloc_backward_workspace(cfg, device="cuda"):

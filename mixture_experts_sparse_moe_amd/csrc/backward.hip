@@ -503,6 +503,11 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const float* dl, cons
     }
 }
 
+// p[0 .. n) = 0 (a fill kernel rather than a memset, so the call stays capturable).
+__global__ __launch_bounds__(256) void fill_zero_f32_kernel(float* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
+}
+
 // dst[j] = sum over chunks c (in order) of part[c * n + j].
 __global__ __launch_bounds__(256) void sum_chunks_kernel(const float* part, int chunks, int64_t n, float* dst) {
     const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -715,6 +720,13 @@ hipError_t launch_bwd_token_sum(const float* dxp, const int32_t* pair_pos, int T
                                 hipStream_t s, int splitk, int64_t part_stride) {
     if (T <= 0) return hipSuccess;
     hipLaunchKernelGGL(bwd_token_sum_kernel, dim3(T), dim3(256), 0, s, dxp, pair_pos, k, d, dx, splitk, part_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(fill_zero_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
     return hipGetLastError();
 }
 

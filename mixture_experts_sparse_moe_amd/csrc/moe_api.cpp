@@ -462,7 +462,8 @@ TransposeRowsArgs rows_t(const void* src, int64_t ld_src, int C, const int32_t* 
 int run_backward(const moe_config* c, const void* x, const void* wr, const void* wg, const void* wu,
                  const void* wd, const void* sg, const void* su, const void* sd, const void* dy,
                  const int32_t* ids, const float* gates, float* dx, float* dwr, float* dwg, float* dwu,
-                 float* dwd, float* dsg, float* dsu, float* dsd, void* ws, hipStream_t s) {
+                 float* dwd, float* dsg, float* dsu, float* dsd, void* ws, hipStream_t s,
+                 int cap = 0x7FFFFFFF) {
     const BwdPlan pl = bwd_plan(c);
     const BwdLayout L = bwd_layout(c);
     const bool bf16 = c->dtype == MOE_BF16;
@@ -478,8 +479,11 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
     float *dHp = at<float>(ws, L.dHp), *dXp = at<float>(ws, L.dXp), *dgate = at<float>(ws, L.dgate);
     float *logits = at<float>(ws, L.logits), *dl = at<float>(ws, L.dl);
 
-    // routing groups of the forward's ids
-    MOE_TRY(run_dispatch(c, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s));
+    // routing groups of the forward's ids; pairs past an expert's capacity are
+    // left out of the groups (pair_pos -1), as in the forward
+    MOE_TRY(run_dispatch(c, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s, cap));
+    // a dropped pair's gate gets no gradient (the pair kernel writes kept pairs only)
+    if ((int64_t)cap < P) MOE_HIP(launch_fill_zero_f32(dgate, P, s));
     // a = x W_gate^T, u = x W_up^T on the grouped rows (the forward's GEMM, with
     // its expert-aligned tile order when experts hold several M tiles)
     const bool aligned = (int64_t)P >= (int64_t)640 * E;
@@ -784,7 +788,20 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
                  const void* ws_down, const void* dy, const int32_t* topk_ids, const float* topk_weights,
                  float* dx, float* dw_router, float* dw_gate, float* dw_up, float* dw_down, float* dws_gate,
                  float* dws_up, float* dws_down, void* ws, size_t ws_bytes, void* stream) {
+    return moe_backward_ex(cfg, nullptr, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, dy, topk_ids,
+                           topk_weights, dx, dw_router, dw_gate, dw_up, dw_down, dws_gate, dws_up, dws_down, ws,
+                           ws_bytes, stream);
+}
+
+int moe_backward_ex(const moe_config* cfg, const moe_options* opts, const void* x, const void* w_router,
+                    const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
+                    const void* ws_up, const void* ws_down, const void* dy, const int32_t* topk_ids,
+                    const float* topk_weights, float* dx, float* dw_router, float* dw_gate, float* dw_up,
+                    float* dw_down, float* dws_gate, float* dws_up, float* dws_down, void* ws, size_t ws_bytes,
+                    void* stream) {
     MOE_TRY(validate_cfg(cfg));
+    MOE_TRY(validate_opts(opts));
+    if (opts && opts->router_stats) return MOE_ERR_UNSUPPORTED;     // the backward computes no statistics
     const bool empty = cfg->num_tokens == 0;
     for (const void* p : {x, dy, (const void*)topk_ids, (const void*)topk_weights, (const void*)dx})
         MOE_TRY(check_ptr(p, empty));
@@ -801,7 +818,7 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
     // T = 0 still runs: the weight gradients are written as zeros
     return run_backward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, dy, topk_ids,
                         topk_weights, dx, dw_router, dw_gate, dw_up, dw_down, dws_gate, dws_up, dws_down, ws,
-                        static_cast<hipStream_t>(stream));
+                        static_cast<hipStream_t>(stream), capacity_of(opts));
 }
 
 int moe_forward(const moe_config* cfg, const void* x, const void* w_router, const void* w_gate,

@@ -167,6 +167,7 @@ hipError_t launch_bwd_router(const BwdRouterArgs& b, hipStream_t s);
 hipError_t launch_bwd_token_sum(const float* dxp, const int32_t* pair_pos, int T, int k, int d, float* dx,
                                 hipStream_t s, int splitk = 1, int64_t part_stride = 0);
 
+hipError_t launch_fill_zero_f32(float* p, int64_t n, hipStream_t s);
 // dW_r [E, d] = dl^T x (x bf16 or fp32) over token chunks; part holds
 // router_wgrad_chunks(T, d, E) x E x d floats.
 int router_wgrad_chunks(int T, int d, int E);

@@ -180,3 +180,23 @@ def test_capacity_helper_matches_page():
     assert moe.capacity(4096, 8, 64, 1.0) == 512
     assert moe.capacity(4096, 8, 64, 1.25) == 640
     assert moe.capacity(10, 2, 3, 1.0) == 7
+
+
+def test_backward_options_are_validated_before_launch():
+    """moe_backward_ex reads the capacity only; statistics are refused, bad
+    options and a short workspace are reported before anything is enqueued."""
+    c = cfg()
+    O = moe.MoeOptions
+    L = moe.lib()
+    need = moe.moe_backward_workspace_bytes(c)
+    assert need > 0 and need % 256 == 0
+
+    def bwd(opts, ws=FAKE, ws_bytes=1 << 40):
+        return L.moe_backward_ex(ctypes.byref(c), ctypes.byref(opts) if opts is not None else None,
+                                 *([FAKE] * 16), None, None, None, ws, ws_bytes, None)
+
+    assert bwd(O(None, 0, 0, FAKE, 0.01)) == moe.MOE_ERR_UNSUPPORTED       # no statistics in the backward
+    assert bwd(O(None, 2, 0, None, 0.0)) == moe.MOE_ERR_UNSUPPORTED        # bias space 0/1
+    assert bwd(O(FAKE + 4, 0, 0, None, 0.0)) == moe.MOE_ERR_ALIGN         # bias alignment
+    assert bwd(O(None, 0, 64, None, 0.0), ws=FAKE, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert bwd(None, ws=None) == moe.MOE_ERR_WORKSPACE

@@ -55,7 +55,7 @@ NAMES = [("dx", "dx"), ("dw_router", "dw_router"), ("dw_gate", "dw_gate"), ("dw_
          ("dw_down", "dw_down"), ("dws_gate", "ds_gate"), ("dws_up", "ds_up"), ("dws_down", "ds_down")]
 
 
-def run_backward(L, ids, wts, dy_d):
+def run_backward(L, ids, wts, dy_d, opts=None):
     import mixture_experts_sparse_moe_amd as moe
     t = torch()
     sh, dv = L.sh, L.d
@@ -68,10 +68,13 @@ def run_backward(L, ids, wts, dy_d):
         out.update(dws_gate=t.full((fs, sh.d), 7.0, **f32), dws_up=t.full((fs, sh.d), 7.0, **f32),
                    dws_down=t.full((sh.d, fs), 7.0, **f32))
     ws = moe.alloc_backward_workspace(L.cfg)
-    moe.moe_backward(L.cfg, dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], dv["ws_gate"],
-                     dv["ws_up"], dv["ws_down"], dy_d, ids, wts, out["dx"], out["dw_router"], out["dw_gate"],
-                     out["dw_up"], out["dw_down"], out.get("dws_gate"), out.get("dws_up"), out.get("dws_down"),
-                     ws=ws)
+    args = (dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], dv["ws_gate"], dv["ws_up"],
+            dv["ws_down"], dy_d, ids, wts, out["dx"], out["dw_router"], out["dw_gate"], out["dw_up"],
+            out["dw_down"], out.get("dws_gate"), out.get("dws_up"), out.get("dws_down"))
+    if opts is None:
+        moe.moe_backward(L.cfg, *args, ws=ws)
+    else:
+        moe.moe_backward_ex(L.cfg, opts, *args, ws=ws)
     return out
 
 
@@ -182,3 +185,49 @@ def test_backward_full_size_sampled(name):
         err = np.abs(got - want).max()
         say(f"[{n}] max|err| {err:.3e}, max|ref| {scale:.3e}")
         assert err <= tau * scale, f"{n}: max|err| {err} > {tau} * {scale}"
+
+
+
+CAPACITY = {
+    # (shape, capacity factor or fixed capacity)
+    "bf16_w256_e8_k2_zipf": (S("b", T=300, d=256, E=8, k=2, d_ff=512, zipf_s=1.2), 0.8),
+    "bf16_w256_decode_e8_k2": (S("b", T=16, d=512, E=8, k=2, d_ff=256), 2),
+    "bf16_e16_k4_sigmoid_shared": (S("b", T=150, d=128, E=16, k=4, d_ff=128, num_shared=1, d_ff_shared=128,
+                                     score_fn=synth.SIGMOID), 1.0),
+    "fp32_e8_k2": (S("b", T=64, d=64, E=8, k=2, d_ff=128, dtype=synth.F32), 0.75),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CAPACITY))
+def test_backward_with_capacity_matches_oracle(name):
+    """moe_backward_ex with an expert capacity: the pairs each expert drops
+    (past its first C in pair order) get no gradient; every gradient against
+    the oracle's backward under the same keep mask (from the oracle's own
+    dispatch of the GPU's ids)."""
+    import mixture_experts_sparse_moe_amd as moe
+    sh, cf = CAPACITY[name]
+    cap = cf if isinstance(cf, int) else moe.capacity(sh.T, sh.k, sh.E, cf)
+    say(f"[case] backward with capacity {cap}: {name} {sh}")
+    inp = synth.make_inputs(sh, 23)
+    L = DeviceLayer(sh, inp)
+    st = L.steps()
+    dy_h = synth.normal(23, 99, sh.T * sh.d, 1.0, sh.dtype).reshape(sh.T, sh.d)
+    dy_ref = synth.bf16_to_f64(dy_h) if sh.dtype == synth.BF16 else dy_h.astype(np.float64)
+    opts = moe.MoeOptions.of(expert_capacity=cap)
+    out = run_backward(L, st["ids"], st["weights"], to_dev(dy_h), opts)
+    out2 = run_backward(L, st["ids"], st["weights"], to_dev(dy_h), opts)
+    torch().cuda.synchronize()
+    gids = to_host(st["ids"])
+    keep = (oracle.dispatch(gids, sh.E, cap)["pair_pos"] >= 0).reshape(sh.T, sh.k)
+    dropped = int((~keep).sum())
+    assert dropped > 0, "the case must drop pairs"
+    ref = oracle.backward(inp, gids, dy_ref, sh.score_fn, sh.renormalize, keep=keep)
+    tau = TAU[sh.dtype]
+    worst = 0.0
+    for gname, rname in NAMES:
+        if gname not in out:
+            continue
+        got = to_host(out[gname]).astype(np.float64)
+        np.testing.assert_array_equal(got, to_host(out2[gname]), err_msg=f"{gname} not deterministic")
+        worst = max(worst, assert_close(got, ref[rname], tau, gname))
+    say(f"[ok] {dropped} of {sh.T * sh.k} pairs dropped; worst max|err|/max|ref| = {worst:.2e}")
