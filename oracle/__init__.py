@@ -8,9 +8,11 @@ Each wrapper below states the definition it evaluates; the C source
 (``moe_oracle.c``) cites the page and section of each step.
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests
-in ``tests/test_oracle_pins.py`` (closed forms, special cases that reduce to a
-dense softmax ensemble or a library routine, brute force over subsets, and
-the pages' printed counts).  None is "parity unpinned".
+in ``tests/test_oracle_pins.py``, ``tests/test_oracle_next.py`` and
+``tests/test_oracle_backward.py`` (closed forms, special cases that reduce to
+a dense softmax ensemble or a library routine, brute force over subsets, the
+pages' printed counts, and central finite differences of the forward for the
+backward).  None is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -91,6 +93,13 @@ def _dtype_of(a: np.ndarray) -> int:
 
 def _c(a):
     return None if a is None else np.ascontiguousarray(a)
+
+
+def _f64(a: np.ndarray) -> np.ndarray:
+    """The stored values widened exactly to fp64 (bf16 bit patterns, fp32 or fp64)."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
 
 
 def logits(x: np.ndarray, w_router: np.ndarray, rows: slice | None = None,
@@ -178,6 +187,40 @@ def router_stats(scores: np.ndarray, ids: np.ndarray, score_fn: int = SOFTMAX,
     return dict(f=f, P=P, l_aux=l_aux, max_over_mean=float(n.max() / n.mean()), counts=n)
 
 
+def aux_loss_logit_grad(lg: np.ndarray, ids: np.ndarray, score_fn: int = SOFTMAX,
+                        alpha: float = 1.0) -> np.ndarray:
+    """dL_aux/dl [T,E] for the load-balancing loss of router_stats,
+    L_aux = alpha E sum_e f_e P_e ("8.6 Mixture of Experts", sec. 3.1: f_e
+    counts the hard assignment and carries no gradient, so the loss trains the
+    router through P_e alone).  With p_t the router probabilities of token t
+    (softmax over the logits, or the sigmoids normalised over the experts) and
+    P_e = (1/T) sum_t p_te:
+        dL_aux/dl_te' = (alpha E / T) sum_e f_e dp_te/dl_te',
+    the Jacobian written out: softmax dp_e/dl_e' = p_e (delta_ee' - p_e');
+    normalised sigmoid p_e = s_e / S, s = sigmoid(l), S = sum s, by the
+    quotient rule dp_e/dl_e' = (delta_ee' s_e (1 - s_e) S - s_e s_e' (1 - s_e')) / S^2."""
+    lg = np.asarray(lg, dtype=np.float64)
+    T, E = lg.shape
+    n = np.zeros(E)
+    for t in range(ids.shape[0]):
+        for j in range(ids.shape[1]):
+            n[ids[t, j]] += 1.0
+    f = n / T
+    out = np.empty((T, E))
+    for t in range(T):
+        if score_fn == SOFTMAX:
+            p = np.exp(lg[t] - lg[t].max())
+            p /= p.sum()
+            J = np.diag(p) - np.outer(p, p)
+        else:
+            sg = 1.0 / (1.0 + np.exp(-lg[t]))
+            S = sg.sum()
+            ds = sg * (1.0 - sg)
+            J = (np.diag(ds) * S - np.outer(sg, ds)) / (S * S)
+        out[t] = alpha * E / T * (f @ J)
+    return out
+
+
 def expert_rows(e: int, x: np.ndarray, rows: np.ndarray, w_gate, w_up, w_down,
                 want_h: bool = False, nthreads: int | None = None):
     """Expert e's SwiGLU on token rows ``rows``: (h [n,d_ff] or None, o [n,d])."""
@@ -262,13 +305,16 @@ def forward(inp: dict, k: int, score_fn: int = SOFTMAX, renormalize: int = 1,
 
 
 def backward(inp: dict, ids: np.ndarray, dy: np.ndarray, score_fn: int = SOFTMAX,
-             renormalize: int = 1, weights: bool = True, keep=None) -> dict:
+             renormalize: int = 1, weights: bool = True, keep=None, aux_alpha: float = 0.0) -> dict:
     """Gradients of L = sum(dy * y) for the routing ``ids`` [T,k] (held fixed):
     dx, dw_router, dw_gate, dw_up, dw_down (and ds_gate, ds_up, ds_down with a
     shared expert), fp64, by the chain rule written out per token.  With
     weights=False only dx (each token's row depends on that token alone).
     keep [T,k] (bool, optional): False marks pairs an expert capacity dropped
-    (as in forward_tokens), which add nothing to y."""
+    (as in forward_tokens), which add nothing to y.  aux_alpha != 0 adds the
+    gradient of the load-balancing loss L_aux (router_stats, same alpha) to dx
+    and dw_router: dl_aux = aux_loss_logit_grad, dx += dl_aux W_r,
+    dw_router += dl_aux^T x."""
     x = _c(inp["x"])
     wr, wg, wu, wd = (_c(inp[n]) for n in ("w_router", "w_gate", "w_up", "w_down"))
     sg, su, sd = (_c(inp.get(n)) for n in ("ws_gate", "ws_up", "ws_down"))
@@ -295,6 +341,11 @@ def backward(inp: dict, ids: np.ndarray, dy: np.ndarray, score_fn: int = SOFTMAX
                                None if kp is None else kp.ctypes.data)
     if rc:
         raise ValueError(f"oracle_backward failed ({rc})")
+    if aux_alpha:
+        dl = aux_loss_logit_grad(logits(x, wr), ids, score_fn, aux_alpha)
+        out["dx"] += dl @ _f64(wr)
+        if weights:
+            out["dw_router"] += dl.T @ _f64(x)
     return out
 
 

@@ -171,3 +171,65 @@ def test_keep_all_equals_plain_backward():
     b = oracle.backward(inp, ids, dy, keep=np.ones((6, 2), bool))
     for n in a:
         np.testing.assert_array_equal(a[n], b[n])
+
+
+def _l_aux(lg, ids, score_fn, alpha):
+    scores = oracle.route(lg, ids.shape[1], score_fn, 1, forced_ids=ids)["scores"]
+    return oracle.router_stats(scores, ids, score_fn, alpha)["l_aux"]
+
+
+@pytest.mark.parametrize("score_fn", [oracle.SOFTMAX, oracle.SIGMOID])
+def test_aux_loss_gradient_matches_finite_differences(score_fn):
+    """dL_aux/dl (the written-out probability Jacobian) against central finite
+    differences of router_stats' L_aux in random logit directions, the
+    assignment (hence f) held fixed."""
+    T, E, k = 7, 6, 2
+    lg = RNG.normal(size=(T, E)) * 1.5
+    ids = oracle.route(lg, k, score_fn)["ids"]
+    g = oracle.aux_loss_logit_grad(lg, ids, score_fn, 0.3)
+    eps = 1e-6
+    for _ in range(4):
+        v = RNG.normal(size=lg.shape)
+        fd = (_l_aux(lg + eps * v, ids, score_fn, 0.3) - _l_aux(lg - eps * v, ids, score_fn, 0.3)) / (2 * eps)
+        an = float(np.sum(g * v))
+        assert abs(fd - an) <= 1e-8 * max(1.0, abs(an)), (fd, an)
+
+
+def test_aux_loss_gradient_vanishes_for_balanced_assignment():
+    """With every expert picked equally often (f_e the same for all e), L_aux
+    = alpha E f sum_e P_e = alpha E f, a constant: the probabilities of each
+    token sum to 1 whatever the logits, so the gradient is zero."""
+    T, E, k = 4, 8, 2
+    lg = RNG.normal(size=(T, E)) * 2.0
+    ids = np.array([[0, 1], [2, 3], [4, 5], [6, 7]])     # f_e = 1/4 for every e
+    for score_fn in (oracle.SOFTMAX, oracle.SIGMOID):
+        g = oracle.aux_loss_logit_grad(lg, ids, score_fn, 1.0)
+        assert np.abs(g).max() < 1e-15
+
+
+@pytest.mark.parametrize("score_fn,S", [(oracle.SOFTMAX, 1), (oracle.SIGMOID, 0)])
+def test_backward_with_aux_loss_matches_finite_differences(score_fn, S):
+    """L = sum(dy * y) + L_aux: the backward with aux_alpha against finite
+    differences of the forward plus router_stats' L_aux, in x and W_r (the
+    expert weights do not enter L_aux)."""
+    T, d, E, k, f = 6, 8, 5, 2, 12
+    inp = _inputs(T, d, E, k, f, S, 4 if S else 0, seed=13)
+    for n in ("x", "w_router"):
+        inp[n] = inp[n] * 2.0
+    ids = oracle.route(oracle.logits(inp["x"], inp["w_router"]), k, score_fn, 1)["ids"]
+    dy = RNG.normal(size=(T, d))
+    alpha = 0.7
+    g = oracle.backward(inp, ids, dy, score_fn, 1, aux_alpha=alpha)
+
+    def loss(p):
+        return _loss(p, ids, dy, score_fn, 1) + _l_aux(oracle.logits(p["x"], p["w_router"]), ids, score_fn, alpha)
+
+    eps = 1e-6
+    for name, gname in (("x", "dx"), ("w_router", "dw_router")):
+        v = RNG.normal(size=inp[name].shape)
+        plus, minus = dict(inp), dict(inp)
+        plus[name] = inp[name] + eps * v
+        minus[name] = inp[name] - eps * v
+        fd = (loss(plus) - loss(minus)) / (2 * eps)
+        an = float(np.sum(g[gname] * v))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), f"{name}: finite difference {fd} vs gradient {an}"
