@@ -291,9 +291,16 @@ int moe_forward_ex(const moe_config* cfg, const moe_options* opts, const void* x
  * expert's first expert_capacity (in pair order, as moe_forward_ex dropped
  * them) added nothing to y, so they get no gradient: their gates' dL/dg is 0
  * and their experts get nothing from them; the router still gets the gates'
- * full Jacobian.  expert_bias and bias_on_scores have no effect (the routing
- * is an input); router_stats must be NULL (MOE_ERR_UNSUPPORTED).  Same
- * arguments, workspace and errors as moe_backward; NULL opts is moe_backward. */
+ * full Jacobian.  With aux_alpha != 0 the gradient of the load-balancing
+ * loss L_aux = aux_alpha E sum_e f_e P_e (as moe_options' statistics define
+ * it; "8.6 Mixture of Experts", sec. 3.1) is added to dx and dw_router: f_e
+ * counts the hard assignment (before any capacity drop) and carries no
+ * gradient, so the loss trains the router through P_e, the mean router
+ * probability (softmax, or the sigmoids normalised over the experts).
+ * expert_bias and bias_on_scores have no effect (the routing is an input);
+ * router_stats must be NULL (MOE_ERR_UNSUPPORTED); a non-finite aux_alpha is
+ * MOE_ERR_SHAPE.  Same arguments, workspace and errors as moe_backward; NULL
+ * opts is moe_backward. */
 int moe_backward_ex(const moe_config* cfg, const moe_options* opts, const void* x, const void* w_router,
                     const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
                     const void* ws_up, const void* ws_down, const void* dy, const int32_t* topk_ids,

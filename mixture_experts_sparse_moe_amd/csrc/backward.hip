@@ -424,6 +424,23 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(BwdRouterArgs b) {
     }
     if (b.score_fn == 1)
         for (int j = 0; j < b.k; ++j) ssum += 1.0f / (1.0f + expf(-l[id[j]]));
+    // load-balancing loss: the token's router probabilities p (softmax) or
+    // q = s / sum s (sigmoid s), and their mean fraction fbar = <f, p>
+    float amx = 0.0f, anorm = 1.0f, fbar = 0.0f;
+    if (b.aux_coef != 0.0f) {
+        if (b.score_fn == 0) {
+            amx = -__builtin_inff();
+            for (int m = 0; m < b.E; ++m) amx = fmaxf(amx, l[m]);
+            anorm = 0.0f;
+            for (int m = 0; m < b.E; ++m) anorm += expf(l[m] - amx);
+            for (int m = 0; m < b.E; ++m) fbar += (float)b.aux_counts[m] * b.inv_T * (expf(l[m] - amx) / anorm);
+        } else {
+            anorm = 0.0f;
+            for (int m = 0; m < b.E; ++m) anorm += 1.0f / (1.0f + expf(-l[m]));
+            for (int m = 0; m < b.E; ++m)
+                fbar += (float)b.aux_counts[m] * b.inv_T * (1.0f / (1.0f + expf(-l[m])) / anorm);
+        }
+    }
     for (int e = lane; e < b.E; e += 64) {
         int j = -1;
         for (int q = 0; q < b.k; ++q)
@@ -441,8 +458,32 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(BwdRouterArgs b) {
             const float ds = b.renorm ? (dg[j] - gdg) / ssum : dg[j];
             v = ds * sg * (1.0f - sg);
         }
+        if (b.aux_coef != 0.0f) {
+            // dL_aux/dl_e = aux_coef p_e (f_e - fbar); for the normalised sigmoid
+            // the Jacobian adds the factor (1 - s_e)
+            float pe;
+            if (b.score_fn == 0) {
+                pe = expf(l[e] - amx) / anorm;
+            } else {
+                const float sg = 1.0f / (1.0f + expf(-l[e]));
+                pe = sg / anorm * (1.0f - sg);
+            }
+            v += b.aux_coef * pe * ((float)b.aux_counts[e] * b.inv_T - fbar);
+        }
         dl[e] = v;
     }
+}
+
+__global__ __launch_bounds__(1024) void count_ids_kernel(const int32_t* ids, int64_t P, int E, int32_t* counts) {
+    __shared__ int hist[256];
+    for (int e = threadIdx.x; e < E; e += 1024) hist[e] = 0;
+    __syncthreads();
+    for (int64_t p = threadIdx.x; p < P; p += 1024) {
+        const int e = ids[p];
+        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 1024) counts[e] = hist[e];
 }
 
 // dx[t, :] = sum over the token's pairs, in slot order, of dXp[pair_pos].
@@ -720,6 +761,12 @@ hipError_t launch_bwd_token_sum(const float* dxp, const int32_t* pair_pos, int T
                                 hipStream_t s, int splitk, int64_t part_stride) {
     if (T <= 0) return hipSuccess;
     hipLaunchKernelGGL(bwd_token_sum_kernel, dim3(T), dim3(256), 0, s, dxp, pair_pos, k, d, dx, splitk, part_stride);
+    return hipGetLastError();
+}
+
+hipError_t launch_count_ids(const int32_t* ids, int64_t P, int E, int32_t* counts, hipStream_t s) {
+    if (E < 1 || E > 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(count_ids_kernel, dim3(1), dim3(1024), 0, s, ids, P, E, counts);
     return hipGetLastError();
 }
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstddef>
 #include <cstdint>
 
@@ -358,7 +359,7 @@ BwdPlan bwd_plan(const moe_config* c) {
 }
 
 struct BwdLayout {
-    size_t counts, offsets, sorted, pos, chunk, A, U, H, DA, DU, dHp, dO, dXp, dgate, logits, dl, rw;
+    size_t counts, offsets, sorted, pos, chunk, A, U, H, DA, DU, dHp, dO, dXp, dgate, logits, dl, rw, auxcnt;
     size_t As, Us, Hs, DAs, DUs, dHs;
     // fast path: DA and DU share rows [da | du] (DA), transposed operands
     size_t kofs, WdT, WguT, dOT, HT, DADUT, XgT, WsdT, WsguT, dyT, HsT, DADUsT, xT;
@@ -386,6 +387,7 @@ BwdLayout bwd_layout(const moe_config* c) {
     L.logits = take(T * E * 4);
     L.dl = take(T * E * 4);
     L.rw = take((size_t)router_wgrad_chunks((int)T, (int)d, (int)E) * E * d * 4);
+    L.auxcnt = take(E * 4);
     if (pl.fast) {
         L.DA = take(P * 2 * f * w);
         L.dXp = take((size_t)pl.xsplit * P * d * 4);
@@ -463,7 +465,7 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
                  const void* wd, const void* sg, const void* su, const void* sd, const void* dy,
                  const int32_t* ids, const float* gates, float* dx, float* dwr, float* dwg, float* dwu,
                  float* dwd, float* dsg, float* dsu, float* dsd, void* ws, hipStream_t s,
-                 int cap = 0x7FFFFFFF) {
+                 int cap = 0x7FFFFFFF, float aux_alpha = 0.0f) {
     const BwdPlan pl = bwd_plan(c);
     const BwdLayout L = bwd_layout(c);
     const bool bf16 = c->dtype == MOE_BF16;
@@ -558,13 +560,22 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
         w2.A = DU; w2.C = dwu;
         MOE_HIP(launch_grad_gemm(w2, true, false, bf16, bf16, s));
     }
-    // router: dl from dg (logits recomputed when the gates need them)
-    const bool need_logits = !(c->score_fn == MOE_SCORE_SOFTMAX && c->renormalize);
+    // router: dl from dg (logits recomputed when the gates or the
+    // load-balancing loss need them)
+    const bool aux = aux_alpha != 0.0f && T > 0;
+    const bool need_logits = !(c->score_fn == MOE_SCORE_SOFTMAX && c->renormalize) || aux;
     if (need_logits) {
         GradGemm gl = grad_gemm(x, d, wr, d, logits, E, T, E, d);
         MOE_HIP(launch_grad_gemm(gl, false, true, bf16, bf16, s));
     }
     BwdRouterArgs ra{ids, gates, dgate, need_logits ? logits : nullptr, dl, T, E, k, c->score_fn, c->renormalize};
+    if (aux) {
+        int32_t* cnt = at<int32_t>(ws, L.auxcnt);
+        MOE_HIP(launch_count_ids(ids, P, E, cnt, s));
+        ra.aux_counts = cnt;
+        ra.aux_coef = aux_alpha * (float)E / (float)T;
+        ra.inv_T = 1.0f / (float)T;
+    }
     MOE_HIP(launch_bwd_router(ra, s));
     MOE_HIP(launch_router_wgrad(dl, x, bf16, T, E, d, at<float>(ws, L.rw), dwr, s));
     GradGemm gx = grad_gemm(dl, E, wr, d, dx, d, T, d, E);
@@ -802,6 +813,7 @@ int moe_backward_ex(const moe_config* cfg, const moe_options* opts, const void* 
     MOE_TRY(validate_cfg(cfg));
     MOE_TRY(validate_opts(opts));
     if (opts && opts->router_stats) return MOE_ERR_UNSUPPORTED;     // the backward computes no statistics
+    if (opts && !std::isfinite(opts->aux_alpha)) return MOE_ERR_SHAPE;
     const bool empty = cfg->num_tokens == 0;
     for (const void* p : {x, dy, (const void*)topk_ids, (const void*)topk_weights, (const void*)dx})
         MOE_TRY(check_ptr(p, empty));
@@ -818,7 +830,7 @@ int moe_backward_ex(const moe_config* cfg, const moe_options* opts, const void* 
     // T = 0 still runs: the weight gradients are written as zeros
     return run_backward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, dy, topk_ids,
                         topk_weights, dx, dw_router, dw_gate, dw_up, dw_down, dws_gate, dws_up, dws_down, ws,
-                        static_cast<hipStream_t>(stream), capacity_of(opts));
+                        static_cast<hipStream_t>(stream), capacity_of(opts), opts ? opts->aux_alpha : 0.0f);
 }
 
 int moe_forward(const moe_config* cfg, const void* x, const void* w_router, const void* w_gate,

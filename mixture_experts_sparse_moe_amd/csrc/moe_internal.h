@@ -158,10 +158,17 @@ struct BwdRouterArgs {
     const int32_t* ids;     // [T, k]
     const float* gates;     // [T, k]
     const float* dgate;     // [T, k] by pair
-    const float* logits;    // [T, E] or nullptr (softmax + renormalise)
+    const float* logits;    // [T, E] or nullptr (softmax + renormalise, no aux loss)
     float* dl;              // [T, E] out
     int T, E, k, score_fn, renorm;
+    // load-balancing loss L_aux = alpha E sum_e f_e P_e: with aux_coef = alpha E / T
+    // (0: none), dl += aux_coef p (f - <f, p>) (softmax) or aux_coef q (1 - s) (f - <f, q>)
+    // (normalised sigmoid), f_e = aux_counts[e] inv_T
+    const int32_t* aux_counts = nullptr;  // [E] pairs per expert before any capacity drop
+    float aux_coef = 0.0f, inv_T = 0.0f;
 };
+// counts[e] = #{p < P : ids[p] = e}, E <= 256 (one workgroup).
+hipError_t launch_count_ids(const int32_t* ids, int64_t P, int E, int32_t* counts, hipStream_t s);
 hipError_t launch_bwd_router(const BwdRouterArgs& b, hipStream_t s);
 // dx[t] = sum over slots j, then K slices, of dxp[slice][pair_pos[t k + j]] (pos -1 skipped).
 hipError_t launch_bwd_token_sum(const float* dxp, const int32_t* pair_pos, int T, int k, int d, float* dx,

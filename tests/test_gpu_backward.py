@@ -231,3 +231,50 @@ def test_backward_with_capacity_matches_oracle(name):
         np.testing.assert_array_equal(got, to_host(out2[gname]), err_msg=f"{gname} not deterministic")
         worst = max(worst, assert_close(got, ref[rname], tau, gname))
     say(f"[ok] {dropped} of {sh.T * sh.k} pairs dropped; worst max|err|/max|ref| = {worst:.2e}")
+
+
+AUX = {
+    "bf16_w256_e8_k2": (S("b", T=300, d=256, E=8, k=2, d_ff=512), 0),
+    "bf16_e16_k4_sigmoid_shared_capacity": (S("b", T=150, d=128, E=16, k=4, d_ff=128, num_shared=1,
+                                              d_ff_shared=128, score_fn=synth.SIGMOID), 40),
+    "fp32_e8_k2_softmax_raw": (S("b", T=64, d=64, E=8, k=2, d_ff=128, renormalize=0, dtype=synth.F32), 0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(AUX))
+def test_backward_with_aux_loss_matches_oracle(name):
+    """moe_backward_ex with aux_alpha: the gradient of the load-balancing loss
+    (f fixed by the assignment, through the mean router probabilities) on top
+    of the layer's.  Checked twice: the whole dx and dw_router against the
+    oracle's backward with the same alpha, and the difference to the run
+    without the loss (the aux term alone) against the oracle's aux term."""
+    import mixture_experts_sparse_moe_amd as moe
+    sh, cap = AUX[name]
+    alpha = 2.0
+    say(f"[case] backward with aux loss alpha {alpha}, capacity {cap}: {name} {sh}")
+    inp = synth.make_inputs(sh, 29)
+    L = DeviceLayer(sh, inp)
+    st = L.steps()
+    dy_h = synth.normal(29, 99, sh.T * sh.d, 1.0, sh.dtype).reshape(sh.T, sh.d)
+    dy_ref = synth.bf16_to_f64(dy_h) if sh.dtype == synth.BF16 else dy_h.astype(np.float64)
+    with_aux = run_backward(L, st["ids"], st["weights"], to_dev(dy_h),
+                            moe.MoeOptions.of(expert_capacity=cap, aux_alpha=alpha))
+    without = run_backward(L, st["ids"], st["weights"], to_dev(dy_h), moe.MoeOptions.of(expert_capacity=cap))
+    torch().cuda.synchronize()
+    gids = to_host(st["ids"])
+    keep = None if not cap else (oracle.dispatch(gids, sh.E, cap)["pair_pos"] >= 0).reshape(sh.T, sh.k)
+    ref = oracle.backward(inp, gids, dy_ref, sh.score_fn, sh.renormalize, keep=keep, aux_alpha=alpha)
+    tau = TAU[sh.dtype]
+    for gname in ("dx", "dw_router"):
+        assert_close(to_host(with_aux[gname]).astype(np.float64), ref[gname], tau, gname)
+    # the aux term alone
+    dl = oracle.aux_loss_logit_grad(oracle.logits(inp["x"], inp["w_router"]), gids, sh.score_fn, alpha)
+    xr = synth.bf16_to_f64(inp["x"]) if sh.dtype == synth.BF16 else inp["x"].astype(np.float64)
+    wr = synth.bf16_to_f64(inp["w_router"]) if sh.dtype == synth.BF16 else inp["w_router"].astype(np.float64)
+    for gname, want in (("dx", dl @ wr), ("dw_router", dl.T @ xr)):
+        got = to_host(with_aux[gname]).astype(np.float64) - to_host(without[gname]).astype(np.float64)
+        r = assert_close(got, want, tau, f"{gname} aux term")
+        say(f"[{gname}] aux term max|ref| {np.abs(want).max():.3e}, rel err {r:.2e}")
+    # the expert weight gradients do not see the loss
+    for gname in ("dw_gate", "dw_up", "dw_down"):
+        np.testing.assert_array_equal(to_host(with_aux[gname]), to_host(without[gname]), err_msg=gname)
