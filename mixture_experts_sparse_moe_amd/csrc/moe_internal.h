@@ -45,7 +45,8 @@ hipError_t launch_router_stats(const float* stats_part, int blocks, int E, int T
                                hipStream_t s);
 // bf16 only: the K chunks in `ranges` ranges, one workgroup per (32 tokens,
 // range), partial logits in part [ranges, T, E] fp32, then a second kernel
-// adds them in range order and selects.  For batches of few token blocks.
+// adds them in range order and selects.  For batches of fewer than 256 token
+// blocks (route_ranges: about 256 workgroups).
 // With d (T <= 32 only; d->ids == a.ids) the second kernel also runs the
 // dispatch of the pairs.
 int route_ranges(int T, int d, bool bf16);
