@@ -49,6 +49,10 @@ CASES = {
     "bf16_w256_e4_k2_long_groups": S("b", T=1200, d=256, E=4, k=2, d_ff=256),
     # dx per pair with its K (2 d_ff = 3072) cut in two slices
     "bf16_w256_e8_k2_dx_split": S("b", T=200, d=256, E=8, k=2, d_ff=1536),
+    # the limits: 256 experts, 16 per token (generic path); 256 groups of the
+    # grouped-K weight gradients, many of them empty (persistent-kernel path)
+    "bf16_e256_k16": S("b", T=100, d=128, E=256, k=16, d_ff=64),
+    "bf16_w256_e256_k8_sigmoid": S("b", T=200, d=256, E=256, k=8, d_ff=256, score_fn=synth.SIGMOID),
 }
 
 NAMES = [("dx", "dx"), ("dw_router", "dw_router"), ("dw_gate", "dw_gate"), ("dw_up", "dw_up"),
