@@ -587,6 +587,9 @@ __device__ __forceinline__ void store_block_f32(float* Cf, int64_t ldc, int rows
 
 // Kernel modes: forward (bf16 C), fp32 C over grouped rows, fp32 C over grouped K.
 constexpr int kModeFwd = 0, kModeF32 = 1, kModeKgroup = 2;
+// dual only: both products stored as bf16, A B0^T to C and A B1^T to C2 (the
+// backward's recomputed pre-activations)
+constexpr int kModeDualOut = 3;
 
 // Main bf16 kernel, persistent: one workgroup of 8 waves per CU walks a list
 // of 256 x 256 tiles of MFMA work.
@@ -623,7 +626,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     constexpr int BM = 256;
     constexpr int BN = DUAL ? 128 : 256;
     constexpr bool KG = MODE == kModeKgroup;
-    static_assert(MODE == kModeFwd || !DUAL, "fp32 products are single GEMMs");
+    static_assert(MODE == kModeFwd || !DUAL || MODE == kModeDualOut, "fp32 products are single GEMMs");
+    static_assert(MODE != kModeDualOut || DUAL, "two outputs need the dual tile");
     constexpr int STG = 256 * kBK;    // elements of one A or B stage (32 KB)
     __shared__ __align__(16) uint16_t sA0[STG], sA1[STG];
     __shared__ __align__(16) uint16_t sB0[STG], sB1[STG];
@@ -802,7 +806,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 #pragma unroll
             for (int bo = 0; bo < (DUAL ? 1 : 2); ++bo) {
                 const int cb = DUAL ? wn * 32 : wn * 64 + bo * 32;
-                if constexpr (MODE == kModeFwd) {
+                if constexpr (MODE == kModeDualOut) {
+                    const int64_t at = (int64_t)(tr.row0 + rb) * g.N + tr.n0 + cb;
+                    float v[16];
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) v[q] = acc[i][0][q];
+                    store_block_bf16(C + at, g.N, tr.nrows - rb, v, lane);
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) v[q] = acc[i][1][q];
+                    store_block_bf16(static_cast<uint16_t*>(g.C2) + at, g.N, tr.nrows - rb, v, lane);
+                } else if constexpr (MODE == kModeFwd) {
                     float v[16];
 #pragma unroll
                     for (int q = 0; q < 16; ++q)
@@ -1167,6 +1180,21 @@ int choose_splitk_skinny(int64_t mt_expected, int N, int K) {
 
 hipError_t launch_grouped_gemm(const GemmGroup& g, bool dual, bool bf16, hipStream_t s) {
     if (g.M == 0) return hipSuccess;
+    if (g.C2) {
+        // both products of the dual tile: the persistent kernel only
+        const int64_t a_rows = g.gather ? ((int64_t)g.M + g.gather_div - 1) / g.gather_div : 0;
+        if (!dual || !bf16 || g.skinny || g.splitk != 1 || g.f32_out || g.kgrouped || g.K % 128 ||
+            g.N % 128 || a_rows * g.K * 2 >= (int64_t(1) << 32))
+            return hipErrorInvalidValue;
+        const dim3 grid(persistent_grid()), block(512);
+        if (g.aligned_bands)
+            hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<true, true, kModeDualOut>), grid, block, 0, s,
+                                  g.t_start, g.t_stop, 0, g, g.N / 128);
+        else
+            hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<true, false, kModeDualOut>), grid, block, 0, s,
+                                  g.t_start, g.t_stop, 0, g, g.N / 128);
+        return hipGetLastError();
+    }
     if (g.f32_out || g.kgrouped) {
         if (dual || !bf16 || g.skinny) return hipErrorInvalidValue;
         return launch_bf16_f32out(g, s);

@@ -489,12 +489,20 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
     // a = x W_gate^T, u = x W_up^T on the grouped rows (the forward's GEMM, with
     // its expert-aligned tile order when experts hold several M tiles)
     const bool aligned = (int64_t)P >= (int64_t)640 * E;
-    GemmGroup ga{x, sorted, k, offsets, E, P, wg, nullptr, A, f, d};
-    ga.aligned_bands = aligned;
-    MOE_HIP(launch_grouped_gemm(ga, false, bf16, s));
-    GemmGroup gu{x, sorted, k, offsets, E, P, wu, nullptr, U, f, d};
-    gu.aligned_bands = aligned;
-    MOE_HIP(launch_grouped_gemm(gu, false, bf16, s));
+    if (pl.fast) {
+        // both from one dual-tile GEMM (the gathered x rows are read once)
+        GemmGroup gau{x, sorted, k, offsets, E, P, wg, wu, A, f, d};
+        gau.C2 = U;
+        gau.aligned_bands = aligned;
+        MOE_HIP(launch_grouped_gemm(gau, true, true, s));
+    } else {
+        GemmGroup ga{x, sorted, k, offsets, E, P, wg, nullptr, A, f, d};
+        ga.aligned_bands = aligned;
+        MOE_HIP(launch_grouped_gemm(ga, false, bf16, s));
+        GemmGroup gu{x, sorted, k, offsets, E, P, wu, nullptr, U, f, d};
+        gu.aligned_bands = aligned;
+        MOE_HIP(launch_grouped_gemm(gu, false, bf16, s));
+    }
     if (pl.fast) {
         const int64_t Q = pl.Q;
         int32_t* kofs = at<int32_t>(ws, L.kofs);

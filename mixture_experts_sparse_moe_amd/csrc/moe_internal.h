@@ -83,6 +83,9 @@ struct GemmGroup {
     //     M and N multiples of 256.
     bool f32_out = false;
     bool accumulate = false;
+    // dual, bf16, persistent kernel only: C = A B0^T and C2 = A B1^T, both
+    // [rows, N] bf16 (no SiLU product)
+    void* C2 = nullptr;
     bool kgrouped = false;
     const int32_t* kofs = nullptr;
     int64_t lda = 0, ldb = 0, ldc = 0, c_gstride = 0;
