@@ -1,0 +1,93 @@
+"""Seeded random layer shapes, beyond the hand-picked cases: both dtypes,
+1 to 256 experts, k up to 16, widths in steps of 64 (ragged against every
+tile), with or without a shared expert, softmax or sigmoid, renormalised or
+raw gates, uniform or Zipf-skewed routing.  Every shape gets the full forward
+check of test_gpu_parity (routing bit-exact, dispatch bit-exact, expert
+outputs and y against the oracle); the shapes small enough for the oracle's
+chain rule also get the backward check."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_harness import TAU, DeviceLayer, assert_close, to_dev, to_host, torch
+from test_gpu_backward import NAMES, run_backward
+from test_gpu_parity import check_layer
+
+pytestmark = pytest.mark.gpu
+S = synth.LayerShape
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch().cuda.is_available():
+        pytest.fail("GPU tests need an MI355X; torch.cuda.is_available() is False")
+    import mixture_experts_sparse_moe_amd as moe
+    moe.lib()
+
+
+def random_shapes(n=48, seed=2026):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = synth.F32 if i % 4 == 0 else synth.BF16
+        E = int(rng.choice([1, 2, 3, 5, 8, 16, 33, 64, 100, 256]))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        T = int(rng.choice([1, 7, 32, 33, 100, 257, 600]))
+        d = 64 * int(rng.integers(1, 9))
+        d_ff = 64 * int(rng.integers(1, 9))
+        shared = bool(rng.random() < 0.3)
+        d_ff_s = 64 * int(rng.integers(1, 5)) if shared else 0
+        score = synth.SIGMOID if rng.random() < 0.4 else synth.SOFTMAX
+        renorm = 0 if rng.random() < 0.25 else 1
+        # the skew shifts x along W_r^T (W_r W_r^T)^-1 b, which needs E <= d
+        zipf = 1.1 if (rng.random() < 0.3 and 4 <= E <= d) else 0.0
+        out.append(S(f"r{i:02d}", T=T, d=d, E=E, k=k, d_ff=d_ff, num_shared=int(shared), d_ff_shared=d_ff_s,
+                     score_fn=score, renormalize=renorm, dtype=dtype, zipf_s=zipf))
+    return out
+
+
+SHAPES = {sh.name: sh for sh in random_shapes()}
+
+
+@pytest.mark.parametrize("name", sorted(SHAPES))
+def test_random_shape_forward(name):
+    sh = SHAPES[name]
+    check_layer(sh, synth.make_inputs(sh, 31))
+
+
+# the oracle's chain rule costs about 12 d d_ff fp64 multiply-adds per pair
+BACKWARD = sorted(n for n, sh in SHAPES.items() if sh.T * sh.k * sh.d * sh.d_ff <= 2.5e8)
+
+
+@pytest.mark.parametrize("name", BACKWARD)
+def test_random_shape_backward(name):
+    sh = SHAPES[name]
+    say(f"[case] backward {sh}")
+    inp = synth.make_inputs(sh, 37)
+    L = DeviceLayer(sh, inp)
+    st = L.steps()
+    dy_h = synth.normal(37, 99, sh.T * sh.d, 1.0, sh.dtype).reshape(sh.T, sh.d)
+    dy_ref = synth.bf16_to_f64(dy_h) if sh.dtype == synth.BF16 else dy_h.astype(np.float64)
+    out = run_backward(L, st["ids"], st["weights"], to_dev(dy_h))
+    torch().cuda.synchronize()
+    gids = to_host(st["ids"])
+    ref = oracle.backward(inp, gids, dy_ref, sh.score_fn, sh.renormalize)
+    tau = TAU[sh.dtype]
+    worst = 0.0
+    for gname, rname in NAMES:
+        if gname not in out:
+            continue
+        want = ref[rname]
+        got = to_host(out[gname]).astype(np.float64)
+        if np.abs(want).max() < 1e-10:       # zero up to the oracle's rounding
+            assert np.abs(got).max() <= 1e-6, f"{gname} should be zero"
+            continue
+        worst = max(worst, assert_close(got, want, tau, gname))
+    say(f"[ok] worst max|err|/max|ref| = {worst:.2e}")
