@@ -91,3 +91,48 @@ def test_random_shape_backward(name):
             continue
         worst = max(worst, assert_close(got, want, tau, gname))
     say(f"[ok] worst max|err|/max|ref| = {worst:.2e}")
+
+
+@pytest.mark.parametrize("name", BACKWARD)
+def test_random_shape_capacity_and_aux_loss(name):
+    """The same shapes trained with an expert capacity (factor 0.8, so pairs
+    are dropped) and the load-balancing loss: moe_forward_ex's y against the
+    oracle's forward without the dropped pairs, and moe_backward_ex's
+    gradients against the oracle's backward with the same keep mask and
+    alpha."""
+    import mixture_experts_sparse_moe_amd as moe
+    t = torch()
+    sh = SHAPES[name]
+    cap = moe.capacity(sh.T, sh.k, sh.E, 0.8)
+    say(f"[case] capacity {cap} + aux loss {sh}")
+    inp = synth.make_inputs(sh, 41)
+    L = DeviceLayer(sh, inp)
+    dv = L.d
+    y = L.empty_act(sh.T, sh.d)
+    ids = t.empty(sh.T, sh.k, dtype=t.int32, device="cuda")
+    wts = t.empty(sh.T, sh.k, dtype=t.float32, device="cuda")
+    moe.moe_forward_ex(L.cfg, moe.MoeOptions.of(expert_capacity=cap), dv["x"], dv["w_router"], dv["w_gate"],
+                       dv["w_up"], dv["w_down"], dv["ws_gate"], dv["ws_up"], dv["ws_down"], y, ids, wts, None, L.ws)
+    dy_h = synth.normal(41, 99, sh.T * sh.d, 1.0, sh.dtype).reshape(sh.T, sh.d)
+    dy_ref = synth.bf16_to_f64(dy_h) if sh.dtype == synth.BF16 else dy_h.astype(np.float64)
+    out = run_backward(L, ids, wts, to_dev(dy_h), moe.MoeOptions.of(expert_capacity=cap, aux_alpha=1.0))
+    t.cuda.synchronize()
+    gids = to_host(ids)
+    keep = (oracle.dispatch(gids, sh.E, cap)["pair_pos"] >= 0).reshape(sh.T, sh.k)
+    tau = TAU[sh.dtype]
+    widen = synth.bf16_to_f64 if sh.dtype == synth.BF16 else (lambda a: a.astype(np.float64))
+    r = oracle.forward_tokens(inp, sh.k, np.arange(sh.T), sh.score_fn, sh.renormalize, forced_ids=gids,
+                              keep=keep.astype(np.int32))
+    rel = assert_close(widen(to_host(y)), r["y"], tau, "y with capacity")
+    ref = oracle.backward(inp, gids, dy_ref, sh.score_fn, sh.renormalize, keep=keep, aux_alpha=1.0)
+    worst = 0.0
+    for gname, rname in NAMES:
+        if gname not in out:
+            continue
+        want = ref[rname]
+        got = to_host(out[gname]).astype(np.float64)
+        if np.abs(want).max() < 1e-10:
+            assert np.abs(got).max() <= 1e-6, f"{gname} should be zero"
+            continue
+        worst = max(worst, assert_close(got, want, tau, gname))
+    say(f"[ok] {int((~keep).sum())} of {sh.T * sh.k} pairs dropped; y {rel:.2e}, gradients {worst:.2e}")
