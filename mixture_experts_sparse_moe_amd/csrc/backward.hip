@@ -19,7 +19,8 @@
 // which the kernel's grouped-K mode sums.  Other shapes use the generic
 // grouped GEMMs here (bf16 MFMA with operands transposed on their way into
 // LDS, or fp32 FMA), which take any layout.  The recomputation of a and u
-// uses the forward's grouped GEMM.
+// uses the forward's grouped GEMM (on the persistent path one dual-tile
+// launch that stores both products).
 #include <algorithm>
 
 #include "device_util.h"

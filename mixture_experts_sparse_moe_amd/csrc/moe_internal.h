@@ -108,7 +108,8 @@ int choose_splitk_skinny(int64_t mt_expected, int N, int K);
 int64_t grouped_m_tiles_upper(int64_t rows, int G, int bm);
 
 // ---- backward -------------------------------------------------------------------
-// Generic grouped GEMM for the backward, fp32 FMA, C fp32:
+// Generic grouped GEMM for the backward (any operand layout; bf16 MFMA when both
+// operands are bf16 in 16-byte pieces, else fp32 FMA), C fp32:
 //   C(m, n) (+)= sum_k A(m, k) B(n, k)
 // rows mode (krows = false): group g owns output rows [offsets[g], offsets[g+1])
 //   (or [0, M) without offsets); A(m, k) = A[src(m) lda + k] with src(m) =
