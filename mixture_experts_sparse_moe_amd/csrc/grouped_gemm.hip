@@ -848,9 +848,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 // rows (dual: NBLK / 2 gate blocks and the same up blocks, so a tile yields
 // 16 NBLK columns of silu(g) * u; single: 32 NBLK columns) over one K range.
 // One workgroup of 4 waves per tile; the K chunks stream through LDS (the
-// shared 32-row product above).  With NST = 3 and NBLK = 4 a workgroup takes
-// 60 KB of LDS, so two run on a CU and one's set-up and epilogue overlap the
-// other's stream.  Logical tile L: N tile fastest, then the M tile (of 32
+// shared 32-row product above).  With NST = 4 and NBLK = 4 a workgroup takes
+// 80 KB of LDS (four 20 KB stages; the tile lookup borrows the last one before
+// the stream starts), so two run on a CU and one's set-up and epilogue overlap
+// the other's stream.  Logical tile L: N tile fastest, then the M tile (of 32
 // rows, by the prefix over the groups), then the K range.  The K walk of a
 // tile starts at a chunk that depends on its N tile and group, so tiles that
 // run together read different offsets of their weight rows.
