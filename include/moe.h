@@ -1,6 +1,7 @@
 /*
- * moe.h -- C ABI of the MI355X (gfx950) top-k Mixture-of-Experts FFN layer,
- * forward pass.
+ * moe.h -- C ABI of the MI355X (gfx950) top-k Mixture-of-Experts FFN layer:
+ * the forward pass (whole, or step by step), its optional routing features
+ * (selection bias, expert capacity, load statistics) and the backward pass.
  *
  * The layer (pages: "Mixture-of-Experts Internals: A Systems Engineer's Field
  * Manual" sec. 2.1; "8.6 -- Mixture of Experts (MoE)" sec. 2 and 4.1;
@@ -15,8 +16,9 @@
  *   y = sum_{i in I} g_i f_i(x) + f_s(x)   f(x) = W_down(silu(W_gate x) * W_up x)
  *
  * Conventions shared by every entry point:
- *   - Ownership: the caller owns every buffer.  The library never allocates,
- *     frees or keeps state between calls; calls are thread-safe.
+ *   - Ownership: the caller owns every buffer.  The library never allocates
+ *     or frees device memory and keeps no state between calls (beyond the
+ *     device's compute-unit count, read once); calls are thread-safe.
  *   - Pointers: every tensor pointer is a DEVICE pointer (HBM of the current
  *     HIP device).  `cfg` is a HOST pointer read during the call only.
  *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
@@ -84,7 +86,8 @@ typedef struct moe_config {
 } moe_config;
 
 /* Bytes of device workspace moe_forward needs for `cfg` (also enough for
- * every other entry point).  0 for an invalid cfg.  Host only. */
+ * every other forward entry point; the backward has its own,
+ * moe_backward_workspace_bytes).  0 for an invalid cfg.  Host only. */
 size_t moe_workspace_bytes(const moe_config* cfg);
 
 /* Human-readable name of a status code.  Host only; static storage. */
@@ -163,8 +166,8 @@ int moe_combine(const moe_config* cfg, const void* expert_out, const float* topk
  *   topk_ids_out [T,k], topk_weights_out [T,k], expert_counts_out [E]:
  *   optional copies of the routing (nullable; the workspace is used when
  *   NULL).
- * Same arithmetic as the entry points above, except that with few tokens the
- * router logits and, in bf16, the down projections may be summed over K
+ * Same arithmetic as the entry points above, except that in bf16 the router
+ * logits (below 8192 tokens) and the down projections may be summed over K
  * ranges (fixed order; deterministic), so results can differ from the
  * step-by-step calls in the last bits and routing at near-ties.
  */
