@@ -56,6 +56,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(DispatchArgs a,
         run = min(run, a.cap);
         a.counts[e] = run;
     }
+    for (int i = threadIdx.x; i < a.nzero; i += kThreads) a.zero[i] = 0;
     expert_scan(a, run, tot, wsum);
 }
 
@@ -75,7 +76,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(DispatchArgs
 }
 
 // All pairs in one chunk: count, scan and scatter in one workgroup.
-__global__ __launch_bounds__(kThreads) void dispatch_single_kernel(DispatchArgs a) { dispatch_in_block(a); }
+__global__ __launch_bounds__(kThreads) void dispatch_single_kernel(DispatchArgs a) {
+    for (int i = threadIdx.x; i < a.nzero; i += kThreads) a.zero[i] = 0;
+    dispatch_in_block(a);
+}
 
 __global__ void fill_zero_kernel(int32_t* a, int na, int32_t* b, int nb) {
     for (int i = threadIdx.x; i < na; i += blockDim.x) a[i] = 0;

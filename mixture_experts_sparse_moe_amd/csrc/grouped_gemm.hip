@@ -585,6 +585,57 @@ __device__ __forceinline__ void store_block_f32(float* Cf, int64_t ldc, int rows
     }
 }
 
+// Tile queue of a persistent workgroup (forward GEMMs with ragged groups).
+// Each XCD's range [xcd per, end) of logical tiles is walked in rounds as
+// without the queue, but only the first three rounds are fixed (tile
+// xcd per + r nslot + slot for round r); later tiles are claimed through
+// counter q[32 xcd] (zeroed before the launch), and a workgroup whose range
+// is used up claims the next tiles of the other XCDs' ranges.  Nearly empty
+// tiles, of which an expert with a few rows past a multiple of 256 has one,
+// then even out between workgroups.  Kept in LDS for thread 0.
+struct TileQueue {
+    int* q;
+    int per, TL, nslot, xcd;
+    int lo, end;    // the own range's claimed part
+};
+
+// Claims from counter c (a global address: a flat atomic would also hold up
+// the LDS waits of the next K stage).  An atomic increment, unlike an atomic
+// add, is not combined across the wave by the compiler, which would wait for
+// its result at once.
+__device__ __forceinline__ int claim_next(int* c) {
+    using gu32 = __attribute__((address_space(1))) unsigned;
+    return (int)__builtin_amdgcn_atomic_inc32((volatile gu32*)c, 0x7FFFFFFFu, __ATOMIC_RELAXED, "agent");
+}
+
+// The next unclaimed tile of another XCD's range, or -1.
+__device__ __forceinline__ int steal_tile(const TileQueue& t) {
+    for (int k = 1; k < 8; ++k) {
+        const int y = (t.xcd + k) & 7;
+        const int lo = y * t.per + 3 * t.nslot, hi = min(t.TL, (y + 1) * t.per);
+        if (lo >= hi) continue;
+        const int c = lo + claim_next(t.q + 32 * y);
+        if (c < hi) return c;
+    }
+    return -1;
+}
+
+// Thread 0 at the start of tile it (it > 0): publishes tile it + 2 in
+// next[(it + 1) & 1] from the claim made at the start of tile it - 1, then
+// claims the tile after it (tiles 1 and 2 are fixed, and tile 3 is claimed
+// at the start of tile 0).  Returns the claim in flight (-1: none), whose
+// value is first needed at the start of tile it + 1, so the K loop's waits
+// cover its latency.
+__device__ __forceinline__ int next_tile_step(const TileQueue& ts, int* next, int it, int claim) {
+    const TileQueue t = ts;
+    int pub = next[1];
+    if (it > 0) {
+        pub = claim < 0 ? -1 : (t.lo + claim < t.end ? t.lo + claim : steal_tile(t));
+        next[(it + 1) & 1] = pub;
+    }
+    return pub >= 0 ? claim_next(t.q + 32 * t.xcd) : -1;
+}
+
 // Kernel modes: forward (bf16 C), fp32 C over grouped rows, fp32 C over grouped K.
 constexpr int kModeFwd = 0, kModeF32 = 1, kModeKgroup = 2;
 // dual only: both products stored as bf16, A B0^T to C and A B1^T to C2 (the
@@ -603,7 +654,8 @@ constexpr int kModeDualOut = 3;
 // round is a window of 4 M tiles x (workgroups / 4) N tiles, so its A and B
 // panels are shared in the XCD's L2 while its tiles advance through K together.
 // With ALIGNED the bands follow the groups instead (up to 6 M tiles of one
-// expert, whose weights are then streamed about once).
+// expert, whose weights are then streamed about once).  With QUEUE only the
+// first three rounds are fixed and later tiles are claimed (TileQueue above).
 // Waves form a 2 x 4 grid: wave (wm, wn) owns 128 rows and two 32-row blocks
 // of B (dual: gate columns 32 wn .. 32 wn + 31 and the same up columns, so
 // silu(g)*u stays in registers; single: B rows 64 wn .. 64 wn + 63), i.e.
@@ -621,13 +673,14 @@ constexpr int kModeDualOut = 3;
 // MODE kModeKgroup (single): every group has all M x N tiles and walks its own
 // K columns (the weight gradients of the backward: sums over each expert's
 // rows, with both operands transposed so that K is contiguous).
-template <bool DUAL, bool ALIGNED, int MODE = kModeFwd>
+template <bool DUAL, bool ALIGNED, int MODE = kModeFwd, bool QUEUE = false>
 __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup g, int tiles_n) {
     constexpr int BM = 256;
     constexpr int BN = DUAL ? 128 : 256;
     constexpr bool KG = MODE == kModeKgroup;
     static_assert(MODE == kModeFwd || !DUAL || MODE == kModeDualOut, "fp32 products are single GEMMs");
     static_assert(MODE != kModeDualOut || DUAL, "two outputs need the dual tile");
+    static_assert(!QUEUE || MODE == kModeFwd, "the tile queue serves the forward GEMMs");
     constexpr int STG = 256 * kBK;    // elements of one A or B stage (32 KB)
     __shared__ __align__(16) uint16_t sA0[STG], sA1[STG];
     __shared__ __align__(16) uint16_t sB0[STG], sB1[STG];
@@ -657,6 +710,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     const int wn_win = max(nslot / kWMW, 1);
     int L = xcd * per + slot;
     if (L >= Lend) return;
+    // queue: at the start of tile i, s_next[i & 1] holds tile i + 1 (or -1)
+    __shared__ int s_next[2];
+    __shared__ TileQueue s_tq;
+    int claim = -1;         // thread 0: counter value of the claim in flight, or -1
+    if (QUEUE && tid == 0) {
+        s_tq = TileQueue{g.queue, per, TL, nslot, xcd, xcd * per + 3 * nslot, Lend};
+        s_next[0] = L + nslot < Lend ? L + nslot : -1;
+        s_next[1] = s_next[0] >= 0 && L + 2 * nslot < Lend ? L + 2 * nslot : -1;
+    }
 
     const int half = lane >> 5, r32 = lane & 31;
     int a_row[4], b_row[2];
@@ -775,9 +837,17 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     MOE_LOAD_FRAGS(sA0, sB0, 0, fa0, fb0, 4);
 
     uint16_t* C = static_cast<uint16_t*>(g.C);
-    for (;;) {
-        const int Ln = L + nslot;
-        const bool more = Ln < Lend;
+    for (int it = 0;; ++it) {
+        int Ln;
+        bool more;
+        if constexpr (QUEUE) {
+            Ln = __builtin_amdgcn_readfirstlane(s_next[it & 1]);
+            more = Ln >= 0;
+            if (tid == 0) claim = next_tile_step(s_tq, s_next, it, claim);
+        } else {
+            Ln = L + nslot;
+            more = Ln < Lend;
+        }
         const TileRef tn = tile_of(more ? Ln : L);
         // the next tile's gathered rows load now; their values are used after
         // the K loop, whose stage waits have long covered them
@@ -1063,13 +1133,23 @@ hipError_t launch_bf16_persistent(const GemmGroup& g, hipStream_t s) {
     constexpr int BN = DUAL ? 128 : 256;
     // one instantiation per tile order: a runtime choice inside the kernel
     // costs the K loop a compiler-inserted wait on the loads in flight
-    if (g.aligned_bands) {
-        hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<DUAL, true>), dim3(persistent_grid()), dim3(512),
-                              0, s, g.t_start, g.t_stop, 0, g, g.N / BN);
+    const dim3 grid(persistent_grid()), block(512);
+    if (g.queue) {
+        if (g.aligned_bands)
+            hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<DUAL, true, kModeFwd, true>), grid, block, 0, s,
+                                  g.t_start, g.t_stop, 0, g, g.N / BN);
+        else
+            hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<DUAL, false, kModeFwd, true>), grid, block, 0, s,
+                                  g.t_start, g.t_stop, 0, g, g.N / BN);
         return hipGetLastError();
     }
-    hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<DUAL, false>), dim3(persistent_grid()), dim3(512), 0, s,
-                          g.t_start, g.t_stop, 0, g, g.N / BN);
+    if (g.aligned_bands) {
+        hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<DUAL, true>), grid, block, 0, s, g.t_start, g.t_stop,
+                              0, g, g.N / BN);
+        return hipGetLastError();
+    }
+    hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<DUAL, false>), grid, block, 0, s, g.t_start, g.t_stop, 0,
+                          g, g.N / BN);
     return hipGetLastError();
 }
 

@@ -20,6 +20,8 @@ struct DispatchArgs {
     int32_t* chunk_counts;  // [nchunks, E] scratch
     int P, E;
     int cap = 0x7FFFFFFF;   // pairs kept per expert (the first ones); the rest get pair_pos -1
+    int32_t* zero = nullptr;  // P > 0: nzero ints set to 0 on the way (the GEMMs' tile-queue counters)
+    int nzero = 0;
 };
 int dispatch_num_chunks(int P);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
@@ -89,6 +91,11 @@ struct GemmGroup {
     bool kgrouped = false;
     const int32_t* kofs = nullptr;
     int64_t lda = 0, ldb = 0, ldc = 0, c_gstride = 0;
+    // bf16 persistent kernel, forward mode: 256 ints, zeroed before the
+    // launch, through which the workgroups claim tiles past their first three
+    // rounds and take other XCDs' tiles once their own run out (nullptr: each
+    // workgroup walks a fixed list)
+    int* queue = nullptr;
 };
 // Dual mode: C = silu(A B0^T) * (A B1^T).  Single: C = A B0^T, or with
 // splitk > 1 the partial products of the K ranges, C slice s = A[:, Ks] B0[:, Ks]^T.

@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_harness import (TAU, DeviceLayer, assert_close, check_routing, oracle_routing, to_host,
+from gpu_harness import (TAU, DeviceLayer, assert_close, check_routing, oracle_routing, to_dev, to_host,
                          torch)
 
 pytestmark = pytest.mark.gpu
@@ -222,3 +222,42 @@ def test_decode_paths_deterministic():
     t.cuda.synchronize()
     for o in outs:
         np.testing.assert_array_equal(to_host(o), to_host(st["expert_out"]))
+
+
+def test_nearly_empty_tiles_through_the_tile_queue():
+    """Every other expert holds 257 rows (a full 256-row tile plus a one-row
+    tile), the rest one row, at widths that give both routed GEMMs 960 tiles
+    (3.75 rounds over 256 CUs), so the persistent kernels claim and steal
+    tiles past their first three rounds.  moe_expert_ffn's rows against the
+    oracle's expert FFN (both tile edges of every expert, and the one-row
+    tiles), and three more calls bitwise equal to the first: which workgroup
+    takes a tile changes between calls, the result may not."""
+    import mixture_experts_sparse_moe_amd as moe
+    t = torch()
+    sh = S("q", T=1024, d=4096, E=40, k=8, d_ff=2048)
+    inp = synth.make_inputs(sh, 11)
+    L = DeviceLayer(sh, inp)
+    counts = np.array([257 if e % 2 == 0 else 1 for e in range(sh.E)], dtype=np.int32)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    P = sh.T * sh.k
+    pairs = np.random.default_rng(11).permutation(P).astype(np.int32)   # rows past offsets[E] unused
+    say(f"[case] tile queue: {int(offsets[-1])} rows in {sh.E} experts, {sh}")
+    sp, off = to_dev(pairs), to_dev(offsets)
+    outs = []
+    for _ in range(4):
+        out = L.empty_act(P, sh.d)
+        moe.moe_expert_ffn(L.cfg, L.d["x"], sp, off, L.d["w_gate"], L.d["w_up"], L.d["w_down"], None, None,
+                           None, out, None, L.ws)
+        outs.append(out)
+    t.cuda.synchronize()
+    n = int(offsets[-1])
+    first = to_host(outs[0])[:n]
+    for o in outs[1:]:
+        np.testing.assert_array_equal(to_host(o)[:n], first)
+    worst = 0.0
+    for e in range(sh.E):
+        local = [0, 255, 256] if counts[e] == 257 else [0]
+        rows = offsets[e] + np.array(local)
+        _, want = oracle.expert_rows(e, inp["x"], pairs[rows] // sh.k, inp["w_gate"], inp["w_up"], inp["w_down"])
+        worst = max(worst, assert_close(synth.bf16_to_f64(first[rows]), want, TAU[sh.dtype], f"expert {e}"))
+    say(f"[ok] worst max|err|/max|ref| = {worst:.2e}")
