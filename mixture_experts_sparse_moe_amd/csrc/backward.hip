@@ -545,6 +545,30 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const float* dl, cons
     }
 }
 
+// The router weight gradient as one bf16 product on the persistent kernel:
+// out [E, 2 Tr] gets out[e][t] = hi and out[e][Tr + t] = lo, where hi is dl[t][e]
+// rounded to bf16 and lo the rest rounded to bf16 (zero for T <= t < Tr), so
+// that hi x + lo x carries about 16 bits of dl.  64 x 64 tiles through LDS:
+// reads along E, writes along t.
+__global__ __launch_bounds__(256) void dl_split_kernel(const float* dl, int T, int E, int Tr, uint16_t* out) {
+    __shared__ float tile[64][65];
+    const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int tt = i >> 6, ee = i & 63;
+        tile[tt][ee] = (t0 + tt < T && e0 + ee < E) ? dl[(int64_t)(t0 + tt) * E + e0 + ee] : 0.0f;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+        const int ee = i >> 6, tt = i & 63;
+        if (e0 + ee >= E) continue;
+        const float v = tile[tt][ee];
+        const uint16_t hi = f32_to_bf16(v);
+        uint16_t* row = out + (int64_t)(e0 + ee) * 2 * Tr + t0 + tt;
+        row[0] = hi;
+        row[Tr] = f32_to_bf16(v - bf16_to_f32(hi));
+    }
+}
+
 // p[0 .. n) = 0 (a fill kernel rather than a memset, so the call stays capturable).
 __global__ __launch_bounds__(256) void fill_zero_f32_kernel(float* p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
@@ -804,6 +828,19 @@ hipError_t launch_router_wgrad(const float* dl, const void* x, bool x_bf16, int 
         const int64_t n = (int64_t)E * d;
         hipLaunchKernelGGL(sum_chunks_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, used, n, dwr);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_dl_split(const float* dl, int T, int E, int Tr, uint16_t* out, hipStream_t s) {
+    if (T < 0 || E <= 0 || Tr < T || Tr % 64) return hipErrorInvalidValue;
+    if (Tr == 0) return hipSuccess;
+    hipLaunchKernelGGL(dl_split_kernel, dim3(Tr / 64, (E + 63) / 64), dim3(256), 0, s, dl, T, E, Tr, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_sum_chunks(const float* part, int chunks, int64_t n, float* dst, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(sum_chunks_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, chunks, n, dst);
     return hipGetLastError();
 }
 

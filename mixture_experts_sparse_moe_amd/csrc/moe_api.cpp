@@ -352,6 +352,12 @@ struct BwdPlan {
     int64_t Q = 0;              // columns of the transposed pair operands (rows padded per expert)
     int64_t Tq = 0;             // columns of the transposed token operands
     int xsplit = 1;             // K split of dx per pair (dXp slices)
+    // dW_r = dl^T x on the persistent kernel (bf16, 32 or more experts): one
+    // product over 2 Tr columns, dl split into bf16 high and low parts and x
+    // transposed twice, its K split into rsplit fp32 slices
+    bool router_mfma = false;
+    int64_t Tr = 0;
+    int rsplit = 1;
 };
 
 BwdPlan bwd_plan(const moe_config* c) {
@@ -374,11 +380,16 @@ BwdPlan bwd_plan(const moe_config* c) {
         const int64_t fs = c->d_ff_shared;
         p.shared_fast = d % 256 == 0 && fs % 256 == 0 && 256 * p.Tq * 2 < lim;
     }
+    // the FMA kernel reads x E / 16 times (DeepSeek-V3 prefill: 4.7 ms); the
+    // product takes ~0.2 ms.  Few experts keep the FMA kernel (Mixtral: 45 us).
+    p.Tr = (T + 511) / 512 * 512;
+    p.router_mfma = E >= 32 && T > 0 && d % 256 == 0 && 256 * 2 * p.Tr * 2 < lim;
+    if (p.router_mfma) p.rsplit = choose_splitk(1, (int)d, (int)(2 * p.Tr));
     return p;
 }
 
 struct BwdLayout {
-    size_t counts, offsets, sorted, pos, chunk, A, U, H, DA, DU, dHp, dO, dXp, dgate, logits, dl, rw, auxcnt;
+    size_t counts, offsets, sorted, pos, chunk, A, U, H, DA, DU, dHp, dO, dXp, dgate, logits, dl, rw, auxcnt, DLT, XT2;
     size_t As, Us, Hs, DAs, DUs, dHs;
     // fast path: DA and DU share rows [da | du] (DA), transposed operands
     size_t kofs, WdT, WguT, dOT, HT, DADUT, XgT, WsdT, WsguT, dyT, HsT, DADUsT, xT;
@@ -405,7 +416,13 @@ BwdLayout bwd_layout(const moe_config* c) {
     L.dgate = take(P * 4);
     L.logits = take(T * E * 4);
     L.dl = take(T * E * 4);
-    L.rw = take((size_t)router_wgrad_chunks((int)T, (int)d, (int)E) * E * d * 4);
+    if (pl.router_mfma) {
+        L.rw = take((size_t)pl.rsplit * E * d * 4);
+        L.DLT = take(E * 2 * (size_t)pl.Tr * w);
+        L.XT2 = take(d * 2 * (size_t)pl.Tr * w);
+    } else {
+        L.rw = take((size_t)router_wgrad_chunks((int)T, (int)d, (int)E) * E * d * 4);
+    }
     L.auxcnt = take(E * 4);
     if (pl.fast) {
         L.DA = take(P * 2 * f * w);
@@ -604,7 +621,24 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
         ra.inv_T = 1.0f / (float)T;
     }
     MOE_HIP(launch_bwd_router(ra, s));
-    MOE_HIP(launch_router_wgrad(dl, x, bf16, T, E, d, at<float>(ws, L.rw), dwr, s));
+    if (pl.router_mfma) {
+        const int tr = (int)pl.Tr;
+        char* XT2 = at<char>(ws, L.XT2);
+        MOE_HIP(launch_dl_split(dl, T, E, tr, at<uint16_t>(ws, L.DLT), s));
+        for (int half = 0; half < 2; ++half)
+            MOE_HIP(launch_transpose_rows(rows_t(x, d, d, nullptr, 1, nullptr, nullptr, nullptr, 1, T, tr,
+                                                 XT2 + (size_t)half * pl.Tr * w, 2 * pl.Tr),
+                                          pl.Tr, s));
+        float* rw = at<float>(ws, L.rw);
+        GemmGroup gr = f32_gemm(at<void>(ws, L.DLT), nullptr, 1, nullptr, 1, E, XT2, pl.rsplit > 1 ? rw : dwr, d, d,
+                                2 * tr);
+        gr.splitk = pl.rsplit;
+        gr.part_stride = (int64_t)E * d;
+        MOE_HIP(launch_grouped_gemm(gr, false, true, s));
+        if (pl.rsplit > 1) MOE_HIP(launch_sum_chunks(rw, pl.rsplit, (int64_t)E * d, dwr, s));
+    } else {
+        MOE_HIP(launch_router_wgrad(dl, x, bf16, T, E, d, at<float>(ws, L.rw), dwr, s));
+    }
     GradGemm gx = grad_gemm(dl, E, wr, d, dx, d, T, d, E);
     gx.accumulate = true;
     MOE_HIP(launch_grad_gemm(gx, false, false, false, bf16, s));

@@ -53,6 +53,9 @@ CASES = {
     # grouped-K weight gradients, many of them empty (persistent-kernel path)
     "bf16_e256_k16": S("b", T=100, d=128, E=256, k=16, d_ff=64),
     "bf16_w256_e256_k8_sigmoid": S("b", T=200, d=256, E=256, k=8, d_ff=256, score_fn=synth.SIGMOID),
+    # 32 experts or more: dW_r as one product over 2 x 3072 token columns (dl
+    # in bf16 high and low parts), its K cut in four fp32 slices
+    "bf16_w256_e32_k2_router_slices": S("b", T=3000, d=256, E=32, k=2, d_ff=256),
 }
 
 NAMES = [("dx", "dx"), ("dw_router", "dw_router"), ("dw_gate", "dw_gate"), ("dw_up", "dw_up"),
