@@ -217,24 +217,27 @@ int run_ffn(const moe_config* c, const void* x, const int32_t* sorted, const int
     const int P = c->num_tokens * c->top_k;
     const Paths pa = paths(c);
     if (P > 0) {
-        // expert-aligned tile bands pay off when experts hold several M tiles
-        // (measured on the down GEMM: -6 % at ~4 tiles per expert, +2 % at ~1.5;
-        // on gate/up -5 % at ~4 tiles per expert, with 16 % less HBM traffic)
-        const bool aligned = (int64_t)P >= (int64_t)640 * c->num_experts;
-        // With about one M tile per expert, about half the experts add a
-        // nearly empty tile: the routed persistent GEMMs then claim tiles
-        // through counters (zeroed by moe_forward's dispatch, else here by a
-        // kernel, not a memset, so that a captured graph replays it), which
-        // evens those tiles out between workgroups (DeepSeek-V3 prefill: -5 %
-        // gate/up, -8 % down).  With several tiles per expert the fixed
-        // schedule is as fast and its windows read 20 % fewer bytes.
-        const bool use_queue = bf16 && !pa.routed_skinny && !aligned;
+        // Tile order of the routed persistent GEMMs: expert-aligned bands, so
+        // that each expert's weights stream about once.  With several M tiles
+        // per expert (640 rows or more) the tiles follow a fixed schedule
+        // (aligned bands measured -6 % on the down GEMM and -5 % on gate/up
+        // at ~4 tiles per expert, with 16 % less HBM traffic).  With about
+        // one tile per expert, about half the experts add a nearly empty
+        // tile: the GEMMs then claim tiles through counters (zeroed by
+        // moe_forward's dispatch, else here by a kernel, not a memset, so that
+        // a captured graph replays it), which evens those tiles out between
+        // workgroups (DeepSeek-V3 prefill: 9.36 -> 8.35 ms with both, where
+        // the aligned order alone was 2 % slower than the plain one).  At
+        // several tiles per expert the queue did not speed the GEMMs up and
+        // its windows read 26 % more bytes.
+        const bool several = (int64_t)P >= (int64_t)640 * c->num_experts;
+        const bool use_queue = bf16 && !pa.routed_skinny && !several;
         if (use_queue && !queue_zeroed)
             MOE_HIP(launch_fill_zero_f32(reinterpret_cast<float*>(queue), kQueueInts, s));
         GemmGroup up{x, sorted, c->top_k, offsets, c->num_experts, P, wg, wu, H, c->d_ff,
                      c->d_model};
         up.skinny = pa.routed_skinny;
-        up.aligned_bands = aligned;
+        up.aligned_bands = true;
         up.queue = use_queue ? queue : nullptr;
         // stage events 1 and 2 are the routed gate/up kernel's own start and
         // end timestamps: no separate records around the dominant kernel
@@ -244,7 +247,7 @@ int run_ffn(const moe_config* c, const void* x, const int32_t* sorted, const int
         }
         MOE_HIP(launch_grouped_gemm(up, true, bf16, s));
         GemmGroup down{H, nullptr, 1, offsets, c->num_experts, P, wd, nullptr, out, c->d_model,
-                       c->d_ff, sp.routed, (int64_t)P * c->d_model, aligned};
+                       c->d_ff, sp.routed, (int64_t)P * c->d_model, true};
         down.skinny = pa.routed_skinny;
         down.queue = use_queue ? queue + 256 : nullptr;
         MOE_HIP(launch_grouped_gemm(down, false, bf16, s));
