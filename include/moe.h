@@ -221,8 +221,8 @@ int moe_forward_staged(const moe_config* cfg, const void* x, const void* w_route
  * is kept from the forward but its routing.  Sums run in a fixed order, no
  * atomics: the result is deterministic.  ws: at least
  * moe_backward_workspace_bytes(cfg) bytes; for bf16 layers whose d and d_ff
- * are multiples of 256 that includes transposed copies of the expert weights
- * (3 E d d_ff bf16) and of the pairs' activations.
+ * are multiples of 256 that includes transposed copies of the pairs'
+ * activations (the weights are read as they are).
  */
 size_t moe_backward_workspace_bytes(const moe_config* cfg);
 int moe_backward(const moe_config* cfg, const void* x, const void* w_router, const void* w_gate,

@@ -13,10 +13,10 @@
 // The GEMMs of the backward are NN (dgrad: the weights are contracted over
 // their output dimension) and TN (weight gradients: a sum over each expert's
 // rows).  bf16 layers whose widths are multiples of 256 run them on the
-// forward's persistent MFMA kernel: the weights are transposed once per call
-// so the data gradients read them along K, and each expert's rows become a
-// range of columns (padded to 128 with zeros) of transposed activations, over
-// which the kernel's grouped-K mode sums.  Other shapes use the generic
+// forward's persistent MFMA kernel: the data gradients read the weights as
+// they are, through the kernel's N-major B mode (transposed LDS reads), and
+// each expert's rows become a range of columns (padded to 128 with zeros) of
+// transposed activations, over which the kernel's grouped-K mode sums.  Other shapes use the generic
 // grouped GEMMs here (bf16 MFMA with operands transposed on their way into
 // LDS, or fp32 FMA), which take any layout.  The recomputation of a and u
 // uses the forward's grouped GEMM (on the persistent path one dual-tile
@@ -583,46 +583,12 @@ __global__ __launch_bounds__(256) void sum_chunks_kernel(const float* part, int 
     dst[j] = v;
 }
 
-// ---- transposes feeding the backward's GEMMs on the forward kernel ----------------
-// That kernel reads both operands along K.  The data gradients contract the
-// weights over their output dimension and the weight gradients sum over rows,
-// so those operands are transposed first (HBM-bound copies, 64 x 64 tiles
-// through LDS, 16-byte loads and stores).
+// ---- transposes feeding the backward's weight gradients on the forward kernel ----------
+// Its grouped-K mode reads both operands along K, and the weight gradients
+// sum over rows, so the pairs' activations are transposed first (HBM-bound
+// copies, 64 x 64 tiles through LDS).
 
 constexpr int kTT = 64;   // transpose tile edge
-
-// dst[b][c][col0 + r] = src[b][r][c] for r < R, c < C (multiples of 64).
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* src, int64_t s_bstride, int64_t ld_src,
-                                                             uint16_t* dst, int64_t d_bstride, int64_t ld_dst,
-                                                             int col0) {
-    __shared__ uint16_t tile[kTT][kTT + 2];
-    const int c0 = blockIdx.x * kTT, r0 = blockIdx.y * kTT;
-    const uint16_t* S = src + blockIdx.z * s_bstride;
-    uint16_t* D = dst + blockIdx.z * d_bstride;
-    const int t = threadIdx.x, cc = (t & 7) * 8;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int r = (t >> 3) + 32 * h;
-        const uint4 v = *reinterpret_cast<const uint4*>(S + (int64_t)(r0 + r) * ld_src + c0 + cc);
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            tile[r][cc + 2 * i] = (uint16_t)(w4[i] & 0xFFFFu);
-            tile[r][cc + 2 * i + 1] = (uint16_t)(w4[i] >> 16);
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int c = (t >> 3) + 32 * h;
-        uint32_t w4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            w4[i] = (uint32_t)tile[cc + 2 * i][c] | ((uint32_t)tile[cc + 2 * i + 1][c] << 16);
-        *reinterpret_cast<uint4*>(D + (int64_t)(c0 + c) * ld_dst + col0 + r0 + cc) =
-            make_uint4(w4[0], w4[1], w4[2], w4[3]);
-    }
-}
 
 // Rows of each group as columns: for q < kofs[G] (one group: q < kpad), in the
 // group e with kofs[e] <= q < kofs[e + 1] and j = q - kofs[e]:
@@ -841,19 +807,6 @@ hipError_t launch_dl_split(const float* dl, int T, int E, int Tr, uint16_t* out,
 hipError_t launch_sum_chunks(const float* part, int chunks, int64_t n, float* dst, hipStream_t s) {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(sum_chunks_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, chunks, n, dst);
-    return hipGetLastError();
-}
-
-hipError_t launch_transpose_bf16(const void* src, int64_t s_bstride, int64_t ld_src, int R, int C, int batch,
-                                 void* dst, int64_t d_bstride, int64_t ld_dst, int col0, hipStream_t s) {
-    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-    if (R % kTT || C % kTT || ld_src % 8 || ld_dst % 8 || col0 % 8 || s_bstride % 8 || d_bstride % 8 ||
-        !al16(src) || !al16(dst) || ld_src < C || ld_dst < col0 + R)
-        return hipErrorInvalidValue;
-    if (R == 0 || C == 0 || batch == 0) return hipSuccess;
-    hipLaunchKernelGGL(transpose_bf16_kernel, dim3(C / kTT, R / kTT, batch), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(src), s_bstride, ld_src, static_cast<uint16_t*>(dst), d_bstride,
-                       ld_dst, col0);
     return hipGetLastError();
 }
 

@@ -437,6 +437,12 @@ struct DmaSrc {
     uint32_t ao[J], bo[J];
     int rot;        // first K stage of the walk (stage s reads stage (s + rot) mod stages)
     int kt;         // grouped K: stages of the tile
+    // B stored [K, N] (N contiguous): K stage s (counted from the start of K)
+    // at b + s bstage, or from stage khalf on at b1 + (s - khalf) bstage;
+    // kbase: the first stage of the tile's K split
+    const char* b1;
+    uint32_t bstage;
+    int khalf, kbase;
 };
 
 // NW waves; wave w stages rows (256 / NW) w .. (256 / NW)(w + 1) - 1 of the A
@@ -506,6 +512,71 @@ __device__ __forceinline__ DmaSrc<32 / NW> dma_src(const GemmGroup& g, const Til
         s.bo[j] = (uint32_t)(DUAL ? (r & 127) : r) * K2 + c * 16;
     }
     return s;
+}
+
+// B stored [K, N] with N contiguous (the backward's data gradients read the
+// weights as they are).  A stage holds 64 K rows of 256 columns (512 bytes);
+// each DMA instruction fills two rows, lane i row i / 32 and 16-byte chunk
+// i % 32, which holds logical chunk (i % 32) ^ 4 bt_swz(row): the 64-byte
+// granules are permuted per row so that the eight rows one transposed read
+// touches sit in different granules.
+__device__ __forceinline__ int bt_swz(int kr) { return (kr & 3) | ((kr & 8) >> 1); }
+
+template <int NW>
+__device__ __forceinline__ DmaSrc<32 / NW> dma_src_bt(const GemmGroup& g, const TileRef& t, const int* src, int w,
+                                                     int lane, int k_split) {
+    constexpr int J = 32 / NW;
+    static_assert(NW == 8, "two B rows per instruction and wave");
+    const uint32_t K2 = (uint32_t)g.K * 2;
+    const int64_t k0 = (int64_t)t.ks * k_split * 2;
+    DmaSrc<J> s;
+    s.rot = __builtin_amdgcn_readfirstlane((t.n0 / 256 + 17 * t.grp) % (k_split / kBK));
+    s.kt = 0;
+    s.a = static_cast<const char*>(g.A) + (g.gather ? 0 : (int64_t)t.row0 * K2) + k0;
+    const int64_t kb = g.b_khalf ? g.b_khalf : g.K;       // K rows of one source per group
+    const int64_t bofs = ((int64_t)t.grp * kb * g.N + t.n0) * 2;
+    s.b = static_cast<const char*>(g.B0) + bofs;
+    s.b1 = static_cast<const char*>(g.b_khalf ? g.B1 : g.B0) + bofs;
+    s.bstage = (uint32_t)kBK * (uint32_t)g.N * 2;
+    s.khalf = g.b_khalf ? (int)(g.b_khalf / kBK) : 0x7FFFFFFF;
+    s.kbase = t.ks * (k_split / kBK);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int r = w * (256 / NW) + j * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
+        const int a_row = g.gather ? src[j] / g.gather_div : src[j];
+        s.ao[j] = (uint32_t)a_row * K2 + c * 16;
+        const int kr = 2 * (J * w + j) + (lane >> 5);     // K row of the stage
+        const int cb = (lane & 31) ^ (4 * bt_swz(kr));
+        s.bo[j] = ((uint32_t)kr * (uint32_t)g.N + 8u * cb) * 2;
+    }
+    return s;
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// The B fragment of one MFMA step from an N-major stage: two transposed LDS
+// reads (ds_read_b64_tr_b16).  In each group of 16 lanes the read hands lane
+// i element i % 4 of the 8-byte pieces read by lanes i / 4, 4 + i / 4,
+// 8 + i / 4 and 12 + i / 4; source lane a of group q points at K row
+// 8 (q / 2) + a / 4 (+ 4 for the second read) and columns 16 (q % 2) + 4 (a % 4)
+// of the 32-column block, so lane l receives K rows 8 (l / 32) .. + 7 of
+// column l % 32, the layout the MFMA expects.  off: the lane's element
+// offset for step 0 (steps are 16 rows apart).
+__device__ __forceinline__ int bt_frag_offset(int n_blk, int lane) {
+    const int q = lane >> 4, a = lane & 15;
+    const int kr = 8 * (q >> 1) + (a >> 2);
+    const int col = n_blk + 16 * (q & 1) + 4 * (a & 3);
+    return kr * 256 + 8 * ((col >> 3) ^ (4 * bt_swz(kr))) + (col & 7);
+}
+
+__device__ __forceinline__ bf16x8_t load_b_tr(const uint16_t* sB, int off) {
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(sB + off));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(sB + off + 4 * 256));
+    const v8i16_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
 }
 
 // Stores one 32 x 32 block of MFMA results as bf16.  Lane (half, r32) holds
@@ -638,6 +709,9 @@ __device__ __forceinline__ int next_tile_step(const TileQueue& ts, int* next, in
 
 // Kernel modes: forward (bf16 C), fp32 C over grouped rows, fp32 C over grouped K.
 constexpr int kModeFwd = 0, kModeF32 = 1, kModeKgroup = 2;
+// fp32 C over grouped rows with B stored [K, N], N contiguous (B0, and B1 for
+// K rows from b_khalf on)
+constexpr int kModeF32BT = 4;
 // dual only: both products stored as bf16, A B0^T to C and A B1^T to C2 (the
 // backward's recomputed pre-activations)
 constexpr int kModeDualOut = 3;
@@ -678,6 +752,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     constexpr int BM = 256;
     constexpr int BN = DUAL ? 128 : 256;
     constexpr bool KG = MODE == kModeKgroup;
+    constexpr bool BT = MODE == kModeF32BT;
     static_assert(MODE == kModeFwd || !DUAL || MODE == kModeDualOut, "fp32 products are single GEMMs");
     static_assert(MODE != kModeDualOut || DUAL, "two outputs need the dual tile");
     static_assert(!QUEUE || MODE == kModeFwd, "the tile queue serves the forward GEMMs");
@@ -721,11 +796,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     }
 
     const int half = lane >> 5, r32 = lane & 31;
-    int a_row[4], b_row[2];
+    int a_row[4], b_row[2], bt_off[2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) a_row[i] = wm * 128 + i * 32 + r32;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) b_row[b] = DUAL ? b * 128 + wn * 32 + r32 : wn * 64 + b * 32 + r32;
+    for (int b = 0; b < 2; ++b) {
+        b_row[b] = DUAL ? b * 128 + wn * 32 + r32 : wn * 64 + b * 32 + r32;
+        bt_off[b] = BT ? bt_frag_offset(wn * 64 + b * 32, lane) : 0;
+    }
 
 // Refill of a stage buffer: every A and B instruction, unconditionally (rows
 // past the tile's end repeat its last row).  Skipping A instructions of empty
@@ -737,7 +815,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
         const int kw_ = KG ? (src_).kt : KT;                                                    \
         const int kp_ = kr_ >= kw_ ? kr_ - kw_ : kr_;                                           \
         const char* ab_ = (src_).a + kp_ * (kBK * 2);                                           \
-        const char* bb_ = (src_).b + kp_ * (kBK * 2);                                           \
+        const char* bb_;                                                                        \
+        if constexpr (BT) {                                                                     \
+            const int gs_ = (src_).kbase + kp_;                                                 \
+            const bool hi_ = gs_ >= (src_).khalf;                                               \
+            bb_ = (hi_ ? (src_).b1 : (src_).b) + (size_t)(hi_ ? gs_ - (src_).khalf : gs_) * (src_).bstage; \
+        } else {                                                                                \
+            bb_ = (src_).b + kp_ * (kBK * 2);                                                   \
+        }                                                                                       \
         _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                         \
             __builtin_amdgcn_global_load_lds(ab_ + (src_).ao[j],                                \
                                              (lds_ptr_t)((sA_) + (w * 32 + j * 8) * kBK), 16, 0, 0); \
@@ -751,8 +836,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
         const int c_ = 2 * (s_) + half;                                                         \
         _Pragma("unroll") for (int i = 0; i < (NA_); ++i) af_[i] = as_bf16x8(                   \
             *reinterpret_cast<const uint4*>((sA_) + a_row[i] * kBK + ((c_ ^ swz(a_row[i])) * 8))); \
-        _Pragma("unroll") for (int b = 0; b < ((NA_) ? 2 : 0); ++b) bf_[b] = as_bf16x8(         \
-            *reinterpret_cast<const uint4*>((sB_) + b_row[b] * kBK + ((c_ ^ swz(b_row[b])) * 8))); \
+        _Pragma("unroll") for (int b = 0; b < ((NA_) ? 2 : 0); ++b) bf_[b] = BT                 \
+            ? load_b_tr((sB_), bt_off[b] + (s_) * (16 * 256))                                   \
+            : as_bf16x8(*reinterpret_cast<const uint4*>((sB_) + b_row[b] * kBK + ((c_ ^ swz(b_row[b])) * 8))); \
     } while (0)
 #define MOE_MFMAS(af_, bf_, NA_)                                                                \
     do {                                                                                        \
@@ -813,7 +899,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
             MOE_STAGE(NA_, NA_, sA0, sB0, sA1, sB1, cur, kt + 2, true);                         \
             MOE_STAGE(NA_, NA_, sA1, sB1, sA0, sB0, cur, kt + 3, true);                         \
         }                                                                                       \
-        nxt = dma_src<DUAL, 8, KG>(g, tn, gsrc, w, lane, KT * kBK);                              \
+        nxt = make_src(tn);                                                                     \
         MOE_STAGE(NA_, NA_, sA0, sB0, sA1, sB1, nxt, 0, more);                                  \
         MOE_STAGE(NA_, 4, sA1, sB1, sA0, sB0, nxt, 1, more);                                    \
     } while (0)
@@ -826,7 +912,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     TileRef tr = tile_of(L);
     int gsrc[4];
     gather_rows<8>(g, tr, w, lane, gsrc);
-    DmaSrc<4> cur = dma_src<DUAL, 8, KG>(g, tr, gsrc, w, lane, KT * kBK);
+    auto make_src = [&](const TileRef& t) {
+        if constexpr (BT) return dma_src_bt<8>(g, t, gsrc, w, lane, KT * kBK);
+        else return dma_src<DUAL, 8, KG>(g, t, gsrc, w, lane, KT * kBK);
+    };
+    DmaSrc<4> cur = make_src(tr);
     bf16x8_t fa0[4], fb0[2], fa1[4], fb1[2];
     // prologue: the first tile's stages 0 and 1
     MOE_DMA(sA0, sB0, cur, 0);
@@ -1176,6 +1266,19 @@ hipError_t launch_bf16_f32out(const GemmGroup& g, hipStream_t s) {
     if (g.splitk < 1 || g.K % (128 * g.splitk) || (g.accumulate && g.splitk != 1) ||
         a_rows * g.K * 2 >= (int64_t(1) << 32))
         return hipErrorInvalidValue;
+    if (g.b_nmajor) {
+        // 32-bit offsets inside one B stage (64 rows of N); two sources split at a stage boundary
+        if ((int64_t)kBK * g.N * 2 >= (int64_t(1) << 32) || (g.b_khalf && (g.K != 2 * g.b_khalf ||
+            g.b_khalf % kBK || !g.B1 || !al16(g.B1))))
+            return hipErrorInvalidValue;
+        if (g.aligned_bands)
+            hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<false, true, kModeF32BT>), grid, block, 0, s,
+                                  g.t_start, g.t_stop, 0, g, g.N / 256);
+        else
+            hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<false, false, kModeF32BT>), grid, block, 0, s,
+                                  g.t_start, g.t_stop, 0, g, g.N / 256);
+        return hipGetLastError();
+    }
     if (g.aligned_bands)
         hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<false, true, kModeF32>), grid, block, 0, s, g.t_start,
                               g.t_stop, 0, g, g.N / 256);

@@ -395,7 +395,7 @@ struct BwdLayout {
     size_t counts, offsets, sorted, pos, chunk, A, U, H, DA, DU, dHp, dO, dXp, dgate, logits, dl, rw, auxcnt, DLT, XT2;
     size_t As, Us, Hs, DAs, DUs, dHs;
     // fast path: DA and DU share rows [da | du] (DA), transposed operands
-    size_t kofs, WdT, WguT, dOT, HT, DADUT, XgT, WsdT, WsguT, dyT, HsT, DADUsT, xT;
+    size_t kofs, dOT, HT, DADUT, XgT, dyT, HsT, DADUsT, xT;
     size_t total;
 };
 
@@ -431,8 +431,6 @@ BwdLayout bwd_layout(const moe_config* c) {
         L.DA = take(P * 2 * f * w);
         L.dXp = take((size_t)pl.xsplit * P * d * 4);
         L.kofs = take((E + 1) * 4);
-        L.WdT = take(E * f * d * w);
-        L.WguT = take(E * d * 2 * f * w);
         L.dOT = take(d * Q * w);
         L.HT = take(f * Q * w);
         L.DADUT = take(2 * f * Q * w);
@@ -449,8 +447,6 @@ BwdLayout bwd_layout(const moe_config* c) {
     L.dHs = take(T * fs * 4);
     if (pl.shared_fast) {
         L.DAs = take(T * 2 * fs * w);
-        L.WsdT = take(fs * d * w);
-        L.WsguT = take(d * 2 * fs * w);
         L.dyT = take(d * Tq * w);
         L.HsT = take(fs * Tq * w);
         L.DADUsT = take(2 * fs * Tq * w);
@@ -545,12 +541,11 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
     if (pl.fast) {
         const int64_t Q = pl.Q;
         int32_t* kofs = at<int32_t>(ws, L.kofs);
-        void *WdT = at<void>(ws, L.WdT), *WguT = at<void>(ws, L.WguT);
         void *dOT = at<void>(ws, L.dOT), *HT = at<void>(ws, L.HT), *DADUT = at<void>(ws, L.DADUT);
         void* XgT = at<void>(ws, L.XgT);
-        // dH' = dy W_down: W_down^T [E, f, d] makes the contraction K-contiguous
-        MOE_HIP(launch_transpose_bf16(wd, (int64_t)d * f, f, d, f, E, WdT, (int64_t)f * d, d, 0, s));
-        GemmGroup g1 = f32_gemm(dy, sorted, k, offsets, E, P, WdT, dHp, f, f, d);
+        // dH' = dy W_down, reading W_down [E, d, f] as it is (K = d rows of N = f)
+        GemmGroup g1 = f32_gemm(dy, sorted, k, offsets, E, P, wd, dHp, f, f, d);
+        g1.b_nmajor = true;
         g1.aligned_bands = aligned;
         MOE_HIP(launch_grouped_gemm(g1, false, true, s));
         // h, dg, [da | du] per pair
@@ -558,10 +553,12 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
                        dy, nullptr, f, d};
         pa.ld_dadu = 2 * (int64_t)f;
         MOE_HIP(launch_bwd_pair(pa, P, true, s));
-        // dx of each pair = [da | du] [W_gate^T | W_up^T]^T (one K walk of 2 f)
-        MOE_HIP(launch_transpose_bf16(wg, (int64_t)f * d, d, f, d, E, WguT, (int64_t)d * 2 * f, 2 * f, 0, s));
-        MOE_HIP(launch_transpose_bf16(wu, (int64_t)f * d, d, f, d, E, WguT, (int64_t)d * 2 * f, 2 * f, f, s));
-        GemmGroup g2 = f32_gemm(DA, nullptr, 1, offsets, E, P, WguT, dXp, d, d, 2 * f);
+        // dx of each pair = [da | du] [W_gate ; W_up] (one K walk of 2 f: rows of
+        // W_gate [E, f, d], then of W_up, read as they are)
+        GemmGroup g2 = f32_gemm(DA, nullptr, 1, offsets, E, P, wg, dXp, d, d, 2 * f);
+        g2.B1 = wu;
+        g2.b_nmajor = true;
+        g2.b_khalf = f;
         g2.splitk = pl.xsplit;
         g2.part_stride = (int64_t)P * d;
         g2.aligned_bands = true;
@@ -657,18 +654,19 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
         MOE_HIP(launch_grouped_gemm(su_, false, bf16, s));
         if (pl.shared_fast) {
             const int64_t Tq = pl.Tq;
-            void *WsdT = at<void>(ws, L.WsdT), *WsguT = at<void>(ws, L.WsguT), *dyT = at<void>(ws, L.dyT);
+            void* dyT = at<void>(ws, L.dyT);
             void *HsT = at<void>(ws, L.HsT), *DADUsT = at<void>(ws, L.DADUsT), *xT = at<void>(ws, L.xT);
-            MOE_HIP(launch_transpose_bf16(sd, 0, fs, d, fs, 1, WsdT, 0, d, 0, s));
-            GemmGroup s1 = f32_gemm(dy, nullptr, 1, nullptr, 1, T, WsdT, dHs, fs, fs, d);
+            GemmGroup s1 = f32_gemm(dy, nullptr, 1, nullptr, 1, T, sd, dHs, fs, fs, d);
+            s1.b_nmajor = true;
             MOE_HIP(launch_grouped_gemm(s1, false, true, s));
             BwdPairArgs sp{nullptr, nullptr, 1, 1, nullptr, As, Us, dHs, Hs, DAs, static_cast<char*>(DAs) + fs * w,
                            nullptr, dy, nullptr, fs, d};
             sp.ld_dadu = 2 * (int64_t)fs;
             MOE_HIP(launch_bwd_pair(sp, T, true, s));
-            MOE_HIP(launch_transpose_bf16(sg, 0, d, fs, d, 1, WsguT, 0, 2 * fs, 0, s));
-            MOE_HIP(launch_transpose_bf16(su, 0, d, fs, d, 1, WsguT, 0, 2 * fs, fs, s));
-            GemmGroup s2 = f32_gemm(DAs, nullptr, 1, nullptr, 1, T, WsguT, dx, d, d, 2 * fs);
+            GemmGroup s2 = f32_gemm(DAs, nullptr, 1, nullptr, 1, T, sg, dx, d, d, 2 * fs);
+            s2.B1 = su;
+            s2.b_nmajor = true;
+            s2.b_khalf = fs;
             s2.accumulate = true;
             MOE_HIP(launch_grouped_gemm(s2, false, true, s));
             const int tq = (int)Tq;

@@ -85,6 +85,12 @@ struct GemmGroup {
     //     M and N multiples of 256.
     bool f32_out = false;
     bool accumulate = false;
+    //   b_nmajor (f32_out, persistent kernel): B stored [G][K][N] with N
+    //     contiguous instead of [G][N][K]; with b_khalf > 0 (K == 2 b_khalf)
+    //     K rows from b_khalf on come from B1 [G][b_khalf][N] (the weights as
+    //     they are: no transposed copies for the data gradients)
+    bool b_nmajor = false;
+    int64_t b_khalf = 0;
     // dual, bf16, persistent kernel only: C = A B0^T and C2 = A B1^T, both
     // [rows, N] bf16 (no SiLU product)
     void* C2 = nullptr;
@@ -198,10 +204,6 @@ hipError_t launch_sum_chunks(const float* part, int chunks, int64_t n, float* ds
 hipError_t launch_router_wgrad(const float* dl, const void* x, bool x_bf16, int T, int E, int d, float* part,
                                float* dwr, hipStream_t s);
 
-// bf16 transposes for the backward's GEMMs on the forward kernel.
-// dst[b][c][col0 + r] = src[b][r][c]; R, C multiples of 64; strides multiples of 8.
-hipError_t launch_transpose_bf16(const void* src, int64_t s_bstride, int64_t ld_src, int R, int C, int batch,
-                                 void* dst, int64_t d_bstride, int64_t ld_dst, int col0, hipStream_t s);
 // Grouped rows as columns, each group's columns starting at kofs[g] (zero past its rows).
 struct TransposeRowsArgs {
     const uint16_t* src;    // source rows [*, ld_src], columns c < C (C multiple of 64)
