@@ -755,7 +755,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     constexpr bool BT = MODE == kModeF32BT;
     static_assert(MODE == kModeFwd || !DUAL || MODE == kModeDualOut, "fp32 products are single GEMMs");
     static_assert(MODE != kModeDualOut || DUAL, "two outputs need the dual tile");
-    static_assert(!QUEUE || MODE == kModeFwd, "the tile queue serves the forward GEMMs");
+    static_assert(!QUEUE || (MODE != kModeKgroup && MODE != kModeF32), "no tile queue in these modes");
     constexpr int STG = 256 * kBK;    // elements of one A or B stage (32 KB)
     __shared__ __align__(16) uint16_t sA0[STG], sA1[STG];
     __shared__ __align__(16) uint16_t sB0[STG], sB1[STG];
@@ -1271,7 +1271,11 @@ hipError_t launch_bf16_f32out(const GemmGroup& g, hipStream_t s) {
         if ((int64_t)kBK * g.N * 2 >= (int64_t(1) << 32) || (g.b_khalf && (g.K != 2 * g.b_khalf ||
             g.b_khalf % kBK || !g.B1 || !al16(g.B1))))
             return hipErrorInvalidValue;
-        if (g.aligned_bands)
+        if (g.queue && !g.aligned_bands) return hipErrorInvalidValue;
+        if (g.queue)
+            hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<false, true, kModeF32BT, true>), grid, block, 0, s,
+                                  g.t_start, g.t_stop, 0, g, g.N / 256);
+        else if (g.aligned_bands)
             hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<false, true, kModeF32BT>), grid, block, 0, s,
                                   g.t_start, g.t_stop, 0, g, g.N / 256);
         else
@@ -1371,7 +1375,11 @@ hipError_t launch_grouped_gemm(const GemmGroup& g, bool dual, bool bf16, hipStre
             g.N % 128 || a_rows * g.K * 2 >= (int64_t(1) << 32))
             return hipErrorInvalidValue;
         const dim3 grid(persistent_grid()), block(512);
-        if (g.aligned_bands)
+        if (g.queue && !g.aligned_bands) return hipErrorInvalidValue;
+        if (g.queue)
+            hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<true, true, kModeDualOut, true>), grid, block, 0, s,
+                                  g.t_start, g.t_stop, 0, g, g.N / 128);
+        else if (g.aligned_bands)
             hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<true, true, kModeDualOut>), grid, block, 0, s,
                                   g.t_start, g.t_stop, 0, g, g.N / 128);
         else

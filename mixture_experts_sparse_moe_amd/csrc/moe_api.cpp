@@ -393,6 +393,7 @@ BwdPlan bwd_plan(const moe_config* c) {
 
 struct BwdLayout {
     size_t counts, offsets, sorted, pos, chunk, A, U, H, DA, DU, dHp, dO, dXp, dgate, logits, dl, rw, auxcnt, DLT, XT2;
+    size_t queue;   // fast path: tile-queue counters of the three routed GEMMs over the pairs
     size_t As, Us, Hs, DAs, DUs, dHs;
     // fast path: DA and DU share rows [da | du] (DA), transposed operands
     size_t kofs, dOT, HT, DADUT, XgT, dyT, HsT, DADUsT, xT;
@@ -428,6 +429,7 @@ BwdLayout bwd_layout(const moe_config* c) {
     }
     L.auxcnt = take(E * 4);
     if (pl.fast) {
+        L.queue = take(3 * 256 * 4);
         L.DA = take(P * 2 * f * w);
         L.dXp = take((size_t)pl.xsplit * P * d * 4);
         L.kofs = take((E + 1) * 4);
@@ -518,17 +520,22 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
 
     // routing groups of the forward's ids; pairs past an expert's capacity are
     // left out of the groups (pair_pos -1), as in the forward
-    MOE_TRY(run_dispatch(c, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s, cap));
+    // The routed GEMMs over the pairs take the forward's tile orders: expert-
+    // aligned bands, and with about one M tile per expert (fewer than 640 rows)
+    // tiles claimed through counters, which the dispatch zeroes on its way.
+    const bool aligned = (int64_t)P >= (int64_t)640 * E;
+    int32_t* q = pl.fast && !aligned && P > 0 ? at<int32_t>(ws, L.queue) : nullptr;
+    MOE_TRY(run_dispatch(c, ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk), s, cap, q,
+                         q ? 3 * 256 : 0));
     // a dropped pair's gate gets no gradient (the pair kernel writes kept pairs only)
     if ((int64_t)cap < P) MOE_HIP(launch_fill_zero_f32(dgate, P, s));
-    // a = x W_gate^T, u = x W_up^T on the grouped rows (the forward's GEMM, with
-    // its expert-aligned tile order when experts hold several M tiles)
-    const bool aligned = (int64_t)P >= (int64_t)640 * E;
+    // a = x W_gate^T, u = x W_up^T on the grouped rows (the forward's GEMM)
     if (pl.fast) {
         // both from one dual-tile GEMM (the gathered x rows are read once)
         GemmGroup gau{x, sorted, k, offsets, E, P, wg, wu, A, f, d};
         gau.C2 = U;
-        gau.aligned_bands = aligned;
+        gau.aligned_bands = aligned || q;
+        gau.queue = q;
         MOE_HIP(launch_grouped_gemm(gau, true, true, s));
     } else {
         GemmGroup ga{x, sorted, k, offsets, E, P, wg, nullptr, A, f, d};
@@ -546,7 +553,8 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
         // dH' = dy W_down, reading W_down [E, d, f] as it is (K = d rows of N = f)
         GemmGroup g1 = f32_gemm(dy, sorted, k, offsets, E, P, wd, dHp, f, f, d);
         g1.b_nmajor = true;
-        g1.aligned_bands = aligned;
+        g1.aligned_bands = aligned || q;
+        g1.queue = q ? q + 256 : nullptr;
         MOE_HIP(launch_grouped_gemm(g1, false, true, s));
         // h, dg, [da | du] per pair
         BwdPairArgs pa{sorted, offsets, E, k, gates, A, U, dHp, H, DA, static_cast<char*>(DA) + f * w, dgate,
@@ -562,6 +570,7 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
         g2.splitk = pl.xsplit;
         g2.part_stride = (int64_t)P * d;
         g2.aligned_bands = true;
+        g2.queue = q ? q + 512 : nullptr;
         MOE_HIP(launch_grouped_gemm(g2, false, true, s));
         MOE_HIP(launch_bwd_token_sum(dXp, pos, T, k, d, dx, s, pl.xsplit, (int64_t)P * d));
         // weight gradients: each expert's rows as a K range of transposed operands
