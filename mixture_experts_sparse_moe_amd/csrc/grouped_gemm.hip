@@ -656,7 +656,8 @@ __device__ __forceinline__ void store_block_f32(float* Cf, int64_t ldc, int rows
     }
 }
 
-// Tile queue of a persistent workgroup (forward GEMMs with ragged groups).
+// Tile queue of a persistent workgroup (GEMMs over ragged expert groups: the
+// forward's, and the backward's recomputation, dH' and dx).
 // Each XCD's range [xcd per, end) of logical tiles is walked in rounds as
 // without the queue, but only the first three rounds are fixed (tile
 // xcd per + r nslot + slot for round r); later tiles are claimed through
