@@ -493,14 +493,22 @@ __global__ __launch_bounds__(1024) void count_ids_kernel(const int32_t* ids, int
 __global__ __launch_bounds__(256) void bwd_token_sum_kernel(const float* dxp, const int32_t* pair_pos, int k, int d,
                                                             float* dx, int splitk, int64_t part_stride) {
     const int t = blockIdx.x;
-    for (int c = threadIdx.x; c < d; c += 256) {
-        float v = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            const int pos = pair_pos[(int64_t)t * k + j];
-            if (pos < 0) continue;
-            for (int sl = 0; sl < splitk; ++sl) v += dxp[sl * part_stride + (int64_t)pos * d + c];
+    int pos[16];                     // k <= 16
+#pragma unroll
+    for (int j = 0; j < 16; ++j) pos[j] = j < k ? pair_pos[(int64_t)t * k + j] : -1;
+    // 4 columns per thread (d % 4 == 0, slices and rows 16-byte aligned); each
+    // column still sums slots in order, slices in order
+    for (int c = threadIdx.x * 4; c < d; c += 1024) {
+        float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (pos[j] < 0) continue;
+            for (int sl = 0; sl < splitk; ++sl) {
+                const float4 q = *reinterpret_cast<const float4*>(dxp + sl * part_stride + (int64_t)pos[j] * d + c);
+                v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+            }
         }
-        dx[(int64_t)t * d + c] = v;
+        *reinterpret_cast<float4*>(dx + (int64_t)t * d + c) = v;
     }
 }
 
@@ -567,6 +575,19 @@ __global__ __launch_bounds__(256) void dl_split_kernel(const float* dl, int T, i
         row[0] = hi;
         row[Tr] = f32_to_bf16(v - bf16_to_f32(hi));
     }
+}
+
+// out [T, 2 E] bf16: out[t][e] = dl[t][e] rounded to bf16, out[t][E + e] the
+// rest rounded to bf16 (the router's part of dx, dl W_r, as one bf16 product
+// over 2 E columns against W_r read twice).
+__global__ __launch_bounds__(256) void dl_rows_kernel(const float* dl, int64_t n, int E, uint16_t* out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int64_t t = i / E, e = i - t * E;
+    const float v = dl[i];
+    const uint16_t hi = f32_to_bf16(v);
+    out[t * 2 * E + e] = hi;
+    out[t * 2 * E + E + e] = f32_to_bf16(v - bf16_to_f32(hi));
 }
 
 // p[0 .. n) = 0 (a fill kernel rather than a memset, so the call stays capturable).
@@ -801,6 +822,13 @@ hipError_t launch_dl_split(const float* dl, int T, int E, int Tr, uint16_t* out,
     if (T < 0 || E <= 0 || Tr < T || Tr % 64) return hipErrorInvalidValue;
     if (Tr == 0) return hipSuccess;
     hipLaunchKernelGGL(dl_split_kernel, dim3(Tr / 64, (E + 63) / 64), dim3(256), 0, s, dl, T, E, Tr, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_dl_rows(const float* dl, int T, int E, uint16_t* out, hipStream_t s) {
+    const int64_t n = (int64_t)T * E;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(dl_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dl, n, E, out);
     return hipGetLastError();
 }
 

@@ -199,6 +199,9 @@ int router_wgrad_chunks(int T, int d, int E);
 // out [E, 2 Tr] bf16 from dl [T, E] fp32: columns t < Tr hold dl rounded to
 // bf16, columns Tr + t the rest rounded to bf16 (zero for t >= T); Tr % 64 == 0.
 hipError_t launch_dl_split(const float* dl, int T, int E, int Tr, uint16_t* out, hipStream_t s);
+// out [T, 2 E] bf16: dl rounded to bf16 in columns e < E, the rest rounded to
+// bf16 in columns E + e.
+hipError_t launch_dl_rows(const float* dl, int T, int E, uint16_t* out, hipStream_t s);
 // dst[j] = sum over c < chunks, in order, of part[c n + j].
 hipError_t launch_sum_chunks(const float* part, int chunks, int64_t n, float* dst, hipStream_t s);
 hipError_t launch_router_wgrad(const float* dl, const void* x, bool x_bf16, int T, int E, int d, float* part,
