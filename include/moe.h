@@ -18,7 +18,10 @@
  * Conventions shared by every entry point:
  *   - Ownership: the caller owns every buffer.  The library never allocates
  *     or frees device memory and keeps no state between calls (beyond the
- *     device's compute-unit count, read once); calls are thread-safe.
+ *     device's compute-unit count, read once); calls are thread-safe.  A
+ *     workspace is scratch for one call at a time (each call sets up what it
+ *     needs in it, tile counters included): calls that may run together on
+ *     different streams need workspaces of their own.
  *   - Pointers: every tensor pointer is a DEVICE pointer (HBM of the current
  *     HIP device).  `cfg` is a HOST pointer read during the call only.
  *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
