@@ -141,8 +141,14 @@ def route(lg: np.ndarray, k: int, score_fn: int = SOFTMAX, renormalize: int = 1,
 
 def capacity(T: int, k: int, E: int, factor: float) -> int:
     """Slots per expert: ceil(T * k / E * factor) ("8.6 Mixture of Experts",
-    sec. 3.2; the pages leave the rounding open)."""
-    return int(np.ceil(T * k / E * factor - 1e-9))
+    sec. 3.2; "from the router to the all-to-all", Capacity and token
+    dropping: tokens per batch over experts, times k, times the factor).  The
+    pages leave the rounding open; the ceiling keeps every slot the formula
+    grants.  Evaluated exactly in rational arithmetic, the factor taken as the
+    decimal it prints as (1.1 is 11/10, not the nearest binary double)."""
+    from fractions import Fraction
+    q = Fraction(int(T) * int(k), int(E)) * Fraction(repr(float(factor)))
+    return int(-((-q.numerator) // q.denominator))
 
 
 def dispatch(ids: np.ndarray, E: int, cap: int | None = None) -> dict:
@@ -164,15 +170,19 @@ def dispatch(ids: np.ndarray, E: int, cap: int | None = None) -> dict:
 
 
 def router_stats(scores: np.ndarray, ids: np.ndarray, score_fn: int = SOFTMAX,
-                 alpha: float = 1.0) -> dict:
+                 alpha: float = 1.0, cap: int | None = None) -> dict:
     """Load-balancing statistics of one batch ("8.6 Mixture of Experts",
-    sec. 3.1; "from the router to the all-to-all", Load balancing):
+    sec. 3.1; "from the router to the all-to-all", Load balancing; "T2.6 --
+    What Mixture of Experts Changes", In practice: per-expert counts,
+    maximum-to-mean load and capacity overflow):
       f_e = n_e / T, with n_e the pairs routed to expert e (before any
             capacity drop); sum_e f_e = k;
       P_e = mean over tokens of the router probability of e: the softmax
             score, or the sigmoid score normalised over all experts;
       L_aux = alpha * E * sum_e f_e P_e (= alpha under uniform routing, k = 1);
-      max_over_mean = max_e n_e / mean_e n_e."""
+      max_over_mean = max_e n_e / mean_e n_e;
+      overflow = pairs an expert capacity ``cap`` drops, sum_e max(0, n_e - cap)
+            (0 without a capacity)."""
     scores = np.asarray(scores, dtype=np.float64)
     T, E = scores.shape
     ids = np.asarray(ids)
@@ -184,7 +194,13 @@ def router_stats(scores: np.ndarray, ids: np.ndarray, score_fn: int = SOFTMAX,
     f = n / T
     P = prob.sum(0) / T
     l_aux = alpha * E * float(np.sum(f * P))
-    return dict(f=f, P=P, l_aux=l_aux, max_over_mean=float(n.max() / n.mean()), counts=n)
+    overflow = 0.0
+    if cap is not None:
+        for e in range(E):
+            if n[e] > cap:
+                overflow += n[e] - cap
+    return dict(f=f, P=P, l_aux=l_aux, max_over_mean=float(n.max() / n.mean()), counts=n,
+                overflow=overflow)
 
 
 def aux_loss_logit_grad(lg: np.ndarray, ids: np.ndarray, score_fn: int = SOFTMAX,

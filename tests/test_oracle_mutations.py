@@ -39,6 +39,10 @@ MUTATIONS = {
     "backward_ignores_drops": ("            if (keep && !keep[t * k + j]) {", "            if (0) {"),
     "shared_grad_ungated_missing": ("for (int r = 0; r < f_s; ++r) dsd[(int64_t)c * f_s + r] += dyt[c] * h[r];",
                                     "for (int r = 0; r < f_s; ++r) dsd[(int64_t)c * f_s + r] += 0.5 * dyt[c] * h[r];"),
+    "expert_rows_row_index": ("swiglu_one(d, f, x, (int64_t)rows[i] * d,", "swiglu_one(d, f, x, (int64_t)i * d,"),
+    "expert_rows_h_shifted": ("if (h_out) memcpy(h_out + i * f, h, sizeof(double) * f);",
+                              "if (h_out) memcpy(h_out + i * f, h + 1, sizeof(double) * (f - 1));"),
+    "logits_row_offset": ("int64_t t = t0 + tt;", "int64_t t = tt;"),
 }
 PIN_FILES = ["test_oracle_pins.py", "test_oracle_next.py", "test_oracle_backward.py"]
 

@@ -99,6 +99,39 @@ def test_capacity_page_example():
     assert int((d["pair_pos"] == -1).sum()) == 88 + sum(max(0, int(c) - 512) for c in
                                                          np.bincount(ids.ravel(), minlength=E)[1:])
     assert oracle.capacity(T, k, E, 1.25) == 640 and oracle.capacity(10, 2, 3, 1.0) == 7
+    # the overflow the statistics report is that expert's 88 plus the others'
+    st = oracle.router_stats(np.full((T, E), 1.0 / E), ids, alpha=1.0, cap=C)
+    assert st["overflow"] == 88 + sum(max(0, int(c) - 512) for c in np.bincount(ids.ravel(), minlength=E)[1:])
+
+
+def test_capacity_rounding():
+    """ceil(T k / E * factor) with the factor read as the decimal it is
+    written as: exact products stay exact (640 * 1.1
+    is 704, though 640 * 1.1 in binary doubles is 704.0000000000001), and a
+    fractional slot count rounds up."""
+    assert oracle.capacity(80, 8, 1, 1.1) == 704
+    assert oracle.capacity(333, 2, 8, 1.0) == 84            # 83.25
+    assert oracle.capacity(4096, 2, 8, 1.25) == 1280
+    assert oracle.capacity(4096, 8, 64, 1.1) == 564         # 563.2
+    assert oracle.capacity(100, 3, 7, 2.0) == 86            # 85.71...
+    assert oracle.capacity(0, 8, 64, 1.25) == 0
+
+
+def test_stats_overflow_counts_dropped_pairs():
+    """Capacity overflow ('T2.6 -- What Mixture of Experts Changes', In
+    practice): the pairs the capacity drops, the same count the dispatch
+    leaves out (pair_pos -1); none without a capacity or with a capacity at
+    or above every count."""
+    T, E, k = 300, 16, 4
+    ids = np.stack([np.concatenate([[e % 3], RNG.permutation(np.arange(3, E))[:k - 1]])
+                    for e in range(T)]).astype(np.int32)
+    s = np.full((T, E), 1.0 / E)
+    n = np.bincount(ids.ravel(), minlength=E)
+    for cap in (1, 40, 75, int(n.max())):
+        st = oracle.router_stats(s, ids, alpha=1.0, cap=cap)
+        assert st["overflow"] == int((oracle.dispatch(ids, E, cap=cap)["pair_pos"] < 0).sum())
+    assert oracle.router_stats(s, ids)["overflow"] == 0
+    assert oracle.router_stats(s, ids, cap=int(n.max()))["overflow"] == 0
 
 
 @pytest.mark.parametrize("T,E,k,cap", [(200, 8, 2, 30), (333, 64, 8, 20), (50, 16, 4, 1)])

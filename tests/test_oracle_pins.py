@@ -208,6 +208,55 @@ def test_union_read_matches_page():
     assert abs(touched / (trials * 64) - g["value"]) < 0.002
 
 
+# --------------------------------------------------------------------------- single expert, row ranges
+
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.F32])
+def test_expert_rows_is_the_dense_expert(dtype):
+    """expert_rows(e, rows) is expert e's SwiGLU on the listed token rows
+    ('8.6 Mixture of Experts', sec. 2; 'What Actually Happens...', Step 4):
+    h = silu(W_gate,e x) * (W_up,e x) and o = W_down,e h, equal to plain
+    matmuls on the widened inputs, for experts past the first, rows out of
+    order and repeated, d != d_ff; the o of a call without h is the same."""
+    sh = synth.LayerShape("t", T=23, d=48, E=5, k=2, d_ff=40, dtype=dtype)
+    inp = synth.make_inputs(sh, 21)
+    x = _f64(inp["x"])
+    rows = np.array([7, 0, 22, 7, 13, 13, 1], dtype=np.int32)
+    for e in (1, 4):
+        wg, wu, wd = (_f64(inp[n][e]) for n in ("w_gate", "w_up", "w_down"))
+        h_want = _silu(x[rows] @ wg.T) * (x[rows] @ wu.T)
+        h, o = oracle.expert_rows(e, inp["x"], rows, inp["w_gate"], inp["w_up"], inp["w_down"], want_h=True)
+        assert h.shape == (rows.size, 40) and o.shape == (rows.size, 48)
+        np.testing.assert_allclose(h, h_want, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(o, h_want @ wd.T, rtol=1e-12, atol=1e-14)
+        h0, o0 = oracle.expert_rows(e, inp["x"], rows, inp["w_gate"], inp["w_up"], inp["w_down"])
+        assert h0 is None
+        np.testing.assert_array_equal(o0, o)
+
+
+def test_expert_rows_matches_top1_layer():
+    """Top-1 with renormalisation: each token's y is its one expert's output
+    (the Switch form, 'from the router to the all-to-all', The router), so
+    expert_rows on the tokens that chose e equals forward_tokens' y there."""
+    sh, inp = _f32_inputs(T=31, d=32, E=4, k=1, f=48, seed=17)
+    r = oracle.forward_tokens(inp, 1, np.arange(31))
+    for e in range(4):
+        toks = np.nonzero(r["ids"][:, 0] == e)[0].astype(np.int32)
+        if toks.size == 0:
+            continue
+        _, o = oracle.expert_rows(e, inp["x"], toks, inp["w_gate"], inp["w_up"], inp["w_down"])
+        np.testing.assert_allclose(o, r["y"][toks], rtol=1e-12, atol=1e-13)
+
+
+def test_logits_of_a_row_range():
+    """logits(rows=slice(a, b)) is rows a..b-1 of x W_r^T (plain matmul)."""
+    sh, inp = _f32_inputs(T=29, d=24, E=7, k=2, f=16, seed=19)
+    want = _f64(inp["x"]) @ _f64(inp["w_router"]).T
+    np.testing.assert_allclose(oracle.logits(inp["x"], inp["w_router"], rows=slice(5, 17)), want[5:17],
+                               rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(oracle.logits(inp["x"], inp["w_router"], rows=slice(20, None)), want[20:],
+                               rtol=1e-13, atol=1e-14)
+
+
 # --------------------------------------------------------------------------- whole layer
 
 def test_dense_softmax_ensemble_when_k_equals_E():
