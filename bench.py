@@ -1,19 +1,30 @@
 """Benchmark of the top-k MoE FFN layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--only]
 
 One step = one whole forward of the layer (route, dispatch, routed SwiGLU
 grouped GEMMs, shared expert, combine) over one batch of seeded synthetic
-inputs already resident in HBM.  The default workload is the Mixtral-8x7B-
-shaped prefill layer (T=4096, d=4096, E=8, k=2, d_ff=14336, bf16).
+inputs already resident in HBM.  The headline workload is the DeepSeek-V3-
+shaped layer (T=8192, d=7168, E=256, k=8, sigmoid gates renormalised over the
+8 chosen, d_ff=2048, one shared expert of 2048, bf16), the largest of the five
+layer shapes; the other four (the tiny fp32 layer, Mixtral-8x7B prefill and
+decode, Hunyuan-A13B) are measured the same way in the same run and reported
+as sub-records under "configs" (--only skips them).
 
-Prints one JSON line with the throughput (tokens/s), the roofline of the
-dominant kernel measured live with HIP events on the launch stream, and the
-CPU oracle timed on a bounded sample of the same workload on the host cores.
-The timed region records two timing events per step, around the dominant
-kernel (created without the system-scope fence, so recording them costs the
-next kernel nothing measurable); the per-stage breakdown comes from a
-separate pass with an event after every stage.
+Prints one JSON line: throughput (tokens/s), the roofline of the dominant
+kernel (the routed gate/up GEMM) measured live with HIP events on the launch
+stream, bound by the larger of its HBM and MFMA floors with the other
+fraction reported beside it, and the CPU oracle timed on a bounded sample of
+the same workload on the host cores; the oracle's outputs on that sample also
+give the parity of the timed output.  The timed region records two timing
+events per step, the gate/up kernel's own launch events (created without the
+system-scope fence, so recording them costs the next kernel nothing
+measurable); the per-stage breakdown comes from a separate pass with an
+event after every stage.
+
+Other modes: --copy-calibration and --traffic-from (HBM bytes of the gate/up
+kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE runs), --counters-from (MFMA
+busy fraction and clock per kernel from a rocprofv3 --pmc run).
 """
 from __future__ import annotations
 
@@ -33,18 +44,22 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+HEADLINE = "deepseek_v3"
+OTHERS = ("mixtral_prefill", "mixtral_decode", "hunyuan_a13b", "tiny")
+TAU = {"bf16": 2e-2, "f32": 1e-4}     # max|err| <= tau * max|y|
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="mixtral_prefill")
+    p.add_argument("--workload", default=HEADLINE)
+    p.add_argument("--only", action="store_true", help="measure the --workload alone (no sub-records)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0,
-                   help="target wall time of the CPU oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=8.0,
+                   help="target wall time of the CPU oracle sample of each workload")
     p.add_argument("--no-ceilings", action="store_true",
                    help="skip the practical ceilings (device copy, torch.matmul yardstick)")
     p.add_argument("--no-options", action="store_true",
@@ -57,6 +72,9 @@ def parse():
                    help="rocprofv3 --pmc output dirs (FETCH_SIZE run of the bench, WRITE_SIZE run "
                         "of the bench, FETCH_SIZE+WRITE_SIZE runs of --copy-calibration); writes "
                         "profiles/traffic.json for --workload")
+    p.add_argument("--counters-from", metavar="PMC_DIR",
+                   help="summarise a rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES, "
+                        "SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE per kernel")
     return p.parse_args()
 
 
@@ -147,7 +165,7 @@ def options_cost(torch, moe, cfg, d, y, ws, stream, sh, steps: int) -> dict:
     layer through the same entry point."""
     g = torch.Generator().manual_seed(0)
     bias = (torch.randn(sh.E, generator=g, dtype=torch.float32) * 0.01).to(d["x"].device)
-    stats = torch.empty(2 * sh.E + 2, dtype=torch.float32, device=d["x"].device)
+    stats = torch.empty(2 * sh.E + 3, dtype=torch.float32, device=d["x"].device)
     cap = moe.capacity(sh.T, sh.k, sh.E, 1.25)
     variants = {
         "plain": moe.MoeOptions.of(),
@@ -256,26 +274,42 @@ def practical_ceilings(torch, dev) -> dict:
 
 
 def cpu_baseline(sh, inp, target_s: float) -> dict:
-    """The oracle as it stands, on a bounded sample of tokens of the same layer."""
+    """The oracle as it stands, on a bounded sample of tokens of the same
+    layer: the first and the last token and seeded random ones, growing
+    until about target_s / 4 to target_s of work.  Returns the rate and, for
+    the parity of the timed output, the sampled tokens with the oracle's y
+    and ids (its own routing)."""
     import oracle
     cores = len(os.sched_getaffinity(0))
-    n = max(cores, 1)
-    tokens_done, t_used, sample_desc = 0, 0.0, ""
+    n = max(cores, 2)
     rng = np.random.default_rng(123)
     while True:
-        toks = np.sort(rng.choice(sh.T, size=min(n, sh.T), replace=False))
+        rnd = rng.choice(sh.T, size=min(n, sh.T), replace=False)
+        toks = np.unique(np.concatenate([[0, sh.T - 1], rnd]))[:max(n, 2)]
         t0 = time.perf_counter()
-        oracle.forward_tokens(inp, sh.k, toks, sh.score_fn, sh.renormalize, nthreads=cores)
+        r = oracle.forward_tokens(inp, sh.k, toks, sh.score_fn, sh.renormalize, nthreads=cores)
         dt = time.perf_counter() - t0
-        tokens_done, t_used = toks.size, dt
-        sample_desc = (f"{toks.size} of {sh.T} tokens (seeded random), full routing and "
-                       f"{sh.k} experts" + (" + shared expert" if sh.num_shared else "") +
-                       " per token, fp64")
         if dt >= target_s / 4 or toks.size >= sh.T:
             break
         n = int(min(sh.T, max(n * 2, n * (target_s / max(dt, 1e-3)) * 0.8)))
-    return {"value": tokens_done / t_used, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": sample_desc, "seconds": round(t_used, 3)}
+    sample = (f"{toks.size} of {sh.T} tokens (first, last, seeded random), full routing and {sh.k} "
+              f"experts" + (" + shared expert" if sh.num_shared else "") + " per token, fp64")
+    return {"value": toks.size / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}, (toks, r["y"], r["ids"])
+
+
+def parity_of(y_gpu: np.ndarray, ids_gpu: np.ndarray, ref, dtype: str) -> dict:
+    """max|y_gpu - y_oracle| / max|y_oracle| over the oracle's sampled tokens
+    whose GPU routing equals the oracle's (a token routed differently at a
+    near-tie is counted, not compared: the tests check those under the
+    GPU's ids)."""
+    toks, y_ref, ids_ref = ref
+    same = (ids_gpu[toks] == ids_ref).all(1)
+    yg = y_gpu[toks][same]
+    yr = y_ref[same]
+    rel = float(np.abs(yg - yr).max() / max(np.abs(yr).max(), 1e-30)) if same.any() else float("nan")
+    return {"tokens": int(toks.size), "routing_differs": int((~same).sum()), "max_err_over_max_y": rel,
+            "tau": TAU[dtype], "ok": bool(rel <= TAU[dtype])}
 
 
 COPY_BYTES = 1 << 30
@@ -302,11 +336,24 @@ GATE_UP_KERNELS = ("gemm_bf16_persistent_kernel<true", "gemm_bf16_skinny_kernel<
 
 
 def _pmc_rows(d):
+    """Counter rows of a rocprofv3 --pmc output directory, from its CSV files
+    or from its rocpd database: dicts with Kernel_Name, Counter_Name,
+    Counter_Value, Dispatch_Id and the dispatch's duration in ns."""
     import csv
     import glob
+    import sqlite3
     rows = []
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
-        rows += list(csv.DictReader(open(f)))
+        for r in csv.DictReader(open(f)):
+            dur = float(r["End_Timestamp"]) - float(r["Start_Timestamp"]) if "End_Timestamp" in r else None
+            rows.append(dict(r, Duration=dur))
+    for f in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+        con = sqlite3.connect(f)
+        q = "select kernel_name, counter_name, value, dispatch_id, duration from counters_collection"
+        for kn, cn, v, di, dur in con.execute(q):
+            rows.append({"Kernel_Name": kn, "Counter_Name": cn, "Counter_Value": v, "Dispatch_Id": di,
+                         "Duration": dur})
+        con.close()
     return rows
 
 
@@ -344,28 +391,51 @@ def traffic_from(args):
     print(json.dumps(rec))
 
 
-def main():
-    args = parse()
-    if args.traffic_from:
-        traffic_from(args)
-        return
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the layer is measured at N=1", file=sys.stderr)
-        sys.exit(2)
-    import torch
 
-    import mixture_experts_sparse_moe_amd as moe
+
+def counters_from(args):
+    """MFMA busy fraction and clock of each kernel from a rocprofv3 --pmc run
+    of SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16 and
+    GRBM_GUI_ACTIVE, averaged over its dispatches:
+      clock    = GRBM_GUI_ACTIVE / 8 (one GRBM per XCD, summed) / duration;
+      mfma busy = SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs)
+                  / (1024 * GRBM_GUI_ACTIVE / 8), rocprofv3's MfmaUtil;
+      MFMA FLOPs = 512 * SQ_INSTS_VALU_MFMA_MOPS_BF16 (executed, padding included).
+    Prints a markdown table."""
+    per = {}
+    for r in _pmc_rows(args.counters_from):
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        e = per.setdefault(key, {"dur": r["Duration"]})
+        e[r["Counter_Name"]] = float(r["Counter_Value"])
+    agg = {}
+    for (kn, _), e in per.items():
+        if "GRBM_GUI_ACTIVE" not in e or not e.get("dur"):
+            continue
+        a = agg.setdefault(kn, [])
+        a.append(e)
+    print("| kernel | dispatches | avg duration (us) | clock (GHz) | MFMA busy | MFMA FLOPs per dispatch | "
+          "TFLOP/s executed |")
+    print("|---|---|---|---|---|---|---|")
+    for kn, es in sorted(agg.items(), key=lambda kv: -sum(e["dur"] for e in kv[1])):
+        dur = np.mean([e["dur"] for e in es]) * 1e-9
+        gui = np.mean([e["GRBM_GUI_ACTIVE"] for e in es]) / 8.0
+        busy = np.mean([e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for e in es])
+        flops = 512.0 * np.mean([e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for e in es])
+        name = kn if len(kn) < 110 else kn[:107] + "..."
+        print(f"| `{name}` | {len(es)} | {dur * 1e6:.1f} | {gui / dur / 1e9:.3f} | "
+              f"{busy / (1024.0 * gui) * 100:.1f} % | {flops:.4g} | {flops / dur / 1e12:.1f} |")
+
+
+def measure(name: str, args, torch, moe, dev, extras: bool) -> dict:
+    """One workload: inputs resident in HBM, warmup, K timed steps of the
+    whole layer (moe_forward_staged, gate/up kernel timed by its own launch
+    events), a separate staged pass for the per-stage times, the roofline of
+    the gate/up kernel, the CPU oracle on a sample (and the parity of the
+    timed output on it); with extras the optional features, the backward and
+    the practical ceilings."""
     import synth
-
-    if not torch.cuda.is_available():
-        sys.exit("bench.py needs a GPU")
-    moe.lib()
-    sh = synth.SHAPES[args.workload]
-    dev = torch.device("cuda:0")
+    sh = synth.SHAPES[name]
+    dt_name = "bf16" if sh.dtype == synth.BF16 else "f32"
     t_gen = time.perf_counter()
     inp = synth.make_inputs(sh, args.seed)
     d = {n: (None if a is None else upload(a, torch, dev)) for n, a in inp.items()}
@@ -376,21 +446,20 @@ def main():
     ws = moe.alloc_workspace(cfg, dev)
     y = torch.empty(sh.T, sh.d, dtype=torch.bfloat16 if sh.dtype else torch.float32, device=dev)
     counts = torch.empty(sh.E, dtype=torch.int32, device=dev)
+    ids = torch.empty(sh.T, sh.k, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(start, evs):
         moe.moe_forward_staged(cfg, d["x"], d["w_router"], d["w_gate"], d["w_up"], d["w_down"],
-                               d["ws_gate"], d["ws_up"], d["ws_down"], y, expert_counts=counts,
+                               d["ws_gate"], d["ws_up"], d["ws_down"], y, topk_ids=ids, expert_counts=counts,
                                ws=ws, start_event=start, stage_events=evs, stream=stream)
 
     tev = TimingEvents()
-
     for _ in range(args.warmup):
         step(None, None)
     torch.cuda.synchronize()
     # Timed region: the whole layer, with two timing events per step around
-    # the dominant kernel (the routed gate/up GEMM, stage 2) on the layer's
-    # stream.
+    # the dominant kernel (the routed gate/up GEMM, stage 2) on the layer's stream.
     gu_ev = [tev.make(2, stream) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -402,6 +471,8 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
     gu_ms = float(np.mean([tev.ms(a, b) for a, b in gu_ev]))
+    y_host = y.float().cpu().numpy().astype(np.float64)
+    ids_host = ids.cpu().numpy()
 
     # Stage breakdown: a separate pass with an event after every stage.
     starts = tev.make(args.steps, stream)
@@ -420,18 +491,23 @@ def main():
     tev.close()
     cnt = counts.cpu().numpy()
     alg = algorithmic(sh, cnt)
-    decode = sh.T * sh.k < 64 * sh.E          # under 64 rows per expert: weight-read bound
-    if decode:
-        achieved = alg["gate_up"]["bytes"] / (gu_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    else:
-        peak = PEAK_BF16_TFLOPS if sh.dtype == synth.BF16 else PEAK_F32_TFLOPS
-        achieved = alg["gate_up"]["flops"] / (gu_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    bf16 = sh.dtype == synth.BF16
+    peak_c = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    gu = alg["gate_up"]
+    t_hbm = gu["bytes"] / (PEAK_HBM_GBS * 1e9)          # floors of the gate/up kernel, s
+    t_mfma = gu["flops"] / (peak_c * 1e12)
+    hbm_roof = {"bound": "hbm", "achieved": gu["bytes"] / (gu_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    cmp_roof = {"bound": "mfma" if bf16 else "alu", "achieved": gu["flops"] / (gu_ms * 1e-3) / 1e12,
+                "peak": peak_c, "unit": "TFLOP/s"}
+    for r_ in (hbm_roof, cmp_roof):
+        r_["frac"] = r_["achieved"] / r_["peak"]
+    roof, other = (hbm_roof, cmp_roof) if t_hbm >= t_mfma else (cmp_roof, hbm_roof)
+    roof = dict(roof)
     roof["kernel"] = "gate_up_gemm (grouped gate/up GEMM + SiLU*up)"
-    roof["per_launch"] = {"flops": alg["gate_up"]["flops"], "bytes": alg["gate_up"]["bytes"],
-                          "avg_ms": gu_ms}
+    roof["per_launch"] = {"flops": gu["flops"], "bytes": gu["bytes"], "avg_ms": gu_ms,
+                          "floor_ms_hbm": t_hbm * 1e3, "floor_ms_compute": t_mfma * 1e3}
+    roof["other_bound"] = other
     roof["traffic"] = None
     src_hash = kernel_source_hash()
     if os.path.exists(TRAFFIC_FILE):
@@ -439,19 +515,14 @@ def main():
         if rec.get("source_hash") == src_hash:
             roof["traffic"] = rec.get("bytes_per_launch")
     layer_s = ms_per_step * 1e-3
+    floor_layer = max(alg["layer_bytes"] / (PEAK_HBM_GBS * 1e9), alg["layer_flops"] / (peak_c * 1e12))
+    gg_ms = gu_ms + float(stage_avg[3])
     out = {
         "metric": "MoE-layer tokens/s",
         "value": sh.T / layer_s,
         "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if sh.dtype == synth.BF16 else "f32",
-        "data": "synthetic (seeded Philox normals; weights N(0,1/fan_in))",
+        "dtype": dt_name,
         "config": {"workload": sh.name, "T": sh.T, "d": sh.d, "E": sh.E, "k": sh.k,
                    "d_ff": sh.d_ff, "num_shared": sh.num_shared, "d_ff_shared": sh.d_ff_shared,
                    "score": "sigmoid" if sh.score_fn else "softmax",
@@ -460,35 +531,84 @@ def main():
         "layer_pct_bf16_peak": alg["layer_flops"] / layer_s / 1e12 / PEAK_BF16_TFLOPS,
         "layer_gbs": alg["layer_bytes"] / layer_s / 1e9,
         "layer_pct_hbm": alg["layer_bytes"] / layer_s / 1e9 / PEAK_HBM_GBS,
-        # separate pass with an event after every stage
+        "layer_floor_ms": floor_layer * 1e3,
+        "layer_frac_of_floor": floor_layer / layer_s,
         "stages_ms": {n: round(float(v), 4) for n, v in zip(moe.STAGE_NAMES, stage_avg)},
         "staged_ms_per_step": round(float(stage_ms.sum(1).mean()), 4),
         "expert_load": {"max_over_mean": float(cnt.max() / max(cnt.mean(), 1e-9)),
                         "touched": alg["touched"], "min": int(cnt.min()), "max": int(cnt.max())},
         "roofline": roof,
         # the routed grouped GEMM: gate/up (timed region) and down (stage pass) kernels
-        "grouped_gemm": {"ms": gu_ms + float(stage_avg[3]),
-                         "tflops": (alg["gate_up"]["flops"] + alg["down"]["flops"]) /
-                                   ((gu_ms + float(stage_avg[3])) * 1e-3) / 1e12,
-                         "gbs": (alg["gate_up"]["bytes"] + alg["down"]["bytes"]) /
-                                ((gu_ms + float(stage_avg[3])) * 1e-3) / 1e9},
+        "grouped_gemm": {"ms": gg_ms,
+                         "tflops": (gu["flops"] + alg["down"]["flops"]) / (gg_ms * 1e-3) / 1e12,
+                         "gbs": (gu["bytes"] + alg["down"]["bytes"]) / (gg_ms * 1e-3) / 1e9},
         "kernel_source_hash": src_hash,
     }
     gg = out["grouped_gemm"]
     gg["frac_bf16_peak"] = gg["tflops"] / PEAK_BF16_TFLOPS
     gg["frac_hbm"] = gg["gbs"] / PEAK_HBM_GBS
-    if not args.no_options:
+    if extras and not args.no_options:
         out["options_ms_per_step"] = options_cost(torch, moe, cfg, d, y, ws, stream, sh,
                                                   max(3, min(args.steps, 20)))
-    if not args.no_backward:
+    if extras and not args.no_backward:
         out["backward"] = backward_cost(torch, moe, cfg, d, sh, stream, 3)
-    if not args.no_ceilings:
+    if extras and not args.no_ceilings:
         out["practical_ceilings"] = practical_ceilings(torch, dev)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(sh, inp, args.cpu_seconds)
-    else:
+    del d, ws, y, counts, ids
+    torch.cuda.empty_cache()
+    if args.no_cpu_baseline:
         out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
+        out["parity"] = None
+    else:
+        out["cpu_baseline"], ref = cpu_baseline(sh, inp, args.cpu_seconds)
+        out["parity"] = parity_of(y_host, ids_host, ref, dt_name)
+    del inp
+    return out
+
+
+def main():
+    args = parse()
+    if args.traffic_from:
+        traffic_from(args)
+        return
+    if args.counters_from:
+        counters_from(args)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the layer is measured at N=1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mixture_experts_sparse_moe_amd as moe
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    moe.lib()
+    dev = torch.device("cuda:0")
+    head = measure(args.workload, args, torch, moe, dev, extras=True)
+    line = {
+        "metric": head.pop("metric"), "value": head.pop("value"), "unit": head.pop("unit"), "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": head.pop("dtype"),
+        "data": "synthetic (seeded Philox normals; weights N(0,1/fan_in))", "config": head.pop("config"),
+    }
+    line.update(head)
+    if not args.only:
+        subs = {}
+        for name in OTHERS:
+            if name == args.workload:
+                continue
+            try:
+                subs[name] = measure(name, args, torch, moe, dev, extras=False)
+            except Exception as exc:            # a failed sub-record is reported, not hidden
+                subs[name] = {"error": f"{type(exc).__name__}: {exc}"}
+            print(f"[bench] {name}: done", file=sys.stderr, flush=True)
+        line["configs"] = subs
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -103,9 +103,17 @@ const char* moe_status_str(int status);
  *   topk_ids [T,k] int32                    out: chosen experts, by descending
  *                                                logit, ties to the lower index
  *   topk_weights [T,k] fp32                 out: gates
- *   topk_gap [T] fp32 (nullable)            out: h_(k) - h_(k+1), the logit
- *                                                margin of the k-th choice
- *                                                (+inf when k == E)
+ *   topk_gap [T,2] fp32 (nullable)          out, per token:
+ *       [t][0] = h_(k) - h_(k+1), the logit margin between the k-th and the
+ *                (k+1)-th choice (with a selection bias, moe_options, the
+ *                margin of the selection key);
+ *       [t][1] = s_(k) - s_(k+1), the score margin of the same two experts
+ *                (softmax over all E, or sigmoid; unbiased scores, so with
+ *                a bias it can be negative), computed without cancellation.
+ *       Both +inf when k == E.  A token whose margins are tiny (a near-tie:
+ *       score margin below about 1e-6, logit margin below about 1e-4, the
+ *       reach of fp32 accumulation) may be routed differently by an exact
+ *       computation; the caller can tell which tokens those are.
  * Logits are accumulated in fp32 (products of bf16 inputs are exact in fp32).
  */
 int moe_route(const moe_config* cfg, const void* x, const void* w_router, int32_t* topk_ids,
@@ -169,6 +177,8 @@ int moe_combine(const moe_config* cfg, const void* expert_out, const float* topk
  *   topk_ids_out [T,k], topk_weights_out [T,k], expert_counts_out [E]:
  *   optional copies of the routing (nullable; the workspace is used when
  *   NULL).
+ *   topk_gap_out [T,2] (nullable): the margins of this call's own routing,
+ *   as moe_route's topk_gap (the near-ties of the layer as it ran).
  * Same arithmetic as the entry points above, except that in bf16 the router
  * logits (below 8192 tokens) and the down projections may be summed over K
  * ranges (fixed order; deterministic), so results can differ from the
@@ -177,7 +187,7 @@ int moe_combine(const moe_config* cfg, const void* expert_out, const float* topk
 int moe_forward(const moe_config* cfg, const void* x, const void* w_router, const void* w_gate,
                 const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,
                 const void* ws_down, void* y, int32_t* topk_ids_out, float* topk_weights_out,
-                int32_t* expert_counts_out, void* ws, size_t ws_bytes, void* stream);
+                int32_t* expert_counts_out, float* topk_gap_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_forward with per-stage timing ("T2.6 -- What Mixture of Experts
@@ -203,8 +213,8 @@ int moe_forward_staged(const moe_config* cfg, const void* x, const void* w_route
                        const void* w_gate, const void* w_up, const void* w_down,
                        const void* ws_gate, const void* ws_up, const void* ws_down, void* y,
                        int32_t* topk_ids_out, float* topk_weights_out,
-                       int32_t* expert_counts_out, void* ws, size_t ws_bytes, void* start_event,
-                       void* const* stage_events, void* stream);
+                       int32_t* expert_counts_out, float* topk_gap_out, void* ws, size_t ws_bytes,
+                       void* start_event, void* const* stage_events, void* stream);
 
 /*
  * Backward pass of the layer for the routing of a forward call ("8.6 Mixture
@@ -254,15 +264,19 @@ int moe_backward(const moe_config* cfg, const void* x, const void* w_router, con
  *       and expert_offsets then count the kept pairs, pair_pos is -1 for a
  *       dropped pair, and sorted_pairs holds offsets[E] entries (the rest
  *       are unspecified).  <= 0: no limit.
- *   router_stats [2E + 2] fp32 (device, nullable): load statistics of the
+ *   router_stats [2E + 3] fp32 (device, nullable): load statistics of the
  *       batch ("8.6 Mixture of Experts", sec. 3.1; "from the router to the
- *       all-to-all", Load balancing):
+ *       all-to-all", Load balancing; "T2.6 -- What Mixture of Experts
+ *       Changes", In practice: counts, maximum-to-mean load, overflow):
  *         [0, E)   f_e = (pairs routed to e, before any capacity drop) / T
  *         [E, 2E)  P_e = mean over tokens of e's router probability (softmax
  *                  score; sigmoid scores normalised over all experts)
  *         [2E]     L_aux = aux_alpha * E * sum_e f_e P_e  (sum_e f_e = k, so
  *                  uniform routing gives aux_alpha * k)
  *         [2E+1]   max_e n_e / mean_e n_e
+ *         [2E+2]   capacity overflow: sum_e max(0, n_e - expert_capacity),
+ *                  the pairs the capacity drops (0 without a capacity);
+ *                  counts are exact below 2^24
  *       Needs the workspace.  Sums are taken in a fixed order.
  */
 typedef struct moe_options {
@@ -288,8 +302,26 @@ int moe_dispatch_ex(const moe_config* cfg, const moe_options* opts, const int32_
 int moe_forward_ex(const moe_config* cfg, const moe_options* opts, const void* x, const void* w_router,
                    const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
                    const void* ws_up, const void* ws_down, void* y, int32_t* topk_ids_out,
-                   float* topk_weights_out, int32_t* expert_counts_out, void* ws, size_t ws_bytes,
-                   void* stream);
+                   float* topk_weights_out, int32_t* expert_counts_out, float* topk_gap_out, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/*
+ * Slots per expert for a capacity factor ("8.6 Mixture of Experts", sec. 3.2;
+ * "Mixture-of-Experts, from the router to the all-to-all", Capacity and
+ * token dropping: tokens per batch times k over the number of experts, times
+ * the factor), for moe_options.expert_capacity:
+ *   ceil(T * k / E * capacity_factor).
+ * The pages leave the rounding open; the ceiling keeps every slot the formula
+ * grants.  The factor is read as the decimal the caller wrote: a product
+ * within 1e-12 (relative) of a whole number is that number, so 640 tokens,
+ * k = 8, E = 8 and factor 1.1 give 704 slots although the product of the
+ * doubles is 704.0000000000001.  The page's example (4,096 tokens, 64
+ * experts, top-8, factor 1.0) gives 512.
+ * Returns the capacity (>= 0), or a negative moe_status: an invalid cfg as
+ * moe_workspace_bytes would reject it, MOE_ERR_SHAPE for a factor that is not
+ * finite and positive, MOE_ERR_UNSUPPORTED for a result past INT32_MAX.
+ * Host only. */
+int moe_capacity(const moe_config* cfg, double capacity_factor);
 
 /* moe_backward with options, for training with an expert capacity ("8.6
  * Mixture of Experts", sec. 3.2; "Mixture-of-Experts, from the router to the

@@ -10,7 +10,7 @@ Entry points (same names as the C ABI):
     moe_workspace_bytes, moe_route, moe_dispatch, moe_expert_ffn,
     moe_combine, moe_forward, moe_forward_staged, moe_status_str,
     moe_route_ex, moe_dispatch_ex, moe_forward_ex (with MoeOptions),
-    moe_backward_workspace_bytes, moe_backward
+    moe_capacity, moe_backward_workspace_bytes, moe_backward, moe_backward_ex
 """
 from __future__ import annotations
 
@@ -30,8 +30,8 @@ MOE_F32, MOE_BF16 = 0, 1
 
 EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_staged",
-           "moe_route_ex", "moe_dispatch_ex", "moe_forward_ex", "moe_backward_workspace_bytes",
-           "moe_backward", "moe_backward_ex")
+           "moe_route_ex", "moe_dispatch_ex", "moe_forward_ex", "moe_capacity",
+           "moe_backward_workspace_bytes", "moe_backward", "moe_backward_ex")
 MOE_NUM_STAGES = 7
 STAGE_NAMES = ("route", "dispatch", "gate_up_gemm", "down_gemm", "shared_gate_up", "shared_down",
                "combine")
@@ -74,10 +74,17 @@ class MoeOptions(ctypes.Structure):
         return o
 
 
+def moe_capacity(cfg: "MoeConfig", capacity_factor: float) -> int:
+    """Slots per expert for a capacity factor, from the library (moe_capacity)."""
+    c = int(lib().moe_capacity(ctypes.byref(cfg), float(capacity_factor)))
+    if c < 0:
+        raise MoeError(c, "moe_capacity")
+    return c
+
+
 def capacity(T: int, k: int, E: int, factor: float) -> int:
-    """Slots per expert, ceil(T k / E * factor) (the pages leave the rounding open)."""
-    import math
-    return int(math.ceil(T * k / E * factor - 1e-9))
+    """moe_capacity for a layer of T tokens, top-k of E experts."""
+    return moe_capacity(MoeConfig.of(T, 64, E, k, 64), factor)
 
 
 _lib = None
@@ -104,17 +111,19 @@ def lib():
         L.moe_expert_ffn.restype = i32
         L.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
         L.moe_combine.restype = i32
-        L.moe_forward.argtypes = [cfgp] + [vp] * 12 + [vp, sz, vp]
+        L.moe_forward.argtypes = [cfgp] + [vp] * 13 + [vp, sz, vp]
         L.moe_forward.restype = i32
-        L.moe_forward_staged.argtypes = [cfgp] + [vp] * 12 + [vp, sz, vp, vp, vp]
+        L.moe_forward_staged.argtypes = [cfgp] + [vp] * 13 + [vp, sz, vp, vp, vp]
         L.moe_forward_staged.restype = i32
         optp = ctypes.POINTER(MoeOptions)
         L.moe_route_ex.argtypes = [cfgp, optp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_route_ex.restype = i32
         L.moe_dispatch_ex.argtypes = [cfgp, optp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_dispatch_ex.restype = i32
-        L.moe_forward_ex.argtypes = [cfgp, optp] + [vp] * 12 + [vp, sz, vp]
+        L.moe_forward_ex.argtypes = [cfgp, optp] + [vp] * 13 + [vp, sz, vp]
         L.moe_forward_ex.restype = i32
+        L.moe_capacity.argtypes = [cfgp, ctypes.c_double]
+        L.moe_capacity.restype = i32
         L.moe_backward_workspace_bytes.argtypes = [cfgp]
         L.moe_backward_workspace_bytes.restype = sz
         L.moe_backward.argtypes = [cfgp] + [vp] * 20 + [sz, vp]
@@ -189,7 +198,7 @@ def moe_route(cfg, x, w_router, topk_ids, topk_weights, topk_gap=None, stream=No
     _check(w_router, "w_router", (E, d), dt, dev)
     _check(topk_ids, "topk_ids", (T, k), torch.int32, dev)
     _check(topk_weights, "topk_weights", (T, k), torch.float32, dev)
-    _check(topk_gap, "topk_gap", (T,), torch.float32, dev, optional=True)
+    _check(topk_gap, "topk_gap", (T, 2), torch.float32, dev, optional=True)
     _rc(lib().moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(topk_ids),
                         _ptr(topk_weights), _ptr(topk_gap), _stream(stream)), "moe_route")
 
@@ -252,7 +261,8 @@ def moe_combine(cfg, expert_out, topk_weights, pair_pos, shared_out, y, stream=N
 
 
 def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
-                topk_ids=None, topk_weights=None, expert_counts=None, ws=None, stream=None):
+                topk_ids=None, topk_weights=None, expert_counts=None, ws=None, stream=None,
+                topk_gap=None):
     torch = _torch()
     T, d, E, k = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k
     dt, dev = _act_dtype(cfg), x.device
@@ -263,15 +273,16 @@ def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
     _check(topk_ids, "topk_ids", (T, k), torch.int32, dev, optional=True)
     _check(topk_weights, "topk_weights", (T, k), torch.float32, dev, optional=True)
     _check(expert_counts, "expert_counts", (E,), torch.int32, dev, optional=True)
+    _check(topk_gap, "topk_gap", (T, 2), torch.float32, dev, optional=True)
     _rc(lib().moe_forward(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up),
                           _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(y),
-                          _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_counts), _ptr(ws),
-                          _ws_bytes(ws), _stream(stream)), "moe_forward")
+                          _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_counts), _ptr(topk_gap),
+                          _ptr(ws), _ws_bytes(ws), _stream(stream)), "moe_forward")
 
 
 def moe_forward_staged(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
                        topk_ids=None, topk_weights=None, expert_counts=None, ws=None,
-                       start_event=None, stage_events=None, stream=None):
+                       start_event=None, stage_events=None, stream=None, topk_gap=None):
     """moe_forward recording ``start_event`` and one event per stage (torch.cuda.Event
     objects created with enable_timing=True, or raw hipEvent_t handles) on the stream."""
     torch = _torch()
@@ -284,6 +295,7 @@ def moe_forward_staged(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, w
     _check(topk_ids, "topk_ids", (T, k), torch.int32, dev, optional=True)
     _check(topk_weights, "topk_weights", (T, k), torch.float32, dev, optional=True)
     _check(expert_counts, "expert_counts", (E,), torch.int32, dev, optional=True)
+    _check(topk_gap, "topk_gap", (T, 2), torch.float32, dev, optional=True)
     if stage_events is not None and len(stage_events) != MOE_NUM_STAGES:
         raise ValueError(f"stage_events needs {MOE_NUM_STAGES} events")
 
@@ -300,7 +312,7 @@ def moe_forward_staged(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, w
     _rc(lib().moe_forward_staged(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(w_gate),
                                  _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up),
                                  _ptr(ws_down), _ptr(y), _ptr(topk_ids), _ptr(topk_weights),
-                                 _ptr(expert_counts), _ptr(ws), _ws_bytes(ws),
+                                 _ptr(expert_counts), _ptr(topk_gap), _ptr(ws), _ws_bytes(ws),
                                  ev_handle(start_event), evs, _stream(stream)),
         "moe_forward_staged")
 
@@ -315,7 +327,7 @@ def _check_opts(cfg, opts, dev):
     torch = _torch()
     b, st = opts._keep if hasattr(opts, "_keep") else (None, None)
     _check(b, "expert_bias", (cfg.num_experts,), torch.float32, dev, optional=True)
-    _check(st, "router_stats", (2 * cfg.num_experts + 2,), torch.float32, dev, optional=True)
+    _check(st, "router_stats", (2 * cfg.num_experts + 3,), torch.float32, dev, optional=True)
 
 
 def moe_route_ex(cfg, opts, x, w_router, topk_ids, topk_weights, topk_gap=None, ws=None, stream=None):
@@ -326,7 +338,7 @@ def moe_route_ex(cfg, opts, x, w_router, topk_ids, topk_weights, topk_gap=None, 
     _check(w_router, "w_router", (E, d), dt, dev)
     _check(topk_ids, "topk_ids", (T, k), torch.int32, dev)
     _check(topk_weights, "topk_weights", (T, k), torch.float32, dev)
-    _check(topk_gap, "topk_gap", (T,), torch.float32, dev, optional=True)
+    _check(topk_gap, "topk_gap", (T, 2), torch.float32, dev, optional=True)
     _check_opts(cfg, opts, dev)
     _rc(lib().moe_route_ex(ctypes.byref(cfg), _opts(opts), _ptr(x), _ptr(w_router), _ptr(topk_ids),
                            _ptr(topk_weights), _ptr(topk_gap), _ptr(ws), _ws_bytes(ws), _stream(stream)),
@@ -350,7 +362,8 @@ def moe_dispatch_ex(cfg, opts, topk_ids, expert_counts, expert_offsets, sorted_p
 
 
 def moe_forward_ex(cfg, opts, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
-                   topk_ids=None, topk_weights=None, expert_counts=None, ws=None, stream=None):
+                   topk_ids=None, topk_weights=None, expert_counts=None, ws=None, stream=None,
+                   topk_gap=None):
     torch = _torch()
     T, d, E, k = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k
     dt, dev = _act_dtype(cfg), x.device
@@ -361,11 +374,12 @@ def moe_forward_ex(cfg, opts, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up,
     _check(topk_ids, "topk_ids", (T, k), torch.int32, dev, optional=True)
     _check(topk_weights, "topk_weights", (T, k), torch.float32, dev, optional=True)
     _check(expert_counts, "expert_counts", (E,), torch.int32, dev, optional=True)
+    _check(topk_gap, "topk_gap", (T, 2), torch.float32, dev, optional=True)
     _check_opts(cfg, opts, dev)
     _rc(lib().moe_forward_ex(ctypes.byref(cfg), _opts(opts), _ptr(x), _ptr(w_router), _ptr(w_gate),
                              _ptr(w_up), _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(y),
-                             _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_counts), _ptr(ws),
-                             _ws_bytes(ws), _stream(stream)), "moe_forward_ex")
+                             _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_counts), _ptr(topk_gap),
+                             _ptr(ws), _ws_bytes(ws), _stream(stream)), "moe_forward_ex")
 
 
 def moe_backward_workspace_bytes(cfg: MoeConfig) -> int:

@@ -189,7 +189,7 @@ int run_route(const moe_config* c, const void* x, const void* w_router, int32_t*
     else MOE_HIP(launch_route(a, bf16, s));
     if (stats)
         MOE_HIP(launch_router_stats(spart, (c->num_tokens + 31) / 32, c->num_experts, c->num_tokens,
-                                    opts->aux_alpha, opts->router_stats, s));
+                                    opts->aux_alpha, capacity_of(opts), opts->router_stats, s));
     return MOE_OK;
 }
 
@@ -287,8 +287,8 @@ int run_combine(const moe_config* c, const void* out, const float* wts, const in
 int forward_impl(const moe_config* cfg, const moe_options* opts, const void* x, const void* w_router,
                  const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
                  const void* ws_up, const void* ws_down, void* y, int32_t* topk_ids_out,
-                 float* topk_weights_out, int32_t* expert_counts_out, void* ws, size_t ws_bytes,
-                 void* start_event, void* const* ev, void* stream) {
+                 float* topk_weights_out, int32_t* expert_counts_out, float* topk_gap_out, void* ws,
+                 size_t ws_bytes, void* start_event, void* const* ev, void* stream) {
     MOE_TRY(validate_cfg(cfg));
     MOE_TRY(validate_opts(opts));
     const bool empty = cfg->num_tokens == 0;
@@ -306,6 +306,7 @@ int forward_impl(const moe_config* cfg, const moe_options* opts, const void* x, 
     if (topk_ids_out) MOE_TRY(check_ptr(topk_ids_out, true));
     if (topk_weights_out) MOE_TRY(check_ptr(topk_weights_out, true));
     if (expert_counts_out) MOE_TRY(check_ptr(expert_counts_out, true));
+    if (topk_gap_out) MOE_TRY(check_ptr(topk_gap_out, true));
     const Layout L = layout(cfg);
     if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     MOE_TRY(check_ptr(ws, false));
@@ -328,8 +329,8 @@ int forward_impl(const moe_config* cfg, const moe_options* opts, const void* x, 
     const DispatchArgs disp{ids, counts, offsets, sorted, pos, at<int32_t>(ws, L.chunk),
                             cfg->num_tokens * cfg->top_k, cfg->num_experts, cap};
     bool dispatched = false;
-    MOE_TRY(run_route(cfg, x, w_router, ids, wts, nullptr, s, at<float>(ws, L.rpart), &disp, &dispatched, opts,
-                      at<float>(ws, L.spart)));
+    MOE_TRY(run_route(cfg, x, w_router, ids, wts, topk_gap_out, s, at<float>(ws, L.rpart), &disp, &dispatched,
+                      opts, at<float>(ws, L.spart)));
     MOE_TRY(mark(ev, 0, s));
     int32_t* queue = at<int32_t>(ws, L.queue);
     if (!dispatched)
@@ -861,21 +862,21 @@ int moe_forward_staged(const moe_config* cfg, const void* x, const void* w_route
                        const void* w_gate, const void* w_up, const void* w_down,
                        const void* ws_gate, const void* ws_up, const void* ws_down, void* y,
                        int32_t* topk_ids_out, float* topk_weights_out,
-                       int32_t* expert_counts_out, void* ws, size_t ws_bytes, void* start_event,
-                       void* const* ev, void* stream) {
+                       int32_t* expert_counts_out, float* topk_gap_out, void* ws, size_t ws_bytes,
+                       void* start_event, void* const* ev, void* stream) {
     return forward_impl(cfg, nullptr, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
-                        topk_ids_out, topk_weights_out, expert_counts_out, ws, ws_bytes, start_event, ev,
-                        stream);
+                        topk_ids_out, topk_weights_out, expert_counts_out, topk_gap_out, ws, ws_bytes,
+                        start_event, ev, stream);
 }
 
 int moe_forward_ex(const moe_config* cfg, const moe_options* opts, const void* x, const void* w_router,
                    const void* w_gate, const void* w_up, const void* w_down, const void* ws_gate,
                    const void* ws_up, const void* ws_down, void* y, int32_t* topk_ids_out,
-                   float* topk_weights_out, int32_t* expert_counts_out, void* ws, size_t ws_bytes,
-                   void* stream) {
+                   float* topk_weights_out, int32_t* expert_counts_out, float* topk_gap_out, void* ws,
+                   size_t ws_bytes, void* stream) {
     return forward_impl(cfg, opts, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
-                        topk_ids_out, topk_weights_out, expert_counts_out, ws, ws_bytes, nullptr, nullptr,
-                        stream);
+                        topk_ids_out, topk_weights_out, expert_counts_out, topk_gap_out, ws, ws_bytes, nullptr,
+                        nullptr, stream);
 }
 
 size_t moe_backward_workspace_bytes(const moe_config* cfg) {
@@ -925,10 +926,23 @@ int moe_backward_ex(const moe_config* cfg, const moe_options* opts, const void* 
 int moe_forward(const moe_config* cfg, const void* x, const void* w_router, const void* w_gate,
                 const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,
                 const void* ws_down, void* y, int32_t* topk_ids_out, float* topk_weights_out,
-                int32_t* expert_counts_out, void* ws, size_t ws_bytes, void* stream) {
+                int32_t* expert_counts_out, float* topk_gap_out, void* ws, size_t ws_bytes, void* stream) {
     return moe_forward_staged(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
-                              topk_ids_out, topk_weights_out, expert_counts_out, ws, ws_bytes,
+                              topk_ids_out, topk_weights_out, expert_counts_out, topk_gap_out, ws, ws_bytes,
                               nullptr, nullptr, stream);
+}
+
+int moe_capacity(const moe_config* cfg, double capacity_factor) {
+    MOE_TRY(validate_cfg(cfg));
+    if (!(capacity_factor > 0.0) || !std::isfinite(capacity_factor)) return MOE_ERR_SHAPE;
+    const double q = (double)cfg->num_tokens * cfg->top_k / cfg->num_experts * capacity_factor;
+    // The factor is a decimal the caller wrote (1.1, 1.25), which a double
+    // holds only to about 1e-16: a product that close to a whole number is
+    // that number (640 * 8 / 8 * 1.1 is 704.0000000000001 in doubles: 704 slots).
+    const double r = std::nearbyint(q);
+    const double c = std::fabs(q - r) <= 1e-12 * std::max(1.0, q) ? r : std::ceil(q);
+    if (c > 2147483647.0) return MOE_ERR_UNSUPPORTED;
+    return (int)c;
 }
 
 }  // extern "C"

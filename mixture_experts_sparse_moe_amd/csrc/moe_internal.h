@@ -32,7 +32,7 @@ struct RouteArgs {
     const void* w;          // [E, d]
     int32_t* ids;           // [T, k]
     float* weights;         // [T, k]
-    float* gap;             // [T] or nullptr
+    float* gap;             // [T, 2] (key margin, score margin) or nullptr
     int T, d, E, k;
     int score_fn;           // 0 softmax, 1 sigmoid
     int renorm;
@@ -42,9 +42,10 @@ struct RouteArgs {
 };
 hipError_t launch_route(const RouteArgs& a, bool bf16, hipStream_t s);
 // Router statistics from the per-block sums of a routing call:
-// out [2E + 2] = f_e (E), P_e (E), L_aux = alpha E sum_e f_e P_e, max_e n_e / mean_e n_e.
-hipError_t launch_router_stats(const float* stats_part, int blocks, int E, int T, float alpha, float* out,
-                               hipStream_t s);
+// out [2E + 3] = f_e (E), P_e (E), L_aux = alpha E sum_e f_e P_e, max_e n_e / mean_e n_e,
+// sum_e max(0, n_e - cap) (cap = INT32_MAX: no capacity, 0).
+hipError_t launch_router_stats(const float* stats_part, int blocks, int E, int T, float alpha, int cap,
+                               float* out, hipStream_t s);
 // bf16 only: the K chunks in `ranges` ranges, one workgroup per (32 tokens,
 // range), partial logits in part [ranges, T, E] fp32, then a second kernel
 // adds them in range order and selects.  For batches of fewer than 256 token

@@ -199,13 +199,30 @@ __device__ __forceinline__ float wave_max_f32(float v) {
     return key_value(wave_max_u64((unsigned long long)ord_bits(v) << 32));
 }
 
+// Score margin s(a) - s(b) between two experts with logits a >= b, without
+// the cancellation of subtracting two rounded scores: softmax
+// e^(a - mx) (1 - e^(b - a)) / z with mx the largest logit and z the sum of
+// e^(l - mx) over all experts; sigmoid s(a) s(-b) (1 - e^(b - a)), since
+// s(a) - s(b) = (e^-b - e^-a) / ((1 + e^-a)(1 + e^-b)).
+__device__ __forceinline__ float score_margin(float a, float b, int score_fn, float mx, float z) {
+    const float d = -expm1f(b - a);
+    if (score_fn == 0) return expf(a - mx) * d / z;
+    return d / ((1.0f + expf(-a)) * (1.0f + expf(b)));
+}
+
+__device__ __forceinline__ float score_of(float l, int score_fn, float mx, float z) {
+    return score_fn == 0 ? expf(l - mx) / z : 1.0f / (1.0f + expf(-l));
+}
+
 // Top-k selection and gates of tokens t0 .. t0 + 31 from their logits in
 // lds[32][kLogitStride]; one wave per token.  Lane owns experts lane + 64 q.
 //   key (what is selected on): the logit; with a bias, logit + bias or
 //       score + bias ("Mixture-of-Experts Internals", sec. 3.3; "from the
 //       router to the all-to-all", Load balancing).  Ties: lower index.
 //   gates: from the unbiased scores, renormalised over the chosen set or not.
-//   gap: key_(k) - key_(k+1).
+//   gap [T, 2]: key_(k) - key_(k+1), and the score margin s_(k) - s_(k+1)
+//       of the same two experts (scores unbiased: softmax over all E or
+//       sigmoid; with a bias it can be negative).
 // With a.stats_part the block's per-expert sums of the chosen count and of
 // the router probability (softmax score, or sigmoid score normalised over all
 // experts) go to a.stats_part[blockIdx.x][2E], summed over the block's tokens
@@ -268,7 +285,7 @@ __device__ __forceinline__ void topk_rows_q(const RouteArgs& a, int t0, float* l
             kv[q] = abias ? (a.bias_on_scores ? sv[q] : lv[q]) + bias[q] : lv[q];
             key[q] = e < a.E ? ((unsigned long long)ord_bits(kv[q]) << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
         }
-        int my_e = 0;
+        int my_e = 0, e_k = 0;
         float my_l = 0.0f, first_l = 0.0f, last_k = 0.0f;
         for (int j = 0; j < a.k; ++j) {
             unsigned long long m = key[0];
@@ -286,13 +303,31 @@ __device__ __forceinline__ void topk_rows_q(const RouteArgs& a, int t0, float* l
             if (lane == j) { my_e = e; my_l = l; }
             if (j == 0) first_l = l;
             last_k = key_value(m);
+            e_k = e;
         }
-        float gap = __builtin_inff();
+        float gap = __builtin_inff(), sgap = __builtin_inff();
         if (a.k < a.E) {
             unsigned long long m = key[0];
 #pragma unroll
             for (int q = 1; q < QN; ++q) m = key[q] > m ? key[q] : m;
-            gap = last_k - key_value(wave_max_u64(m));
+            m = wave_max_u64(m);
+            gap = last_k - key_value(m);
+            if (a.gap) {
+                // score margin of the k-th and (k+1)-th choices
+                const int e_k1 = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
+                const float la = lrow[e_k], lb = lrow[e_k1];
+                const float mxs = abias ? mx : first_l;     // the largest logit
+                float z = 1.0f;
+                if (a.score_fn == 0) {
+                    float part = 0.0f;
+#pragma unroll
+                    for (int q = 0; q < QN; ++q)
+                        if (lane + 64 * q < a.E) part += expf(lv[q] - mxs);
+                    z = wave_sum(part);
+                }
+                sgap = abias ? score_of(la, a.score_fn, mxs, z) - score_of(lb, a.score_fn, mxs, z)
+                             : score_margin(la, lb, a.score_fn, mxs, z);
+            }
         }
         const bool mine = lane < a.k;
         // largest logit among the chosen (the first chosen unless biased)
@@ -321,7 +356,10 @@ __device__ __forceinline__ void topk_rows_q(const RouteArgs& a, int t0, float* l
             a.weights[(int64_t)t * a.k + lane] = g;
             if (s_ids) s_ids[row * a.k + lane] = my_e;
         }
-        if (lane == 0 && a.gap) a.gap[t] = gap;
+        if (lane == 0 && a.gap) {
+            a.gap[2 * (int64_t)t] = gap;
+            a.gap[2 * (int64_t)t + 1] = sgap;
+        }
     }
     if (stats) {
         // waves' sums in LDS (the logit tile is no longer read), then added
@@ -435,11 +473,13 @@ __global__ __launch_bounds__(kFinishThreads) void route_finish_kernel(RouteArgs 
 
 // Statistics of the whole batch from the per-block sums, added in block
 // order: f_e = n_e / T, P_e = (sum of probabilities) / T, then (thread 0, in
-// expert order) L_aux = alpha E sum_e f_e P_e and max_e n_e / mean_e n_e
-// ("8.6 Mixture of Experts", sec. 3.1; "from the router to the all-to-all",
-// Load balancing).
+// expert order) L_aux = alpha E sum_e f_e P_e, max_e n_e / mean_e n_e and the
+// capacity overflow sum_e max(0, n_e - cap) ("8.6 Mixture of Experts", sec.
+// 3.1; "from the router to the all-to-all", Load balancing; "T2.6 -- What
+// Mixture of Experts Changes", In practice).  Counts are whole numbers in
+// fp32, exact below 2^24.
 __global__ __launch_bounds__(256) void router_stats_kernel(const float* part, int blocks, int E, int T,
-                                                           float alpha, float* out) {
+                                                           float alpha, int cap, float* out) {
     __shared__ float s_fp[256], s_n[256];
     const int e = threadIdx.x;
     if (e < E) {
@@ -456,23 +496,25 @@ __global__ __launch_bounds__(256) void router_stats_kernel(const float* part, in
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        float acc = 0.0f, mx = 0.0f, tot = 0.0f;
+        float acc = 0.0f, mx = 0.0f, tot = 0.0f, over = 0.0f;
         for (int i = 0; i < E; ++i) {
             acc += s_fp[i];
             mx = fmaxf(mx, s_n[i]);
             tot += s_n[i];
+            over += fmaxf(s_n[i] - (float)cap, 0.0f);
         }
         out[2 * E] = alpha * (float)E * acc;
         out[2 * E + 1] = tot > 0.0f ? mx / (tot / (float)E) : 0.0f;
+        out[2 * E + 2] = over;
     }
 }
 
 }  // namespace
 
-hipError_t launch_router_stats(const float* stats_part, int blocks, int E, int T, float alpha, float* out,
-                               hipStream_t s) {
-    if (E < 1 || E > 256 || blocks < 1 || T < 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(router_stats_kernel, dim3(1), dim3(256), 0, s, stats_part, blocks, E, T, alpha, out);
+hipError_t launch_router_stats(const float* stats_part, int blocks, int E, int T, float alpha, int cap,
+                               float* out, hipStream_t s) {
+    if (E < 1 || E > 256 || blocks < 1 || T < 1 || cap < 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(router_stats_kernel, dim3(1), dim3(256), 0, s, stats_part, blocks, E, T, alpha, cap, out);
     return hipGetLastError();
 }
 

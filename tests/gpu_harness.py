@@ -66,10 +66,11 @@ class DeviceLayer:
         ids = t.empty(sh.T, sh.k, dtype=t.int32, device=self.device)
         wts = t.empty(sh.T, sh.k, dtype=t.float32, device=self.device)
         counts = t.empty(sh.E, dtype=t.int32, device=self.device)
+        gap = t.empty(sh.T, 2, dtype=t.float32, device=self.device)
         moe.moe_forward(self.cfg, dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"],
                         dv["ws_gate"], dv["ws_up"], dv["ws_down"], y, ids, wts, counts, self.ws,
-                        stream=stream)
-        return dict(y=y, ids=ids, weights=wts, counts=counts)
+                        stream=stream, topk_gap=gap)
+        return dict(y=y, ids=ids, weights=wts, counts=counts, gap=gap)
 
     def steps(self) -> dict:
         """The layer through the four step entry points, keeping every output."""
@@ -78,7 +79,7 @@ class DeviceLayer:
         P = sh.T * sh.k
         ids = t.empty(sh.T, sh.k, dtype=t.int32, device=dev)
         wts = t.empty(sh.T, sh.k, dtype=t.float32, device=dev)
-        gap = t.empty(sh.T, dtype=t.float32, device=dev)
+        gap = t.empty(sh.T, 2, dtype=t.float32, device=dev)
         moe.moe_route(self.cfg, dv["x"], dv["w_router"], ids, wts, gap)
         counts = t.empty(sh.E, dtype=t.int32, device=dev)
         offsets = t.empty(sh.E + 1, dtype=t.int32, device=dev)
@@ -95,37 +96,44 @@ class DeviceLayer:
                     sorted_pairs=sp, pair_pos=pp, expert_out=out, shared_out=so, y=y)
 
 
-def check_routing(gpu_ids: np.ndarray, ref: dict, k: int) -> np.ndarray:
-    """Ids must equal the oracle's, in order, except at near-ties.
+def check_ids(gpu_ids: np.ndarray, oracle_ids: np.ndarray, key: np.ndarray, key_score: np.ndarray,
+              key_tol: float, score_tol: float = NEAR_TIE) -> np.ndarray:
+    """GPU ids against the oracle's, slot by slot, with near-ties exempted.
 
-    A token may differ only where the oracle's score gap between the
-    neighbouring ranks involved is below NEAR_TIE and the logit gap is below
-    LOGIT_TIE (fp32 accumulation error; a larger logit gap is a bug).  For an
-    exempted token the GPU's list must still be a valid top-k up to that
-    band.  Returns the exempted token indices."""
-    oid = ref["ids"]
+    key [T,E]: the oracle's selection key (fp64: the logit, or the logit or
+    score plus a selection bias); key_score [T,E]: the same key in score
+    space (the scores themselves for a logit key, the key itself when it is
+    already a score).  A token's list may differ from the oracle's only at
+    slots j where the GPU's expert is tied with the oracle's expert of that
+    slot: |key gap| < key_tol (fp32 accumulation reach; a larger gap is a
+    bug) and |score gap| < score_tol (1e-6, the near-tie rule).  So every
+    reorder and every set change sits at a near-tie, and the list stays a
+    valid top-k in descending order up to that band.  The k ids must be
+    distinct experts.  Returns the exempted token indices."""
+    T, k = oracle_ids.shape
+    E = key.shape[1]
     exempt = []
-    for t in np.nonzero((gpu_ids != oid).any(1))[0]:
-        s, lg = ref["scores"][t], ref["logits"][t]
-        E = s.size
-        order = sorted(range(E), key=lambda e: (-lg[e], e))[:min(k + 1, E)]
-        g_s = s[order[:-1]] - s[order[1:]]
-        g_l = lg[order[:-1]] - lg[order[1:]]
-        tie = (g_s < NEAR_TIE) & (g_l < LOGIT_TIE)
-        same_set = set(gpu_ids[t].tolist()) == set(oid[t].tolist())
-        if same_set:
-            # only the order differs: every adjacent swap must be a near-tie
-            j = int(np.nonzero(gpu_ids[t] != oid[t])[0][0])
-            ok = bool(tie[j])
-        else:
-            ok = k < E and bool(tie[k - 1])
-        gs = s[gpu_ids[t]]
-        ok = ok and bool(np.all(gs >= s[order[k - 1]] - NEAR_TIE))
-        ok = ok and bool(np.all(gs[:-1] >= gs[1:] - NEAR_TIE))
-        assert ok, (f"token {t}: gpu ids {gpu_ids[t].tolist()} != oracle {oid[t].tolist()}; "
-                    f"score gaps {g_s.tolist()}, logit gaps {g_l.tolist()}")
+    for t in np.nonzero((gpu_ids != oracle_ids).any(1))[0]:
+        g, o = gpu_ids[t], oracle_ids[t]
+        ok = len(set(g.tolist())) == k and bool(np.all((g >= 0) & (g < E)))
+        bad = []
+        for j in np.nonzero(g != o)[0]:
+            if not ok:
+                break
+            dk = abs(key[t, g[j]] - key[t, o[j]])
+            ds = abs(key_score[t, g[j]] - key_score[t, o[j]])
+            if not (dk < key_tol and ds < score_tol):
+                bad.append((int(j), int(g[j]), int(o[j]), float(dk), float(ds)))
+        assert ok and not bad, (f"token {t}: gpu ids {g.tolist()} != oracle {o.tolist()}; "
+                                f"(slot, gpu, oracle, key gap, score gap) outside the near-tie band: {bad}")
         exempt.append(int(t))
     return np.array(exempt, dtype=np.int64)
+
+
+def check_routing(gpu_ids: np.ndarray, ref: dict, k: int) -> np.ndarray:
+    """Plain routing (key = logit): check_ids with the oracle's logits and
+    scores, logit band LOGIT_TIE, score band NEAR_TIE."""
+    return check_ids(gpu_ids, ref["ids"], ref["logits"], ref["scores"], LOGIT_TIE, NEAR_TIE)
 
 
 def oracle_routing(inp: dict, sh: synth.LayerShape) -> dict:
@@ -133,6 +141,19 @@ def oracle_routing(inp: dict, sh: synth.LayerShape) -> dict:
     r = oracle.route(lg, sh.k, sh.score_fn, sh.renormalize)
     r["logits"] = lg
     return r
+
+
+def check_gaps(gap: np.ndarray, ref: dict, k: int, E: int, skip=()) -> None:
+    """GPU margins [T,2] against the oracle's: the key (logit) margin within
+    1e-3 absolute + 1e-4 relative (fp32 logits), the score margin within
+    2e-6 absolute + 1e-3 relative (fp32 scores); +inf for both when k == E.
+    Tokens in ``skip`` (routed differently at a near-tie) are left out."""
+    if k == E:
+        assert np.all(np.isinf(gap))
+        return
+    ok = np.setdiff1d(np.arange(gap.shape[0]), np.asarray(skip, dtype=np.int64))
+    np.testing.assert_allclose(gap[ok, 0], ref["gap_logit"][ok], atol=1e-3, rtol=1e-4, err_msg="key margin")
+    np.testing.assert_allclose(gap[ok, 1], ref["gap_score"][ok], atol=2e-6, rtol=1e-3, err_msg="score margin")
 
 
 def assert_close(got: np.ndarray, want: np.ndarray, tau: float, what: str):

@@ -94,7 +94,8 @@ def test_config_validation(kw, status):
     assert route(c) == status
     assert moe.moe_workspace_bytes(c) == 0
     L = moe.lib()
-    assert L.moe_forward(ctypes.byref(c), *([FAKE] * 12), FAKE, 1 << 40, None) == status
+    assert L.moe_forward(ctypes.byref(c), *([FAKE] * 13), FAKE, 1 << 40, None) == status
+    assert moe.lib().moe_capacity(ctypes.byref(c), 1.0) == status
     assert L.moe_dispatch(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == status
     assert L.moe_combine(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
 
@@ -121,7 +122,7 @@ def test_workspace_checks():
     L = moe.lib()
     need = moe.moe_workspace_bytes(c)
     assert need > 0 and need % 256 == 0
-    args = [FAKE] * 12
+    args = [FAKE] * 13
     assert L.moe_forward(ctypes.byref(c), *args, None, need, None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_forward(ctypes.byref(c), *args, FAKE, need - 1, None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_forward_staged(ctypes.byref(c), *args, FAKE, need - 1, None, None, None) == moe.MOE_ERR_WORKSPACE
@@ -175,11 +176,56 @@ def test_options_are_validated_before_launch():
     assert route_ex(cfg(k=0), O(None, 0, 0, None, 0.0)) == moe.MOE_ERR_SHAPE
 
 
-def test_capacity_helper_matches_page():
-    # 4,096 tokens, 64 experts, top-8, factor 1.0 -> 512 slots
+def test_capacity_matches_page():
+    """moe_capacity: the page's 4,096 tokens, 64 experts, top-8, factor 1.0
+    give 512 slots ('from the router to the all-to-all', Capacity and token
+    dropping); factor 1.25 gives 640; a whole-number product stays whole
+    although its doubles are not (640 * 8 / 8 * 1.1 = 704.0000000000001)."""
     assert moe.capacity(4096, 8, 64, 1.0) == 512
     assert moe.capacity(4096, 8, 64, 1.25) == 640
     assert moe.capacity(10, 2, 3, 1.0) == 7
+    assert moe.capacity(640, 8, 8, 1.1) == 704
+    assert moe.capacity(4096, 8, 64, 1.1) == 564
+    assert moe.capacity(0, 8, 64, 1.25) == 0
+
+
+def test_capacity_agrees_with_exact_rational():
+    """The library's rounding against the oracle's exact rational ceiling over
+    token counts, widths and decimal factors."""
+    import oracle
+    for T in (1, 7, 97, 333, 640, 1000, 4096, 8192, 65535):
+        for E, k in ((8, 2), (64, 8), (256, 8), (6, 4), (3, 1), (100, 3)):
+            for f in (0.5, 0.75, 0.8, 0.9, 1.0, 1.05, 1.1, 1.2, 1.25, 1.3, 1.5, 2.0, 3.7):
+                assert moe.capacity(T, k, E, f) == oracle.capacity(T, k, E, f), (T, E, k, f)
+
+
+def test_capacity_rejects_bad_factors():
+    L = moe.lib()
+    c = cfg()
+    for f in (0.0, -1.0, float("nan"), float("inf")):
+        assert L.moe_capacity(ctypes.byref(c), f) == moe.MOE_ERR_SHAPE
+    assert L.moe_capacity(ctypes.byref(cfg(T=2**26, E=8, k=8)), 1e3) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_capacity(None, 1.0) == moe.MOE_ERR_NULL
+
+
+def test_forward_entry_points_take_the_gap_after_the_counts():
+    """moe_forward, moe_forward_staged and moe_forward_ex take a nullable
+    float* topk_gap_out right after expert_counts_out (the near-ties of the
+    call's own routing), and reject a misaligned one before any launch."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name in ("moe_forward", "moe_forward_staged", "moe_forward_ex"):
+        m = re.search(r"\b%s\s*\(([^;]*?)\)\s*;" % name, src)
+        params = [p.strip() for p in m.group(1).split(",")]
+        i = params.index("int32_t* expert_counts_out")
+        assert params[i + 1] == "float* topk_gap_out", (name, params)
+    c = cfg()
+    L = moe.lib()
+    need = moe.moe_workspace_bytes(c)
+    args = [FAKE] * 12
+    assert L.moe_forward(ctypes.byref(c), *args, FAKE + 4, FAKE, need, None) == moe.MOE_ERR_ALIGN
+    assert L.moe_forward_staged(ctypes.byref(c), *args, FAKE + 4, FAKE, need, None, None, None) == \
+        moe.MOE_ERR_ALIGN
+    assert L.moe_forward_ex(ctypes.byref(c), None, *args, FAKE + 4, FAKE, need, None) == moe.MOE_ERR_ALIGN
 
 
 def test_backward_options_are_validated_before_launch():

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_harness import TAU, DeviceLayer, assert_close, to_dev, to_host, torch
+from gpu_harness import LOGIT_TIE, NEAR_TIE, TAU, DeviceLayer, assert_close, check_ids, to_dev, to_host, torch
 
 pytestmark = pytest.mark.gpu
 S = synth.LayerShape
@@ -34,15 +34,27 @@ def moe_mod():
     return moe
 
 
-def check_ids_keyspace(gids, ref, tol):
-    """Ids equal the oracle's in order, except where the oracle's key gap at
-    the k-th choice (or an adjacent swap) is below tol.  Returns exempt tokens."""
-    oid = ref["ids"]
-    bad = np.nonzero((gids != oid).any(1))[0]
-    for t in bad:
-        assert ref["gap_logit"][t] < tol or set(gids[t]) == set(oid[t]), \
-            f"token {t}: gpu {gids[t].tolist()} oracle {oid[t].tolist()} key gap {ref['gap_logit'][t]:.3e}"
-    return bad
+def selection_keys(lg, scores, b, on_scores, score_fn):
+    """The oracle's selection key [T,E] for a selection bias b, and the key in
+    score space: key = score + b (already a score), or key = logit + b,
+    whose score image is the score function of the biased logits (softmax
+    over the experts, or the sigmoid)."""
+    if on_scores:
+        key = scores + b
+        return key, key
+    key = lg + b
+    if score_fn == synth.SIGMOID:
+        return key, 1.0 / (1.0 + np.exp(-key))
+    e = np.exp(key - key.max(1, keepdims=True))
+    return key, e / e.sum(1, keepdims=True)
+
+
+def check_ids_keyspace(gids, ref, key, key_score, on_scores):
+    """Ids in order against the oracle's biased selection, by the near-tie
+    rule of the plain path (check_ids): every differing slot sits at a
+    near-tie of the selection key (score space 1e-6; a logit key also within
+    the fp32 logit band).  Returns exempt tokens."""
+    return check_ids(gids, ref["ids"], key, key_score, NEAR_TIE if on_scores else LOGIT_TIE, NEAR_TIE)
 
 
 def run_route_ex(L, opts):
@@ -50,7 +62,7 @@ def run_route_ex(L, opts):
     sh = L.sh
     ids = t.empty(sh.T, sh.k, dtype=t.int32, device="cuda")
     wts = t.empty(sh.T, sh.k, dtype=t.float32, device="cuda")
-    gap = t.empty(sh.T, dtype=t.float32, device="cuda")
+    gap = t.empty(sh.T, 2, dtype=t.float32, device="cuda")
     moe_mod().moe_route_ex(L.cfg, opts, L.d["x"], L.d["w_router"], ids, wts, gap, ws=L.ws)
     return ids, wts, gap
 
@@ -62,10 +74,11 @@ def run_forward_ex(L, opts):
     ids = t.empty(sh.T, sh.k, dtype=t.int32, device="cuda")
     wts = t.empty(sh.T, sh.k, dtype=t.float32, device="cuda")
     counts = t.empty(sh.E, dtype=t.int32, device="cuda")
+    gap = t.empty(sh.T, 2, dtype=t.float32, device="cuda")
     dv = L.d
     moe_mod().moe_forward_ex(L.cfg, opts, dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"],
-                             dv["ws_gate"], dv["ws_up"], dv["ws_down"], y, ids, wts, counts, L.ws)
-    return dict(y=y, ids=ids, weights=wts, counts=counts)
+                             dv["ws_gate"], dv["ws_up"], dv["ws_down"], y, ids, wts, counts, L.ws, topk_gap=gap)
+    return dict(y=y, ids=ids, weights=wts, counts=counts, gap=gap)
 
 
 BIAS_CASES = {
@@ -98,15 +111,21 @@ def test_selection_bias(name):
                        bias_on_scores=on_scores)
     plain = oracle.route(lg, sh.k, sh.score_fn, sh.renormalize)
     changed = int((ref["ids"] != plain["ids"]).any(1).sum())
-    tol = 2e-6 if on_scores else 1e-4
+    key, key_score = selection_keys(lg, plain["scores"], b.astype(np.float64), on_scores, sh.score_fn)
     gids = to_host(ids)
-    ex = check_ids_keyspace(gids, ref, tol)
+    ex = check_ids_keyspace(gids, ref, key, key_score, on_scores)
     fids = to_host(fw["ids"])
-    check_ids_keyspace(fids, ref, tol)
+    fex = check_ids_keyspace(fids, ref, key, key_score, on_scores)
     rf = oracle.route(lg, sh.k, sh.score_fn, sh.renormalize, forced_ids=gids)
     np.testing.assert_allclose(to_host(wts), rf["gates"], atol=1e-5, rtol=0)
-    ok = np.setdiff1d(np.arange(sh.T), ex)
-    np.testing.assert_allclose(to_host(gap)[ok], ref["gap_logit"][ok], atol=tol * 10 + 1e-5, rtol=1e-4)
+    # margins: the selection key's (score-space keys to fp32 score accuracy,
+    # logit keys as the plain logits), and the unbiased score margin of the
+    # same two experts
+    for g, skip in ((to_host(gap), ex), (to_host(fw["gap"]), fex)):
+        ok = np.setdiff1d(np.arange(sh.T), skip)
+        np.testing.assert_allclose(g[ok, 0], ref["gap_logit"][ok], atol=2e-6 if on_scores else 1e-3,
+                                   rtol=1e-3 if on_scores else 1e-4, err_msg="key margin")
+        np.testing.assert_allclose(g[ok, 1], ref["gap_score"][ok], atol=2e-6, rtol=1e-3, err_msg="score margin")
     rff = oracle.route(lg, sh.k, sh.score_fn, sh.renormalize, forced_ids=fids)
     np.testing.assert_allclose(to_host(fw["weights"]), rff["gates"], atol=1e-5, rtol=0)
     toks = np.arange(sh.T) if sh.T <= 64 else np.unique(np.concatenate([[0, sh.T - 1],
@@ -156,7 +175,9 @@ def test_capacity_drops(name):
     moe = moe_mod()
     t = torch()
     cap = moe.capacity(sh.T, sh.k, sh.E, factor)
-    opts = moe.MoeOptions.of(expert_capacity=cap)
+    assert cap == oracle.capacity(sh.T, sh.k, sh.E, factor)
+    stats = t.full((2 * sh.E + 3,), -1.0, dtype=t.float32, device="cuda")
+    opts = moe.MoeOptions.of(expert_capacity=cap, router_stats=stats)
     st = L.steps()                                   # plain routing: the ids to dispatch
     P = sh.T * sh.k
     counts = t.empty(sh.E, dtype=t.int32, device="cuda")
@@ -180,6 +201,12 @@ def test_capacity_drops(name):
     fids = to_host(fw["ids"])
     fd = oracle.dispatch(fids, sh.E, cap=cap)
     np.testing.assert_array_equal(to_host(fw["counts"]), fd["counts"])
+    # the statistics' overflow: the pairs this capacity drops from the call's routing
+    lg = oracle.logits(inp["x"], inp["w_router"])
+    sref = oracle.router_stats(oracle.route(lg, sh.k, sh.score_fn, sh.renormalize)["scores"], fids,
+                               sh.score_fn, 0.0, cap=cap)
+    g = to_host(stats)
+    assert g[2 * sh.E + 2] == sref["overflow"] == int((fd["pair_pos"] < 0).sum())
     keep = (fd["pair_pos"] >= 0).reshape(sh.T, sh.k).astype(np.int32)
     rng = np.random.default_rng(1)
     toks = np.arange(sh.T) if sh.T <= 80 else np.unique(np.concatenate([[0, sh.T - 1],
@@ -208,8 +235,8 @@ def test_router_stats(name):
     L = DeviceLayer(sh, inp)
     moe = moe_mod()
     t = torch()
-    out = t.full((2 * sh.E + 2,), -1.0, dtype=t.float32, device="cuda")
-    out2 = t.full((2 * sh.E + 2,), -1.0, dtype=t.float32, device="cuda")
+    out = t.full((2 * sh.E + 3,), -1.0, dtype=t.float32, device="cuda")
+    out2 = t.full((2 * sh.E + 3,), -1.0, dtype=t.float32, device="cuda")
     alpha = 0.01
     ids, _, _ = run_route_ex(L, moe.MoeOptions.of(router_stats=out, aux_alpha=alpha))
     fw = run_forward_ex(L, moe.MoeOptions.of(router_stats=out2, aux_alpha=alpha))
@@ -224,6 +251,7 @@ def test_router_stats(name):
         np.testing.assert_allclose(g[E:2 * E], ref["P"], atol=2e-6, rtol=1e-4)
         np.testing.assert_allclose(g[2 * E], ref["l_aux"], rtol=1e-4)
         np.testing.assert_allclose(g[2 * E + 1], ref["max_over_mean"], rtol=1e-6)
+        assert g[2 * E + 2] == 0.0          # no capacity: no overflow
     say(f"[ok] L_aux {float(to_host(out)[2 * sh.E]):.5f} max/mean {float(to_host(out)[2 * sh.E + 1]):.3f}")
 
 
