@@ -190,6 +190,30 @@ int moe_forward(const moe_config* cfg, const void* x, const void* w_router, cons
                 int32_t* expert_counts_out, float* topk_gap_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The caller passes inputs and outputs only (same meaning as moe_forward);
+ * the workspace is the library's own: a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES in device memory, one per GPU, which each GPU the
+ * library runs on holds from module load until the process ends.  Nothing
+ * is allocated or freed: no hipMalloc, no allocating library routine.
+ *   Limit: layers whose moe_workspace_bytes(cfg) exceed the array (decode-
+ *   sized batches fit: Mixtral-8x7B widths up to about 256 tokens) return
+ *   MOE_ERR_WORKSPACE before anything is enqueued.
+ *   Sharing: every call on one GPU uses that GPU's array, which keeps the
+ *   last call's contents (each call sets up what it needs, counters
+ *   included).  Calls that overlap on one GPU, on different streams or from
+ *   different threads, race on it: serialise them.
+ * The first call on a device looks up the array's address on that device
+ * (current device); a failure there returns MOE_ERR_HIP.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const moe_config* cfg, const void* x, const void* w_router, const void* w_gate,
+                        const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,
+                        const void* ws_down, void* y, int32_t* topk_ids_out, float* topk_weights_out,
+                        int32_t* expert_counts_out, float* topk_gap_out, void* stream);
+
+/*
  * moe_forward with per-stage timing ("T2.6 -- What Mixture of Experts
  * Changes", In practice: watch per-expert counts and expert compute time;
  * profile each stage).  Same arguments and results as moe_forward, plus

@@ -31,7 +31,8 @@ MOE_F32, MOE_BF16 = 0, 1
 EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_staged",
            "moe_route_ex", "moe_dispatch_ex", "moe_forward_ex", "moe_capacity",
-           "moe_backward_workspace_bytes", "moe_backward", "moe_backward_ex")
+           "moe_backward_workspace_bytes", "moe_backward", "moe_backward_ex", "moe_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_NUM_STAGES = 7
 STAGE_NAMES = ("route", "dispatch", "gate_up_gemm", "down_gemm", "shared_gate_up", "shared_down",
                "combine")
@@ -124,6 +125,8 @@ def lib():
         L.moe_forward_ex.restype = i32
         L.moe_capacity.argtypes = [cfgp, ctypes.c_double]
         L.moe_capacity.restype = i32
+        L.moe_forward_noalloc.argtypes = [cfgp] + [vp] * 13 + [vp]
+        L.moe_forward_noalloc.restype = i32
         L.moe_backward_workspace_bytes.argtypes = [cfgp]
         L.moe_backward_workspace_bytes.restype = sz
         L.moe_backward.argtypes = [cfgp] + [vp] * 20 + [sz, vp]
@@ -278,6 +281,29 @@ def moe_forward(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
                           _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(y),
                           _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_counts), _ptr(topk_gap),
                           _ptr(ws), _ws_bytes(ws), _stream(stream)), "moe_forward")
+
+
+def moe_forward_noalloc(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,
+                        topk_ids=None, topk_weights=None, expert_counts=None, topk_gap=None, stream=None):
+    """moe_forward without a workspace argument: the library's own fixed
+    device array (NOALLOC_SCRATCH_BYTES per GPU) serves as the workspace.
+    Layers that need more raise MoeError(MOE_ERR_WORKSPACE); calls that
+    overlap on one GPU race on the array."""
+    torch = _torch()
+    T, d, E, k = cfg.num_tokens, cfg.d_model, cfg.num_experts, cfg.top_k
+    dt, dev = _act_dtype(cfg), x.device
+    _check(x, "x", (T, d), dt, dev)
+    _check(w_router, "w_router", (E, d), dt, dev)
+    _check_experts(cfg, dev, w_gate, w_up, w_down, ws_gate, ws_up, ws_down)
+    _check(y, "y", (T, d), dt, dev)
+    _check(topk_ids, "topk_ids", (T, k), torch.int32, dev, optional=True)
+    _check(topk_weights, "topk_weights", (T, k), torch.float32, dev, optional=True)
+    _check(expert_counts, "expert_counts", (E,), torch.int32, dev, optional=True)
+    _check(topk_gap, "topk_gap", (T, 2), torch.float32, dev, optional=True)
+    _rc(lib().moe_forward_noalloc(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(w_gate), _ptr(w_up),
+                                  _ptr(w_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), _ptr(y),
+                                  _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_counts), _ptr(topk_gap),
+                                  _stream(stream)), "moe_forward_noalloc")
 
 
 def moe_forward_staged(cfg, x, w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, y,

@@ -738,6 +738,8 @@ int run_backward(const moe_config* c, const void* x, const void* wr, const void*
 
 }  // namespace
 
+int moe::validate_config(const moe_config* cfg) { return validate_cfg(cfg); }
+
 extern "C" {
 
 size_t moe_workspace_bytes(const moe_config* cfg) {

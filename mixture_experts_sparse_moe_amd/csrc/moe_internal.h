@@ -5,9 +5,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+struct moe_config;
+
 namespace moe {
 
 using bf16_t = uint16_t;  // bf16 storage: upper half of an IEEE fp32
+
+// The C ABI's check of a moe_config: MOE_OK or the negative status the entry
+// points return for it (host only).
+int validate_config(const moe_config* cfg);
 
 // ---- dispatch: histogram, scan, stable scatter ------------------------------
 constexpr int kDispatchChunk = 2048;   // pairs per chunk (one workgroup each)

@@ -246,3 +246,15 @@ def test_backward_options_are_validated_before_launch():
     assert bwd(O(FAKE + 4, 0, 0, None, 0.0)) == moe.MOE_ERR_ALIGN         # bias alignment
     assert bwd(O(None, 0, 64, None, 0.0), ws=FAKE, ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
     assert bwd(None, ws=None) == moe.MOE_ERR_WORKSPACE
+
+
+def test_noalloc_rejects_layers_past_its_array():
+    """moe_forward_noalloc refuses a layer whose workspace exceeds its fixed
+    array (here the Mixtral-8x7B prefill layer) before touching the GPU; a
+    bad config is still a config error."""
+    L = moe.lib()
+    big = moe.MoeConfig.of(4096, 4096, 8, 2, 14336)
+    assert moe.moe_workspace_bytes(big) > moe.NOALLOC_SCRATCH_BYTES
+    assert L.moe_forward_noalloc(ctypes.byref(big), *([FAKE] * 13), None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_forward_noalloc(None, *([FAKE] * 13), None) == moe.MOE_ERR_NULL
+    assert L.moe_forward_noalloc(ctypes.byref(cfg(k=9)), *([FAKE] * 13), None) == moe.MOE_ERR_SHAPE
