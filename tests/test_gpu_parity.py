@@ -13,8 +13,9 @@ Every case uses seeded synthetic inputs (``synth``).  Rules:
 Small cases span several GEMM tiles in M, N and K with ragged tails; the
 full-size layer shapes check all routing and dispatch outputs, and the
 expert outputs and y on a stratified sample: the first and the last grouped
-row of every (expert, 256-row M tile) of the routed GEMMs' tile lists (so
-every tile of every schedule, the one-row tails included) and their tokens.
+row of every M tile of every expert (both the 256-row tiles with a short last
+one and the even split, so every tile of every schedule, the one-row tails
+included) and their tokens.
 """
 import os
 import sys
@@ -66,12 +67,19 @@ def need_gpu():
 
 
 def tile_edge_rows(offsets: np.ndarray, bm: int = 256) -> np.ndarray:
-    """First and last grouped row of every M tile of bm rows of every expert."""
+    """First and last grouped row of every M tile of every expert, for both
+    ways the GEMMs cut an expert's n rows into m = ceil(n / bm) tiles: full
+    tiles of bm rows and a short last one, or m tiles of ceil(n / m) rows."""
     rows = []
     for e in range(offsets.size - 1):
         a, b = int(offsets[e]), int(offsets[e + 1])
-        for r0 in range(a, b, bm):
-            rows += [r0, min(r0 + bm, b) - 1]
+        n = b - a
+        if n == 0:
+            continue
+        m = -(-n // bm)
+        for h in (bm, -(-n // m)):
+            for r0 in range(a, b, h):
+                rows += [r0, min(r0 + h, b) - 1]
     return np.unique(np.array(rows, dtype=np.int64))
 
 
