@@ -68,10 +68,12 @@ def parse():
                    help="skip timing the backward pass (moe_backward)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of 1 GiB (the reference for HBM counters)")
-    p.add_argument("--traffic-from", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_DIR"),
-                   help="rocprofv3 --pmc output dirs (FETCH_SIZE run of the bench, WRITE_SIZE run "
-                        "of the bench, FETCH_SIZE+WRITE_SIZE runs of --copy-calibration); writes "
-                        "profiles/traffic.json for --workload")
+    p.add_argument("--traffic-from", nargs=4, metavar=("READ_DIR", "WRITE_DIR", "COPY_READ_DIR", "COPY_WRITE_DIR"),
+                   help="rocprofv3 --pmc output dirs: TCC_EA0_RDREQ_32B/64B/128B_sum and WRITE_SIZE runs "
+                        "of the bench, the same two of --copy-calibration; writes profiles/traffic.json "
+                        "for --workload")
+    p.add_argument("--trace-summary", metavar="TRACE_DIR",
+                   help="markdown table of a rocprofv3 --kernel-trace --stats run (its kernel_stats.csv)")
     p.add_argument("--counters-from", metavar="PMC_DIR",
                    help="summarise a rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES, "
                         "SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE per kernel")
@@ -137,25 +139,32 @@ def upload(a: np.ndarray, torch, dev):
     return torch.from_numpy(a).to(dev)
 
 
-def algorithmic(sh, counts: np.ndarray) -> dict:
+def algorithmic(sh, counts: np.ndarray, shared_merged: bool = False) -> dict:
     """Algorithmic work of the layer and of its two expert GEMM kernels.
 
     FLOPs: router 2TdE, routed experts 6 d d_ff per pair (4 in gate/up, 2 in
     down), shared expert 6 d d_ff_s per token.  Bytes: weights of the experts
     actually touched (union read), the router weights, x read once, y written
     once, 8 bytes of routing per pair; per kernel, its weights plus its
-    activation input and output."""
+    activation input and output.  shared_merged: the two kernels also run the
+    shared expert (its weights, T more rows of H and of the down product; x
+    is still read once)."""
     w = sh.elem_bytes
-    T, d, E, k, f = sh.T, sh.d, sh.E, sh.k, sh.d_ff
+    T, d, E, k, f, fs = sh.T, sh.d, sh.E, sh.k, sh.d_ff, sh.d_ff_shared
     touched = int((counts > 0).sum())
     P = T * k
     layer_flops = sh.flops()
-    layer_bytes = (E * d * w + touched * 3 * d * f * w + sh.num_shared * 3 * d * sh.d_ff_shared * w
+    layer_bytes = (E * d * w + touched * 3 * d * f * w + sh.num_shared * 3 * d * fs * w
                    + 2 * T * d * w + P * 8)
     gate_up = dict(flops=4.0 * P * d * f, bytes=touched * 2 * d * f * w + T * d * w + P * f * w)
     down = dict(flops=2.0 * P * d * f, bytes=touched * d * f * w + P * f * w + P * d * w)
+    if shared_merged:
+        gate_up = dict(flops=gate_up["flops"] + 4.0 * T * d * fs,
+                       bytes=gate_up["bytes"] + 2 * d * fs * w + T * fs * w)
+        down = dict(flops=down["flops"] + 2.0 * T * d * fs,
+                    bytes=down["bytes"] + d * fs * w + T * fs * w + T * d * w)
     return dict(layer_flops=layer_flops, layer_bytes=layer_bytes, gate_up=gate_up, down=down,
-                touched=touched)
+                touched=touched, shared_merged=shared_merged)
 
 
 def options_cost(torch, moe, cfg, d, y, ws, stream, sh, steps: int) -> dict:
@@ -316,8 +325,8 @@ COPY_BYTES = 1 << 30
 
 
 def copy_calibration():
-    """A plain 1 GiB device-to-device copy: its FETCH_SIZE / WRITE_SIZE readings
-    give the scale between those counters and bytes moved."""
+    """A plain 1 GiB device-to-device copy: the HBM counters must read 1 GiB
+    fetched and 1 GiB written for it (a check of the byte formulas)."""
     import torch
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
@@ -328,11 +337,14 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": COPY_BYTES}), flush=True)
 
 
-# the gate/up GEMM kernel as rocprofv3 names it (bf16, dual mode; prefix of
-# the template argument list)
-# the routed gate/up GEMM: the 256-row tile kernel, or the 32-row one for
-# decode-sized batches (one of them runs per workload)
-GATE_UP_KERNELS = ("gemm_bf16_persistent_kernel<true", "gemm_bf16_skinny_kernel<true")
+# the routed GEMM kernels as rocprofv3 names them (prefix of the template
+# argument list): the 256-row tile kernel, or the 32-row one for decode-sized
+# batches (one of them runs per workload); dual = gate/up, single = down; the
+# routed ones take the expert-aligned tile order (template argument 2), the
+# shared expert's do not
+GATE_UP_KERNELS = ("gemm_bf16_persistent_kernel<true, true", "gemm_bf16_skinny_kernel<true")
+DOWN_KERNELS = ("gemm_bf16_persistent_kernel<false, true", "gemm_bf16_skinny_kernel<false")
+READ_COUNTERS = ("TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum")
 
 
 def _pmc_rows(d):
@@ -363,27 +375,37 @@ def _per_dispatch(rows, counter, names):
     return sum(vals) / len(vals) if vals else None
 
 
+def _read_bytes(rows, names):
+    """Fabric read bytes per dispatch: the L2's 32-, 64- and 128-byte read
+    requests to the fabric, 32 n32 + 64 n64 + 128 n128 (FETCH_SIZE's formula
+    counts this chip's 128-byte requests as 64 bytes: it reads half a copy)."""
+    n = [_per_dispatch(rows, c, names) for c in READ_COUNTERS]
+    return None if None in n else 32 * n[0] + 64 * n[1] + 128 * n[2]
+
+
 def traffic_from(args):
-    """HBM bytes per launch of the gate/up GEMM from rocprofv3 FETCH_SIZE and
-    WRITE_SIZE runs, each scaled by the same counter's reading for the 1 GiB copy."""
-    fetch_dir, write_dir, copy_dir = args.traffic_from
-    copy_rows = _pmc_rows(copy_dir)
-    # the copy kernel is the largest dispatch of the calibration run
-    cf = max((float(r["Counter_Value"]) for r in copy_rows if r["Counter_Name"] == "FETCH_SIZE"),
-             default=None)
-    cw = max((float(r["Counter_Value"]) for r in copy_rows if r["Counter_Name"] == "WRITE_SIZE"),
-             default=None)
-    f_kib = _per_dispatch(_pmc_rows(fetch_dir), "FETCH_SIZE", GATE_UP_KERNELS)
-    w_kib = _per_dispatch(_pmc_rows(write_dir), "WRITE_SIZE", GATE_UP_KERNELS)
-    if None in (cf, cw, f_kib, w_kib):
-        sys.exit(f"missing counters: copy {cf} {cw}, kernel {f_kib} {w_kib}")
-    f_scale, w_scale = COPY_BYTES / cf, COPY_BYTES / cw
-    rec = {"kernel": "grouped gate/up GEMM (" + " or ".join(GATE_UP_KERNELS) + ", ...>)",
-           "fetch_kib": f_kib, "write_kib": w_kib,
-           "copy_fetch_kib": cf, "copy_write_kib": cw,
-           "fetch_scale_bytes_per_kib": f_scale, "write_scale_bytes_per_kib": w_scale,
-           "bytes_per_launch": f_kib * f_scale + w_kib * w_scale,
+    """HBM bytes per launch of the routed GEMMs from rocprofv3 runs: fabric
+    reads from the TCC_EA0_RDREQ_32B/64B/128B counts, writes from WRITE_SIZE
+    (KiB); both checked on a 1 GiB copy (--copy-calibration), which must read
+    1 GiB and write 1 GiB.  Writes profiles/traffic.json for --workload."""
+    rd_dir, wr_dir, crd_dir, cwr_dir = args.traffic_from
+    copy_names = ("copyBuffer", "elementwise_kernel")
+    crd = max((_read_bytes([r for r in _pmc_rows(crd_dir) if n in r["Kernel_Name"]], (n,)) or 0.0)
+              for n in copy_names)
+    cwr = max((float(r["Counter_Value"]) * 1024 for r in _pmc_rows(cwr_dir) if r["Counter_Name"] == "WRITE_SIZE"),
+              default=None)
+    rows_rd, rows_wr = _pmc_rows(rd_dir), _pmc_rows(wr_dir)
+    rec = {"method": "reads: 32 TCC_EA0_RDREQ_32B + 64 TCC_EA0_RDREQ_64B + 128 TCC_EA0_RDREQ_128B; "
+                     "writes: WRITE_SIZE KiB * 1024; per dispatch, averaged",
+           "copy_check": {"copy_bytes": COPY_BYTES, "read_bytes": crd, "write_bytes": cwr},
            "source_hash": kernel_source_hash()}
+    for tag, names in (("gate_up", GATE_UP_KERNELS), ("down", DOWN_KERNELS)):
+        rb = _read_bytes(rows_rd, names)
+        wk = _per_dispatch(rows_wr, "WRITE_SIZE", names)
+        if rb is None or wk is None:
+            sys.exit(f"missing counters for {tag}: read {rb}, write {wk}")
+        rec[tag] = {"read_bytes": rb, "write_bytes": wk * 1024, "bytes_per_launch": rb + wk * 1024}
+    rec["bytes_per_launch"] = rec["gate_up"]["bytes_per_launch"]
     data = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
     data[args.workload] = rec
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
@@ -391,6 +413,21 @@ def traffic_from(args):
     print(json.dumps(rec))
 
 
+def trace_summary(args):
+    """The kernel_stats.csv of a rocprofv3 --kernel-trace --stats run as a
+    markdown table (durations in us; calls include warm-up launches)."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(args.trace_summary, "**", "*kernel_stats.csv"), recursive=True)
+    if not f:
+        sys.exit(f"no kernel_stats.csv under {args.trace_summary}")
+    print("| kernel | calls | avg (us) | min (us) | max (us) | share |")
+    print("|---|---|---|---|---|---|")
+    for r in csv.DictReader(open(f[0])):
+        name = r["Name"].replace("void ", "").replace("moe::(anonymous namespace)::", "")
+        name = name.replace("(moe::GemmGroup, int)", "").replace("(moe::", "(")
+        print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+              f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} % |")
 
 
 def counters_from(args):
@@ -490,7 +527,8 @@ def measure(name: str, args, torch, moe, dev, extras: bool) -> dict:
     stage_avg = stage_ms.mean(0)
     tev.close()
     cnt = counts.cpu().numpy()
-    alg = algorithmic(sh, cnt)
+    plan = moe.moe_forward_plan(cfg)
+    alg = algorithmic(sh, cnt, plan["shared_merged"])
     bf16 = sh.dtype == synth.BF16
     peak_c = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     gu = alg["gate_up"]
@@ -504,7 +542,8 @@ def measure(name: str, args, torch, moe, dev, extras: bool) -> dict:
         r_["frac"] = r_["achieved"] / r_["peak"]
     roof, other = (hbm_roof, cmp_roof) if t_hbm >= t_mfma else (cmp_roof, hbm_roof)
     roof = dict(roof)
-    roof["kernel"] = "gate_up_gemm (grouped gate/up GEMM + SiLU*up)"
+    roof["kernel"] = "gate_up_gemm (grouped gate/up GEMM + SiLU*up" + (
+        ", the shared expert as one more group)" if plan["shared_merged"] else ")")
     roof["per_launch"] = {"flops": gu["flops"], "bytes": gu["bytes"], "avg_ms": gu_ms,
                           "floor_ms_hbm": t_hbm * 1e3, "floor_ms_compute": t_mfma * 1e3}
     roof["other_bound"] = other
@@ -537,6 +576,7 @@ def measure(name: str, args, torch, moe, dev, extras: bool) -> dict:
         "staged_ms_per_step": round(float(stage_ms.sum(1).mean()), 4),
         "expert_load": {"max_over_mean": float(cnt.max() / max(cnt.mean(), 1e-9)),
                         "touched": alg["touched"], "min": int(cnt.min()), "max": int(cnt.max())},
+        "plan": plan,
         "roofline": roof,
         # the routed grouped GEMM: gate/up (timed region) and down (stage pass) kernels
         "grouped_gemm": {"ms": gg_ms,
@@ -573,6 +613,9 @@ def main():
         return
     if args.counters_from:
         counters_from(args)
+        return
+    if args.trace_summary:
+        trace_summary(args)
         return
     if args.copy_calibration:
         copy_calibration()

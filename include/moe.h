@@ -183,6 +183,10 @@ int moe_combine(const moe_config* cfg, const void* expert_out, const float* topk
  * logits (below 8192 tokens) and the down projections may be summed over K
  * ranges (fixed order; deterministic), so results can differ from the
  * step-by-step calls in the last bits and routing at near-ties.
+ * A bf16 shared expert as wide as the routed ones (d_ff_shared == d_ff)
+ * runs inside the routed GEMMs' launches, as one more group of T rows with
+ * its own weights, when those GEMMs take 256-row tiles without K splits and
+ * no capacity is set; its products are the same as on its own launches.
  */
 int moe_forward(const moe_config* cfg, const void* x, const void* w_router, const void* w_gate,
                 const void* w_up, const void* w_down, const void* ws_gate, const void* ws_up,
@@ -225,7 +229,9 @@ int moe_forward_noalloc(const moe_config* cfg, const void* x, const void* w_rout
  *                 that kernel's own duration):
  *                 0 route, 1 dispatch, 2 routed gate/up GEMM (+SiLU*up),
  *                 3 routed down GEMM, 4 shared gate/up, 5 shared down,
- *                 6 combine.  Stages 4-5 are empty when num_shared == 0;
+ *                 6 combine.  Stages 4-5 are empty when num_shared == 0
+ *                 and when the shared expert runs inside the routed GEMMs
+ *                 (see moe_forward; its time then counts in stages 2-3);
  *                 stage 1 is empty when the batch is at most 32 bf16
  *                 tokens with a K-split router, whose last kernel then
  *                 also groups the pairs (its time counts in stage 0).
@@ -346,6 +352,20 @@ int moe_forward_ex(const moe_config* cfg, const moe_options* opts, const void* x
  * finite and positive, MOE_ERR_UNSUPPORTED for a result past INT32_MAX.
  * Host only. */
 int moe_capacity(const moe_config* cfg, double capacity_factor);
+
+/*
+ * How moe_forward (no capacity) lays the layer out on kernels, for reading
+ * its per-stage times and kernel traces ("T2.6 -- What Mixture of Experts
+ * Changes", In practice: profile each stage).  plan_out [4] int32, host:
+ *   [0] rows per tile of the routed expert GEMMs (256, or 32 for few pairs;
+ *       fp32 layers report 256 and use a plain tiled kernel),
+ *   [1] K splits of the routed down GEMM (1 = none),
+ *   [2] K splits of the shared down GEMM (0 when num_shared == 0),
+ *   [3] 1 when the shared expert runs inside the routed GEMMs' launches
+ *       (stages 4-5 of moe_forward_staged empty), else 0.
+ * Returns MOE_OK, an invalid cfg's moe_status, or MOE_ERR_NULL.  Host only.
+ */
+int moe_forward_plan(const moe_config* cfg, int32_t* plan_out);
 
 /* moe_backward with options, for training with an expert capacity ("8.6
  * Mixture of Experts", sec. 3.2; "Mixture-of-Experts, from the router to the

@@ -10,7 +10,8 @@ Entry points (same names as the C ABI):
     moe_workspace_bytes, moe_route, moe_dispatch, moe_expert_ffn,
     moe_combine, moe_forward, moe_forward_staged, moe_status_str,
     moe_route_ex, moe_dispatch_ex, moe_forward_ex (with MoeOptions),
-    moe_capacity, moe_backward_workspace_bytes, moe_backward, moe_backward_ex
+    moe_capacity, moe_forward_plan, moe_backward_workspace_bytes, moe_backward,
+    moe_backward_ex, moe_forward_noalloc
 """
 from __future__ import annotations
 
@@ -31,7 +32,8 @@ MOE_F32, MOE_BF16 = 0, 1
 EXPORTS = ("moe_workspace_bytes", "moe_status_str", "moe_route", "moe_dispatch",
            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_staged",
            "moe_route_ex", "moe_dispatch_ex", "moe_forward_ex", "moe_capacity",
-           "moe_backward_workspace_bytes", "moe_backward", "moe_backward_ex", "moe_forward_noalloc")
+           "moe_backward_workspace_bytes", "moe_backward", "moe_backward_ex", "moe_forward_noalloc",
+           "moe_forward_plan")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_NUM_STAGES = 7
 STAGE_NAMES = ("route", "dispatch", "gate_up_gemm", "down_gemm", "shared_gate_up", "shared_down",
@@ -83,6 +85,17 @@ def moe_capacity(cfg: "MoeConfig", capacity_factor: float) -> int:
     return c
 
 
+def moe_forward_plan(cfg: "MoeConfig") -> dict:
+    """How moe_forward lays the layer out on kernels (moe_forward_plan):
+    tile rows of the routed GEMMs, K splits of the routed and the shared down
+    GEMMs, and whether the shared expert runs inside the routed launches."""
+    out = (ctypes.c_int32 * 4)()
+    st = int(lib().moe_forward_plan(ctypes.byref(cfg), out))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_forward_plan")
+    return dict(tile_rows=out[0], routed_splits=out[1], shared_splits=out[2], shared_merged=bool(out[3]))
+
+
 def capacity(T: int, k: int, E: int, factor: float) -> int:
     """moe_capacity for a layer of T tokens, top-k of E experts."""
     return moe_capacity(MoeConfig.of(T, 64, E, k, 64), factor)
@@ -125,6 +138,8 @@ def lib():
         L.moe_forward_ex.restype = i32
         L.moe_capacity.argtypes = [cfgp, ctypes.c_double]
         L.moe_capacity.restype = i32
+        L.moe_forward_plan.argtypes = [cfgp, vp]
+        L.moe_forward_plan.restype = i32
         L.moe_forward_noalloc.argtypes = [cfgp] + [vp] * 13 + [vp]
         L.moe_forward_noalloc.restype = i32
         L.moe_backward_workspace_bytes.argtypes = [cfgp]

@@ -57,6 +57,9 @@ __global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(DispatchArgs a,
         a.counts[e] = run;
     }
     for (int i = threadIdx.x; i < a.nzero; i += kThreads) a.zero[i] = 0;
+    // the trailing group (no capacity, so the experts' pairs end at P)
+    for (int i = threadIdx.x; i < a.tail; i += kThreads) a.sorted_pairs[a.P + i] = i * a.tail_mul;
+    if (a.tail && threadIdx.x == 0) a.offsets[a.E + 1] = a.P + a.tail;
     expert_scan(a, run, tot, wsum);
 }
 
@@ -92,6 +95,7 @@ int dispatch_num_chunks(int P) { return (P + kDispatchChunk - 1) / kDispatchChun
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     const int nchunks = dispatch_num_chunks(a.P);
+    if (a.tail && (nchunks < 2 || a.cap != 0x7FFFFFFF || a.tail < 0)) return hipErrorInvalidValue;
     if (a.P == 0) {
         // no pairs: counts and offsets are all zero (a kernel, not a memset,
         // so that the call can be captured into a graph)

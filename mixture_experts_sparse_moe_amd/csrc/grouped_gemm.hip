@@ -305,7 +305,7 @@ __device__ __forceinline__ int tile_prefix(const GemmGroup& g, int* s_tb, int* s
             s_tb[tid] = v + before - nt;
             s_off[tid] = off;
         }
-        if (tid == g.G - 1) {           // G <= 256 < threads
+        if (tid == g.G - 1) {           // G <= 257 < threads
             s_tb[g.G] = v + before;
             s_off[g.G] = g.offsets[g.G];
         }
@@ -490,7 +490,11 @@ __device__ __forceinline__ void gather_rows(const GemmGroup& g, const TileRef& t
     }
 }
 
-template <bool DUAL, int NW, bool KG = false>
+// LAST: a last group with weights of its own is possible (B0_last); only the
+// tile-queue instantiations take it, which leaves the others' code as it was
+// (the extra pointer choice moved the register allocation of the fixed-order
+// dual kernel and put waits for all loads into its K loop: +6 % there).
+template <bool DUAL, int NW, bool KG = false, bool LAST = false>
 __device__ __forceinline__ DmaSrc<32 / NW> dma_src(const GemmGroup& g, const TileRef& t, const int* src,
                                                   int w, int lane, int k_split) {
     constexpr int J = 32 / NW;
@@ -523,9 +527,13 @@ __device__ __forceinline__ DmaSrc<32 / NW> dma_src(const GemmGroup& g, const Til
     s.rot = __builtin_amdgcn_readfirstlane((t.n0 / (DUAL ? 128 : 256) + 17 * t.grp) % (k_split / kBK));
     s.a = static_cast<const char*>(g.A) + (g.gather ? 0 : (int64_t)t.row0 * K2) + k0;
     // dual: the first half of the waves stage gate rows n0 .. n0 + 127, the
-    // second half the same up rows
-    s.b = static_cast<const char*>(DUAL ? (w < NW / 2 ? g.B0 : g.B1) : g.B0) +
-          ((int64_t)t.grp * g.N + t.n0) * K2 + k0;
+    // second half the same up rows; a last group with weights of its own
+    // (the shared expert) reads them from B0_last / B1_last
+    const bool own = LAST && g.B0_last != nullptr && t.grp == g.G - 1;
+    const void* b0 = own ? g.B0_last : g.B0;
+    const void* b1 = own ? g.B1_last : g.B1;
+    s.b = static_cast<const char*>(DUAL ? (w < NW / 2 ? b0 : b1) : b0) +
+          ((int64_t)(own ? 0 : t.grp) * g.N + t.n0) * K2 + k0;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
         const int r = w * (256 / NW) + j * 8 + (lane >> 3);
@@ -786,7 +794,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     constexpr bool BAL = DUAL && QUEUE;
     __shared__ __align__(16) uint16_t sA0[STG], sA1[STG];
     __shared__ __align__(16) uint16_t sB0[STG], sB1[STG];
-    __shared__ int s_tb[257], s_off[257];
+    __shared__ int s_tb[258], s_off[258];     // up to 257 groups (256 experts + a shared one)
     __shared__ int s_wsum[8];
 
     const int tid = threadIdx.x;
@@ -888,7 +896,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_[i], bf_[b], acc[i][b], 0, 0, 0);    \
     } while (0)
 // The MFMAs of a step with the fragment reads of the following step between
-// them: 8 MFMAs / 6 reads for 4 row blocks, 4 / 4 for 2.
+// them: 2 NA MFMAs and NA + 2 reads for NA live row blocks.
 #define MOE_INTERLEAVE(NA_)                                                                     \
     do {                                                                                        \
         if ((NA_) == 4) {                                                                       \
@@ -897,11 +905,23 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                              \
             }                                                                                   \
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                  \
+        } else if ((NA_) == 3) {                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < 5; ++i_) {                                  \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                              \
+            }                                                                                   \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
         } else if ((NA_) == 2) {                                                                \
             _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                  \
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                              \
             }                                                                                   \
+        } else if ((NA_) == 1) {                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < 2; ++i_) {                                  \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                              \
+            }                                                                                   \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                  \
         }                                                                                       \
     } while (0)
 // One K stage from buffer (sAc, sBc) for NA_ row blocks; after the barrier
@@ -955,7 +975,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     gather_rows<8>(g, tr, w, lane, gsrc);
     auto make_src = [&](const TileRef& t) {
         if constexpr (BT) return dma_src_bt<8>(g, t, gsrc, w, lane, KT * kBK);
-        else return dma_src<DUAL, 8, KG>(g, t, gsrc, w, lane, KT * kBK);
+        else return dma_src<DUAL, 8, KG, QUEUE>(g, t, gsrc, w, lane, KT * kBK);
     };
     DmaSrc<4> cur = make_src(tr);
     bf16x8_t fa0[4], fb0[2], fa1[4], fb1[2];
@@ -993,10 +1013,16 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 #pragma unroll
                 for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-        // live row blocks of this wave: 4 (3 or 4 with rows), 2 (1 or 2) or 0
+        // live row blocks of this wave (32 rows each, from its first row): the
+        // K loop runs the MFMAs and fragment reads of those blocks only
+        // (one loop per count: with two counts, 2 and 4, the DeepSeek-V3
+        // gate/up GEMM ran 24 % more MFMA work than its rows, with one per
+        // count 11 %; layer -0.3 %, Mixtral prefill -0.5 %)
         const int blocks = min(4, max(0, (tr.nrows - wm * 128 + 31) >> 5));
-        if (blocks > 2) MOE_KLOOP(4);
-        else if (blocks > 0) MOE_KLOOP(2);
+        if (blocks == 4) MOE_KLOOP(4);
+        else if (blocks == 3) MOE_KLOOP(3);
+        else if (blocks == 2) MOE_KLOOP(2);
+        else if (blocks == 1) MOE_KLOOP(1);
         else MOE_KLOOP(0);
 
         // epilogue: the next tile's first two stages are in flight meanwhile
@@ -1409,6 +1435,18 @@ int choose_splitk_skinny(int64_t mt_expected, int N, int K) {
 
 hipError_t launch_grouped_gemm(const GemmGroup& g, bool dual, bool bf16, hipStream_t s) {
     if (g.M == 0) return hipSuccess;
+    if (g.B0_last) {
+        // a last group with weights of its own: the forward's persistent kernels
+        // with the tile queue only
+        const int64_t a_rows = g.gather ? ((int64_t)g.M + g.gather_div - 1) / g.gather_div : 0;
+        const bool persistent = bf16 && !g.skinny && !g.f32_out && !g.kgrouped && !g.C2 && g.splitk == 1 &&
+                                g.K % 128 == 0 && a_rows * g.K * 2 < (int64_t(1) << 32) && g.offsets &&
+                                g.queue && g.aligned_bands && !g.b_nmajor && g.G >= 2 && g.G <= 257 &&
+                                (dual ? (g.N % 128 == 0 && g.B1_last) : g.N % 256 == 0);
+        if (!persistent) return hipErrorInvalidValue;
+    } else if (g.G > 256) {
+        return hipErrorInvalidValue;
+    }
     if (g.C2) {
         // both products of the dual tile: the persistent kernel only
         const int64_t a_rows = g.gather ? ((int64_t)g.M + g.gather_div - 1) / g.gather_div : 0;

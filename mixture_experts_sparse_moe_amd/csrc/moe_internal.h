@@ -28,6 +28,12 @@ struct DispatchArgs {
     int cap = 0x7FFFFFFF;   // pairs kept per expert (the first ones); the rest get pair_pos -1
     int32_t* zero = nullptr;  // P > 0: nzero ints set to 0 on the way (the GEMMs' tile-queue counters)
     int nzero = 0;
+    // tail > 0 (no capacity; several chunks): one more group of `tail` rows
+    // after the experts' pairs, sorted_pairs[P + i] = i * tail_mul and
+    // offsets[E + 1] = P + tail (the shared expert's tokens as a group of the
+    // routed GEMMs)
+    int tail = 0;
+    int tail_mul = 1;
 };
 int dispatch_num_chunks(int P);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
@@ -109,6 +115,11 @@ struct GemmGroup {
     // rounds and take other XCDs' tiles once their own run out (nullptr: each
     // workgroup walks a fixed list)
     int* queue = nullptr;
+    // bf16 persistent kernel, forward mode, non-null: the last group (G - 1)
+    // takes its weights from B0_last [N, K] (and B1_last, dual) instead of
+    // B0 + (G - 1) N K
+    const void* B0_last = nullptr;
+    const void* B1_last = nullptr;
 };
 // Dual mode: C = silu(A B0^T) * (A B1^T).  Single: C = A B0^T, or with
 // splitk > 1 the partial products of the K ranges, C slice s = A[:, Ks] B0[:, Ks]^T.

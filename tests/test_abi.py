@@ -258,3 +258,27 @@ def test_noalloc_rejects_layers_past_its_array():
     assert L.moe_forward_noalloc(ctypes.byref(big), *([FAKE] * 13), None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_forward_noalloc(None, *([FAKE] * 13), None) == moe.MOE_ERR_NULL
     assert L.moe_forward_noalloc(ctypes.byref(cfg(k=9)), *([FAKE] * 13), None) == moe.MOE_ERR_SHAPE
+
+
+def test_forward_plan():
+    """moe_forward_plan (host only): DeepSeek-V3's shared expert, as wide as
+    its routed experts, runs inside the routed GEMMs; a narrower one, an fp32
+    layer, a capacity-free decode batch on 32-row tiles and a layer without a
+    shared expert do not."""
+    ds = moe.MoeConfig.of(8192, 7168, 256, 8, 2048, 1, 2048, moe.MOE_SCORE_SIGMOID)
+    assert moe.moe_forward_plan(ds) == dict(tile_rows=256, routed_splits=1, shared_splits=1,
+                                            shared_merged=True)
+    narrow = moe.MoeConfig.of(8192, 7168, 256, 8, 2048, 1, 1024, moe.MOE_SCORE_SIGMOID)
+    assert not moe.moe_forward_plan(narrow)["shared_merged"]
+    f32 = moe.MoeConfig.of(512, 256, 8, 2, 256, 1, 256, dtype=moe.MOE_F32)
+    assert not moe.moe_forward_plan(f32)["shared_merged"]
+    dec = moe.MoeConfig.of(8, 2048, 256, 8, 256, 1, 256, moe.MOE_SCORE_SIGMOID)
+    p = moe.moe_forward_plan(dec)
+    assert p["tile_rows"] == 32 and not p["shared_merged"]
+    mix = moe.MoeConfig.of(4096, 4096, 8, 2, 14336)
+    p = moe.moe_forward_plan(mix)
+    assert p["shared_splits"] == 0 and not p["shared_merged"] and p["routed_splits"] >= 1
+    L = moe.lib()
+    assert L.moe_forward_plan(ctypes.byref(ds), None) == moe.MOE_ERR_NULL
+    out = (ctypes.c_int32 * 4)()
+    assert L.moe_forward_plan(ctypes.byref(cfg(k=0)), out) == moe.MOE_ERR_SHAPE

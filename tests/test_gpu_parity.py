@@ -50,6 +50,12 @@ SMALL = {
     "bf16_decode_e100_k3": S("c", T=70, d=512, E=100, k=3, d_ff=320),
     "fp32_e32_k4_sigmoid_shared": S("c", T=130, d=128, E=32, k=4, d_ff=192, num_shared=1,
                                     d_ff_shared=128, score_fn=synth.SIGMOID, dtype=synth.F32),
+    # a shared expert as wide as the routed ones, about one M tile per
+    # expert: moe_forward runs it as one more group of the routed GEMMs
+    "bf16_e64_k6_sigmoid_shared_same_width": S("c", T=700, d=512, E=64, k=6, d_ff=256, num_shared=1,
+                                               d_ff_shared=256, score_fn=synth.SIGMOID),
+    "bf16_e32_k4_zipf_shared_same_width": S("c", T=900, d=768, E=32, k=4, d_ff=384, num_shared=1,
+                                            d_ff_shared=384, zipf_s=1.1),
 }
 
 
