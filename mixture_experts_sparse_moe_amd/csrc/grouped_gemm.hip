@@ -610,6 +610,37 @@ __device__ __forceinline__ bf16x8_t load_b_tr(const uint16_t* sB, int off) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// store_block_bf16 with every store issued: the block's rows go through a
+// buffer resource of rows_left rows (none if rows_left <= 0), whose bounds
+// check drops the stores of rows past the end.  A block thus issues exactly
+// four stores per lane, whatever its rows, so a later wait can leave a known
+// number of them in flight.
+__device__ __forceinline__ void store_block_bf16_all(uint16_t* Cb, int64_t ldc, int rows_left, const float* v,
+                                                     int lane) {
+    const int half = lane >> 5, r32 = lane & 31, j = r32 & 3;
+    const uint32_t sel = (j & 1) ? 0x03020706u : 0x05040100u;
+    const int recs = rows_left > 0 ? (int)((int64_t)rows_left * ldc * 2) : 0;
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc((void*)Cb, (short)0, recs, 0x00020000);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const uint32_t d0 = pack_bf16x2(v[4 * a + 0], v[4 * a + 1]);
+        const uint32_t d1 = pack_bf16x2(v[4 * a + 2], v[4 * a + 3]);
+        const uint32_t n0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d0, 0xB1, 0xF, 0xF, true);
+        const uint32_t n1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d1, 0xB1, 0xF, 0xF, true);
+        const uint32_t e0 = __builtin_amdgcn_perm(n0, d0, sel);
+        const uint32_t e1 = __builtin_amdgcn_perm(n1, d1, sel);
+        const uint32_t s = (j & 2) ? e0 : e1;
+        const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)s, 0x4E, 0xF, 0xF, true);
+        u32x2_t out;
+        out.x = (j & 2) ? r : e0;
+        out.y = (j & 2) ? e1 : r;
+        const int row = 8 * a + 4 * half + j;
+        __builtin_amdgcn_raw_buffer_store_b64(out, rc, (int)((row * ldc + (r32 - j)) * 2), 0, 0);
+    }
+}
+
 // Stores one 32 x 32 block of MFMA results as bf16.  Lane (half, r32) holds
 // column r32 of block rows 8 a + 4 half + b in v[4 a + b].  Inside each quad
 // of lanes a 4 x 4 transpose (two DPP exchanges and byte permutes) gives lane
@@ -789,6 +820,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     static_assert(MODE != kModeDualOut || DUAL, "two outputs need the dual tile");
     static_assert(!QUEUE || (MODE != kModeKgroup && MODE != kModeF32), "no tile queue in these modes");
     constexpr int STG = 256 * kBK;    // elements of one A or B stage (32 KB)
+    // A tile's first K-stage wait: with every epilogue store issued (forward
+    // dual mode: 4 per block, 4 blocks), vmcnt(kEpiStores) covers the stage
+    // DMA issued before them and leaves the stores in flight (vector memory
+    // operations complete in issue order for this counter).  Gate/up GEMMs
+    // -0.3 to -0.9 %; for the single GEMMs the stores of dead blocks cost more
+    // than the wait (DeepSeek-V3 down +0.8 %), so they keep skipping them.
+    constexpr bool kAllStores = MODE == kModeFwd && DUAL;
+    constexpr int kEpiStores = kAllStores ? 16 : 0;
+    constexpr int kWaitFirst = (7 << 4) | (kEpiStores & 15) | ((kEpiStores >> 4) << 14);
     // even M split for the gate/up tiles claimed through the queue (about one
     // M tile per expert)
     constexpr bool BAL = DUAL && QUEUE;
@@ -928,7 +968,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 // that buffer is refilled with stage kd_ of src_ (if fetch_) and the first
 // fragments of (sAn, sBn) are read for NN_ row blocks (at a tile boundary,
 // all 4: the next tile may have more live rows).
-#define MOE_STAGE(NA_, NN_, sAc, sBc, sAn, sBn, src_, kd_, fetch_)                              \
+#define MOE_STAGE_W(NA_, NN_, sAc, sBc, sAn, sBn, src_, kd_, fetch_, wait_)                     \
     do {                                                                                        \
         MOE_LOAD_FRAGS(sAc, sBc, 1, fa1, fb1, NA_);                                             \
         MOE_MFMAS(fa0, fb0, NA_);                                                               \
@@ -942,7 +982,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
         MOE_MFMAS(fa0, fb0, NA_);                                                               \
         MOE_INTERLEAVE(NA_);                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                      \
-        __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);                                              \
+        __builtin_amdgcn_s_waitcnt(wait_);                                                      \
         __builtin_amdgcn_s_barrier();                                                           \
         __builtin_amdgcn_sched_barrier(0);                                                      \
         if (fetch_) MOE_DMA(sAc, sBc, src_, kd_);                                               \
@@ -952,11 +992,21 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
         MOE_INTERLEAVE((NN_) < (NA_) ? (NN_) : (NA_));                                          \
         __builtin_amdgcn_sched_barrier(0);                                                      \
     } while (0)
-// The K stages of one tile for a wave with NA_ live row blocks.
+#define MOE_STAGE(NA_, NN_, sAc, sBc, sAn, sBn, src_, kd_, fetch_)                              \
+    MOE_STAGE_W(NA_, NN_, sAc, sBc, sAn, sBn, src_, kd_, fetch_, kWaitVm0Lgkm0)
+// The K stages of one tile for a wave with NA_ live row blocks.  The first
+// stage's wait leaves the previous tile's epilogue stores in flight (kWaitFirst).
 #define MOE_KLOOP(NA_)                                                                          \
     do {                                                                                        \
         const int kl_ = KG ? cur.kt : KT;                                                       \
-        for (int kt = 0; kt < kl_ - 2; kt += 2) {                                               \
+        if (kl_ > 2) {                                                                          \
+            MOE_STAGE_W(NA_, NA_, sA0, sB0, sA1, sB1, cur, 2, true, kWaitFirst);                \
+            gather_rows<8>(g, tn, w, lane, gsrc);                                               \
+            MOE_STAGE(NA_, NA_, sA1, sB1, sA0, sB0, cur, 3, true);                              \
+        } else {                                                                                \
+            gather_rows<8>(g, tn, w, lane, gsrc);                                               \
+        }                                                                                       \
+        for (int kt = 2; kt < kl_ - 2; kt += 2) {                                               \
             MOE_STAGE(NA_, NA_, sA0, sB0, sA1, sB1, cur, kt + 2, true);                         \
             MOE_STAGE(NA_, NA_, sA1, sB1, sA0, sB0, cur, kt + 3, true);                         \
         }                                                                                       \
@@ -1000,9 +1050,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
             more = Ln < Lend;
         }
         const TileRef tn = tile_of(more ? Ln : L);
-        // the next tile's gathered rows load now; their values are used after
-        // the K loop, whose stage waits have long covered them
-        gather_rows<8>(g, tn, w, lane, gsrc);
+        // the next tile's gathered rows load after the K loop's first stage
+        // (behind the previous epilogue's stores and that stage's wait); their
+        // values are used at the end of the K loop
         DmaSrc<4> nxt;
 
         f32x16_t acc[4][2];
@@ -1025,11 +1075,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
         else if (blocks == 1) MOE_KLOOP(1);
         else MOE_KLOOP(0);
 
-        // epilogue: the next tile's first two stages are in flight meanwhile
+        // epilogue: the next tile's first two stages are in flight meanwhile.
+        // kAllStores: every store is issued (kEpiStores per lane; those of rows
+        // past the tile's end are dropped by their bounds), so the next tile's
+        // first wait leaves them in flight instead of waiting for all of them.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rb = wm * 128 + i * 32;
-            if (rb >= tr.nrows) break;
+            if (!kAllStores && rb >= tr.nrows) break;
 #pragma unroll
             for (int bo = 0; bo < (DUAL ? 1 : 2); ++bo) {
                 const int cb = DUAL ? wn * 32 : wn * 64 + bo * 32;
@@ -1047,8 +1100,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 #pragma unroll
                     for (int q = 0; q < 16; ++q)
                         v[q] = DUAL ? silu_f32(acc[i][0][q]) * acc[i][1][q] : acc[i][bo][q];
-                    store_block_bf16(C + tr.ks * g.part_stride + (int64_t)(tr.row0 + rb) * g.N + tr.n0 + cb, g.N,
-                                     tr.nrows - rb, v, lane);
+                    uint16_t* Cb = C + tr.ks * g.part_stride + (int64_t)(tr.row0 + rb) * g.N + tr.n0 + cb;
+                    if constexpr (kAllStores) store_block_bf16_all(Cb, g.N, tr.nrows - rb, v, lane);
+                    else store_block_bf16(Cb, g.N, tr.nrows - rb, v, lane);
                 } else {
                     float* Cf = static_cast<float*>(g.C) +
                                 (KG ? (int64_t)tr.grp * g.c_gstride : (int64_t)tr.ks * g.part_stride) +
@@ -1067,6 +1121,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 #undef MOE_MFMAS
 #undef MOE_INTERLEAVE
 #undef MOE_STAGE
+#undef MOE_STAGE_W
 #undef MOE_KLOOP
 }
 
