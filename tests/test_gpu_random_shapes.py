@@ -62,6 +62,40 @@ def test_random_shape_forward(name):
     check_layer(sh, synth.make_inputs(sh, 31))
 
 
+def random_merged_shapes(n=6, seed=7):
+    """bf16 layers whose shared expert moe_forward runs inside the routed
+    GEMMs: as wide as the routed experts, about one M tile per expert (the
+    tile queue), more than one dispatch chunk of pairs, d a multiple of 256."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        E = int(rng.choice([16, 32, 64, 100, 256]))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        d = 256 * int(rng.integers(1, 4))
+        d_ff = 128 * int(rng.integers(1, 5))
+        T = int(rng.integers(200, 1500))
+        P = T * k
+        if not (P > 2048 and P < 640 * E and P > 32 * E):
+            continue
+        score = synth.SIGMOID if rng.random() < 0.5 else synth.SOFTMAX
+        zipf = 1.1 if (rng.random() < 0.3 and E <= d) else 0.0
+        out.append(S(f"m{len(out):02d}", T=T, d=d, E=E, k=k, d_ff=d_ff, num_shared=1, d_ff_shared=d_ff,
+                     score_fn=score, zipf_s=zipf))
+    return out
+
+
+MERGED = {sh.name: sh for sh in random_merged_shapes()}
+
+
+@pytest.mark.parametrize("name", sorted(MERGED))
+def test_random_shape_forward_shared_merged(name):
+    import mixture_experts_sparse_moe_amd as moe
+    from gpu_harness import cfg_of
+    sh = MERGED[name]
+    assert moe.moe_forward_plan(cfg_of(sh))["shared_merged"], "the shape must take the merged path"
+    check_layer(sh, synth.make_inputs(sh, 43))
+
+
 # the oracle's chain rule costs about 12 d d_ff fp64 multiply-adds per pair
 BACKWARD = sorted(n for n, sh in SHAPES.items() if sh.T * sh.k * sh.d * sh.d_ff <= 2.5e8)
 
