@@ -250,15 +250,28 @@ def backward_cost(torch, moe, cfg, d, sh, stream, steps: int) -> dict:
 
 def practical_ceilings(torch, dev) -> dict:
     """Measured ceilings on the same GPU, next to the nominal peaks: a 1 GiB
-    device copy (read + write bytes / time) and one bf16 4096 x 14336 x 4096
-    torch.matmul (a library yardstick only; nothing of the layer uses it)."""
+    device copy (read + write bytes / time), a 4 GiB streaming read (torch row
+    sums of an fp32 [2^18, 4096] tensor: read bytes / time, the writes are
+    0.02 %), and one bf16 4096 x 14336 x 4096 torch.matmul (a library
+    yardstick only; nothing of the layer uses any of them)."""
     out = {}
+    big = torch.empty(READ_BYTES // 4, dtype=torch.float32, device=dev).uniform_().view(-1, 4096)
+    for _ in range(3):
+        r = big.sum(dim=1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        r = big.sum(dim=1)
+    e1.record()
+    e1.synchronize()
+    out["read_gbs"] = READ_BYTES * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del big, r
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(10):
         dst.copy_(src)
@@ -322,6 +335,7 @@ def parity_of(y_gpu: np.ndarray, ids_gpu: np.ndarray, ref, dtype: str) -> dict:
 
 
 COPY_BYTES = 1 << 30
+READ_BYTES = 4 << 30        # streaming-read ceiling
 
 
 def copy_calibration():
