@@ -34,6 +34,10 @@ FORWARD = {
     # persistent 256 x 256 GEMMs with a K-split down projection, shared expert
     "prefill_e8_k2_shared": S("g", T=1024, d=512, E=8, k=2, d_ff=1024, num_shared=1, d_ff_shared=512),
     "prefill_e32_k4_sigmoid": S("g", T=512, d=256, E=32, k=4, d_ff=256, score_fn=synth.SIGMOID),
+    # tile queue, shared expert as wide as the routed ones: it runs as one more
+    # group of the routed GEMMs (the dispatch writes its rows on every replay)
+    "prefill_e32_k4_shared_in_routed": S("g", T=1024, d=512, E=32, k=4, d_ff=512, num_shared=1,
+                                         d_ff_shared=512, score_fn=synth.SIGMOID),
 }
 
 
