@@ -1,10 +1,11 @@
 """moe_forward_noalloc, the forward for callers that cannot allocate (its
 workspace is the library's fixed per-GPU device array), against moe_forward
-with a workspace the caller allocated: three calls in a row on the same
-array, each smaller than the one before (a prefill-sized layer whose GEMMs
-claim tiles through counters kept in the array, a decode-sized layer on the
-32-row kernels with the router's fused dispatch, a five-token layer), every
-output bitwise equal to moe_forward's (same kernels, same launches)."""
+with a workspace the caller allocated: four calls in a row on the same
+array, each smaller than the one before (a layer whose shared expert runs
+inside the routed GEMMs, a prefill-sized layer whose GEMMs claim tiles
+through counters kept in the array, a decode-sized layer on the 32-row
+kernels with the router's fused dispatch, a five-token layer), every output
+bitwise equal to moe_forward's (same kernels, same launches)."""
 import sys
 
 import numpy as np
@@ -17,6 +18,7 @@ pytestmark = pytest.mark.gpu
 S = synth.LayerShape
 
 CASES = [
+    S("n0", T=1024, d=512, E=32, k=4, d_ff=512, num_shared=1, d_ff_shared=512, score_fn=synth.SIGMOID),
     S("n1", T=600, d=256, E=8, k=2, d_ff=384, router_scale=4.0),
     S("n2", T=48, d=1024, E=16, k=4, d_ff=512, num_shared=1, d_ff_shared=256, score_fn=synth.SIGMOID),
     S("n3", T=5, d=512, E=8, k=2, d_ff=256),
@@ -39,6 +41,9 @@ def test_noalloc_forward_equals_forward_with_workspace():
     layers = [DeviceLayer(sh, synth.make_inputs(sh, 50 + i)) for i, sh in enumerate(CASES)]
     for L in layers:
         assert moe.moe_workspace_bytes(L.cfg) <= moe.NOALLOC_SCRATCH_BYTES
+    assert moe.moe_forward_plan(layers[0].cfg)["shared_merged"]
+    sizes = [moe.moe_workspace_bytes(L.cfg) for L in layers]
+    assert sizes == sorted(sizes, reverse=True)
     got, want = [], []
     for L in layers:
         print(f"[case] noalloc {L.sh}", file=sys.stderr, flush=True)
@@ -65,8 +70,8 @@ def test_noalloc_forward_equals_forward_with_workspace():
     L = layers[0]
     o = _outputs(L, t)
     dv = L.d
-    moe.moe_forward_noalloc(L.cfg, dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], None, None,
-                            None, o["y"], o["ids"], o["wts"], o["counts"], o["gap"])
+    moe.moe_forward_noalloc(L.cfg, dv["x"], dv["w_router"], dv["w_gate"], dv["w_up"], dv["w_down"], dv["ws_gate"],
+                            dv["ws_up"], dv["ws_down"], o["y"], o["ids"], o["wts"], o["counts"], o["gap"])
     t.cuda.synchronize()
     for n in ("y", "ids", "wts", "counts", "gap"):
         np.testing.assert_array_equal(to_host(o[n]), to_host(want[0][n]), err_msg=f"again {n}")
