@@ -282,3 +282,24 @@ def test_forward_plan():
     assert L.moe_forward_plan(ctypes.byref(ds), None) == moe.MOE_ERR_NULL
     out = (ctypes.c_int32 * 4)()
     assert L.moe_forward_plan(ctypes.byref(cfg(k=0)), out) == moe.MOE_ERR_SHAPE
+
+
+def test_forward_plan_shared_placement_boundaries():
+    """Where moe_forward_plan puts a same-width shared expert (host only):
+    inside the routed GEMMs only with the tile queue (fewer than 640 pairs per
+    expert), more than one dispatch chunk (over 2048 pairs), 256-row tiles
+    (over 32 pairs per expert), d a multiple of 256 and d_ff of 128, bf16."""
+    def plan(T, d, E, k, f, fs=None, dtype=moe.MOE_BF16):
+        c = moe.MoeConfig.of(T, d, E, k, f, 1, f if fs is None else fs, moe.MOE_SCORE_SIGMOID, dtype=dtype)
+        return moe.moe_forward_plan(c)["shared_merged"]
+
+    assert plan(1024, 512, 32, 4, 512)                    # 4096 pairs, 128 per expert
+    assert not plan(1024, 512, 32, 4, 512, fs=256)        # narrower shared expert
+    assert not plan(1024, 512, 32, 4, 512, dtype=moe.MOE_F32)
+    assert not plan(1024, 384, 32, 4, 512)                # d not a multiple of 256
+    assert not plan(1024, 512, 32, 4, 448)                # d_ff not a multiple of 128
+    assert not plan(512, 512, 32, 4, 512)                 # 2048 pairs: one dispatch chunk
+    assert plan(513, 512, 32, 4, 512)                     # 2052 pairs: two chunks
+    assert not plan(5120, 512, 8, 1, 512)                 # 640 pairs per expert: fixed schedule
+    assert plan(5119, 512, 8, 1, 512)
+    assert not plan(2100, 512, 256, 1, 512)               # 8 pairs per expert: 32-row kernels
