@@ -357,8 +357,10 @@ int moe_capacity(const moe_config* cfg, double capacity_factor);
  * How moe_forward (no capacity) lays the layer out on kernels, for reading
  * its per-stage times and kernel traces ("T2.6 -- What Mixture of Experts
  * Changes", In practice: profile each stage).  plan_out [4] int32, host:
- *   [0] rows per tile of the routed expert GEMMs (256, or 32 for few pairs;
- *       fp32 layers report 256 and use a plain tiled kernel),
+ *   [0] rows per tile of the routed expert GEMMs: 256; 288 when the experts
+ *       hold 224 to 287 rows on average with the tile queue (fewer than 640
+ *       rows per expert), so that experts of 257..288 rows are one tile; 32
+ *       for few pairs (fp32 layers report 256 and use a plain tiled kernel),
  *   [1] K splits of the routed down GEMM (1 = none),
  *   [2] K splits of the shared down GEMM (0 when num_shared == 0),
  *   [3] 1 when the shared expert runs inside the routed GEMMs' launches

@@ -1125,6 +1125,286 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 #undef MOE_KLOOP
 }
 
+// Tall tiles for layers with about one M tile per expert (the tile-queue
+// regime): 288 rows x 256 B rows on 12 waves, for the forward's routed
+// GEMMs (and the shared expert as their last group).  With 256-row tiles an
+// expert of 257..288 rows takes two tiles of about 140 rows, and such a tile
+// costs 85 % of a full one (it streams the whole weight panel through the DMA
+// path for half the rows); with 288-row tiles nearly every expert of a
+// DeepSeek-V3-sized layer (about 256 rows each) is one tile.
+// Waves form a 3 x 4 grid: wave (wm, wn) owns rows 96 wm .. 96 wm + 95 (three
+// 32-row blocks) and the same two 32-row blocks of B as in the 256-row kernel,
+// so 96 fp32 accumulators per lane, within the 168 registers that three waves
+// per SIMD leave.  Per K stage each wave issues three A and three B DMA
+// instructions of 8 rows: A blocks 3 w .. 3 w + 2 (36 blocks = 288 rows), B
+// blocks 3 w .. 3 w + 2, of which blocks 32..35 are spare (their lanes issue
+// no request, through the bounds check of their buffer resource) and land
+// in LDS rows 256..287 of the B buffer, which no fragment reads.  The K stage
+// loop, the stream of stages across tiles, the tile order (expert-aligned
+// bands), the queue and the epilogue are those of the 256-row kernel.
+struct TallSrc {
+    const char* a;      // A: the start of A (gathered rows) or of the tile's rows
+    const char* b0;     // B panel: gate rows (dual) or the weight rows
+    const char* b1;     // dual: the up rows of the same columns
+    uint32_t ao[3];     // A offsets of this lane's three instructions (kDeadOff: row past the end)
+    int rot;            // first K stage of the walk
+};
+
+template <bool DUAL>
+__global__ __launch_bounds__(768, 1) void gemm_bf16_tall_kernel(GemmGroup g, int tiles_n) {
+    constexpr int NB = 3;                  // 32-row blocks per wave
+    constexpr int BM = 3 * NB * 32;        // 288
+    constexpr int BN = DUAL ? 128 : 256;   // output columns of a tile
+    constexpr int STG = BM * kBK;          // elements of one A or B stage buffer (36 KB)
+    constexpr bool BAL = DUAL;             // even M split for the gate/up tiles
+    constexpr int kEpiStores = DUAL ? 4 * NB : 0;
+    constexpr int kWaitFirst = (7 << 4) | (kEpiStores & 15) | ((kEpiStores >> 4) << 14);
+    __shared__ __align__(16) uint16_t sA0[STG], sA1[STG];
+    __shared__ __align__(16) uint16_t sB0[STG], sB1[STG];
+    __shared__ int s_tb[258], s_off[258];
+    __shared__ int s_wsum[12];
+    __shared__ int s_next[2];
+    __shared__ TileQueue s_tq;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = w >> 2, wn = w & 3;
+    const int KT = g.K / kBK;
+
+    const int G = tile_prefix<BM>(g, s_tb, s_off, s_wsum);
+    const int mt_total = s_tb[G];
+    const int TL = mt_total * tiles_n;
+    const int nslot = gridDim.x >> 3;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per = ((TL + 7) / 8 + nslot - 1) / nslot * nslot;
+    const int Lend = min(TL, (xcd + 1) * per);
+    const int wn_win = max(nslot / kWMW, 1);
+    int L = xcd * per + slot;
+    if (L >= Lend) return;
+    int claim = -1;
+    if (tid == 0) {
+        s_tq = TileQueue{g.queue, per, TL, nslot, xcd, xcd * per + 3 * nslot, Lend};
+        s_next[0] = L + nslot < Lend ? L + nslot : -1;
+        s_next[1] = s_next[0] >= 0 && L + 2 * nslot < Lend ? L + 2 * nslot : -1;
+    }
+
+    const int half = lane >> 5, r32 = lane & 31;
+    int a_row[NB], b_row[2];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) a_row[i] = wm * (NB * 32) + i * 32 + r32;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) b_row[b] = DUAL ? b * 128 + wn * 32 + r32 : wn * 64 + b * 32 + r32;
+
+    // B offsets of this lane's three instructions: the same for every tile
+    const uint32_t K2 = (uint32_t)g.K * 2;
+    uint32_t bo[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int r = (3 * w + j) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
+        bo[j] = r >= 256 ? kDeadOff : (uint32_t)(DUAL ? (r & 127) : r) * K2 + c * 16;
+    }
+    // gathered pair ids of this lane's A rows (rows past the end repeat the last)
+    auto gather = [&](const TileRef& t, int* src) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int r = min((3 * w + j) * 8 + (lane >> 3), t.nrows - 1);
+            src[j] = g.gather ? g.gather[t.row0 + r] : r;
+        }
+    };
+    auto make_src = [&](const TileRef& t, const int* src) {
+        TallSrc s;
+        s.rot = __builtin_amdgcn_readfirstlane((t.n0 / BN + 17 * t.grp) % KT);
+        s.a = static_cast<const char*>(g.A) + (g.gather ? 0 : (int64_t)t.row0 * K2);
+        const bool own = g.B0_last != nullptr && t.grp == g.G - 1;
+        const int64_t pan = ((int64_t)(own ? 0 : t.grp) * g.N + t.n0) * K2;
+        s.b0 = static_cast<const char*>(own ? g.B0_last : g.B0) + pan;
+        s.b1 = DUAL ? static_cast<const char*>(own ? g.B1_last : g.B1) + pan : s.b0;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int r = (3 * w + j) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ swz(r);
+            const int arow = g.gather ? src[j] / g.gather_div : src[j];
+            s.ao[j] = r >= t.nrows ? kDeadOff : (uint32_t)arow * K2 + c * 16;
+        }
+        return s;
+    };
+
+// Refill of a stage buffer: three A and three B instructions per wave, all
+// through bounds-checked buffer resources, unconditionally.
+#define TALL_DMA(sA_, sB_, src_, kt_)                                                           \
+    do {                                                                                        \
+        const int kr_ = (kt_) + (src_).rot;                                                     \
+        const uint32_t ko_ = (uint32_t)(kr_ >= KT ? kr_ - KT : kr_) * (kBK * 2u);               \
+        const __amdgpu_buffer_rsrc_t ra_ =                                                      \
+            __builtin_amdgcn_make_buffer_rsrc((void*)(src_).a, (short)0, (int)kDeadOff, 0x00020000); \
+        _Pragma("unroll") for (int j = 0; j < 3; ++j)                                           \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(                                           \
+                ra_, (lds_ptr_t)((sA_) + (3 * w + j) * 8 * kBK), 16,                            \
+                (int)__builtin_elementwise_add_sat((src_).ao[j], ko_), 0, 0, 0);                \
+        _Pragma("unroll") for (int j = 0; j < 3; ++j) {                                         \
+            const char* bp_ = DUAL && 3 * w + j >= 16 ? (src_).b1 : (src_).b0;                  \
+            const __amdgpu_buffer_rsrc_t rb_ =                                                  \
+                __builtin_amdgcn_make_buffer_rsrc((void*)bp_, (short)0, (int)kDeadOff, 0x00020000); \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(                                           \
+                rb_, (lds_ptr_t)((sB_) + (3 * w + j) * 8 * kBK), 16,                            \
+                (int)__builtin_elementwise_add_sat(bo[j], ko_), 0, 0, 0);                       \
+        }                                                                                       \
+    } while (0)
+#define TALL_FRAGS(sA_, sB_, s_, af_, bf_, NA_)                                                 \
+    do {                                                                                        \
+        const int c_ = 2 * (s_) + half;                                                         \
+        _Pragma("unroll") for (int i = 0; i < (NA_); ++i) af_[i] = as_bf16x8(                   \
+            *reinterpret_cast<const uint4*>((sA_) + a_row[i] * kBK + ((c_ ^ swz(a_row[i])) * 8))); \
+        _Pragma("unroll") for (int b = 0; b < ((NA_) ? 2 : 0); ++b) bf_[b] = as_bf16x8(         \
+            *reinterpret_cast<const uint4*>((sB_) + b_row[b] * kBK + ((c_ ^ swz(b_row[b])) * 8))); \
+    } while (0)
+#define TALL_MFMAS(af_, bf_, NA_)                                                               \
+    do {                                                                                        \
+        _Pragma("unroll") for (int i = 0; i < (NA_); ++i)                                       \
+            _Pragma("unroll") for (int b = 0; b < 2; ++b) acc[i][b] =                           \
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(af_[i], bf_[b], acc[i][b], 0, 0, 0);    \
+    } while (0)
+// MFMAs of a step with the next step's fragment reads between them
+#define TALL_INTERLEAVE(NA_)                                                                    \
+    do {                                                                                        \
+        if ((NA_) == 3) {                                                                       \
+            _Pragma("unroll") for (int i_ = 0; i_ < 5; ++i_) {                                  \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                              \
+            }                                                                                   \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                  \
+        } else if ((NA_) == 2) {                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                                  \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                              \
+            }                                                                                   \
+        } else if ((NA_) == 1) {                                                                \
+            _Pragma("unroll") for (int i_ = 0; i_ < 2; ++i_) {                                  \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              \
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                              \
+            }                                                                                   \
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                  \
+        }                                                                                       \
+    } while (0)
+#define TALL_STAGE_W(NA_, NN_, sAc, sBc, sAn, sBn, src_, kd_, fetch_, wait_)                    \
+    do {                                                                                        \
+        TALL_FRAGS(sAc, sBc, 1, fa1, fb1, NA_);                                                 \
+        TALL_MFMAS(fa0, fb0, NA_);                                                              \
+        TALL_INTERLEAVE(NA_);                                                                   \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        TALL_FRAGS(sAc, sBc, 2, fa0, fb0, NA_);                                                 \
+        TALL_MFMAS(fa1, fb1, NA_);                                                              \
+        TALL_INTERLEAVE(NA_);                                                                   \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        TALL_FRAGS(sAc, sBc, 3, fa1, fb1, NA_);                                                 \
+        TALL_MFMAS(fa0, fb0, NA_);                                                              \
+        TALL_INTERLEAVE(NA_);                                                                   \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        __builtin_amdgcn_s_waitcnt(wait_);                                                      \
+        __builtin_amdgcn_s_barrier();                                                           \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        if (fetch_) TALL_DMA(sAc, sBc, src_, kd_);                                              \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        TALL_FRAGS(sAn, sBn, 0, fa0, fb0, NN_);                                                 \
+        TALL_MFMAS(fa1, fb1, NA_);                                                              \
+        TALL_INTERLEAVE((NN_) < (NA_) ? (NN_) : (NA_));                                         \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+    } while (0)
+#define TALL_STAGE(NA_, NN_, sAc, sBc, sAn, sBn, src_, kd_, fetch_)                             \
+    TALL_STAGE_W(NA_, NN_, sAc, sBc, sAn, sBn, src_, kd_, fetch_, kWaitVm0Lgkm0)
+#define TALL_KLOOP(NA_)                                                                         \
+    do {                                                                                        \
+        if (KT > 2) {                                                                           \
+            TALL_STAGE_W(NA_, NA_, sA0, sB0, sA1, sB1, cur, 2, true, kWaitFirst);               \
+            gather(tn, gsrc);                                                                   \
+            TALL_STAGE(NA_, NA_, sA1, sB1, sA0, sB0, cur, 3, true);                             \
+        } else {                                                                                \
+            gather(tn, gsrc);                                                                   \
+        }                                                                                       \
+        for (int kt = 2; kt < KT - 2; kt += 2) {                                                \
+            TALL_STAGE(NA_, NA_, sA0, sB0, sA1, sB1, cur, kt + 2, true);                        \
+            TALL_STAGE(NA_, NA_, sA1, sB1, sA0, sB0, cur, kt + 3, true);                        \
+        }                                                                                       \
+        nxt = make_src(tn, gsrc);                                                               \
+        TALL_STAGE(NA_, NA_, sA0, sB0, sA1, sB1, nxt, 0, more);                                 \
+        TALL_STAGE(NA_, 0, sA1, sB1, sA0, sB0, nxt, 1, more);                                   \
+    } while (0)
+
+    auto tile_of = [&](int Lt) {
+        return split_tile_at<BM, BN, true, BAL>(s_tb, s_off, G, mt_total, tiles_n, wn_win, Lt);
+    };
+    TileRef tr = tile_of(L);
+    int gsrc[3];
+    gather(tr, gsrc);
+    TallSrc cur = make_src(tr, gsrc);
+    bf16x8_t fa0[NB], fb0[2], fa1[NB], fb1[2];
+    TALL_DMA(sA0, sB0, cur, 0);
+    TALL_DMA(sA1, sB1, cur, 1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    TALL_FRAGS(sA0, sB0, 0, fa0, fb0, NB);
+
+    uint16_t* C = static_cast<uint16_t*>(g.C);
+    for (int it = 0;; ++it) {
+        const int Ln = __builtin_amdgcn_readfirstlane(s_next[it & 1]);
+        const bool more = Ln >= 0;
+        if (tid == 0) claim = next_tile_step(s_tq, s_next, it, claim);
+        const TileRef tn = tile_of(more ? Ln : L);
+        TallSrc nxt;
+
+        f32x16_t acc[NB][2];
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+        // live row blocks of this wave; a wave with one runs the two-block loop
+        // (a third K loop variant made the compiler spill 90 registers per lane
+        // around the loops)
+        const int blocks = min(NB, max(0, (tr.nrows - wm * (NB * 32) + 31) >> 5));
+        if (blocks == 3) TALL_KLOOP(3);
+        else if (blocks > 0) TALL_KLOOP(2);
+        else TALL_KLOOP(0);
+
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int rb = wm * (NB * 32) + i * 32;
+            if (!DUAL && rb >= tr.nrows) break;
+#pragma unroll
+            for (int bo_ = 0; bo_ < (DUAL ? 1 : 2); ++bo_) {
+                const int cb = DUAL ? wn * 32 : wn * 64 + bo_ * 32;
+                float v[16];
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    v[q] = DUAL ? silu_f32(acc[i][0][q]) * acc[i][1][q] : acc[i][bo_][q];
+                // buffer stores (32-bit offsets from a scalar base): the rows past
+                // the end are dropped by the bounds check
+                store_block_bf16_all(C + (int64_t)(tr.row0 + rb) * g.N + tr.n0 + cb, g.N, tr.nrows - rb, v,
+                                     lane);
+            }
+        }
+        if (!more) break;
+        // the next tile's first fragments (its stage 0 landed before the last
+        // barrier): read after the epilogue, so that they do not hold registers
+        // through it
+        TALL_FRAGS(sA0, sB0, 0, fa0, fb0, NB);
+        L = Ln;
+        tr = tn;
+        cur = nxt;
+    }
+#undef TALL_DMA
+#undef TALL_FRAGS
+#undef TALL_MFMAS
+#undef TALL_INTERLEAVE
+#undef TALL_STAGE
+#undef TALL_STAGE_W
+#undef TALL_KLOOP
+}
+
 // Few rows per group (decode): the weights are the stream and the MFMA work
 // is small, so the tile is 32 rows of one group x NBLK blocks of 32 weight
 // rows (dual: NBLK / 2 gate blocks and the same up blocks, so a tile yields
@@ -1346,6 +1626,13 @@ hipError_t launch_bf16_persistent(const GemmGroup& g, hipStream_t s) {
     // one instantiation per tile order: a runtime choice inside the kernel
     // costs the K loop a compiler-inserted wait on the loads in flight
     const dim3 grid(persistent_grid()), block(512);
+    if (g.tall) {
+        // 288-row tiles on 12 waves: the tile queue and the expert-aligned order only
+        if (!g.queue || !g.aligned_bands || g.splitk != 1) return hipErrorInvalidValue;
+        hipExtLaunchKernelGGL((gemm_bf16_tall_kernel<DUAL>), grid, dim3(768), 0, s, g.t_start, g.t_stop, 0, g,
+                              g.N / BN);
+        return hipGetLastError();
+    }
     if (g.queue) {
         if (g.aligned_bands)
             hipExtLaunchKernelGGL((gemm_bf16_persistent_kernel<DUAL, true, kModeFwd, true>), grid, block, 0, s,

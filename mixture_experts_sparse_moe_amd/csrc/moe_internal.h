@@ -120,6 +120,9 @@ struct GemmGroup {
     // B0 + (G - 1) N K
     const void* B0_last = nullptr;
     const void* B1_last = nullptr;
+    // bf16 persistent kernel, forward mode with the tile queue and the
+    // expert-aligned order: 288-row tiles on 12 waves instead of 256-row ones
+    bool tall = false;
 };
 // Dual mode: C = silu(A B0^T) * (A B1^T).  Single: C = A B0^T, or with
 // splitk > 1 the partial products of the K ranges, C slice s = A[:, Ks] B0[:, Ks]^T.

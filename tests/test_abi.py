@@ -266,7 +266,7 @@ def test_forward_plan():
     layer, a capacity-free decode batch on 32-row tiles and a layer without a
     shared expert do not."""
     ds = moe.MoeConfig.of(8192, 7168, 256, 8, 2048, 1, 2048, moe.MOE_SCORE_SIGMOID)
-    assert moe.moe_forward_plan(ds) == dict(tile_rows=256, routed_splits=1, shared_splits=1,
+    assert moe.moe_forward_plan(ds) == dict(tile_rows=288, routed_splits=1, shared_splits=1,
                                             shared_merged=True)
     narrow = moe.MoeConfig.of(8192, 7168, 256, 8, 2048, 1, 1024, moe.MOE_SCORE_SIGMOID)
     assert not moe.moe_forward_plan(narrow)["shared_merged"]
@@ -282,6 +282,27 @@ def test_forward_plan():
     assert L.moe_forward_plan(ctypes.byref(ds), None) == moe.MOE_ERR_NULL
     out = (ctypes.c_int32 * 4)()
     assert L.moe_forward_plan(ctypes.byref(cfg(k=0)), out) == moe.MOE_ERR_SHAPE
+
+
+def test_forward_plan_tile_rows_boundaries():
+    """Rows per tile of the routed GEMMs (host only): 288 exactly when the
+    experts hold 224 to 287 rows on average and the tile queue runs (bf16,
+    over 32 and under 640 rows per expert), else 256 (32 for few rows)."""
+    def rows(T, k, E, dtype=moe.MOE_BF16):
+        c = moe.MoeConfig.of(T, 512, E, k, 512, 0, 0, moe.MOE_SCORE_SIGMOID, dtype=dtype)
+        return moe.moe_forward_plan(c)["tile_rows"]
+
+    assert rows(8192, 8, 256) == 288                      # 256 rows per expert
+    assert rows(7168, 8, 256) == 288                      # 224: the lower end
+    assert rows(7167, 8, 256) == 256                      # just under 224
+    assert rows(9215, 8, 256) == 288                      # 287.97
+    assert rows(9216, 8, 256) == 256                      # 288: the upper end is open
+    assert rows(8192, 8, 256, moe.MOE_F32) == 256
+    assert rows(1024, 2, 8) == 288                        # 256 per expert, 8 experts
+    assert rows(900, 2, 8) == 288                         # 225 per expert
+    assert rows(2048, 2, 8) == 256                        # 512 per expert (tile queue, two tiles)
+    assert rows(4096, 2, 8) == 256                        # 1024 per expert (no tile queue)
+    assert rows(32, 8, 256) == 32                         # decode
 
 
 def test_forward_plan_shared_placement_boundaries():

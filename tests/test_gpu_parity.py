@@ -56,6 +56,13 @@ SMALL = {
                                                d_ff_shared=256, score_fn=synth.SIGMOID),
     "bf16_e32_k4_zipf_shared_same_width": S("c", T=900, d=768, E=32, k=4, d_ff=384, num_shared=1,
                                             d_ff_shared=384, zipf_s=1.1),
+    # 224 to 287 rows per expert on average: 288-row tiles on 12 waves (an
+    # expert of 257..288 rows is one tile), with the shared expert inside the
+    # routed GEMMs, on its own, and with skewed routing
+    "bf16_e32_k8_sigmoid_shared_same_width_tall": S("c", T=1024, d=512, E=32, k=8, d_ff=256, num_shared=1,
+                                                    d_ff_shared=256, score_fn=synth.SIGMOID),
+    "bf16_e16_k4_shared_tall": S("c", T=1000, d=256, E=16, k=4, d_ff=384, num_shared=1, d_ff_shared=128),
+    "bf16_e32_k8_zipf_tall": S("c", T=1024, d=256, E=32, k=8, d_ff=256, zipf_s=1.1),
 }
 
 
@@ -72,20 +79,22 @@ def need_gpu():
     moe.lib()   # raises if the library is missing
 
 
-def tile_edge_rows(offsets: np.ndarray, bm: int = 256) -> np.ndarray:
+def tile_edge_rows(offsets: np.ndarray, bms=(256, 288)) -> np.ndarray:
     """First and last grouped row of every M tile of every expert, for both
-    ways the GEMMs cut an expert's n rows into m = ceil(n / bm) tiles: full
-    tiles of bm rows and a short last one, or m tiles of ceil(n / m) rows."""
+    tile heights bm of the persistent GEMMs and both ways they cut an
+    expert's n rows into m = ceil(n / bm) tiles: full tiles of bm rows and a
+    short last one, or m tiles of ceil(n / m) rows."""
     rows = []
     for e in range(offsets.size - 1):
         a, b = int(offsets[e]), int(offsets[e + 1])
         n = b - a
         if n == 0:
             continue
-        m = -(-n // bm)
-        for h in (bm, -(-n // m)):
-            for r0 in range(a, b, h):
-                rows += [r0, min(r0 + h, b) - 1]
+        for bm in bms:
+            m = -(-n // bm)
+            for h in (bm, -(-n // m)):
+                for r0 in range(a, b, h):
+                    rows += [r0, min(r0 + h, b) - 1]
     return np.unique(np.array(rows, dtype=np.int64))
 
 
@@ -178,8 +187,8 @@ FULL = ["mixtral_decode", "mixtral_prefill", "hunyuan_a13b", "deepseek_v3"]
 def test_full_size_layer(name):
     """The full-size layer shapes: every routing and dispatch output; the
     expert outputs of the first and last grouped row of every (expert,
-    256-row M tile) (decode: every row); y on those rows' tokens plus the
-    first, the last and 22 seeded random tokens."""
+    256- or 288-row M tile) (decode: every row); y on those rows' tokens plus
+    the first, the last and 22 seeded random tokens."""
     sh = synth.SHAPES[name]
     say(f"[gen] {name}")
     inp = synth.make_inputs(sh, 0)
@@ -309,4 +318,50 @@ def test_nearly_empty_tiles_through_the_tile_queue():
         rows = offsets[e] + np.array(local)
         _, want = oracle.expert_rows(e, inp["x"], pairs[rows] // sh.k, inp["w_gate"], inp["w_up"], inp["w_down"])
         worst = max(worst, assert_close(synth.bf16_to_f64(first[rows]), want, TAU[sh.dtype], f"expert {e}"))
+    say(f"[ok] worst max|err|/max|ref| = {worst:.2e}")
+
+
+def test_tall_tiles_live_block_edges():
+    """288-row tiles on 12 waves (a layer with 224 to 287 rows per expert on
+    average): experts of 0..577 rows, at every edge of a wave's 32-row blocks
+    (31/32/33), of a wave's 96 rows (95/96/97, 191/192/193), of the old and
+    the new tile height (255..257, 287..289) and of two tiles (575..577), so
+    waves run the three-, two- and zero-block K loops and the even split of
+    the gate/up tiles and the full-plus-short split of the down tiles both
+    occur.  Every row of moe_expert_ffn against the oracle's expert FFN, and
+    two more calls bitwise equal to the first."""
+    import mixture_experts_sparse_moe_amd as moe
+    from gpu_harness import cfg_of
+    t = torch()
+    counts = np.array([0, 1, 31, 32, 33, 95, 96, 97, 191, 192, 193, 255, 256, 257, 287, 288, 289,
+                       575, 576, 577, 300, 300, 300, 300], dtype=np.int32)
+    sh = S("tall", T=691, d=512, E=counts.size, k=8, d_ff=256)
+    assert moe.moe_forward_plan(cfg_of(sh))["tile_rows"] == 288
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    P = sh.T * sh.k
+    assert offsets[-1] <= P
+    inp = synth.make_inputs(sh, 13)
+    L = DeviceLayer(sh, inp)
+    pairs = np.random.default_rng(13).permutation(P).astype(np.int32)   # rows past offsets[E] unused
+    say(f"[case] tall tiles: {int(offsets[-1])} rows in {sh.E} experts, {sh}")
+    sp, off = to_dev(pairs), to_dev(offsets)
+    outs = []
+    for _ in range(3):
+        out = L.empty_act(P, sh.d)
+        moe.moe_expert_ffn(L.cfg, L.d["x"], sp, off, L.d["w_gate"], L.d["w_up"], L.d["w_down"], None, None,
+                           None, out, None, L.ws)
+        outs.append(out)
+    t.cuda.synchronize()
+    n = int(offsets[-1])
+    first = to_host(outs[0])[:n]
+    for o in outs[1:]:
+        np.testing.assert_array_equal(to_host(o)[:n], first)
+    worst = 0.0
+    for e in range(sh.E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        _, want = oracle.expert_rows(e, inp["x"], pairs[a:b] // sh.k, inp["w_gate"], inp["w_up"], inp["w_down"])
+        worst = max(worst, assert_close(synth.bf16_to_f64(first[a:b]), want, TAU[sh.dtype],
+                                        f"expert {e} ({b - a} rows)"))
     say(f"[ok] worst max|err|/max|ref| = {worst:.2e}")

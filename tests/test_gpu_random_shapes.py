@@ -96,6 +96,42 @@ def test_random_shape_forward_shared_merged(name):
     check_layer(sh, synth.make_inputs(sh, 43))
 
 
+def random_tall_shapes(n=6, seed=11):
+    """bf16 layers whose routed GEMMs take 288-row tiles: 224 to 287 rows per
+    expert on average, d a multiple of 256 and d_ff of 128 (the persistent
+    kernels), with or without a shared expert (as wide as the routed ones,
+    so inside their launches, or narrower), uniform or skewed routing."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        E = int(rng.choice([8, 16, 32, 64]))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        d = 256 * int(rng.integers(1, 3))
+        d_ff = 128 * int(rng.integers(1, 4))
+        T = -(-E * int(rng.integers(224, 288)) // k)
+        if not 224 * E <= T * k < 288 * E:
+            continue
+        shared = int(rng.integers(0, 3))           # none, same width, narrower
+        d_ff_s = (d_ff, 128)[shared - 1] if shared else 0
+        score = synth.SIGMOID if rng.random() < 0.5 else synth.SOFTMAX
+        zipf = 1.1 if (rng.random() < 0.3 and E <= d) else 0.0
+        out.append(S(f"t{len(out):02d}", T=T, d=d, E=E, k=k, d_ff=d_ff, num_shared=int(shared > 0),
+                     d_ff_shared=d_ff_s, score_fn=score, zipf_s=zipf))
+    return out
+
+
+TALL = {sh.name: sh for sh in random_tall_shapes()}
+
+
+@pytest.mark.parametrize("name", sorted(TALL))
+def test_random_shape_forward_tall_tiles(name):
+    import mixture_experts_sparse_moe_amd as moe
+    from gpu_harness import cfg_of
+    sh = TALL[name]
+    assert moe.moe_forward_plan(cfg_of(sh))["tile_rows"] == 288, "the shape must take the 288-row tiles"
+    check_layer(sh, synth.make_inputs(sh, 47))
+
+
 # the oracle's chain rule costs about 12 d d_ff fp64 multiply-adds per pair
 BACKWARD = sorted(n for n, sh in SHAPES.items() if sh.T * sh.k * sh.d * sh.d_ff <= 2.5e8)
 
