@@ -356,8 +356,10 @@ def copy_calibration():
 # batches (one of them runs per workload); dual = gate/up, single = down; the
 # routed ones take the expert-aligned tile order (template argument 2), the
 # shared expert's do not
-GATE_UP_KERNELS = ("gemm_bf16_persistent_kernel<true, true", "gemm_bf16_skinny_kernel<true")
-DOWN_KERNELS = ("gemm_bf16_persistent_kernel<false, true", "gemm_bf16_skinny_kernel<false")
+GATE_UP_KERNELS = ("gemm_bf16_persistent_kernel<true, true", "gemm_bf16_tall_kernel<true",
+                   "gemm_bf16_skinny_kernel<true")
+DOWN_KERNELS = ("gemm_bf16_persistent_kernel<false, true", "gemm_bf16_tall_kernel<false",
+                "gemm_bf16_skinny_kernel<false")
 READ_COUNTERS = ("TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum")
 
 

@@ -1141,7 +1141,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 // no request, through the bounds check of their buffer resource) and land
 // in LDS rows 256..287 of the B buffer, which no fragment reads.  The K stage
 // loop, the stream of stages across tiles, the tile order (expert-aligned
-// bands), the queue and the epilogue are those of the 256-row kernel.
+// bands) and the queue are those of the 256-row kernel; the epilogue issues
+// every store of both the dual and the single tile, and the next tile's
+// first fragments are read after it.
 struct TallSrc {
     const char* a;      // A: the start of A (gathered rows) or of the tile's rows
     const char* b0;     // B panel: gate rows (dual) or the weight rows
@@ -1157,7 +1159,11 @@ __global__ __launch_bounds__(768, 1) void gemm_bf16_tall_kernel(GemmGroup g, int
     constexpr int BN = DUAL ? 128 : 256;   // output columns of a tile
     constexpr int STG = BM * kBK;          // elements of one A or B stage buffer (36 KB)
     constexpr bool BAL = DUAL;             // even M split for the gate/up tiles
-    constexpr int kEpiStores = DUAL ? 4 * NB : 0;
+    // every epilogue store is issued (4 per 32 x 32 block; rows past the end
+    // are dropped by the bounds check), so the next tile's first wait leaves
+    // them in flight (the down GEMM at DeepSeek-V3: -1.9 %, where the 256-row
+    // kernel, with more dead blocks, measured +0.8 %)
+    constexpr int kEpiStores = 4 * NB * (DUAL ? 1 : 2);
     constexpr int kWaitFirst = (7 << 4) | (kEpiStores & 15) | ((kEpiStores >> 4) << 14);
     __shared__ __align__(16) uint16_t sA0[STG], sA1[STG];
     __shared__ __align__(16) uint16_t sB0[STG], sB1[STG];
@@ -1373,7 +1379,6 @@ __global__ __launch_bounds__(768, 1) void gemm_bf16_tall_kernel(GemmGroup g, int
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const int rb = wm * (NB * 32) + i * 32;
-            if (!DUAL && rb >= tr.nrows) break;
 #pragma unroll
             for (int bo_ = 0; bo_ < (DUAL ? 1 : 2); ++bo_) {
                 const int cb = DUAL ? wn * 32 : wn * 64 + bo_ * 32;
@@ -1381,8 +1386,6 @@ __global__ __launch_bounds__(768, 1) void gemm_bf16_tall_kernel(GemmGroup g, int
 #pragma unroll
                 for (int q = 0; q < 16; ++q)
                     v[q] = DUAL ? silu_f32(acc[i][0][q]) * acc[i][1][q] : acc[i][bo_][q];
-                // buffer stores (32-bit offsets from a scalar base): the rows past
-                // the end are dropped by the bounds check
                 store_block_bf16_all(C + (int64_t)(tr.row0 + rb) * g.N + tr.n0 + cb, g.N, tr.nrows - rb, v,
                                      lane);
             }
