@@ -2,7 +2,7 @@
 workspace is the library's fixed per-GPU device array), against moe_forward
 with a workspace the caller allocated: four calls in a row on the same
 array, each smaller than the one before (a layer whose shared expert runs
-inside the routed GEMMs, a prefill-sized layer whose GEMMs claim tiles
+inside the routed GEMMs, on 288-row tiles, a prefill-sized layer whose GEMMs claim tiles
 through counters kept in the array, a decode-sized layer on the 32-row
 kernels with the router's fused dispatch, a five-token layer), every output
 bitwise equal to moe_forward's (same kernels, same launches)."""
@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 S = synth.LayerShape
 
 CASES = [
-    S("n0", T=1024, d=512, E=32, k=4, d_ff=512, num_shared=1, d_ff_shared=512, score_fn=synth.SIGMOID),
+    S("n0", T=1024, d=512, E=16, k=4, d_ff=512, num_shared=1, d_ff_shared=512, score_fn=synth.SIGMOID),
     S("n1", T=600, d=256, E=8, k=2, d_ff=384, router_scale=4.0),
     S("n2", T=48, d=1024, E=16, k=4, d_ff=512, num_shared=1, d_ff_shared=256, score_fn=synth.SIGMOID),
     S("n3", T=5, d=512, E=8, k=2, d_ff=256),
@@ -42,6 +42,7 @@ def test_noalloc_forward_equals_forward_with_workspace():
     for L in layers:
         assert moe.moe_workspace_bytes(L.cfg) <= moe.NOALLOC_SCRATCH_BYTES
     assert moe.moe_forward_plan(layers[0].cfg)["shared_merged"]
+    assert moe.moe_forward_plan(layers[0].cfg)["tile_rows"] == 288
     sizes = [moe.moe_workspace_bytes(L.cfg) for L in layers]
     assert sizes == sorted(sizes, reverse=True)
     got, want = [], []
