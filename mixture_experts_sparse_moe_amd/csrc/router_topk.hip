@@ -132,7 +132,7 @@ __device__ __forceinline__ void logits_bf16(const RouteArgs& a, int t0, int c0, 
     for (int i = 0; i < BPW; ++i)
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
-    skinny_mma<Sh, false>(src, nc, 0, sX0, sX1, sX2, sX3, sW0, sW1, sW2, sW3, acc);
+    skinny_mma<Sh, false, 0>(src, nc, 0, sX0, sX1, sX2, sX3, sW0, sW1, sW2, sW3, acc);
     const int b0 = skinny_block<Sh, false>(w, 0);
 
     // D element j of block i: token row 8 (j / 4) + 4 half + j % 4, expert r32

@@ -44,13 +44,17 @@ __device__ __forceinline__ int skinny_block(int w, int i) {
     return PAIRED ? gi + Sh::NG * i : gi * Sh::BPW + i;
 }
 
+// B_POLICY: cache policy operand of the B loads (2, non-temporal, for a
+// stream of weights read once: the decode GEMMs, whose gate/up took 0.324 ->
+// 0.287 ms with it; 0 for the router, whose workgroups all re-read W_r from
+// the L2 and lost 6 % with nt).
 // src[0]: this lane's A row 8 w + lane / 8 at its swizzled 16-byte chunk, in
 // the first chunk of the K range; src[j], j >= 1: B row 8 (w + 4 j - 4) +
 // lane / 8 likewise.  Chunk c of the range is at byte offset 128 c.  Adds
 // the products of nchunks chunks, walked from chunk rot (< nchunks), into
 // acc.  Every wave of the workgroup must call it; on return this wave's DMAs
 // have landed (other waves' only after a barrier).
-template <class Sh, bool PAIRED>
+template <class Sh, bool PAIRED, int B_POLICY>
 __device__ __forceinline__ void skinny_mma(const char* const* src, int nchunks, int rot, uint16_t* sX0,
                                            uint16_t* sX1, uint16_t* sX2, uint16_t* sX3, uint16_t* sW0,
                                            uint16_t* sW1, uint16_t* sW2, uint16_t* sW3, f32x16_t* acc) {
@@ -69,7 +73,7 @@ __device__ __forceinline__ void skinny_mma(const char* const* src, int nchunks, 
                                          (lds_ptr_t)((sX_) + 8 * w * kSkChunk), 16, 0, 0);      \
         _Pragma("unroll") for (int j = 1; j < P; ++j)                                           \
             __builtin_amdgcn_global_load_lds((const void*)(src[j] + ko_),                       \
-                                             (lds_ptr_t)((sW_) + 8 * (w + 4 * j - 4) * kSkChunk), 16, 0, 0); \
+                                             (lds_ptr_t)((sW_) + 8 * (w + 4 * j - 4) * kSkChunk), 16, 0, B_POLICY); \
     } while (0)
 
 #define MOE_SK_MFMA(sX_, sW_)                                                                   \
