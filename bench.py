@@ -139,6 +139,16 @@ def upload(a: np.ndarray, torch, dev):
     return torch.from_numpy(a).to(dev)
 
 
+def device_tile_rows(counts, d_ff: int, slots: int = 256) -> int:
+    """Tile height moe_forward takes on the device for a layer of 640 or
+    more rows per expert: 288 when the gate/up GEMM's 288-row tiles take fewer
+    rounds of the persistent grid than 256-row ones, a 288-row round weighing
+    9/8 (the rule moe_forward_plan documents)."""
+    tn = 2 * d_ff // 256
+    r = {bm: -(-sum(-(-int(n) // bm) for n in counts) * tn // slots) for bm in (256, 288)}
+    return 288 if 9 * r[288] < 8 * r[256] else 256
+
+
 def algorithmic(sh, counts: np.ndarray, shared_merged: bool = False) -> dict:
     """Algorithmic work of the layer and of its two expert GEMM kernels.
 
@@ -544,6 +554,9 @@ def measure(name: str, args, torch, moe, dev, extras: bool) -> dict:
     tev.close()
     cnt = counts.cpu().numpy()
     plan = moe.moe_forward_plan(cfg)
+    if plan["tile_rows"] == 0:
+        # chosen on the device per call: the library's documented rule on these counts
+        plan["tile_rows_chosen"] = device_tile_rows(cnt, sh.d_ff)
     alg = algorithmic(sh, cnt, plan["shared_merged"])
     bf16 = sh.dtype == synth.BF16
     peak_c = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS

@@ -360,8 +360,13 @@ int moe_capacity(const moe_config* cfg, double capacity_factor);
  *   [0] rows per tile of the routed expert GEMMs: 256; 288 when the experts
  *       hold 224 to 287 rows on average with the tile queue (fewer than 640
  *       rows per expert), so that experts of 257..288 rows are one tile; 32
- *       for few pairs (fp32 layers report 256 and use a plain tiled kernel),
- *   [1] K splits of the routed down GEMM (1 = none),
+ *       for few pairs (fp32 layers report 256 and use a plain tiled kernel);
+ *       0 when each call chooses between 256 and 288 on the device from the
+ *       expert counts (bf16, 640 or more rows per expert, d a multiple of
+ *       256 and d_ff of 128): both kernels of each GEMM are launched and the
+ *       one not chosen exits at once,
+ *   [1] K splits of the routed down GEMM (1 = none; with [0] = 0, of its
+ *       256-row kernel: the 288-row one does not split),
  *   [2] K splits of the shared down GEMM (0 when num_shared == 0),
  *   [3] 1 when the shared expert runs inside the routed GEMMs' launches
  *       (stages 4-5 of moe_forward_staged empty), else 0.

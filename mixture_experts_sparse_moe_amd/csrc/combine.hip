@@ -61,6 +61,11 @@ __device__ __forceinline__ void load_row_sum(const uint16_t* p, int slices, int6
 template <int S>
 __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(CombineArgs a) {
     constexpr int JB = 8 / S;
+    // launched beside the combine of the other tile height's K split: run only
+    // if the device-side choice of the routed GEMMs' tile height is this one
+    if (a.choice.offsets &&
+        tall_tiles_chosen(a.choice.offsets, a.choice.E, a.choice.tiles_n, a.choice.slots) != (a.choice.rows == 288))
+        return;
     const int t = blockIdx.x;
     __shared__ int s_pos[16];
     __shared__ float s_w[16];

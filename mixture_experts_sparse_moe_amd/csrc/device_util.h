@@ -51,4 +51,31 @@ constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) 
 // ... and for lgkmcnt == 0 as well (every LDS access of the wave done).
 constexpr int wait_vmcnt_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
+// The tile height of the routed GEMMs of a layer with several M tiles per
+// expert, from the experts' rows n_e = offsets[e + 1] - offsets[e]: true
+// (288-row tiles) if their gate/up tiles take fewer rounds of the persistent
+// grid than 256-row tiles would, a 288-row round weighing 9/8 of a 256-row
+// one (its rows).  Rounds = ceil(M tiles x tiles_n / slots).  Every wave
+// computes it on its own from the same integers, so all the kernels of a call
+// agree.  Mixtral prefill (982-1068 rows per expert): 14 rounds against 16,
+// 288; Hunyuan-A13B (Zipf-skewed, 199-6363 rows): 25 against 27, 256.
+__device__ __forceinline__ bool tall_tiles_chosen(const int32_t* offsets, int E, int tiles_n, int slots) {
+    int t256 = 0, t288 = 0;
+    for (int e = (int)(threadIdx.x & 63); e < E; e += 64) {
+        const int n = offsets[e + 1] - offsets[e];
+        t256 += (n + 255) / 256;
+        t288 += (n + 287) / 288;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        t256 += __shfl_xor(t256, o, 64);
+        t288 += __shfl_xor(t288, o, 64);
+    }
+    t256 = __builtin_amdgcn_readfirstlane(t256);
+    t288 = __builtin_amdgcn_readfirstlane(t288);
+    const int64_t r256 = ((int64_t)t256 * tiles_n + slots - 1) / slots;
+    const int64_t r288 = ((int64_t)t288 * tiles_n + slots - 1) / slots;
+    return 9 * r288 < 8 * r256;
+}
+
 }  // namespace moe

@@ -841,6 +841,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
     __shared__ int s_tb[258], s_off[258];     // up to 257 groups (256 experts + a shared one)
     __shared__ int s_wsum[8];
 
+    // launched beside the 288-row kernel: run only if the 256-row tiles are chosen
+    if constexpr (MODE == kModeFwd)
+        if (g.choice.offsets &&
+            tall_tiles_chosen(g.choice.offsets, g.choice.E, g.choice.tiles_n, g.choice.slots) != (g.choice.rows == 288))
+            return;
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w >> 2, wn = w & 3;
@@ -1156,7 +1161,7 @@ struct TallSrc {
     int rot;            // first K stage of the walk
 };
 
-template <bool DUAL>
+template <bool DUAL, bool QUEUE>
 __global__ __launch_bounds__(768, 1) void gemm_bf16_tall_kernel(GemmGroup g, int tiles_n) {
     constexpr int NB = 3;                  // 32-row blocks per wave
     constexpr int BM = 3 * NB * 32;        // 288
@@ -1176,6 +1181,10 @@ __global__ __launch_bounds__(768, 1) void gemm_bf16_tall_kernel(GemmGroup g, int
     __shared__ int s_next[2];
     __shared__ TileQueue s_tq;
 
+    // launched beside the 256-row kernel: run only if the 288-row tiles are chosen
+    if (g.choice.offsets &&
+        tall_tiles_chosen(g.choice.offsets, g.choice.E, g.choice.tiles_n, g.choice.slots) != (g.choice.rows == 288))
+        return;
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w >> 2, wn = w & 3;
@@ -1191,8 +1200,10 @@ __global__ __launch_bounds__(768, 1) void gemm_bf16_tall_kernel(GemmGroup g, int
     const int wn_win = max(nslot / kWMW, 1);
     int L = xcd * per + slot;
     if (L >= Lend) return;
+    // queue: at the start of tile i, s_next[i & 1] holds tile i + 1 (or -1);
+    // fixed schedule: every nslot-th tile of the XCD's range
     int claim = -1;
-    if (tid == 0) {
+    if (QUEUE && tid == 0) {
         s_tq = TileQueue{g.queue, per, TL, nslot, xcd, xcd * per + 3 * nslot, Lend};
         s_next[0] = L + nslot < Lend ? L + nslot : -1;
         s_next[1] = s_next[0] >= 0 && L + 2 * nslot < Lend ? L + 2 * nslot : -1;
@@ -1361,9 +1372,16 @@ __global__ __launch_bounds__(768, 1) void gemm_bf16_tall_kernel(GemmGroup g, int
 
     uint16_t* C = static_cast<uint16_t*>(g.C);
     for (int it = 0;; ++it) {
-        const int Ln = __builtin_amdgcn_readfirstlane(s_next[it & 1]);
-        const bool more = Ln >= 0;
-        if (tid == 0) claim = next_tile_step(s_tq, s_next, it, claim);
+        int Ln;
+        bool more;
+        if constexpr (QUEUE) {
+            Ln = __builtin_amdgcn_readfirstlane(s_next[it & 1]);
+            more = Ln >= 0;
+            if (tid == 0) claim = next_tile_step(s_tq, s_next, it, claim);
+        } else {
+            Ln = L + nslot;
+            more = Ln < Lend;
+        }
         const TileRef tn = tile_of(more ? Ln : L);
         TallSrc nxt;
 
@@ -1637,10 +1655,15 @@ hipError_t launch_bf16_persistent(const GemmGroup& g, hipStream_t s) {
     // costs the K loop a compiler-inserted wait on the loads in flight
     const dim3 grid(persistent_grid()), block(512);
     if (g.tall) {
-        // 288-row tiles on 12 waves: the tile queue and the expert-aligned order only
-        if (!g.queue || !g.aligned_bands || g.splitk != 1) return hipErrorInvalidValue;
-        hipExtLaunchKernelGGL((gemm_bf16_tall_kernel<DUAL>), grid, dim3(768), 0, s, g.t_start, g.t_stop, 0, g,
-                              g.N / BN);
+        // 288-row tiles on 12 waves: the expert-aligned order, no K split; the
+        // fixed schedule only as one side of a device-side choice
+        if (!g.aligned_bands || g.splitk != 1 || !(g.queue || g.choice.offsets)) return hipErrorInvalidValue;
+        if (g.queue)
+            hipExtLaunchKernelGGL((gemm_bf16_tall_kernel<DUAL, true>), grid, dim3(768), 0, s, g.t_start, g.t_stop,
+                                  0, g, g.N / BN);
+        else
+            hipExtLaunchKernelGGL((gemm_bf16_tall_kernel<DUAL, false>), grid, dim3(768), 0, s, g.t_start,
+                                  g.t_stop, 0, g, g.N / BN);
         return hipGetLastError();
     }
     if (g.queue) {
@@ -1740,6 +1763,8 @@ hipError_t launch_f32(const GemmGroup& g, hipStream_t s) {
 }
 
 }  // namespace
+
+int persistent_slots() { return persistent_grid(); }
 
 int64_t grouped_m_tiles_upper(int64_t rows, int G, int bm) {
     // sum_e ceil(n_e / bm) <= floor((sum_e n_e + G*(bm-1)) / bm)

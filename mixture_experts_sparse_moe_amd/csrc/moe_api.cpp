@@ -169,6 +169,23 @@ bool routed_tall(const moe_config* c) {
     return P >= 224 * E && P < 288 * E;
 }
 
+// With several M tiles per expert (the fixed schedule) the routed GEMMs'
+// tile height is chosen on the device from the expert counts
+// (tall_tiles_chosen): moe_forward launches the 256-row and the 288-row
+// kernel of each GEMM, and the one not chosen exits at once.  Whole layers,
+// same session, each height forced: Mixtral prefill (experts of 982-1068
+// rows) 2.83 ms on 256-row tiles, 2.64 ms on 288-row ones (35 -> 32 M tiles,
+// the down GEMM unsplit); Hunyuan-A13B (Zipf-skewed, 199-6363 rows) 4.81 ms
+// against 4.90 ms.  The average rows per expert, which the host knows, is
+// 1024 for both.  bf16 layers whose GEMMs both fit the persistent kernels
+// (d a multiple of 256, d_ff of 128, gathered rows under 4 GiB).
+bool routed_choice(const moe_config* c) {
+    if (c->dtype != MOE_BF16 || c->num_tokens == 0 || paths(c).routed_skinny || routed_queue(c)) return false;
+    const int64_t T = c->num_tokens, P = T * c->top_k, d = c->d_model, f = c->d_ff;
+    return d % 256 == 0 && f % 128 == 0 && T * d * 2 < (int64_t(1) << 32) && P * f * 2 < (int64_t(1) << 32) &&
+           c->num_experts <= 256;
+}
+
 // moe_forward computes the shared expert in the routed GEMMs' launches, as one
 // more group (its T tokens after the T k pairs; its weights through the
 // GEMMs' last-group pointers), when it is as wide as the routed experts, the
@@ -283,29 +300,52 @@ int run_ffn(const moe_config* c, const void* x, const int32_t* sorted, const int
             MOE_HIP(launch_fill_zero_f32(reinterpret_cast<float*>(queue), kQueueInts, s));
         // merged: the shared expert's T tokens are group E (rows P .. P + T)
         const int G = c->num_experts + (merged ? 1 : 0), rows = P + (merged ? c->num_tokens : 0);
+        // tile height chosen on the device: the 256-row kernels (down split
+        // in sp.routed K ranges) and the 288-row ones (unsplit) both launch
+        const bool choose = routed_choice(c);
+        TileChoice tc;
+        if (choose) tc = TileChoice{offsets, c->num_experts, 2 * c->d_ff / 256, persistent_slots(), 256};
         GemmGroup up{x, sorted, c->top_k, offsets, G, rows, wg, wu, H, c->d_ff, c->d_model};
         up.skinny = pa.routed_skinny;
         up.aligned_bands = true;
         up.queue = use_queue ? queue : nullptr;
         up.tall = routed_tall(c);
+        up.choice = tc;
         if (merged) {
             up.B0_last = sg;
             up.B1_last = su;
         }
         // stage events 1 and 2 are the routed gate/up kernel's own start and
-        // end timestamps: no separate records around the dominant kernel
-        if (ev) {
-            up.t_start = static_cast<hipEvent_t>(ev[1]);
-            up.t_stop = static_cast<hipEvent_t>(ev[2]);
-        }
+        // end timestamps (with a choice, the first launch's start and the
+        // second's end): no separate records around the dominant kernel
+        hipEvent_t e1 = ev ? static_cast<hipEvent_t>(ev[1]) : nullptr;
+        hipEvent_t e2 = ev ? static_cast<hipEvent_t>(ev[2]) : nullptr;
+        up.t_start = e1;
+        up.t_stop = choose ? nullptr : e2;
         MOE_HIP(launch_grouped_gemm(up, true, bf16, s));
+        if (choose) {
+            GemmGroup up288 = up;
+            up288.tall = true;
+            up288.choice.rows = 288;
+            up288.t_start = nullptr;
+            up288.t_stop = e2;
+            MOE_HIP(launch_grouped_gemm(up288, true, bf16, s));
+        }
         GemmGroup down{H, nullptr, 1, offsets, G, rows, wd, nullptr, out, c->d_model,
                        c->d_ff, sp.routed, (int64_t)P * c->d_model, true};
         down.skinny = pa.routed_skinny;
         down.queue = use_queue ? queue + 256 : nullptr;
         down.tall = routed_tall(c) && sp.routed == 1;
+        down.choice = tc;
         if (merged) down.B0_last = sd;
         MOE_HIP(launch_grouped_gemm(down, false, bf16, s));
+        if (choose) {
+            GemmGroup down288 = down;
+            down288.tall = true;
+            down288.splitk = 1;
+            down288.choice.rows = 288;
+            MOE_HIP(launch_grouped_gemm(down288, false, bf16, s));
+        }
         MOE_TRY(mark(ev, 3, s));
     } else {
         MOE_TRY(mark(ev, 1, s));
@@ -330,12 +370,23 @@ int run_ffn(const moe_config* c, const void* x, const int32_t* sorted, const int
     return MOE_OK;
 }
 
+// offsets (moe_forward, when routed_choice): the routed down GEMM wrote
+// sp.routed slices on 256-row tiles or one on 288-row tiles, as the device
+// chose; with sp.routed > 1 a combine for each launches and one exits.
 int run_combine(const moe_config* c, const void* out, const float* wts, const int32_t* pos,
-                const void* shared_out, void* y, hipStream_t s, Splits sp = Splits{1, 1}) {
+                const void* shared_out, void* y, hipStream_t s, Splits sp = Splits{1, 1},
+                const int32_t* offsets = nullptr) {
     const int64_t P = (int64_t)c->num_tokens * c->top_k;
     CombineArgs a{out, wts, pos, shared_out, y, c->num_tokens, c->d_model, c->top_k,
                   sp.routed, P * c->d_model, sp.shared, (int64_t)c->num_tokens * c->d_model};
+    const bool choose = offsets && sp.routed > 1 && routed_choice(c);
+    if (choose) a.choice = TileChoice{offsets, c->num_experts, 2 * c->d_ff / 256, persistent_slots(), 256};
     MOE_HIP(launch_combine(a, c->dtype == MOE_BF16, s));
+    if (choose) {
+        a.splitk = 1;
+        a.choice.rows = 288;
+        MOE_HIP(launch_combine(a, c->dtype == MOE_BF16, s));
+    }
     return MOE_OK;
 }
 
@@ -397,7 +448,7 @@ int forward_impl(const moe_config* cfg, const moe_options* opts, const void* x, 
     const Splits sp = splits(cfg);
     MOE_TRY(run_ffn(cfg, x, sorted, offsets, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, O, S,
                     at<void>(ws, L.H), at<void>(ws, L.Hs), queue, !dispatched, s, ev, sp, merged));
-    MOE_TRY(run_combine(cfg, O, wts, pos, S, y, s, sp));
+    MOE_TRY(run_combine(cfg, O, wts, pos, S, y, s, sp, offsets));
     return mark(ev, 6, s);
 }
 
@@ -1008,7 +1059,7 @@ int moe_forward_plan(const moe_config* cfg, int32_t* plan_out) {
     if (plan_out == nullptr) return MOE_ERR_NULL;
     const Paths pa = paths(cfg);
     const Splits sp = splits(cfg);
-    plan_out[0] = pa.routed_skinny ? 32 : routed_tall(cfg) ? 288 : 256;
+    plan_out[0] = pa.routed_skinny ? 32 : routed_tall(cfg) ? 288 : routed_choice(cfg) ? 0 : 256;
     plan_out[1] = sp.routed;
     plan_out[2] = cfg->num_shared ? sp.shared : 0;
     plan_out[3] = merged_shared(cfg, 0x7FFFFFFF) ? 1 : 0;

@@ -68,6 +68,21 @@ int route_ranges(int T, int d, bool bf16);
 hipError_t launch_route_split(const RouteArgs& a, int ranges, float* part, const DispatchArgs* d,
                               hipStream_t s);
 
+// ---- tile height chosen on the device ---------------------------------------
+// With several M tiles per expert (the routed GEMMs' fixed schedule) the
+// expert counts decide whether 256-row tiles (8 waves) or 288-row tiles (12
+// waves; the down GEMM unsplit) take less time, and only the device holds
+// them.  moe_forward then launches both kernels of each GEMM (and, when the
+// K splits differ, a combine for each), and a kernel given a TileChoice runs
+// only if the choice is its tile height (tall_tiles_chosen, device_util.h).
+struct TileChoice {
+    const int32_t* offsets = nullptr;  // [E + 1] grouped rows per expert; nullptr: no choice
+    int E = 0;
+    int tiles_n = 0;    // N tiles of 256 columns of the gate/up GEMM (2 d_ff / 256)
+    int slots = 0;      // workgroups of the persistent grid
+    int rows = 0;       // the tile height this kernel stands for: 256 or 288
+};
+
 // ---- grouped GEMMs ----------------------------------------------------------
 // One "problem group" of the grouped GEMM: rows of A (optionally gathered)
 // times per-group weight matrices.  Row r of group g spans
@@ -122,7 +137,11 @@ struct GemmGroup {
     const void* B1_last = nullptr;
     // bf16 persistent kernel, forward mode with the tile queue and the
     // expert-aligned order: 288-row tiles on 12 waves instead of 256-row ones
+    // (also on the fixed schedule, when launched with a choice)
     bool tall = false;
+    // bf16 persistent kernel, forward mode: run only if the device-side choice
+    // of tile height is choice.rows (choice.offsets nullptr: always run)
+    TileChoice choice;
 };
 // Dual mode: C = silu(A B0^T) * (A B1^T).  Single: C = A B0^T, or with
 // splitk > 1 the partial products of the K ranges, C slice s = A[:, Ks] B0[:, Ks]^T.
@@ -140,6 +159,8 @@ bool skinny_fits(int N, int K, bool dual, int splitk);
 int choose_splitk_skinny(int64_t mt_expected, int N, int K);
 // Upper bound of M-tiles over all groups for tile height bm.
 int64_t grouped_m_tiles_upper(int64_t rows, int G, int bm);
+// Workgroups of the persistent GEMM grid on the current device (CUs, a multiple of 8).
+int persistent_slots();
 
 // ---- backward -------------------------------------------------------------------
 // Generic grouped GEMM for the backward (any operand layout; bf16 MFMA when both
@@ -259,6 +280,7 @@ struct CombineArgs {
     int64_t part_stride = 0;// elements between expert_out slices
     int shared_splitk = 1;  // the same for the shared rows
     int64_t shared_stride = 0;
+    TileChoice choice;      // bf16: run only if the device-side choice is choice.rows
 };
 hipError_t launch_combine(const CombineArgs& a, bool bf16, hipStream_t s);
 

@@ -278,6 +278,9 @@ def test_forward_plan():
     mix = moe.MoeConfig.of(4096, 4096, 8, 2, 14336)
     p = moe.moe_forward_plan(mix)
     assert p["shared_splits"] == 0 and not p["shared_merged"] and p["routed_splits"] >= 1
+    assert p["tile_rows"] == 0                            # chosen on the device per call
+    odd = moe.MoeConfig.of(4096, 4096 + 128, 8, 2, 14336)   # d not a multiple of 256: no choice
+    assert moe.moe_forward_plan(odd)["tile_rows"] == 256
     L = moe.lib()
     assert L.moe_forward_plan(ctypes.byref(ds), None) == moe.MOE_ERR_NULL
     out = (ctypes.c_int32 * 4)()
@@ -287,7 +290,9 @@ def test_forward_plan():
 def test_forward_plan_tile_rows_boundaries():
     """Rows per tile of the routed GEMMs (host only): 288 exactly when the
     experts hold 224 to 287 rows on average and the tile queue runs (bf16,
-    over 32 and under 640 rows per expert), else 256 (32 for few rows)."""
+    over 32 and under 640 rows per expert); 0 (each call chooses 256 or 288
+    on the device) for bf16 layers of 640 rows per expert or more whose
+    widths fit both kernels; else 256 (32 for few rows)."""
     def rows(T, k, E, dtype=moe.MOE_BF16):
         c = moe.MoeConfig.of(T, 512, E, k, 512, 0, 0, moe.MOE_SCORE_SIGMOID, dtype=dtype)
         return moe.moe_forward_plan(c)["tile_rows"]
@@ -301,7 +306,8 @@ def test_forward_plan_tile_rows_boundaries():
     assert rows(1024, 2, 8) == 288                        # 256 per expert, 8 experts
     assert rows(900, 2, 8) == 288                         # 225 per expert
     assert rows(2048, 2, 8) == 256                        # 512 per expert (tile queue, two tiles)
-    assert rows(4096, 2, 8) == 256                        # 1024 per expert (no tile queue)
+    assert rows(4096, 2, 8) == 0                          # 1024 per expert (no tile queue): chosen on the device
+    assert rows(4096, 2, 8, moe.MOE_F32) == 256
     assert rows(32, 8, 256) == 32                         # decode
 
 

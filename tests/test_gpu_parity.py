@@ -63,7 +63,23 @@ SMALL = {
                                                     d_ff_shared=256, score_fn=synth.SIGMOID),
     "bf16_e16_k4_shared_tall": S("c", T=1000, d=256, E=16, k=4, d_ff=384, num_shared=1, d_ff_shared=128),
     "bf16_e32_k8_zipf_tall": S("c", T=1024, d=256, E=32, k=8, d_ff=256, zipf_s=1.1),
+    # 640 or more rows per expert: the tile height is chosen on the device
+    # from the counts, and moe_forward splits the 256-row down GEMM in 4 K
+    # ranges (the 288-row one never): experts of 761..867 rows take 288-row
+    # tiles, experts of 633..733 rows 256-row ones (test_device_tile_choice)
+    "bf16_e8_k2_fixed_choose288": S("c", T=3264, d=256, E=8, k=2, d_ff=8192),
+    "bf16_e8_k2_fixed_choose256": S("c", T=2720, d=256, E=8, k=2, d_ff=8192),
 }
+
+
+def tile_choice_rows(counts, d_ff, slots=256):
+    """The tile height the library chooses on the device for a layer of 640
+    or more rows per expert (written out from its documented rule): 288 when
+    the gate/up GEMM's 288-row tiles take fewer rounds of the persistent grid
+    than 256-row ones, a 288-row round weighing 9/8."""
+    tn = 2 * d_ff // 256
+    r = {bm: -(-sum(-(-int(n) // bm) for n in counts) * tn // slots) for bm in (256, 288)}
+    return 288 if 9 * r[288] < 8 * r[256] else 256
 
 
 def say(msg):
@@ -344,6 +360,58 @@ def test_tall_tiles_live_block_edges():
     L = DeviceLayer(sh, inp)
     pairs = np.random.default_rng(13).permutation(P).astype(np.int32)   # rows past offsets[E] unused
     say(f"[case] tall tiles: {int(offsets[-1])} rows in {sh.E} experts, {sh}")
+    sp, off = to_dev(pairs), to_dev(offsets)
+    outs = []
+    for _ in range(3):
+        out = L.empty_act(P, sh.d)
+        moe.moe_expert_ffn(L.cfg, L.d["x"], sp, off, L.d["w_gate"], L.d["w_up"], L.d["w_down"], None, None,
+                           None, out, None, L.ws)
+        outs.append(out)
+    t.cuda.synchronize()
+    n = int(offsets[-1])
+    first = to_host(outs[0])[:n]
+    for o in outs[1:]:
+        np.testing.assert_array_equal(to_host(o)[:n], first)
+    worst = 0.0
+    for e in range(sh.E):
+        a, b = int(offsets[e]), int(offsets[e + 1])
+        if a == b:
+            continue
+        _, want = oracle.expert_rows(e, inp["x"], pairs[a:b] // sh.k, inp["w_gate"], inp["w_up"], inp["w_down"])
+        worst = max(worst, assert_close(synth.bf16_to_f64(first[a:b]), want, TAU[sh.dtype],
+                                        f"expert {e} ({b - a} rows)"))
+    say(f"[ok] worst max|err|/max|ref| = {worst:.2e}")
+
+
+def test_device_tile_choice():
+    """The two fixed-schedule cases above take the tile height they are meant
+    to cover (test_small_layer checks their outputs), and a layer whose experts
+    sit at the edges of the 288-row kernel's row blocks and tiles (0, 1, 31..33,
+    95..97, 287..289, 575..577 rows) among experts of 769..864 rows runs the
+    288-row kernels on the fixed schedule: every row of moe_expert_ffn against
+    the oracle's expert FFN, and two more calls bitwise equal to the first."""
+    import mixture_experts_sparse_moe_amd as moe
+    from gpu_harness import cfg_of
+    t = torch()
+    for name, want in (("bf16_e8_k2_fixed_choose288", 288), ("bf16_e8_k2_fixed_choose256", 256)):
+        sh = SMALL[name]
+        plan = moe.moe_forward_plan(cfg_of(sh))
+        assert plan["tile_rows"] == 0 and plan["routed_splits"] == 4, plan
+        counts = oracle_routing(synth.make_inputs(sh, 0), sh)
+        counts = np.bincount(counts["ids"].ravel(), minlength=sh.E)
+        assert tile_choice_rows(counts, sh.d_ff) == want, (name, counts.tolist())
+    edges = [0, 1, 31, 32, 33, 95, 96, 97, 287, 288, 289, 575, 576, 577]
+    counts = np.array(edges + [769 + 9 * i for i in range(11)], dtype=np.int32)
+    sh = S("fixed288", T=2000, d=256, E=counts.size, k=8, d_ff=8192)
+    assert sh.T * sh.k >= 640 * sh.E and int(counts.sum()) <= sh.T * sh.k
+    assert moe.moe_forward_plan(cfg_of(sh))["tile_rows"] == 0
+    assert tile_choice_rows(counts, sh.d_ff) == 288
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    P = sh.T * sh.k
+    inp = synth.make_inputs(sh, 17)
+    L = DeviceLayer(sh, inp)
+    pairs = np.random.default_rng(17).permutation(P).astype(np.int32)   # rows past offsets[E] unused
+    say(f"[case] fixed-schedule 288-row tiles: {int(offsets[-1])} rows in {sh.E} experts, {sh}")
     sp, off = to_dev(pairs), to_dev(offsets)
     outs = []
     for _ in range(3):
