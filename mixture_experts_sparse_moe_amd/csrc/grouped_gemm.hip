@@ -1252,10 +1252,13 @@ __global__ __launch_bounds__(768, 1) void gemm_bf16_tall_kernel(GemmGroup g, int
     };
 
 // Refill of a stage buffer: three A and three B instructions per wave, all
-// through bounds-checked buffer resources, unconditionally.  The weight rows,
-// read by one M tile per expert here, are loaded with the non-temporal cache
-// policy (nt), which leaves the L2 to the gathered x rows that the N tiles
-// of an expert share (DeepSeek-V3 gate/up 4.40 -> 4.26 ms, layer -2.2 %).
+// through bounds-checked buffer resources, unconditionally.  With the tile
+// queue (about one M tile per expert) the weight rows, read by one M tile,
+// are loaded with the non-temporal cache policy (nt), which leaves the L2 to
+// the gathered x rows that the N tiles of an expert share (DeepSeek-V3
+// gate/up 4.40 -> 4.26 ms, layer -2.2 %); on the fixed schedule several M
+// tiles of an expert share each weight panel, which the plain policy keeps
+// in L2 for them.
 #define TALL_DMA(sA_, sB_, src_, kt_)                                                           \
     do {                                                                                        \
         const int kr_ = (kt_) + (src_).rot;                                                     \
@@ -1272,7 +1275,7 @@ __global__ __launch_bounds__(768, 1) void gemm_bf16_tall_kernel(GemmGroup g, int
                 __builtin_amdgcn_make_buffer_rsrc((void*)bp_, (short)0, (int)kDeadOff, 0x00020000); \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(                                           \
                 rb_, (lds_ptr_t)((sB_) + (3 * w + j) * 8 * kBK), 16,                            \
-                (int)__builtin_elementwise_add_sat(bo[j], ko_), 0, 0, kCacheNT);                \
+                (int)__builtin_elementwise_add_sat(bo[j], ko_), 0, 0, QUEUE ? kCacheNT : 0);    \
         }                                                                                       \
     } while (0)
 #define TALL_FRAGS(sA_, sB_, s_, af_, bf_, NA_)                                                 \
