@@ -38,6 +38,9 @@ FORWARD = {
     # group of the routed GEMMs (the dispatch writes its rows on every replay)
     "prefill_e32_k4_shared_in_routed": S("g", T=1024, d=512, E=32, k=4, d_ff=512, num_shared=1,
                                          d_ff_shared=512, score_fn=synth.SIGMOID),
+    # 640 or more rows per expert: both tile heights' GEMMs and both combines
+    # are captured; the device picks one of each on every replay
+    "prefill_e8_k2_tile_choice": S("g", T=3264, d=256, E=8, k=2, d_ff=8192),
 }
 
 

@@ -20,6 +20,10 @@ CASES = {
                           score_fn=synth.SIGMOID),
     "shared_on_its_own": S("s", T=1024, d=512, E=8, k=2, d_ff=1024, num_shared=1, d_ff_shared=512),
     "decode": S("s", T=32, d=512, E=8, k=2, d_ff=512),
+    # 640 or more rows per expert: the tile height is chosen on the device, so
+    # both gate/up kernels run between events 1 and 2 (the first one's start,
+    # the second one's end), and both combines of the two K splits
+    "tile_choice": S("s", T=3264, d=256, E=8, k=2, d_ff=8192),
 }
 
 
