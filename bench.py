@@ -362,10 +362,12 @@ def copy_calibration():
 
 
 # the routed GEMM kernels as rocprofv3 names them (prefix of the template
-# argument list): the 256-row tile kernel, or the 32-row one for decode-sized
-# batches (one of them runs per workload); dual = gate/up, single = down; the
-# routed ones take the expert-aligned tile order (template argument 2), the
-# shared expert's do not
+# argument list): the 256-row tile kernel, the 288-row one, or the 32-row one
+# for decode-sized batches; dual = gate/up, single = down; the routed ones take
+# the expert-aligned tile order (template argument 2), the shared expert's do
+# not.  Where the tile height is chosen on the device both the 256- and the
+# 288-row kernel are launched and one exits at once: the traffic is that of the
+# kernel of the two that read the most
 GATE_UP_KERNELS = ("gemm_bf16_persistent_kernel<true, true", "gemm_bf16_tall_kernel<true",
                    "gemm_bf16_skinny_kernel<true")
 DOWN_KERNELS = ("gemm_bf16_persistent_kernel<false, true", "gemm_bf16_tall_kernel<false",
@@ -409,6 +411,14 @@ def _read_bytes(rows, names):
     return None if None in n else 32 * n[0] + 64 * n[1] + 128 * n[2]
 
 
+def _busiest_kernel(rows, names):
+    """Of the kernels matching names, the full name of the one whose
+    dispatches read the most (None if none matches)."""
+    kns = {r["Kernel_Name"] for r in rows if any(n in r["Kernel_Name"] for n in names)}
+    best = max(kns, key=lambda kn: _read_bytes(rows, (kn,)) or 0.0, default=None)
+    return best
+
+
 def traffic_from(args):
     """HBM bytes per launch of the routed GEMMs from rocprofv3 runs: fabric
     reads from the TCC_EA0_RDREQ_32B/64B/128B counts, writes from WRITE_SIZE
@@ -426,11 +436,12 @@ def traffic_from(args):
            "copy_check": {"copy_bytes": COPY_BYTES, "read_bytes": crd, "write_bytes": cwr},
            "source_hash": kernel_source_hash()}
     for tag, names in (("gate_up", GATE_UP_KERNELS), ("down", DOWN_KERNELS)):
-        rb = _read_bytes(rows_rd, names)
-        wk = _per_dispatch(rows_wr, "WRITE_SIZE", names)
+        kn = _busiest_kernel(rows_rd, names)
+        rb = _read_bytes(rows_rd, (kn,)) if kn else None
+        wk = _per_dispatch(rows_wr, "WRITE_SIZE", (kn,)) if kn else None
         if rb is None or wk is None:
             sys.exit(f"missing counters for {tag}: read {rb}, write {wk}")
-        rec[tag] = {"read_bytes": rb, "write_bytes": wk * 1024, "bytes_per_launch": rb + wk * 1024}
+        rec[tag] = {"kernel": kn, "read_bytes": rb, "write_bytes": wk * 1024, "bytes_per_launch": rb + wk * 1024}
     rec["bytes_per_launch"] = rec["gate_up"]["bytes_per_launch"]
     data = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
     data[args.workload] = rec
