@@ -397,9 +397,31 @@ def test_device_tile_choice():
         sh = SMALL[name]
         plan = moe.moe_forward_plan(cfg_of(sh))
         assert plan["tile_rows"] == 0 and plan["routed_splits"] == 4, plan
-        counts = oracle_routing(synth.make_inputs(sh, 0), sh)
+        inp = synth.make_inputs(sh, 0)
+        counts = oracle_routing(inp, sh)
         counts = np.bincount(counts["ids"].ravel(), minlength=sh.E)
         assert tile_choice_rows(counts, sh.d_ff) == want, (name, counts.tolist())
+        # Which kernels moe_forward ran, seen in its output: the step calls on
+        # moe_forward's own routing never split the down GEMM (moe_expert_ffn
+        # writes the finished product), so their y is bitwise moe_forward's
+        # when it took the 288-row tiles (unsplit), and differs in the last
+        # bits when it took the 256-row ones (four bf16 K slices).
+        L = DeviceLayer(sh, inp)
+        fw = L.forward()
+        P = sh.T * sh.k
+        counts_d = t.empty(sh.E, dtype=t.int32, device="cuda")
+        offsets = t.empty(sh.E + 1, dtype=t.int32, device="cuda")
+        sp = t.empty(P, dtype=t.int32, device="cuda")
+        pp = t.empty(P, dtype=t.int32, device="cuda")
+        moe.moe_dispatch(L.cfg, fw["ids"], counts_d, offsets, sp, pp, L.ws)
+        out = L.empty_act(P, sh.d)
+        moe.moe_expert_ffn(L.cfg, L.d["x"], sp, offsets, L.d["w_gate"], L.d["w_up"], L.d["w_down"], None, None,
+                           None, out, None, L.ws)
+        y = L.empty_act(sh.T, sh.d)
+        moe.moe_combine(L.cfg, out, fw["weights"], pp, None, y)
+        t.cuda.synchronize()
+        same = np.array_equal(to_host(y), to_host(fw["y"]))
+        assert same == (want == 288), f"{name}: moe_forward's y {'equals' if same else 'differs from'} the unsplit one"
     edges = [0, 1, 31, 32, 33, 95, 96, 97, 287, 288, 289, 575, 576, 577]
     counts = np.array(edges + [769 + 9 * i for i in range(11)], dtype=np.int32)
     sh = S("fixed288", T=2000, d=256, E=counts.size, k=8, d_ff=8192)
