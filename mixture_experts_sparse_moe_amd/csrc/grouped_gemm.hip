@@ -615,6 +615,7 @@ __device__ __forceinline__ bf16x8_t load_b_tr(const uint16_t* sB, int off) {
 }
 
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // store_block_bf16 with every store issued: the block's rows go through a
 // buffer resource of rows_left rows (none if rows_left <= 0), whose bounds
@@ -642,6 +643,70 @@ __device__ __forceinline__ void store_block_bf16_all(uint16_t* Cb, int64_t ldc, 
         out.y = (j & 2) ? e1 : r;
         const int row = 8 * a + 4 * half + j;
         __builtin_amdgcn_raw_buffer_store_b64(out, rc, (int)((row * ldc + (r32 - j)) * 2), 0, 0);
+    }
+}
+
+// Two adjacent 32 x 32 blocks of MFMA results (columns 0..31 and 32..63 of a
+// 64-column span) as bf16, in whole 128-byte row pieces.  After the 4 x 4
+// quad transpose of each block (lane j = r32 % 4 of quad q = r32 / 4 holds
+// row 8 a + 4 half + j, columns 4 q .. 4 q + 3), the lanes of quads q and
+// q ^ 1 swap halves (DPP row shifts by 4 lanes): an even quad ends with
+// columns 4 q .. 4 q + 7 of block 0, an odd quad columns 4 (q - 1) ..
+// 4 (q - 1) + 7 of block 1.  One 16-byte store per lane and a then writes 8
+// rows of 128 bytes: half the store instructions of an 8-byte store per block
+// and no half-written cache lines (DeepSeek-V3 down GEMM: its stores, left
+// out altogether in a timing-only build, cost 12 % of it).  ALL: every lane
+// issues its 4 stores through a buffer resource of rows_left rows, whose bounds
+// check drops the rows past the end; else rows past the end are not stored.
+template <bool ALL>
+__device__ __forceinline__ void store_pair_bf16(uint16_t* Cb, int64_t ldc, int rows_left, const float* v0,
+                                                const float* v1, int lane) {
+    const int half = lane >> 5, r32 = lane & 31, j = r32 & 3;
+    const bool odd = (r32 >> 2) & 1;
+    const uint32_t sel = (j & 1) ? 0x03020706u : 0x05040100u;
+    const int col = odd ? 32 + (r32 - j) - 4 : r32 - j;
+    const int recs = rows_left > 0 ? (int)((int64_t)rows_left * ldc * 2) : 0;
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc((void*)Cb, (short)0, recs, 0x00020000);
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        uint32_t q0[2], q1[2];   // this lane's row, 4 columns, of block 0 and of block 1
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const float* v = b ? v1 : v0;
+            uint32_t* o = b ? q1 : q0;
+            const uint32_t d0 = pack_bf16x2(v[4 * a + 0], v[4 * a + 1]);
+            const uint32_t d1 = pack_bf16x2(v[4 * a + 2], v[4 * a + 3]);
+            const uint32_t n0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d0, 0xB1, 0xF, 0xF, true);
+            const uint32_t n1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)d1, 0xB1, 0xF, 0xF, true);
+            const uint32_t e0 = __builtin_amdgcn_perm(n0, d0, sel);
+            const uint32_t e1 = __builtin_amdgcn_perm(n1, d1, sel);
+            const uint32_t sq = (j & 2) ? e0 : e1;
+            const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)sq, 0x4E, 0xF, 0xF, true);
+            o[0] = (j & 2) ? r : e0;
+            o[1] = (j & 2) ? e1 : r;
+        }
+        // an even quad passes its block-1 piece to the odd quad 4 lanes up and
+        // takes that quad's block-0 piece (row_shl:4: lane i reads lane i + 4;
+        // row_shr:4: lane i reads lane i - 4; both stay inside a row of 16 lanes)
+        const uint32_t s0 = odd ? q0[0] : q1[0], s1 = odd ? q0[1] : q1[1];
+        const uint32_t up0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s0, 0x104, 0xF, 0xF, true);
+        const uint32_t up1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0x104, 0xF, 0xF, true);
+        const uint32_t dn0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s0, 0x114, 0xF, 0xF, true);
+        const uint32_t dn1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0x114, 0xF, 0xF, true);
+        u32x4_t out;
+        out.x = odd ? dn0 : q0[0];
+        out.y = odd ? dn1 : q0[1];
+        out.z = odd ? q1[0] : up0;
+        out.w = odd ? q1[1] : up1;
+        const int row = 8 * a + 4 * half + j;
+        if constexpr (ALL) {
+            __builtin_amdgcn_raw_buffer_store_b128(out, rc, (int)((row * ldc + col) * 2), 0, 0);
+        } else {
+            if (row < rows_left) *reinterpret_cast<u32x4_t*>(Cb + row * ldc + col) = out;
+        }
+        // one row group at a time: interleaving them raised the register use
+        // of the 288-row down kernel past its budget (spills)
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -1104,14 +1169,24 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_persistent_kernel(GemmGroup 
 #pragma unroll
                     for (int q = 0; q < 16; ++q) v[q] = acc[i][1][q];
                     store_block_bf16(static_cast<uint16_t*>(g.C2) + at, g.N, tr.nrows - rb, v, lane);
-                } else if constexpr (MODE == kModeFwd) {
+                } else if constexpr (MODE == kModeFwd && DUAL) {
                     float v[16];
 #pragma unroll
-                    for (int q = 0; q < 16; ++q)
-                        v[q] = DUAL ? silu_f32(acc[i][0][q]) * acc[i][1][q] : acc[i][bo][q];
+                    for (int q = 0; q < 16; ++q) v[q] = silu_f32(acc[i][0][q]) * acc[i][1][q];
                     uint16_t* Cb = C + tr.ks * g.part_stride + (int64_t)(tr.row0 + rb) * g.N + tr.n0 + cb;
-                    if constexpr (kAllStores) store_block_bf16_all(Cb, g.N, tr.nrows - rb, v, lane);
-                    else store_block_bf16(Cb, g.N, tr.nrows - rb, v, lane);
+                    store_block_bf16_all(Cb, g.N, tr.nrows - rb, v, lane);
+                } else if constexpr (MODE == kModeFwd) {
+                    // both 32-column blocks of the wave at once, as whole 128-byte rows
+                    if (bo == 0) {
+                        float v0[16], v1[16];
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) {
+                            v0[q] = acc[i][0][q];
+                            v1[q] = acc[i][1][q];
+                        }
+                        uint16_t* Cb = C + tr.ks * g.part_stride + (int64_t)(tr.row0 + rb) * g.N + tr.n0 + cb;
+                        store_pair_bf16<false>(Cb, g.N, tr.nrows - rb, v0, v1, lane);
+                    }
                 } else {
                     float* Cf = static_cast<float*>(g.C) +
                                 (KG ? (int64_t)tr.grp * g.c_gstride : (int64_t)tr.ks * g.part_stride) +
@@ -1172,7 +1247,7 @@ __global__ __launch_bounds__(768, 1) void gemm_bf16_tall_kernel(GemmGroup g, int
     // are dropped by the bounds check), so the next tile's first wait leaves
     // them in flight (the down GEMM at DeepSeek-V3: -1.9 %, where the 256-row
     // kernel, with more dead blocks, measured +0.8 %)
-    constexpr int kEpiStores = 4 * NB * (DUAL ? 1 : 2);
+    constexpr int kEpiStores = 4 * NB;
     constexpr int kWaitFirst = (7 << 4) | (kEpiStores & 15) | ((kEpiStores >> 4) << 14);
     __shared__ __align__(16) uint16_t sA0[STG], sA1[STG];
     __shared__ __align__(16) uint16_t sB0[STG], sB1[STG];
@@ -1407,15 +1482,21 @@ __global__ __launch_bounds__(768, 1) void gemm_bf16_tall_kernel(GemmGroup g, int
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const int rb = wm * (NB * 32) + i * 32;
-#pragma unroll
-            for (int bo_ = 0; bo_ < (DUAL ? 1 : 2); ++bo_) {
-                const int cb = DUAL ? wn * 32 : wn * 64 + bo_ * 32;
+            if constexpr (DUAL) {
                 float v[16];
 #pragma unroll
-                for (int q = 0; q < 16; ++q)
-                    v[q] = DUAL ? silu_f32(acc[i][0][q]) * acc[i][1][q] : acc[i][bo_][q];
-                store_block_bf16_all(C + (int64_t)(tr.row0 + rb) * g.N + tr.n0 + cb, g.N, tr.nrows - rb, v,
+                for (int q = 0; q < 16; ++q) v[q] = silu_f32(acc[i][0][q]) * acc[i][1][q];
+                store_block_bf16_all(C + (int64_t)(tr.row0 + rb) * g.N + tr.n0 + wn * 32, g.N, tr.nrows - rb, v,
                                      lane);
+            } else {
+                float v0[16], v1[16];
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    v0[q] = acc[i][0][q];
+                    v1[q] = acc[i][1][q];
+                }
+                store_pair_bf16<true>(C + (int64_t)(tr.row0 + rb) * g.N + tr.n0 + wn * 64, g.N, tr.nrows - rb, v0,
+                                      v1, lane);
             }
         }
         if (!more) break;
