@@ -544,7 +544,8 @@ def measure(name: str, args, torch, moe, dev, extras: bool) -> dict:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
-    gu_ms = float(np.mean([tev.ms(a, b) for a, b in gu_ev]))
+    gu_each = np.array([tev.ms(a, b) for a, b in gu_ev])
+    gu_ms = float(gu_each.mean())
     y_host = y.float().cpu().numpy().astype(np.float64)
     ids_host = ids.cpu().numpy()
 
@@ -614,6 +615,13 @@ def measure(name: str, args, torch, moe, dev, extras: bool) -> dict:
         "layer_frac_of_floor": floor_layer / layer_s,
         "stages_ms": {n: round(float(v), 4) for n, v in zip(moe.STAGE_NAMES, stage_avg)},
         "staged_ms_per_step": round(float(stage_ms.sum(1).mean()), 4),
+        # spread over the steps: the whole layer per step (start event to the
+        # last stage's, staged pass) and the gate/up kernel per launch (timed pass)
+        "step_ms_stats": {"median": round(float(np.median(stage_ms.sum(1))), 4),
+                          "min": round(float(stage_ms.sum(1).min()), 4),
+                          "p90": round(float(np.percentile(stage_ms.sum(1), 90)), 4)},
+        "gate_up_ms_stats": {"median": round(float(np.median(gu_each)), 4), "min": round(float(gu_each.min()), 4),
+                             "p90": round(float(np.percentile(gu_each, 90)), 4)},
         "expert_load": {"max_over_mean": float(cnt.max() / max(cnt.mean(), 1e-9)),
                         "touched": alg["touched"], "min": int(cnt.min()), "max": int(cnt.max())},
         "plan": plan,
