@@ -326,8 +326,14 @@ def cpu_baseline(sh, inp, target_s: float) -> dict:
         n = int(min(sh.T, max(n * 2, n * (target_s / max(dt, 1e-3)) * 0.8)))
     sample = (f"{toks.size} of {sh.T} tokens (first, last, seeded random), full routing and {sh.k} "
               f"experts" + (" + shared expert" if sh.num_shared else "") + " per token, fp64")
-    return {"value": toks.size / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 3)}, (toks, r["y"], r["ids"])
+    out = {"value": toks.size / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": sample, "seconds": round(dt, 3)}
+    if toks.size >= sh.T:
+        # a whole small layer: also on one thread, the per-core rate
+        t0 = time.perf_counter()
+        oracle.forward_tokens(inp, sh.k, toks, sh.score_fn, sh.renormalize, nthreads=1)
+        out["single_thread_value"] = toks.size / (time.perf_counter() - t0)
+    return out, (toks, r["y"], r["ids"])
 
 
 def parity_of(y_gpu: np.ndarray, ids_gpu: np.ndarray, ref, dtype: str) -> dict:

@@ -163,6 +163,9 @@ CAP_CASES = {
     "decode_e16_k4": (S("c", T=20, d=1024, E=16, k=4, d_ff=128), 0.8),
     "chunks_e32_k4": (S("c", T=1300, d=128, E=32, k=4, d_ff=64, zipf_s=1.1), 1.1),
     "fp32_e8_k2": (S("c", T=64, d=64, E=8, k=2, d_ff=128, dtype=synth.F32), 0.75),
+    # 640 or more rows per expert: the tile height chosen on the device from
+    # the kept counts, and a combine for each down K split
+    "fixed_tile_choice_e8_k2": (S("c", T=3264, d=256, E=8, k=2, d_ff=8192), 1.0),
 }
 
 
