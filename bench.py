@@ -258,7 +258,7 @@ def backward_cost(torch, moe, cfg, d, sh, stream, steps: int) -> dict:
     return out
 
 
-def practical_ceilings(torch, dev) -> dict:
+def practical_ceilings(torch, dev, sh=None) -> dict:
     """Measured ceilings on the same GPU, next to the nominal peaks: a 1 GiB
     device copy (read + write bytes / time), a 4 GiB streaming read (torch row
     sums of an fp32 [2^18, 4096] tensor: read bytes / time, the writes are
@@ -302,7 +302,44 @@ def practical_ceilings(torch, dev) -> dict:
     out["torch_matmul_bf16_tflops"] = 2.0 * 4096 * 14336 * 4096 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
     out["torch_matmul_shape"] = "4096x14336x4096"
     del a, b, c
+    if sh is not None and sh.dtype == synth_bf16():
+        out["torch_bmm_bf16"] = grouped_yardstick(torch, dev, sh)
     return out
+
+
+def synth_bf16():
+    import synth
+    return synth.BF16
+
+
+def grouped_yardstick(torch, dev, sh) -> dict:
+    """The layer's two routed expert products as torch.bmm (hipBLASLt
+    batched GEMMs), one batch per routed expert, every expert holding the
+    average T k / E rows: [E, M, d] x [E, d, 2 d_ff] (gate and up as one
+    product) and [E, M, d_ff] x [E, d_ff, d], both operands contiguous.  The
+    routed experts' weight bytes and FLOPs, without the routing's raggedness,
+    the gathered rows, SiLU or the shared expert; a library yardstick only."""
+    G = sh.E
+    M = max(1, sh.T * sh.k // sh.E)
+    res = {"groups": G, "rows": M}
+    for tag, K, N in (("gate_up", sh.d, 2 * sh.d_ff), ("down", sh.d_ff, sh.d)):
+        a = torch.empty(G, M, K, device=dev, dtype=torch.bfloat16).normal_()
+        b = torch.empty(G, K, N, device=dev, dtype=torch.bfloat16).normal_(0.0, K ** -0.5)
+        for _ in range(2):
+            c = torch.bmm(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            c = torch.bmm(a, b)
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        flops = 2.0 * G * M * K * N
+        nbytes = 2.0 * G * (M * K + K * N + M * N)
+        res[tag] = {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12, "gbs": nbytes / (ms * 1e-3) / 1e9}
+        del a, b, c
+    return res
 
 
 def cpu_baseline(sh, inp, target_s: float) -> dict:
@@ -647,7 +684,7 @@ def measure(name: str, args, torch, moe, dev, extras: bool) -> dict:
     if extras and not args.no_backward:
         out["backward"] = backward_cost(torch, moe, cfg, d, sh, stream, 3)
     if extras and not args.no_ceilings:
-        out["practical_ceilings"] = practical_ceilings(torch, dev)
+        out["practical_ceilings"] = practical_ceilings(torch, dev, sh)
     del d, ws, y, counts, ids
     torch.cuda.empty_cache()
     if args.no_cpu_baseline:
