@@ -5,7 +5,7 @@
 // matmul.  Here the grouping is a stable counting sort of pair ids
 // p = t*k + j by expert id, done in three small kernels with no float
 // atomics, so the result is deterministic:
-//   1. count:   one workgroup per chunk of kDispatchChunk pairs builds an LDS
+//   1. count:   one workgroup per chunk of kScatterChunk pairs builds an LDS
 //               histogram (integer LDS atomics) -> chunk_counts[chunk][e].
 //   2. scan:    one workgroup: per-expert totals over chunks, exclusive scan
 //               over experts -> counts, offsets; chunk_counts becomes each
@@ -34,8 +34,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_count_kernel(DispatchArgs a
     __shared__ int hist[256];
     for (int e = threadIdx.x; e < a.E; e += kThreads) hist[e] = 0;
     __syncthreads();
-    const int64_t p0 = (int64_t)blockIdx.x * kDispatchChunk;
-    const int64_t p1 = min((int64_t)a.P, p0 + kDispatchChunk);
+    const int64_t p0 = (int64_t)blockIdx.x * kScatterChunk;
+    const int64_t p1 = min((int64_t)a.P, p0 + kScatterChunk);
     for (int64_t p = p0 + threadIdx.x; p < p1; p += kThreads) atomicAdd(&hist[a.ids[p]], 1);
     __syncthreads();
     for (int e = threadIdx.x; e < a.E; e += kThreads)
@@ -48,10 +48,17 @@ __global__ __launch_bounds__(kThreads) void dispatch_scan_kernel(DispatchArgs a,
     const int e = threadIdx.x;
     int run = 0;
     if (e < a.E) {
-        for (int c = 0; c < nchunks; ++c) {
-            int v = a.chunk_counts[(int64_t)c * a.E + e];
-            a.chunk_counts[(int64_t)c * a.E + e] = run;   // exclusive within expert
-            run += v;
+        // eight chunks' counts loaded together, then rewritten as each
+        // chunk's first rank inside the expert
+        for (int c0 = 0; c0 < nchunks; c0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = c0 + i < nchunks ? a.chunk_counts[(int64_t)(c0 + i) * a.E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (c0 + i < nchunks) a.chunk_counts[(int64_t)(c0 + i) * a.E + e] = run;   // exclusive within expert
+                run += v[i];
+            }
         }
         run = min(run, a.cap);
         a.counts[e] = run;
@@ -73,8 +80,8 @@ __global__ __launch_bounds__(kThreads) void dispatch_scatter_kernel(DispatchArgs
         for (int q = 0; q < kWaves; ++q) wcount[q][e] = 0;
     }
     __syncthreads();
-    const int64_t p0 = (int64_t)blockIdx.x * kDispatchChunk;
-    const int64_t p1 = min((int64_t)a.P, p0 + kDispatchChunk);
+    const int64_t p0 = (int64_t)blockIdx.x * kScatterChunk;
+    const int64_t p1 = min((int64_t)a.P, p0 + kScatterChunk);
     scatter_range(a, p0, p1, running, base, wcount);
 }
 
@@ -91,7 +98,10 @@ __global__ void fill_zero_kernel(int32_t* a, int na, int32_t* b, int nb) {
 
 }  // namespace
 
-int dispatch_num_chunks(int P) { return (P + kDispatchChunk - 1) / kDispatchChunk; }
+// Chunks of 512 pairs: the scatter walks its chunk 256 pairs at a time, with
+// barriers between rounds, so smaller chunks spread it over more CUs
+// (DeepSeek-V3, 65,536 pairs: 128 workgroups instead of 32).
+int dispatch_num_chunks(int P) { return P <= kDispatchChunk ? 1 : (P + kScatterChunk - 1) / kScatterChunk; }
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     const int nchunks = dispatch_num_chunks(a.P);

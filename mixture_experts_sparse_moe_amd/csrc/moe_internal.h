@@ -16,7 +16,8 @@ using bf16_t = uint16_t;  // bf16 storage: upper half of an IEEE fp32
 int validate_config(const moe_config* cfg);
 
 // ---- dispatch: histogram, scan, stable scatter ------------------------------
-constexpr int kDispatchChunk = 2048;   // pairs per chunk (one workgroup each)
+constexpr int kDispatchChunk = 2048;   // at most this many pairs: one workgroup does the whole dispatch
+constexpr int kScatterChunk = 512;     // more pairs: chunks of this many, one workgroup each
 struct DispatchArgs {
     const int32_t* ids;     // [P]
     int32_t* counts;        // [E]
@@ -35,6 +36,7 @@ struct DispatchArgs {
     int tail = 0;
     int tail_mul = 1;
 };
+// 1 for P <= kDispatchChunk (one workgroup), else chunks of kScatterChunk pairs.
 int dispatch_num_chunks(int P);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 
