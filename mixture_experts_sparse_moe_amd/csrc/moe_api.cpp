@@ -137,7 +137,7 @@ Layout layout(const moe_config* c) {
     L.O = take(sp.routed * P * c->d_model * elem(c));
     L.S = take(c->num_shared ? sp.shared * T * c->d_model * elem(c) : 0);
     const int rr = route_ranges(c->num_tokens, c->d_model, c->dtype == MOE_BF16);
-    L.rpart = take(rr > 1 ? (size_t)rr * T * E * sizeof(float) : 0);
+    L.rpart = take(c->dtype == MOE_BF16 && (rr > 1 || E <= 128) ? (size_t)rr * T * E * sizeof(float) : 0);
     L.spart = take(((T + 31) / 32) * 2 * E * sizeof(float));
     L.total = o;
     L.dispatch_need = align_up(nchunks * E * sizeof(int32_t));
@@ -249,8 +249,18 @@ int run_route(const moe_config* c, const void* x, const void* w_router, int32_t*
     const int rr = route_ranges(c->num_tokens, c->d_model, bf16);
     const bool fuse = part && rr > 1 && disp && c->num_tokens <= 32;
     if (dispatched) *dispatched = fuse;
-    if (part && rr > 1) MOE_HIP(launch_route_split(a, rr, part, fuse ? disp : nullptr, s));
-    else MOE_HIP(launch_route(a, bf16, s));
+    // With the workspace's partial logits (moe_forward, bf16) and at most 128
+    // experts, the logits and the selection run as two kernels even without a
+    // K split: the selection then has 16 waves per workgroup (two tokens each)
+    // where the fused kernel's 4 waves walk 8 tokens each after the MFMA loop,
+    // alone on their SIMDs (Hunyuan-A13B, 64 experts: 47 -> 40 us).  With 256
+    // experts the separate selection took as long as it saved (DeepSeek-V3:
+    // 115 -> 118 us).  One range adds nothing to the logits: the same values as
+    // the fused kernel's.
+    if (part && bf16 && (rr > 1 || c->num_experts <= 128))
+        MOE_HIP(launch_route_split(a, rr, part, fuse ? disp : nullptr, s));
+    else
+        MOE_HIP(launch_route(a, bf16, s));
     if (stats)
         MOE_HIP(launch_router_stats(spart, (c->num_tokens + 31) / 32, c->num_experts, c->num_tokens,
                                     opts->aux_alpha, capacity_of(opts), opts->router_stats, s));
