@@ -108,6 +108,28 @@ Splits splits(const moe_config* c) {
     return sp;
 }
 
+// How moe_forward's router runs (bf16, with the workspace's partial logits).
+// ranges 0: the fused kernel (fp32 layers).  Else logits and selection as
+// two kernels over `ranges` K ranges: fewer than 256 blocks of 32 tokens (K
+// split so that about 256 workgroups run) or at most 128 experts (one range:
+// the selection then has 16 waves per workgroup where the fused kernel's 4
+// waves walk 8 tokens each after the MFMA loop, alone on their SIMDs;
+// Hunyuan-A13B, 64 experts: 47 -> 40 us); or, for 129..256 experts (wide),
+// tiles of 64 tokens so that the W_r stream every workgroup reads serves
+// twice the tokens, K split to about 256 workgroups (DeepSeek-V3).  One
+// range adds nothing to the logits: the same values as the fused kernel's.
+struct RoutePlan {
+    int ranges;
+    bool wide;
+};
+
+RoutePlan route_plan(const moe_config* c) {
+    if (c->dtype != MOE_BF16 || c->num_tokens <= 0) return RoutePlan{0, false};
+    const int rr = route_ranges(c->num_tokens, c->d_model, true);
+    if (rr > 1 || c->num_experts <= 128) return RoutePlan{rr, false};
+    return RoutePlan{route_ranges64(c->num_tokens, c->d_model), true};
+}
+
 // Device workspace layout.  Every region starts on a 256-byte boundary.
 struct Layout {
     size_t ids, wts, counts, offsets, chunk, sorted, pos, H, O, Hs, S, rpart, spart, total, queue;
@@ -136,8 +158,8 @@ Layout layout(const moe_config* c) {
     const Splits sp = splits(c);
     L.O = take(sp.routed * P * c->d_model * elem(c));
     L.S = take(c->num_shared ? sp.shared * T * c->d_model * elem(c) : 0);
-    const int rr = route_ranges(c->num_tokens, c->d_model, c->dtype == MOE_BF16);
-    L.rpart = take(c->dtype == MOE_BF16 && (rr > 1 || E <= 128) ? (size_t)rr * T * E * sizeof(float) : 0);
+    const RoutePlan rp = route_plan(c);
+    L.rpart = take((size_t)rp.ranges * T * E * sizeof(float));
     L.spart = take(((T + 31) / 32) * 2 * E * sizeof(float));
     L.total = o;
     L.dispatch_need = align_up(nchunks * E * sizeof(int32_t));
@@ -246,21 +268,12 @@ int run_route(const moe_config* c, const void* x, const void* w_router, int32_t*
         a.stats_part = stats ? spart : nullptr;
     }
     const bool bf16 = c->dtype == MOE_BF16;
-    const int rr = route_ranges(c->num_tokens, c->d_model, bf16);
-    const bool fuse = part && rr > 1 && disp && c->num_tokens <= 32;
+    const RoutePlan rp = route_plan(c);
+    const bool fuse = part && rp.ranges > 1 && !rp.wide && disp && c->num_tokens <= 32;
     if (dispatched) *dispatched = fuse;
-    // With the workspace's partial logits (moe_forward, bf16) and at most 128
-    // experts, the logits and the selection run as two kernels even without a
-    // K split: the selection then has 16 waves per workgroup (two tokens each)
-    // where the fused kernel's 4 waves walk 8 tokens each after the MFMA loop,
-    // alone on their SIMDs (Hunyuan-A13B, 64 experts: 47 -> 40 us).  With 256
-    // experts the separate selection took as long as it saved (DeepSeek-V3:
-    // 115 -> 118 us).  One range adds nothing to the logits: the same values as
-    // the fused kernel's.
-    if (part && bf16 && (rr > 1 || c->num_experts <= 128))
-        MOE_HIP(launch_route_split(a, rr, part, fuse ? disp : nullptr, s));
-    else
-        MOE_HIP(launch_route(a, bf16, s));
+    if (part && rp.wide) MOE_HIP(launch_route_split64(a, rp.ranges, part, s));
+    else if (part && rp.ranges > 0) MOE_HIP(launch_route_split(a, rp.ranges, part, fuse ? disp : nullptr, s));
+    else MOE_HIP(launch_route(a, bf16, s));
     if (stats)
         MOE_HIP(launch_router_stats(spart, (c->num_tokens + 31) / 32, c->num_experts, c->num_tokens,
                                     opts->aux_alpha, capacity_of(opts), opts->router_stats, s));

@@ -427,6 +427,59 @@ __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a, float* 
     }
 }
 
+// 64 tokens per workgroup for 129..256 experts: the W_r chunks a workgroup
+// streams through LDS serve twice the tokens of route_partial_kernel's 32
+// (at DeepSeek-V3's shape the router's logits are bound by that stream: every
+// workgroup reads all of W_r).  Range r = blockIdx.y of the K chunks; the
+// fp32 logits go from the accumulators straight to part[r][T][E].
+__global__ __launch_bounds__(256) void route_partial64_kernel(RouteArgs a, float* part) {
+    using Sh = SkinnyShape<8, 3, 1, 2>;
+    __shared__ __align__(16) uint16_t sX0[Sh::XS], sX1[Sh::XS], sX2[Sh::XS];
+    __shared__ __align__(16) uint16_t sW0[Sh::WS], sW1[Sh::WS], sW2[Sh::WS];
+    const int t0 = blockIdx.x * 64;
+    const int r = blockIdx.y, nr = gridDim.y, n = a.d / kSkChunk;
+    const int c0 = (int)((int64_t)r * n / nr), c1 = (int)((int64_t)(r + 1) * n / nr);
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int half = lane >> 5, r32 = lane & 31;
+    const int64_t rowb = (int64_t)a.d * 2;
+    const int64_t kb = (int64_t)c0 * (kSkChunk * 2);
+    // A rows: the 64 tokens (rows past T repeat the last); B rows: the experts
+    // (rows past E repeat the last)
+    const char* src[Sh::P];
+#pragma unroll
+    for (int ia = 0; ia < Sh::NA; ++ia) {
+        const int rx = 32 * ia + 8 * w + (lane >> 3);
+        const int tok = min(t0 + rx, a.T - 1);
+        src[ia] = static_cast<const char*>(a.x) + tok * rowb + kb + (((lane & 7) ^ swz(rx)) * 16);
+    }
+#pragma unroll
+    for (int j = Sh::NA; j < Sh::P; ++j) {
+        const int rw = 8 * (w + 4 * (j - Sh::NA)) + (lane >> 3);
+        const int e = min(rw, a.E - 1);
+        src[j] = static_cast<const char*>(a.w) + e * rowb + kb + (((lane & 7) ^ swz(rw)) * 16);
+    }
+    f32x16_t acc[Sh::NA * Sh::BPW];
+#pragma unroll
+    for (int i = 0; i < Sh::NA * Sh::BPW; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
+    skinny_mma<Sh, false, 0>(src, c1 - c0, 0, sX0, sX1, sX2, sX2, sW0, sW1, sW2, sW2, acc);
+    // D element j of tile (ia, i): token row 32 ia + 8 (j / 4) + 4 half + j % 4, expert block w BPW + i
+    float* out = part + (int64_t)r * a.T * a.E;
+#pragma unroll
+    for (int ia = 0; ia < Sh::NA; ++ia)
+#pragma unroll
+        for (int i = 0; i < Sh::BPW; ++i) {
+            const int e = skinny_block<Sh, false>(w, i) * 32 + r32;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int t = t0 + 32 * ia + 8 * (j >> 2) + 4 * half + (j & 3);
+                if (t < a.T && e < a.E) out[(int64_t)t * a.E + e] = acc[ia * Sh::BPW + i][j];
+            }
+        }
+}
+
 // ... and one workgroup per token block adds the ranges in order and selects,
 // kFinishThreads threads (two tokens per wave: the selection is a chain of
 // wave reductions, so few tokens per wave keep it short).  With DISPATCH
@@ -549,6 +602,25 @@ hipError_t launch_route_split(const RouteArgs& a, int ranges, float* part, const
         if (d) MOE_FINISH(true, 4); else MOE_FINISH(false, 4);
     }
 #undef MOE_FINISH
+    return hipGetLastError();
+}
+
+int route_ranges64(int T, int d) {
+    if (T <= 0) return 1;
+    const int blocks = (T + 63) / 64;
+    // about 256 workgroups, each range at least 4 chunks of 64 (DeepSeek-V3,
+    // 128 blocks of 64 tokens: 2 ranges)
+    const int r = std::min((256 + blocks - 1) / blocks, d / (4 * kSkChunk));
+    return std::max(r, 1);
+}
+
+hipError_t launch_route_split64(const RouteArgs& a, int ranges, float* part, hipStream_t s) {
+    if (a.T == 0) return hipSuccess;
+    if (ranges < 1 || ranges > a.d / kSkChunk || a.E > 256 || a.E <= 128 || a.d % kSkChunk)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(route_partial64_kernel, dim3((a.T + 63) / 64, ranges), dim3(256), 0, s, a, part);
+    hipLaunchKernelGGL((route_finish_kernel<false, 4>), dim3((a.T + kBT - 1) / kBT), dim3(kFinishThreads), 0, s, a,
+                       (const float*)part, ranges, DispatchArgs{});
     return hipGetLastError();
 }
 

@@ -25,16 +25,19 @@ namespace moe {
 
 constexpr int kSkChunk = 64;            // K elements per stage
 
-template <int NBLK_, int NST_ = (NBLK_ >= 8 ? 3 : 4), int KS_ = (NBLK_ >= 4 ? 1 : 4 / NBLK_)>
+// NA: A blocks of 32 rows (the router's 64-token tiles take 2; each wave then
+// holds NA x BPW accumulator tiles, acc[ia * BPW + i]).
+template <int NBLK_, int NST_ = (NBLK_ >= 8 ? 3 : 4), int KS_ = (NBLK_ >= 4 ? 1 : 4 / NBLK_), int NA_ = 1>
 struct SkinnyShape {
-    static constexpr int NBLK = NBLK_, NST = NST_, KS = KS_;
-    static constexpr int XS = 32 * kSkChunk;                   // A stage (elements)
+    static constexpr int NBLK = NBLK_, NST = NST_, KS = KS_, NA = NA_;
+    static constexpr int XS = NA * 32 * kSkChunk;              // A stage (elements)
     static constexpr int WS = NBLK * 32 * kSkChunk;            // B stage (elements)
     static constexpr int NG = 4 / KS;                          // wave groups
     static constexpr int BPW = NBLK / NG;                      // blocks per wave
     static constexpr int NS = 4 / KS;                          // K steps per wave per chunk
-    static constexpr int P = 1 + NBLK;                         // DMA instructions per wave per chunk
+    static constexpr int P = NA + NBLK;                        // DMA instructions per wave per chunk
     static_assert(NST >= 3 && NST <= 4 && KS * NG == 4 && BPW * NG == NBLK, "shape");
+    static_assert(NA == 1 || KS == 1, "two A blocks: whole K steps per wave");
 };
 
 // Block i of wave w.
@@ -48,9 +51,9 @@ __device__ __forceinline__ int skinny_block(int w, int i) {
 // stream of weights read once: the decode GEMMs, whose gate/up took 0.324 ->
 // 0.287 ms with it; 0 for the router, whose workgroups all re-read W_r from
 // the L2 and lost 6 % with nt).
-// src[0]: this lane's A row 8 w + lane / 8 at its swizzled 16-byte chunk, in
-// the first chunk of the K range; src[j], j >= 1: B row 8 (w + 4 j - 4) +
-// lane / 8 likewise.  Chunk c of the range is at byte offset 128 c.  Adds
+// src[ia], ia < NA: this lane's A row 32 ia + 8 w + lane / 8 at its swizzled
+// 16-byte chunk, in the first chunk of the K range; src[j], j >= NA: B row
+// 8 (w + 4 (j - NA)) + lane / 8 likewise.  Chunk c of the range is at byte offset 128 c.  Adds
 // the products of nchunks chunks, walked from chunk rot (< nchunks), into
 // acc.  Every wave of the workgroup must call it; on return this wave's DMAs
 // have landed (other waves' only after a barrier).
@@ -69,24 +72,28 @@ __device__ __forceinline__ void skinny_mma(const char* const* src, int nchunks, 
         int c_ = min((st_), nchunks - 1) + rot;                                                 \
         c_ = c_ >= nchunks ? c_ - nchunks : c_;                                                 \
         const int64_t ko_ = (int64_t)c_ * (kSkChunk * 2);                                       \
-        __builtin_amdgcn_global_load_lds((const void*)(src[0] + ko_),                           \
-                                         (lds_ptr_t)((sX_) + 8 * w * kSkChunk), 16, 0, 0);      \
-        _Pragma("unroll") for (int j = 1; j < P; ++j)                                           \
+        _Pragma("unroll") for (int ia = 0; ia < Sh::NA; ++ia)                                   \
+            __builtin_amdgcn_global_load_lds((const void*)(src[ia] + ko_),                      \
+                                             (lds_ptr_t)((sX_) + (32 * ia + 8 * w) * kSkChunk), 16, 0, 0); \
+        _Pragma("unroll") for (int j = Sh::NA; j < P; ++j)                                      \
             __builtin_amdgcn_global_load_lds((const void*)(src[j] + ko_),                       \
-                                             (lds_ptr_t)((sW_) + 8 * (w + 4 * j - 4) * kSkChunk), 16, 0, B_POLICY); \
+                                             (lds_ptr_t)((sW_) + 8 * (w + 4 * (j - Sh::NA)) * kSkChunk), 16, 0, B_POLICY); \
     } while (0)
 
 #define MOE_SK_MFMA(sX_, sW_)                                                                   \
     do {                                                                                        \
         _Pragma("unroll") for (int s_ = 0; s_ < NS; ++s_) {                                     \
             const int c_ = 2 * (s0 + s_) + half;                                                \
-            const bf16x8_t xa_ = as_bf16x8(*reinterpret_cast<const uint4*>(                     \
-                (sX_) + r32 * kSkChunk + ((c_ ^ swz(r32)) * 8)));                               \
+            bf16x8_t xa_[Sh::NA];                                                               \
+            _Pragma("unroll") for (int ia = 0; ia < Sh::NA; ++ia) xa_[ia] = as_bf16x8(          \
+                *reinterpret_cast<const uint4*>((sX_) + (32 * ia + r32) * kSkChunk +            \
+                                                ((c_ ^ swz(32 * ia + r32)) * 8)));              \
             _Pragma("unroll") for (int i_ = 0; i_ < BPW; ++i_) {                                \
                 const int r_ = skinny_block<Sh, PAIRED>(w, i_) * 32 + r32;                      \
                 const bf16x8_t wb_ = as_bf16x8(*reinterpret_cast<const uint4*>(                 \
                     (sW_) + r_ * kSkChunk + ((c_ ^ swz(r_)) * 8)));                             \
-                acc[i_] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa_, wb_, acc[i_], 0, 0, 0);  \
+                _Pragma("unroll") for (int ia = 0; ia < Sh::NA; ++ia) acc[ia * BPW + i_] =      \
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa_[ia], wb_, acc[ia * BPW + i_], 0, 0, 0); \
             }                                                                                   \
         }                                                                                       \
     } while (0)
