@@ -115,8 +115,8 @@ Splits splits(const moe_config* c) {
 // the selection then has 16 waves per workgroup where the fused kernel's 4
 // waves walk 8 tokens each after the MFMA loop, alone on their SIMDs;
 // Hunyuan-A13B, 64 experts: 47 -> 40 us); or, for 129..256 experts (wide),
-// tiles of 64 tokens so that the W_r stream every workgroup reads serves
-// twice the tokens, K split to about 256 workgroups (DeepSeek-V3).  One
+// tiles of 128 tokens so that the W_r stream every workgroup reads serves
+// four times the tokens, K split to about 256 workgroups (DeepSeek-V3).  One
 // range adds nothing to the logits: the same values as the fused kernel's.
 struct RoutePlan {
     int ranges;
@@ -127,7 +127,7 @@ RoutePlan route_plan(const moe_config* c) {
     if (c->dtype != MOE_BF16 || c->num_tokens <= 0) return RoutePlan{0, false};
     const int rr = route_ranges(c->num_tokens, c->d_model, true);
     if (rr > 1 || c->num_experts <= 128) return RoutePlan{rr, false};
-    return RoutePlan{route_ranges64(c->num_tokens, c->d_model), true};
+    return RoutePlan{route_ranges_wide(c->num_tokens, c->d_model), true};
 }
 
 // Device workspace layout.  Every region starts on a 256-byte boundary.
@@ -271,7 +271,7 @@ int run_route(const moe_config* c, const void* x, const void* w_router, int32_t*
     const RoutePlan rp = route_plan(c);
     const bool fuse = part && rp.ranges > 1 && !rp.wide && disp && c->num_tokens <= 32;
     if (dispatched) *dispatched = fuse;
-    if (part && rp.wide) MOE_HIP(launch_route_split64(a, rp.ranges, part, s));
+    if (part && rp.wide) MOE_HIP(launch_route_split_wide(a, rp.ranges, part, s));
     else if (part && rp.ranges > 0) MOE_HIP(launch_route_split(a, rp.ranges, part, fuse ? disp : nullptr, s));
     else MOE_HIP(launch_route(a, bf16, s));
     if (stats)

@@ -69,12 +69,12 @@ hipError_t launch_router_stats(const float* stats_part, int blocks, int E, int T
 int route_ranges(int T, int d, bool bf16);
 hipError_t launch_route_split(const RouteArgs& a, int ranges, float* part, const DispatchArgs* d,
                               hipStream_t s);
-// bf16, 129..256 experts: 64 tokens per workgroup (the W_r stream serves
-// twice the tokens), ranges of K chunks (route_ranges64: about 256
+// bf16, 129..256 experts: 128 tokens per workgroup (the W_r stream serves
+// four times the tokens), ranges of K chunks (route_ranges_wide: about 256
 // workgroups), partial logits in part [ranges, T, E] fp32, then the same
 // selection kernel.
-int route_ranges64(int T, int d);
-hipError_t launch_route_split64(const RouteArgs& a, int ranges, float* part, hipStream_t s);
+int route_ranges_wide(int T, int d);
+hipError_t launch_route_split_wide(const RouteArgs& a, int ranges, float* part, hipStream_t s);
 
 // ---- tile height chosen on the device ---------------------------------------
 // With several M tiles per expert (the routed GEMMs' fixed schedule) the

@@ -40,6 +40,7 @@ namespace moe {
 namespace {
 
 constexpr int kBT = 32;          // tokens per workgroup
+constexpr int kWideNA = 4;       // route_partial_wide_kernel: 32-token blocks per workgroup
 constexpr int kMaxE = 256;
 constexpr int kLogitStride = kMaxE + 1;
 constexpr int kLogitFloats = kBT * kLogitStride;
@@ -427,16 +428,18 @@ __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a, float* 
     }
 }
 
-// 64 tokens per workgroup for 129..256 experts: the W_r chunks a workgroup
-// streams through LDS serve twice the tokens of route_partial_kernel's 32
+// 32 NA tokens per workgroup (NA = kWideNA token blocks of 32) for 129..256
+// experts: the W_r chunks a workgroup streams through LDS serve NA times the
+// tokens of route_partial_kernel's 32
 // (at DeepSeek-V3's shape the router's logits are bound by that stream: every
 // workgroup reads all of W_r).  Range r = blockIdx.y of the K chunks; the
 // fp32 logits go from the accumulators straight to part[r][T][E].
-__global__ __launch_bounds__(256) void route_partial64_kernel(RouteArgs a, float* part) {
-    using Sh = SkinnyShape<8, 3, 1, 2>;
+template <int NA>
+__global__ __launch_bounds__(256) void route_partial_wide_kernel(RouteArgs a, float* part) {
+    using Sh = SkinnyShape<8, 3, 1, NA>;
     __shared__ __align__(16) uint16_t sX0[Sh::XS], sX1[Sh::XS], sX2[Sh::XS];
     __shared__ __align__(16) uint16_t sW0[Sh::WS], sW1[Sh::WS], sW2[Sh::WS];
-    const int t0 = blockIdx.x * 64;
+    const int t0 = blockIdx.x * (32 * NA);
     const int r = blockIdx.y, nr = gridDim.y, n = a.d / kSkChunk;
     const int c0 = (int)((int64_t)r * n / nr), c1 = (int)((int64_t)(r + 1) * n / nr);
     const int lane = threadIdx.x & 63;
@@ -444,7 +447,7 @@ __global__ __launch_bounds__(256) void route_partial64_kernel(RouteArgs a, float
     const int half = lane >> 5, r32 = lane & 31;
     const int64_t rowb = (int64_t)a.d * 2;
     const int64_t kb = (int64_t)c0 * (kSkChunk * 2);
-    // A rows: the 64 tokens (rows past T repeat the last); B rows: the experts
+    // A rows: the 32 NA tokens (rows past T repeat the last); B rows: the experts
     // (rows past E repeat the last)
     const char* src[Sh::P];
 #pragma unroll
@@ -605,20 +608,21 @@ hipError_t launch_route_split(const RouteArgs& a, int ranges, float* part, const
     return hipGetLastError();
 }
 
-int route_ranges64(int T, int d) {
+int route_ranges_wide(int T, int d) {
     if (T <= 0) return 1;
-    const int blocks = (T + 63) / 64;
+    const int blocks = (T + 32 * kWideNA - 1) / (32 * kWideNA);
     // about 256 workgroups, each range at least 4 chunks of 64 (DeepSeek-V3,
-    // 128 blocks of 64 tokens: 2 ranges)
+    // 64 blocks of 128 tokens: 4 ranges)
     const int r = std::min((256 + blocks - 1) / blocks, d / (4 * kSkChunk));
     return std::max(r, 1);
 }
 
-hipError_t launch_route_split64(const RouteArgs& a, int ranges, float* part, hipStream_t s) {
+hipError_t launch_route_split_wide(const RouteArgs& a, int ranges, float* part, hipStream_t s) {
     if (a.T == 0) return hipSuccess;
     if (ranges < 1 || ranges > a.d / kSkChunk || a.E > 256 || a.E <= 128 || a.d % kSkChunk)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(route_partial64_kernel, dim3((a.T + 63) / 64, ranges), dim3(256), 0, s, a, part);
+    hipLaunchKernelGGL(route_partial_wide_kernel<kWideNA>, dim3((a.T + 32 * kWideNA - 1) / (32 * kWideNA), ranges),
+                       dim3(256), 0, s, a, part);
     hipLaunchKernelGGL((route_finish_kernel<false, 4>), dim3((a.T + kBT - 1) / kBT), dim3(kFinishThreads), 0, s, a,
                        (const float*)part, ranges, DispatchArgs{});
     return hipGetLastError();
