@@ -40,7 +40,9 @@ namespace moe {
 namespace {
 
 constexpr int kBT = 32;          // tokens per workgroup
-constexpr int kWideNA = 4;       // route_partial_wide_kernel: 32-token blocks per workgroup
+// route_partial_wide_kernel: 32-token blocks per workgroup (DeepSeek-V3 route
+// 117 us with the fused kernel, 86 us with 2 blocks, 83 us with 4)
+constexpr int kWideNA = 4;
 constexpr int kMaxE = 256;
 constexpr int kLogitStride = kMaxE + 1;
 constexpr int kLogitFloats = kBT * kLogitStride;
