@@ -1,11 +1,12 @@
 """The device-side tile-height rule as the bench labels it and the GPU tests
 expect it (host only).  The rule itself runs in the kernels
-(tall_tiles_chosen); bench.device_tile_rows and the parity tests'
-tile_choice_rows restate it from its documentation, and
+(tall_tiles_chosen); bench.device_tile_rows (and the parity tests'
+tile_choice_rows) restate it from its documentation, and
 test_device_tile_choice checks on the GPU, through moe_forward's output, that
-the kernels take the height these name.  Here: the two restatements agree,
-and the layer shapes whose routing the documentation quotes get the heights
-it names (Mixtral prefill 288, Hunyuan-A13B 256)."""
+the kernels take the height the restatement names.  Here: the bench's
+restatement agrees with the rule written out once more by loops, and the
+layer shapes whose routing the documentation quotes get the heights it names
+(Mixtral prefill 288, Hunyuan-A13B 256)."""
 import os
 import sys
 
